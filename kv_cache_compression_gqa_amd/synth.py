@@ -1,0 +1,222 @@
+"""Seeded synthetic inputs for the compressed-KV decode path.
+
+This module only draws random numbers and lays them out; it holds none of the method's arithmetic, so the CPU
+oracle (tests) and the HIP path can both be fed from it.
+
+Structure of a decode workload, per unit u = (layer, batch, kv_head):
+  * a unit-level query direction qbar ~ N(0, I_D);
+  * prefill keys and values ~ N(0, 1), except
+      - ``n_salient`` positions drawn without replacement from [1, len) whose keys are 4 * qbar/|qbar|
+        (keys aligned with the queries, logit about +4 above the noise), and
+      - position 0 (the attention sink) whose key is 8 * qbar/|qbar|;
+  * per decode step: q_h = qbar + eps (eps ~ N(0, I_D)) for each of the G query heads of the group, and one new
+    key and value ~ N(0, 1) appended to the cache;
+  * everything is cast (round-to-nearest-even) to the K/V storage dtype; queries use the same dtype.
+
+Every unit has its own PCG64 stream, seeded from (workload seed, flat unit id), so any subset of units can be
+regenerated on its own.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from .configs import DecodeWorkload, CriticalKVWorkload, RetentionWorkload
+
+
+def unit_rng(seed: int, unit: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), int(unit)])))
+
+
+def to_storage_bits(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float values to the storage dtype (RNE) and return the raw 16-bit patterns."""
+    if dtype == "f16":
+        return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+        return t.view(torch.int16).numpy().view(np.uint16)
+    raise ValueError(dtype)
+
+
+def bits_to_f32(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact widening of 16-bit storage patterns to float32 (for building inputs and for display)."""
+    if dtype == "f16":
+        return bits.view(np.float16).astype(np.float32)
+    if dtype == "bf16":
+        return (bits.astype(np.uint32) << 16).view(np.float32)
+    raise ValueError(dtype)
+
+
+def sequence_lengths(cfg: DecodeWorkload) -> np.ndarray:
+    if cfg.context is not None:
+        return np.full(cfg.batch, cfg.context, dtype=np.int64)
+    lo, hi = cfg.context_range
+    rng = unit_rng(cfg.seed, 1 << 23)
+    return rng.integers(lo, hi + 1, size=cfg.batch, dtype=np.int64)
+
+
+@dataclass
+class DecodeInputs:
+    """Host arrays for a decode workload (all K/V/q data as 16-bit storage patterns)."""
+
+    cfg: DecodeWorkload
+    units: np.ndarray          # [U'] flat unit ids held here
+    lengths: np.ndarray        # [U'] prefill length per held unit
+    n_windows: np.ndarray      # [U'] routable windows = len // W
+    tail0: np.ndarray          # [U'] initial tail length = len % W
+    n_windows_max: int
+    k_win: np.ndarray          # [U'][NW][W][D] uint16
+    v_win: np.ndarray
+    k_tail0: np.ndarray        # [U'][W][D] uint16 (first tail0 rows valid)
+    v_tail0: np.ndarray
+    q: np.ndarray              # [S][U'][G][D] uint16
+    k_new: np.ndarray          # [S][U'][D] uint16
+    v_new: np.ndarray
+    salient: list             # per held unit: sorted salient positions
+
+
+def _unit_decode_draws(cfg: DecodeWorkload, unit: int, length: int, steps: int):
+    rng = unit_rng(cfg.seed, unit)
+    D = cfg.head_dim
+    qbar = rng.standard_normal(D)
+    K = rng.standard_normal((length, D))
+    V = rng.standard_normal((length, D))
+    ns = cfg.salient_count(length)
+    sal = np.sort(rng.choice(np.arange(1, length), size=ns, replace=False)) if ns > 0 else np.zeros(0, np.int64)
+    direction = qbar / np.linalg.norm(qbar)
+    K[sal] = 4.0 * direction
+    K[0] = 8.0 * direction
+    eps = rng.standard_normal((steps, cfg.group, D))
+    q = qbar[None, None, :] + eps
+    k_new = rng.standard_normal((steps, D))
+    v_new = rng.standard_normal((steps, D))
+    return K, V, q, k_new, v_new, sal
+
+
+def make_decode(cfg: DecodeWorkload, units=None, steps: int | None = None) -> DecodeInputs:
+    """Generate the prefill cache and per-step (q, k, v) for the listed units (default: all)."""
+    steps = cfg.steps if steps is None else steps
+    all_units = np.arange(cfg.n_units) if units is None else np.asarray(units, dtype=np.int64)
+    seq_lens = sequence_lengths(cfg)
+    lens = np.array([seq_lens[cfg.unit_coords(int(u))[1]] for u in all_units], dtype=np.int64)
+    W, D, G = cfg.window, cfg.head_dim, cfg.group
+    nw = lens // W
+    NW = int((seq_lens // W).max())
+    Up = len(all_units)
+    k_win = np.zeros((Up, NW, W, D), np.uint16)
+    v_win = np.zeros((Up, NW, W, D), np.uint16)
+    k_t = np.zeros((Up, W, D), np.uint16)
+    v_t = np.zeros((Up, W, D), np.uint16)
+    q = np.zeros((steps, Up, G, D), np.uint16)
+    kn = np.zeros((steps, Up, D), np.uint16)
+    vn = np.zeros((steps, Up, D), np.uint16)
+    sal_list = []
+    for j, u in enumerate(all_units):
+        L = int(lens[j])
+        K, V, qq, k_new, v_new, sal = _unit_decode_draws(cfg, int(u), L, steps)
+        n = int(nw[j]) * W
+        kb = to_storage_bits(K, cfg.dtype)
+        vb = to_storage_bits(V, cfg.dtype)
+        k_win[j, :nw[j]] = kb[:n].reshape(nw[j], W, D)
+        v_win[j, :nw[j]] = vb[:n].reshape(nw[j], W, D)
+        k_t[j, :L - n] = kb[n:]
+        v_t[j, :L - n] = vb[n:]
+        q[:, j] = to_storage_bits(qq, cfg.dtype)
+        kn[:, j] = to_storage_bits(k_new, cfg.dtype)
+        vn[:, j] = to_storage_bits(v_new, cfg.dtype)
+        sal_list.append(sal)
+    return DecodeInputs(cfg=cfg, units=all_units, lengths=lens, n_windows=nw.astype(np.int64),
+                        tail0=(lens - nw * W).astype(np.int64), n_windows_max=NW, k_win=k_win, v_win=v_win,
+                        k_tail0=k_t, v_tail0=v_t, q=q, k_new=kn, v_new=vn, salient=sal_list)
+
+
+# ----------------------------------------------------------------------------------------------------------
+# CriticalKV prefill-selection inputs
+
+
+@dataclass
+class CriticalKVInputs:
+    cfg: CriticalKVWorkload
+    q_obs: np.ndarray   # [Hq][n_obs][D] uint16 (queries at positions n - n_obs + j)
+    k: np.ndarray       # [Hkv][n][D] uint16
+    v: np.ndarray       # [Hkv][n][D] uint16
+    w_o: np.ndarray     # [Hq*D][d_model] uint16, row index = h*D + d (input feature), column = output feature
+    salient: list
+
+
+def make_criticalkv(cfg: CriticalKVWorkload, n_keys: int | None = None, d_model: int | None = None,
+                    n_salient: int | None = None) -> CriticalKVInputs:
+    """Inputs for the observation-window selection. ``n_keys``/``d_model``/``n_salient`` shrink it for tests."""
+    n = cfg.n_keys if n_keys is None else n_keys
+    dm = cfg.d_model if d_model is None else d_model
+    ns = cfg.n_salient if n_salient is None else n_salient
+    D, G, T = cfg.head_dim, cfg.group, cfg.n_obs
+    q = np.zeros((cfg.hq, T, D), np.uint16)
+    k = np.zeros((cfg.hkv, n, D), np.uint16)
+    v = np.zeros((cfg.hkv, n, D), np.uint16)
+    sal_list = []
+    for g in range(cfg.hkv):
+        rng = unit_rng(cfg.seed, g)
+        qbar = rng.standard_normal(D)
+        K = rng.standard_normal((n, D))
+        V = rng.standard_normal((n, D))
+        hi = max(2, n - T - 1)
+        sal = np.sort(rng.choice(np.arange(1, hi), size=min(ns, hi - 1), replace=False))
+        direction = qbar / np.linalg.norm(qbar)
+        K[sal] = 4.0 * direction
+        K[0] = 8.0 * direction
+        eps = rng.standard_normal((G, T, D))
+        q[g * G:(g + 1) * G] = to_storage_bits(qbar[None, None, :] + eps, cfg.dtype)
+        k[g] = to_storage_bits(K, cfg.dtype)
+        v[g] = to_storage_bits(V, cfg.dtype)
+        sal_list.append(sal)
+    rng = unit_rng(cfg.seed, 1 << 20)
+    w = rng.standard_normal((cfg.hq * D, dm)) / 64.0
+    return CriticalKVInputs(cfg=cfg, q_obs=q, k=k, v=v, w_o=to_storage_bits(w, cfg.dtype), salient=sal_list)
+
+
+# ----------------------------------------------------------------------------------------------------------
+# DBTrimKV global-budget inputs
+
+
+def make_retention_beta(cfg: RetentionWorkload, layers: int | None = None, n_tokens: int | None = None):
+    """Per-entry retention beta ~ Beta(a, b), clipped to [2^-24, 1 - 2^-24], float32, shape [L][Hkv][T]."""
+    L = cfg.layers if layers is None else layers
+    T = cfg.n_tokens if n_tokens is None else n_tokens
+    out = np.empty((L, cfg.hkv, T), np.float32)
+    for l in range(L):
+        rng = unit_rng(cfg.seed, l)
+        b = rng.beta(cfg.beta_a, cfg.beta_b, size=(cfg.hkv, T))
+        out[l] = np.clip(b, 2.0 ** -24, 1.0 - 2.0 ** -24).astype(np.float32)
+    return out
+
+
+def make_page_table(cfg: RetentionWorkload, layers: int | None = None, n_tokens: int | None = None):
+    """Source page table [L][Hkv][T/page] int32: a seeded permutation of all page ids."""
+    L = cfg.layers if layers is None else layers
+    T = cfg.n_tokens if n_tokens is None else n_tokens
+    n_pages = L * cfg.hkv * (T // cfg.page)
+    rng = unit_rng(cfg.seed, 1 << 21)
+    return rng.permutation(n_pages).astype(np.int32).reshape(L, cfg.hkv, T // cfg.page)
+
+
+def pool_row_bits(row_ids: np.ndarray, head_dim: int, seed: int, dtype: str = "bf16",
+                  pool_rows: int = 1 << 16) -> np.ndarray:
+    """K/V pool rows for the paged cache: row r (global row id = page*page_size + slot) takes row
+    (r * 40503 + 17) mod pool_rows of a seeded N(0,1) table, so huge pools need only a small table."""
+    table = pool_table_bits(head_dim, seed, dtype, pool_rows)
+    idx = (row_ids.astype(np.int64) * 40503 + 17) % pool_rows
+    return table[idx]
+
+
+_POOL_CACHE: dict = {}
+
+
+def pool_table_bits(head_dim: int, seed: int, dtype: str = "bf16", pool_rows: int = 1 << 16) -> np.ndarray:
+    key = (head_dim, seed, dtype, pool_rows)
+    if key not in _POOL_CACHE:
+        rng = unit_rng(seed, 1 << 22)
+        _POOL_CACHE[key] = to_storage_bits(rng.standard_normal((pool_rows, head_dim)), dtype)
+    return _POOL_CACHE[key]

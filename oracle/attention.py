@@ -1,0 +1,37 @@
+"""Grouped-query decode attention and window mass, written out in fp64.
+
+Source: QEvict page, "Mecanismos Principais": window importance is attention accumulated over time, attention is
+materialised to compute it, and grouped-query attention is supported. Standard scaled dot-product attention:
+s_{h,i} = q_h . k_i / sqrt(D), p_h = softmax_i(s_h), o_h = sum_i p_{h,i} v_i, for the G query heads h that share
+one KV head. Window mass (reading of the GQA aggregation, which the page leaves open): the mean over the G heads
+of the probability that falls in the window, mass_w = (1/G) sum_h sum_{i in w} p_{h,i}.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def gqa_decode(q: np.ndarray, K: np.ndarray, V: np.ndarray):
+    """q [G][D], K [n][D], V [n][D] (fp64) -> (logits [G][n], p [G][n], o [G][D])."""
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    D = q.shape[-1]
+    s = (q @ K.T) / math.sqrt(D)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    p = e / e.sum(axis=1, keepdims=True)
+    o = p @ V
+    return s, p, o
+
+
+def window_mass(p: np.ndarray, key_window: np.ndarray, n_windows: int) -> np.ndarray:
+    """p [G][n], key_window [n] (window id, or -1 for keys outside any window) -> mass [n_windows]."""
+    G = p.shape[0]
+    per_key = p.sum(axis=0) / G
+    mass = np.zeros(n_windows, np.float64)
+    sel = key_window >= 0
+    np.add.at(mass, key_window[sel], per_key[sel])
+    return mass

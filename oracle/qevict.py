@@ -1,0 +1,149 @@
+"""QEvict decode run for one unit (batch, layer, KV head), step by step.
+
+Source: QEvict page —
+  * "Metodologia: QEvict": the history is split into contiguous windows, routed under a fixed memory budget to
+    a full-precision tier, a recoverable INT2 tier that stays attendable, or eviction (lowest-confidence windows
+    only, and permanently);
+  * "Mecanismos Principais": window importance is attention accumulated over time (cumulative score); demotion
+    full -> quantized when importance falls; promotion quantized -> full by dequantisation when the cumulative
+    score rises; the write-once ledger quantises a window only at its first demotion and reuses that low-bit copy
+    for every later promotion and demotion; attention is materialised to update the scores; GQA is supported.
+
+Readings where the page is silent (each is listed with its reason in the design notes):
+  * routing unit = (batch, layer, KV head); per-unit budgets b_full / b_int2 in windows;
+  * cumulative score = plain sum over decode steps of the window mass (mean over the G query heads of the
+    probability in the window), starting at 0 at the first decode step;
+  * order inside a step: append (k_t, v_t) -> attend over the current tiers -> accumulate -> route when
+    t % R == 0 (the new tiers serve from step t+1);
+  * routing ranks the resident windows by (score desc, window asc): ranks [0, b_full) FULL, the next b_int2
+    INT2, the rest EVICTED for good;
+  * the partial last window and every decode-time token form an unrouted tail that is always attended;
+  * a promoted window's full-precision data is RNE_storage(x^) of its ledger copy; its ledger is kept;
+  * keys and values of INT2 windows are attended as x^ = fl32(c*s + z).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from .attention import gqa_decode, window_mass
+from .fp import f32_to_storage_rne, storage_to_f64
+from .int2 import dequantize, quantize
+from .select import EVICTED, FULL, INT2, three_tier
+
+
+@dataclass
+class StepResult:
+    logits: np.ndarray      # [G][n_res] (scaled by 1/sqrt(D))
+    p: np.ndarray           # [G][n_res]
+    o: np.ndarray           # [G][D]
+    mass: np.ndarray        # [n_windows] (0 for non-resident windows)
+    key_window: np.ndarray  # [n_res] window id of each resident key, -1 for tail keys
+    tail_mass: float
+
+
+@dataclass
+class RoutePlan:
+    tier_before: np.ndarray
+    tier_after: np.ndarray
+    quantized: np.ndarray   # windows quantised now (first demotion), ascending
+    promoted: np.ndarray    # INT2 -> FULL, ascending
+    demoted: np.ndarray     # FULL -> INT2 (all, ascending)
+    evicted: np.ndarray     # resident -> EVICTED, ascending
+
+
+class QEvictUnit:
+    def __init__(self, k_win: np.ndarray, v_win: np.ndarray, k_tail: np.ndarray, v_tail: np.ndarray,
+                 dtype: str):
+        """k_win/v_win [n_w][W][D] storage patterns; k_tail/v_tail [t0][D] storage patterns."""
+        self.dtype = dtype
+        self.kw = np.array(k_win, dtype=np.uint16, copy=True)
+        self.vw = np.array(v_win, dtype=np.uint16, copy=True)
+        self.n_windows, self.W, self.D = self.kw.shape
+        self.tail_k = [np.array(r, np.uint16) for r in k_tail]
+        self.tail_v = [np.array(r, np.uint16) for r in v_tail]
+        self.tier = np.full(self.n_windows, FULL, np.int8)
+        self.cum = np.zeros(self.n_windows, np.float64)
+        self.ledger = {}  # w -> dict(kc, ks, kz, vc, vs, vz)
+        self.t = 0
+
+    # -- state views ------------------------------------------------------------------------------------------
+    def resident_windows(self):
+        return np.flatnonzero(self.tier == FULL), np.flatnonzero(self.tier == INT2)
+
+    def window_values(self, w: int):
+        """Attended (K, V) of window w in fp64 under its current tier."""
+        if self.tier[w] == FULL:
+            return storage_to_f64(self.kw[w], self.dtype), storage_to_f64(self.vw[w], self.dtype)
+        if self.tier[w] == INT2:
+            e = self.ledger[w]
+            return (dequantize(e["kc"], e["ks"], e["kz"]).astype(np.float64),
+                    dequantize(e["vc"], e["vs"], e["vz"]).astype(np.float64))
+        raise ValueError("evicted window has no values")
+
+    def assemble(self):
+        """Resident keys in attention order: FULL windows ascending, INT2 windows ascending, then the tail."""
+        full, int2 = self.resident_windows()
+        Ks, Vs, kw = [], [], []
+        for w in list(full) + list(int2):
+            k, v = self.window_values(int(w))
+            Ks.append(k)
+            Vs.append(v)
+            kw.append(np.full(self.W, w, np.int64))
+        if self.tail_k:
+            Ks.append(storage_to_f64(np.stack(self.tail_k), self.dtype))
+            Vs.append(storage_to_f64(np.stack(self.tail_v), self.dtype))
+            kw.append(np.full(len(self.tail_k), -1, np.int64))
+        return np.concatenate(Ks), np.concatenate(Vs), np.concatenate(kw)
+
+    # -- one decode step -------------------------------------------------------------------------------------
+    def step(self, q_bits: np.ndarray, k_new=None, v_new=None) -> StepResult:
+        if k_new is not None:
+            self.tail_k.append(np.array(k_new, np.uint16))
+            self.tail_v.append(np.array(v_new, np.uint16))
+        K, V, kw = self.assemble()
+        q = storage_to_f64(q_bits, self.dtype)
+        s, p, o = gqa_decode(q, K, V)
+        mass = window_mass(p, kw, self.n_windows)
+        self.cum += mass
+        self.t += 1
+        tail_mass = float(p[:, kw < 0].sum() / p.shape[0])
+        return StepResult(logits=s, p=p, o=o, mass=mass, key_window=kw, tail_mass=tail_mass)
+
+    # -- routing event ---------------------------------------------------------------------------------------
+    def _quantize_window(self, w: int):
+        kc, ks, kz = quantize(self.kw[w], self.dtype)
+        vc, vs, vz = quantize(self.vw[w], self.dtype)
+        self.ledger[w] = dict(kc=kc, ks=ks, kz=kz, vc=vc, vs=vs, vz=vz)
+
+    def route(self, b_full: int, b_int2: int, scores=None) -> RoutePlan:
+        """Re-tier the resident windows. ``scores`` replaces the oracle's own cumulative scores (used to feed
+        the router the GPU's fp32 scores, so that selections can be compared bit for bit)."""
+        sc = self.cum if scores is None else np.asarray(scores, dtype=np.float64)
+        before = self.tier.copy()
+        after = three_tier(sc, before, b_full, b_int2)
+        demoted = np.flatnonzero((before == FULL) & (after == INT2))
+        promoted = np.flatnonzero((before == INT2) & (after == FULL))
+        evicted = np.flatnonzero((before != EVICTED) & (after == EVICTED))
+        quantized = np.array([w for w in demoted if int(w) not in self.ledger], dtype=np.int64)
+        for w in quantized:
+            self._quantize_window(int(w))
+        for w in promoted:
+            e = self.ledger[int(w)]
+            self.kw[w] = f32_to_storage_rne(dequantize(e["kc"], e["ks"], e["kz"]), self.dtype)
+            self.vw[w] = f32_to_storage_rne(dequantize(e["vc"], e["vs"], e["vz"]), self.dtype)
+        for w in evicted:
+            self.ledger.pop(int(w), None)
+        self.tier = after
+        return RoutePlan(tier_before=before, tier_after=after, quantized=quantized, promoted=promoted,
+                         demoted=demoted, evicted=evicted)
+
+
+def full_cache_attention(k_win: np.ndarray, v_win: np.ndarray, k_tail: np.ndarray, v_tail: np.ndarray,
+                         q_bits: np.ndarray, dtype: str):
+    """Plain attention over the whole uncompressed cache (windows in position order, then the tail)."""
+    D = k_win.shape[-1]
+    K = np.concatenate([storage_to_f64(k_win.reshape(-1, D), dtype), storage_to_f64(k_tail.reshape(-1, D), dtype)])
+    V = np.concatenate([storage_to_f64(v_win.reshape(-1, D), dtype), storage_to_f64(v_tail.reshape(-1, D), dtype)])
+    return gqa_decode(storage_to_f64(q_bits, dtype), K, V)
