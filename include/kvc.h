@@ -1,0 +1,219 @@
+/* kvc.h — C ABI of the compressed-KV GQA decode library for AMD MI355X (gfx950).
+ *
+ * One decode step of grouped-query attention over a window-routed, partly INT2-quantised KV cache, as the
+ * QEvict page ("Resumo Técnico: QEvict") describes it: contiguous windows, cumulative attention scores,
+ * three tiers (full precision / recoverable INT2 / evicted) under a fixed budget, and a write-once quantisation
+ * ledger reused by every later promotion and demotion.
+ *
+ * Conventions for every entry point
+ *   - Returns 0 (KVC_OK) or a negative kvc_status. Nothing aborts, nothing throws across the ABI.
+ *   - Arguments are validated on the host before any GPU work; an invalid call returns synchronously and
+ *     launches nothing.
+ *   - All pointers are DEVICE pointers unless a field says "host". The caller allocates and owns every buffer,
+ *     workspaces included (sizes from the *_workspace queries). The library allocates no device memory, keeps
+ *     no pointer after a call returns and has no global state; buffers must stay valid until the stream has
+ *     executed the work.
+ *   - Work is enqueued on the given stream (0 = the default stream); nothing synchronises and nothing is
+ *     copied device->host, so sequences of calls can be captured in a HIP graph.
+ *   - Results are bitwise reproducible run to run (no floating-point atomics; fixed combine order).
+ *   - Errors found by a kernel (a write-once violation, counts above the host bounds, NaN scores) are OR-ed
+ *     into kvc_cache.status as KVC_DEV_* bits; read it with kvc_read_device_status().
+ */
+#ifndef KVC_H_
+#define KVC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVC_ABI_VERSION 1
+
+typedef enum {
+  KVC_OK = 0,
+  KVC_E_INVALID = -1,      /* null pointer, bad size, misaligned buffer, inconsistent arguments */
+  KVC_E_UNSUPPORTED = -2,  /* head_dim != 128, window != 32, group not in {1,2,4,8}, unknown dtype or mode */
+  KVC_E_WORKSPACE = -3,    /* workspace missing or smaller than the *_workspace query says */
+  KVC_E_LEDGER = -4,       /* write-once ledger violation (reported on the host path) */
+  KVC_E_BUDGET = -5,       /* a budget or bound is negative or larger than the capacity */
+  KVC_E_HIP = -6           /* a HIP launch failed */
+} kvc_status;
+
+/* Bits OR-ed into *kvc_cache.status by kernels. */
+#define KVC_DEV_LEDGER_REWRITE 0x1  /* quantise asked for a window whose ledger copy already exists: skipped */
+#define KVC_DEV_BOUND_EXCEEDED 0x2  /* a device count exceeded the host bound given for the launch */
+#define KVC_DEV_NAN_SCORE 0x4       /* a routing score was NaN; that unit was not re-routed */
+
+typedef enum { KVC_F16 = 0, KVC_BF16 = 1 } kvc_dtype;
+typedef enum { KVC_TIER_FULL = 0, KVC_TIER_INT2 = 1, KVC_TIER_EVICTED = 2 } kvc_tier;
+
+/* The compressed cache of U independent units. A unit is one (batch, layer, KV head); its G query heads share
+ * it (grouped-query attention, QEvict page, "Mecanismos Principais"). Window w of a unit holds prefill
+ * positions [w*W, (w+1)*W) (QEvict page, "Metodologia": contiguous windows). Storage is indexed by window
+ * position, so promotion and demotion never move another window's data:
+ *
+ *   k_win, v_win   [U][NW][W][D]   K/V storage dtype. The full-precision copy of window w. Valid while w is
+ *                                  FULL; rewritten with the dequantised ledger copy when w is promoted.
+ *   k_codes,v_codes[U][NW][W][D/4] INT2 ledger codes: element 4b+j of a token row in bits 2j..2j+1 of byte b.
+ *   k_meta, v_meta [U][NW][W][D/32] one 32-bit word per (token, 32-element group): fp16 scale in bits 0..15,
+ *                                  fp16 zero in bits 16..31. Dequantised value x = fmaf(code, scale, zero).
+ *   k_tail, v_tail [U][TM][D]      unrouted tail: the partial last prefill window plus every decode-time token,
+ *                                  always attended, outside the budgets.
+ *   tail_len       [U] int32       valid tail rows (advanced by kvc_decode_attn when it appends a token).
+ *   n_windows      [U] int32       routable windows of the unit (<= NW).
+ *   tier           [U][NW] int8    kvc_tier of every window (entries >= n_windows unused).
+ *   ledgered       [U][NW] uint8   1 once the window's INT2 copy exists (write-once); cleared at eviction.
+ *   cum            [U][NW] float   cumulative window score (sum over steps of the window's attention mass).
+ *   res_list       [U][NW] int32   resident windows: the n_full FULL ids ascending, then the n_int2 INT2 ids
+ *                                  ascending.
+ *   n_full, n_int2 [U] int32       lengths of the two parts of res_list.
+ *   status         [1] int32       device error bits (KVC_DEV_*).
+ *
+ * All K/V rows must be 16-byte aligned (every base pointer 256-byte aligned is sufficient). */
+typedef struct kvc_cache {
+  int32_t n_units;       /* U >= 1 */
+  int32_t group;         /* G query heads per KV head: 1, 2, 4 or 8 */
+  int32_t head_dim;      /* D, must be 128 */
+  int32_t window;        /* W, must be 32 */
+  int32_t n_windows_max; /* NW >= 1 */
+  int32_t tail_max;      /* TM >= 1 */
+  int32_t kv_dtype;      /* kvc_dtype */
+  int32_t reserved;      /* must be 0 */
+  const int32_t* n_windows;
+  void* k_win;
+  void* v_win;
+  uint8_t* k_codes;
+  uint8_t* v_codes;
+  uint32_t* k_meta;
+  uint32_t* v_meta;
+  void* k_tail;
+  void* v_tail;
+  int32_t* tail_len;
+  int8_t* tier;
+  uint8_t* ledgered;
+  float* cum;
+  int32_t* res_list;
+  int32_t* n_full;
+  int32_t* n_int2;
+  int32_t* status;
+} kvc_cache;
+
+/* One decode step (QEvict page, "Mecanismos Principais": attention is materialised to update the cumulative
+ * window scores; GQA supported). Per unit, the resident key set R is: the FULL windows (ascending), the INT2
+ * windows (ascending, dequantised in registers), the tail, and — when k_new is given — the new token appended at
+ * tail position tail_len. For each query head h of the unit:
+ *   s_{h,i} = q_h . k_i / sqrt(D)   p_{h,i} = softmax over R   o_h = sum_i p_{h,i} v_i      (fp32 accumulate)
+ *   mass_w  = (1/G) sum_h sum_{i in w} p_{h,i}   for every resident window w;  cum_w += mass_w (if asked).
+ *
+ *   q        [U][G][D]   storage dtype.
+ *   k_new    [U][D]      storage dtype, or NULL (no append). Appended to the tail by this call; tail_len
+ *            is incremented at the end of the step. Requires tail_len < tail_max on every unit.
+ *   v_new    [U][D]      with k_new.
+ *   out      [U][G][D]   float, or NULL (score-only step).
+ *   probs    [U][G][probs_stride] float or NULL: per-key probabilities in resident order (FULL keys, INT2 keys,
+ *            tail keys, new key). probs_stride >= max over units of W*(n_full+n_int2) + tail_len + (k_new?1:0).
+ *   mass     [U][NW] float or NULL: this step's window mass (0 for windows that are not resident).
+ *   accumulate_cum  0 or 1.
+ *   max_full, max_int2, max_tail   HOST upper bounds over units of n_full, n_int2 and tail_len (before the
+ *            append). They size the grid; a unit whose device count exceeds them sets KVC_DEV_BOUND_EXCEEDED and
+ *            its step is undefined.
+ * Workspace: kvc_decode_attn_workspace() bytes, any contents, 256-byte aligned. */
+typedef struct kvc_decode_args {
+  const void* q;
+  const void* k_new;
+  const void* v_new;
+  float* out;
+  float* probs;
+  float* mass;
+  int32_t probs_stride;
+  int32_t accumulate_cum;
+  int32_t max_full;
+  int32_t max_int2;
+  int32_t max_tail;
+  int32_t reserved;
+} kvc_decode_args;
+
+/* Three-tier routing (QEvict page, "Metodologia: QEvict" and "Mecanismos Principais"). Per unit, the resident
+ * windows (tier != EVICTED) are ranked by (score desc, window index asc); ranks [0, budget_full) become FULL,
+ * the next budget_int2 become INT2, the rest EVICTED — permanently (evicted windows are never ranked again).
+ * Outputs, per unit:
+ *   tier, res_list, n_full, n_int2 of the cache are rewritten; ledgered is cleared for evicted windows;
+ *   quant_list[u][0..n_quant[u])  windows going FULL -> INT2 with no ledger copy yet (ascending): pass to
+ *                                 kvc_quantize_int2 (their first demotion, the only time they are quantised);
+ *   promo_list[u][0..n_promo[u])  windows going INT2 -> FULL (ascending): pass to kvc_promote.
+ *   A FULL -> INT2 move of a window that already has a ledger copy is a pure index remap.
+ *   scores         [U][NW] float, or NULL to rank by cache.cum. Must be finite (NaN: KVC_DEV_NAN_SCORE, the
+ *                  unit keeps its tiers).
+ *   budget_full, budget_int2   [U] int32 device arrays (>= 0).
+ *   quant_list, promo_list     [U][NW] int32;  n_quant, n_promo  [U] int32. */
+typedef struct kvc_tier_route_args {
+  const kvc_cache* cache;
+  const float* scores;
+  const int32_t* budget_full;
+  const int32_t* budget_int2;
+  int32_t* quant_list;
+  int32_t* n_quant;
+  int32_t* promo_list;
+  int32_t* n_promo;
+} kvc_tier_route_args;
+
+/* Modes of kvc_score / kvc_route. */
+#define KVC_SCORE_WINDOWS 0  /* args: const kvc_window_score_args* */
+#define KVC_ROUTE_TIERS 0    /* args: const kvc_tier_route_args*   */
+
+/* kvc_score(KVC_SCORE_WINDOWS): the scoring half of a decode step — the same kernels as kvc_decode_attn with
+ * out = NULL: probabilities, window mass and the cumulative score update over the mixed cache. */
+typedef struct kvc_window_score_args {
+  const kvc_cache* cache;
+  const kvc_decode_args* step; /* step->out is ignored */
+} kvc_window_score_args;
+
+int kvc_abi_version(void);
+const char* kvc_status_str(int status);
+
+/* Bytes of workspace kvc_decode_attn needs for these bounds (0 on invalid arguments). */
+size_t kvc_decode_attn_workspace(const kvc_cache* cache, const kvc_decode_args* step);
+
+int kvc_decode_attn(const kvc_cache* cache, const kvc_decode_args* step, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+/* Workspace for kvc_score in the given mode (KVC_SCORE_WINDOWS: same as kvc_decode_attn). */
+size_t kvc_score_workspace(int32_t mode, const void* args);
+int kvc_score(int32_t mode, const void* args, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Routing in the given mode; KVC_ROUTE_TIERS needs no workspace (pass NULL, 0). */
+size_t kvc_route_workspace(int32_t mode, const void* args);
+int kvc_route(int32_t mode, const void* args, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Write-once INT2 quantisation (QEvict page, "Mecanismos Principais", write-once quantization ledger): for
+ * every listed window, K and V are quantised from their current full-precision copy into the ledger and the
+ * window is marked ledgered. A listed window that is already ledgered is skipped and KVC_DEV_LEDGER_REWRITE is
+ * set: the ledger is never rewritten.
+ *   list [U][list_stride] int32 window ids; count [U] int32 entries per unit; max_total = HOST bound of
+ *   sum(count) (sizes the launch; 0 launches nothing).
+ * Quantiser, per token and per 32-element group (INT2 is the width the page names; the rest is this library's
+ * format): lo/hi = min/max (fp32); zero z = largest fp16 <= lo; scale s = smallest fp16 >=
+ * fl32(fl32(hi - z) / 3), or 0 if hi == z; code = #{k in 0..2 : fl32(x - z) >= (k + 0.5) * s} (0 if s == 0).
+ * Precondition: |x| < 65504. */
+int kvc_quantize_int2(const kvc_cache* cache, const int32_t* list, const int32_t* count, int32_t list_stride,
+                      int64_t max_total, hipStream_t stream);
+
+/* Promotion (QEvict page, "Mecanismos Principais": a quantized window whose cumulative score rises is
+ * dequantised and promoted back to full precision): for every listed window, k_win/v_win are rewritten with
+ * round-to-nearest-even(fmaf(code, scale, zero)) in the storage dtype. The ledger copy is kept. Same list
+ * conventions as kvc_quantize_int2. */
+int kvc_promote(const kvc_cache* cache, const int32_t* list, const int32_t* count, int32_t list_stride,
+                int64_t max_total, hipStream_t stream);
+
+/* Reads *cache->status into *host_status (synchronises the stream) and, if clear != 0, zeroes it. */
+int kvc_read_device_status(const kvc_cache* cache, int32_t* host_status, int32_t clear, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H_ */

@@ -1,0 +1,107 @@
+"""ctypes binding of the C ABI in include/kvc.h (argument marshalling only; all work runs in the HIP library).
+
+The library is loaded from ``kv_cache_compression_gqa_amd/lib/libkvc.so`` (built in-tree by
+``kv_cache_compression_gqa_amd.build``). If it is missing, every call raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libkvc.so")
+_lib = None
+
+KVC_OK, KVC_E_INVALID, KVC_E_UNSUPPORTED, KVC_E_WORKSPACE, KVC_E_LEDGER, KVC_E_BUDGET, KVC_E_HIP = \
+    0, -1, -2, -3, -4, -5, -6
+KVC_DEV_LEDGER_REWRITE, KVC_DEV_BOUND_EXCEEDED, KVC_DEV_NAN_SCORE = 0x1, 0x2, 0x4
+KVC_F16, KVC_BF16 = 0, 1
+TIER_FULL, TIER_INT2, TIER_EVICTED = 0, 1, 2
+KVC_SCORE_WINDOWS = 0
+KVC_ROUTE_TIERS = 0
+
+P = C.c_void_p
+
+
+class KvcError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        msg = lib().kvc_status_str(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{what}: kvc status {status} ({msg})")
+
+
+class KvcCache(C.Structure):
+    _fields_ = [("n_units", C.c_int32), ("group", C.c_int32), ("head_dim", C.c_int32), ("window", C.c_int32),
+                ("n_windows_max", C.c_int32), ("tail_max", C.c_int32), ("kv_dtype", C.c_int32),
+                ("reserved", C.c_int32),
+                ("n_windows", P), ("k_win", P), ("v_win", P), ("k_codes", P), ("v_codes", P), ("k_meta", P),
+                ("v_meta", P), ("k_tail", P), ("v_tail", P), ("tail_len", P), ("tier", P), ("ledgered", P),
+                ("cum", P), ("res_list", P), ("n_full", P), ("n_int2", P), ("status", P)]
+
+
+class KvcDecodeArgs(C.Structure):
+    _fields_ = [("q", P), ("k_new", P), ("v_new", P), ("out", P), ("probs", P), ("mass", P),
+                ("probs_stride", C.c_int32), ("accumulate_cum", C.c_int32), ("max_full", C.c_int32),
+                ("max_int2", C.c_int32), ("max_tail", C.c_int32), ("reserved", C.c_int32)]
+
+
+class KvcTierRouteArgs(C.Structure):
+    _fields_ = [("cache", C.POINTER(KvcCache)), ("scores", P), ("budget_full", P), ("budget_int2", P),
+                ("quant_list", P), ("n_quant", P), ("promo_list", P), ("n_promo", P)]
+
+
+class KvcWindowScoreArgs(C.Structure):
+    _fields_ = [("cache", C.POINTER(KvcCache)), ("step", C.POINTER(KvcDecodeArgs))]
+
+
+# name -> (restype, argtypes); every symbol include/kvc.h declares
+SIGNATURES = {
+    "kvc_abi_version": (C.c_int, []),
+    "kvc_status_str": (C.c_char_p, [C.c_int]),
+    "kvc_decode_attn_workspace": (C.c_size_t, [C.POINTER(KvcCache), C.POINTER(KvcDecodeArgs)]),
+    "kvc_decode_attn": (C.c_int, [C.POINTER(KvcCache), C.POINTER(KvcDecodeArgs), P, C.c_size_t, P]),
+    "kvc_score_workspace": (C.c_size_t, [C.c_int32, P]),
+    "kvc_score": (C.c_int, [C.c_int32, P, P, C.c_size_t, P]),
+    "kvc_route_workspace": (C.c_size_t, [C.c_int32, P]),
+    "kvc_route": (C.c_int, [C.c_int32, P, P, C.c_size_t, P]),
+    "kvc_quantize_int2": (C.c_int, [C.POINTER(KvcCache), P, P, C.c_int32, C.c_int64, P]),
+    "kvc_promote": (C.c_int, [C.POINTER(KvcCache), P, P, C.c_int32, C.c_int64, P]),
+    "kvc_read_device_status": (C.c_int, [C.POINTER(KvcCache), C.POINTER(C.c_int32), C.c_int32, P]),
+}
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load (once) and return the HIP library. Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {_LIB_PATH} is missing "
+                               "(run `python -m kv_cache_compression_gqa_amd.build`)")
+        L = C.CDLL(_LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        if L.kvc_abi_version() != 1:
+            raise RuntimeError("kvc ABI version mismatch")
+        _lib = L
+    return _lib
+
+
+def check(status: int, what: str):
+    if status != KVC_OK:
+        raise KvcError(status, what)
+
+
+def ptr(t) -> int | None:
+    """Device pointer of a torch tensor (or None)."""
+    return None if t is None else t.data_ptr()
+
+
+def stream_handle(stream=None) -> int:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream

@@ -1,0 +1,170 @@
+// C-ABI entry points: host-side validation, workspace sizing, dispatch. No device memory is allocated here and
+// no state is kept between calls.
+#include <stdint.h>
+
+#include "kvc_internal.h"
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_cache(const kvc_cache* c) {
+  if (c == nullptr) return KVC_E_INVALID;
+  if (c->head_dim != kvc::kD || c->window != kvc::kW) return KVC_E_UNSUPPORTED;
+  if (!(c->group == 1 || c->group == 2 || c->group == 4 || c->group == 8)) return KVC_E_UNSUPPORTED;
+  if (c->kv_dtype != KVC_F16 && c->kv_dtype != KVC_BF16) return KVC_E_UNSUPPORTED;
+  if (c->n_units < 1 || c->n_units > 16384 || c->n_windows_max < 1 || c->n_windows_max > 16384 ||
+      c->tail_max < 1 || c->reserved != 0) {
+    return KVC_E_INVALID;
+  }
+  const void* need16[] = {c->k_win, c->v_win, c->k_tail, c->v_tail, c->k_codes, c->v_codes, c->k_meta, c->v_meta};
+  for (const void* p : need16) {
+    if (p == nullptr || !aligned(p, 16)) return KVC_E_INVALID;
+  }
+  const void* need4[] = {c->n_windows, c->tail_len, c->cum, c->res_list, c->n_full, c->n_int2, c->status};
+  for (const void* p : need4) {
+    if (p == nullptr || !aligned(p, 4)) return KVC_E_INVALID;
+  }
+  if (c->tier == nullptr || c->ledgered == nullptr) return KVC_E_INVALID;
+  return KVC_OK;
+}
+
+int check_decode(const kvc_cache* c, const kvc_decode_args* a, bool need_out) {
+  int st = check_cache(c);
+  if (st != KVC_OK) return st;
+  if (a == nullptr || a->q == nullptr || !aligned(a->q, 16) || a->reserved != 0) return KVC_E_INVALID;
+  if ((a->k_new == nullptr) != (a->v_new == nullptr)) return KVC_E_INVALID;
+  if (a->k_new != nullptr && (!aligned(a->k_new, 16) || !aligned(a->v_new, 16))) return KVC_E_INVALID;
+  if (need_out && a->out == nullptr) return KVC_E_INVALID;
+  if (a->accumulate_cum != 0 && a->accumulate_cum != 1) return KVC_E_INVALID;
+  const int has_new = a->k_new != nullptr ? 1 : 0;
+  if (a->max_full < 0 || a->max_int2 < 0 || a->max_tail < 0) return KVC_E_BUDGET;
+  if (int64_t(a->max_full) + a->max_int2 > c->n_windows_max) return KVC_E_BUDGET;
+  if (int64_t(a->max_tail) + has_new > c->tail_max) return KVC_E_BUDGET;
+  if (int64_t(a->max_full) + a->max_int2 + a->max_tail + has_new == 0) return KVC_E_INVALID;
+  if (a->probs != nullptr) {
+    const int64_t need = int64_t(kvc::kW) * (a->max_full + a->max_int2) + a->max_tail + has_new;
+    if (a->probs_stride < need) return KVC_E_INVALID;
+  }
+  return KVC_OK;
+}
+
+int run_decode(const kvc_cache* c, const kvc_decode_args* a, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (ws == nullptr || !aligned(ws, 256) || ws_bytes < kvc::decode_workspace_bytes(*c, *a)) return KVC_E_WORKSPACE;
+  return kvc::launch_decode(*c, *a, ws, s) == hipSuccess ? KVC_OK : KVC_E_HIP;
+}
+
+int check_list(const kvc_cache* c, const int32_t* list, const int32_t* count, int32_t stride, int64_t max_total) {
+  int st = check_cache(c);
+  if (st != KVC_OK) return st;
+  if (max_total < 0) return KVC_E_BUDGET;
+  if (max_total == 0) return KVC_OK;
+  if (list == nullptr || count == nullptr || !aligned(list, 4) || !aligned(count, 4)) return KVC_E_INVALID;
+  if (stride < 1) return KVC_E_INVALID;
+  if (max_total > int64_t(c->n_units) * c->n_windows_max) return KVC_E_BUDGET;
+  return KVC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvc_abi_version(void) { return KVC_ABI_VERSION; }
+
+const char* kvc_status_str(int status) {
+  switch (status) {
+    case KVC_OK: return "ok";
+    case KVC_E_INVALID: return "invalid argument";
+    case KVC_E_UNSUPPORTED: return "unsupported shape, dtype or mode";
+    case KVC_E_WORKSPACE: return "workspace missing, misaligned or too small";
+    case KVC_E_LEDGER: return "write-once ledger violation";
+    case KVC_E_BUDGET: return "budget or bound out of range";
+    case KVC_E_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t kvc_decode_attn_workspace(const kvc_cache* cache, const kvc_decode_args* step) {
+  if (check_decode(cache, step, false) != KVC_OK) return 0;
+  return kvc::decode_workspace_bytes(*cache, *step);
+}
+
+int kvc_decode_attn(const kvc_cache* cache, const kvc_decode_args* step, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  const int st = check_decode(cache, step, true);
+  if (st != KVC_OK) return st;
+  return run_decode(cache, step, workspace, workspace_bytes, stream);
+}
+
+size_t kvc_score_workspace(int32_t mode, const void* args) {
+  if (args == nullptr) return 0;
+  if (mode == KVC_SCORE_WINDOWS) {
+    const kvc_window_score_args* a = static_cast<const kvc_window_score_args*>(args);
+    return kvc_decode_attn_workspace(a->cache, a->step);
+  }
+  return 0;
+}
+
+int kvc_score(int32_t mode, const void* args, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (args == nullptr) return KVC_E_INVALID;
+  if (mode == KVC_SCORE_WINDOWS) {
+    const kvc_window_score_args* a = static_cast<const kvc_window_score_args*>(args);
+    const int st = check_decode(a->cache, a->step, false);
+    if (st != KVC_OK) return st;
+    kvc_decode_args step = *a->step;
+    step.out = nullptr;
+    return run_decode(a->cache, &step, workspace, workspace_bytes, stream);
+  }
+  return KVC_E_UNSUPPORTED;
+}
+
+size_t kvc_route_workspace(int32_t mode, const void* args) {
+  (void)args;
+  (void)mode;
+  return 0;
+}
+
+int kvc_route(int32_t mode, const void* args, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (args == nullptr) return KVC_E_INVALID;
+  if (mode == KVC_ROUTE_TIERS) {
+    const kvc_tier_route_args* a = static_cast<const kvc_tier_route_args*>(args);
+    const int st = check_cache(a->cache);
+    if (st != KVC_OK) return st;
+    const void* ptrs[] = {a->budget_full, a->budget_int2, a->quant_list, a->n_quant, a->promo_list, a->n_promo};
+    for (const void* p : ptrs) {
+      if (p == nullptr || !aligned(p, 4)) return KVC_E_INVALID;
+    }
+    if (a->scores != nullptr && !aligned(a->scores, 4)) return KVC_E_INVALID;
+    return kvc::launch_route_tiers(*a, stream) == hipSuccess ? KVC_OK : KVC_E_HIP;
+  }
+  return KVC_E_UNSUPPORTED;
+}
+
+int kvc_quantize_int2(const kvc_cache* cache, const int32_t* list, const int32_t* count, int32_t list_stride,
+                      int64_t max_total, hipStream_t stream) {
+  const int st = check_list(cache, list, count, list_stride, max_total);
+  if (st != KVC_OK) return st;
+  return kvc::launch_quantize(*cache, list, count, list_stride, max_total, stream) == hipSuccess ? KVC_OK
+                                                                                                 : KVC_E_HIP;
+}
+
+int kvc_promote(const kvc_cache* cache, const int32_t* list, const int32_t* count, int32_t list_stride,
+                int64_t max_total, hipStream_t stream) {
+  const int st = check_list(cache, list, count, list_stride, max_total);
+  if (st != KVC_OK) return st;
+  return kvc::launch_promote(*cache, list, count, list_stride, max_total, stream) == hipSuccess ? KVC_OK
+                                                                                                : KVC_E_HIP;
+}
+
+int kvc_read_device_status(const kvc_cache* cache, int32_t* host_status, int32_t clear, hipStream_t stream) {
+  if (cache == nullptr || cache->status == nullptr || host_status == nullptr) return KVC_E_INVALID;
+  if (hipMemcpyAsync(host_status, cache->status, sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess) {
+    return KVC_E_HIP;
+  }
+  if (clear != 0 && hipMemsetAsync(cache->status, 0, sizeof(int32_t), stream) != hipSuccess) return KVC_E_HIP;
+  return hipStreamSynchronize(stream) == hipSuccess ? KVC_OK : KVC_E_HIP;
+}
+
+}  // extern "C"

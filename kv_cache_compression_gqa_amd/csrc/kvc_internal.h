@@ -1,0 +1,95 @@
+// Internal helpers shared by the gfx950 kernels and the C-ABI layer of the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include "kvc.h"
+
+namespace kvc {
+
+constexpr int kD = 128;           // head_dim
+constexpr int kW = 32;            // window length in tokens
+constexpr int kGroupElems = 32;   // INT2 group: 32 contiguous head_dim elements of one token
+constexpr int kGroups = kD / kGroupElems;
+constexpr int kCodeBytes = kD / 4;  // packed INT2 codes per token row
+constexpr int kWave = 64;
+
+// ---- storage conversions (16-bit patterns) ----------------------------------------------------------------
+struct BF16 {
+  static __device__ __forceinline__ float lo(uint32_t x) { return __uint_as_float(x << 16); }
+  static __device__ __forceinline__ float hi(uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); }
+  static __device__ __forceinline__ float one(uint16_t x) { return __uint_as_float(uint32_t(x) << 16); }
+  // round to nearest even (finite inputs)
+  static __device__ __forceinline__ uint16_t from_float(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return uint16_t(u >> 16);
+  }
+};
+
+struct F16 {
+  static __device__ __forceinline__ float lo(uint32_t x) { return __half2float(__ushort_as_half(uint16_t(x))); }
+  static __device__ __forceinline__ float hi(uint32_t x) {
+    return __half2float(__ushort_as_half(uint16_t(x >> 16)));
+  }
+  static __device__ __forceinline__ float one(uint16_t x) { return __half2float(__ushort_as_half(x)); }
+  static __device__ __forceinline__ uint16_t from_float(float f) { return __half_as_ushort(__float2half_rn(f)); }
+};
+
+// 8 consecutive storage elements (16 bytes) -> 8 floats
+template <class T>
+__device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
+  f[0] = T::lo(v.x); f[1] = T::hi(v.x);
+  f[2] = T::lo(v.y); f[3] = T::hi(v.y);
+  f[4] = T::lo(v.z); f[5] = T::hi(v.z);
+  f[6] = T::lo(v.w); f[7] = T::hi(v.w);
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) { return __half2float(__ushort_as_half(uint16_t(h))); }
+
+// ---- wave reductions --------------------------------------------------------------------------------------
+__device__ __forceinline__ float xor_sum(float v, int mask) { return v + __shfl_xor(v, mask, kWave); }
+__device__ __forceinline__ float xor_max(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, kWave)); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = xor_max(v, m);
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = xor_sum(v, m);
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// exp(a - b) with exp(-inf - x) = 0 and no NaN when both are -inf
+__device__ __forceinline__ float exp_diff(float a, float b) { return a == -INFINITY ? 0.0f : __expf(a - b); }
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---- launchers (host) -------------------------------------------------------------------------------------
+struct DecodeGrid {
+  int chunks_full;  // chunks of full-precision windows per unit
+  int chunks_int2;  // chunks of INT2 windows per unit
+  int chunks_tail;  // chunks of tail tokens per unit
+  int chunks() const { return chunks_full + chunks_int2 + chunks_tail; }
+};
+
+DecodeGrid decode_grid(const kvc_decode_args& a);
+size_t decode_workspace_bytes(const kvc_cache& c, const kvc_decode_args& a);
+hipError_t launch_decode(const kvc_cache& c, const kvc_decode_args& a, void* ws, hipStream_t s);
+hipError_t launch_route_tiers(const kvc_tier_route_args& a, hipStream_t s);
+hipError_t launch_quantize(const kvc_cache& c, const int32_t* list, const int32_t* count, int32_t stride,
+                           int64_t max_total, hipStream_t s);
+hipError_t launch_promote(const kvc_cache& c, const int32_t* list, const int32_t* count, int32_t stride,
+                          int64_t max_total, hipStream_t s);
+
+}  // namespace kvc

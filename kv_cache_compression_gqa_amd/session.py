@@ -1,0 +1,177 @@
+"""Device-side state of a windowed three-tier decode run and the step/route loop that drives the C ABI.
+
+PyTorch only provides device memory and the stream; every step of the path runs in the HIP library.
+
+A ``DecodeSession`` owns the cache tensors of U units and does, per decode step t (1-based):
+    kvc_decode_attn   append (k_t, v_t) to the tail, attend over FULL + INT2 + tail, add the window mass to cum;
+    every ``route_every`` steps:
+    kvc_route         re-tier the resident windows by cumulative score under the per-unit budgets;
+    kvc_quantize_int2 quantise the windows demoted for the first time (write-once ledger);
+    kvc_promote       dequantise the windows promoted back to full precision.
+The host never reads device state inside a step: the launch bounds it passes (how many FULL / INT2 windows and
+tail rows a unit can have) follow from the budgets alone, because routing always fills the tiers in rank order.
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import numpy as np
+import torch
+
+from . import abi
+from .synth import DecodeInputs
+
+
+def _dev(a: np.ndarray, dtype, device):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device=device, dtype=dtype)
+
+
+def _bits(a: np.ndarray, device):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device)
+
+
+class DecodeSession:
+    def __init__(self, inp: DecodeInputs, device="cuda", tail_max: int | None = None, steps: int | None = None,
+                 budgets=None):
+        cfg = inp.cfg
+        self.cfg = cfg
+        self.inp = inp
+        self.device = torch.device(device)
+        U = len(inp.units)
+        NW = inp.n_windows_max
+        W, D, G = cfg.window, cfg.head_dim, cfg.group
+        S = inp.q.shape[0] if steps is None else steps
+        self.U, self.NW, self.G, self.D, self.W = U, NW, G, D, W
+        self.TM = tail_max if tail_max is not None else int(inp.tail0.max()) + S + 1
+        dev = self.device
+        self.k_win = _bits(inp.k_win, dev)
+        self.v_win = _bits(inp.v_win, dev)
+        self.k_codes = torch.zeros((U, NW, W, D // 4), dtype=torch.uint8, device=dev)
+        self.v_codes = torch.zeros_like(self.k_codes)
+        self.k_meta = torch.zeros((U, NW, W, D // 32), dtype=torch.int32, device=dev)
+        self.v_meta = torch.zeros_like(self.k_meta)
+        self.k_tail = torch.zeros((U, self.TM, D), dtype=torch.int16, device=dev)
+        self.v_tail = torch.zeros_like(self.k_tail)
+        t0 = int(inp.tail0.max())
+        if t0 > 0:
+            self.k_tail[:, :t0] = _bits(inp.k_tail0[:, :t0], dev)
+            self.v_tail[:, :t0] = _bits(inp.v_tail0[:, :t0], dev)
+        self.tail_len = _dev(inp.tail0.astype(np.int32), torch.int32, dev)
+        self.n_windows = _dev(inp.n_windows.astype(np.int32), torch.int32, dev)
+        self.tier = torch.zeros((U, NW), dtype=torch.int8, device=dev)
+        self.ledgered = torch.zeros((U, NW), dtype=torch.uint8, device=dev)
+        self.cum = torch.zeros((U, NW), dtype=torch.float32, device=dev)
+        res = np.tile(np.arange(NW, dtype=np.int32), (U, 1))
+        self.res_list = _dev(res, torch.int32, dev)
+        self.n_full = _dev(inp.n_windows.astype(np.int32), torch.int32, dev)
+        self.n_int2 = torch.zeros(U, dtype=torch.int32, device=dev)
+        self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+        # per-step inputs
+        self.q = _bits(inp.q, dev)
+        self.k_new = _bits(inp.k_new, dev)
+        self.v_new = _bits(inp.v_new, dev)
+        self.out = torch.zeros((U, G, D), dtype=torch.float32, device=dev)
+        # budgets
+        if budgets is None:
+            bf = np.array([cfg.budgets(int(n))[0] for n in inp.n_windows], np.int32)
+            bq = np.array([cfg.budgets(int(n))[1] for n in inp.n_windows], np.int32)
+        else:
+            bf, bq = (np.asarray(b, np.int32) for b in budgets)
+        self.bf_host, self.bq_host = bf, bq
+        self.budget_full = _dev(bf, torch.int32, dev)
+        self.budget_int2 = _dev(bq, torch.int32, dev)
+        self.quant_list = torch.zeros((U, NW), dtype=torch.int32, device=dev)
+        self.promo_list = torch.zeros((U, NW), dtype=torch.int32, device=dev)
+        self.n_quant = torch.zeros(U, dtype=torch.int32, device=dev)
+        self.n_promo = torch.zeros(U, dtype=torch.int32, device=dev)
+        # host-side bounds (never read back from the device)
+        self.h_full = inp.n_windows.astype(np.int64).copy()
+        self.h_int2 = np.zeros(U, np.int64)
+        self.h_tail = inp.tail0.astype(np.int64).copy()
+        self.t = 0
+        self._cache = abi.KvcCache(
+            n_units=U, group=G, head_dim=D, window=W, n_windows_max=NW, tail_max=self.TM,
+            kv_dtype=abi.KVC_BF16 if cfg.dtype == "bf16" else abi.KVC_F16, reserved=0,
+            n_windows=abi.ptr(self.n_windows), k_win=abi.ptr(self.k_win), v_win=abi.ptr(self.v_win),
+            k_codes=abi.ptr(self.k_codes), v_codes=abi.ptr(self.v_codes), k_meta=abi.ptr(self.k_meta),
+            v_meta=abi.ptr(self.v_meta), k_tail=abi.ptr(self.k_tail), v_tail=abi.ptr(self.v_tail),
+            tail_len=abi.ptr(self.tail_len), tier=abi.ptr(self.tier), ledgered=abi.ptr(self.ledgered),
+            cum=abi.ptr(self.cum), res_list=abi.ptr(self.res_list), n_full=abi.ptr(self.n_full),
+            n_int2=abi.ptr(self.n_int2), status=abi.ptr(self.status))
+        self._ws = None
+        self._ws_bytes = 0
+
+    # -- bounds -----------------------------------------------------------------------------------------------
+    def bounds(self):
+        return int(self.h_full.max()), int(self.h_int2.max()), int(self.h_tail.max())
+
+    def probs_stride(self, append=True):
+        mf, mq, mt = self.bounds()
+        return self.W * (mf + mq) + mt + (1 if append else 0)
+
+    # -- one decode step --------------------------------------------------------------------------------------
+    def decode_args(self, t_index: int, out=None, probs=None, mass=None, append=True, accumulate=True,
+                    score_only=False):
+        mf, mq, mt = self.bounds()
+        a = abi.KvcDecodeArgs(
+            q=abi.ptr(self.q[t_index]),
+            k_new=abi.ptr(self.k_new[t_index]) if append else None,
+            v_new=abi.ptr(self.v_new[t_index]) if append else None,
+            out=None if score_only else abi.ptr(self.out if out is None else out),
+            probs=abi.ptr(probs), mass=abi.ptr(mass),
+            probs_stride=0 if probs is None else int(probs.shape[-1]),
+            accumulate_cum=1 if accumulate else 0, max_full=mf, max_int2=mq, max_tail=mt, reserved=0)
+        return a
+
+    def workspace(self, args: abi.KvcDecodeArgs):
+        L = abi.lib()
+        need = L.kvc_decode_attn_workspace(C.byref(self._cache), C.byref(args))
+        if need == 0:
+            raise abi.KvcError(abi.KVC_E_INVALID, "kvc_decode_attn_workspace")
+        if self._ws is None or self._ws_bytes < need:
+            self._ws = torch.empty(int(need * 1.25) + 4096, dtype=torch.uint8, device=self.device)
+            self._ws_bytes = self._ws.numel()
+        return self._ws
+
+    def step(self, probs=None, mass=None, append=True, route=True, stream=None):
+        """Decode step t+1 using the pre-generated inputs of that step; routes when due."""
+        ti = self.t
+        args = self.decode_args(ti, probs=probs, mass=mass, append=append)
+        ws = self.workspace(args)
+        L = abi.lib()
+        abi.check(L.kvc_decode_attn(C.byref(self._cache), C.byref(args), abi.ptr(ws), self._ws_bytes,
+                                    abi.stream_handle(stream)), "kvc_decode_attn")
+        if append:
+            self.h_tail += 1
+        self.t += 1
+        if route and self.cfg.route_every > 0 and self.t % self.cfg.route_every == 0:
+            self.route(stream=stream)
+        return self.out
+
+    # -- routing event ----------------------------------------------------------------------------------------
+    def route(self, scores=None, stream=None):
+        L = abi.lib()
+        sh = abi.stream_handle(stream)
+        ra = abi.KvcTierRouteArgs(
+            cache=C.pointer(self._cache), scores=abi.ptr(scores), budget_full=abi.ptr(self.budget_full),
+            budget_int2=abi.ptr(self.budget_int2), quant_list=abi.ptr(self.quant_list), n_quant=abi.ptr(self.n_quant),
+            promo_list=abi.ptr(self.promo_list), n_promo=abi.ptr(self.n_promo))
+        abi.check(L.kvc_route(abi.KVC_ROUTE_TIERS, C.byref(ra), None, 0, sh), "kvc_route")
+        # bounds of this event's lists: first demotions <= min(b_int2, FULL before); promotions <= min(b_full,
+        # INT2 before)
+        q_bound = int(np.minimum(self.bq_host, self.h_full).sum())
+        p_bound = int(np.minimum(self.bf_host, self.h_int2).sum())
+        abi.check(L.kvc_quantize_int2(C.byref(self._cache), abi.ptr(self.quant_list), abi.ptr(self.n_quant),
+                                      self.NW, q_bound, sh), "kvc_quantize_int2")
+        abi.check(L.kvc_promote(C.byref(self._cache), abi.ptr(self.promo_list), abi.ptr(self.n_promo), self.NW,
+                                p_bound, sh), "kvc_promote")
+        n_res = self.h_full + self.h_int2
+        new_full = np.minimum(self.bf_host, n_res)
+        new_int2 = np.minimum(self.bq_host, n_res - new_full)
+        self.h_full, self.h_int2 = new_full.astype(np.int64), new_int2.astype(np.int64)
+
+    def device_status(self, clear=True, stream=None) -> int:
+        st = C.c_int32(0)
+        abi.check(abi.lib().kvc_read_device_status(C.byref(self._cache), C.byref(st), 1 if clear else 0,
+                                                   abi.stream_handle(stream)), "kvc_read_device_status")
+        return int(st.value)

@@ -1,0 +1,111 @@
+"""The C-ABI library loads on a machine without a GPU, exports every function include/kvc.h declares, and its
+host-side validation rejects bad arguments before any GPU work (no compute call is made here)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from kv_cache_compression_gqa_amd import abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "kvc.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvc_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    L = abi.lib()
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in abi.SIGNATURES, n
+    assert L.kvc_abi_version() == 1
+
+
+def test_struct_sizes_match_header_layout():
+    # 8 int32 + 17 pointers
+    assert C.sizeof(abi.KvcCache) == 8 * 4 + 17 * 8
+    assert C.sizeof(abi.KvcDecodeArgs) == 6 * 8 + 6 * 4
+    assert C.sizeof(abi.KvcTierRouteArgs) == 8 * 8
+
+
+def test_status_strings():
+    L = abi.lib()
+    for st in range(-6, 1):
+        assert len(L.kvc_status_str(st)) > 0
+
+
+FAKE = 0x10000  # 64 KiB-aligned fake device address; validation fails before anything dereferences it
+
+
+def good_cache(**over):
+    kw = dict(n_units=2, group=4, head_dim=128, window=32, n_windows_max=32, tail_max=64, kv_dtype=abi.KVC_BF16,
+              reserved=0)
+    for f, _ in abi.KvcCache._fields_[8:]:
+        kw[f] = FAKE
+    kw.update(over)
+    return abi.KvcCache(**kw)
+
+
+def good_step(**over):
+    kw = dict(q=FAKE, k_new=FAKE, v_new=FAKE, out=FAKE, probs=None, mass=None, probs_stride=0, accumulate_cum=1,
+              max_full=8, max_int2=8, max_tail=10, reserved=0)
+    kw.update(over)
+    return abi.KvcDecodeArgs(**kw)
+
+
+@pytest.mark.parametrize("cache_over,step_over,status", [
+    (dict(head_dim=64), {}, abi.KVC_E_UNSUPPORTED),
+    (dict(window=16), {}, abi.KVC_E_UNSUPPORTED),
+    (dict(group=3), {}, abi.KVC_E_UNSUPPORTED),
+    (dict(kv_dtype=7), {}, abi.KVC_E_UNSUPPORTED),
+    (dict(n_units=0), {}, abi.KVC_E_INVALID),
+    (dict(k_win=None), {}, abi.KVC_E_INVALID),
+    (dict(k_tail=FAKE + 2), {}, abi.KVC_E_INVALID),
+    ({}, dict(q=None), abi.KVC_E_INVALID),
+    ({}, dict(v_new=None), abi.KVC_E_INVALID),
+    ({}, dict(out=None), abi.KVC_E_INVALID),
+    ({}, dict(max_full=-1), abi.KVC_E_BUDGET),
+    ({}, dict(max_full=30, max_int2=8), abi.KVC_E_BUDGET),
+    ({}, dict(max_tail=64), abi.KVC_E_BUDGET),
+    ({}, dict(probs=FAKE, probs_stride=10), abi.KVC_E_INVALID),
+    ({}, dict(accumulate_cum=2), abi.KVC_E_INVALID),
+])
+def test_decode_attn_validation(cache_over, step_over, status):
+    L = abi.lib()
+    c, s = good_cache(**cache_over), good_step(**step_over)
+    assert L.kvc_decode_attn(C.byref(c), C.byref(s), FAKE, 1 << 30, None) == status
+
+
+def test_decode_attn_workspace_checks():
+    L = abi.lib()
+    c, s = good_cache(), good_step()
+    need = L.kvc_decode_attn_workspace(C.byref(c), C.byref(s))
+    assert need > 0
+    assert L.kvc_decode_attn(C.byref(c), C.byref(s), FAKE, need - 1, None) == abi.KVC_E_WORKSPACE
+    assert L.kvc_decode_attn(C.byref(c), C.byref(s), None, need, None) == abi.KVC_E_WORKSPACE
+    assert L.kvc_decode_attn(C.byref(c), C.byref(s), FAKE + 16, need, None) == abi.KVC_E_WORKSPACE
+    assert L.kvc_decode_attn_workspace(C.byref(good_cache(head_dim=64)), C.byref(s)) == 0
+
+
+def test_route_and_list_validation():
+    L = abi.lib()
+    c = good_cache()
+    ra = abi.KvcTierRouteArgs(cache=C.pointer(c), scores=None, budget_full=FAKE, budget_int2=None,
+                              quant_list=FAKE, n_quant=FAKE, promo_list=FAKE, n_promo=FAKE)
+    assert L.kvc_route(abi.KVC_ROUTE_TIERS, C.byref(ra), None, 0, None) == abi.KVC_E_INVALID
+    assert L.kvc_route(99, C.byref(ra), None, 0, None) == abi.KVC_E_UNSUPPORTED
+    assert L.kvc_route(abi.KVC_ROUTE_TIERS, None, None, 0, None) == abi.KVC_E_INVALID
+    assert L.kvc_quantize_int2(C.byref(c), FAKE, FAKE, 32, -1, None) == abi.KVC_E_BUDGET
+    assert L.kvc_quantize_int2(C.byref(c), FAKE, FAKE, 32, 2 * 32 + 1, None) == abi.KVC_E_BUDGET
+    assert L.kvc_quantize_int2(C.byref(c), None, FAKE, 32, 5, None) == abi.KVC_E_INVALID
+    assert L.kvc_promote(C.byref(c), FAKE, FAKE, 0, 5, None) == abi.KVC_E_INVALID
+    assert L.kvc_promote(C.byref(good_cache(window=8)), FAKE, FAKE, 32, 5, None) == abi.KVC_E_UNSUPPORTED
+    # nothing to do is accepted without touching the device
+    assert L.kvc_quantize_int2(C.byref(c), None, None, 32, 0, None) == abi.KVC_OK
+    assert L.kvc_score(5, C.byref(ra), None, 0, None) == abi.KVC_E_UNSUPPORTED

@@ -1,0 +1,179 @@
+"""GPU parity of the windowed three-tier decode path against the oracle (needs an MI355X).
+
+Covers: per-step attention output, per-key probabilities, window mass and cumulative score; routing tiers and
+lists (bit-exact on the GPU's scores); write-once ledger bytes; promoted copies; adversarial quantiser groups;
+adversarial routing scores (ties, zeros, signed zeros); the write-once violation flag; determinism.
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_compression_gqa_amd import configs, synth
+from kv_cache_compression_gqa_amd.session import DecodeSession
+from oracle import select as osel
+from tests.decode_parity import compare_route, make_oracles, run_decode_parity
+
+pytestmark = pytest.mark.gpu
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def test_tiny_run_matches_oracle(gpu_lib):
+    log("case: tiny_gqa4_ctx1k_f16, 8 steps, route every 4")
+    run_decode_parity(configs.TINY, log=log)
+
+
+def test_tiny_bf16_run_matches_oracle(gpu_lib):
+    cfg = dataclasses.replace(configs.TINY, dtype="bf16", name="tiny_bf16", seed=11)
+    log("case: tiny bf16 variant, 8 steps")
+    run_decode_parity(cfg, log=log)
+
+
+def test_ragged_tail_and_odd_budgets(gpu_lib):
+    # 3 KV heads x G=2, context 1000 (31 windows + 8-token tail), budgets 5 / 7, route every 3 steps
+    cfg = dataclasses.replace(configs.TINY, name="ragged", seed=12, hq=6, hkv=3, context=1000, n_salient=9,
+                              budget_full=5, budget_int2=7, steps=10, route_every=3)
+    log("case: ragged tail (1000 tokens), G=2, budgets 5/7")
+    run_decode_parity(cfg, log=log)
+
+
+def test_group_of_eight_and_one(gpu_lib):
+    for hq, hkv in ((16, 2), (2, 2)):
+        cfg = dataclasses.replace(configs.TINY, name=f"g{hq // hkv}", seed=13, hq=hq, hkv=hkv, context=640,
+                                  n_salient=5, budget_full=4, budget_int2=6, steps=6, route_every=2)
+        log(f"case: G={hq // hkv}")
+        run_decode_parity(cfg, log=log)
+
+
+def test_llama_layer_32k_run_matches_oracle(gpu_lib):
+    # every unit runs on the GPU in one launch; the oracle follows two units exactly through all 64 steps
+    log("case: llama3_8b_layer_ctx32k_bf16, 64 steps, oracle on units 0 and 5")
+    run_decode_parity(configs.LLAMA3_8B_LAYER_32K, check_units=[0, 5], log=log)
+
+
+def _adversarial_rows(dtype, rng):
+    rows = []
+    rows.append(np.full(128, 0.375))                                     # constant groups
+    rows.append(np.where(np.arange(128) % 2 == 0, -0.5, 1.0))            # two-valued
+    k = rng.integers(0, 4, 128)
+    k[::32], k[1::32] = 0, 3
+    rows.append(-1.5 + 0.25 * k)                                         # exactly on the grid
+    rows.append(rng.standard_normal(128) * 1e-5)                         # fp16-subnormal zeros/scales
+    rows.append(rng.standard_normal(128) * 3000.0)                       # large magnitudes
+    rows.append(np.concatenate([np.full(32, -0.0), np.full(32, 0.0), rng.standard_normal(64)]))
+    rows.append(rng.uniform(-1, 1, 128) * 60000.0)                       # near the fp16 range
+    base = np.stack(rows)
+    out = np.concatenate([base, rng.standard_normal((32 - len(rows), 128))])
+    return synth.to_storage_bits(out, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_quantise_and_promote_adversarial_groups(gpu_lib, dtype):
+    cfg = dataclasses.replace(configs.TINY, dtype=dtype, name=f"adv_{dtype}", seed=14)
+    inp = synth.make_decode(cfg, steps=2)
+    rng = np.random.default_rng(15)
+    for w in range(8, 16):
+        inp.k_win[0, w] = _adversarial_rows(dtype, rng)
+        inp.v_win[0, w] = _adversarial_rows(dtype, rng)
+    sess = DecodeSession(inp)
+    oracles = make_oracles(inp)
+    nw = inp.n_windows_max
+    # windows 0..7 FULL, 8..15 INT2 (first demotion: quantised), rest evicted
+    sc = np.zeros((len(inp.units), nw), np.float32)
+    sc[:, :16] = np.arange(16, 0, -1)
+    scores = torch.from_numpy(sc).cuda()
+    sess.route(scores=scores)
+    torch.cuda.synchronize()
+    compare_route(sess, oracles, sc.astype(np.float64))
+    # promote 8..15 back to FULL, demote 0..7 to INT2 (their first demotion)
+    sc2 = np.zeros_like(sc)
+    sc2[:, 8:16] = 10.0
+    sc2[:, 0:8] = 5.0
+    sess.route(scores=torch.from_numpy(sc2).cuda())
+    torch.cuda.synchronize()
+    compare_route(sess, oracles, sc2.astype(np.float64))
+    assert sess.device_status() == 0
+
+
+def test_route_adversarial_scores(gpu_lib):
+    cfg = dataclasses.replace(configs.TINY, name="route_adv", seed=16)
+    inp = synth.make_decode(cfg, steps=1)
+    rng = np.random.default_rng(17)
+    cases = [np.zeros(32), np.full(32, 1.0), np.where(np.arange(32) % 2 == 0, -0.0, 0.0),
+             np.round(rng.random(32), 1), np.arange(32, dtype=float), np.arange(32, 0, -1, dtype=float),
+             np.where(rng.random(32) < 0.5, 1e-30, 1e30)]
+    for case in cases:
+        for bf, bq in ((8, 8), (0, 5), (5, 0), (0, 0), (32, 0), (20, 20), (3, 40)):
+            sess = DecodeSession(inp, budgets=(np.full(2, bf), np.full(2, bq)))
+            oracles = make_oracles(inp)
+            sc = np.stack([case, case[::-1]]).astype(np.float32)
+            sess.route(scores=torch.from_numpy(sc).cuda())
+            torch.cuda.synchronize()
+            compare_route(sess, oracles, sc.astype(np.float64))
+    log("route: 49 adversarial cases match")
+
+
+def test_write_once_violation_is_refused(gpu_lib):
+    inp = synth.make_decode(configs.TINY, steps=1)
+    sess = DecodeSession(inp)
+    sc = np.zeros((2, 32), np.float32)
+    sc[:, :16] = np.arange(16, 0, -1)
+    sess.route(scores=torch.from_numpy(sc).cuda())
+    torch.cuda.synchronize()
+    assert sess.device_status() == 0
+    before = (sess.k_codes.clone(), sess.k_meta.clone(), sess.v_codes.clone())
+    # ask for window 10 (already ledgered) again, after scribbling over its full-precision copy
+    sess.k_win[0, 10].fill_(123)
+    lst = torch.zeros((2, 32), dtype=torch.int32, device="cuda")
+    lst[0, 0] = 10
+    cnt = torch.tensor([1, 0], dtype=torch.int32, device="cuda")
+    import ctypes as C
+    from kv_cache_compression_gqa_amd import abi
+    abi.check(abi.lib().kvc_quantize_int2(C.byref(sess._cache), abi.ptr(lst), abi.ptr(cnt), 32, 1,
+                                          abi.stream_handle()), "quantize")
+    torch.cuda.synchronize()
+    assert sess.device_status() & abi.KVC_DEV_LEDGER_REWRITE
+    assert torch.equal(before[0], sess.k_codes) and torch.equal(before[1], sess.k_meta)
+    assert torch.equal(before[2], sess.v_codes)
+
+
+def test_probabilities_sum_to_one_and_runs_are_bitwise_reproducible(gpu_lib):
+    results = []
+    for _ in range(2):
+        inp = synth.make_decode(configs.TINY)
+        sess = DecodeSession(inp)
+        outs = []
+        for t in range(8):
+            pr = torch.zeros((2, 4, sess.probs_stride()), device="cuda")
+            sess.step(probs=pr)
+            torch.cuda.synchronize()
+            sums = pr.double().sum(-1)
+            assert torch.all((sums - 1).abs() < 1e-5), sums
+            outs.append((sess.out.clone(), pr.clone(), sess.cum.clone(), sess.tier.clone()))
+        results.append(outs)
+    for a, b in zip(*results):
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
+
+
+def test_score_only_matches_decode(gpu_lib):
+    import ctypes as C
+    from kv_cache_compression_gqa_amd import abi
+    inp = synth.make_decode(configs.TINY, steps=1)
+    s1, s2 = DecodeSession(inp), DecodeSession(inp)
+    s1.step(route=False)
+    args = s2.decode_args(0, score_only=True)
+    ws = s2.workspace(args)
+    sa = abi.KvcWindowScoreArgs(cache=C.pointer(s2._cache), step=C.pointer(args))
+    abi.check(abi.lib().kvc_score(abi.KVC_SCORE_WINDOWS, C.byref(sa), abi.ptr(ws), s2._ws_bytes,
+                                  abi.stream_handle()), "kvc_score")
+    torch.cuda.synchronize()
+    assert torch.equal(s1.cum, s2.cum)
+    assert torch.equal(s1.tail_len, s2.tail_len)
+    assert torch.all(s2.out == 0)
