@@ -1,0 +1,227 @@
+"""Throughput of the compressed-KV GQA decode step on one MI355X.
+
+Workload: one Llama-3-8B-shaped attention layer at 32K context (batch 1, 32 query heads / 8 KV heads, head_dim
+128, bf16 K/V, window 32, 20% of windows full precision + 30% INT2 + 50% evicted, routing every 16 steps).
+A step is one decode step of that schedule in its routed steady state: append the new token, attend over the
+FULL + INT2 + tail keys with the window mass and cumulative score fused in, and — every 16th step — re-route the
+windows (radix select), quantise first demotions into the write-once ledger and promote by dequantisation.
+
+Cold caches: R independent replicas (distinct seeds; >= 1 GB of cache in total, far above the 256 MB Infinity
+Cache) are stepped round-robin. Warm-up takes every replica through its first 16 full-cache steps and first
+routing event; the K timed steps are captured in one HIP graph and replayed once between barriers.
+
+value  = KV tokens scored + routed + attended per second = sum over timed steps of the resident positions of the
+         sequence (FULL and INT2 window tokens + tail + new token) / wall time.
+roofline = the decode kernels' algorithmic bytes per launch (resident K/V bytes: 512 B per full-precision token,
+         96 B per INT2 token incl. its scale/zero words, 512 B per tail token, plus q) / their average duration,
+         measured with HIP events recorded around every decode launch inside the timed graph.
+cpu_baseline = the CPU oracle (fp64 numpy) on a bounded sample of the same routed steps.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--replicas R] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import dataclasses
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=128)
+    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="launch steps eagerly instead of one captured graph")
+    return ap.parse_args()
+
+
+def step_bytes_and_tokens(sess, W=32, D=128):
+    """Algorithmic HBM bytes and KV tokens of the next decode step of a session (host-side counts)."""
+    nf, nq, tl = int(sess.h_full.max()), int(sess.h_int2.max()), int(sess.h_tail.max())
+    U, G = sess.U, sess.G
+    tok_full, tok_int2, tok_tail = nf * W, nq * W, tl + 1
+    per_unit = tok_full * 2 * D * 2 + tok_int2 * 2 * (D // 4 + (D // 32) * 4) + tok_tail * 2 * D * 2 + G * D * 2
+    positions = tok_full + tok_int2 + tok_tail
+    return U * per_unit, positions
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in ("decode_attn.hip", "kvc_internal.h"):
+        h.update(open(os.path.join(ROOT, "kv_cache_compression_gqa_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(launch_bytes):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if it was taken on this kernel."""
+    path = os.path.join(ROOT, "profiles", "decode_attn_llama3_8b_layer_32k_traffic.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sha") != kernel_source_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, min_seconds=10.0, max_steps=160):
+    """Time the oracle on routed steps of the same workload: every KV-head unit of one layer is taken through its
+    full-cache phase and first routing event (untimed), then routed steps (with a routing event every 16) are
+    timed, one step of every unit per round, until ``min_seconds`` of CPU work or ``max_steps`` rounds."""
+    sys.path.insert(0, ROOT)
+    from kv_cache_compression_gqa_amd import synth
+    from oracle.qevict import QEvictUnit
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    units = cfg.n_units
+    inp = synth.make_decode(cfg, steps=cfg.route_every + max_steps)
+    ors = []
+    for j in range(units):
+        nw = int(inp.n_windows[j])
+        o = QEvictUnit(inp.k_win[j, :nw], inp.v_win[j, :nw], inp.k_tail0[j, :0], inp.v_tail0[j, :0], cfg.dtype)
+        for t in range(cfg.route_every):
+            o.step(inp.q[t, j], inp.k_new[t, j], inp.v_new[t, j])
+        o.route(*cfg.budgets(nw))
+        ors.append(o)
+    tokens = 0.0
+    rounds = 0
+    t0 = time.perf_counter()
+    while rounds < max_steps and (time.perf_counter() - t0) < min_seconds:
+        t = cfg.route_every + rounds
+        for j, o in enumerate(ors):
+            r = o.step(inp.q[t, j], inp.k_new[t, j], inp.v_new[t, j])
+            tokens += r.p.shape[1] / cfg.hkv    # one unit carries one KV head of the sequence's tokens
+            if (t + 1) % cfg.route_every == 0:
+                o.route(*cfg.budgets(o.n_windows))
+        rounds += 1
+    elapsed = time.perf_counter() - t0
+    return {"value": tokens / elapsed, "unit": "KV tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rounds} routed decode steps (routing every {cfg.route_every}) of all {units} KV-head units "
+                      f"of one 32K layer after an untimed full-cache phase; fp64 numpy oracle; {elapsed:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+              "(the per-unit work shards with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    sys.path.insert(0, ROOT)
+    from kv_cache_compression_gqa_amd import configs, synth
+    from kv_cache_compression_gqa_amd.session import DecodeSession
+
+    cfg = configs.LLAMA3_8B_LAYER_32K
+    R = args.replicas
+    if args.warmup < cfg.route_every * R:
+        print(f"warmup raised to {cfg.route_every * R} so every replica is past its first routing event",
+              file=sys.stderr)
+        args.warmup = cfg.route_every * R
+    per_rep = (args.warmup + 2 * args.steps + R - 1) // R + 1
+    torch.cuda.set_device(0)
+    sessions = []
+    for r in range(R):
+        inp = synth.make_decode(dataclasses.replace(cfg, seed=cfg.seed * 1000 + r), steps=per_rep)
+        s = DecodeSession(inp, tail_max=per_rep + 1)
+        s.reserve_workspace(per_rep)
+        sessions.append(s)
+    torch.cuda.synchronize()
+    print(f"replicas ready: {R} x {cfg.name}", file=sys.stderr, flush=True)
+
+    # warm-up: every replica through its full-cache phase and first routing event
+    for i in range(args.warmup):
+        sessions[i % R].step()
+    torch.cuda.synchronize()
+    print(f"warm-up done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    K = args.steps
+    plan = []  # (bytes, positions) per timed step, from the host-side counts at the time the step is issued
+
+    def issue(i, events=None):
+        s = sessions[i % R]
+        plan.append(step_bytes_and_tokens(s))
+        s.step(events=events)
+
+    # timed region: K steps, captured in one HIP graph and replayed once (or launched eagerly with --eager)
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(K):
+                issue(args.warmup + i)
+        torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(K):
+            issue(args.warmup + i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    timed_plan = list(plan)
+    print(f"timed region: {K} steps in {wall * 1e3:.3f} ms", file=sys.stderr, flush=True)
+
+    # kernel timing: the next K steps of the same replicas, HIP events around every decode launch. The GPU is
+    # first kept busy so that the host has enqueued every step before the GPU reaches it: each event pair then
+    # brackets GPU work only, never a host submission gap.
+    plan.clear()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    busy = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    for _ in range(60):
+        busy.fill_(1.0)
+    for i in range(K):
+        issue(args.warmup + K + i, events=events[i])
+    torch.cuda.synchronize()
+    del busy
+    kern_ms = [a.elapsed_time(b) for a, b in events]
+    kern_plan = list(plan)
+    st = [s.device_status() for s in sessions]
+    if any(st):
+        print(f"device status bits set: {st}", file=sys.stderr)
+        sys.exit(1)
+    total_bytes = sum(b for b, _ in timed_plan)
+    total_pos = sum(p for _, p in timed_plan)
+    avg_kern_s = float(np.mean(kern_ms)) * 1e-3
+    avg_bytes = sum(b for b, _ in kern_plan) / K
+    achieved = avg_bytes / avg_kern_s / 1e9
+    traffic = traffic_from_profile(avg_bytes)
+    rec = {
+        "metric": "KV tokens scored+routed+attended/s per decode step; % of HBM roofline",
+        "value": total_pos / wall,
+        "unit": "KV tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": wall / K * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": 1, "q_heads": cfg.hq, "kv_heads": cfg.hkv, "head_dim": 128,
+                   "context": cfg.context, "window": cfg.window, "tiers": "20% full / 30% int2 / 50% evicted",
+                   "route_every": cfg.route_every, "phase": "routed steady state", "replicas": R,
+                   "launch": "eager" if graph is None else "hip graph"},
+        "hbm_roofline_frac_step": total_bytes / wall / (HBM_PEAK_GBS * 1e9),
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "kvc_decode_attn (decode_partial + decode_combine)",
+                     "avg_launch_us": avg_kern_s * 1e6, "median_launch_us": float(np.median(kern_ms)) * 1e3,
+                     "algorithmic_bytes_per_launch": avg_bytes},
+    }
+    if not args.no_cpu_baseline:
+        print("timing the CPU oracle sample", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -332,12 +332,20 @@ __global__ __launch_bounds__(kBlock) void decode_partial(DecodeParams p) {
   }
 }
 
+// Combine: kCombineBlocks workgroups per unit. Each recomputes the per-head merge weights f[c][h] =
+// exp(m_c - M_h) / L_h of the unit's chunks (cheap), then handles its slice of the outputs, windows and probs.
+constexpr int kCombineBlocks = 8;
+constexpr int kMaxChunks = 1024;
+
 template <int G>
 __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
-  const int u = blockIdx.x;
+  const int u = blockIdx.x / kCombineBlocks;
+  const int b = blockIdx.x - u * kCombineBlocks;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
   __shared__ float sM[G], sL[G];
+  __shared__ float f[kMaxChunks / 4][G];   // reused in 4 slices when CH > kMaxChunks / 4
+  __shared__ float red[4][64];
   const float* ml = p.part_ml + size_t(u) * p.CH * G * 2;
   for (int h = wave; h < G; h += 4) {
     float mx = -INFINITY;
@@ -353,17 +361,49 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
   }
   __syncthreads();
   if (p.out != nullptr) {
+    // this block's 64 outputs (of G*D); 4 threads per output, each over a fixed quarter of the chunks
+    const int per_block = G * kD / kCombineBlocks;
     const float* po = p.part_o + size_t(u) * p.CH * G * kD;
-    for (int idx = threadIdx.x; idx < G * kD; idx += 256) {
-      const int h = idx / kD;
-      float acc = 0.0f;
-      for (int c = 0; c < p.CH; ++c) acc += po[size_t(c) * G * kD + idx] * exp_diff(ml[(c * G + h) * 2], sM[h]);
-      p.out[size_t(u) * G * kD + idx] = acc / sL[h];
+    const int q4 = threadIdx.x >> 6;
+    float acc[(G * kD / kCombineBlocks + 63) / 64];
+#pragma unroll
+    for (int k = 0; k < (per_block + 63) / 64; ++k) acc[k] = 0.0f;
+    for (int c0 = 0; c0 < p.CH; c0 += kMaxChunks / 4) {
+      const int cn = min(kMaxChunks / 4, p.CH - c0);
+      for (int i = threadIdx.x; i < cn * G; i += 256) {
+        const int c = i / G, h = i - c * G;
+        f[c][h] = exp_diff(ml[((c0 + c) * G + h) * 2], sM[h]) / sL[h];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < (per_block + 63) / 64; ++k) {
+        const int local = k * 64 + lane;
+        if (local < per_block) {
+          const int idx = b * per_block + local;
+          const int h = idx / kD;
+          float a = 0.0f;
+#pragma unroll 8
+          for (int c = q4; c < cn; c += 4) a += po[size_t(c0 + c) * G * kD + idx] * f[c][h];
+          acc[k] += a;
+        }
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int k = 0; k < (per_block + 63) / 64; ++k) {
+      red[q4][lane] = acc[k];
+      __syncthreads();
+      const int local = k * 64 + threadIdx.x;
+      if (threadIdx.x < 64 && local < per_block) {
+        p.out[size_t(u) * G * kD + b * per_block + local] = ((red[0][threadIdx.x] + red[1][threadIdx.x]) +
+                                                             red[2][threadIdx.x]) + red[3][threadIdx.x];
+      }
+      __syncthreads();
     }
   }
   const size_t unit_win = size_t(u) * p.NW;
   const int nw = min(max(p.n_windows[u], 0), p.NW);
-  for (int w = threadIdx.x; w < nw; w += 256) {
+  for (int w = b * 256 + threadIdx.x; w < nw; w += 256 * kCombineBlocks) {
     float mass = 0.0f;
     if (p.tier[unit_win + w] != KVC_TIER_EVICTED) {
 #pragma unroll
@@ -383,11 +423,11 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
     const int n_res = (nf + nq) * kW + tl + has_new;
     for (int h = 0; h < G; ++h) {
       float* pr = p.probs + (size_t(u) * G + h) * p.probs_stride;
-      for (int i = threadIdx.x; i < n_res; i += 256) pr[i] = exp_diff(pr[i], sM[h]) / sL[h];
+      for (int i = b * 256 + threadIdx.x; i < n_res; i += 256 * kCombineBlocks) pr[i] = exp_diff(pr[i], sM[h]) / sL[h];
     }
   }
   __syncthreads();
-  if (has_new && threadIdx.x == 0) p.tail_len[u] = tl + 1;
+  if (b == 0 && has_new && threadIdx.x == 0) p.tail_len[u] = tl + 1;
 }
 
 template <int G, class T>
@@ -395,7 +435,7 @@ hipError_t launch_g(const DecodeParams& p, int U, hipStream_t s) {
   hipLaunchKernelGGL((decode_partial<G, T>), dim3(U * p.CH), dim3(kBlock), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine<G>), dim3(U), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((decode_combine<G>), dim3(U * kCombineBlocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -133,14 +133,29 @@ class DecodeSession:
             self._ws_bytes = self._ws.numel()
         return self._ws
 
-    def step(self, probs=None, mass=None, append=True, route=True, stream=None):
-        """Decode step t+1 using the pre-generated inputs of that step; routes when due."""
+    def reserve_workspace(self, extra_steps: int):
+        """Allocate the decode workspace for the largest bounds the next ``extra_steps`` steps can reach (so no
+        allocation happens later, e.g. while a graph is being captured)."""
+        saved = self.h_tail.copy()
+        self.h_tail = self.h_tail + extra_steps
+        try:
+            self.workspace(self.decode_args(0, probs=None))
+        finally:
+            self.h_tail = saved
+
+    def step(self, probs=None, mass=None, append=True, route=True, stream=None, events=None):
+        """Decode step t+1 using the pre-generated inputs of that step; routes when due. ``events`` = (before,
+        after) torch events recorded on the stream around the decode launch."""
         ti = self.t
         args = self.decode_args(ti, probs=probs, mass=mass, append=append)
         ws = self.workspace(args)
         L = abi.lib()
+        if events is not None:
+            events[0].record()
         abi.check(L.kvc_decode_attn(C.byref(self._cache), C.byref(args), abi.ptr(ws), self._ws_bytes,
                                     abi.stream_handle(stream)), "kvc_decode_attn")
+        if events is not None:
+            events[1].record()
         if append:
             self.h_tail += 1
         self.t += 1
