@@ -56,13 +56,19 @@ typedef enum { KVC_TIER_FULL = 0, KVC_TIER_INT2 = 1, KVC_TIER_EVICTED = 2 } kvc_
  * positions [w*W, (w+1)*W) (QEvict page, "Metodologia": contiguous windows). Storage is indexed by window
  * position, so promotion and demotion never move another window's data:
  *
- *   k_win, v_win   [U][NW][W][D]   K/V storage dtype. The full-precision copy of window w. Valid while w is
- *                                  FULL; rewritten with the dequantised ledger copy when w is promoted.
- *   k_codes,v_codes[U][NW][W][D/4] INT2 ledger codes: element 4b+j of a token row in bits 2j..2j+1 of byte b.
- *   k_meta, v_meta [U][NW][W][D/32] one 32-bit word per (token, 32-element group): fp16 scale in bits 0..15,
+ *   k_win          [U][NW][W][D]   K storage dtype, token-major. The full-precision copy of window w, valid while
+ *                                  w is FULL; rewritten with the dequantised ledger copy when w is promoted.
+ *   v_win          [U][NW][D][W]   V storage dtype, head_dim-major inside each window (V^T), same lifetime.
+ *   k_codes        [U][NW][W][32]  INT2 ledger, K: 32 bytes per token; byte 8*s + 2*g + h holds the codes of
+ *                                  head_dim 32g + 8s + 4h + e (e = 0..3) at bits 2e.
+ *   k_meta         [U][NW][W][4]   one 32-bit word per (token, 32-element group g): fp16 scale in bits 0..15,
  *                                  fp16 zero in bits 16..31. Dequantised value x = fmaf(code, scale, zero).
- *   k_tail, v_tail [U][TM][D]      unrouted tail: the partial last prefill window plus every decode-time token,
+ *   v_codes        [U][NW][16][4][8] 16-bit words: word (r, q, dt) holds the codes of tokens 8q + e
+ *                                  (e = 0..7) of head_dim 16dt + r at bits 2e.
+ *   v_meta         [U][NW][4][4][8] words: word (q, g, e) = scale/zero of token 8q + e, group g.
+ *   k_tail         [U][TM][D]      unrouted tail: the partial last prefill window plus every decode-time token,
  *                                  always attended, outside the budgets.
+ *   v_tail         [U][TM/32][D][32]  the same tail tokens, head_dim-major inside each 32-token block.
  *   tail_len       [U] int32       valid tail rows (advanced by kvc_decode_attn when it appends a token).
  *   n_windows      [U] int32       routable windows of the unit (<= NW).
  *   tier           [U][NW] int8    kvc_tier of every window (entries >= n_windows unused).
@@ -73,6 +79,7 @@ typedef enum { KVC_TIER_FULL = 0, KVC_TIER_INT2 = 1, KVC_TIER_EVICTED = 2 } kvc_
  *   n_full, n_int2 [U] int32       lengths of the two parts of res_list.
  *   status         [1] int32       device error bits (KVC_DEV_*).
  *
+ * The layouts put, for every MFMA operand the decode kernel builds, one lane's data in one 16-byte load.
  * All K/V rows must be 16-byte aligned (every base pointer 256-byte aligned is sufficient). */
 typedef struct kvc_cache {
   int32_t n_units;       /* U >= 1 */
@@ -80,7 +87,7 @@ typedef struct kvc_cache {
   int32_t head_dim;      /* D, must be 128 */
   int32_t window;        /* W, must be 32 */
   int32_t n_windows_max; /* NW >= 1 */
-  int32_t tail_max;      /* TM >= 1 */
+  int32_t tail_max;      /* TM >= 32, a multiple of 32 */
   int32_t kv_dtype;      /* kvc_dtype */
   int32_t reserved;      /* must be 0 */
   const int32_t* n_windows;

@@ -14,7 +14,7 @@ int check_cache(const kvc_cache* c) {
   if (!(c->group == 1 || c->group == 2 || c->group == 4 || c->group == 8)) return KVC_E_UNSUPPORTED;
   if (c->kv_dtype != KVC_F16 && c->kv_dtype != KVC_BF16) return KVC_E_UNSUPPORTED;
   if (c->n_units < 1 || c->n_units > 16384 || c->n_windows_max < 1 || c->n_windows_max > 16384 ||
-      c->tail_max < 1 || c->reserved != 0) {
+      c->tail_max < 32 || c->tail_max % 32 != 0 || c->reserved != 0) {
     return KVC_E_INVALID;
   }
   const void* need16[] = {c->k_win, c->v_win, c->k_tail, c->v_tail, c->k_codes, c->v_codes, c->k_meta, c->v_meta};

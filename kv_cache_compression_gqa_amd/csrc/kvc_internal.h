@@ -76,14 +76,7 @@ __device__ __forceinline__ float exp_diff(float a, float b) { return a == -INFIN
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // ---- launchers (host) -------------------------------------------------------------------------------------
-struct DecodeGrid {
-  int chunks_full;  // chunks of full-precision windows per unit
-  int chunks_int2;  // chunks of INT2 windows per unit
-  int chunks_tail;  // chunks of tail tokens per unit
-  int chunks() const { return chunks_full + chunks_int2 + chunks_tail; }
-};
-
-DecodeGrid decode_grid(const kvc_decode_args& a);
+int decode_slices(const kvc_cache& c, const kvc_decode_args& a);
 size_t decode_workspace_bytes(const kvc_cache& c, const kvc_decode_args& a);
 hipError_t launch_decode(const kvc_cache& c, const kvc_decode_args& a, void* ws, hipStream_t s);
 hipError_t launch_route_tiers(const kvc_tier_route_args& a, hipStream_t s);

@@ -18,7 +18,7 @@ import ctypes as C
 import numpy as np
 import torch
 
-from . import abi
+from . import abi, layout
 from .synth import DecodeInputs
 
 
@@ -42,20 +42,23 @@ class DecodeSession:
         W, D, G = cfg.window, cfg.head_dim, cfg.group
         S = inp.q.shape[0] if steps is None else steps
         self.U, self.NW, self.G, self.D, self.W = U, NW, G, D, W
-        self.TM = tail_max if tail_max is not None else int(inp.tail0.max()) + S + 1
+        tm = tail_max if tail_max is not None else int(inp.tail0.max()) + S + 1
+        self.TM = max(32, (tm + 31) // 32 * 32)
         dev = self.device
         self.k_win = _bits(inp.k_win, dev)
-        self.v_win = _bits(inp.v_win, dev)
+        self.v_win = _bits(layout.v_win_to_lib(inp.v_win), dev)   # [U][NW][D][W]
         self.k_codes = torch.zeros((U, NW, W, D // 4), dtype=torch.uint8, device=dev)
-        self.v_codes = torch.zeros_like(self.k_codes)
+        self.v_codes = torch.zeros((U, NW, 16, 4, 8), dtype=torch.int16, device=dev)
         self.k_meta = torch.zeros((U, NW, W, D // 32), dtype=torch.int32, device=dev)
-        self.v_meta = torch.zeros_like(self.k_meta)
+        self.v_meta = torch.zeros((U, NW, 4, 4, 8), dtype=torch.int32, device=dev)
         self.k_tail = torch.zeros((U, self.TM, D), dtype=torch.int16, device=dev)
-        self.v_tail = torch.zeros_like(self.k_tail)
+        self.v_tail = torch.zeros((U, self.TM // W, D, W), dtype=torch.int16, device=dev)
         t0 = int(inp.tail0.max())
         if t0 > 0:
             self.k_tail[:, :t0] = _bits(inp.k_tail0[:, :t0], dev)
-            self.v_tail[:, :t0] = _bits(inp.v_tail0[:, :t0], dev)
+            vt = np.zeros((U, W, D), np.uint16)
+            vt[:, :t0] = inp.v_tail0[:, :t0]
+            self.v_tail[:, 0] = _bits(layout.v_tail_to_lib(vt)[:, 0], dev)
         self.tail_len = _dev(inp.tail0.astype(np.int32), torch.int32, dev)
         self.n_windows = _dev(inp.n_windows.astype(np.int32), torch.int32, dev)
         self.tier = torch.zeros((U, NW), dtype=torch.int8, device=dev)

@@ -12,9 +12,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from kv_cache_compression_gqa_amd import synth
+from kv_cache_compression_gqa_amd import layout, synth
 from kv_cache_compression_gqa_amd.session import DecodeSession
-from oracle import int2 as oint2
 from oracle.qevict import QEvictUnit
 from oracle.select import FULL, INT2
 
@@ -62,7 +61,7 @@ def compare_route(sess: DecodeSession, oracles, gpu_cum):
     pl = sess.promo_list.cpu().numpy()
     led = sess.ledgered.cpu().numpy()
     kc = sess.k_codes.cpu().numpy()
-    vc = sess.v_codes.cpu().numpy()
+    vc = sess.v_codes.cpu().numpy().view(np.uint16)
     km = sess.k_meta.cpu().numpy().view(np.uint32)
     vm = sess.v_meta.cpu().numpy().view(np.uint32)
     kw = sess.k_win.cpu().numpy().view(np.uint16)
@@ -80,13 +79,13 @@ def compare_route(sess: DecodeSession, oracles, gpu_cum):
         for w in range(nw):
             assert bool(led[j, w]) == (w in o.ledger), f"ledger flag unit {j} window {w}"
         for w, e in o.ledger.items():
-            assert kc[j, w].tobytes() == oint2.pack_codes(e["kc"]).tobytes(), f"K codes unit {j} window {w}"
-            assert vc[j, w].tobytes() == oint2.pack_codes(e["vc"]).tobytes(), f"V codes unit {j} window {w}"
-            assert km[j, w].tobytes() == oint2.pack_meta(e["ks"], e["kz"]).tobytes(), f"K meta {j} {w}"
-            assert vm[j, w].tobytes() == oint2.pack_meta(e["vs"], e["vz"]).tobytes(), f"V meta {j} {w}"
+            assert kc[j, w].tobytes() == layout.k_codes_to_lib(e["kc"]).tobytes(), f"K codes unit {j} window {w}"
+            assert vc[j, w].tobytes() == layout.v_codes_to_lib(e["vc"]).tobytes(), f"V codes unit {j} window {w}"
+            assert km[j, w].tobytes() == layout.k_meta_to_lib(e["ks"], e["kz"]).tobytes(), f"K meta {j} {w}"
+            assert vm[j, w].tobytes() == layout.v_meta_to_lib(e["vs"], e["vz"]).tobytes(), f"V meta {j} {w}"
         for w in full:
             assert kw[j, w].tobytes() == o.kw[w].tobytes(), f"K full copy unit {j} window {w}"
-            assert vw[j, w].tobytes() == o.vw[w].tobytes(), f"V full copy unit {j} window {w}"
+            assert layout.v_win_from_lib(vw[j, w]).tobytes() == o.vw[w].tobytes(), f"V full copy unit {j} window {w}"
 
 
 def run_decode_parity(cfg, units=None, steps=None, check_units=None, check_steps=None, probs=True, log=print):
