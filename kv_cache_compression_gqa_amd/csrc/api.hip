@@ -46,6 +46,7 @@ int check_decode(const kvc_cache* c, const kvc_decode_args* a, bool need_out) {
     const int64_t need = int64_t(kvc::kW) * (a->max_full + a->max_int2) + a->max_tail + has_new;
     if (a->probs_stride < need) return KVC_E_INVALID;
   }
+  if (!kvc::decode_supported(*c, *a)) return KVC_E_UNSUPPORTED;
   return KVC_OK;
 }
 

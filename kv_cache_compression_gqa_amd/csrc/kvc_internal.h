@@ -77,6 +77,7 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // ---- launchers (host) -------------------------------------------------------------------------------------
 int decode_slices(const kvc_cache& c, const kvc_decode_args& a);
+bool decode_supported(const kvc_cache& c, const kvc_decode_args& a);
 size_t decode_workspace_bytes(const kvc_cache& c, const kvc_decode_args& a);
 hipError_t launch_decode(const kvc_cache& c, const kvc_decode_args& a, void* ws, hipStream_t s);
 hipError_t launch_route_tiers(const kvc_tier_route_args& a, hipStream_t s);
