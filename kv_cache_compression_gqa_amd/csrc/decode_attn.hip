@@ -10,13 +10,14 @@
 //   * dense task: one FULL window or one 32-token tail block: K (8 KiB) and V^T (8 KiB) straight into the MFMA
 //     operand registers (16 bytes per lane per instruction);
 //   * INT2 task: kQW INT2 windows: codes into registers, the per-token scale/zero words through LDS.
-//   Task t of a unit: t < max_full -> FULL window res_list[t]; then the tail blocks; then the INT2 windows in
-//   groups of kQW. Tasks past the device counts are empty. The INT2 window ids are read at the offset the device
-//   count usually has (n_full == max_full) together with the counts, and re-read only when it differs.
+//   Tasks of a unit, in launch order: the INT2 windows in groups of kQW (their loads are the most scattered and
+//   their arithmetic the longest, so they go first), the tail blocks, then FULL window res_list[f] per task.
+//   Tasks past the device counts are empty. The INT2 window ids are read at the offset the device count usually
+//   has (n_full == max_full) together with the counts, and re-read only when it differs.
 //   * q.K^T on MFMA (v_mfma_f32_16x16x32 bf16/f16): A = the G query heads (rows, zero-padded to 16), B = 16
 //     tokens x 32 head_dim of K. INT2 keys enter B as 128+c (bf16) / 1024+c (fp16) bit patterns, one group of 32
 //     head_dim per MFMA; the group's scale/zero are applied to the fp32 product:  s*acc + (z - magic*s)*sum(q).
-//   * softmax over the task's keys (max, exp, sums by 16-lane butterflies); each window's exp-sum and the
+//   * softmax over the task's keys (max, exp, sums by DPP reductions over 16-lane rows); each window's exp-sum and the
 //     reference max it is relative to are written for the score.
 //   * P.V on MFMA: A = 16 head_dim x 32 tokens of V (V is stored transposed per window), B = P^T split into a
 //     high and a low part (columns 0..G-1 and G..2G-1) so the product keeps ~16 bits of P. INT2 values enter A as
@@ -176,11 +177,7 @@ __device__ __forceinline__ void task_softmax(f32x4 (&S)[NWIN][2], WaveOut& wo, f
     float v = fmaxf(S[0][0][r], S[0][1][r]);
 #pragma unroll
     for (int i = 1; i < NWIN; ++i) v = fmaxf(v, fmaxf(S[i][0][r], S[i][1][r]));
-    v = xor_max(v, 1);
-    v = xor_max(v, 2);
-    v = xor_max(v, 4);
-    v = xor_max(v, 8);
-    wo.m[r] = v;
+    wo.m[r] = row_max16(v);
   }
 #pragma unroll
   for (int i = 0; i < NWIN; ++i) {
@@ -195,11 +192,7 @@ __device__ __forceinline__ void task_softmax(f32x4 (&S)[NWIN][2], WaveOut& wo, f
     float tot = 0.0f;
 #pragma unroll
     for (int i = 0; i < NWIN; ++i) {
-      float v = S[i][0][r] + S[i][1][r];
-      v = xor_sum(v, 1);
-      v = xor_sum(v, 2);
-      v = xor_sum(v, 4);
-      v = xor_sum(v, 8);
+      const float v = row_sum16(S[i][0][r] + S[i][1][r]);
       ws[i][r] = v;
       tot += v;
     }
@@ -487,14 +480,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   c.unit_win = size_t(u) * p.NW;
   const int32_t* res = p.res_list + c.unit_win;
   const int MF = p.max_full;
-  const int t_tail = MF, t_int2 = MF + p.n_tb, t_end = MF + p.n_tb + p.n_qt;
+  const int t_tail = p.n_qt, t_full = p.n_qt + p.n_tb, t_end = t_full + MF;
+  const int q0 = task * kQW;    // INT2 task: first INT2 slot
+  const int f = task - t_full;  // FULL task: slot in res_list
 
   // one vector load gathers the unit's device counts (lanes 0..2) and this wave's window ids (lanes 3..): the
-  // FULL window res_list[task], or the INT2 windows at the usual offset n_full == max_full (re-read otherwise)
-  const int q0 = (task - t_int2) * kQW;
+  // FULL window res_list[f], or the INT2 windows at the usual offset n_full == max_full (re-read otherwise)
   int gv;
   {
-    const int ridx = task < t_tail ? task : min(max(MF + q0 + lane - 3, 0), p.NW - 1);
+    const int ridx = min(max(task >= t_full ? f : MF + q0 + lane - 3, 0), p.NW - 1);
     const int32_t* cnt = lane == 0 ? p.n_full : (lane == 1 ? p.n_int2 : p.tail_len);
     const int32_t* gp = lane < 3 ? cnt + u : res + ridx;
     gv = *gp;
@@ -534,37 +528,37 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   float* plds = plds_all[wave];
 
   if (task < t_tail) {
-    int id = sid[0];
-    if (task < c.nf) {
-      if (unsigned(id) >= unsigned(p.NW)) {
-        if (lane == 0) atomicOr(p.status, KVC_DEV_BOUND_EXCEEDED);
-      } else {
-        dense_task<G, T, PROBS, false>(p, c, id, 0, kW, task * kW, aq, plds, wo);
+    if (q0 < c.nq) {
+      if (c.nf != MF) {
+#pragma unroll
+        for (int i = 0; i < kQW; ++i) sid[i] = res[min(c.nf + q0 + i, p.NW - 1)];
       }
+      int ids[kQW];
+      bool ok[kQW];
+      bool bad = false;
+#pragma unroll
+      for (int i = 0; i < kQW; ++i) {
+        const bool in_range = unsigned(sid[i]) < unsigned(p.NW);
+        ok[i] = q0 + i < c.nq && in_range;
+        bad |= q0 + i < c.nq && !in_range;
+        ids[i] = ok[i] ? sid[i] : 0;
+      }
+      if (bad && lane == 0) atomicOr(p.status, KVC_DEV_BOUND_EXCEEDED);
+      int2_task<G, T, PROBS>(p, c, ids, ok, (c.nf + q0) * kW, aq, plds, meta_all[wave], wo);
     }
-  } else if (task < t_int2) {
+  } else if (task < t_full) {
     const int blk = task - t_tail;
     if (kW * blk < c.total_tail) {
       dense_task<G, T, PROBS, true>(p, c, 0, blk, min(kW, c.total_tail - kW * blk), (c.nf + c.nq + blk) * kW, aq,
                                     plds, wo);
     }
-  } else if (task < t_end && q0 < c.nq) {
-    if (c.nf != MF) {
-#pragma unroll
-      for (int i = 0; i < kQW; ++i) sid[i] = res[min(c.nf + q0 + i, p.NW - 1)];
+  } else if (task < t_end && f < c.nf) {
+    const int id = sid[0];
+    if (unsigned(id) >= unsigned(p.NW)) {
+      if (lane == 0) atomicOr(p.status, KVC_DEV_BOUND_EXCEEDED);
+    } else {
+      dense_task<G, T, PROBS, false>(p, c, id, 0, kW, f * kW, aq, plds, wo);
     }
-    int ids[kQW];
-    bool ok[kQW];
-    bool bad = false;
-#pragma unroll
-    for (int i = 0; i < kQW; ++i) {
-      const bool in_range = unsigned(sid[i]) < unsigned(p.NW);
-      ok[i] = q0 + i < c.nq && in_range;
-      bad |= q0 + i < c.nq && !in_range;
-      ids[i] = ok[i] ? sid[i] : 0;
-    }
-    if (bad && lane == 0) atomicOr(p.status, KVC_DEV_BOUND_EXCEEDED);
-    int2_task<G, T, PROBS>(p, c, ids, ok, (c.nf + q0) * kW, aq, plds, meta_all[wave], wo);
   }
 
   // ---- wave result: O[h][d] = acc(col h) + acc(col h + G) + bias(group of d); merged over the 4 waves ----
@@ -577,7 +571,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float lo = __shfl_down(wo.acc[dt][r], G, kWave);
+      const float lo = dpp_f<0x100 + G>(wo.acc[dt][r]);  // column col + G of the same row
       if (c.col < G) sm_o[wave][c.col][16 * dt + 4 * c.q + r] = wo.acc[dt][r] + lo + wo.bias[dt >> 1];
     }
   }
@@ -616,10 +610,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   }
 }
 
-// Combine: p.CB workgroups per unit. Each merges the unit's partials into the per-head (M, 1/L) (one pass, fixed
-// order), then handles its slice of the outputs, windows and probabilities. The window loads are issued before
-// the partials are read.
-constexpr int kFChunk = 1024;
+// Combine: p.CB workgroups per unit; workgroup b owns E = G*D/CB output elements (thread (e, pg): element e,
+// partials pg, pg + PG, ... with PG = 256/E, at most kPre of them per thread in the usual case) and a contiguous
+// range of the unit's windows. Every load that does not depend on the merged (M, L) — the partial outputs and
+// maxima of this thread, its windows' exp-sums, tiers and scores — is issued first; then each workgroup merges
+// the partials' (m, l) per head (one pass, fixed order), weights and sums its outputs in a fixed order (bitwise
+// reproducible), and turns its windows' exp-sums into probability mass.
+constexpr int kPre = 8;
 
 template <int G>
 __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
@@ -628,12 +625,27 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
   const int CH = p.P;
+  const int E = G * kD / p.CB;
+  const int PG = 256 / E;
+  const int e = threadIdx.x % E, pg = threadIdx.x / E;
+  const int idx = b * E + e;
+  const int h_out = idx / kD;
   const size_t unit_win = size_t(u) * p.NW;
   const int nw = min(max(p.n_windows[u], 0), p.NW);
-  const int wstride = 256 * p.CB;
+  const int wpb = (nw + p.CB - 1) / p.CB;
+  const int wb = b * wpb, we = min(nw, wb + wpb);
+  const float* ml = p.part_ml + size_t(u) * CH * G * 2;
+  const float* po = p.part_o + size_t(u) * CH * G * kD + idx;
 
-  // first window of this thread: loads in flight while the partials are merged
-  const int w0 = b * 256 + threadIdx.x;
+  float ov[kPre], mv[kPre];
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) {
+    const int cc = pg + k * PG;
+    const bool in = p.out != nullptr && cc < CH;
+    ov[k] = in ? po[size_t(cc) * G * kD] : 0.0f;
+    mv[k] = in ? ml[(cc * G + h_out) * 2] : -INFINITY;
+  }
+  const int w0 = wb + int(threadIdx.x);
   bool res0 = false;
   float ws0[G], wr0[G], cum0 = 0.0f;
 #pragma unroll
@@ -641,7 +653,7 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
     ws0[h] = 0.0f;
     wr0[h] = -INFINITY;
   }
-  if (w0 < nw) {
+  if (w0 < we) {
     res0 = p.tier[unit_win + w0] != KVC_TIER_EVICTED;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -652,9 +664,7 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
   }
 
   __shared__ float sM[G], sInvL[G];
-  __shared__ float f[kFChunk][G];
   __shared__ float red[256];
-  const float* ml = p.part_ml + size_t(u) * CH * G * 2;
   for (int h = wave; h < G; h += 4) {
     float mr = -INFINITY, lr = 0.0f;
     for (int cc = lane; cc < CH; cc += kWave) {
@@ -673,36 +683,21 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
   __syncthreads();
 
   if (p.out != nullptr) {
-    const int E = G * kD / p.CB;  // output elements of this block (a power of two, <= 256)
-    const int PG = 256 / E;       // partial groups
-    const int e = threadIdx.x % E, pg = threadIdx.x / E;
-    const int idx = b * E + e;
-    const int h = idx / kD;
-    const float* po = p.part_o + size_t(u) * CH * G * kD;
+    const float Mh = sM[h_out], iL = sInvL[h_out];
     float acc = 0.0f;
-    for (int c0 = 0; c0 < CH; c0 += kFChunk) {
-      const int cn = min(kFChunk, CH - c0);
-      for (int i = threadIdx.x; i < cn * G; i += 256) {
-        const int cc = i / G, hh = i - cc * G;
-        f[cc][hh] = exp_diff(ml[((c0 + cc) * G + hh) * 2], sM[hh]) * sInvL[hh];
-      }
-      __syncthreads();
-      float a = 0.0f;
-#pragma unroll 4
-      for (int cc = pg; cc < cn; cc += PG) a += po[size_t(c0 + cc) * G * kD + idx] * f[cc][h];
-      acc += a;
-      __syncthreads();
-    }
-    red[threadIdx.x] = acc;
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) acc += ov[k] * exp_diff(mv[k], Mh);
+    for (int cc = pg + kPre * PG; cc < CH; cc += PG) acc += po[size_t(cc) * G * kD] * exp_diff(ml[(cc * G + h_out) * 2], Mh);
+    red[threadIdx.x] = acc * iL;
     __syncthreads();
-    if (threadIdx.x < E) {
+    if (int(threadIdx.x) < E) {
       float o = 0.0f;
       for (int g2 = 0; g2 < PG; ++g2) o += red[g2 * E + threadIdx.x];
       p.out[size_t(u) * G * kD + idx] = o;
     }
   }
   // window mass = (1/G) sum_h wsum * exp(wref - M_h) / L_h; cumulative score += mass
-  for (int w = w0; w < nw; w += wstride) {
+  for (int w = w0; w < we; w += 256) {
     bool resident = res0;
     float cw = cum0;
     if (w != w0) {
@@ -730,7 +725,7 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
     const int n_res = (nf + nq) * kW + tl + has_new;
     for (int h = 0; h < G; ++h) {
       float* pr = p.probs + (size_t(u) * G + h) * p.probs_stride;
-      for (int i = b * 256 + threadIdx.x; i < n_res; i += wstride) pr[i] = exp_diff(pr[i], sM[h]) * sInvL[h];
+      for (int i = b * 256 + threadIdx.x; i < n_res; i += 256 * p.CB) pr[i] = exp_diff(pr[i], sM[h]) * sInvL[h];
     }
   }
   if (b == 0 && has_new) {
@@ -774,10 +769,12 @@ TaskCounts task_counts(const kvc_decode_args& a) {
   return t;
 }
 
-int combine_blocks(const kvc_cache& c) {
-  // the output slice of a combine workgroup (G*D/CB elements) must fit its 256 threads
-  const int min_cb = c.group > 2 ? c.group / 2 : 1;
-  return c.n_units >= 256 ? min_cb : 8;
+int combine_blocks(const kvc_cache& c, int P) {
+  // partial groups so that a thread holds at most kPre partials, output elements E = 256 / PG (at most G*D)
+  int pg = 1;
+  while (pg < 256 && pg * kPre < P) pg *= 2;
+  const int E = min(256 / pg, c.group * kD);
+  return c.group * kD / E;
 }
 
 }  // namespace
@@ -834,7 +831,7 @@ hipError_t launch_decode(const kvc_cache& c, const kvc_decode_args& a, void* ws,
   p.n_tb = tc.n_tb;
   p.n_qt = tc.n_qt;
   p.P = decode_slices(c, a);
-  p.CB = combine_blocks(c);
+  p.CB = combine_blocks(c, p.P);
   if (p.P > kMaxParts) return hipErrorInvalidValue;
   const size_t U = size_t(c.n_units), G = size_t(c.group), P = size_t(p.P);
   char* w = static_cast<char*>(ws);
