@@ -169,8 +169,76 @@ typedef struct kvc_tier_route_args {
 } kvc_tier_route_args;
 
 /* Modes of kvc_score / kvc_route. */
-#define KVC_SCORE_WINDOWS 0  /* args: const kvc_window_score_args* */
-#define KVC_ROUTE_TIERS 0    /* args: const kvc_tier_route_args*   */
+#define KVC_SCORE_WINDOWS 0      /* args: const kvc_window_score_args* */
+#define KVC_SCORE_RETENTION 1    /* args: const kvc_retention_args*    */
+#define KVC_ROUTE_TIERS 0        /* args: const kvc_tier_route_args*   */
+#define KVC_ROUTE_GLOBAL_TOPM 1  /* args: const kvc_topm_args*         */
+
+/* kvc_score(KVC_SCORE_RETENTION): DBTrimKV retention score (DBTrimKV page, "Metodologia: Evicção Baseada em
+ * Retenção Global", section 2: token i's retention weight at step t is beta_i^(t - i)). Written as its logarithm,
+ *   score[r][i] = float(t - i) * logf(beta[r][i])      (fp32; the order is that of beta^(t - i))
+ * because the power underflows to 0 for most entries of long contexts. Rows r are (layer, KV head) pairs.
+ *   beta   [n_rows][n_tokens] float in (0, 1), 16-byte aligned;  score [n_rows][n_tokens] float, 16-byte aligned.
+ *   n_tokens % 4 == 0, n_rows * n_tokens < 2^31. No workspace. */
+typedef struct kvc_retention_args {
+  const float* beta;
+  float* score;
+  int64_t n_rows;
+  int32_t n_tokens;
+  int32_t t;
+} kvc_retention_args;
+
+/* kvc_route(KVC_ROUTE_GLOBAL_TOPM): one global budget (DBTrimKV page, "Metodologia", section 3: every entry of
+ * every layer and head is ranked on one scale and the top M are kept). The kept set is the first m entries in
+ * the order (score desc, flat index asc), so it is unique.
+ *   scores     [n] float, finite, 16-byte aligned; rows of row_len entries (row_len % 16 == 0, n % row_len == 0,
+ *              n < 2^31); 0 <= m <= n.
+ *   keep       [n] uint8 out, 1 = kept (16-byte aligned);  row_counts [n / row_len] int32 out: kept per row.
+ *   status     int32 device error bits (KVC_DEV_NAN_SCORE: a NaN score was seen; the result is then undefined).
+ * Workspace: kvc_route_workspace(KVC_ROUTE_GLOBAL_TOPM, args) bytes, any contents. */
+typedef struct kvc_topm_args {
+  const float* scores;
+  int64_t n;
+  int64_t m;
+  int32_t row_len;
+  int32_t reserved;
+  uint8_t* keep;
+  int32_t* row_counts;
+  int32_t* status;
+} kvc_topm_args;
+
+/* kvc_compact_pages: per-row variable-length paged lists (DBTrimKV page, "Metodologia", section 4: paged
+ * storage lets every head keep a sequence of its own length). Out of place: for every row r (a (layer, KV head)
+ * pair) the kept positions, ascending, are copied into fresh pages of `page` rows; row r owns output pages
+ * page_offset[r] .. page_offset[r] + n_pages[r] - 1 (consecutive, rows in order), its last page's unused rows
+ * are zeroed.
+ *   keep        [n_rows][n_tokens] uint8 (0/1), 16-byte aligned; n_tokens % 16 == 0, n_tokens % page == 0.
+ *   page_table  [n_rows][n_tokens / page] int32: source page id of each block of `page` positions.
+ *   k_pool, v_pool  [n_src_pages][page][head_dim] storage dtype (fp16/bf16), head_dim == 128.
+ *   k_out, v_out    [out_pages_max][page][head_dim] storage dtype out.
+ *   lengths, page_offset, n_pages   [n_rows] int32 out.
+ *   status      int32 device error bits: KVC_DEV_BOUND_EXCEEDED if the pages exceed out_pages_max (the excess is
+ *               not written) or a page id is outside [0, n_src_pages) (that row is not copied).
+ * Workspace: kvc_compact_pages_workspace(args) bytes, any contents. */
+typedef struct kvc_compact_args {
+  const uint8_t* keep;
+  const int32_t* page_table;
+  const void* k_pool;
+  const void* v_pool;
+  void* k_out;
+  void* v_out;
+  int32_t* lengths;
+  int32_t* page_offset;
+  int32_t* n_pages;
+  int32_t* status;
+  int64_t n_rows;
+  int64_t n_src_pages;
+  int64_t out_pages_max;
+  int32_t n_tokens;
+  int32_t page;
+  int32_t head_dim;
+  int32_t kv_dtype;
+} kvc_compact_args;
 
 /* kvc_score(KVC_SCORE_WINDOWS): the scoring half of a decode step — the same kernels as kvc_decode_attn with
  * out = NULL: probabilities, window mass and the cumulative score update over the mixed cache. */
@@ -215,6 +283,9 @@ int kvc_quantize_int2(const kvc_cache* cache, const int32_t* list, const int32_t
  * conventions as kvc_quantize_int2. */
 int kvc_promote(const kvc_cache* cache, const int32_t* list, const int32_t* count, int32_t list_stride,
                 int64_t max_total, hipStream_t stream);
+
+size_t kvc_compact_pages_workspace(const kvc_compact_args* args);
+int kvc_compact_pages(const kvc_compact_args* args, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Reads *cache->status into *host_status (synchronises the stream) and, if clear != 0, zeroes it. */
 int kvc_read_device_status(const kvc_cache* cache, int32_t* host_status, int32_t clear, hipStream_t stream);

@@ -16,8 +16,8 @@ KVC_OK, KVC_E_INVALID, KVC_E_UNSUPPORTED, KVC_E_WORKSPACE, KVC_E_LEDGER, KVC_E_B
 KVC_DEV_LEDGER_REWRITE, KVC_DEV_BOUND_EXCEEDED, KVC_DEV_NAN_SCORE = 0x1, 0x2, 0x4
 KVC_F16, KVC_BF16 = 0, 1
 TIER_FULL, TIER_INT2, TIER_EVICTED = 0, 1, 2
-KVC_SCORE_WINDOWS = 0
-KVC_ROUTE_TIERS = 0
+KVC_SCORE_WINDOWS, KVC_SCORE_RETENTION = 0, 1
+KVC_ROUTE_TIERS, KVC_ROUTE_GLOBAL_TOPM = 0, 1
 
 P = C.c_void_p
 
@@ -53,6 +53,22 @@ class KvcWindowScoreArgs(C.Structure):
     _fields_ = [("cache", C.POINTER(KvcCache)), ("step", C.POINTER(KvcDecodeArgs))]
 
 
+class KvcRetentionArgs(C.Structure):
+    _fields_ = [("beta", P), ("score", P), ("n_rows", C.c_int64), ("n_tokens", C.c_int32), ("t", C.c_int32)]
+
+
+class KvcTopmArgs(C.Structure):
+    _fields_ = [("scores", P), ("n", C.c_int64), ("m", C.c_int64), ("row_len", C.c_int32), ("reserved", C.c_int32),
+                ("keep", P), ("row_counts", P), ("status", P)]
+
+
+class KvcCompactArgs(C.Structure):
+    _fields_ = [("keep", P), ("page_table", P), ("k_pool", P), ("v_pool", P), ("k_out", P), ("v_out", P),
+                ("lengths", P), ("page_offset", P), ("n_pages", P), ("status", P), ("n_rows", C.c_int64),
+                ("n_src_pages", C.c_int64), ("out_pages_max", C.c_int64), ("n_tokens", C.c_int32),
+                ("page", C.c_int32), ("head_dim", C.c_int32), ("kv_dtype", C.c_int32)]
+
+
 # name -> (restype, argtypes); every symbol include/kvc.h declares
 SIGNATURES = {
     "kvc_abi_version": (C.c_int, []),
@@ -66,6 +82,8 @@ SIGNATURES = {
     "kvc_quantize_int2": (C.c_int, [C.POINTER(KvcCache), P, P, C.c_int32, C.c_int64, P]),
     "kvc_promote": (C.c_int, [C.POINTER(KvcCache), P, P, C.c_int32, C.c_int64, P]),
     "kvc_read_device_status": (C.c_int, [C.POINTER(KvcCache), C.POINTER(C.c_int32), C.c_int32, P]),
+    "kvc_compact_pages_workspace": (C.c_size_t, [C.POINTER(KvcCompactArgs)]),
+    "kvc_compact_pages": (C.c_int, [C.POINTER(KvcCompactArgs), P, C.c_size_t, P]),
 }
 
 

@@ -66,6 +66,46 @@ int check_list(const kvc_cache* c, const int32_t* list, const int32_t* count, in
   return KVC_OK;
 }
 
+int check_retention(const kvc_retention_args* a) {
+  if (a == nullptr || a->beta == nullptr || a->score == nullptr) return KVC_E_INVALID;
+  if (!aligned(a->beta, 16) || !aligned(a->score, 16)) return KVC_E_INVALID;
+  if (a->n_rows < 0 || a->n_tokens <= 0 || a->n_tokens % 4 != 0) return KVC_E_INVALID;
+  if (a->n_rows * int64_t(a->n_tokens) >= (int64_t(1) << 31)) return KVC_E_UNSUPPORTED;
+  return KVC_OK;
+}
+
+int check_topm(const kvc_topm_args* a) {
+  if (a == nullptr || a->scores == nullptr || a->keep == nullptr || a->row_counts == nullptr ||
+      a->status == nullptr || a->reserved != 0) {
+    return KVC_E_INVALID;
+  }
+  if (!aligned(a->scores, 16) || !aligned(a->keep, 16) || !aligned(a->row_counts, 4) || !aligned(a->status, 4)) {
+    return KVC_E_INVALID;
+  }
+  if (a->row_len <= 0 || a->row_len % 16 != 0 || a->n < 0 || a->n % a->row_len != 0) return KVC_E_INVALID;
+  if (a->n >= (int64_t(1) << 31)) return KVC_E_UNSUPPORTED;
+  if (a->m < 0 || a->m > a->n) return KVC_E_BUDGET;
+  return KVC_OK;
+}
+
+int check_compact(const kvc_compact_args* a) {
+  if (a == nullptr) return KVC_E_INVALID;
+  const void* need16[] = {a->keep, a->k_pool, a->v_pool, a->k_out, a->v_out};
+  for (const void* p : need16) {
+    if (p == nullptr || !aligned(p, 16)) return KVC_E_INVALID;
+  }
+  const void* need4[] = {a->page_table, a->lengths, a->page_offset, a->n_pages, a->status};
+  for (const void* p : need4) {
+    if (p == nullptr || !aligned(p, 4)) return KVC_E_INVALID;
+  }
+  if (a->head_dim != kvc::kD) return KVC_E_UNSUPPORTED;
+  if (a->kv_dtype != KVC_F16 && a->kv_dtype != KVC_BF16) return KVC_E_UNSUPPORTED;
+  if (a->page <= 0 || a->n_tokens <= 0 || a->n_tokens % 16 != 0 || a->n_tokens % a->page != 0) return KVC_E_INVALID;
+  if (a->n_rows < 0 || a->n_src_pages < 0 || a->out_pages_max < 0) return KVC_E_INVALID;
+  if (a->n_rows * int64_t(a->n_tokens) >= (int64_t(1) << 31) || a->n_rows > 65535) return KVC_E_UNSUPPORTED;
+  return KVC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -103,7 +143,7 @@ size_t kvc_score_workspace(int32_t mode, const void* args) {
     const kvc_window_score_args* a = static_cast<const kvc_window_score_args*>(args);
     return kvc_decode_attn_workspace(a->cache, a->step);
   }
-  return 0;
+  return 0;  // KVC_SCORE_RETENTION needs none
 }
 
 int kvc_score(int32_t mode, const void* args, void* workspace, size_t workspace_bytes, hipStream_t stream) {
@@ -116,18 +156,25 @@ int kvc_score(int32_t mode, const void* args, void* workspace, size_t workspace_
     step.out = nullptr;
     return run_decode(a->cache, &step, workspace, workspace_bytes, stream);
   }
+  if (mode == KVC_SCORE_RETENTION) {
+    const kvc_retention_args* a = static_cast<const kvc_retention_args*>(args);
+    const int st = check_retention(a);
+    if (st != KVC_OK) return st;
+    return kvc::launch_retention_score(*a, stream) == hipSuccess ? KVC_OK : KVC_E_HIP;
+  }
   return KVC_E_UNSUPPORTED;
 }
 
 size_t kvc_route_workspace(int32_t mode, const void* args) {
-  (void)args;
-  (void)mode;
+  if (mode == KVC_ROUTE_GLOBAL_TOPM) {
+    const kvc_topm_args* a = static_cast<const kvc_topm_args*>(args);
+    if (check_topm(a) != KVC_OK) return 0;
+    return kvc::topm_workspace_bytes(*a);
+  }
   return 0;
 }
 
 int kvc_route(int32_t mode, const void* args, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (args == nullptr) return KVC_E_INVALID;
   if (mode == KVC_ROUTE_TIERS) {
     const kvc_tier_route_args* a = static_cast<const kvc_tier_route_args*>(args);
@@ -140,7 +187,31 @@ int kvc_route(int32_t mode, const void* args, void* workspace, size_t workspace_
     if (a->scores != nullptr && !aligned(a->scores, 4)) return KVC_E_INVALID;
     return kvc::launch_route_tiers(*a, stream) == hipSuccess ? KVC_OK : KVC_E_HIP;
   }
+  if (mode == KVC_ROUTE_GLOBAL_TOPM) {
+    const kvc_topm_args* a = static_cast<const kvc_topm_args*>(args);
+    const int st = check_topm(a);
+    if (st != KVC_OK) return st;
+    if (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < kvc::topm_workspace_bytes(*a)) {
+      return KVC_E_WORKSPACE;
+    }
+    return kvc::launch_topm(*a, workspace, stream) == hipSuccess ? KVC_OK : KVC_E_HIP;
+  }
   return KVC_E_UNSUPPORTED;
+}
+
+size_t kvc_compact_pages_workspace(const kvc_compact_args* args) {
+  if (check_compact(args) != KVC_OK) return 0;
+  return kvc::compact_workspace_bytes(*args);
+}
+
+int kvc_compact_pages(const kvc_compact_args* args, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_compact(args);
+  if (st != KVC_OK) return st;
+  if (args->n_rows == 0) return KVC_OK;
+  if (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < kvc::compact_workspace_bytes(*args)) {
+    return KVC_E_WORKSPACE;
+  }
+  return kvc::launch_compact(*args, workspace, stream) == hipSuccess ? KVC_OK : KVC_E_HIP;
 }
 
 int kvc_quantize_int2(const kvc_cache* cache, const int32_t* list, const int32_t* count, int32_t list_stride,

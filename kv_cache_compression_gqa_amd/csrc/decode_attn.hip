@@ -39,7 +39,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlock = kWavesPerBlock * kWave;
-constexpr int kQW = 2;              // INT2 windows per wave task
+constexpr int kQW = 1;              // INT2 windows per wave task
 constexpr int kMaxParts = 16384;    // workgroups (partials) per unit
 constexpr int kMetaWords = kW * kGroups;  // scale/zero words per window and per K or V
 constexpr float kInvSqrtD = 0.088388347648318440550f;  // 1/sqrt(128)

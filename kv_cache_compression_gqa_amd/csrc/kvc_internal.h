@@ -107,4 +107,10 @@ hipError_t launch_quantize(const kvc_cache& c, const int32_t* list, const int32_
 hipError_t launch_promote(const kvc_cache& c, const int32_t* list, const int32_t* count, int32_t stride,
                           int64_t max_total, hipStream_t s);
 
+hipError_t launch_retention_score(const kvc_retention_args& a, hipStream_t s);
+size_t topm_workspace_bytes(const kvc_topm_args& a);
+hipError_t launch_topm(const kvc_topm_args& a, void* ws, hipStream_t s);
+size_t compact_workspace_bytes(const kvc_compact_args& a);
+hipError_t launch_compact(const kvc_compact_args& a, void* ws, hipStream_t s);
+
 }  // namespace kvc

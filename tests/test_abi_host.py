@@ -109,3 +109,42 @@ def test_route_and_list_validation():
     # nothing to do is accepted without touching the device
     assert L.kvc_quantize_int2(C.byref(c), None, None, 32, 0, None) == abi.KVC_OK
     assert L.kvc_score(5, C.byref(ra), None, 0, None) == abi.KVC_E_UNSUPPORTED
+
+
+def _status_of(fn, *args):
+    return fn(*args)
+
+
+def test_retention_topm_compact_validation_rejects_before_launch():
+    L = abi.lib()
+    # retention score: n_tokens must be a multiple of 4
+    a = abi.KvcRetentionArgs(beta=FAKE, score=FAKE, n_rows=4, n_tokens=6, t=6)
+    assert L.kvc_score(abi.KVC_SCORE_RETENTION, C.cast(C.byref(a), C.c_void_p), None, 0, None) == abi.KVC_E_INVALID
+    a = abi.KvcRetentionArgs(beta=FAKE + 4, score=FAKE, n_rows=4, n_tokens=8, t=8)
+    assert L.kvc_score(abi.KVC_SCORE_RETENTION, C.cast(C.byref(a), C.c_void_p), None, 0, None) == abi.KVC_E_INVALID
+    # top-M: m outside [0, n], row length not a multiple of 16, missing workspace
+    def topm(**over):
+        kw = dict(scores=FAKE, n=64, m=8, row_len=32, reserved=0, keep=FAKE, row_counts=FAKE, status=FAKE)
+        kw.update(over)
+        t = abi.KvcTopmArgs(**kw)
+        return L.kvc_route(abi.KVC_ROUTE_GLOBAL_TOPM, C.cast(C.byref(t), C.c_void_p), None, 0, None), t
+    assert topm(m=65)[0] == abi.KVC_E_BUDGET
+    assert topm(m=-1)[0] == abi.KVC_E_BUDGET
+    assert topm(row_len=24, n=48)[0] == abi.KVC_E_INVALID
+    assert topm(n=50)[0] == abi.KVC_E_INVALID
+    assert topm()[0] == abi.KVC_E_WORKSPACE
+    st, t = topm()
+    assert L.kvc_route_workspace(abi.KVC_ROUTE_GLOBAL_TOPM, C.cast(C.byref(t), C.c_void_p)) > 0
+    # compaction: head_dim other than 128, page not dividing the row, missing workspace
+    def compact(**over):
+        kw = dict(keep=FAKE, page_table=FAKE, k_pool=FAKE, v_pool=FAKE, k_out=FAKE, v_out=FAKE, lengths=FAKE,
+                  page_offset=FAKE, n_pages=FAKE, status=FAKE, n_rows=4, n_src_pages=16, out_pages_max=16,
+                  n_tokens=64, page=16, head_dim=128, kv_dtype=abi.KVC_BF16)
+        kw.update(over)
+        c = abi.KvcCompactArgs(**kw)
+        return L.kvc_compact_pages(C.byref(c), None, 0, None), c
+    assert compact(head_dim=64)[0] == abi.KVC_E_UNSUPPORTED
+    assert compact(page=24)[0] == abi.KVC_E_INVALID
+    assert compact(kv_dtype=7)[0] == abi.KVC_E_UNSUPPORTED
+    assert compact()[0] == abi.KVC_E_WORKSPACE
+    assert L.kvc_compact_pages_workspace(C.byref(compact()[1])) > 0

@@ -1,0 +1,134 @@
+"""GPU parity of the global retention path (log-retention score, global top-M, per-row paged compaction) against
+the CPU oracle, through the C ABI.
+
+Bars: scores within 2e-3 relative of the fp64 oracle; the keep mask bit-exact against the oracle's top-M fed the
+GPU's fp32 scores (ties to the lower flat index); row counts, lengths and page offsets exact; every output row
+byte-equal to its source pool row, unused rows of a last page zero."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from kv_cache_compression_gqa_amd import abi, configs, synth
+from oracle import dbtrim, select
+from tests.decode_parity import rel_check
+
+pytestmark = pytest.mark.gpu
+
+RTOL = 2e-3
+
+
+def _run_scores_topm(beta_np, t, m):
+    import torch
+    from kv_cache_compression_gqa_amd import retention
+    beta = torch.from_numpy(beta_np).cuda()
+    sc = retention.retention_scores(beta, t)
+    tm = retention.global_topm(sc, m)
+    torch.cuda.synchronize()
+    return sc, tm
+
+
+def _check_topm(sc_gpu, tm, m):
+    s = sc_gpu.cpu().numpy().astype(np.float64)
+    keep_ref = select.global_topm(s.reshape(-1), m).reshape(s.shape)
+    keep = tm.keep.cpu().numpy().astype(bool)
+    assert int(tm.status.item()) == 0
+    mism = np.argwhere(keep != keep_ref)
+    assert mism.size == 0, f"keep mask differs at {mism.shape[0]} entries, first {tuple(mism[0])}"
+    np.testing.assert_array_equal(tm.row_counts.cpu().numpy(), keep_ref.sum(axis=1))
+    return keep_ref
+
+
+def _pools(n_src_pages, page, D, seed_k, seed_v, dtype):
+    """K/V pools on the GPU: row r is row (r * 40503 + 17) mod 65536 of a seeded table (the generator's rule)."""
+    import torch
+    tk = torch.from_numpy(synth.pool_table_bits(D, seed_k, dtype).view(np.int16)).cuda()
+    tv = torch.from_numpy(synth.pool_table_bits(D, seed_v, dtype).view(np.int16)).cuda()
+    rows = torch.arange(n_src_pages * page, device="cuda", dtype=torch.int64)
+    idx = (rows * 40503 + 17) % tk.shape[0]
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    k = tk[idx].view(tdt).view(n_src_pages, page, D)
+    v = tv[idx].view(tdt).view(n_src_pages, page, D)
+    return k, v
+
+
+def _check_compaction(keep, pt_np, cfg, L, T):
+    import torch
+    from kv_cache_compression_gqa_amd import retention
+    rows = keep.shape[0]
+    page, D = cfg.page, cfg.head_dim
+    n_src = L * cfg.hkv * (T // page)
+    k_pool, v_pool = _pools(n_src, page, D, cfg.seed * 7 + 1, cfg.seed * 7 + 2, cfg.dtype)
+    src, lengths, page_offset, n_pages = dbtrim.compact_rows(keep.reshape(L, cfg.hkv, T), pt_np, page)
+    total = int(n_pages.sum())
+    keep_t = torch.from_numpy(keep.astype(np.uint8)).cuda()
+    pt = torch.from_numpy(pt_np.reshape(rows, T // page).astype(np.int32)).cuda()
+    dt = abi.KVC_BF16 if cfg.dtype == "bf16" else abi.KVC_F16
+    out = retention.compact_pages(keep_t, pt, k_pool, v_pool, out_pages_max=total + 3, kv_dtype=dt)
+    torch.cuda.synchronize()
+    assert int(out.status.item()) == 0
+    np.testing.assert_array_equal(out.lengths.cpu().numpy(), lengths)
+    np.testing.assert_array_equal(out.page_offset.cpu().numpy(), page_offset)
+    np.testing.assert_array_equal(out.n_pages.cpu().numpy(), n_pages)
+    src_t = torch.from_numpy(src).cuda()
+    live = src_t >= 0
+    for name, pool, got in (("K", k_pool, out.k), ("V", v_pool, out.v)):
+        g = got.view(torch.int16).reshape(-1, D)[: total * page]
+        exp = pool.view(torch.int16).reshape(-1, D)[src_t.clamp(min=0)]
+        exp[~live] = 0
+        bad = (g != exp).any(dim=1)
+        assert not bool(bad.any()), f"{name}: {int(bad.sum())} output rows differ, first {int(bad.nonzero()[0])}"
+
+
+@pytest.mark.parametrize("layers,T", [(2, 2048), (1, 4112)])
+def test_retention_small(gpu_lib, layers, T):
+    cfg = configs.DBTRIM_128K
+    beta = synth.make_retention_beta(cfg, layers=layers, n_tokens=T).reshape(layers * cfg.hkv, T)
+    t = T
+    m = int(np.floor(cfg.keep_frac * beta.size))
+    sc, tm = _run_scores_topm(beta, t, m)
+    ref = dbtrim.log_retention(beta[None], t)[0]
+    rel_check("retention score", sc.cpu().numpy(), ref, rtol=RTOL)
+    keep = _check_topm(sc, tm, m)
+    pt = synth.make_page_table(cfg, layers=layers, n_tokens=T)
+    _check_compaction(keep, pt, cfg, layers, T)
+
+
+@pytest.mark.parametrize("m_kind", ["zero", "one", "ties", "all"])
+def test_topm_edge_cases_and_ties(gpu_lib, m_kind):
+    """Scores on a coarse grid so that thousands of entries tie across many blocks; m cuts inside a tie group."""
+    import torch
+    from kv_cache_compression_gqa_amd import retention
+    rng = np.random.default_rng(11)
+    rows, row_len = 12, 40960
+    s = (np.round(rng.standard_normal((rows, row_len)) * 3.0) / 3.0).astype(np.float32)
+    s[3, 100:200] = 0.0
+    s[4, 50:80] = -0.0
+    n = s.size
+    order = select.rank_order(s.reshape(-1).astype(np.float64))
+    m = {"zero": 0, "one": 1, "all": n}.get(m_kind)
+    if m is None:
+        key = s.reshape(-1)[order]
+        m = int(n * 0.37)
+        assert key[m - 1] == key[m]  # the cut falls inside a tie group
+    tm = retention.global_topm(torch.from_numpy(s).cuda(), m)
+    torch.cuda.synchronize()
+    _check_topm(torch.from_numpy(s), tm, m)
+
+
+def test_retention_full_size(gpu_lib):
+    """32 layers x 8 KV heads x 131072 tokens, M = 10%: every score, the whole keep mask and every copied row."""
+    import torch
+    cfg = configs.DBTRIM_128K
+    L, H, T = cfg.layers, cfg.hkv, cfg.n_tokens
+    print(f"full-size retention: {L}x{H}x{T}, M={cfg.keep}", flush=True)
+    beta = synth.make_retention_beta(cfg).reshape(L * H, T)
+    sc, tm = _run_scores_topm(beta, cfg.t, cfg.keep)
+    ref = dbtrim.log_retention(beta[None], cfg.t)[0]
+    g = sc.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(g - ref) <= RTOL * np.abs(ref) + 1e-12)
+    keep = _check_topm(sc, tm, cfg.keep)
+    assert int(keep.sum()) == cfg.keep
+    pt = synth.make_page_table(cfg)
+    _check_compaction(keep, pt, cfg, L, T)
+    torch.cuda.empty_cache()
