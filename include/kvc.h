@@ -171,8 +171,58 @@ typedef struct kvc_tier_route_args {
 /* Modes of kvc_score / kvc_route. */
 #define KVC_SCORE_WINDOWS 0      /* args: const kvc_window_score_args* */
 #define KVC_SCORE_RETENTION 1    /* args: const kvc_retention_args*    */
+#define KVC_SCORE_CRITICALKV 2   /* args: const kvc_criticalkv_args*   */
 #define KVC_ROUTE_TIERS 0        /* args: const kvc_tier_route_args*   */
 #define KVC_ROUTE_GLOBAL_TOPM 1  /* args: const kvc_topm_args*         */
+#define KVC_ROUTE_TWO_STAGE 2    /* args: const kvc_two_stage_args*    */
+
+/* kvc_score(KVC_SCORE_CRITICALKV): CriticalKV scores of one layer at prefill (CriticalKV page, "Framework
+ * Teórico": the output perturbation is bounded through the attention weights and the values projected by W_O;
+ * "Algoritmo: Seleção Constrainda por Perturbação": attention weights from the observation window, second-stage
+ * score A_i * |V_i W_O|_1 with the projected values). For KV head g and each query head h of its group:
+ *   A_{h,i}  = (1/n_obs) sum_j softmax_i(q_{h,j} . k_{g,i} / sqrt(D)), query j at position n_keys - n_obs + j
+ *              seeing keys 0 .. n_keys - n_obs + j (causal);
+ *   N_{h,i}  = sum_c | sum_d V[g][i][d] * W_O[h*D + d][c] |   (fp32 accumulate);
+ *   A_g[i]   = mean_h A_{h,i};   S2_g[i] = mean_h A_{h,i} * N_{h,i}.
+ *   q_obs [hq][n_obs][D], k, v [hkv][n_keys][D], w_o [hq*D][d_model] row-major: storage dtype, 16-byte aligned.
+ *   a_head, norm [hq][n_keys] float out; a_group, s2_group [hkv][n_keys] float out.
+ *   Requires n_obs == 32, D == 128, hq / hkv in {1, 2, 4, 8}, d_model % 64 == 0, n_keys >= 32.
+ * Workspace: kvc_score_workspace(KVC_SCORE_CRITICALKV, args) bytes, any contents. */
+typedef struct kvc_criticalkv_args {
+  const void* q_obs;
+  const void* k;
+  const void* v;
+  const void* w_o;
+  float* a_head;
+  float* norm;
+  float* a_group;
+  float* s2_group;
+  int32_t n_keys;
+  int32_t hq;
+  int32_t hkv;
+  int32_t n_obs;
+  int32_t head_dim;
+  int32_t d_model;
+  int32_t kv_dtype;
+  int32_t reserved;
+} kvc_criticalkv_args;
+
+/* kvc_route(KVC_ROUTE_TWO_STAGE): CriticalKV's two-stage budgeted selection (CriticalKV page, "Algoritmo:
+ * Seleção Constrainda por Perturbação"), per row (KV head): the first budget1 entries in (a desc, index asc)
+ * order, then the first budget - budget1 of the remaining entries in (s2 desc, index asc) order; the union is
+ * written ascending.
+ *   a, s2  [rows][n] float (finite);  idx [rows][budget] int32 out.  0 <= budget1 <= budget <= n <= 65536.
+ *   budget1 = floor(alpha * budget) is the caller's (an integer, so no float rounding is left to the library).
+ * No workspace. */
+typedef struct kvc_two_stage_args {
+  const float* a;
+  const float* s2;
+  int32_t* idx;
+  int32_t rows;
+  int32_t n;
+  int32_t budget;
+  int32_t budget1;
+} kvc_two_stage_args;
 
 /* kvc_score(KVC_SCORE_RETENTION): DBTrimKV retention score (DBTrimKV page, "Metodologia: Evicção Baseada em
  * Retenção Global", section 2: token i's retention weight at step t is beta_i^(t - i)). Written as its logarithm,

@@ -16,8 +16,8 @@ KVC_OK, KVC_E_INVALID, KVC_E_UNSUPPORTED, KVC_E_WORKSPACE, KVC_E_LEDGER, KVC_E_B
 KVC_DEV_LEDGER_REWRITE, KVC_DEV_BOUND_EXCEEDED, KVC_DEV_NAN_SCORE = 0x1, 0x2, 0x4
 KVC_F16, KVC_BF16 = 0, 1
 TIER_FULL, TIER_INT2, TIER_EVICTED = 0, 1, 2
-KVC_SCORE_WINDOWS, KVC_SCORE_RETENTION = 0, 1
-KVC_ROUTE_TIERS, KVC_ROUTE_GLOBAL_TOPM = 0, 1
+KVC_SCORE_WINDOWS, KVC_SCORE_RETENTION, KVC_SCORE_CRITICALKV = 0, 1, 2
+KVC_ROUTE_TIERS, KVC_ROUTE_GLOBAL_TOPM, KVC_ROUTE_TWO_STAGE = 0, 1, 2
 
 P = C.c_void_p
 
@@ -67,6 +67,17 @@ class KvcCompactArgs(C.Structure):
                 ("lengths", P), ("page_offset", P), ("n_pages", P), ("status", P), ("n_rows", C.c_int64),
                 ("n_src_pages", C.c_int64), ("out_pages_max", C.c_int64), ("n_tokens", C.c_int32),
                 ("page", C.c_int32), ("head_dim", C.c_int32), ("kv_dtype", C.c_int32)]
+
+
+class KvcCriticalKVArgs(C.Structure):
+    _fields_ = [("q_obs", P), ("k", P), ("v", P), ("w_o", P), ("a_head", P), ("norm", P), ("a_group", P),
+                ("s2_group", P), ("n_keys", C.c_int32), ("hq", C.c_int32), ("hkv", C.c_int32), ("n_obs", C.c_int32),
+                ("head_dim", C.c_int32), ("d_model", C.c_int32), ("kv_dtype", C.c_int32), ("reserved", C.c_int32)]
+
+
+class KvcTwoStageArgs(C.Structure):
+    _fields_ = [("a", P), ("s2", P), ("idx", P), ("rows", C.c_int32), ("n", C.c_int32), ("budget", C.c_int32),
+                ("budget1", C.c_int32)]
 
 
 # name -> (restype, argtypes); every symbol include/kvc.h declares

@@ -106,6 +106,27 @@ int check_compact(const kvc_compact_args* a) {
   return KVC_OK;
 }
 
+int check_criticalkv(const kvc_criticalkv_args* a) {
+  if (a == nullptr || a->reserved != 0) return KVC_E_INVALID;
+  const void* need16[] = {a->q_obs, a->k, a->v, a->w_o, a->a_head, a->norm, a->a_group, a->s2_group};
+  for (const void* p : need16) {
+    if (p == nullptr || !aligned(p, 16)) return KVC_E_INVALID;
+  }
+  if (a->kv_dtype != KVC_F16 && a->kv_dtype != KVC_BF16) return KVC_E_UNSUPPORTED;
+  if (a->n_keys <= 0 || a->hq <= 0 || a->hkv <= 0 || a->d_model <= 0) return KVC_E_INVALID;
+  if (!kvc::criticalkv_supported(*a)) return KVC_E_UNSUPPORTED;
+  return KVC_OK;
+}
+
+int check_two_stage(const kvc_two_stage_args* a) {
+  if (a == nullptr || a->a == nullptr || a->s2 == nullptr || a->idx == nullptr) return KVC_E_INVALID;
+  if (!aligned(a->a, 4) || !aligned(a->s2, 4) || !aligned(a->idx, 4)) return KVC_E_INVALID;
+  if (a->rows < 0 || a->n < 0) return KVC_E_INVALID;
+  if (a->n > 65536) return KVC_E_UNSUPPORTED;
+  if (a->budget < 0 || a->budget1 < 0 || a->budget1 > a->budget || a->budget > a->n) return KVC_E_BUDGET;
+  return KVC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -143,6 +164,11 @@ size_t kvc_score_workspace(int32_t mode, const void* args) {
     const kvc_window_score_args* a = static_cast<const kvc_window_score_args*>(args);
     return kvc_decode_attn_workspace(a->cache, a->step);
   }
+  if (mode == KVC_SCORE_CRITICALKV) {
+    const kvc_criticalkv_args* a = static_cast<const kvc_criticalkv_args*>(args);
+    if (check_criticalkv(a) != KVC_OK) return 0;
+    return kvc::criticalkv_workspace_bytes(*a);
+  }
   return 0;  // KVC_SCORE_RETENTION needs none
 }
 
@@ -161,6 +187,15 @@ int kvc_score(int32_t mode, const void* args, void* workspace, size_t workspace_
     const int st = check_retention(a);
     if (st != KVC_OK) return st;
     return kvc::launch_retention_score(*a, stream) == hipSuccess ? KVC_OK : KVC_E_HIP;
+  }
+  if (mode == KVC_SCORE_CRITICALKV) {
+    const kvc_criticalkv_args* a = static_cast<const kvc_criticalkv_args*>(args);
+    const int st = check_criticalkv(a);
+    if (st != KVC_OK) return st;
+    if (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < kvc::criticalkv_workspace_bytes(*a)) {
+      return KVC_E_WORKSPACE;
+    }
+    return kvc::launch_criticalkv(*a, workspace, stream) == hipSuccess ? KVC_OK : KVC_E_HIP;
   }
   return KVC_E_UNSUPPORTED;
 }
@@ -195,6 +230,13 @@ int kvc_route(int32_t mode, const void* args, void* workspace, size_t workspace_
       return KVC_E_WORKSPACE;
     }
     return kvc::launch_topm(*a, workspace, stream) == hipSuccess ? KVC_OK : KVC_E_HIP;
+  }
+  if (mode == KVC_ROUTE_TWO_STAGE) {
+    const kvc_two_stage_args* a = static_cast<const kvc_two_stage_args*>(args);
+    const int st = check_two_stage(a);
+    if (st != KVC_OK) return st;
+    if (a->rows == 0 || a->budget == 0) return KVC_OK;
+    return kvc::launch_two_stage(*a, stream) == hipSuccess ? KVC_OK : KVC_E_HIP;
   }
   return KVC_E_UNSUPPORTED;
 }

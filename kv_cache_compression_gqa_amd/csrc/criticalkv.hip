@@ -1,0 +1,475 @@
+// CriticalKV scores and two-stage selection for one layer at prefill.
+//
+// What it computes follows the CriticalKV page ("Resumo Técnico: CriticalKV"):
+//   * "Framework Teórico": the output perturbation of dropping an entry is bounded through its attention weight A
+//     and its value projected by the output matrix, V W_O;
+//   * "Algoritmo: Seleção Constrainda por Perturbação" (Algorithm 1): a first budget b' = alpha * b goes to the
+//     entries of highest attention weight, the rest to the entries of highest A_i * |V_i W_O|_1 (the printed
+//     formula drops W_O; the bound and the prose are about the projected values, so they are used). A comes from
+//     the host method's observation window (the trailing prompt queries, causal).
+//   Per KV head g with query heads h of its group: A_{h,i} = (1/T) sum_j p_{h,j,i} over the T observation
+//   queries; N_{h,i} = sum_c |sum_d V_{g,i,d} W_O[h*D + d, c]|; A_g = mean_h A_{h,i}; S2_g = mean_h A_{h,i} N_{h,i}.
+//
+// Kernels:
+//   wo_transpose: W_O [Hq*D][d_model] -> [Hq][d_model][D], so that every MFMA B fragment is one 16-byte load.
+//   proj_norm: N on MFMA (v_mfma_f32_32x32x16): a workgroup keeps 256 tokens of V_g in registers (4 waves x 2
+//     tiles of 32 tokens x 128 head_dim) and streams W_O,h through LDS in blocks of 32 output columns (double
+//     buffered, rows padded to 272 bytes so the 16-byte reads are conflict-free); after each block's 8 k-steps the
+//     |.| of the 32x32 products is added to per-row partial sums, so the tokens x d_model product is never stored.
+//   obs_attn<1>: per (KV head, chunk of keys) the logits of the G*T observation rows against the chunk on MFMA in
+//     the transposed orientation (A = 16 keys x 32 head_dim, B = 16 query rows), online (max, sum) per row;
+//   obs_combine: merges the chunks' (max, sum) per row;
+//   obs_attn<2>: recomputes the logits, p = exp(s - m) / l, and sums each head's T rows with DPP row reductions
+//     into A_{h,i};
+//   group_scores: A_g and S2_g;
+//   two_stage: one workgroup per KV head: two radix selects (8-bit digits) in (score desc, index asc) order, the
+//     second over the entries the first did not take; output ascending.
+#include <algorithm>
+
+#include "kvc_internal.h"
+
+namespace kvc {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kObs = 32;           // observation queries
+constexpr int kObsChunk = 512;     // keys per obs_attn workgroup
+constexpr int kTokBlk = 256;       // tokens per proj_norm workgroup
+constexpr int kColBlk = 32;        // output columns per LDS block
+constexpr int kWtStride = kD + 8;  // LDS row of one output column: 128 head_dim + 8 padding (272 bytes)
+constexpr float kInvSqrtD = 0.088388347648318440550f;
+
+template <class T> struct Mfma;
+template <> struct Mfma<BF16> {
+  static __device__ __forceinline__ f32x4 m16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x16 m32(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+  }
+};
+template <> struct Mfma<F16> {
+  static __device__ __forceinline__ f32x4 m16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  }
+  static __device__ __forceinline__ f32x16 m32(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  }
+};
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// ---- W_O transpose: wt[h][c][d] = w_o[h*D + d][c] -----------------------------------------------------------------
+__global__ __launch_bounds__(256) void wo_transpose(const uint16_t* __restrict__ w_o, uint16_t* __restrict__ wt,
+                                                    int dm) {
+  __shared__ uint16_t tile[64][66];
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;  // r = h*D + d; 64 rows never straddle a head
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int rr = i / 64, cc = i % 64;
+    tile[rr][cc] = w_o[size_t(r0 + rr) * dm + c0 + cc];
+  }
+  __syncthreads();
+  const int h = r0 / kD, d0 = r0 % kD;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int cc = i / 64, rr = i % 64;
+    wt[(size_t(h) * dm + c0 + cc) * kD + d0 + rr] = tile[rr][cc];
+  }
+}
+
+// ---- N = |V_g W_O,h|_1 per token ------------------------------------------------------------------------------
+template <class T>
+__global__ __launch_bounds__(256) void proj_norm(const uint16_t* __restrict__ v, const uint16_t* __restrict__ wt,
+                                                 float* __restrict__ norm, int n, int group, int dm) {
+  __shared__ __attribute__((aligned(16))) uint16_t wl[2][kColBlk * kWtStride];
+  const int h = blockIdx.y, g = h / group;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tok0 = blockIdx.x * kTokBlk + 64 * wave;
+  // A fragments: tile t = tokens tok0 + 32t + lane%32; k-step j = head_dim 16j + 8*(lane/32) .. +7
+  u32x4 a[2][8];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int tok = min(tok0 + 32 * t + (lane & 31), n - 1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[t][j] = ld16(v + (size_t(g) * n + tok) * kD + 16 * j + 8 * (lane >> 5));
+  }
+  const uint16_t* wh = wt + size_t(h) * dm * kD;
+  // W block cb: columns 32cb .. 32cb+31, 256 contiguous bytes each; thread i moves 16-byte pieces i and i + 256
+  auto load_w = [&](int cb, u32x4 (&r)[2]) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int idx = threadIdx.x + 256 * k;
+      r[k] = ld16(wh + size_t(kColBlk * cb + (idx >> 4)) * kD + 8 * (idx & 15));
+    }
+  };
+  auto store_w = [&](int buf, const u32x4 (&r)[2]) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int idx = threadIdx.x + 256 * k;
+      *reinterpret_cast<u32x4*>(&wl[buf][(idx >> 4) * kWtStride + 8 * (idx & 15)]) = r[k];
+    }
+  };
+  float part[2][16];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) part[t][i] = 0.0f;
+  }
+  u32x4 pre[2];
+  load_w(0, pre);
+  store_w(0, pre);
+  __syncthreads();
+  const int ncb = dm / kColBlk;
+  for (int cb = 0; cb < ncb; ++cb) {
+    const int buf = cb & 1;
+    const bool more = cb + 1 < ncb;
+    if (more) load_w(cb + 1, pre);
+    f32x16 acc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) acc[t] = f32x16{};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const u32x4 b = *reinterpret_cast<const u32x4*>(&wl[buf][(lane & 31) * kWtStride + 16 * j + 8 * (lane >> 5)]);
+      acc[0] = Mfma<T>::m32(a[0][j], b, acc[0]);
+      acc[1] = Mfma<T>::m32(a[1][j], b, acc[1]);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) part[t][i] += fabsf(acc[t][i]);
+    }
+    if (more) store_w(buf ^ 1, pre);
+    __syncthreads();
+  }
+  // row sums over the 32 columns (lanes of one half-wave); D row of acc[i]: 8*(i/4) + 4*(lane/32) + i%4
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float s = row_sum16(part[t][i]);
+      s += __shfl_xor(s, 16, kWave);
+      const int tok = tok0 + 32 * t + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      if ((lane & 31) == 0 && tok < n) norm[size_t(h) * n + tok] = s;
+    }
+  }
+}
+
+// ---- observation-window attention -----------------------------------------------------------------------------
+// One workgroup = the G heads of KV head g (one wave per head) x one chunk of keys. Per wave: B = the head's 32
+// query rows (2 column tiles), A = 16 keys per tile. S^T lane layout: column = query row 16ct + lane%16, rows =
+// keys 4*(lane/16) + r of the tile.
+template <class T, int PASS>
+__global__ __launch_bounds__(512) void obs_attn(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                int n, int group, int chunks, float* __restrict__ part_ml,
+                                                const float* __restrict__ row_ml, float* __restrict__ a_head) {
+  const int g = blockIdx.y, ch = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = g * group + wave;
+  const int col = lane & 15, qq = lane >> 4;
+  u32x4 bq[2][4];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) bq[ct][kk] = ld16(q + (size_t(h) * kObs + 16 * ct + col) * kD + 32 * kk + 8 * qq);
+  }
+  float m[2], l[2], rm[2], ril[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    m[ct] = -INFINITY;
+    l[ct] = 0.0f;
+    if (PASS == 2) {
+      const int row = wave * kObs + 16 * ct + col;
+      rm[ct] = row_ml[(size_t(g) * group * kObs + row) * 2];
+      const float lt = row_ml[(size_t(g) * group * kObs + row) * 2 + 1];
+      ril[ct] = lt > 0.0f ? 1.0f / lt : 0.0f;
+    }
+  }
+  const int key0 = ch * kObsChunk;
+  const int nkeys = min(kObsChunk, n - key0);
+  const uint16_t* kg = k + size_t(g) * n * kD;
+  constexpr int kBatch = 8;  // key tiles whose loads are in flight together
+  for (int tb = 0; tb * 16 < nkeys; tb += kBatch) {
+    u32x4 ka[kBatch][4];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int tok = min(key0 + 16 * (tb + b) + col, n - 1);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) ka[b][kk] = ld16(kg + size_t(tok) * kD + 32 * kk + 8 * qq);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int tile_key0 = key0 + 16 * (tb + b);
+      if (tile_key0 >= key0 + nkeys) break;
+      f32x4 s[2];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        s[ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) s[ct] = Mfma<T>::m16(ka[b][kk], bq[ct][kk], s[ct]);
+      }
+      float pv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const int obs_pos = n - kObs + 16 * ct + col;  // position of this column's query
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = tile_key0 + 4 * qq + r;
+          const bool ok = key < n && key <= obs_pos;
+          const float sv = ok ? s[ct][r] * kInvSqrtD : -INFINITY;
+          if (PASS == 1) {
+            s[ct][r] = sv;
+          } else {
+            pv[r] += exp_diff(sv, rm[ct]) * ril[ct];
+          }
+        }
+        if (PASS == 1) {
+          const float mt = fmaxf(fmaxf(s[ct][0], s[ct][1]), fmaxf(s[ct][2], s[ct][3]));
+          const float mn = fmaxf(m[ct], mt);
+          float add = 0.0f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) add += exp_diff(s[ct][r], mn);
+          l[ct] = l[ct] * exp_diff(m[ct], mn) + add;
+          m[ct] = mn;
+        }
+      }
+      if (PASS == 2) {
+        // sum over the head's 32 query rows: the two column tiles are already added; now the 16 columns
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float tot = row_sum16(pv[r]) * (1.0f / kObs);
+          const int key = tile_key0 + 4 * qq + r;
+          if (col == 0 && key < n) a_head[size_t(h) * n + key] = tot;
+        }
+      }
+    }
+  }
+  if (PASS == 1) {
+    // merge the four 16-lane groups (different keys, same query rows)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+      for (int x = 16; x <= 32; x <<= 1) {
+        const float mo = __shfl_xor(m[ct], x, kWave), lo = __shfl_xor(l[ct], x, kWave);
+        const float mn = fmaxf(m[ct], mo);
+        l[ct] = l[ct] * exp_diff(m[ct], mn) + lo * exp_diff(mo, mn);
+        m[ct] = mn;
+      }
+      if (qq == 0) {
+        const int row = wave * kObs + 16 * ct + col;
+        float* o = part_ml + ((size_t(g) * chunks + ch) * group * kObs + row) * 2;
+        o[0] = m[ct];
+        o[1] = l[ct];
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void obs_combine(const float* __restrict__ part_ml, float* __restrict__ row_ml,
+                                                   int rows_per_g, int chunks) {
+  const int g = blockIdx.x;
+  for (int row = threadIdx.x; row < rows_per_g; row += 256) {
+    float m = -INFINITY, l = 0.0f;
+    for (int c = 0; c < chunks; ++c) {
+      const float* p = part_ml + ((size_t(g) * chunks + c) * rows_per_g + row) * 2;
+      const float mn = fmaxf(m, p[0]);
+      l = l * exp_diff(m, mn) + p[1] * exp_diff(p[0], mn);
+      m = mn;
+    }
+    row_ml[(size_t(g) * rows_per_g + row) * 2] = m;
+    row_ml[(size_t(g) * rows_per_g + row) * 2 + 1] = l;
+  }
+}
+
+__global__ __launch_bounds__(256) void group_scores(const float* __restrict__ a_head, const float* __restrict__ norm,
+                                                    float* __restrict__ a_group, float* __restrict__ s2_group, int n,
+                                                    int hkv, int group) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= int64_t(n) * hkv) return;
+  const int g = int(i / n), key = int(i - int64_t(g) * n);
+  float a = 0.0f, s2 = 0.0f;
+  for (int hh = 0; hh < group; ++hh) {
+    const size_t idx = size_t(g * group + hh) * n + key;
+    a += a_head[idx];
+    s2 += a_head[idx] * norm[idx];
+  }
+  a_group[i] = a / group;
+  s2_group[i] = s2 / group;
+}
+
+// ---- two-stage selection ----------------------------------------------------------------------------------------
+constexpr int kSelThreads = 1024;
+constexpr int kSelMaxN = 65536;
+
+__device__ __forceinline__ uint32_t sel_key(float s) {
+  const uint32_t u = __float_as_uint(s == 0.0f ? 0.0f : s);
+  return ~((u & 0x80000000u) ? ~u : (u | 0x80000000u));  // smaller key = larger score
+}
+
+struct SelShared {
+  uint32_t taken[kSelMaxN / 32];  // stage-1 picks (bit per entry)
+  uint32_t hist[256];
+  uint32_t scan[kSelThreads];
+  uint32_t prefix;
+  int32_t need;
+};
+
+// Marks (in sh.taken, or as output when mark == false) the first b entries in (score desc, index asc) order among
+// the entries not yet taken. Thread t owns entries [t*per, t*per + per).
+__device__ void select_stage(const float* __restrict__ sc, int n, int b, int per, SelShared& sh) {
+  const int t = threadIdx.x;
+  const int i0 = t * per, i1 = min(n, i0 + per);
+  if (t == 0) {
+    sh.prefix = 0u;
+    sh.need = b;
+  }
+  __syncthreads();
+  if (b <= 0) return;
+  for (int pass = 0; pass < 4; ++pass) {
+    for (int i = t; i < 256; i += kSelThreads) sh.hist[i] = 0u;
+    __syncthreads();
+    const uint32_t prefix = sh.prefix;
+    const int shift = 24 - 8 * pass;
+    for (int i = i0; i < i1; ++i) {
+      if ((sh.taken[i >> 5] >> (i & 31)) & 1u) continue;
+      const uint32_t key = sel_key(sc[i]);
+      if (pass > 0 && (key >> (shift + 8)) != prefix) continue;
+      atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (t == 0) {
+      int need = sh.need, bin = 0;
+      while (bin < 255 && int(sh.hist[bin]) < need) need -= int(sh.hist[bin++]);
+      sh.prefix = (prefix << 8) | uint32_t(bin);
+      sh.need = need;
+    }
+    __syncthreads();
+  }
+  const uint32_t thr = sh.prefix;
+  const int need = sh.need;
+  // ties at the threshold go in index order: exclusive scan of per-thread tie counts
+  uint32_t ties = 0;
+  for (int i = i0; i < i1; ++i) {
+    if (!((sh.taken[i >> 5] >> (i & 31)) & 1u) && sel_key(sc[i]) == thr) ++ties;
+  }
+  sh.scan[t] = ties;
+  __syncthreads();
+  if (t == 0) {
+    uint32_t acc = 0;
+    for (int x = 0; x < kSelThreads; ++x) {
+      const uint32_t v = sh.scan[x];
+      sh.scan[x] = acc;
+      acc += v;
+    }
+  }
+  __syncthreads();
+  uint32_t rank = sh.scan[t];
+  for (int i = i0; i < i1; ++i) {
+    if ((sh.taken[i >> 5] >> (i & 31)) & 1u) continue;
+    const uint32_t key = sel_key(sc[i]);
+    bool take = key < thr;
+    if (key == thr) {
+      take = int(rank) < need;
+      ++rank;
+    }
+    if (take) atomicOr(&sh.taken[i >> 5], 1u << (i & 31));
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kSelThreads) void two_stage(const float* __restrict__ a, const float* __restrict__ s2,
+                                                         int n, int budget, int budget1, int32_t* __restrict__ idx) {
+  __shared__ SelShared sh;
+  const int row = blockIdx.x;
+  const int per = (n + kSelThreads - 1) / kSelThreads;
+  for (int i = threadIdx.x; i < kSelMaxN / 32; i += kSelThreads) sh.taken[i] = 0u;
+  __syncthreads();
+  select_stage(a + size_t(row) * n, n, budget1, per, sh);
+  select_stage(s2 + size_t(row) * n, n, budget - budget1, per, sh);
+  // ascending output: exclusive scan of per-thread counts
+  const int t = threadIdx.x;
+  const int i0 = t * per, i1 = min(n, i0 + per);
+  uint32_t cnt = 0;
+  for (int i = i0; i < i1; ++i) cnt += (sh.taken[i >> 5] >> (i & 31)) & 1u;
+  sh.scan[t] = cnt;
+  __syncthreads();
+  if (t == 0) {
+    uint32_t acc = 0;
+    for (int x = 0; x < kSelThreads; ++x) {
+      const uint32_t v = sh.scan[x];
+      sh.scan[x] = acc;
+      acc += v;
+    }
+  }
+  __syncthreads();
+  uint32_t o = sh.scan[t];
+  for (int i = i0; i < i1; ++i) {
+    if ((sh.taken[i >> 5] >> (i & 31)) & 1u) {
+      if (int(o) < budget) idx[size_t(row) * budget + o] = i;
+      ++o;
+    }
+  }
+}
+
+size_t al(size_t x) { return align_up(x, 256); }
+
+int obs_chunks(const kvc_criticalkv_args& a) { return (a.n_keys + kObsChunk - 1) / kObsChunk; }
+
+}  // namespace
+
+size_t criticalkv_workspace_bytes(const kvc_criticalkv_args& a) {
+  const size_t G = size_t(a.hq / a.hkv);
+  return al(size_t(a.hq) * a.d_model * kD * 2) + al(size_t(a.hkv) * obs_chunks(a) * G * kObs * 2 * 4) +
+         al(size_t(a.hkv) * G * kObs * 2 * 4);
+}
+
+bool criticalkv_supported(const kvc_criticalkv_args& a) {
+  const int G = a.hkv > 0 ? a.hq / a.hkv : 0;
+  return a.n_obs == kObs && a.head_dim == kD && (G == 1 || G == 2 || G == 4 || G == 8) && a.hq == G * a.hkv &&
+         a.d_model % 64 == 0 && a.d_model >= 64 && a.n_keys >= kObs;
+}
+
+template <class T>
+hipError_t launch_ckv(const kvc_criticalkv_args& a, void* ws, hipStream_t s) {
+  const int G = a.hq / a.hkv, n = a.n_keys, dm = a.d_model, chunks = obs_chunks(a);
+  char* w = static_cast<char*>(ws);
+  uint16_t* wt = reinterpret_cast<uint16_t*>(w);
+  w += al(size_t(a.hq) * dm * kD * 2);
+  float* part_ml = reinterpret_cast<float*>(w);
+  w += al(size_t(a.hkv) * chunks * G * kObs * 2 * 4);
+  float* row_ml = reinterpret_cast<float*>(w);
+  const uint16_t* q = static_cast<const uint16_t*>(a.q_obs);
+  const uint16_t* k = static_cast<const uint16_t*>(a.k);
+  const uint16_t* v = static_cast<const uint16_t*>(a.v);
+  hipLaunchKernelGGL(wo_transpose, dim3(dm / 64, a.hq * kD / 64), dim3(256), 0, s, static_cast<const uint16_t*>(a.w_o),
+                     wt, dm);
+  hipLaunchKernelGGL((proj_norm<T>), dim3((n + kTokBlk - 1) / kTokBlk, a.hq), dim3(256), 0, s, v, wt, a.norm, n, G, dm);
+  hipLaunchKernelGGL((obs_attn<T, 1>), dim3(chunks, a.hkv), dim3(64 * G), 0, s, q, k, n, G, chunks, part_ml,
+                     static_cast<const float*>(nullptr), static_cast<float*>(nullptr));
+  hipLaunchKernelGGL(obs_combine, dim3(a.hkv), dim3(256), 0, s, part_ml, row_ml, G * kObs, chunks);
+  hipLaunchKernelGGL((obs_attn<T, 2>), dim3(chunks, a.hkv), dim3(64 * G), 0, s, q, k, n, G, chunks,
+                     static_cast<float*>(nullptr), row_ml, a.a_head);
+  const int64_t tot = int64_t(n) * a.hkv;
+  hipLaunchKernelGGL(group_scores, dim3(unsigned((tot + 255) / 256)), dim3(256), 0, s, a.a_head, a.norm, a.a_group,
+                     a.s2_group, n, a.hkv, G);
+  return hipGetLastError();
+}
+
+hipError_t launch_criticalkv(const kvc_criticalkv_args& a, void* ws, hipStream_t s) {
+  return a.kv_dtype == KVC_BF16 ? launch_ckv<BF16>(a, ws, s) : launch_ckv<F16>(a, ws, s);
+}
+
+hipError_t launch_two_stage(const kvc_two_stage_args& a, hipStream_t s) {
+  hipLaunchKernelGGL(two_stage, dim3(a.rows), dim3(kSelThreads), 0, s, a.a, a.s2, a.n, a.budget, a.budget1, a.idx);
+  return hipGetLastError();
+}
+
+}  // namespace kvc

@@ -112,5 +112,9 @@ size_t topm_workspace_bytes(const kvc_topm_args& a);
 hipError_t launch_topm(const kvc_topm_args& a, void* ws, hipStream_t s);
 size_t compact_workspace_bytes(const kvc_compact_args& a);
 hipError_t launch_compact(const kvc_compact_args& a, void* ws, hipStream_t s);
+size_t criticalkv_workspace_bytes(const kvc_criticalkv_args& a);
+bool criticalkv_supported(const kvc_criticalkv_args& a);
+hipError_t launch_criticalkv(const kvc_criticalkv_args& a, void* ws, hipStream_t s);
+hipError_t launch_two_stage(const kvc_two_stage_args& a, hipStream_t s);
 
 }  // namespace kvc

@@ -148,3 +148,32 @@ def test_retention_topm_compact_validation_rejects_before_launch():
     assert compact(kv_dtype=7)[0] == abi.KVC_E_UNSUPPORTED
     assert compact()[0] == abi.KVC_E_WORKSPACE
     assert L.kvc_compact_pages_workspace(C.byref(compact()[1])) > 0
+
+
+def test_criticalkv_and_two_stage_validation_rejects_before_launch():
+    L = abi.lib()
+
+    def ckv(**over):
+        kw = dict(q_obs=FAKE, k=FAKE, v=FAKE, w_o=FAKE, a_head=FAKE, norm=FAKE, a_group=FAKE, s2_group=FAKE,
+                  n_keys=1024, hq=8, hkv=2, n_obs=32, head_dim=128, d_model=256, kv_dtype=abi.KVC_BF16, reserved=0)
+        kw.update(over)
+        c = abi.KvcCriticalKVArgs(**kw)
+        pc = C.cast(C.byref(c), C.c_void_p)
+        return L.kvc_score(abi.KVC_SCORE_CRITICALKV, pc, None, 0, None), L.kvc_score_workspace(abi.KVC_SCORE_CRITICALKV, pc)
+    assert ckv(n_obs=16)[0] == abi.KVC_E_UNSUPPORTED
+    assert ckv(hq=6)[0] == abi.KVC_E_UNSUPPORTED
+    assert ckv(d_model=100)[0] == abi.KVC_E_UNSUPPORTED
+    assert ckv(kv_dtype=5)[0] == abi.KVC_E_UNSUPPORTED
+    assert ckv(reserved=1)[0] == abi.KVC_E_INVALID
+    st, ws = ckv()
+    assert st == abi.KVC_E_WORKSPACE and ws >= 8 * 256 * 128 * 2
+
+    def ts(**over):
+        kw = dict(a=FAKE, s2=FAKE, idx=FAKE, rows=2, n=100, budget=10, budget1=5)
+        kw.update(over)
+        t = abi.KvcTwoStageArgs(**kw)
+        return L.kvc_route(abi.KVC_ROUTE_TWO_STAGE, C.cast(C.byref(t), C.c_void_p), None, 0, None)
+    assert ts(budget=101) == abi.KVC_E_BUDGET
+    assert ts(budget1=11) == abi.KVC_E_BUDGET
+    assert ts(n=70000, budget=10) == abi.KVC_E_UNSUPPORTED
+    assert ts(budget=0, budget1=0) == abi.KVC_OK  # nothing to select: no launch
