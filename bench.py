@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch steps eagerly instead of one captured graph")
+    ap.add_argument("--workload", default="llama3_8b_layer_32k",
+                    choices=["llama3_8b_layer_32k", "criticalkv_64k", "dbtrim_128k"],
+                    help="the decode step (default), the CriticalKV prefill selection or the DBTrimKV global budget")
     return ap.parse_args()
 
 
@@ -120,6 +123,10 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
               "(the per-unit work shards with no exchange; see the design notes)", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "criticalkv_64k":
+        return bench_criticalkv(args)
+    if args.workload == "dbtrim_128k":
+        return bench_dbtrim(args)
     import torch
     sys.path.insert(0, ROOT)
     from kv_cache_compression_gqa_amd import configs, synth
@@ -221,6 +228,185 @@ def main():
         print("timing the CPU oracle sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(rec), flush=True)
+
+
+def _timed_calls(fn, K, W):
+    """Run fn W times untimed, then K times with HIP events around each call on the current stream; returns
+    (wall seconds for the K calls, list of per-call event milliseconds)."""
+    import torch
+    for _ in range(W):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [a.elapsed_time(b) for a, b in ev]
+
+
+def bench_criticalkv(args):
+    """CriticalKV prefill selection of one layer: scores (observation attention A, |V W_O|_1, group means) and the
+    two-stage selection, 65536 keys, 32/8 heads, d_model 4096, bf16."""
+    import torch
+    sys.path.insert(0, ROOT)
+    from kv_cache_compression_gqa_amd import abi, configs, criticalkv, synth
+    cfg = configs.CRITICALKV_64K
+    torch.cuda.set_device(0)
+    inp = synth.make_criticalkv(cfg)
+    t = {name: torch.from_numpy(getattr(inp, name).view(np.int16)).cuda().view(torch.bfloat16)
+         for name in ("q_obs", "k", "v", "w_o")}
+    print(f"inputs ready: {cfg.name}", file=sys.stderr, flush=True)
+    holder = {}
+
+    def run():
+        out = criticalkv.scores(t["q_obs"], t["k"], t["v"], t["w_o"], abi.KVC_BF16)
+        holder["idx"] = criticalkv.two_stage(out["a_group"], out["s2_group"], cfg.budget, cfg.alpha)
+        holder["out"] = out
+
+    K = max(1, min(args.steps, 10))
+    wall, ms = _timed_calls(run, K, 2)
+    n, hq, hkv, D, dm = cfg.n_keys, cfg.hq, cfg.hkv, cfg.head_dim, cfg.d_model
+    flops_n = 2.0 * n * D * dm * hq                        # V_g W_O,h for every query head
+    flops_a = 2 * 2.0 * n * D * cfg.n_obs * hq             # two passes of q.K^T over the observation rows
+    avg_s = float(np.mean(ms)) * 1e-3
+    rec = {
+        "metric": "KV entries scored+selected/s (CriticalKV prefill selection, one layer)",
+        "value": n * hkv * K / wall, "unit": "KV entries/s", "n_gpus": 1, "steps": K, "warmup": 2,
+        "ms_per_step": wall / K * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "n_keys": n, "q_heads": hq, "kv_heads": hkv, "head_dim": D, "d_model": dm,
+                   "n_obs": cfg.n_obs, "budget": cfg.budget, "alpha": cfg.alpha},
+        "roofline": {"bound": "mfma", "achieved": (flops_n + flops_a) / avg_s / 1e12, "peak": 2500.0,
+                     "unit": "TFLOP/s", "frac": (flops_n + flops_a) / avg_s / 1e12 / 2500.0, "traffic": None,
+                     "kernel": "kvc_score(CRITICALKV) + kvc_route(TWO_STAGE) (proj_norm dominates)",
+                     "avg_launch_us": avg_s * 1e6, "algorithmic_flops_per_launch": flops_n + flops_a},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_criticalkv(cfg, inp)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline_criticalkv(cfg, inp):
+    """The oracle on KV heads of the same layer (each with its G query heads: A, N and S2 over all keys, then
+    the two-stage selection), one head at a time until at least 10 s of CPU work or all heads."""
+    from oracle import criticalkv as ock
+    from oracle import fp as ofp
+    threads = _oracle_threads()
+    G, D = cfg.group, cfg.head_dim
+    heads, el = 0, 0.0
+    while heads < cfg.hkv and el < 10.0:
+        g = heads
+        q = ofp.storage_to_f64(inp.q_obs[g * G:(g + 1) * G], cfg.dtype)
+        k = ofp.storage_to_f64(inp.k[g:g + 1], cfg.dtype)
+        v = ofp.storage_to_f64(inp.v[g:g + 1], cfg.dtype)
+        w = ofp.storage_to_f64(inp.w_o[g * G * D:(g + 1) * G * D], cfg.dtype)
+        t0 = time.perf_counter()
+        A, N, A_g, S2_g = ock.scores(q, k, v, w, G)
+        ock.select(A_g, S2_g, cfg.budget, cfg.alpha)
+        el += time.perf_counter() - t0
+        heads += 1
+    return {"value": heads * cfg.n_keys / el, "unit": "KV entries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{heads} of {cfg.hkv} KV heads ({G} query heads each, all {cfg.n_keys} keys, d_model "
+                      f"{cfg.d_model}): fp64 numpy oracle scores + two-stage selection; {el:.1f} s"}
+
+
+def bench_dbtrim(args):
+    """DBTrimKV global budget: log-retention scores, global top-M and paged compaction over 32 layers x 8 KV heads
+    x 131072 tokens (bf16 K/V pools of 2,097,152 16-token pages)."""
+    import torch
+    sys.path.insert(0, ROOT)
+    from kv_cache_compression_gqa_amd import abi, configs, retention, synth
+    cfg = configs.DBTRIM_128K
+    torch.cuda.set_device(0)
+    L, H, T, page, D = cfg.layers, cfg.hkv, cfg.n_tokens, cfg.page, cfg.head_dim
+    rows = L * H
+    beta = torch.from_numpy(synth.make_retention_beta(cfg).reshape(rows, T)).cuda()
+    pt = torch.from_numpy(synth.make_page_table(cfg).reshape(rows, T // page).astype(np.int32)).cuda()
+    n_src = rows * (T // page)
+    pools = []
+    for sd in (cfg.seed * 7 + 1, cfg.seed * 7 + 2):
+        tab = torch.from_numpy(synth.pool_table_bits(D, sd, cfg.dtype).view(np.int16)).cuda()
+        idx = (torch.arange(n_src * page, device="cuda", dtype=torch.int64) * 40503 + 17) % tab.shape[0]
+        pools.append(tab[idx].view(torch.bfloat16).view(n_src, page, D))
+        del idx
+    out_pages = cfg.keep // page + rows + 1
+    print(f"inputs ready: {cfg.name}", file=sys.stderr, flush=True)
+    st = {}
+
+    def score():
+        st["s"] = retention.retention_scores(beta, cfg.t)
+
+    def topm():
+        st["tm"] = retention.global_topm(st["s"], cfg.keep)
+
+    def compact():
+        st["c"] = retention.compact_pages(st["tm"].keep, pt, pools[0], pools[1], out_pages, abi.KVC_BF16)
+
+    K = max(1, min(args.steps, 10))
+    score()
+    topm()
+    res = {}
+    for name, fn in (("score", score), ("topm", topm), ("compact", compact)):
+        res[name] = _timed_calls(fn, K, 1)
+    torch.cuda.synchronize()
+    if int(st["tm"].status.item()) or int(st["c"].status.item()):
+        print("device status bits set", file=sys.stderr)
+        sys.exit(1)
+    kept = int(st["c"].lengths.sum().item())
+    wall = sum(w for w, _ in res.values())
+    comp_s = float(np.mean(res["compact"][1])) * 1e-3
+    comp_bytes = kept * D * 2 * 2 * 2 + rows * T  # K and V rows read and written, plus the keep mask
+    rec = {
+        "metric": "KV entries scored+selected+compacted/s (DBTrimKV global budget)",
+        "value": cfg.n_entries * K / wall, "unit": "KV entries/s", "n_gpus": 1, "steps": K, "warmup": 1,
+        "ms_per_step": wall / K * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "layers": L, "kv_heads": H, "n_tokens": T, "page": page,
+                   "keep": cfg.keep, "ms_score": float(np.mean(res["score"][1])),
+                   "ms_topm": float(np.mean(res["topm"][1])), "ms_compact": comp_s * 1e3},
+        "roofline": {"bound": "hbm", "achieved": comp_bytes / comp_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": comp_bytes / comp_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "kvc_compact_pages (compact_copy dominates)", "avg_launch_us": comp_s * 1e6,
+                     "algorithmic_bytes_per_launch": comp_bytes},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_dbtrim(cfg)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline_dbtrim(cfg, layers=16):
+    """The oracle on the first `layers` layers (a budget of 10% of their entries): scores, top-M, compaction plan
+    and the row gather of the kept K/V rows."""
+    from kv_cache_compression_gqa_amd import synth
+    from oracle import dbtrim
+    threads = _oracle_threads()
+    beta = synth.make_retention_beta(cfg, layers=layers)
+    pt = synth.make_page_table(cfg, layers=layers)
+    m = int(np.floor(cfg.keep_frac * beta.size))
+    t0 = time.perf_counter()
+    s = dbtrim.log_retention(beta, cfg.t)
+    keep = dbtrim.keep_mask(s, m)
+    src, lengths, off, n_pages = dbtrim.compact_rows(keep, pt, cfg.page)
+    live = src[src >= 0]
+    rows_k = synth.pool_row_bits(live, cfg.head_dim, cfg.seed * 7 + 1, cfg.dtype)
+    rows_v = synth.pool_row_bits(live, cfg.head_dim, cfg.seed * 7 + 2, cfg.dtype)
+    el = time.perf_counter() - t0
+    assert rows_k.shape[0] == rows_v.shape[0] == m
+    return {"value": beta.size / el, "unit": "KV entries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{layers} of {cfg.layers} layers ({beta.size} entries, M = 10%): fp64 numpy oracle scores, "
+                      f"top-M, compaction plan and K/V row gather; {el:.1f} s"}
+
+
+def _oracle_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        return len(os.sched_getaffinity(0))
 
 
 if __name__ == "__main__":

@@ -264,7 +264,7 @@ typedef struct kvc_topm_args {
  * are zeroed.
  *   keep        [n_rows][n_tokens] uint8 (0/1), 16-byte aligned; n_tokens % 16 == 0, n_tokens % page == 0.
  *   page_table  [n_rows][n_tokens / page] int32: source page id of each block of `page` positions.
- *   k_pool, v_pool  [n_src_pages][page][head_dim] storage dtype (fp16/bf16), head_dim == 128.
+ *   k_pool, v_pool  [n_src_pages][page][head_dim] storage dtype (fp16/bf16), head_dim == 128, n_src_pages >= 1.
  *   k_out, v_out    [out_pages_max][page][head_dim] storage dtype out.
  *   lengths, page_offset, n_pages   [n_rows] int32 out.
  *   status      int32 device error bits: KVC_DEV_BOUND_EXCEEDED if the pages exceed out_pages_max (the excess is

@@ -101,7 +101,7 @@ int check_compact(const kvc_compact_args* a) {
   if (a->head_dim != kvc::kD) return KVC_E_UNSUPPORTED;
   if (a->kv_dtype != KVC_F16 && a->kv_dtype != KVC_BF16) return KVC_E_UNSUPPORTED;
   if (a->page <= 0 || a->n_tokens <= 0 || a->n_tokens % 16 != 0 || a->n_tokens % a->page != 0) return KVC_E_INVALID;
-  if (a->n_rows < 0 || a->n_src_pages < 0 || a->out_pages_max < 0) return KVC_E_INVALID;
+  if (a->n_rows < 0 || a->n_src_pages < 1 || a->out_pages_max < 0) return KVC_E_INVALID;
   if (a->n_rows * int64_t(a->n_tokens) >= (int64_t(1) << 31) || a->n_rows > 65535) return KVC_E_UNSUPPORTED;
   return KVC_OK;
 }

@@ -273,17 +273,31 @@ __global__ __launch_bounds__(512) void obs_attn(const uint16_t* __restrict__ q, 
   }
 }
 
+// one wave per observation row: lanes merge strided chunks, then a butterfly merges the lanes (fixed order)
 __global__ __launch_bounds__(256) void obs_combine(const float* __restrict__ part_ml, float* __restrict__ row_ml,
                                                    int rows_per_g, int chunks) {
-  const int g = blockIdx.x;
-  for (int row = threadIdx.x; row < rows_per_g; row += 256) {
-    float m = -INFINITY, l = 0.0f;
-    for (int c = 0; c < chunks; ++c) {
-      const float* p = part_ml + ((size_t(g) * chunks + c) * rows_per_g + row) * 2;
-      const float mn = fmaxf(m, p[0]);
-      l = l * exp_diff(m, mn) + p[1] * exp_diff(p[0], mn);
-      m = mn;
-    }
+  const int g = blockIdx.y;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & (kWave - 1);
+  if (row >= rows_per_g) return;
+  float m = -INFINITY, l = 0.0f;
+  for (int c = lane; c < chunks; c += kWave) {
+    const float* p = part_ml + ((size_t(g) * chunks + c) * rows_per_g + row) * 2;
+    const float mn = fmaxf(m, p[0]);
+    l = l * exp_diff(m, mn) + p[1] * exp_diff(p[0], mn);
+    m = mn;
+  }
+#pragma unroll
+  for (int x = 1; x < kWave; x <<= 1) {
+    const float mo = __shfl_xor(m, x, kWave), lo = __shfl_xor(l, x, kWave);
+    const float mn = fmaxf(m, mo);
+    // combine in lane order so that every lane gets the same bits
+    const bool first = (lane & x) == 0;
+    const float la = first ? l : lo, ma = first ? m : mo, lb = first ? lo : l, mb = first ? mo : m;
+    l = la * exp_diff(ma, mn) + lb * exp_diff(mb, mn);
+    m = mn;
+  }
+  if (lane == 0) {
     row_ml[(size_t(g) * rows_per_g + row) * 2] = m;
     row_ml[(size_t(g) * rows_per_g + row) * 2 + 1] = l;
   }
@@ -306,8 +320,12 @@ __global__ __launch_bounds__(256) void group_scores(const float* __restrict__ a_
 }
 
 // ---- two-stage selection ----------------------------------------------------------------------------------------
+// One workgroup of 1024 threads per row; thread t owns entries [64t, 64t + 64) (index order = thread order), whose
+// keys stay in registers for every pass.
 constexpr int kSelThreads = 1024;
-constexpr int kSelMaxN = 65536;
+constexpr int kSelPer = 64;
+constexpr int kSelMaxN = kSelThreads * kSelPer;
+constexpr int kSelWaves = kSelThreads / kWave;
 
 __device__ __forceinline__ uint32_t sel_key(float s) {
   const uint32_t u = __float_as_uint(s == 0.0f ? 0.0f : s);
@@ -315,105 +333,135 @@ __device__ __forceinline__ uint32_t sel_key(float s) {
 }
 
 struct SelShared {
-  uint32_t taken[kSelMaxN / 32];  // stage-1 picks (bit per entry)
-  uint32_t hist[256];
-  uint32_t scan[kSelThreads];
+  uint32_t hist[kSelWaves][256];
+  uint32_t wsum[kSelWaves];
   uint32_t prefix;
   int32_t need;
 };
 
-// Marks (in sh.taken, or as output when mark == false) the first b entries in (score desc, index asc) order among
-// the entries not yet taken. Thread t owns entries [t*per, t*per + per).
-__device__ void select_stage(const float* __restrict__ sc, int n, int b, int per, SelShared& sh) {
-  const int t = threadIdx.x;
-  const int i0 = t * per, i1 = min(n, i0 + per);
-  if (t == 0) {
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const uint32_t o = __shfl_up(v, d, kWave);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// exclusive prefix of v over the block in thread order
+__device__ uint32_t block_excl_scan(uint32_t v, SelShared& sh) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
+  const uint32_t inc = wave_incl_scan(v);
+  if (lane == kWave - 1) sh.wsum[wave] = inc;
+  __syncthreads();
+  uint32_t base = 0;
+  for (int w = 0; w < wave; ++w) base += sh.wsum[w];
+  __syncthreads();
+  return base + inc - v;
+}
+
+// Takes (sets in `taken`) the first b eligible entries (eligible: valid and not taken) in (key asc, index asc).
+__device__ void select_stage(const uint32_t (&key)[kSelPer], uint64_t valid, uint64_t& taken, int b, SelShared& sh) {
+  if (b <= 0) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
+  const uint64_t elig = valid & ~taken;
+  if (threadIdx.x == 0) {
     sh.prefix = 0u;
     sh.need = b;
   }
-  __syncthreads();
-  if (b <= 0) return;
   for (int pass = 0; pass < 4; ++pass) {
-    for (int i = t; i < 256; i += kSelThreads) sh.hist[i] = 0u;
+    for (int i = threadIdx.x; i < kSelWaves * 256; i += kSelThreads) (&sh.hist[0][0])[i] = 0u;
     __syncthreads();
     const uint32_t prefix = sh.prefix;
     const int shift = 24 - 8 * pass;
-    for (int i = i0; i < i1; ++i) {
-      if ((sh.taken[i >> 5] >> (i & 31)) & 1u) continue;
-      const uint32_t key = sel_key(sc[i]);
-      if (pass > 0 && (key >> (shift + 8)) != prefix) continue;
-      atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+#pragma unroll
+    for (int e = 0; e < kSelPer; ++e) {
+      const bool match = ((elig >> e) & 1u) && (pass == 0 || (key[e] >> (shift + 8)) == prefix);
+      if (match) atomicAdd(&sh.hist[wave][(key[e] >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (t == 0) {
-      int need = sh.need, bin = 0;
-      while (bin < 255 && int(sh.hist[bin]) < need) need -= int(sh.hist[bin++]);
-      sh.prefix = (prefix << 8) | uint32_t(bin);
-      sh.need = need;
+    if (wave == 0) {
+      // lane l holds bins 4l .. 4l+3 (summed over the per-wave copies); first bin whose running count reaches need
+      uint32_t c[4], tot = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        uint32_t x = 0;
+        for (int w = 0; w < kSelWaves; ++w) x += sh.hist[w][4 * lane + k];
+        c[k] = x;
+        tot += x;
+      }
+      const uint32_t inc = wave_incl_scan(tot);
+      const int need = sh.need;
+      const uint64_t hit = __ballot(int(inc) >= need);
+      const int l0 = hit ? __builtin_ctzll(hit) : kWave - 1;
+      if (lane == l0) {
+        int rem = need - int(inc - tot);
+        int bin = 4 * lane;
+        for (int k = 0; k < 3 && int(c[k]) < rem; ++k) {
+          rem -= int(c[k]);
+          ++bin;
+        }
+        sh.prefix = (prefix << 8) | uint32_t(bin);
+        sh.need = rem;
+      }
     }
     __syncthreads();
   }
   const uint32_t thr = sh.prefix;
   const int need = sh.need;
-  // ties at the threshold go in index order: exclusive scan of per-thread tie counts
   uint32_t ties = 0;
-  for (int i = i0; i < i1; ++i) {
-    if (!((sh.taken[i >> 5] >> (i & 31)) & 1u) && sel_key(sc[i]) == thr) ++ties;
-  }
-  sh.scan[t] = ties;
-  __syncthreads();
-  if (t == 0) {
-    uint32_t acc = 0;
-    for (int x = 0; x < kSelThreads; ++x) {
-      const uint32_t v = sh.scan[x];
-      sh.scan[x] = acc;
-      acc += v;
-    }
-  }
-  __syncthreads();
-  uint32_t rank = sh.scan[t];
-  for (int i = i0; i < i1; ++i) {
-    if ((sh.taken[i >> 5] >> (i & 31)) & 1u) continue;
-    const uint32_t key = sel_key(sc[i]);
-    bool take = key < thr;
-    if (key == thr) {
+#pragma unroll
+  for (int e = 0; e < kSelPer; ++e) ties += ((elig >> e) & 1u) && key[e] == thr ? 1u : 0u;
+  uint32_t rank = block_excl_scan(ties, sh);
+#pragma unroll
+  for (int e = 0; e < kSelPer; ++e) {
+    if (!((elig >> e) & 1u)) continue;
+    bool take = key[e] < thr;
+    if (key[e] == thr) {
       take = int(rank) < need;
       ++rank;
     }
-    if (take) atomicOr(&sh.taken[i >> 5], 1u << (i & 31));
+    if (take) taken |= uint64_t(1) << e;
   }
   __syncthreads();
+}
+
+__device__ __forceinline__ void load_keys(const float* __restrict__ sc, int n, int i0, uint32_t (&key)[kSelPer],
+                                          uint64_t& valid) {
+  valid = 0;
+#pragma unroll
+  for (int e = 0; e < kSelPer; e += 4) {
+    const int i = i0 + e;
+    float4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (i + 3 < n) v = *reinterpret_cast<const float4*>(sc + i);
+    const float vs[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bool ok = i + c < n;
+      const float x = ok ? (i + 3 < n ? vs[c] : sc[i + c]) : 0.0f;
+      key[e + c] = sel_key(x);
+      valid |= uint64_t(ok ? 1 : 0) << (e + c);
+    }
+  }
 }
 
 __global__ __launch_bounds__(kSelThreads) void two_stage(const float* __restrict__ a, const float* __restrict__ s2,
                                                          int n, int budget, int budget1, int32_t* __restrict__ idx) {
   __shared__ SelShared sh;
   const int row = blockIdx.x;
-  const int per = (n + kSelThreads - 1) / kSelThreads;
-  for (int i = threadIdx.x; i < kSelMaxN / 32; i += kSelThreads) sh.taken[i] = 0u;
-  __syncthreads();
-  select_stage(a + size_t(row) * n, n, budget1, per, sh);
-  select_stage(s2 + size_t(row) * n, n, budget - budget1, per, sh);
+  const int i0 = threadIdx.x * kSelPer;
+  uint32_t key[kSelPer];
+  uint64_t valid, taken = 0;
+  load_keys(a + size_t(row) * n, n, i0, key, valid);
+  select_stage(key, valid, taken, budget1, sh);
+  load_keys(s2 + size_t(row) * n, n, i0, key, valid);
+  select_stage(key, valid, taken, budget - budget1, sh);
   // ascending output: exclusive scan of per-thread counts
-  const int t = threadIdx.x;
-  const int i0 = t * per, i1 = min(n, i0 + per);
-  uint32_t cnt = 0;
-  for (int i = i0; i < i1; ++i) cnt += (sh.taken[i >> 5] >> (i & 31)) & 1u;
-  sh.scan[t] = cnt;
-  __syncthreads();
-  if (t == 0) {
-    uint32_t acc = 0;
-    for (int x = 0; x < kSelThreads; ++x) {
-      const uint32_t v = sh.scan[x];
-      sh.scan[x] = acc;
-      acc += v;
-    }
-  }
-  __syncthreads();
-  uint32_t o = sh.scan[t];
-  for (int i = i0; i < i1; ++i) {
-    if ((sh.taken[i >> 5] >> (i & 31)) & 1u) {
-      if (int(o) < budget) idx[size_t(row) * budget + o] = i;
+  uint32_t o = block_excl_scan(uint32_t(__popcll(taken)), sh);
+  for (int e = 0; e < kSelPer; ++e) {
+    if ((taken >> e) & 1u) {
+      if (int(o) < budget) idx[size_t(row) * budget + o] = i0 + e;
       ++o;
     }
   }
@@ -454,7 +502,8 @@ hipError_t launch_ckv(const kvc_criticalkv_args& a, void* ws, hipStream_t s) {
   hipLaunchKernelGGL((proj_norm<T>), dim3((n + kTokBlk - 1) / kTokBlk, a.hq), dim3(256), 0, s, v, wt, a.norm, n, G, dm);
   hipLaunchKernelGGL((obs_attn<T, 1>), dim3(chunks, a.hkv), dim3(64 * G), 0, s, q, k, n, G, chunks, part_ml,
                      static_cast<const float*>(nullptr), static_cast<float*>(nullptr));
-  hipLaunchKernelGGL(obs_combine, dim3(a.hkv), dim3(256), 0, s, part_ml, row_ml, G * kObs, chunks);
+  hipLaunchKernelGGL(obs_combine, dim3((G * kObs + 3) / 4, a.hkv), dim3(256), 0, s, part_ml, row_ml, G * kObs,
+                     chunks);
   hipLaunchKernelGGL((obs_attn<T, 2>), dim3(chunks, a.hkv), dim3(64 * G), 0, s, q, k, n, G, chunks,
                      static_cast<float*>(nullptr), row_ml, a.a_head);
   const int64_t tot = int64_t(n) * a.hkv;

@@ -28,10 +28,13 @@
 namespace kvc {
 namespace {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kTB = 256;
 constexpr int kChunk = 8192;     // entries per top-M block (inside one row)
 constexpr int kCChunk = 4096;    // positions per compaction block (inside one row)
 constexpr int kBins = 2048;
+constexpr int kVecPerThread = kChunk / (4 * kTB);  // float4 loads per thread and top-M block
 
 // ---- retention score ----------------------------------------------------------------------------------------
 __global__ __launch_bounds__(kTB) void retention_score_kernel(const float* __restrict__ beta, float* __restrict__ score,
@@ -85,6 +88,29 @@ __device__ __forceinline__ BlockRange block_range(int64_t b, int32_t row_len, in
   return r;
 }
 
+// exclusive prefix (thread order) of one value per thread over a 256-thread block; *total gets the block sum
+template <class V>
+__device__ V block_excl_scan(V v, V* wsum, V* total) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  V inc = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const V o = __shfl_up(inc, d, kWave);
+    if (lane >= d) inc += o;
+  }
+  if (lane == kWave - 1) wsum[wave] = inc;
+  __syncthreads();
+  V base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kTB / kWave; ++w) {
+    base += w < wave ? wsum[w] : V(0);
+    tot += wsum[w];
+  }
+  __syncthreads();
+  *total = tot;
+  return base + inc - v;
+}
+
 __global__ __launch_bounds__(kTB) void topm_clear(TopmWs ws, int32_t* row_counts, int64_t n_rows) {
   const int64_t i = int64_t(blockIdx.x) * kTB + threadIdx.x;
   if (i < 3 * kBins) ws.hist[i] = 0u;
@@ -114,9 +140,16 @@ __global__ __launch_bounds__(kTB) void topm_hist(const float* __restrict__ score
   __syncthreads();
   const uint32_t prefix = P == 0 ? 0u : ws.state->prefix;
   const BlockRange r = block_range(blockIdx.x, row_len, kChunk);
-  for (int64_t e = r.beg + 4 * threadIdx.x; e < r.end; e += 4 * kTB) {
-    const float4 v = *reinterpret_cast<const float4*>(scores + e);
-    const float vs[4] = {v.x, v.y, v.z, v.w};
+  float4 v[kVecPerThread];  // every load of the thread in flight at once (clamped into the block's range)
+#pragma unroll
+  for (int u = 0; u < kVecPerThread; ++u) {
+    const int64_t e = min(r.beg + 4 * (threadIdx.x + kTB * u), r.end - 4);
+    v[u] = *reinterpret_cast<const float4*>(scores + e);
+  }
+#pragma unroll
+  for (int u = 0; u < kVecPerThread; ++u) {
+    if (r.beg + 4 * (threadIdx.x + kTB * u) >= r.end) break;
+    const float vs[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       uint32_t bin;
@@ -136,23 +169,27 @@ __global__ __launch_bounds__(kTB) void topm_pick(TopmWs ws, int64_t m) {
   constexpr int nb = P == 2 ? 1024 : kBins;
   constexpr int per = nb / kTB;
   constexpr int bits = P == 2 ? 10 : 11;
-  __shared__ int64_t part[kTB];
-  const int64_t need = P == 0 ? m : ws.state->need;
-  const uint32_t* hp = ws.hist + P * kBins;
-  int64_t mine = 0;
+  __shared__ long long wsum[kTB / kWave];
+  const long long need = P == 0 ? m : ws.state->need;
+  const uint32_t prev = P == 0 ? 0u : ws.state->prefix;
+  const uint32_t* hp = ws.hist + P * kBins + threadIdx.x * per;
+  uint32_t c[per];
+  long long mine = 0;
 #pragma unroll
-  for (int k = 0; k < per; ++k) mine += hp[threadIdx.x * per + k];
-  part[threadIdx.x] = mine;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int64_t base = 0;
-    int t = 0;
-    while (t < kTB - 1 && base + part[t] < need) base += part[t++];
-    int b = t * per;
-    while (b < t * per + per - 1 && base + int64_t(hp[b]) < need) base += hp[b++];
-    const uint32_t prev = P == 0 ? 0u : ws.state->prefix;
-    ws.state->prefix = (prev << bits) | uint32_t(b);
-    ws.state->need = need - base;
+  for (int k = 0; k < per; ++k) {
+    c[k] = hp[k];
+    mine += c[k];
+  }
+  long long total;
+  const long long excl = block_excl_scan<long long>(mine, wsum, &total);
+  // the thread whose bins hold the need-th key (need <= 0: nothing to take, bin 0; need > total cannot happen)
+  const bool mine_bin = need <= 0 ? threadIdx.x == 0 : (excl < need && excl + mine >= need);
+  if (mine_bin) {
+    long long rem = need - excl;
+    int b = 0;
+    while (b < per - 1 && rem > c[b]) rem -= c[b++];
+    ws.state->prefix = (prev << bits) | uint32_t(threadIdx.x * per + b);
+    ws.state->need = need <= 0 ? 0 : rem;
   }
 }
 
@@ -164,8 +201,17 @@ __global__ __launch_bounds__(kTB) void topm_mark(const float* __restrict__ score
   const BlockRange r = block_range(blockIdx.x, row_len, kChunk);
   uint32_t kept = 0, ties = 0;
   bool nan = false;
-  for (int64_t e = r.beg + 4 * threadIdx.x; e < r.end; e += 4 * kTB) {
-    const float4 v = *reinterpret_cast<const float4*>(scores + e);
+  float4 vv[kVecPerThread];
+#pragma unroll
+  for (int u = 0; u < kVecPerThread; ++u) {
+    const int64_t e = min(r.beg + 4 * (threadIdx.x + kTB * u), r.end - 4);
+    vv[u] = *reinterpret_cast<const float4*>(scores + e);
+  }
+#pragma unroll
+  for (int u = 0; u < kVecPerThread; ++u) {
+    const int64_t e = r.beg + 4 * (threadIdx.x + kTB * u);
+    if (e >= r.end) break;
+    const float4 v = vv[u];
     const float vs[4] = {v.x, v.y, v.z, v.w};
     uint32_t out = 0;
 #pragma unroll
@@ -201,27 +247,17 @@ __global__ __launch_bounds__(kTB) void topm_mark(const float* __restrict__ score
 
 // one workgroup: exclusive scan of the blocks' tie counts -> how many ties each block takes
 __global__ __launch_bounds__(kTB) void topm_tie_scan(TopmWs ws, int64_t n_blocks) {
-  __shared__ int64_t part[kTB];
+  __shared__ long long wsum[kTB / kWave];
   const int64_t per = (n_blocks + kTB - 1) / kTB;
   const int64_t b0 = threadIdx.x * per, b1 = min(n_blocks, b0 + per);
-  int64_t mine = 0;
+  long long mine = 0;
   for (int64_t b = b0; b < b1; ++b) mine += ws.tie_cnt[b];
-  part[threadIdx.x] = mine;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int64_t acc = 0;
-    for (int t = 0; t < kTB; ++t) {
-      const int64_t v = part[t];
-      part[t] = acc;
-      acc += v;
-    }
-  }
-  __syncthreads();
-  const int64_t need = ws.state->need;
-  int64_t off = part[threadIdx.x];
+  long long total;
+  long long off = block_excl_scan<long long>(mine, wsum, &total);
+  const long long need = ws.state->need;
   for (int64_t b = b0; b < b1; ++b) {
-    const int64_t c = ws.tie_cnt[b];
-    ws.tie_take[b] = uint32_t(max(int64_t(0), min(c, need - off)));
+    const long long c = ws.tie_cnt[b];
+    ws.tie_take[b] = uint32_t(max(0LL, min(c, need - off)));
     off += c;
   }
 }
@@ -231,8 +267,7 @@ __global__ __launch_bounds__(kTB) void topm_fix(const float* __restrict__ scores
                                                 int32_t* row_counts, TopmWs ws, int32_t row_len) {
   const uint32_t take = ws.tie_take[blockIdx.x];
   if (take == 0u) return;
-  __shared__ uint32_t pre[kTB];
-  __shared__ uint32_t tot_s;
+  __shared__ uint32_t wsum[kTB / kWave];
   const uint32_t thr = ws.state->prefix;
   const BlockRange r = block_range(blockIdx.x, row_len, kChunk);
   uint32_t done = 0;  // ties already seen before this iteration, in index order
@@ -250,19 +285,8 @@ __global__ __launch_bounds__(kTB) void topm_fix(const float* __restrict__ scores
         }
       }
     }
-    pre[threadIdx.x] = cnt;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      uint32_t acc = 0;
-      for (int t = 0; t < kTB; ++t) {
-        const uint32_t v = pre[t];
-        pre[t] = acc;
-        acc += v;
-      }
-      tot_s = acc;
-    }
-    __syncthreads();
-    uint32_t rank = done + pre[threadIdx.x];
+    uint32_t tot;
+    uint32_t rank = done + block_excl_scan<uint32_t>(cnt, wsum, &tot);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       if ((flags >> c) & 1u) {
@@ -270,8 +294,7 @@ __global__ __launch_bounds__(kTB) void topm_fix(const float* __restrict__ scores
         ++rank;
       }
     }
-    done += tot_s;
-    __syncthreads();
+    done += tot;
     if (done >= take) break;
   }
   if (threadIdx.x == 0) atomicAdd(&row_counts[r.row], int(take));
@@ -301,10 +324,10 @@ __global__ __launch_bounds__(kTB) void compact_count(const uint8_t* __restrict__
 __global__ __launch_bounds__(kTB) void compact_plan(CompactWs ws, int64_t n_rows, int32_t chunks, int32_t page,
                                                     int32_t* lengths, int32_t* page_offset, int32_t* n_pages,
                                                     int64_t out_pages_max, int32_t* status) {
-  __shared__ int64_t part[kTB];
+  __shared__ long long wsum[kTB / kWave];
   const int64_t per = (n_rows + kTB - 1) / kTB;
   const int64_t r0 = threadIdx.x * per, r1 = min(n_rows, r0 + per);
-  int64_t mine = 0;
+  long long mine = 0;
   for (int64_t row = r0; row < r1; ++row) {
     int off = 0;
     for (int c = 0; c < chunks; ++c) {
@@ -316,85 +339,79 @@ __global__ __launch_bounds__(kTB) void compact_plan(CompactWs ws, int64_t n_rows
     n_pages[row] = np;
     mine += np;
   }
-  part[threadIdx.x] = mine;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int64_t acc = 0;
-    for (int t = 0; t < kTB; ++t) {
-      const int64_t v = part[t];
-      part[t] = acc;
-      acc += v;
-    }
-    if (acc > out_pages_max) atomicOr(status, KVC_DEV_BOUND_EXCEEDED);
-  }
-  __syncthreads();
-  int64_t off = part[threadIdx.x];
+  long long total;
+  long long off = block_excl_scan<long long>(mine, wsum, &total);
+  if (threadIdx.x == 0 && total > out_pages_max) atomicOr(status, KVC_DEV_BOUND_EXCEEDED);
   for (int64_t row = r0; row < r1; ++row) {
     page_offset[row] = int32_t(off);
     off += n_pages[row];
   }
 }
 
-// ordered copy of the kept rows of one (row, chunk): ranks by a block scan over 16-position runs, then 16 lanes
-// per copied 128-element row (one 16-byte access each for K and V)
+// ordered copy of the kept rows of one (row, chunk): the chunk's page ids go to LDS in one coalesced read, ranks
+// come from a block scan over 16-position runs, then 16 lanes copy one 128-element row (one 16-byte access each
+// for K and V), four rows per thread with every load issued before the stores
 __global__ __launch_bounds__(kTB) void compact_copy(const uint8_t* __restrict__ keep, const int32_t* __restrict__ pt,
                                                     const uint4* __restrict__ k_pool, const uint4* __restrict__ v_pool,
                                                     uint4* __restrict__ k_out, uint4* __restrict__ v_out, CompactWs ws,
                                                     const int32_t* __restrict__ page_offset, int32_t row_len,
                                                     int32_t page, int64_t n_src_pages, int64_t out_pages_max,
                                                     int32_t* status) {
-  __shared__ int pre[kTB];
-  __shared__ int64_t src_s[kCChunk];
-  __shared__ int64_t dst_s[kCChunk];
+  __shared__ int32_t src_s[kCChunk];
+  __shared__ int32_t pg_s[kCChunk];  // page id per block of `page` positions of the chunk (page >= 1)
+  __shared__ int wsum[kTB / kWave];
   const BlockRange r = block_range(blockIdx.x, row_len, kCChunk);
   const int64_t pos0 = r.beg - r.row * row_len;  // first position of the chunk within its row
+  const int npg = int((r.end - r.beg + page - 1) / page);
+  const int32_t* ptr = pt + r.row * (row_len / page) + pos0 / page;
+  for (int i = threadIdx.x; i < npg; i += kTB) pg_s[i] = ptr[i];
   const int64_t e = r.beg + 16 * threadIdx.x;
   uint32_t bits = 0;
-  int cnt = 0;
   if (e < r.end) {
     const uint4 v = *reinterpret_cast<const uint4*>(keep + e);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int j = 0; j < 16; ++j) bits |= ((w[j >> 2] >> (8 * (j & 3))) & 1u) << j;
-    cnt = __popc(bits);
   }
-  pre[threadIdx.x] = cnt;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int t = 0; t < kTB; ++t) {
-      const int v = pre[t];
-      pre[t] = acc;
-      acc += v;
-    }
-  }
-  __syncthreads();
-  const int n_kept = pre[kTB - 1] + (threadIdx.x == kTB - 1 ? cnt : 0);
-  const int64_t dst0 = int64_t(page_offset[r.row]) * page + ws.chunk_off[blockIdx.x];
-  int k = pre[threadIdx.x];
+  int nk;
+  int k = block_excl_scan<int>(__popc(bits), wsum, &nk);  // (contains the barrier that publishes pg_s)
   bool bad = false;
   for (int j = 0; j < 16; ++j) {
     if ((bits >> j) & 1u) {
-      const int64_t pos = pos0 + 16 * threadIdx.x + j;
-      const int64_t src_page = pt[r.row * (row_len / page) + pos / page];
+      const int p = 16 * threadIdx.x + j;  // position within the chunk (pos0 is a multiple of page)
+      const int64_t src_page = pg_s[p / page];
       const bool ok = src_page >= 0 && src_page < n_src_pages;
       bad |= !ok;
-      src_s[k] = ok ? src_page * page + pos % page : -1;
-      dst_s[k] = dst0 + k;
-      ++k;
+      src_s[k++] = ok ? int32_t(src_page * page + p % page) : -1;
     }
   }
   if (bad) atomicOr(status, KVC_DEV_BOUND_EXCEEDED);
-  __shared__ int tot_s;
-  if (threadIdx.x == kTB - 1) tot_s = n_kept;
   __syncthreads();
-  const int nk = tot_s;
+  const int64_t dst0 = int64_t(page_offset[r.row]) * page + ws.chunk_off[blockIdx.x];
+  const int64_t cap = out_pages_max * page;
   const int sub = threadIdx.x & 15;
-  for (int i = threadIdx.x >> 4; i < nk; i += kTB / 16) {
-    const int64_t s = src_s[i], d = dst_s[i];
-    if (s < 0 || d >= out_pages_max * page) continue;
-    k_out[d * 16 + sub] = k_pool[s * 16 + sub];
-    v_out[d * 16 + sub] = v_pool[s * 16 + sub];
+  for (int i0 = threadIdx.x >> 4; i0 < nk; i0 += 4 * (kTB / 16)) {
+    u32x4 kv[4], vv[4];
+    int src[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = min(i0 + u * (kTB / 16), nk - 1);
+      src[u] = src_s[i];
+      const size_t sidx = size_t(max(src[u], 0)) * 16 + sub;  // row 0 stands in for a rejected page id
+      kv[u] = reinterpret_cast<const u32x4*>(k_pool)[sidx];
+      vv[u] = reinterpret_cast<const u32x4*>(v_pool)[sidx];
+    }
+    // keep the eight loads ahead of the conditional stores (else each pair is sunk into its store's branch)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) asm volatile("" ::"v"(kv[u]), "v"(vv[u]));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * (kTB / 16);
+      if (i < nk && src[u] >= 0 && dst0 + i < cap) {
+        reinterpret_cast<u32x4*>(k_out)[size_t(dst0 + i) * 16 + sub] = kv[u];
+        reinterpret_cast<u32x4*>(v_out)[size_t(dst0 + i) * 16 + sub] = vv[u];
+      }
+    }
   }
 }
 
