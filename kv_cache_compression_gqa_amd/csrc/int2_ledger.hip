@@ -76,8 +76,19 @@ __device__ void unit_prefix(const int32_t* count, int U, int stride, int* pre) {
   const int wave = threadIdx.x >> 6;
   const int seg = (U + kBlock - 1) / kBlock;
   const int lo = min(U, int(threadIdx.x) * seg), hi = min(U, lo + seg);
+  // the thread's counts are fetched 8 at a time (independent loads in flight together)
   int local = 0;
-  for (int i = lo; i < hi; ++i) local += min(max(0, count[i]), stride);
+  for (int i0 = lo; i0 < hi; i0 += 8) {
+    int v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = i0 + k < hi ? count[i0 + k] : 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      pre[i0 + k < hi ? i0 + k : U] = min(max(0, v[k]), stride);  // clamped count, scanned below
+      local += min(max(0, v[k]), stride);
+    }
+  }
+  __syncthreads();
   int inc = local;
   for (int d = 1; d < kWave; d <<= 1) {
     const int a = __shfl_up(inc, d, kWave);
@@ -89,9 +100,11 @@ __device__ void unit_prefix(const int32_t* count, int U, int stride, int* pre) {
   for (int w = 0; w < wave; ++w) base += wave_tot[w];
   int run = base + inc - local;
   for (int i = lo; i < hi; ++i) {
+    const int c = pre[i];
     pre[i] = run;
-    run += min(max(0, count[i]), stride);
+    run += c;
   }
+  __syncthreads();
   if (threadIdx.x == kBlock - 1) pre[U] = run;
   __syncthreads();
 }

@@ -31,22 +31,38 @@ def _bits(a: np.ndarray, device):
 
 
 class DecodeSession:
+    """``unit_map`` (optional, [U] ints): unit u of the session starts from held unit ``unit_map[u]`` of ``inp``
+    (its cache, tail and per-step inputs are copied on the device), so that many units can share one seeded
+    draw while every unit keeps memory and state of its own."""
+
     def __init__(self, inp: DecodeInputs, device="cuda", tail_max: int | None = None, steps: int | None = None,
-                 budgets=None):
+                 budgets=None, unit_map=None):
         cfg = inp.cfg
         self.cfg = cfg
         self.inp = inp
         self.device = torch.device(device)
-        U = len(inp.units)
+        dev = self.device
+        umap = np.arange(len(inp.units)) if unit_map is None else np.asarray(unit_map, np.int64)
+        self.unit_map = umap
+        idx = torch.from_numpy(umap).to(dev)
+
+        def expand(t):  # held units -> session units (device gather)
+            return t if unit_map is None else t.index_select(0, idx).contiguous()
+
+        def expand_steps(t):
+            return t if unit_map is None else t.index_select(1, idx).contiguous()
+
+        n_windows_u = inp.n_windows[umap]
+        tail0_u = inp.tail0[umap]
+        U = len(umap)
         NW = inp.n_windows_max
         W, D, G = cfg.window, cfg.head_dim, cfg.group
         S = inp.q.shape[0] if steps is None else steps
         self.U, self.NW, self.G, self.D, self.W = U, NW, G, D, W
         tm = tail_max if tail_max is not None else int(inp.tail0.max()) + S + 1
         self.TM = max(32, (tm + 31) // 32 * 32)
-        dev = self.device
-        self.k_win = _bits(inp.k_win, dev)
-        self.v_win = _bits(layout.v_win_to_lib(inp.v_win), dev)   # [U][NW][D][W]
+        self.k_win = expand(_bits(inp.k_win, dev))
+        self.v_win = expand(_bits(layout.v_win_to_lib(inp.v_win), dev))   # [U][NW][D][W]
         self.k_codes = torch.zeros((U, NW, W, D // 4), dtype=torch.uint8, device=dev)
         self.v_codes = torch.zeros((U, NW, 16, 4, 8), dtype=torch.int16, device=dev)
         self.k_meta = torch.zeros((U, NW, W, D // 32), dtype=torch.int32, device=dev)
@@ -55,29 +71,29 @@ class DecodeSession:
         self.v_tail = torch.zeros((U, self.TM // W, D, W), dtype=torch.int16, device=dev)
         t0 = int(inp.tail0.max())
         if t0 > 0:
-            self.k_tail[:, :t0] = _bits(inp.k_tail0[:, :t0], dev)
-            vt = np.zeros((U, W, D), np.uint16)
+            self.k_tail[:, :t0] = expand(_bits(inp.k_tail0[:, :t0], dev))
+            vt = np.zeros((len(inp.units), W, D), np.uint16)
             vt[:, :t0] = inp.v_tail0[:, :t0]
-            self.v_tail[:, 0] = _bits(layout.v_tail_to_lib(vt)[:, 0], dev)
-        self.tail_len = _dev(inp.tail0.astype(np.int32), torch.int32, dev)
-        self.n_windows = _dev(inp.n_windows.astype(np.int32), torch.int32, dev)
+            self.v_tail[:, 0] = expand(_bits(layout.v_tail_to_lib(vt)[:, 0], dev))
+        self.tail_len = _dev(tail0_u.astype(np.int32), torch.int32, dev)
+        self.n_windows = _dev(n_windows_u.astype(np.int32), torch.int32, dev)
         self.tier = torch.zeros((U, NW), dtype=torch.int8, device=dev)
         self.ledgered = torch.zeros((U, NW), dtype=torch.uint8, device=dev)
         self.cum = torch.zeros((U, NW), dtype=torch.float32, device=dev)
         res = np.tile(np.arange(NW, dtype=np.int32), (U, 1))
         self.res_list = _dev(res, torch.int32, dev)
-        self.n_full = _dev(inp.n_windows.astype(np.int32), torch.int32, dev)
+        self.n_full = _dev(n_windows_u.astype(np.int32), torch.int32, dev)
         self.n_int2 = torch.zeros(U, dtype=torch.int32, device=dev)
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
         # per-step inputs
-        self.q = _bits(inp.q, dev)
-        self.k_new = _bits(inp.k_new, dev)
-        self.v_new = _bits(inp.v_new, dev)
+        self.q = expand_steps(_bits(inp.q, dev))
+        self.k_new = expand_steps(_bits(inp.k_new, dev))
+        self.v_new = expand_steps(_bits(inp.v_new, dev))
         self.out = torch.zeros((U, G, D), dtype=torch.float32, device=dev)
         # budgets
         if budgets is None:
-            bf = np.array([cfg.budgets(int(n))[0] for n in inp.n_windows], np.int32)
-            bq = np.array([cfg.budgets(int(n))[1] for n in inp.n_windows], np.int32)
+            bf = np.array([cfg.budgets(int(n))[0] for n in n_windows_u], np.int32)
+            bq = np.array([cfg.budgets(int(n))[1] for n in n_windows_u], np.int32)
         else:
             bf, bq = (np.asarray(b, np.int32) for b in budgets)
         self.bf_host, self.bq_host = bf, bq
@@ -88,9 +104,9 @@ class DecodeSession:
         self.n_quant = torch.zeros(U, dtype=torch.int32, device=dev)
         self.n_promo = torch.zeros(U, dtype=torch.int32, device=dev)
         # host-side bounds (never read back from the device)
-        self.h_full = inp.n_windows.astype(np.int64).copy()
+        self.h_full = n_windows_u.astype(np.int64).copy()
         self.h_int2 = np.zeros(U, np.int64)
-        self.h_tail = inp.tail0.astype(np.int64).copy()
+        self.h_tail = tail0_u.astype(np.int64).copy()
         self.t = 0
         self._cache = abi.KvcCache(
             n_units=U, group=G, head_dim=D, window=W, n_windows_max=NW, tail_max=self.TM,

@@ -132,6 +132,18 @@ def make_decode(cfg: DecodeWorkload, units=None, steps: int | None = None) -> De
                         k_tail0=k_t, v_tail0=v_t, q=q, k_new=kn, v_new=vn, salient=sal_list)
 
 
+def make_decode_shared_layers(cfg: DecodeWorkload, steps: int | None = None):
+    """Held inputs for the units of layer 0 (one seeded draw per (sequence, KV head), each at its sequence's
+    length) and the map that starts every unit (layer l, b, g) from held unit (0, b, g). The layers then share
+    their initial contents while each keeps memory and state of its own; generating every layer's draw on the
+    host would take minutes at 32 layers x batch 16."""
+    base = np.array([cfg.unit_index(0, b, g) for b in range(cfg.batch) for g in range(cfg.hkv)], dtype=np.int64)
+    inp = make_decode(cfg, units=base, steps=steps)
+    umap = np.array([cfg.unit_coords(u)[1] * cfg.hkv + cfg.unit_coords(u)[2] for u in range(cfg.n_units)],
+                    dtype=np.int64)
+    return inp, umap
+
+
 # ----------------------------------------------------------------------------------------------------------
 # CriticalKV prefill-selection inputs
 

@@ -40,63 +40,70 @@ def row_check(name, g, r, rtol=RTOL):
         assert err <= lim, f"{name} head {h}: max err {err} > {lim}"
 
 
-def make_oracles(inp, units=None):
+def make_oracles(inp, units=None, unit_map=None):
+    """Oracle units keyed by session unit j (held unit unit_map[j] of ``inp``)."""
+    umap = np.arange(len(inp.units)) if unit_map is None else np.asarray(unit_map)
     out = {}
-    for j in (range(len(inp.units)) if units is None else units):
-        nw = int(inp.n_windows[j])
-        t0 = int(inp.tail0[j])
-        out[j] = QEvictUnit(inp.k_win[j, :nw], inp.v_win[j, :nw], inp.k_tail0[j, :t0], inp.v_tail0[j, :t0],
+    for j in (range(len(umap)) if units is None else units):
+        b = int(umap[j])
+        nw = int(inp.n_windows[b])
+        t0 = int(inp.tail0[b])
+        out[j] = QEvictUnit(inp.k_win[b, :nw], inp.v_win[b, :nw], inp.k_tail0[b, :t0], inp.v_tail0[b, :t0],
                             inp.cfg.dtype)
     return out
 
 
 def compare_route(sess: DecodeSession, oracles, gpu_cum):
-    tier = sess.tier.cpu().numpy()
-    res = sess.res_list.cpu().numpy()
-    nf = sess.n_full.cpu().numpy()
-    nq = sess.n_int2.cpu().numpy()
-    qn = sess.n_quant.cpu().numpy()
-    ql = sess.quant_list.cpu().numpy()
-    pn = sess.n_promo.cpu().numpy()
-    pl = sess.promo_list.cpu().numpy()
-    led = sess.ledgered.cpu().numpy()
-    kc = sess.k_codes.cpu().numpy()
-    vc = sess.v_codes.cpu().numpy().view(np.uint16)
-    km = sess.k_meta.cpu().numpy().view(np.uint32)
-    vm = sess.v_meta.cpu().numpy().view(np.uint32)
-    kw = sess.k_win.cpu().numpy().view(np.uint16)
-    vw = sess.v_win.cpu().numpy().view(np.uint16)
-    for j, o in oracles.items():
+    """Routing of the oracle units (fed the GPU's cumulative scores) against the session: tiers, resident lists,
+    plan lists, ledger flags and bytes, full-precision copies of resident FULL windows. Only the checked units'
+    rows are copied to the host."""
+    keys = sorted(oracles)
+    sel = torch.tensor(keys, dtype=torch.int64, device=sess.device)
+    g = lambda t: t.index_select(0, sel).cpu().numpy()  # noqa: E731
+    tier, res, nf, nq = g(sess.tier), g(sess.res_list), g(sess.n_full), g(sess.n_int2)
+    qn, ql, pn, pl, led = g(sess.n_quant), g(sess.quant_list), g(sess.n_promo), g(sess.promo_list), g(sess.ledgered)
+    kc = g(sess.k_codes)
+    vc = g(sess.v_codes).view(np.uint16)
+    km = g(sess.k_meta).view(np.uint32)
+    vm = g(sess.v_meta).view(np.uint32)
+    kw = g(sess.k_win).view(np.uint16)
+    vw = g(sess.v_win).view(np.uint16)
+    for r, j in enumerate(keys):
+        o = oracles[j]
         nw = o.n_windows
         plan = o.route(int(sess.bf_host[j]), int(sess.bq_host[j]), scores=gpu_cum[j, :nw])
-        np.testing.assert_array_equal(tier[j, :nw], o.tier, err_msg=f"tiers unit {j}")
+        np.testing.assert_array_equal(tier[r, :nw], o.tier, err_msg=f"tiers unit {j}")
         full, q2 = o.resident_windows()
-        assert nf[j] == full.size and nq[j] == q2.size
-        np.testing.assert_array_equal(res[j, :nf[j]], full)
-        np.testing.assert_array_equal(res[j, nf[j]:nf[j] + nq[j]], q2)
-        np.testing.assert_array_equal(ql[j, :qn[j]], plan.quantized)
-        np.testing.assert_array_equal(pl[j, :pn[j]], plan.promoted)
+        assert nf[r] == full.size and nq[r] == q2.size
+        np.testing.assert_array_equal(res[r, :nf[r]], full)
+        np.testing.assert_array_equal(res[r, nf[r]:nf[r] + nq[r]], q2)
+        np.testing.assert_array_equal(ql[r, :qn[r]], plan.quantized)
+        np.testing.assert_array_equal(pl[r, :pn[r]], plan.promoted)
         for w in range(nw):
-            assert bool(led[j, w]) == (w in o.ledger), f"ledger flag unit {j} window {w}"
+            assert bool(led[r, w]) == (w in o.ledger), f"ledger flag unit {j} window {w}"
         for w, e in o.ledger.items():
-            assert kc[j, w].tobytes() == layout.k_codes_to_lib(e["kc"]).tobytes(), f"K codes unit {j} window {w}"
-            assert vc[j, w].tobytes() == layout.v_codes_to_lib(e["vc"]).tobytes(), f"V codes unit {j} window {w}"
-            assert km[j, w].tobytes() == layout.k_meta_to_lib(e["ks"], e["kz"]).tobytes(), f"K meta {j} {w}"
-            assert vm[j, w].tobytes() == layout.v_meta_to_lib(e["vs"], e["vz"]).tobytes(), f"V meta {j} {w}"
+            assert kc[r, w].tobytes() == layout.k_codes_to_lib(e["kc"]).tobytes(), f"K codes unit {j} window {w}"
+            assert vc[r, w].tobytes() == layout.v_codes_to_lib(e["vc"]).tobytes(), f"V codes unit {j} window {w}"
+            assert km[r, w].tobytes() == layout.k_meta_to_lib(e["ks"], e["kz"]).tobytes(), f"K meta {j} {w}"
+            assert vm[r, w].tobytes() == layout.v_meta_to_lib(e["vs"], e["vz"]).tobytes(), f"V meta {j} {w}"
         for w in full:
-            assert kw[j, w].tobytes() == o.kw[w].tobytes(), f"K full copy unit {j} window {w}"
-            assert layout.v_win_from_lib(vw[j, w]).tobytes() == o.vw[w].tobytes(), f"V full copy unit {j} window {w}"
+            assert kw[r, w].tobytes() == o.kw[w].tobytes(), f"K full copy unit {j} window {w}"
+            assert layout.v_win_from_lib(vw[r, w]).tobytes() == o.vw[w].tobytes(), f"V full copy unit {j} window {w}"
 
 
-def run_decode_parity(cfg, units=None, steps=None, check_units=None, check_steps=None, probs=True, log=print):
+def run_decode_parity(cfg, units=None, steps=None, check_units=None, check_steps=None, probs=True, log=print,
+                      inp=None, unit_map=None):
     """Run ``steps`` decode steps (routing on the workload's cadence) on the GPU for every unit, and on the oracle
     for the units in ``check_units`` (default all; units are independent, so a sample of them is followed exactly).
-    Outputs are compared at every step in ``check_steps`` (default all); routing at every event."""
-    inp = synth.make_decode(cfg, units=units, steps=steps)
+    Outputs are compared at every step in ``check_steps`` (default all); routing at every event. ``inp`` and
+    ``unit_map`` (optional) give held inputs and the held unit each session unit starts from."""
+    if inp is None:
+        inp = synth.make_decode(cfg, units=units, steps=steps)
     S = inp.q.shape[0]
-    sess = DecodeSession(inp)
-    U = len(inp.units)
-    oracles = make_oracles(inp, check_units)
+    sess = DecodeSession(inp, unit_map=unit_map)
+    U = sess.U
+    umap = sess.unit_map
+    oracles = make_oracles(inp, check_units, unit_map)
     check_steps = set(range(S)) if check_steps is None else set(check_steps)
     for t in range(S):
         stride = sess.probs_stride()
@@ -109,7 +116,8 @@ def run_decode_parity(cfg, units=None, steps=None, check_units=None, check_steps
         mass_h = mass.cpu().numpy()
         cum_h = sess.cum.cpu().numpy()
         for j, o in oracles.items():
-            r = o.step(inp.q[t, j], inp.k_new[t, j], inp.v_new[t, j])
+            b = int(umap[j])
+            r = o.step(inp.q[t, b], inp.k_new[t, b], inp.v_new[t, b])
             if t not in check_steps:
                 continue
             nw = oracles[j].n_windows

@@ -177,3 +177,15 @@ def test_score_only_matches_decode(gpu_lib):
     assert torch.equal(s1.cum, s2.cum)
     assert torch.equal(s1.tail_len, s2.tail_len)
     assert torch.all(s2.out == 0)
+
+
+def test_batched_32_layers_batch_16_full_size(gpu_lib):
+    """4096 units (32 layers x batch 16 x 8 KV heads), lengths uniform in [4096, 8192] per sequence, 25% FULL +
+    25% INT2 per unit, routing after every step: every unit runs on the GPU; sampled units across layers,
+    sequences and heads follow the oracle exactly (outputs, probabilities, mass and cum every step; tiers,
+    lists, ledger and promoted copies at every routing event)."""
+    cfg = configs.BATCHED_32L_B16
+    inp, umap = synth.make_decode_shared_layers(cfg)
+    print(f"batched: {cfg.n_units} units, lengths {sorted(set(inp.lengths.tolist()))[:3]}..", flush=True)
+    check = [0, 9, 130, 1234, 2048 + 77, cfg.n_units - 1]
+    run_decode_parity(cfg, inp=inp, unit_map=umap, check_units=check, probs=True)
