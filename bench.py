@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch steps eagerly instead of one captured graph")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run one plain device-to-device copy of this many MiB (counter calibration)")
     ap.add_argument("--workload", default="llama3_8b_layer_32k",
                     choices=["llama3_8b_layer_32k", "batched_32l_b16", "criticalkv_64k", "dbtrim_128k"],
                     help="the decode step (default), the CriticalKV prefill selection or the DBTrimKV global budget")
@@ -156,6 +158,12 @@ def main():
         sessions[i % R].step()
     torch.cuda.synchronize()
     print(f"warm-up done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    if args.copy_mib > 0:
+        src = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     K = args.steps
     plan = []  # (bytes, positions) per timed step, from the host-side counts at the time the step is issued
