@@ -617,6 +617,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
 // the partials' (m, l) per head (one pass, fixed order), weights and sums its outputs in a fixed order (bitwise
 // reproducible), and turns its windows' exp-sums into probability mass.
 constexpr int kPre = 8;
+constexpr int kMlPre = 4;
 
 template <int G>
 __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
@@ -645,29 +646,37 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
     ov[k] = in ? po[size_t(cc) * G * kD] : 0.0f;
     mv[k] = in ? ml[(cc * G + h_out) * 2] : -INFINITY;
   }
+  // first window of this thread: unconditional loads (index clamped into the unit), used only if w0 < we
   const int w0 = wb + int(threadIdx.x);
-  bool res0 = false;
-  float ws0[G], wr0[G], cum0 = 0.0f;
+  const int w0c = min(w0, p.NW - 1);
+  const int tier0 = p.tier[unit_win + w0c];
+  float ws0[G], wr0[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    ws0[h] = 0.0f;
-    wr0[h] = -INFINITY;
+    ws0[h] = p.wsum[(unit_win + w0c) * G + h];
+    wr0[h] = p.wref[(unit_win + w0c) * G + h];
   }
-  if (w0 < we) {
-    res0 = p.tier[unit_win + w0] != KVC_TIER_EVICTED;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      ws0[h] = p.wsum[(unit_win + w0) * G + h];
-      wr0[h] = p.wref[(unit_win + w0) * G + h];
-    }
-    if (p.accumulate) cum0 = p.cum[unit_win + w0];
-  }
+  const float cum0 = p.cum[unit_win + w0c];
 
   __shared__ float sM[G], sInvL[G];
   __shared__ float red[256];
   for (int h = wave; h < G; h += 4) {
+    // the lane's first kMlPre (m, l) pairs are loaded together, the rest (more than 256 partials) in a loop
+    float pm[kMlPre], pl[kMlPre];
+#pragma unroll
+    for (int k = 0; k < kMlPre; ++k) {
+      const int cc = lane + kWave * k;
+      pm[k] = cc < CH ? ml[(cc * G + h) * 2] : -INFINITY;
+      pl[k] = cc < CH ? ml[(cc * G + h) * 2 + 1] : 0.0f;
+    }
     float mr = -INFINITY, lr = 0.0f;
-    for (int cc = lane; cc < CH; cc += kWave) {
+#pragma unroll
+    for (int k = 0; k < kMlPre; ++k) {
+      const float mn = fmaxf(mr, pm[k]);
+      lr = lr * exp_diff(mr, mn) + pl[k] * exp_diff(pm[k], mn);
+      mr = mn;
+    }
+    for (int cc = lane + kWave * kMlPre; cc < CH; cc += kWave) {
       const float mc = ml[(cc * G + h) * 2], lc = ml[(cc * G + h) * 2 + 1];
       const float mn = fmaxf(mr, mc);
       lr = lr * exp_diff(mr, mn) + lc * exp_diff(mc, mn);
@@ -698,7 +707,7 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
   }
   // window mass = (1/G) sum_h wsum * exp(wref - M_h) / L_h; cumulative score += mass
   for (int w = w0; w < we; w += 256) {
-    bool resident = res0;
+    bool resident = tier0 != KVC_TIER_EVICTED;
     float cw = cum0;
     if (w != w0) {
       resident = p.tier[unit_win + w] != KVC_TIER_EVICTED;
