@@ -31,13 +31,18 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-file device flags. criticalkv.hip: MFMA accumulators in ordinary VGPRs, so that the |.| sums of a finished
+# tile read them directly while the next tile's MFMAs run (no accumulator-register copies).
+FILE_FLAGS = {"criticalkv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON_FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -40,7 +40,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kObs = 32;           // observation queries
 constexpr int kObsChunk = 512;     // keys per obs_attn workgroup
 constexpr int kTokBlk = 256;       // tokens per proj_norm workgroup
-constexpr int kColBlk = 32;        // output columns per LDS block
+constexpr int kColBlk = 64;        // output columns per LDS block
+constexpr int kWPieces = kColBlk * 128 / 8 / 256;  // 16-byte pieces of one W block per proj_norm thread
 constexpr int kWtStride = kD + 8;  // LDS row of one output column: 128 head_dim + 8 padding (272 bytes)
 constexpr float kInvSqrtD = 0.088388347648318440550f;
 
@@ -102,53 +103,75 @@ __global__ __launch_bounds__(256) void proj_norm(const uint16_t* __restrict__ v,
     for (int j = 0; j < 8; ++j) a[t][j] = ld16(v + (size_t(g) * n + tok) * kD + 16 * j + 8 * (lane >> 5));
   }
   const uint16_t* wh = wt + size_t(h) * dm * kD;
-  // W block cb: columns 32cb .. 32cb+31, 256 contiguous bytes each; thread i moves 16-byte pieces i and i + 256
-  auto load_w = [&](int cb, u32x4 (&r)[2]) {
+  // W block cb: columns kColBlk*cb .., 256 contiguous bytes each; thread i moves the 16-byte pieces i + 256k
+  auto load_w = [&](int cb, u32x4 (&r)[kWPieces]) {
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < kWPieces; ++k) {
       const int idx = threadIdx.x + 256 * k;
       r[k] = ld16(wh + size_t(kColBlk * cb + (idx >> 4)) * kD + 8 * (idx & 15));
     }
   };
-  auto store_w = [&](int buf, const u32x4 (&r)[2]) {
+  auto store_w = [&](int buf, const u32x4 (&r)[kWPieces]) {
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < kWPieces; ++k) {
       const int idx = threadIdx.x + 256 * k;
       *reinterpret_cast<u32x4*>(&wl[buf][(idx >> 4) * kWtStride + 8 * (idx & 15)]) = r[k];
     }
   };
-  float part[2][16];
+  // B fragments of the 32 columns 32sb .. 32sb+31 of LDS block buf: column lane%32, k = 16j + 8*(lane/32) .. +7
+  auto read_b = [&](int buf, int sb, u32x4 (&b)[8]) {
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+    for (int j = 0; j < 8; ++j)
+      b[j] = *reinterpret_cast<const u32x4*>(&wl[buf][(32 * sb + (lane & 31)) * kWtStride + 16 * j + 8 * (lane >> 5)]);
+  };
+  // One tile's 8 MFMAs with the |.| sums of the previously finished tile interleaved between them (the VALU runs
+  // while the matrix core works); the fence keeps the whole chain inside this phase.
+  auto phase = [&](const u32x4 (&at)[8], const u32x4 (&b)[8], f32x16& part, const f32x16& done) {
+    f32x16 c = Mfma<T>::m32(at[0], b[0], f32x16{});
 #pragma unroll
-    for (int i = 0; i < 16; ++i) part[t][i] = 0.0f;
-  }
-  u32x4 pre[2];
+    for (int j = 1; j < 8; ++j) c = Mfma<T>::m32(at[j], b[j], c);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) part[i] += fabsf(done[i]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read of the next B fragments, if any
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+    }
+    asm volatile("" : "+v"(c));
+    __builtin_amdgcn_sched_barrier(0);
+    return c;
+  };
+  // Software pipeline: while the MFMAs of one tile run, the VALU adds up the |.| of the tile finished before it.
+  f32x16 part0 = f32x16{}, part1 = f32x16{}, acc0, acc1 = f32x16{};
+  u32x4 pre[kWPieces];
   load_w(0, pre);
   store_w(0, pre);
   __syncthreads();
   const int ncb = dm / kColBlk;
   for (int cb = 0; cb < ncb; ++cb) {
     const int buf = cb & 1;
-    const bool more = cb + 1 < ncb;
-    if (more) load_w(cb + 1, pre);
-    f32x16 acc[2];
+    load_w(min(cb + 1, ncb - 1), pre);
+    u32x4 b[8];
+    read_b(buf, 0, b);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) acc[t] = f32x16{};
+    for (int sb = 0; sb < kColBlk / 32; ++sb) {
+      acc0 = phase(a[0], b, part1, acc1);
+      u32x4 bn[8];
+      if (sb + 1 < kColBlk / 32) read_b(buf, sb + 1, bn);
+      acc1 = phase(a[1], b, part0, acc0);
+      if (sb + 1 < kColBlk / 32) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const u32x4 b = *reinterpret_cast<const u32x4*>(&wl[buf][(lane & 31) * kWtStride + 16 * j + 8 * (lane >> 5)]);
-      acc[0] = Mfma<T>::m32(a[0][j], b, acc[0]);
-      acc[1] = Mfma<T>::m32(a[1][j], b, acc[1]);
+        for (int j = 0; j < 8; ++j) b[j] = bn[j];
+      }
     }
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) part[t][i] += fabsf(acc[t][i]);
-    }
-    if (more) store_w(buf ^ 1, pre);
+    store_w(buf ^ 1, pre);  // the last block's copy lands in the buffer no later block reads
     __syncthreads();
   }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) part1[i] += fabsf(acc1[i]);
+  const f32x16 part[2] = {part0, part1};
   // row sums over the 32 columns (lanes of one half-wave); D row of acc[i]: 8*(i/4) + 4*(lane/32) + i%4
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
