@@ -41,8 +41,7 @@ constexpr int kObs = 32;           // observation queries
 constexpr int kObsChunk = 512;     // keys per obs_attn workgroup
 constexpr int kTokBlk = 256;       // tokens per proj_norm workgroup
 constexpr int kColBlk = 64;        // output columns per LDS block
-constexpr int kWPieces = kColBlk * 128 / 8 / 256;  // 16-byte pieces of one W block per proj_norm thread
-constexpr int kWtStride = kD + 8;  // LDS row of one output column: 128 head_dim + 8 padding (272 bytes)
+static_assert(kColBlk == 64, "proj_norm's pipeline is written for two 32-column sub-blocks per W block");
 constexpr float kInvSqrtD = 0.088388347648318440550f;
 
 template <class T> struct Mfma;
@@ -87,12 +86,22 @@ __global__ __launch_bounds__(256) void wo_transpose(const uint16_t* __restrict__
 }
 
 // ---- N = |V_g W_O,h|_1 per token ------------------------------------------------------------------------------
+// W blocks reach LDS through the load unit directly (global_load_lds_dwordx4: lane i of a wave writes 16 bytes at
+// M0 + 16 i), issued as inline asm so that the compiler, which cannot tell which LDS bytes such a load writes, does
+// not wait for it before every LDS read; the kernel waits for it explicitly before the barrier that publishes it.
+// Nothing else in proj_norm uses M0.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
+}
+
+// Column c of an LDS W block holds its 16 chunks of 8 head_dim values with chunk q at slot q ^ (c % 16), so the
+// 16 columns of one B-fragment read hit 16 distinct 16-byte bank groups.
 template <class T>
 __global__ __launch_bounds__(256) void proj_norm(const uint16_t* __restrict__ v, const uint16_t* __restrict__ wt,
                                                  float* __restrict__ norm, int n, int group, int dm) {
-  __shared__ __attribute__((aligned(16))) uint16_t wl[2][kColBlk * kWtStride];
+  __shared__ __attribute__((aligned(16))) uint16_t wl[2][kColBlk * kD];
   const int h = blockIdx.y, g = h / group;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tok0 = blockIdx.x * kTokBlk + 64 * wave;
   // A fragments: tile t = tokens tok0 + 32t + lane%32; k-step j = head_dim 16j + 8*(lane/32) .. +7
   u32x4 a[2][8];
@@ -103,74 +112,86 @@ __global__ __launch_bounds__(256) void proj_norm(const uint16_t* __restrict__ v,
     for (int j = 0; j < 8; ++j) a[t][j] = ld16(v + (size_t(g) * n + tok) * kD + 16 * j + 8 * (lane >> 5));
   }
   const uint16_t* wh = wt + size_t(h) * dm * kD;
-  // W block cb: columns kColBlk*cb .., 256 contiguous bytes each; thread i moves the 16-byte pieces i + 256k
-  auto load_w = [&](int cb, u32x4 (&r)[kWPieces]) {
+  typedef __attribute__((address_space(3))) uint16_t lds_u16;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u16*)(&wl[0][0])));
+  // block cb -> buffer buf: the wave's instruction k moves columns 4m .. 4m+3 (m = 4k + wave), 1 KB
+  auto dma_block = [&](int cb, int buf) {
 #pragma unroll
-    for (int k = 0; k < kWPieces; ++k) {
-      const int idx = threadIdx.x + 256 * k;
-      r[k] = ld16(wh + size_t(kColBlk * cb + (idx >> 4)) * kD + 8 * (idx & 15));
+    for (int k = 0; k < kColBlk / 16; ++k) {
+      const int m = 4 * k + wave;
+      const int c = 4 * m + (lane >> 4);
+      const int q = (lane & 15) ^ (c & 15);
+      dma16(wh + size_t(kColBlk * cb + c) * kD + 8 * q, lds0 + uint32_t(buf * kColBlk * kD * 2 + m * 1024));
     }
   };
-  auto store_w = [&](int buf, const u32x4 (&r)[kWPieces]) {
-#pragma unroll
-    for (int k = 0; k < kWPieces; ++k) {
-      const int idx = threadIdx.x + 256 * k;
-      *reinterpret_cast<u32x4*>(&wl[buf][(idx >> 4) * kWtStride + 8 * (idx & 15)]) = r[k];
-    }
-  };
-  // B fragments of the 32 columns 32sb .. 32sb+31 of LDS block buf: column lane%32, k = 16j + 8*(lane/32) .. +7
+  // B fragments of columns 32sb .. 32sb+31 of buffer buf: column lane%32, k = 16j + 8*(lane/32) .. +7
   auto read_b = [&](int buf, int sb, u32x4 (&b)[8]) {
+    const int c = 32 * sb + (lane & 31);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      b[j] = *reinterpret_cast<const u32x4*>(&wl[buf][(32 * sb + (lane & 31)) * kWtStride + 16 * j + 8 * (lane >> 5)]);
+    for (int j = 0; j < 8; ++j) {
+      const int q = 2 * j + (lane >> 5);
+      b[j] = *reinterpret_cast<const u32x4*>(&wl[buf][c * kD + 8 * (q ^ (c & 15))]);
+    }
   };
-  // One tile's 8 MFMAs with the |.| sums of the previously finished tile interleaved between them (the VALU runs
-  // while the matrix core works); the fence keeps the whole chain inside this phase.
-  auto phase = [&](const u32x4 (&at)[8], const u32x4 (&b)[8], f32x16& part, const f32x16& done) {
-    f32x16 c = Mfma<T>::m32(at[0], b[0], f32x16{});
+  f32x16 part0 = f32x16{}, part1 = f32x16{};
+  // One sub-block of 32 columns: two independent MFMA chains (tiles 0 and 1), with the |.| sums of the previous
+  // sub-block's products (x, y) and the LDS reads of the next sub-block's B fragments interleaved between them.
+  auto sub = [&](u32x4 (&b)[8], f32x16& x, f32x16& y, int nbuf, int nsb) {
+    f32x16 nx = Mfma<T>::m32(a[0][0], b[0], f32x16{});
+    f32x16 ny = Mfma<T>::m32(a[1][0], b[0], f32x16{});
 #pragma unroll
-    for (int j = 1; j < 8; ++j) c = Mfma<T>::m32(at[j], b[j], c);
+    for (int j = 1; j < 8; ++j) {
+      nx = Mfma<T>::m32(a[0][j], b[j], nx);
+      ny = Mfma<T>::m32(a[1][j], b[j], ny);
+    }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) part[i] += fabsf(done[i]);
+    for (int i = 0; i < 16; ++i) {
+      part0[i] += fabsf(x[i]);
+      part1[i] += fabsf(y[i]);
+    }
+    read_b(nbuf, nsb, b);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read of the next B fragments, if any
       __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
     }
-    asm volatile("" : "+v"(c));
+    asm volatile("" : "+v"(nx), "+v"(ny));
     __builtin_amdgcn_sched_barrier(0);
-    return c;
+    x = nx;
+    y = ny;
   };
-  // Software pipeline: while the MFMAs of one tile run, the VALU adds up the |.| of the tile finished before it.
-  f32x16 part0 = f32x16{}, part1 = f32x16{}, acc0, acc1 = f32x16{};
-  u32x4 pre[kWPieces];
-  load_w(0, pre);
-  store_w(0, pre);
-  __syncthreads();
   const int ncb = dm / kColBlk;
+  dma_block(0, 0);
+  dma_block(min(1, ncb - 1), 1);
+  // The compiler waits for the A fragments here (it does not count the copies), so no wait for them is left
+  // inside the loop, where it would also wait for the copy in flight.
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) asm volatile("" ::"v"(a[t][j]));
+  }
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kColBlk / 16) : "memory");  // block 0 landed
+  __syncthreads();
+  u32x4 b[8];
+  read_b(0, 0, b);
+  f32x16 x = f32x16{}, y = f32x16{};
   for (int cb = 0; cb < ncb; ++cb) {
-    const int buf = cb & 1;
-    load_w(min(cb + 1, ncb - 1), pre);
-    u32x4 b[8];
-    read_b(buf, 0, b);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int sb = 0; sb < kColBlk / 32; ++sb) {
-      acc0 = phase(a[0], b, part1, acc1);
-      u32x4 bn[8];
-      if (sb + 1 < kColBlk / 32) read_b(buf, sb + 1, bn);
-      acc1 = phase(a[1], b, part0, acc0);
-      if (sb + 1 < kColBlk / 32) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) b[j] = bn[j];
-      }
-    }
-    store_w(buf ^ 1, pre);  // the last block's copy lands in the buffer no later block reads
-    __syncthreads();
+    const int cur = cb & 1;
+    sub(b, x, y, cur, 1);  // columns 0..31 of block cb; fetches the B fragments of columns 32..63
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of block cb + 1 has landed
+    __syncthreads();       // everyone's has, and block cb's buffer is no longer read
+    dma_block(min(cb + 2, ncb - 1), cur);
+    sub(b, x, y, cur ^ 1, 0);  // columns 32..63; fetches block cb + 1's first B fragments (unused after the last)
   }
 #pragma unroll
-  for (int i = 0; i < 16; ++i) part1[i] += fabsf(acc1[i]);
+  for (int i = 0; i < 16; ++i) {
+    part0[i] += fabsf(x[i]);
+    part1[i] += fabsf(y[i]);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no copy into LDS outlives the workgroup
   const f32x16 part[2] = {part0, part1};
   // row sums over the 32 columns (lanes of one half-wave); D row of acc[i]: 8*(i/4) + 4*(lane/32) + i%4
 #pragma unroll
