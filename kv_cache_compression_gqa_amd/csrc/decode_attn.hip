@@ -4,7 +4,7 @@
 // full-precision tier and the INT2 tier, dequantised in registers), the cumulative window score updated from
 // each window's attention mass, grouped-query attention (G query heads share one KV head).
 //
-// decode_partial: one workgroup of 4 waves per (unit, slice); every wave owns ONE task and issues all of its
+// decode_partial: one workgroup of 8 waves per (unit, slice); every wave owns ONE task and issues all of its
 // loads at once, so a CU keeps its whole share of a step in flight (a decode step moves ~130 KB per CU at the
 // 32K-context shape, less than the CU's register file):
 //   * dense task: one FULL window or one 32-token tail block: K (8 KiB) and V^T (8 KiB) straight into the MFMA
@@ -22,7 +22,7 @@
 //   * P.V on MFMA: A = 16 head_dim x 32 tokens of V (V is stored transposed per window), B = P^T split into a
 //     high and a low part (columns 0..G-1 and G..2G-1) so the product keeps ~16 bits of P. INT2 values enter A as
 //     exact fp16 codes and the per-token scale is folded into B (P*s); the zero term sum(P*z) is a VALU bias.
-//   The four waves merge their (m, l, o) in LDS into one partial per workgroup.
+//   The eight waves merge their (m, l, o) in LDS into one partial per workgroup.
 // decode_combine: merges the partials of a unit in a fixed order (bitwise reproducible), writes o, converts the
 // window exp-sums into probability mass, adds it to the cumulative score, finalises the optional probabilities
 // and appends the step's token to the tail.
@@ -37,7 +37,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWavesPerBlock = 4;
+constexpr int kWavesPerBlock = 8;
 constexpr int kBlock = kWavesPerBlock * kWave;
 constexpr int kQW = 1;              // INT2 windows per wave task
 constexpr int kMaxParts = 16384;    // workgroups (partials) per unit
@@ -79,7 +79,24 @@ struct DecodeParams {
   float* part_o;   // [U][P][G][D]
   float* wsum;     // [U][NW][G]
   float* wref;     // [U][NW][G]
+  int32_t* unit_tl;  // [U] the tail length the step's partials were computed with (before the append)
 };
+
+// The compiler fetches kernel arguments on first use, each fetch a round trip it then waits for; these pins make
+// it fetch a kernel's arguments together at entry.
+__device__ __forceinline__ void fetch_args_partial(const DecodeParams& p) {
+  asm volatile("" ::"s"(p.NW), "s"(p.TM), "s"(p.k_win), "s"(p.v_win), "s"(p.k_codes), "s"(p.v_codes), "s"(p.k_meta),
+               "s"(p.v_meta), "s"(p.k_tail), "s"(p.v_tail), "s"(p.res_list), "s"(p.n_full), "s"(p.n_int2),
+               "s"(p.tail_len));
+  asm volatile("" ::"s"(p.q), "s"(p.k_new), "s"(p.max_full), "s"(p.max_int2), "s"(p.max_tail), "s"(p.n_tb),
+               "s"(p.n_qt), "s"(p.P), "s"(p.part_ml), "s"(p.part_o), "s"(p.wsum), "s"(p.wref), "s"(p.unit_tl));
+}
+__device__ __forceinline__ void fetch_args_combine(const DecodeParams& p) {
+  asm volatile("" ::"s"(p.NW), "s"(p.TM), "s"(p.P), "s"(p.CB), "s"(p.out), "s"(p.part_ml), "s"(p.part_o), "s"(p.tier),
+               "s"(p.wsum), "s"(p.wref), "s"(p.cum), "s"(p.n_windows), "s"(p.mass), "s"(p.accumulate));
+  asm volatile("" ::"s"(p.probs), "s"(p.probs_stride), "s"(p.k_new), "s"(p.v_new), "s"(p.k_tail), "s"(p.v_tail),
+               "s"(p.tail_len), "s"(p.unit_tl), "s"(p.n_full), "s"(p.n_int2), "s"(p.max_full), "s"(p.max_int2));
+}
 
 // ---- MFMA and conversions per storage dtype ----------------------------------------------------------------
 struct MBF16 {
@@ -460,6 +477,7 @@ __device__ __forceinline__ void int2_task(const DecodeParams& p, const Ctx& c, c
 
 template <int G, class T, bool PROBS>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void decode_partial(DecodeParams p) {
+  fetch_args_partial(p);
   const int u = blockIdx.x / p.P;
   const int sl = blockIdx.x - u * p.P;
   const int lane = threadIdx.x & (kWave - 1);
@@ -505,6 +523,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   c.tl = min(max(tl_dev, 0), p.max_tail);
   c.has_new = p.k_new != nullptr ? 1 : 0;
   c.total_tail = c.tl + c.has_new;
+  // the combine appends the new token and advances tail_len; its workgroups read this copy instead, so that
+  // none of them can see the advanced value
+  if (sl == 0 && threadIdx.x == 0) p.unit_tl[u] = c.tl;
   if (sl == 0 && threadIdx.x == 0 && (c.nf != nf_dev || c.nq != nq_dev || c.tl != tl_dev)) {
     atomicOr(p.status, KVC_DEV_BOUND_EXCEEDED);
   }
@@ -561,7 +582,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     }
   }
 
-  // ---- wave result: O[h][d] = acc(col h) + acc(col h + G) + bias(group of d); merged over the 4 waves ----
+  // ---- wave result: O[h][d] = acc(col h) + acc(col h + G) + bias(group of d); merged over the workgroup's waves ----
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     wo.bias[g] = xor_sum(wo.bias[g], 16);
@@ -619,8 +640,31 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
 constexpr int kPre = 8;
 constexpr int kMlPre = 4;
 
+// the G per-head values of one window (16-byte aligned rows for G = 4, 8; the workspace is 256-byte aligned)
+template <int G>
+__device__ __forceinline__ void load_heads(const float* src, float (&dst)[G]) {
+  if constexpr (G % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < G / 4; ++i) {
+      const float4 v = reinterpret_cast<const float4*>(src)[i];
+      dst[4 * i] = v.x;
+      dst[4 * i + 1] = v.y;
+      dst[4 * i + 2] = v.z;
+      dst[4 * i + 3] = v.w;
+    }
+  } else if constexpr (G == 2) {
+    const float2 v = *reinterpret_cast<const float2*>(src);
+    dst[0] = v.x;
+    dst[1] = v.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < G; ++i) dst[i] = src[i];
+  }
+}
+
 template <int G>
 __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
+  fetch_args_combine(p);
   const int u = blockIdx.x / p.CB;
   const int b = blockIdx.x - u * p.CB;
   const int lane = threadIdx.x & (kWave - 1);
@@ -632,12 +676,27 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
   const int idx = b * E + e;
   const int h_out = idx / kD;
   const size_t unit_win = size_t(u) * p.NW;
-  const int nw = min(max(p.n_windows[u], 0), p.NW);
-  const int wpb = (nw + p.CB - 1) / p.CB;
-  const int wb = b * wpb, we = min(nw, wb + wpb);
+  // the window range is cut from the capacity, so that no load waits for the unit's window count
+  const int wpb = (p.NW + p.CB - 1) / p.CB;
+  const int wb = b * wpb;
   const float* ml = p.part_ml + size_t(u) * CH * G * 2;
   const float* po = p.part_o + size_t(u) * CH * G * kD + idx;
 
+  // (m, l) of the partials of the heads this wave merges (h = wave + 4i), the first kMlPre per lane
+  constexpr int kHP = (G + 3) / 4;
+  float pm[kHP][kMlPre], pl[kHP][kMlPre];
+#pragma unroll
+  for (int i = 0; i < kHP; ++i) {
+    const int h = wave + 4 * i;
+#pragma unroll
+    for (int k = 0; k < kMlPre; ++k) {
+      const int cc = lane + kWave * k;
+      const bool in = h < G && cc < CH;
+      const float2 v = in ? *reinterpret_cast<const float2*>(ml + (cc * G + h) * 2) : make_float2(-INFINITY, 0.0f);
+      pm[i][k] = v.x;
+      pl[i][k] = v.y;
+    }
+  }
   float ov[kPre], mv[kPre];
 #pragma unroll
   for (int k = 0; k < kPre; ++k) {
@@ -651,29 +710,32 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
   const int w0c = min(w0, p.NW - 1);
   const int tier0 = p.tier[unit_win + w0c];
   float ws0[G], wr0[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    ws0[h] = p.wsum[(unit_win + w0c) * G + h];
-    wr0[h] = p.wref[(unit_win + w0c) * G + h];
-  }
+  load_heads<G>(p.wsum + (unit_win + w0c) * G, ws0);
+  load_heads<G>(p.wref + (unit_win + w0c) * G, wr0);
   const float cum0 = p.cum[unit_win + w0c];
+  const int nw = min(max(p.n_windows[u], 0), p.NW);
+  const int we = min(nw, wb + wpb);
+  // the append's loads (tail length, the new K row and V column), issued with the others
+  const int has_new = p.k_new != nullptr ? 1 : 0;
+  const int tl = p.unit_tl[u];
+  const bool appender = b == 0 && has_new;
+  u32x4 kn = u32x4{0u, 0u, 0u, 0u};
+  uint16_t vn = 0;
+  if (appender && threadIdx.x < 16) kn = reinterpret_cast<const u32x4*>(p.k_new + size_t(u) * kD)[threadIdx.x];
+  if (appender && threadIdx.x < kD) vn = p.v_new[size_t(u) * kD + threadIdx.x];
 
   __shared__ float sM[G], sInvL[G];
   __shared__ float red[256];
-  for (int h = wave; h < G; h += 4) {
-    // the lane's first kMlPre (m, l) pairs are loaded together, the rest (more than 256 partials) in a loop
-    float pm[kMlPre], pl[kMlPre];
 #pragma unroll
-    for (int k = 0; k < kMlPre; ++k) {
-      const int cc = lane + kWave * k;
-      pm[k] = cc < CH ? ml[(cc * G + h) * 2] : -INFINITY;
-      pl[k] = cc < CH ? ml[(cc * G + h) * 2 + 1] : 0.0f;
-    }
+  for (int i = 0; i < kHP; ++i) {
+    const int h = wave + 4 * i;
+    if (h >= G) break;
+    // the preloaded (m, l) pairs first, the rest (more than 256 partials) in a loop
     float mr = -INFINITY, lr = 0.0f;
 #pragma unroll
     for (int k = 0; k < kMlPre; ++k) {
-      const float mn = fmaxf(mr, pm[k]);
-      lr = lr * exp_diff(mr, mn) + pl[k] * exp_diff(pm[k], mn);
+      const float mn = fmaxf(mr, pm[i][k]);
+      lr = lr * exp_diff(mr, mn) + pl[i][k] * exp_diff(pm[i][k], mn);
       mr = mn;
     }
     for (int cc = lane + kWave * kMlPre; cc < CH; cc += kWave) {
@@ -700,8 +762,17 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
     red[threadIdx.x] = acc * iL;
     __syncthreads();
     if (int(threadIdx.x) < E) {
+      // sequential order; eight LDS reads in flight at a time
       float o = 0.0f;
-      for (int g2 = 0; g2 < PG; ++g2) o += red[g2 * E + threadIdx.x];
+      int g2 = 0;
+      for (; g2 + 8 <= PG; g2 += 8) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = red[(g2 + j) * E + threadIdx.x];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o += v[j];
+      }
+      for (; g2 < PG; ++g2) o += red[g2 * E + threadIdx.x];
       p.out[size_t(u) * G * kD + idx] = o;
     }
   }
@@ -726,8 +797,6 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
     }
     if (p.mass != nullptr) p.mass[unit_win + w] = mass;
   }
-  const int has_new = p.k_new != nullptr ? 1 : 0;
-  const int tl = min(max(p.tail_len[u], 0), p.max_tail);
   if (p.probs != nullptr) {
     const int nf = min(max(p.n_full[u], 0), p.max_full);
     const int nq = min(max(p.n_int2[u], 0), p.max_int2);
@@ -737,19 +806,12 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
       for (int i = b * 256 + threadIdx.x; i < n_res; i += 256 * p.CB) pr[i] = exp_diff(pr[i], sM[h]) * sInvL[h];
     }
   }
-  if (b == 0 && has_new) {
+  if (appender) {
     // append the step's token to the tail (K row-major, V into its head_dim-major 32-token block)
-    if (threadIdx.x < 16) {
-      reinterpret_cast<u32x4*>(p.k_tail + (size_t(u) * p.TM + tl) * kD)[threadIdx.x] =
-          reinterpret_cast<const u32x4*>(p.k_new + size_t(u) * kD)[threadIdx.x];
-    }
-    if (threadIdx.x < kD) {
-      p.v_tail[(size_t(u) * p.TM + (tl & ~(kW - 1))) * kD + threadIdx.x * kW + (tl & (kW - 1))] =
-          p.v_new[size_t(u) * kD + threadIdx.x];
-    }
+    if (threadIdx.x < 16) reinterpret_cast<u32x4*>(p.k_tail + (size_t(u) * p.TM + tl) * kD)[threadIdx.x] = kn;
+    if (threadIdx.x < kD) p.v_tail[(size_t(u) * p.TM + (tl & ~(kW - 1))) * kD + threadIdx.x * kW + (tl & (kW - 1))] = vn;
+    if (threadIdx.x == 0) p.tail_len[u] = tl + 1;
   }
-  __syncthreads();
-  if (b == 0 && has_new && threadIdx.x == 0) p.tail_len[u] = tl + 1;
 }
 
 template <int G, class T>
@@ -802,6 +864,7 @@ size_t decode_workspace_bytes(const kvc_cache& c, const kvc_decode_args& a) {
   b += align_up(U * P * G * 2 * sizeof(float), 256);
   b += align_up(U * P * G * kD * sizeof(float), 256);
   b += 2 * align_up(U * size_t(c.n_windows_max) * G * sizeof(float), 256);
+  b += align_up(U * sizeof(int32_t), 256);
   return b;
 }
 
@@ -851,6 +914,8 @@ hipError_t launch_decode(const kvc_cache& c, const kvc_decode_args& a, void* ws,
   p.wsum = reinterpret_cast<float*>(w);
   w += align_up(U * size_t(c.n_windows_max) * G * sizeof(float), 256);
   p.wref = reinterpret_cast<float*>(w);
+  w += align_up(U * size_t(c.n_windows_max) * G * sizeof(float), 256);
+  p.unit_tl = reinterpret_cast<int32_t*>(w);
   const int Ui = c.n_units;
   const bool bf = c.kv_dtype == KVC_BF16;
   switch (c.group) {

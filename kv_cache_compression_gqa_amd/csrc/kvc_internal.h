@@ -74,15 +74,18 @@ __device__ __forceinline__ float row_sum16(float v) {
   return v + dpp_f<0x140>(v);
 }
 
+// Max / sum over the wave: DPP inside each row, then the four row results through scalar registers (fixed order,
+// every lane gets the same bits).
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = xor_max(v, m);
-  return v;
+  v = row_max16(v);
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = xor_sum(v, m);
-  return v;
+  v = row_sum16(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 
 __device__ __forceinline__ int wave_sum_int(int v) {
