@@ -462,7 +462,7 @@ def bench_dbtrim(args):
                    "ms_topm": float(np.mean(res["topm"][1])), "ms_compact": comp_s * 1e3},
         "roofline": {"bound": "hbm", "achieved": comp_bytes / comp_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": comp_bytes / comp_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "kvc_compact_pages (compact_copy dominates)", "avg_launch_us": comp_s * 1e6,
+                     "kernel": "kvc_compact_pages (compact_gather dominates)", "avg_launch_us": comp_s * 1e6,
                      "algorithmic_bytes_per_launch": comp_bytes},
     }
     if not args.no_cpu_baseline:

@@ -268,7 +268,7 @@ typedef struct kvc_topm_args {
  *   k_out, v_out    [out_pages_max][page][head_dim] storage dtype out.
  *   lengths, page_offset, n_pages   [n_rows] int32 out.
  *   status      int32 device error bits: KVC_DEV_BOUND_EXCEEDED if the pages exceed out_pages_max (the excess is
- *               not written) or a page id is outside [0, n_src_pages) (that row is not copied).
+ *               not written) or a page id is outside [0, n_src_pages) (that row is written as zeros).
  * Workspace: kvc_compact_pages_workspace(args) bytes, any contents. */
 typedef struct kvc_compact_args {
   const uint8_t* keep;

@@ -19,8 +19,9 @@
 //   threshold and counts the threshold ties per block. A scan of those counts gives each block its share of
 //   the ties, which a fix-up pass takes in index order (only blocks with ties do work).
 //   compaction: per (row, chunk) counts, one workgroup that scans rows and chunks (lengths, page offsets), an
-//   ordered copy of the kept rows (16 lanes x 16 bytes per 128-element row), and a pass that zeroes the unused
-//   rows of each row's last page.
+//   index pass that writes the source pool row of every output row (-1 for the unused rows of a row's last
+//   page), and a gather in output order (16 lanes x 16 bytes per 128-element row, eight rows per lane group in
+//   flight) that copies each row or writes zeros.
 #include <algorithm>
 
 #include "kvc_internal.h"
@@ -302,8 +303,9 @@ __global__ __launch_bounds__(kTB) void topm_fix(const float* __restrict__ scores
 
 // ---- compaction ----------------------------------------------------------------------------------------------
 struct CompactWs {
-  int32_t* chunk_cnt;  // [rows * chunks]
-  int32_t* chunk_off;  // [rows * chunks] position of the chunk's first kept entry within its row
+  int32_t* chunk_cnt;   // [rows * chunks]
+  int32_t* chunk_off;   // [rows * chunks] position of the chunk's first kept entry within its row
+  int32_t* src_of_dst;  // [out_pages_max * page] source pool row of each output row, -1 for a zero row
 };
 
 __global__ __launch_bounds__(kTB) void compact_count(const uint8_t* __restrict__ keep, CompactWs ws, int32_t row_len) {
@@ -348,15 +350,15 @@ __global__ __launch_bounds__(kTB) void compact_plan(CompactWs ws, int64_t n_rows
   }
 }
 
-// ordered copy of the kept rows of one (row, chunk): the chunk's page ids go to LDS in one coalesced read, ranks
-// come from a block scan over 16-position runs, then 16 lanes copy one 128-element row (one 16-byte access each
-// for K and V), four rows per thread with every load issued before the stores
-__global__ __launch_bounds__(kTB) void compact_copy(const uint8_t* __restrict__ keep, const int32_t* __restrict__ pt,
-                                                    const uint4* __restrict__ k_pool, const uint4* __restrict__ v_pool,
-                                                    uint4* __restrict__ k_out, uint4* __restrict__ v_out, CompactWs ws,
-                                                    const int32_t* __restrict__ page_offset, int32_t row_len,
-                                                    int32_t page, int64_t n_src_pages, int64_t out_pages_max,
-                                                    int32_t* status) {
+// source row of every output row, per (row, chunk): the chunk's page ids go to LDS in one coalesced read, ranks
+// come from a block scan over 16-position runs; a rejected page id gives -1, and so do the unused rows of a row's
+// last page (marked by the block holding the row's last chunk)
+__global__ __launch_bounds__(kTB) void compact_index(const uint8_t* __restrict__ keep, const int32_t* __restrict__ pt,
+                                                     CompactWs ws, const int32_t* __restrict__ lengths,
+                                                     const int32_t* __restrict__ page_offset,
+                                                     const int32_t* __restrict__ n_pages, int32_t row_len,
+                                                     int32_t page, int64_t n_src_pages, int64_t out_pages_max,
+                                                     int32_t* status) {
   __shared__ int32_t src_s[kCChunk];
   __shared__ int32_t pg_s[kCChunk];  // page id per block of `page` positions of the chunk (page >= 1)
   __shared__ int wsum[kTB / kWave];
@@ -387,48 +389,57 @@ __global__ __launch_bounds__(kTB) void compact_copy(const uint8_t* __restrict__ 
   }
   if (bad) atomicOr(status, KVC_DEV_BOUND_EXCEEDED);
   __syncthreads();
-  const int64_t dst0 = int64_t(page_offset[r.row]) * page + ws.chunk_off[blockIdx.x];
+  const int64_t base = int64_t(page_offset[r.row]) * page;
+  const int64_t dst0 = base + ws.chunk_off[blockIdx.x];
   const int64_t cap = out_pages_max * page;
-  const int sub = threadIdx.x & 15;
-  for (int i0 = threadIdx.x >> 4; i0 < nk; i0 += 4 * (kTB / 16)) {
-    u32x4 kv[4], vv[4];
-    int src[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = min(i0 + u * (kTB / 16), nk - 1);
-      src[u] = src_s[i];
-      const size_t sidx = size_t(max(src[u], 0)) * 16 + sub;  // row 0 stands in for a rejected page id
-      kv[u] = reinterpret_cast<const u32x4*>(k_pool)[sidx];
-      vv[u] = reinterpret_cast<const u32x4*>(v_pool)[sidx];
-    }
-    // keep the eight loads ahead of the conditional stores (else each pair is sunk into its store's branch)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) asm volatile("" ::"v"(kv[u]), "v"(vv[u]));
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * (kTB / 16);
-      if (i < nk && src[u] >= 0 && dst0 + i < cap) {
-        reinterpret_cast<u32x4*>(k_out)[size_t(dst0 + i) * 16 + sub] = kv[u];
-        reinterpret_cast<u32x4*>(v_out)[size_t(dst0 + i) * 16 + sub] = vv[u];
-      }
-    }
+  for (int i = threadIdx.x; i < nk; i += kTB) {
+    if (dst0 + i < cap) ws.src_of_dst[dst0 + i] = src_s[i];
+  }
+  if (r.end == (r.row + 1) * int64_t(row_len)) {
+    const int64_t last = min(base + int64_t(n_pages[r.row]) * page, cap);
+    for (int64_t d = base + lengths[r.row] + threadIdx.x; d < last; d += kTB) ws.src_of_dst[d] = -1;
   }
 }
 
-// zero the unused rows of every row's last page
-__global__ __launch_bounds__(kTB) void compact_zero_tail(uint4* __restrict__ k_out, uint4* __restrict__ v_out,
-                                                         const int32_t* __restrict__ lengths,
-                                                         const int32_t* __restrict__ page_offset,
-                                                         const int32_t* __restrict__ n_pages, int32_t page,
-                                                         int64_t out_pages_max) {
-  const int64_t row = blockIdx.x;
-  const int64_t first = int64_t(page_offset[row]) * page + lengths[row];
-  const int64_t last = (int64_t(page_offset[row]) + n_pages[row]) * page;
-  const uint4 z = {0u, 0u, 0u, 0u};
-  for (int64_t i = first * 16 + threadIdx.x; i < last * 16; i += kTB) {
-    if (i / 16 >= out_pages_max * page) break;
-    k_out[i] = z;
-    v_out[i] = z;
+// the copy itself, in output order: 16 lanes move one 128-element row (one 16-byte access each for K and V), kGU
+// rows per lane group with every load issued before the stores; source -1 writes zeros
+constexpr int kGU = 8;
+constexpr int kGRows = (kTB / 16) * kGU;  // output rows per workgroup
+__global__ __launch_bounds__(kTB) void compact_gather(const int32_t* __restrict__ src_of_dst,
+                                                      const uint4* __restrict__ k_pool,
+                                                      const uint4* __restrict__ v_pool, uint4* __restrict__ k_out,
+                                                      uint4* __restrict__ v_out,
+                                                      const int32_t* __restrict__ page_offset,
+                                                      const int32_t* __restrict__ n_pages, int64_t n_rows,
+                                                      int32_t page, int64_t out_pages_max) {
+  const int64_t total = min((int64_t(page_offset[n_rows - 1]) + n_pages[n_rows - 1]) * page, out_pages_max * page);
+  const int64_t d0 = int64_t(blockIdx.x) * kGRows;
+  if (d0 >= total) return;
+  const int grp = threadIdx.x >> 4, sub = threadIdx.x & 15;
+  int src[kGU];
+#pragma unroll
+  for (int u = 0; u < kGU; ++u) {
+    const int64_t d = d0 + grp + 16 * u;
+    src[u] = d < total ? src_of_dst[d] : -2;
+  }
+  u32x4 kv[kGU], vv[kGU];
+#pragma unroll
+  for (int u = 0; u < kGU; ++u) {
+    const size_t si = size_t(max(src[u], 0)) * 16 + sub;  // row 0 stands in for a zero row
+    kv[u] = reinterpret_cast<const u32x4*>(k_pool)[si];
+    vv[u] = reinterpret_cast<const u32x4*>(v_pool)[si];
+  }
+  // keep the loads ahead of the conditional stores (else each pair is sunk into its store's branch)
+#pragma unroll
+  for (int u = 0; u < kGU; ++u) asm volatile("" ::"v"(kv[u]), "v"(vv[u]));
+  const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int u = 0; u < kGU; ++u) {
+    if (src[u] >= -1) {
+      const size_t di = size_t(d0 + grp + 16 * u) * 16 + sub;
+      reinterpret_cast<u32x4*>(k_out)[di] = src[u] >= 0 ? kv[u] : z;
+      reinterpret_cast<u32x4*>(v_out)[di] = src[u] >= 0 ? vv[u] : z;
+    }
   }
 }
 
@@ -491,25 +502,34 @@ int64_t compact_blocks(const kvc_compact_args& a) {
   return a.n_rows * int64_t((a.n_tokens + kCChunk - 1) / kCChunk);
 }
 
-size_t compact_workspace_bytes(const kvc_compact_args& a) { return 2 * al(size_t(compact_blocks(a)) * sizeof(int32_t)); }
+size_t compact_workspace_bytes(const kvc_compact_args& a) {
+  return 2 * al(size_t(compact_blocks(a)) * sizeof(int32_t)) + al(size_t(a.out_pages_max) * a.page * sizeof(int32_t));
+}
 
 hipError_t launch_compact(const kvc_compact_args& a, void* ws_ptr, hipStream_t s) {
   char* w = static_cast<char*>(ws_ptr);
   const int64_t nb = compact_blocks(a);
+  if (nb == 0) return hipSuccess;  // no rows
   CompactWs ws;
   ws.chunk_cnt = reinterpret_cast<int32_t*>(w);
   w += al(size_t(nb) * sizeof(int32_t));
   ws.chunk_off = reinterpret_cast<int32_t*>(w);
+  w += al(size_t(nb) * sizeof(int32_t));
+  ws.src_of_dst = reinterpret_cast<int32_t*>(w);
   const int chunks = (a.n_tokens + kCChunk - 1) / kCChunk;
   hipLaunchKernelGGL(compact_count, dim3(unsigned(nb)), dim3(kTB), 0, s, a.keep, ws, a.n_tokens);
   hipLaunchKernelGGL(compact_plan, dim3(1), dim3(kTB), 0, s, ws, a.n_rows, chunks, a.page, a.lengths, a.page_offset,
                      a.n_pages, a.out_pages_max, a.status);
-  hipLaunchKernelGGL(compact_copy, dim3(unsigned(nb)), dim3(kTB), 0, s, a.keep, a.page_table,
-                     static_cast<const uint4*>(a.k_pool), static_cast<const uint4*>(a.v_pool),
-                     static_cast<uint4*>(a.k_out), static_cast<uint4*>(a.v_out), ws, a.page_offset, a.n_tokens,
-                     a.page, a.n_src_pages, a.out_pages_max, a.status);
-  hipLaunchKernelGGL(compact_zero_tail, dim3(unsigned(a.n_rows)), dim3(kTB), 0, s, static_cast<uint4*>(a.k_out),
-                     static_cast<uint4*>(a.v_out), a.lengths, a.page_offset, a.n_pages, a.page, a.out_pages_max);
+  hipLaunchKernelGGL(compact_index, dim3(unsigned(nb)), dim3(kTB), 0, s, a.keep, a.page_table, ws, a.lengths,
+                     a.page_offset, a.n_pages, a.n_tokens, a.page, a.n_src_pages, a.out_pages_max, a.status);
+  const int64_t cap_rows = a.out_pages_max * a.page;
+  const int64_t gb = (cap_rows + kGRows - 1) / kGRows;
+  if (gb > 0) {
+    hipLaunchKernelGGL(compact_gather, dim3(unsigned(gb)), dim3(kTB), 0, s, ws.src_of_dst,
+                       static_cast<const uint4*>(a.k_pool), static_cast<const uint4*>(a.v_pool),
+                       static_cast<uint4*>(a.k_out), static_cast<uint4*>(a.v_out), a.page_offset, a.n_pages,
+                       a.n_rows, a.page, a.out_pages_max);
+  }
   return hipGetLastError();
 }
 
