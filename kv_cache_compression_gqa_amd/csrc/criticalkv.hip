@@ -364,12 +364,14 @@ __global__ __launch_bounds__(256) void group_scores(const float* __restrict__ a_
 }
 
 // ---- two-stage selection ----------------------------------------------------------------------------------------
-// One workgroup of 1024 threads per row; thread t owns entries [64t, 64t + 64) (index order = thread order), whose
-// keys stay in registers for every pass.
+// One workgroup of 1024 threads per row; thread t owns entries [64t, 64t + 64) (index order = thread order). The
+// row's scores (256 KB at most) are re-read for every pass (they stay in L2); only the per-thread taken bits are
+// kept in registers.
 constexpr int kSelThreads = 1024;
 constexpr int kSelPer = 64;
 constexpr int kSelMaxN = kSelThreads * kSelPer;
 constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kSelBatch = 8;  // float4 loads in flight per thread
 
 __device__ __forceinline__ uint32_t sel_key(float s) {
   const uint32_t u = __float_as_uint(s == 0.0f ? 0.0f : s);
@@ -405,11 +407,42 @@ __device__ uint32_t block_excl_scan(uint32_t v, SelShared& sh) {
   return base + inc - v;
 }
 
-// Takes (sets in `taken`) the first b eligible entries (eligible: valid and not taken) in (key asc, index asc).
-__device__ void select_stage(const uint32_t (&key)[kSelPer], uint64_t valid, uint64_t& taken, int b, SelShared& sh) {
+// f(e, key) for each of the thread's entries e (index i0 + e < n), in ascending e, kSelBatch float4 loads at a time
+template <class F>
+__device__ __forceinline__ void for_keys(const float* __restrict__ sc, int n, int i0, F&& f) {
+#pragma unroll
+  for (int c0 = 0; c0 < kSelPer / 4; c0 += kSelBatch) {
+    float4 v[kSelBatch];
+#pragma unroll
+    for (int k = 0; k < kSelBatch; ++k) {
+      const int i = i0 + 4 * (c0 + k);
+      if (i + 3 < n) {
+        v[k] = *reinterpret_cast<const float4*>(sc + i);
+      } else {
+        v[k].x = i < n ? sc[i] : 0.0f;
+        v[k].y = i + 1 < n ? sc[i + 1] : 0.0f;
+        v[k].z = i + 2 < n ? sc[i + 2] : 0.0f;
+        v[k].w = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kSelBatch; ++k) {
+      const float x[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = 4 * (c0 + k) + j;
+        if (i0 + e < n) f(e, sel_key(x[j]));
+      }
+    }
+  }
+}
+
+// Takes (sets in `taken`) the first b entries not yet taken in (key asc, index asc).
+__device__ __forceinline__ void select_stage(const float* __restrict__ sc, int n, int i0, uint64_t& taken, int b,
+                                             SelShared& sh) {
   if (b <= 0) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
-  const uint64_t elig = valid & ~taken;
+  const uint64_t done = taken;
   if (threadIdx.x == 0) {
     sh.prefix = 0u;
     sh.need = b;
@@ -419,10 +452,47 @@ __device__ void select_stage(const uint32_t (&key)[kSelPer], uint64_t valid, uin
     __syncthreads();
     const uint32_t prefix = sh.prefix;
     const int shift = 24 - 8 * pass;
+    if (pass == 0) {
+      // the top digit takes few distinct values (score exponents): the wave's lanes are grouped by bin first, so
+      // that each distinct bin costs one LDS atomic instead of one per lane
 #pragma unroll
-    for (int e = 0; e < kSelPer; ++e) {
-      const bool match = ((elig >> e) & 1u) && (pass == 0 || (key[e] >> (shift + 8)) == prefix);
-      if (match) atomicAdd(&sh.hist[wave][(key[e] >> shift) & 255u], 1u);
+      for (int c0 = 0; c0 < kSelPer / 4; c0 += kSelBatch) {
+        float4 v[kSelBatch];
+#pragma unroll
+        for (int k = 0; k < kSelBatch; ++k) {
+          const int i = i0 + 4 * (c0 + k);
+          if (i + 3 < n) {
+            v[k] = *reinterpret_cast<const float4*>(sc + i);
+          } else {
+            v[k].x = i < n ? sc[i] : 0.0f;
+            v[k].y = i + 1 < n ? sc[i + 1] : 0.0f;
+            v[k].z = i + 2 < n ? sc[i + 2] : 0.0f;
+            v[k].w = 0.0f;
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < kSelBatch; ++k) {
+          const float x[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int e = 4 * (c0 + k) + j;
+            const bool match = i0 + e < n && !((done >> e) & 1u);
+            const uint32_t bin = sel_key(x[j]) >> 24;
+            uint64_t act = __ballot(match);
+            while (act) {
+              const int leader = __builtin_ctzll(act);
+              const uint32_t lb = uint32_t(__builtin_amdgcn_readlane(int(bin), leader));
+              const uint64_t same = __ballot(match && bin == lb);
+              if (lane == leader) atomicAdd(&sh.hist[wave][lb], uint32_t(__popcll(same)));
+              act &= ~same;
+            }
+          }
+        }
+      }
+    } else {
+      for_keys(sc, n, i0, [&](int e, uint32_t key) {
+        if (!((done >> e) & 1u) && (key >> (shift + 8)) == prefix) atomicAdd(&sh.hist[wave][(key >> shift) & 255u], 1u);
+      });
     }
     __syncthreads();
     if (wave == 0) {
@@ -455,39 +525,24 @@ __device__ void select_stage(const uint32_t (&key)[kSelPer], uint64_t valid, uin
   const uint32_t thr = sh.prefix;
   const int need = sh.need;
   uint32_t ties = 0;
-#pragma unroll
-  for (int e = 0; e < kSelPer; ++e) ties += ((elig >> e) & 1u) && key[e] == thr ? 1u : 0u;
+  uint64_t below = 0, tie = 0;
+  for_keys(sc, n, i0, [&](int e, uint32_t key) {
+    if ((done >> e) & 1u) return;
+    below |= uint64_t(key < thr ? 1 : 0) << e;
+    tie |= uint64_t(key == thr ? 1 : 0) << e;
+  });
+  ties = uint32_t(__popcll(tie));
   uint32_t rank = block_excl_scan(ties, sh);
-#pragma unroll
-  for (int e = 0; e < kSelPer; ++e) {
-    if (!((elig >> e) & 1u)) continue;
-    bool take = key[e] < thr;
-    if (key[e] == thr) {
-      take = int(rank) < need;
-      ++rank;
-    }
-    if (take) taken |= uint64_t(1) << e;
+  // the first `need` threshold ties in index order are taken with every key below the threshold
+  uint64_t t = below;
+  while (tie) {
+    const int e = __builtin_ctzll(tie);
+    if (int(rank) < need) t |= uint64_t(1) << e;
+    ++rank;
+    tie &= tie - 1;
   }
+  taken |= t;
   __syncthreads();
-}
-
-__device__ __forceinline__ void load_keys(const float* __restrict__ sc, int n, int i0, uint32_t (&key)[kSelPer],
-                                          uint64_t& valid) {
-  valid = 0;
-#pragma unroll
-  for (int e = 0; e < kSelPer; e += 4) {
-    const int i = i0 + e;
-    float4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (i + 3 < n) v = *reinterpret_cast<const float4*>(sc + i);
-    const float vs[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const bool ok = i + c < n;
-      const float x = ok ? (i + 3 < n ? vs[c] : sc[i + c]) : 0.0f;
-      key[e + c] = sel_key(x);
-      valid |= uint64_t(ok ? 1 : 0) << (e + c);
-    }
-  }
 }
 
 __global__ __launch_bounds__(kSelThreads) void two_stage(const float* __restrict__ a, const float* __restrict__ s2,
@@ -495,19 +550,17 @@ __global__ __launch_bounds__(kSelThreads) void two_stage(const float* __restrict
   __shared__ SelShared sh;
   const int row = blockIdx.x;
   const int i0 = threadIdx.x * kSelPer;
-  uint32_t key[kSelPer];
-  uint64_t valid, taken = 0;
-  load_keys(a + size_t(row) * n, n, i0, key, valid);
-  select_stage(key, valid, taken, budget1, sh);
-  load_keys(s2 + size_t(row) * n, n, i0, key, valid);
-  select_stage(key, valid, taken, budget - budget1, sh);
+  uint64_t taken = 0;
+  select_stage(a + size_t(row) * n, n, i0, taken, budget1, sh);
+  select_stage(s2 + size_t(row) * n, n, i0, taken, budget - budget1, sh);
   // ascending output: exclusive scan of per-thread counts
   uint32_t o = block_excl_scan(uint32_t(__popcll(taken)), sh);
-  for (int e = 0; e < kSelPer; ++e) {
-    if ((taken >> e) & 1u) {
-      if (int(o) < budget) idx[size_t(row) * budget + o] = i0 + e;
-      ++o;
-    }
+  uint64_t t = taken;
+  while (t) {
+    const int e = __builtin_ctzll(t);
+    if (int(o) < budget) idx[size_t(row) * budget + o] = i0 + e;
+    ++o;
+    t &= t - 1;
   }
 }
 
