@@ -2,10 +2,10 @@
 // only at its first demotion; the low-bit copy is kept and reused for every later promotion and demotion, so the
 // approximation error never compounds; promotion dequantises the copy back to full precision).
 //
-// Both kernels walk a flat list given as per-unit lists + per-unit counts: every workgroup computes the exclusive
-// prefix of the counts in LDS, then strides over the flat items (one window per workgroup iteration, so no launch
-// depends on a device-side count). Per window, 128 threads handle K and 128 handle V, one (token, 32-element
-// group) each; V, whose storage is transposed, is staged through LDS.
+// Both kernels walk per-unit lists + per-unit counts: workgroup (u, s) of a U x S grid takes items s, s + S, ... of
+// unit u (one window per workgroup iteration; S is sized from the host bound, so no launch depends on a
+// device-side count). Per window, 128 threads handle K and 128 handle V, one (token, 32-element group) each; V,
+// whose storage is transposed, is staged through LDS.
 //
 // Quantiser (all decisions in fp32 so that they are bit-reproducible; contraction is disabled for this file):
 //   lo, hi = group min / max; zero z = largest fp16 <= lo; scale s = smallest fp16 >= fl32(fl32(hi - z) / 3)
@@ -13,6 +13,8 @@
 // Storage layouts (see include/kvc.h): K codes of a token row: byte 8*s + 2*g + h holds head_dim 32g + 8s + 4h + e
 // at bits 2e; V codes: 16-bit word (r, q, dt) of a window holds tokens 8q + e of head_dim 16dt + r at bits 2e;
 // V meta: word (q, g, e) = token 8q + e, group g.
+#include <algorithm>
+
 #include "kvc_internal.h"
 
 #pragma clang fp contract(off)
@@ -69,72 +71,20 @@ __device__ __forceinline__ uint64_t quantize_group(const float (&x)[kGroupElems]
   return packed;
 }
 
-// Exclusive prefix of count[0..U) (each clamped to [0, stride]) into pre[0..U], pre[U] = total.
-__device__ void unit_prefix(const int32_t* count, int U, int stride, int* pre) {
-  __shared__ int wave_tot[kBlock / kWave];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
-  const int seg = (U + kBlock - 1) / kBlock;
-  const int lo = min(U, int(threadIdx.x) * seg), hi = min(U, lo + seg);
-  // the thread's counts are fetched 8 at a time (independent loads in flight together)
-  int local = 0;
-  for (int i0 = lo; i0 < hi; i0 += 8) {
-    int v[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = i0 + k < hi ? count[i0 + k] : 0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      pre[i0 + k < hi ? i0 + k : U] = min(max(0, v[k]), stride);  // clamped count, scanned below
-      local += min(max(0, v[k]), stride);
-    }
-  }
-  __syncthreads();
-  int inc = local;
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int a = __shfl_up(inc, d, kWave);
-    if (lane >= d) inc += a;
-  }
-  if (lane == kWave - 1) wave_tot[wave] = inc;
-  __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += wave_tot[w];
-  int run = base + inc - local;
-  for (int i = lo; i < hi; ++i) {
-    const int c = pre[i];
-    pre[i] = run;
-    run += c;
-  }
-  __syncthreads();
-  if (threadIdx.x == kBlock - 1) pre[U] = run;
-  __syncthreads();
-}
-
-// unit owning flat item `item`: the last u with pre[u] <= item
-__device__ __forceinline__ int find_unit(const int* pre, int U, int item) {
-  int lo = 0, hi = U;  // invariant pre[lo] <= item < pre[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (pre[mid] <= item) lo = mid; else hi = mid;
-  }
-  return lo;
-}
-
 template <class T>
 __global__ __launch_bounds__(kBlock) void quantize_kernel(kvc_cache c, const int32_t* list, const int32_t* count,
                                                           int stride) {
-  extern __shared__ int pre[];
   __shared__ uint16_t vt[kD * kW];     // V^T window [d][t]
   __shared__ uint8_t vcode[kD * kW];   // V codes [d][t]
   __shared__ int s_skip;
-  const int U = c.n_units, NW = c.n_windows_max;
-  unit_prefix(count, U, stride, pre);
-  const int total = pre[U];
+  const int NW = c.n_windows_max;
+  const int u = blockIdx.x;
+  const int n = min(max(count[u], 0), stride);
   const int half = threadIdx.x >> 7;         // 0 = K, 1 = V
   const int tok = (threadIdx.x & 127) >> 2;
   const int grp = threadIdx.x & 3;
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
-    const int u = find_unit(pre, U, item);
-    const int w = list[size_t(u) * stride + (item - pre[u])];
+  for (int j = blockIdx.y; j < n; j += gridDim.y) {
+    const int w = list[size_t(u) * stride + j];
     const size_t win = size_t(u) * NW + w;
     if (threadIdx.x == 0) s_skip = unsigned(w) >= unsigned(NW) ? 2 : (c.ledgered[win] != 0 ? 1 : 0);
     __syncthreads();
@@ -198,19 +148,17 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(kvc_cache c, const int
 template <class T>
 __global__ __launch_bounds__(kBlock) void promote_kernel(kvc_cache c, const int32_t* list, const int32_t* count,
                                                          int stride) {
-  extern __shared__ int pre[];
   __shared__ uint16_t vcw[kW * kD / 8];  // V code words of the window
   __shared__ uint32_t vmeta[kW * kGroups];
   __shared__ uint16_t vt[kD * kW];      // promoted V^T [d][t]
-  const int U = c.n_units, NW = c.n_windows_max;
-  unit_prefix(count, U, stride, pre);
-  const int total = pre[U];
+  const int NW = c.n_windows_max;
+  const int u = blockIdx.x;
+  const int n = min(max(count[u], 0), stride);
   const int half = threadIdx.x >> 7;
   const int tok = (threadIdx.x & 127) >> 2;
   const int grp = threadIdx.x & 3;
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
-    const int u = find_unit(pre, U, item);
-    const int w = list[size_t(u) * stride + (item - pre[u])];
+  for (int j = blockIdx.y; j < n; j += gridDim.y) {
+    const int w = list[size_t(u) * stride + j];
     if (unsigned(w) >= unsigned(NW)) {
       if (threadIdx.x == 0) atomicOr(c.status, KVC_DEV_BOUND_EXCEEDED);
       continue;
@@ -263,34 +211,33 @@ __global__ __launch_bounds__(kBlock) void promote_kernel(kvc_cache c, const int3
   }
 }
 
-int list_grid(int64_t max_total) { return int(max_total < 2048 ? max_total : 2048); }
+// U x S grid: S workgroups per unit, from the host bound on the items per unit, capped at about 16384 workgroups
+dim3 list_grid(int U, int64_t max_total) {
+  const int64_t per_unit = (max_total + U - 1) / U;
+  const int64_t cap = std::max<int64_t>(1, 16384 / U);
+  return dim3(unsigned(U), unsigned(std::max<int64_t>(1, std::min(per_unit, std::min<int64_t>(cap, 65535)))));
+}
 
 }  // namespace
 
 hipError_t launch_quantize(const kvc_cache& c, const int32_t* list, const int32_t* count, int32_t stride,
                            int64_t max_total, hipStream_t s) {
-  if (max_total <= 0) return hipSuccess;
-  const size_t lds = (size_t(c.n_units) + 1) * sizeof(int);
+  if (max_total <= 0 || c.n_units <= 0) return hipSuccess;
   if (c.kv_dtype == KVC_BF16) {
-    hipLaunchKernelGGL(quantize_kernel<BF16>, dim3(list_grid(max_total)), dim3(kBlock), lds, s, c, list, count,
-                       stride);
+    hipLaunchKernelGGL(quantize_kernel<BF16>, list_grid(c.n_units, max_total), dim3(kBlock), 0, s, c, list, count, stride);
   } else {
-    hipLaunchKernelGGL(quantize_kernel<F16>, dim3(list_grid(max_total)), dim3(kBlock), lds, s, c, list, count,
-                       stride);
+    hipLaunchKernelGGL(quantize_kernel<F16>, list_grid(c.n_units, max_total), dim3(kBlock), 0, s, c, list, count, stride);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_promote(const kvc_cache& c, const int32_t* list, const int32_t* count, int32_t stride,
                           int64_t max_total, hipStream_t s) {
-  if (max_total <= 0) return hipSuccess;
-  const size_t lds = (size_t(c.n_units) + 1) * sizeof(int);
+  if (max_total <= 0 || c.n_units <= 0) return hipSuccess;
   if (c.kv_dtype == KVC_BF16) {
-    hipLaunchKernelGGL(promote_kernel<BF16>, dim3(list_grid(max_total)), dim3(kBlock), lds, s, c, list, count,
-                       stride);
+    hipLaunchKernelGGL(promote_kernel<BF16>, list_grid(c.n_units, max_total), dim3(kBlock), 0, s, c, list, count, stride);
   } else {
-    hipLaunchKernelGGL(promote_kernel<F16>, dim3(list_grid(max_total)), dim3(kBlock), lds, s, c, list, count,
-                       stride);
+    hipLaunchKernelGGL(promote_kernel<F16>, list_grid(c.n_units, max_total), dim3(kBlock), 0, s, c, list, count, stride);
   }
   return hipGetLastError();
 }
