@@ -4,13 +4,13 @@
 // full-precision tier and the INT2 tier, dequantised in registers), the cumulative window score updated from
 // each window's attention mass, grouped-query attention (G query heads share one KV head).
 //
-// decode_partial: one workgroup of 8 waves per (unit, slice); every wave owns ONE task and issues all of its
+// decode_partial: one workgroup of WPB waves per (unit, slice); every wave owns ONE task and issues all of its
 // loads at once, so a CU keeps its whole share of a step in flight (a decode step moves ~130 KB per CU at the
 // 32K-context shape, less than the CU's register file):
 //   * dense task: one FULL window or one 32-token tail block: K (8 KiB) and V^T (8 KiB) straight into the MFMA
 //     operand registers (16 bytes per lane per instruction);
-//   * INT2 task: kQW INT2 windows: codes into registers, the per-token scale/zero words through LDS.
-//   Tasks of a unit, in launch order: the INT2 windows in groups of kQW (their loads are the most scattered and
+//   * INT2 task: QW INT2 windows: codes into registers, the per-token scale/zero words through LDS.
+//   Tasks of a unit, in launch order: the INT2 windows in groups of QW (their loads are the most scattered and
 //   their arithmetic the longest, so they go first), the tail blocks, then FULL window res_list[f] per task.
 //   Tasks past the device counts are empty. The INT2 window ids are read at the offset the device count usually
 //   has (n_full == max_full) together with the counts, and re-read only when it differs.
@@ -22,7 +22,7 @@
 //   * P.V on MFMA: A = 16 head_dim x 32 tokens of V (V is stored transposed per window), B = P^T split into a
 //     high and a low part (columns 0..G-1 and G..2G-1) so the product keeps ~16 bits of P. INT2 values enter A as
 //     exact fp16 codes and the per-token scale is folded into B (P*s); the zero term sum(P*z) is a VALU bias.
-//   The eight waves merge their (m, l, o) in LDS into one partial per workgroup.
+//   The workgroup's waves merge their (m, l, o) in LDS into one partial per workgroup.
 // decode_combine: merges the partials of a unit in a fixed order (bitwise reproducible), writes o, converts the
 // window exp-sums into probability mass, adds it to the cumulative score, finalises the optional probabilities
 // and appends the step's token to the tail.
@@ -37,9 +37,9 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWavesPerBlock = 8;
-constexpr int kBlock = kWavesPerBlock * kWave;
-constexpr int kQW = 1;              // INT2 windows per wave task
+// Launch shapes (QW INT2 windows per wave task, WPB waves per workgroup, both template parameters): a step that
+// fills the GPU in about one round of workgroups takes (1, 8), the shortest chain per task and the fewest partials;
+// a step of many rounds takes (2, 4), more bytes per wave slot and a finer workgroup turnover.
 constexpr int kMaxParts = 16384;    // workgroups (partials) per unit
 constexpr int kMetaWords = kW * kGroups;  // scale/zero words per window and per K or V
 constexpr float kInvSqrtD = 0.088388347648318440550f;  // 1/sqrt(128)
@@ -377,18 +377,18 @@ __device__ __forceinline__ void q_group_sums(const Ctx& c, const u32x4 (&aq)[4],
   }
 }
 
-// kQW INT2 windows (ok[i]: window i exists; masked windows read window 0 and contribute nothing).
-template <int G, class T, bool PROBS>
-__device__ __forceinline__ void int2_task(const DecodeParams& p, const Ctx& c, const int (&ids)[kQW],
-                                          const bool (&ok)[kQW], int pos0, const u32x4 (&aq)[4], float* plds,
+// QW INT2 windows (ok[i]: window i exists; masked windows read window 0 and contribute nothing).
+template <int G, class T, bool PROBS, int QW>
+__device__ __forceinline__ void int2_task(const DecodeParams& p, const Ctx& c, const int (&ids)[QW],
+                                          const bool (&ok)[QW], int pos0, const u32x4 (&aq)[4], float* plds,
                                           uint32_t* ms, WaveOut& wo) {
   using M = typename MfmaOf<T>::M;
   // all loads first: K codes (tokens col and 16 + col, bytes 8q .. 8q+7), V codes (16 bytes of this lane's
   // operand rows), and 8 bytes of each of the K and V scale/zero tables (lane l: words 2l, 2l+1)
-  u32x4 kc[kQW], vc[kQW];
-  uint2 km[kQW], vm[kQW];
+  u32x4 kc[QW], vc[QW];
+  uint2 km[QW], vm[QW];
 #pragma unroll
-  for (int i = 0; i < kQW; ++i) {
+  for (int i = 0; i < QW; ++i) {
     const size_t win = c.unit_win + ids[i];
     const uint8_t* kcb = p.k_codes + win * (kW * kCodeBytes);
     const uint2 a = ld8(kcb + c.col * kCodeBytes + 8 * c.q);
@@ -400,7 +400,7 @@ __device__ __forceinline__ void int2_task(const DecodeParams& p, const Ctx& c, c
   }
   __builtin_amdgcn_sched_barrier(0);  // every load of the task is issued before the first use
 #pragma unroll
-  for (int i = 0; i < kQW; ++i) {
+  for (int i = 0; i < QW; ++i) {
     const uint2 z2 = {0u, 0u};
     *reinterpret_cast<uint2*>(ms + (2 * i) * kMetaWords + 2 * c.lane) = ok[i] ? km[i] : z2;
     *reinterpret_cast<uint2*>(ms + (2 * i + 1) * kMetaWords + 2 * c.lane) = ok[i] ? vm[i] : z2;
@@ -408,9 +408,9 @@ __device__ __forceinline__ void int2_task(const DecodeParams& p, const Ctx& c, c
   float qsum[4][4];
   q_group_sums<G, T>(c, aq, qsum);
   // logits: one MFMA per (16 tokens, group), the group's scale and zero applied to the fp32 product
-  f32x4 S[kQW][2];
+  f32x4 S[QW][2];
 #pragma unroll
-  for (int i = 0; i < kQW; ++i) {
+  for (int i = 0; i < QW; ++i) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       S[i][t] = zero4();
@@ -433,10 +433,10 @@ __device__ __forceinline__ void int2_task(const DecodeParams& p, const Ctx& c, c
     }
     if (PROBS && ok[i]) store_logits<G>(p, c, S[i], pos0 + kW * i, kW);
   }
-  float ws[kQW][4];
-  task_softmax<kQW>(S, wo, ws);
+  float ws[QW][4];
+  task_softmax<QW>(S, wo, ws);
 #pragma unroll
-  for (int i = 0; i < kQW; ++i) {
+  for (int i = 0; i < QW; ++i) {
     if (ok[i]) store_window_sums<G>(p, c, ids[i], ws[i], wo.m);
   }
   // P.V: A = exact fp16 codes of 16 head_dim x 32 tokens, B = (P * scale)^T hi/lo, bias = sum P * zero
@@ -445,7 +445,7 @@ __device__ __forceinline__ void int2_task(const DecodeParams& p, const Ctx& c, c
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) wo.acc[dt] = zero4();
 #pragma unroll
-  for (int i = 0; i < kQW; ++i) {
+  for (int i = 0; i < QW; ++i) {
     float x[8];
     p_to_b<G>(c, S[i], plds, x);
     const uint32_t* vmw = ms + (2 * i + 1) * kMetaWords + c.q * 32;
@@ -475,20 +475,20 @@ __device__ __forceinline__ void int2_task(const DecodeParams& p, const Ctx& c, c
   }
 }
 
-template <int G, class T, bool PROBS>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void decode_partial(DecodeParams p) {
+template <int G, class T, bool PROBS, int QW, int WPB>
+__global__ __launch_bounds__(WPB * kWave) __attribute__((amdgpu_waves_per_eu(4))) void decode_partial(DecodeParams p) {
   fetch_args_partial(p);
   const int u = blockIdx.x / p.P;
   const int sl = blockIdx.x - u * p.P;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int task = sl * kWavesPerBlock + wave;  // wave-uniform (scalar)
+  const int task = sl * WPB + wave;  // wave-uniform (scalar)
 
-  __shared__ __attribute__((aligned(16))) float sm_o[kWavesPerBlock][G][kD];
-  __shared__ float sm_m[kWavesPerBlock][G];
-  __shared__ float sm_l[kWavesPerBlock][G];
-  __shared__ __attribute__((aligned(16))) float plds_all[kWavesPerBlock][8 * 32];
-  __shared__ __attribute__((aligned(16))) uint32_t meta_all[kWavesPerBlock][kQW * 2 * kMetaWords];
+  __shared__ __attribute__((aligned(16))) float sm_o[WPB][G][kD];
+  __shared__ float sm_m[WPB][G];
+  __shared__ float sm_l[WPB][G];
+  __shared__ __attribute__((aligned(16))) float plds_all[WPB][8 * 32];
+  __shared__ __attribute__((aligned(16))) uint32_t meta_all[WPB][QW * 2 * kMetaWords];
 
   Ctx c;
   c.u = u;
@@ -499,7 +499,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   const int32_t* res = p.res_list + c.unit_win;
   const int MF = p.max_full;
   const int t_tail = p.n_qt, t_full = p.n_qt + p.n_tb, t_end = t_full + MF;
-  const int q0 = task * kQW;    // INT2 task: first INT2 slot
+  const int q0 = task * QW;    // INT2 task: first INT2 slot
   const int f = task - t_full;  // FULL task: slot in res_list
 
   // one vector load gathers the unit's device counts (lanes 0..2) and this wave's window ids (lanes 3..): the
@@ -511,9 +511,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     const int32_t* gp = lane < 3 ? cnt + u : res + ridx;
     gv = *gp;
   }
-  int sid[kQW];
+  int sid[QW];
 #pragma unroll
-  for (int i = 0; i < kQW; ++i) sid[i] = __builtin_amdgcn_readlane(gv, 3 + i);
+  for (int i = 0; i < QW; ++i) sid[i] = __builtin_amdgcn_readlane(gv, 3 + i);
   // device counts are clamped to the host bounds the grid was sized for, so every index stays in range
   const int nf_dev = __builtin_amdgcn_readlane(gv, 0);
   const int nq_dev = __builtin_amdgcn_readlane(gv, 1);
@@ -552,20 +552,20 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     if (q0 < c.nq) {
       if (c.nf != MF) {
 #pragma unroll
-        for (int i = 0; i < kQW; ++i) sid[i] = res[min(c.nf + q0 + i, p.NW - 1)];
+        for (int i = 0; i < QW; ++i) sid[i] = res[min(c.nf + q0 + i, p.NW - 1)];
       }
-      int ids[kQW];
-      bool ok[kQW];
+      int ids[QW];
+      bool ok[QW];
       bool bad = false;
 #pragma unroll
-      for (int i = 0; i < kQW; ++i) {
+      for (int i = 0; i < QW; ++i) {
         const bool in_range = unsigned(sid[i]) < unsigned(p.NW);
         ok[i] = q0 + i < c.nq && in_range;
         bad |= q0 + i < c.nq && !in_range;
         ids[i] = ok[i] ? sid[i] : 0;
       }
       if (bad && lane == 0) atomicOr(p.status, KVC_DEV_BOUND_EXCEEDED);
-      int2_task<G, T, PROBS>(p, c, ids, ok, (c.nf + q0) * kW, aq, plds, meta_all[wave], wo);
+      int2_task<G, T, PROBS, QW>(p, c, ids, ok, (c.nf + q0) * kW, aq, plds, meta_all[wave], wo);
     }
   } else if (task < t_full) {
     const int blk = task - t_tail;
@@ -608,24 +608,24 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   }
   __syncthreads();
   const size_t part = size_t(u) * p.P + sl;
-  for (int i = threadIdx.x; i < G * kD; i += kBlock) {
+  for (int i = threadIdx.x; i < G * kD; i += (WPB * kWave)) {
     const int h = i / kD;
     float Mx = sm_m[0][h];
 #pragma unroll
-    for (int w = 1; w < kWavesPerBlock; ++w) Mx = fmaxf(Mx, sm_m[w][h]);
+    for (int w = 1; w < WPB; ++w) Mx = fmaxf(Mx, sm_m[w][h]);
     float O = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWavesPerBlock; ++w) O += sm_o[w][h][i % kD] * exp_diff(sm_m[w][h], Mx);
+    for (int w = 0; w < WPB; ++w) O += sm_o[w][h][i % kD] * exp_diff(sm_m[w][h], Mx);
     p.part_o[part * G * kD + i] = O;
   }
   if (threadIdx.x < G) {
     const int h = threadIdx.x;
     float Mx = sm_m[0][h];
 #pragma unroll
-    for (int w = 1; w < kWavesPerBlock; ++w) Mx = fmaxf(Mx, sm_m[w][h]);
+    for (int w = 1; w < WPB; ++w) Mx = fmaxf(Mx, sm_m[w][h]);
     float L = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWavesPerBlock; ++w) L += sm_l[w][h] * exp_diff(sm_m[w][h], Mx);
+    for (int w = 0; w < WPB; ++w) L += sm_l[w][h] * exp_diff(sm_m[w][h], Mx);
     p.part_ml[(part * G + h) * 2 + 0] = Mx;
     p.part_ml[(part * G + h) * 2 + 1] = L;
   }
@@ -814,12 +814,25 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
   }
 }
 
-template <int G, class T>
-hipError_t launch_g(const DecodeParams& p, int U, hipStream_t s) {
+struct Shape {
+  int qw, wpb;
+};
+
+template <int G, class T, int QW, int WPB>
+void launch_partial(const DecodeParams& p, int U, hipStream_t s) {
   if (p.probs != nullptr) {
-    hipLaunchKernelGGL((decode_partial<G, T, true>), dim3(U * p.P), dim3(kBlock), 0, s, p);
+    hipLaunchKernelGGL((decode_partial<G, T, true, QW, WPB>), dim3(U * p.P), dim3(WPB * kWave), 0, s, p);
   } else {
-    hipLaunchKernelGGL((decode_partial<G, T, false>), dim3(U * p.P), dim3(kBlock), 0, s, p);
+    hipLaunchKernelGGL((decode_partial<G, T, false, QW, WPB>), dim3(U * p.P), dim3(WPB * kWave), 0, s, p);
+  }
+}
+
+template <int G, class T>
+hipError_t launch_g(const DecodeParams& p, int U, Shape sh, hipStream_t s) {
+  if (sh.qw == 1) {
+    launch_partial<G, T, 1, 8>(p, U, s);
+  } else {
+    launch_partial<G, T, 2, 4>(p, U, s);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -831,13 +844,33 @@ struct TaskCounts {
   int n_tb, n_qt, tasks;
 };
 
-TaskCounts task_counts(const kvc_decode_args& a) {
+TaskCounts task_counts(const kvc_decode_args& a, int qw) {
   const int has_new = a.k_new != nullptr ? 1 : 0;
   TaskCounts t;
   t.n_tb = (a.max_tail + has_new + kW - 1) / kW;
-  t.n_qt = (a.max_int2 + kQW - 1) / kQW;
+  t.n_qt = (a.max_int2 + qw - 1) / qw;
   t.tasks = a.max_full + t.n_tb + t.n_qt;
   return t;
+}
+
+// compute units of the current device (cached per device)
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  return cus[dev];
+}
+
+// (1, 8) while the (1, 8) grid fits in two rounds of resident workgroups (two 8-wave workgroups per CU at four
+// waves per SIMD), else (2, 4)
+Shape decode_shape(const kvc_cache& c, const kvc_decode_args& a) {
+  const TaskCounts t = task_counts(a, 1);
+  const int64_t wgs = int64_t(c.n_units) * ((t.tasks + 7) / 8);
+  return wgs <= 2 * 2 * int64_t(device_cus()) ? Shape{1, 8} : Shape{2, 4};
 }
 
 int combine_blocks(const kvc_cache& c, int P) {
@@ -851,9 +884,9 @@ int combine_blocks(const kvc_cache& c, int P) {
 }  // namespace
 
 int decode_slices(const kvc_cache& c, const kvc_decode_args& a) {
-  (void)c;
-  const TaskCounts t = task_counts(a);
-  return max(1, (t.tasks + kWavesPerBlock - 1) / kWavesPerBlock);
+  const Shape sh = decode_shape(c, a);
+  const TaskCounts t = task_counts(a, sh.qw);
+  return max(1, (t.tasks + sh.wpb - 1) / sh.wpb);
 }
 
 bool decode_supported(const kvc_cache& c, const kvc_decode_args& a) { return decode_slices(c, a) <= kMaxParts; }
@@ -899,7 +932,8 @@ hipError_t launch_decode(const kvc_cache& c, const kvc_decode_args& a, void* ws,
   p.max_full = a.max_full;
   p.max_int2 = a.max_int2;
   p.max_tail = a.max_tail;
-  const TaskCounts tc = task_counts(a);
+  const Shape sh = decode_shape(c, a);
+  const TaskCounts tc = task_counts(a, sh.qw);
   p.n_tb = tc.n_tb;
   p.n_qt = tc.n_qt;
   p.P = decode_slices(c, a);
@@ -919,10 +953,10 @@ hipError_t launch_decode(const kvc_cache& c, const kvc_decode_args& a, void* ws,
   const int Ui = c.n_units;
   const bool bf = c.kv_dtype == KVC_BF16;
   switch (c.group) {
-    case 1: return bf ? launch_g<1, BF16>(p, Ui, s) : launch_g<1, F16>(p, Ui, s);
-    case 2: return bf ? launch_g<2, BF16>(p, Ui, s) : launch_g<2, F16>(p, Ui, s);
-    case 4: return bf ? launch_g<4, BF16>(p, Ui, s) : launch_g<4, F16>(p, Ui, s);
-    case 8: return bf ? launch_g<8, BF16>(p, Ui, s) : launch_g<8, F16>(p, Ui, s);
+    case 1: return bf ? launch_g<1, BF16>(p, Ui, sh, s) : launch_g<1, F16>(p, Ui, sh, s);
+    case 2: return bf ? launch_g<2, BF16>(p, Ui, sh, s) : launch_g<2, F16>(p, Ui, sh, s);
+    case 4: return bf ? launch_g<4, BF16>(p, Ui, sh, s) : launch_g<4, F16>(p, Ui, sh, s);
+    case 8: return bf ? launch_g<8, BF16>(p, Ui, sh, s) : launch_g<8, F16>(p, Ui, sh, s);
     default: return hipErrorInvalidValue;
   }
 }
