@@ -758,7 +758,18 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
     float acc = 0.0f;
 #pragma unroll
     for (int k = 0; k < kPre; ++k) acc += ov[k] * exp_diff(mv[k], Mh);
-    for (int cc = pg + kPre * PG; cc < CH; cc += PG) acc += po[size_t(cc) * G * kD] * exp_diff(ml[(cc * G + h_out) * 2], Mh);
+    // partials beyond the preloaded ones, eight loads in flight at a time (same sequential order)
+    for (int cc0 = pg + kPre * PG; cc0 < CH; cc0 += 8 * PG) {
+      float o8[8], m8[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int cc = cc0 + k * PG;
+        o8[k] = cc < CH ? po[size_t(cc) * G * kD] : 0.0f;
+        m8[k] = cc < CH ? ml[(cc * G + h_out) * 2] : -INFINITY;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc += o8[k] * exp_diff(m8[k], Mh);
+    }
     red[threadIdx.x] = acc * iL;
     __syncthreads();
     if (int(threadIdx.x) < E) {
@@ -877,8 +888,16 @@ int combine_blocks(const kvc_cache& c, int P) {
   // partial groups so that a thread holds at most kPre partials, output elements E = 256 / PG (at most G*D)
   int pg = 1;
   while (pg < 256 && pg * kPre < P) pg *= 2;
-  const int E = min(256 / pg, c.group * kD);
-  return c.group * kD / E;
+  int E = min(256 / pg, c.group * kD);
+  int cb = c.group * kD / E;
+  // many units: fewer, fuller workgroups (about four per CU in all); a thread then takes more partials, the ones
+  // past kPre eight loads at a time
+  const int target = max(1, 4 * device_cus() / max(1, c.n_units));
+  while (cb > target && cb % 2 == 0 && 2 * E <= 256) {
+    E *= 2;
+    cb /= 2;
+  }
+  return cb;
 }
 
 }  // namespace

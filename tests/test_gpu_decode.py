@@ -51,6 +51,19 @@ def test_group_of_eight_and_one(gpu_lib):
         run_decode_parity(cfg, log=log)
 
 
+def test_many_units_two_int2_windows_per_task(gpu_lib):
+    """1280 units: a step takes many rounds of workgroups, so the launch switches to two INT2 windows per wave
+    task and 4-wave workgroups. G = 8 (f16), 1 (bf16) and 2 (f16), probabilities on; the oracle follows units
+    spread over layers, sequences and heads."""
+    for hq, hkv, batch, dtype in ((16, 2, 20, "f16"), (4, 4, 10, "bf16"), (8, 4, 10, "f16")):
+        cfg = dataclasses.replace(configs.TINY, name=f"many_g{hq // hkv}", seed=14, hq=hq, hkv=hkv, dtype=dtype,
+                                  layers=32, batch=batch, context=640, n_salient=5, budget_full=4, budget_int2=7,
+                                  steps=4, route_every=2)
+        inp, umap = synth.make_decode_shared_layers(cfg)
+        log(f"case: {cfg.name}, {cfg.n_units} units, {dtype}")
+        run_decode_parity(cfg, inp=inp, unit_map=umap, check_units=[0, 333, 777, cfg.n_units - 1], log=log)
+
+
 def test_llama_layer_32k_run_matches_oracle(gpu_lib):
     # every unit runs on the GPU in one launch; the oracle follows two units exactly through all 64 steps
     log("case: llama3_8b_layer_ctx32k_bf16, 64 steps, oracle on units 0 and 5")
