@@ -2,9 +2,9 @@
 // Principais"): per unit, resident windows are ranked by (score desc, window asc); the first budget_full go to the
 // full-precision tier, the next budget_int2 to the INT2 tier, the rest are evicted for good.
 //
-// One workgroup per unit. The two rank thresholds are found by an exact MSB-first radix select over
-// order-preserving 32-bit keys (4 passes of 8 bits, LDS histogram, one wave scans the 256 bins); keys equal to a
-// threshold are admitted lowest index first through an exclusive scan in window order. The new resident lists
+// One workgroup per unit. The two rank thresholds are found together by an exact MSB-first radix select over
+// order-preserving 32-bit keys (4 passes of 8 bits, per-wave LDS histograms, one wave per threshold scans the 256
+// bins); keys equal to a threshold are admitted lowest index first through an exclusive scan in window order. The new resident lists
 // and the quantise / promote lists come from one more in-order scan, so every output is deterministic.
 #include "kvc_internal.h"
 
@@ -13,6 +13,12 @@ namespace {
 
 constexpr int kBlock = 256;
 constexpr int kWaves = kBlock / kWave;
+// window flag byte in LDS
+constexpr uint8_t kOldTier = 3;     // bits 0-1: tier before routing
+constexpr uint8_t kLedgered = 4;    // bit 2: INT2 copy present
+constexpr uint8_t kValid = 8;       // bit 3: resident (while loading: the score is NaN)
+constexpr int kNewShift = 4;
+constexpr uint8_t kNewTier = 0x30;  // bits 4-5: tier after routing
 
 // fp32 -> uint32 with the same order (-0 folded onto +0); NaN is screened out before.
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -62,33 +68,60 @@ __device__ int4 block_scan4(int4 v, int4* sm_waves, int4& tot) {
 }
 
 struct SelectShared {
-  uint32_t hist[256];
-  int digit;
-  int krem;
+  uint32_t hist[2][kWaves][256];  // per selection, per wave
+  int digit[2];
+  int krem[2];
 };
 
-// Value T of the k-th largest valid key (k >= 1) and how many keys equal to T belong to the top k.
-__device__ void radix_kth(const uint32_t* keys, const uint8_t* valid, int n, int k, SelectShared& sh,
-                          uint32_t& T, int& need) {
+// Both rank thresholds in one series of passes: for s = 0, 1, the value T[s] of the k[s]-th largest valid key
+// (k[s] >= 1; k[s] <= 0 leaves selection s idle) and how many keys equal to T[s] belong to the top k[s]. Each pass
+// takes 8 bits (MSB first) into per-wave LDS histograms; the top digit, which few distinct values share, groups
+// the wave's lanes by bin before one atomic per distinct bin. Wave s then scans selection s's 256 bins.
+__device__ void radix_kth2(const uint32_t* keys, const uint8_t* wm, int n, const int (&k)[2], SelectShared& sh,
+                           uint32_t (&T)[2], int (&need)[2]) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
-  uint32_t prefix = 0u, mask = 0u;
-  int krem = k;
+  uint32_t prefix[2] = {0u, 0u}, mask = 0u;
+  int krem[2] = {k[0], k[1]};
+  const bool active[2] = {k[0] > 0, k[1] > 0};
   for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < 256; i += kBlock) sh.hist[i] = 0u;
+    for (int i = threadIdx.x; i < 2 * kWaves * 256; i += kBlock) (&sh.hist[0][0][0])[i] = 0u;
     __syncthreads();
-    for (int i = threadIdx.x; i < n; i += kBlock) {
-      if (valid[i] && (keys[i] & mask) == prefix) atomicAdd(&sh.hist[(keys[i] >> shift) & 255u], 1u);
+    for (int i0 = 0; i0 < n; i0 += kBlock) {  // uniform trip count (the ballots below need the whole wave)
+      const int i = i0 + int(threadIdx.x);
+      const bool ok = i < n && (wm[i] & kValid);
+      const uint32_t key = ok ? keys[i] : 0u;
+      const uint32_t bin = (key >> shift) & 255u;
+#pragma unroll
+      for (int sel = 0; sel < 2; ++sel) {
+        const bool m = ok && active[sel] && (key & mask) == prefix[sel];
+        if (shift == 24) {
+          uint64_t act = __ballot(m);
+          while (act) {
+            const int leader = __builtin_ctzll(act);
+            const uint32_t lb = uint32_t(__builtin_amdgcn_readlane(int(bin), leader));
+            const uint64_t same = __ballot(m && bin == lb);
+            if (lane == leader) atomicAdd(&sh.hist[sel][wave][lb], uint32_t(__popcll(same)));
+            act &= ~same;
+          }
+        } else if (m) {
+          atomicAdd(&sh.hist[sel][wave][bin], 1u);
+        }
+      }
     }
     __syncthreads();
-    if (wave == 0) {
-      // lane owns bins 4*lane .. 4*lane+3; "above" = keys in bins with a larger digit
+    if (wave < 2 && active[wave]) {
+      const int sel = wave;
+      // lane owns bins 4*lane .. 4*lane+3 (summed over the wave copies); "above" = keys in bins with a larger digit
       int c[4];
       int own = 0;
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        c[b] = int(sh.hist[4 * lane + b]);
-        own += c[b];
+        int x = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) x += int(sh.hist[sel][w][4 * lane + b]);
+        c[b] = x;
+        own += x;
       }
       // suffix sum over lanes: sum of own over lanes > lane
       int inc = own;
@@ -98,51 +131,82 @@ __device__ void radix_kth(const uint32_t* keys, const uint8_t* valid, int n, int
         if (lane + d < kWave) inc += a;
       }
       int above = inc - own;
+      const int kr = krem[sel];
 #pragma unroll
       for (int b = 3; b >= 0; --b) {
-        if (above < krem && krem <= above + c[b]) {
-          sh.digit = 4 * lane + b;
-          sh.krem = krem - above;
+        if (above < kr && kr <= above + c[b]) {
+          sh.digit[sel] = 4 * lane + b;
+          sh.krem[sel] = kr - above;
         }
         above += c[b];
       }
     }
     __syncthreads();
-    const uint32_t d = uint32_t(sh.digit);
-    krem = sh.krem;
-    prefix |= d << shift;
+#pragma unroll
+    for (int sel = 0; sel < 2; ++sel) {
+      if (active[sel]) {
+        prefix[sel] |= uint32_t(sh.digit[sel]) << shift;
+        krem[sel] = sh.krem[sel];
+      }
+    }
     mask |= 255u << shift;
-    __syncthreads();
   }
-  T = prefix;
-  need = krem;
+  T[0] = prefix[0];
+  T[1] = prefix[1];
+  need[0] = krem[0];
+  need[1] = krem[1];
 }
 
 __global__ __launch_bounds__(kBlock) void route_tiers_kernel(kvc_tier_route_args a, kvc_cache c) {
   extern __shared__ uint8_t dyn[];
   const int u = blockIdx.x;
   const int NW = c.n_windows_max;
+  // per window, in LDS: the key and one byte of flags (old tier, ledgered, valid, new tier)
   uint32_t* keys = reinterpret_cast<uint32_t*>(dyn);
-  uint8_t* valid = dyn + size_t(NW) * 4;
+  uint8_t* wm = dyn + size_t(NW) * 4;
   __shared__ SelectShared sh;
   __shared__ int4 sm_waves[kWaves];
   __shared__ int s_flag[2];
 
   const size_t base = size_t(u) * NW;
-  const int n = min(max(c.n_windows[u], 0), NW);
   const float* sc = a.scores != nullptr ? a.scores + base : c.cum + base;
   if (threadIdx.x == 0) {
     s_flag[0] = 0;
     s_flag[1] = 0;
   }
+  // every window slot's tables are loaded at once (none of the addresses waits for the window count), then read
+  // from LDS only
+  const int n_raw = c.n_windows[u];
+  for (int i0 = threadIdx.x; i0 < NW; i0 += 4 * kBlock) {  // four windows' loads in flight per thread
+    float f[4];
+    int t[4], lg[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = min(i0 + j * kBlock, NW - 1);
+      t[j] = c.tier[base + i];
+      f[j] = sc[i];
+      lg[j] = c.ledgered[base + i];
+    }
+    // every use of the twelve loads comes after this point (in/out operands), so none is waited on early
+    asm volatile("" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]),
+                 "+v"(lg[0]), "+v"(lg[1]), "+v"(lg[2]), "+v"(lg[3]));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = i0 + j * kBlock;
+      if (i < NW) {
+        keys[i] = order_key(f[j]);
+        wm[i] = uint8_t((t[j] & kOldTier) | (lg[j] != 0 ? kLedgered : 0) | (isnan(f[j]) ? kValid : 0));  // kValid: NaN
+      }
+    }
+  }
+  const int n = min(max(n_raw, 0), NW);
   __syncthreads();
   int nres_local = 0;
   for (int i = threadIdx.x; i < n; i += kBlock) {
-    const bool v = c.tier[base + i] != KVC_TIER_EVICTED;
-    const float f = sc[i];
-    if (v && isnan(f)) atomicOr(&s_flag[0], 1);
-    valid[i] = v ? 1 : 0;
-    keys[i] = order_key(f);
+    const uint8_t f = wm[i];
+    const bool v = (f & kOldTier) != KVC_TIER_EVICTED;
+    if (v && (f & kValid)) atomicOr(&s_flag[0], 1);
+    wm[i] = uint8_t((f & ~kValid) | (v ? kValid : 0));
     nres_local += v ? 1 : 0;
   }
   atomicAdd(&s_flag[1], nres_local);
@@ -156,10 +220,12 @@ __global__ __launch_bounds__(kBlock) void route_tiers_kernel(kvc_tier_route_args
   const int bq = max(0, a.budget_int2[u]);
   const int k1 = min(bf, n_res);
   const int k2 = min(bf + bq, n_res);
-  uint32_t T1 = 0u, T2 = 0u;
-  int need1 = 0, need2 = 0;
-  if (k1 > 0) radix_kth(keys, valid, n, k1, sh, T1, need1);
-  if (k2 > 0) radix_kth(keys, valid, n, k2, sh, T2, need2);
+  const int kk[2] = {k1, k2};
+  uint32_t TT[2] = {0u, 0u};
+  int nn[2] = {0, 0};
+  radix_kth2(keys, wm, n, kk, sh, TT, nn);
+  const uint32_t T1 = TT[0], T2 = TT[1];
+  const int need1 = nn[0], need2 = nn[1];
 
   // contiguous segment of windows per thread, so that scans follow window order
   const int seg = (n + kBlock - 1) / kBlock;
@@ -169,7 +235,7 @@ __global__ __launch_bounds__(kBlock) void route_tiers_kernel(kvc_tier_route_args
   // pass 1: rank among keys equal to each threshold
   int4 cnt = make_int4(0, 0, 0, 0);
   for (int i = lo; i < hi; ++i) {
-    if (valid[i]) {
+    if (wm[i] & kValid) {
       cnt.x += (k1 > 0 && keys[i] == T1) ? 1 : 0;
       cnt.y += (k2 > 0 && keys[i] == T2) ? 1 : 0;
     }
@@ -181,7 +247,8 @@ __global__ __launch_bounds__(kBlock) void route_tiers_kernel(kvc_tier_route_args
   int4 cnt2 = make_int4(0, 0, 0, 0);
   for (int i = lo; i < hi; ++i) {
     int8_t nt = KVC_TIER_EVICTED;
-    if (valid[i]) {
+    const uint8_t f = wm[i];
+    if (f & kValid) {
       bool top1 = false, top2 = false;
       if (k1 > 0) {
         if (keys[i] > T1) top1 = true;
@@ -193,21 +260,22 @@ __global__ __launch_bounds__(kBlock) void route_tiers_kernel(kvc_tier_route_args
       }
       nt = top1 ? KVC_TIER_FULL : (top2 ? KVC_TIER_INT2 : KVC_TIER_EVICTED);
     }
-    const int8_t old = c.tier[base + i];
-    valid[i] = uint8_t(nt);  // reuse: new tier (0, 1, 2)
+    const int8_t old = int8_t(f & kOldTier);
+    wm[i] = uint8_t((f & ~kNewTier) | (nt << kNewShift));
     cnt2.x += nt == KVC_TIER_FULL;
     cnt2.y += nt == KVC_TIER_INT2;
-    cnt2.z += (old == KVC_TIER_FULL && nt == KVC_TIER_INT2 && c.ledgered[base + i] == 0);
+    cnt2.z += (old == KVC_TIER_FULL && nt == KVC_TIER_INT2 && !(f & kLedgered));
     cnt2.w += (old == KVC_TIER_INT2 && nt == KVC_TIER_FULL);
   }
   int4 tot2;
   int4 pos = block_scan4(cnt2, sm_waves, tot2);
   for (int i = lo; i < hi; ++i) {
-    const int8_t nt = int8_t(valid[i]);
-    const int8_t old = c.tier[base + i];
+    const uint8_t f = wm[i];
+    const int8_t nt = int8_t((f & kNewTier) >> kNewShift);
+    const int8_t old = int8_t(f & kOldTier);
     if (nt == KVC_TIER_FULL) c.res_list[base + pos.x++] = i;
     if (nt == KVC_TIER_INT2) c.res_list[base + tot2.x + pos.y++] = i;
-    if (old == KVC_TIER_FULL && nt == KVC_TIER_INT2 && c.ledgered[base + i] == 0) a.quant_list[base + pos.z++] = i;
+    if (old == KVC_TIER_FULL && nt == KVC_TIER_INT2 && !(f & kLedgered)) a.quant_list[base + pos.z++] = i;
     if (old == KVC_TIER_INT2 && nt == KVC_TIER_FULL) a.promo_list[base + pos.w++] = i;
     if (nt == KVC_TIER_EVICTED && old != KVC_TIER_EVICTED) c.ledgered[base + i] = 0;
     c.tier[base + i] = nt;
