@@ -371,7 +371,7 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelPer = 64;
 constexpr int kSelMaxN = kSelThreads * kSelPer;
 constexpr int kSelWaves = kSelThreads / kWave;
-constexpr int kSelBatch = 8;  // float4 loads in flight per thread
+constexpr int kSelBatch = 16;  // float4 loads in flight per thread (all of them)
 
 __device__ __forceinline__ uint32_t sel_key(float s) {
   const uint32_t u = __float_as_uint(s == 0.0f ? 0.0f : s);
@@ -380,6 +380,7 @@ __device__ __forceinline__ uint32_t sel_key(float s) {
 
 struct SelShared {
   uint32_t hist[kSelWaves][256];
+  uint32_t bins[256];
   uint32_t wsum[kSelWaves];
   uint32_t prefix;
   int32_t need;
@@ -437,7 +438,10 @@ __device__ __forceinline__ void for_keys(const float* __restrict__ sc, int n, in
   }
 }
 
-// Takes (sets in `taken`) the first b entries not yet taken in (key asc, index asc).
+// Takes (sets in `taken`) the first b entries not yet taken in (key asc, index asc). Each pass: 8-bit digit
+// histograms in per-wave LDS copies, summed per bin by 256 threads, then one wave finds the bin holding the
+// need-th key. (Grouping a wave's lanes by bin before the atomic, tried for the top digit, cost as much as the
+// contention it saved on attention-like scores and three times more on widely spread ones.)
 __device__ __forceinline__ void select_stage(const float* __restrict__ sc, int n, int i0, uint64_t& taken, int b,
                                              SelShared& sh) {
   if (b <= 0) return;
@@ -452,58 +456,26 @@ __device__ __forceinline__ void select_stage(const float* __restrict__ sc, int n
     __syncthreads();
     const uint32_t prefix = sh.prefix;
     const int shift = 24 - 8 * pass;
-    if (pass == 0) {
-      // the top digit takes few distinct values (score exponents): the wave's lanes are grouped by bin first, so
-      // that each distinct bin costs one LDS atomic instead of one per lane
-#pragma unroll
-      for (int c0 = 0; c0 < kSelPer / 4; c0 += kSelBatch) {
-        float4 v[kSelBatch];
-#pragma unroll
-        for (int k = 0; k < kSelBatch; ++k) {
-          const int i = i0 + 4 * (c0 + k);
-          if (i + 3 < n) {
-            v[k] = *reinterpret_cast<const float4*>(sc + i);
-          } else {
-            v[k].x = i < n ? sc[i] : 0.0f;
-            v[k].y = i + 1 < n ? sc[i + 1] : 0.0f;
-            v[k].z = i + 2 < n ? sc[i + 2] : 0.0f;
-            v[k].w = 0.0f;
-          }
-        }
-#pragma unroll
-        for (int k = 0; k < kSelBatch; ++k) {
-          const float x[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int e = 4 * (c0 + k) + j;
-            const bool match = i0 + e < n && !((done >> e) & 1u);
-            const uint32_t bin = sel_key(x[j]) >> 24;
-            uint64_t act = __ballot(match);
-            while (act) {
-              const int leader = __builtin_ctzll(act);
-              const uint32_t lb = uint32_t(__builtin_amdgcn_readlane(int(bin), leader));
-              const uint64_t same = __ballot(match && bin == lb);
-              if (lane == leader) atomicAdd(&sh.hist[wave][lb], uint32_t(__popcll(same)));
-              act &= ~same;
-            }
-          }
-        }
+    for_keys(sc, n, i0, [&](int e, uint32_t key) {
+      if (!((done >> e) & 1u) && (pass == 0 || (key >> (shift + 8)) == prefix)) {
+        atomicAdd(&sh.hist[wave][(key >> shift) & 255u], 1u);
       }
-    } else {
-      for_keys(sc, n, i0, [&](int e, uint32_t key) {
-        if (!((done >> e) & 1u) && (key >> (shift + 8)) == prefix) atomicAdd(&sh.hist[wave][(key >> shift) & 255u], 1u);
-      });
+    });
+    __syncthreads();
+    if (threadIdx.x < 256) {  // the per-wave copies summed per bin, by 256 threads at once
+      uint32_t x = 0;
+#pragma unroll
+      for (int w = 0; w < kSelWaves; ++w) x += sh.hist[w][threadIdx.x];
+      sh.bins[threadIdx.x] = x;
     }
     __syncthreads();
     if (wave == 0) {
-      // lane l holds bins 4l .. 4l+3 (summed over the per-wave copies); first bin whose running count reaches need
+      // lane l holds bins 4l .. 4l+3; first bin whose running count reaches need
       uint32_t c[4], tot = 0;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        uint32_t x = 0;
-        for (int w = 0; w < kSelWaves; ++w) x += sh.hist[w][4 * lane + k];
-        c[k] = x;
-        tot += x;
+        c[k] = sh.bins[4 * lane + k];
+        tot += c[k];
       }
       const uint32_t inc = wave_incl_scan(tot);
       const int need = sh.need;
