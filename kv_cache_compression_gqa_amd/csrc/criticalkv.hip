@@ -440,8 +440,9 @@ __device__ __forceinline__ void for_keys(const float* __restrict__ sc, int n, in
 
 // Takes (sets in `taken`) the first b entries not yet taken in (key asc, index asc). Each pass: 8-bit digit
 // histograms in per-wave LDS copies, summed per bin by 256 threads, then one wave finds the bin holding the
-// need-th key. (Grouping a wave's lanes by bin before the atomic, tried for the top digit, cost as much as the
-// contention it saved on attention-like scores and three times more on widely spread ones.)
+// need-th key. For the top digit, a per-thread four-entry count cache takes the place of most atomics; grouping
+// a wave's lanes by bin before each atomic, tried before, cost as much as the contention it saved on
+// attention-like scores and three times more on widely spread ones.
 __device__ __forceinline__ void select_stage(const float* __restrict__ sc, int n, int i0, uint64_t& taken, int b,
                                              SelShared& sh) {
   if (b <= 0) return;
@@ -456,11 +457,42 @@ __device__ __forceinline__ void select_stage(const float* __restrict__ sc, int n
     __syncthreads();
     const uint32_t prefix = sh.prefix;
     const int shift = 24 - 8 * pass;
-    for_keys(sc, n, i0, [&](int e, uint32_t key) {
-      if (!((done >> e) & 1u) && (pass == 0 || (key >> (shift + 8)) == prefix)) {
-        atomicAdd(&sh.hist[wave][(key >> shift) & 255u], 1u);
+    if (pass == 0) {
+      // the top digit (sign and exponent bits) takes few distinct values per thread: counts gather in a four-entry
+      // per-thread cache and reach LDS when evicted or at the end
+      uint32_t cb[4] = {256u, 256u, 256u, 256u}, cc[4] = {0u, 0u, 0u, 0u};
+      for_keys(sc, n, i0, [&](int e, uint32_t key) {
+        if ((done >> e) & 1u) return;
+        const uint32_t b = key >> 24;
+        if (b == cb[0]) {
+          ++cc[0];
+        } else if (b == cb[1]) {
+          ++cc[1];
+        } else if (b == cb[2]) {
+          ++cc[2];
+        } else if (b == cb[3]) {
+          ++cc[3];
+        } else {
+          if (cc[3] != 0u) atomicAdd(&sh.hist[wave][cb[3]], cc[3]);
+          cb[3] = cb[2];
+          cc[3] = cc[2];
+          cb[2] = cb[1];
+          cc[2] = cc[1];
+          cb[1] = cb[0];
+          cc[1] = cc[0];
+          cb[0] = b;
+          cc[0] = 1u;
+        }
+      });
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (cc[j] != 0u) atomicAdd(&sh.hist[wave][cb[j]], cc[j]);
       }
-    });
+    } else {
+      for_keys(sc, n, i0, [&](int e, uint32_t key) {
+        if (!((done >> e) & 1u) && (key >> (shift + 8)) == prefix) atomicAdd(&sh.hist[wave][(key >> shift) & 255u], 1u);
+      });
+    }
     __syncthreads();
     if (threadIdx.x < 256) {  // the per-wave copies summed per bin, by 256 threads at once
       uint32_t x = 0;
