@@ -103,7 +103,7 @@ def make_decode(cfg: DecodeWorkload, units=None, steps: int | None = None) -> De
     lens = np.array([seq_lens[cfg.unit_coords(int(u))[1]] for u in all_units], dtype=np.int64)
     W, D, G = cfg.window, cfg.head_dim, cfg.group
     nw = lens // W
-    NW = int((seq_lens // W).max())
+    NW = max(1, int((seq_lens // W).max()))  # window capacity (at least one slot, even when no window is full)
     Up = len(all_units)
     k_win = np.zeros((Up, NW, W, D), np.uint16)
     v_win = np.zeros((Up, NW, W, D), np.uint16)

@@ -51,6 +51,25 @@ def test_group_of_eight_and_one(gpu_lib):
         run_decode_parity(cfg, log=log)
 
 
+@pytest.mark.parametrize("case", ["no_budget", "full_budget", "context_below_one_window", "exactly_one_window"])
+def test_degenerate_budgets_and_contexts(gpu_lib, case):
+    """Budgets 0/0 (every window evicted at the first event, then the tail alone is attended), a FULL budget equal to
+    the window count (nothing quantised or evicted), a context shorter than one window (no window at all: the tail
+    alone, with routing over an empty set), and a context of exactly one window (empty prefill tail)."""
+    base = dict(name=f"degenerate_{case}", seed=15, context=640, n_salient=5, steps=6, route_every=2)
+    if case == "no_budget":
+        base.update(budget_full=0, budget_int2=0)
+    elif case == "full_budget":
+        base.update(budget_full=20, budget_int2=0)
+    elif case == "context_below_one_window":
+        base.update(context=20, n_salient=1, budget_full=1, budget_int2=1)
+    else:
+        base.update(context=32, n_salient=1, budget_full=1, budget_int2=1)
+    cfg = dataclasses.replace(configs.TINY, **base)
+    log(f"case: {case}")
+    run_decode_parity(cfg, log=log)
+
+
 def test_many_units_two_int2_windows_per_task(gpu_lib):
     """1280 units: a step takes many rounds of workgroups, so the launch switches to two INT2 windows per wave
     task and 4-wave workgroups. G = 8 (f16), 1 (bf16) and 2 (f16), probabilities on; the oracle follows units
