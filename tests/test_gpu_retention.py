@@ -116,6 +116,42 @@ def test_topm_edge_cases_and_ties(gpu_lib, m_kind):
     _check_topm(torch.from_numpy(s), tm, m)
 
 
+def test_compaction_edge_rows(gpu_lib):
+    """Rows with nothing kept, everything kept, exactly one page, one row past a page, only the last position, and
+    a random tenth, over two 4096-position chunks per row; then a rejected source page id, whose rows must come
+    out as zeros with the bound bit raised."""
+    import torch
+    from kv_cache_compression_gqa_amd import retention
+    cfg = configs.DBTRIM_128K
+    T = 8192
+    rng = np.random.default_rng(21)
+    keep = np.zeros((cfg.hkv, T), dtype=bool)
+    keep[1] = True
+    keep[2, rng.choice(T, 16, replace=False)] = True
+    keep[3, 4090:4107] = True                      # 17 kept, straddling the chunk boundary
+    keep[4, T - 1] = True
+    keep[5] = rng.random(T) < 0.1
+    keep[6, :4096] = True                          # first chunk only
+    keep[7, 4096:] = rng.random(4096) < 0.5        # second chunk only
+    pt = synth.make_page_table(cfg, layers=1, n_tokens=T)
+    _check_compaction(keep, pt, cfg, 1, T)
+    # a page id outside the pool: its kept rows are written as zeros and the bound bit is raised
+    n_src = cfg.hkv * (T // cfg.page)
+    bad = pt.copy().reshape(cfg.hkv, T // cfg.page)
+    bad[1, 3] = n_src
+    k_pool, v_pool = _pools(n_src, cfg.page, cfg.head_dim, 11, 12, cfg.dtype)
+    keep_t = torch.from_numpy(keep.astype(np.uint8)).cuda()
+    out = retention.compact_pages(keep_t, torch.from_numpy(bad.astype(np.int32)).cuda(), k_pool, v_pool,
+                                  out_pages_max=int(np.ceil(keep.sum(axis=1) / cfg.page).sum()) + 1,
+                                  kv_dtype=abi.KVC_BF16)
+    torch.cuda.synchronize()
+    assert int(out.status.item()) & abi.KVC_DEV_BOUND_EXCEEDED
+    start = int(out.page_offset[1].item()) * cfg.page + 3 * cfg.page  # row 1 keeps everything: page 3's rows
+    for got in (out.k, out.v):
+        rows = got.view(torch.int16).reshape(-1, cfg.head_dim)[start:start + cfg.page]
+        assert not bool(rows.any()), "rows of the rejected page are not zero"
+
+
 def test_retention_full_size(gpu_lib):
     """32 layers x 8 KV heads x 131072 tokens, M = 10%: every score, the whole keep mask and every copied row."""
     import torch
