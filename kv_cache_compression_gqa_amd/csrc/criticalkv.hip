@@ -25,6 +25,7 @@
 //   two_stage: one workgroup per KV head: two radix selects (8-bit digits) in (score desc, index asc) order, the
 //     second over the entries the first did not take; output ascending.
 #include <algorithm>
+#include <type_traits>
 
 #include "kvc_internal.h"
 
@@ -240,61 +241,71 @@ __global__ __launch_bounds__(512) void obs_attn(const uint16_t* __restrict__ q, 
   const int nkeys = min(kObsChunk, n - key0);
   const uint16_t* kg = k + size_t(g) * n * kD;
   constexpr int kBatch = 8;  // key tiles whose loads are in flight together
-  for (int tb = 0; tb * 16 < nkeys; tb += kBatch) {
-    u32x4 ka[kBatch][4];
+  // MASKED: the chunk holds keys past the end or inside the observation window (causal mask), which only the last
+  // chunks do; the others skip the per-element checks
+  auto sweep = [&](auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
+    for (int tb = 0; tb * 16 < nkeys; tb += kBatch) {
+      u32x4 ka[kBatch][4];
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int tok = min(key0 + 16 * (tb + b) + col, n - 1);
+      for (int b = 0; b < kBatch; ++b) {
+        const int tok = min(key0 + 16 * (tb + b) + col, n - 1);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) ka[b][kk] = ld16(kg + size_t(tok) * kD + 32 * kk + 8 * qq);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int tile_key0 = key0 + 16 * (tb + b);
-      if (tile_key0 >= key0 + nkeys) break;
-      f32x4 s[2];
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        s[ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) s[ct] = Mfma<T>::m16(ka[b][kk], bq[ct][kk], s[ct]);
+        for (int kk = 0; kk < 4; ++kk) ka[b][kk] = ld16(kg + size_t(tok) * kD + 32 * kk + 8 * qq);
       }
-      float pv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const int obs_pos = n - kObs + 16 * ct + col;  // position of this column's query
+      for (int b = 0; b < kBatch; ++b) {
+        const int tile_key0 = key0 + 16 * (tb + b);
+        if (tile_key0 >= key0 + nkeys) break;
+        f32x4 s[2];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = tile_key0 + 4 * qq + r;
-          const bool ok = key < n && key <= obs_pos;
-          const float sv = ok ? s[ct][r] * kInvSqrtD : -INFINITY;
+        for (int ct = 0; ct < 2; ++ct) {
+          s[ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) s[ct] = Mfma<T>::m16(ka[b][kk], bq[ct][kk], s[ct]);
+        }
+        float pv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          const int obs_pos = n - kObs + 16 * ct + col;  // position of this column's query
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = tile_key0 + 4 * qq + r;
+            const bool ok = !MASKED || (key < n && key <= obs_pos);
+            const float sv = ok ? s[ct][r] * kInvSqrtD : -INFINITY;
+            if (PASS == 1) {
+              s[ct][r] = sv;
+            } else {
+              pv[r] += exp_diff(sv, rm[ct]) * ril[ct];
+            }
+          }
           if (PASS == 1) {
-            s[ct][r] = sv;
-          } else {
-            pv[r] += exp_diff(sv, rm[ct]) * ril[ct];
+            const float mt = fmaxf(fmaxf(s[ct][0], s[ct][1]), fmaxf(s[ct][2], s[ct][3]));
+            const float mn = fmaxf(m[ct], mt);
+            float add = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) add += exp_diff(s[ct][r], mn);
+            l[ct] = l[ct] * exp_diff(m[ct], mn) + add;
+            m[ct] = mn;
           }
         }
-        if (PASS == 1) {
-          const float mt = fmaxf(fmaxf(s[ct][0], s[ct][1]), fmaxf(s[ct][2], s[ct][3]));
-          const float mn = fmaxf(m[ct], mt);
-          float add = 0.0f;
+        if (PASS == 2) {
+          // sum over the head's 32 query rows: the two column tiles are already added; now the 16 columns
 #pragma unroll
-          for (int r = 0; r < 4; ++r) add += exp_diff(s[ct][r], mn);
-          l[ct] = l[ct] * exp_diff(m[ct], mn) + add;
-          m[ct] = mn;
-        }
-      }
-      if (PASS == 2) {
-        // sum over the head's 32 query rows: the two column tiles are already added; now the 16 columns
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float tot = row_sum16(pv[r]) * (1.0f / kObs);
-          const int key = tile_key0 + 4 * qq + r;
-          if (col == 0 && key < n) a_head[size_t(h) * n + key] = tot;
+          for (int r = 0; r < 4; ++r) {
+            const float tot = row_sum16(pv[r]) * (1.0f / kObs);
+            const int key = tile_key0 + 4 * qq + r;
+            if (col == 0 && key < n) a_head[size_t(h) * n + key] = tot;
+          }
         }
       }
     }
+  };
+  if (key0 + kObsChunk <= n - kObs) {
+    sweep(std::false_type{});
+  } else {
+    sweep(std::true_type{});
   }
   if (PASS == 1) {
     // merge the four 16-lane groups (different keys, same query rows)
