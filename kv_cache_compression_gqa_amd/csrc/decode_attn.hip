@@ -478,8 +478,11 @@ __device__ __forceinline__ void int2_task(const DecodeParams& p, const Ctx& c, c
 template <int G, class T, bool PROBS, int QW, int WPB>
 __global__ __launch_bounds__(WPB * kWave) __attribute__((amdgpu_waves_per_eu(4))) void decode_partial(DecodeParams p) {
   fetch_args_partial(p);
-  const int u = blockIdx.x / p.P;
-  const int sl = blockIdx.x - u * p.P;
+  // one-round launches (WPB 8) go slice-major, so that every unit's slices are spread over the launch order; many
+  // rounds (WPB 4) keep a unit's slices together
+  const int nu = int(gridDim.x) / p.P;
+  const int u = WPB == 8 ? int(blockIdx.x) % nu : int(blockIdx.x) / p.P;
+  const int sl = WPB == 8 ? int(blockIdx.x) / nu : int(blockIdx.x) - u * p.P;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int task = sl * WPB + wave;  // wave-uniform (scalar)
