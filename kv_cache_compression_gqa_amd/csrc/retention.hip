@@ -133,6 +133,12 @@ __device__ __forceinline__ bool digit_of(uint32_t key, uint32_t prefix, uint32_t
   }
 }
 
+// A histogram workgroup of pass P takes hist_group(P) consecutive chunks of one row: one LDS clear and one flush
+// of the 2048 bins to the global histogram serve all of them (the flush's global atomics land on the same few
+// hot bins from every workgroup; passes 0 and 1 gain, pass 2, with few matching keys, runs one chunk each). The next chunk's loads are issued
+// before the current chunk's atomics.
+constexpr int hist_group(int P) { return P == 2 ? 1 : 4; }
+
 template <int P>
 __global__ __launch_bounds__(kTB) void topm_hist(const float* __restrict__ scores, TopmWs ws, int32_t row_len) {
   __shared__ uint32_t h[4][kBins];
@@ -140,22 +146,38 @@ __global__ __launch_bounds__(kTB) void topm_hist(const float* __restrict__ score
   for (int i = threadIdx.x; i < 4 * kBins; i += kTB) (&h[0][0])[i] = 0u;
   __syncthreads();
   const uint32_t prefix = P == 0 ? 0u : ws.state->prefix;
-  const BlockRange r = block_range(blockIdx.x, row_len, kChunk);
-  float4 v[kVecPerThread];  // every load of the thread in flight at once (clamped into the block's range)
+  const int per_row = (row_len + kChunk - 1) / kChunk;
+  constexpr int kG = hist_group(P);
+  const int groups = (per_row + kG - 1) / kG;
+  const int64_t row = blockIdx.x / groups;
+  const int c0 = int(blockIdx.x - row * groups) * kG;
+  const int nc = min(kG, per_row - c0);
+  // every load of a chunk in flight at once (clamped into the chunk's range)
+  auto load = [&](int c, float4 (&v)[kVecPerThread]) {
+    const BlockRange r = block_range(row * per_row + c, row_len, kChunk);
 #pragma unroll
-  for (int u = 0; u < kVecPerThread; ++u) {
-    const int64_t e = min(r.beg + 4 * (threadIdx.x + kTB * u), r.end - 4);
-    v[u] = *reinterpret_cast<const float4*>(scores + e);
-  }
-#pragma unroll
-  for (int u = 0; u < kVecPerThread; ++u) {
-    if (r.beg + 4 * (threadIdx.x + kTB * u) >= r.end) break;
-    const float vs[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      uint32_t bin;
-      if (digit_of<P>(desc_key(vs[c]), prefix, bin)) atomicAdd(&h[wave][bin], 1u);
+    for (int u = 0; u < kVecPerThread; ++u) {
+      const int64_t e = min(r.beg + 4 * (threadIdx.x + kTB * u), r.end - 4);
+      v[u] = *reinterpret_cast<const float4*>(scores + e);
     }
+  };
+  float4 v[kVecPerThread], vn[kVecPerThread];
+  load(c0, v);
+  for (int k = 0; k < nc; ++k) {
+    if (k + 1 < nc) load(c0 + k + 1, vn);
+    const BlockRange r = block_range(row * per_row + c0 + k, row_len, kChunk);
+#pragma unroll
+    for (int u = 0; u < kVecPerThread; ++u) {
+      if (r.beg + 4 * (threadIdx.x + kTB * u) >= r.end) break;
+      const float vs[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        uint32_t bin;
+        if (digit_of<P>(desc_key(vs[c]), prefix, bin)) atomicAdd(&h[wave][bin], 1u);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kVecPerThread; ++u) v[u] = vn[u];
   }
   __syncthreads();
   for (int bin = threadIdx.x; bin < kBins; bin += kTB) {
@@ -486,11 +508,13 @@ hipError_t launch_topm(const kvc_topm_args& a, void* ws_ptr, hipStream_t s) {
   // m == 0 and m == n need no special case: the picks then select the first key's bin with nothing to take, or
   // the last key's bin with every key taken
   const dim3 grid{unsigned(nb), 1, 1};
-  hipLaunchKernelGGL(topm_hist<0>, grid, dim3(kTB), 0, s, a.scores, ws, a.row_len);
+  const int64_t per_row = (a.row_len + kChunk - 1) / kChunk;
+  auto hgrid = [&](int g) { return dim3{unsigned(n_rows * ((per_row + g - 1) / g)), 1, 1}; };
+  hipLaunchKernelGGL(topm_hist<0>, hgrid(hist_group(0)), dim3(kTB), 0, s, a.scores, ws, a.row_len);
   hipLaunchKernelGGL(topm_pick<0>, dim3(1), dim3(kTB), 0, s, ws, a.m);
-  hipLaunchKernelGGL(topm_hist<1>, grid, dim3(kTB), 0, s, a.scores, ws, a.row_len);
+  hipLaunchKernelGGL(topm_hist<1>, hgrid(hist_group(1)), dim3(kTB), 0, s, a.scores, ws, a.row_len);
   hipLaunchKernelGGL(topm_pick<1>, dim3(1), dim3(kTB), 0, s, ws, a.m);
-  hipLaunchKernelGGL(topm_hist<2>, grid, dim3(kTB), 0, s, a.scores, ws, a.row_len);
+  hipLaunchKernelGGL(topm_hist<2>, hgrid(hist_group(2)), dim3(kTB), 0, s, a.scores, ws, a.row_len);
   hipLaunchKernelGGL(topm_pick<2>, dim3(1), dim3(kTB), 0, s, ws, a.m);
   hipLaunchKernelGGL(topm_mark, grid, dim3(kTB), 0, s, a.scores, a.keep, a.row_counts, ws, a.row_len, a.status);
   hipLaunchKernelGGL(topm_tie_scan, dim3(1), dim3(kTB), 0, s, ws, nb);
