@@ -135,8 +135,8 @@ __device__ __forceinline__ bool digit_of(uint32_t key, uint32_t prefix, uint32_t
 
 // A histogram workgroup of pass P takes hist_group(P) consecutive chunks of one row: one LDS clear and one flush
 // of the 2048 bins to the global histogram serve all of them (the flush's global atomics land on the same few
-// hot bins from every workgroup; passes 0 and 1 gain, pass 2, with few matching keys, runs one chunk each). The next chunk's loads are issued
-// before the current chunk's atomics.
+// hot bins from every workgroup). Passes 0 and 1 gain; pass 2, with few matching keys, runs one chunk each. The
+// next chunk's loads are issued before the current chunk's atomics.
 constexpr int hist_group(int P) { return P == 2 ? 1 : 4; }
 
 template <int P>
