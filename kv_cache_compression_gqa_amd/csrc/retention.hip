@@ -382,7 +382,7 @@ __global__ __launch_bounds__(kTB) void compact_index(const uint8_t* __restrict__
                                                      int32_t page, int64_t n_src_pages, int64_t out_pages_max,
                                                      int32_t* status) {
   __shared__ int32_t src_s[kCChunk];
-  __shared__ int32_t pg_s[kCChunk];  // page id per block of `page` positions of the chunk (page >= 1)
+  extern __shared__ int32_t pg_s[];  // page id per block of `page` positions of the chunk (sized at launch)
   __shared__ int wsum[kTB / kWave];
   const BlockRange r = block_range(blockIdx.x, row_len, kCChunk);
   const int64_t pos0 = r.beg - r.row * row_len;  // first position of the chunk within its row
@@ -544,7 +544,8 @@ hipError_t launch_compact(const kvc_compact_args& a, void* ws_ptr, hipStream_t s
   hipLaunchKernelGGL(compact_count, dim3(unsigned(nb)), dim3(kTB), 0, s, a.keep, ws, a.n_tokens);
   hipLaunchKernelGGL(compact_plan, dim3(1), dim3(kTB), 0, s, ws, a.n_rows, chunks, a.page, a.lengths, a.page_offset,
                      a.n_pages, a.out_pages_max, a.status);
-  hipLaunchKernelGGL(compact_index, dim3(unsigned(nb)), dim3(kTB), 0, s, a.keep, a.page_table, ws, a.lengths,
+  const size_t pg_lds = size_t((kCChunk + a.page - 1) / a.page) * sizeof(int32_t);
+  hipLaunchKernelGGL(compact_index, dim3(unsigned(nb)), dim3(kTB), pg_lds, s, a.keep, a.page_table, ws, a.lengths,
                      a.page_offset, a.n_pages, a.n_tokens, a.page, a.n_src_pages, a.out_pages_max, a.status);
   const int64_t cap_rows = a.out_pages_max * a.page;
   const int64_t gb = (cap_rows + kGRows - 1) / kGRows;
