@@ -240,20 +240,41 @@ __global__ __launch_bounds__(512) void obs_attn(const uint16_t* __restrict__ q, 
   const int key0 = ch * kObsChunk;
   const int nkeys = min(kObsChunk, n - key0);
   const uint16_t* kg = k + size_t(g) * n * kD;
-  constexpr int kBatch = 8;  // key tiles whose loads are in flight together
+  // The workgroup's waves (one per query head) share the chunk's keys: batches of kBatch key tiles (64 keys,
+  // 16 KiB) are copied global -> LDS by the load unit (global_load_lds_dwordx4; the next batch while the current
+  // one is computed) instead of every wave loading the same keys. Key row r's 16-byte chunk q sits at slot
+  // q ^ (r % 16), so each A-fragment read (16 rows, one chunk each) is conflict-free.
+  constexpr int kBatch = 4;
+  __shared__ __attribute__((aligned(16))) uint16_t ks[2][kBatch * 16 * kD];
+  typedef __attribute__((address_space(3))) uint16_t lds_u16;
+  const uint32_t ks0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u16*)(&ks[0][0])));
+  const int ntiles = (nkeys + 15) / 16;
+  const int nbatch = (ntiles + kBatch - 1) / kBatch;
+  // batch bt -> buffer buf: instruction m (of 16, taken by the waves in turn) moves key rows 4m .. 4m+3
+  auto copy_batch = [&](int bt, int buf) {
+    for (int m = wave; m < kBatch * 4; m += group) {
+      const int row = 4 * m + (lane >> 4);
+      const int qc = (lane & 15) ^ (row & 15);
+      const int tok = min(key0 + kBatch * 16 * bt + row, n - 1);
+      dma16(kg + size_t(tok) * kD + 8 * qc, ks0 + uint32_t(buf * kBatch * 16 * kD * 2 + m * 1024));
+    }
+  };
   // MASKED: the chunk holds keys past the end or inside the observation window (causal mask), which only the last
   // chunks do; the others skip the per-element checks
   auto sweep = [&](auto masked) {
     constexpr bool MASKED = decltype(masked)::value;
-    for (int tb = 0; tb * 16 < nkeys; tb += kBatch) {
+    for (int bt = 0; bt < nbatch; ++bt) {
+      const int cur = bt & 1;
+      if (bt + 1 < nbatch) copy_batch(bt + 1, cur ^ 1);
+      const int tb = bt * kBatch;
       u32x4 ka[kBatch][4];
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
-        const int tok = min(key0 + 16 * (tb + b) + col, n - 1);
+        const int row = 16 * b + col;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) ka[b][kk] = ld16(kg + size_t(tok) * kD + 32 * kk + 8 * qq);
+        for (int kk = 0; kk < 4; ++kk)
+          ka[b][kk] = *reinterpret_cast<const u32x4*>(&ks[cur][row * kD + 8 * ((4 * kk + qq) ^ col)]);
       }
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
         const int tile_key0 = key0 + 16 * (tb + b);
@@ -300,8 +321,13 @@ __global__ __launch_bounds__(512) void obs_attn(const uint16_t* __restrict__ q, 
           }
         }
       }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of the next batch has landed
+      __syncthreads();                                   // everyone's has, and the current buffer is free
     }
   };
+  copy_batch(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
   if (key0 + kObsChunk <= n - kObs) {
     sweep(std::false_type{});
   } else {
