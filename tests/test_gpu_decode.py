@@ -2,7 +2,8 @@
 
 Covers: per-step attention output, per-key probabilities, window mass and cumulative score; routing tiers and
 lists (bit-exact on the GPU's scores); write-once ledger bytes; promoted copies; adversarial quantiser groups;
-adversarial routing scores (ties, zeros, signed zeros); the write-once violation flag; determinism.
+adversarial routing scores (ties, zeros, signed zeros); the write-once violation flag; ledger lists over more units
+than one launch serves, with ragged counts and bad ids; determinism.
 """
 import dataclasses
 import sys
@@ -173,6 +174,83 @@ def test_write_once_violation_is_refused(gpu_lib):
     assert sess.device_status() & abi.KVC_DEV_LEDGER_REWRITE
     assert torch.equal(before[0], sess.k_codes) and torch.equal(before[1], sess.k_meta)
     assert torch.equal(before[2], sess.v_codes)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_ledger_lists_over_more_units_than_one_launch_span(gpu_lib, dtype):
+    """kvc_quantize_int2, then kvc_promote, on per-unit lists over 4100 units (the library serves at most 4096
+    units per launch), with ragged counts (0 to 8 windows, one unit listing every window, one empty list) and
+    out-of-range ids: codes, scale/zero words, ledger flags and promoted copies are byte-exact against the oracle
+    quantiser on sampled units on both sides of the span boundary, and the bad ids set the bound status bit."""
+    import ctypes as C
+    from kv_cache_compression_gqa_amd import abi, layout
+    from oracle.fp import f32_to_storage_rne
+    from oracle.int2 import dequantize, quantize
+    cfg = dataclasses.replace(configs.TINY, dtype=dtype, name=f"ledger_span_{dtype}", seed=24)
+    inp = synth.make_decode(cfg, steps=1)
+    U = 4100
+    umap = np.arange(U) % len(inp.units)
+    sess = DecodeSession(inp, unit_map=umap)
+    NW = sess.NW
+    rng = np.random.default_rng(25)
+    counts = rng.integers(0, 9, U)
+    counts[[3, 4097]] = NW
+    counts[[10, 4096]] = (0, 5)
+    lists = np.zeros((U, NW), np.int32)
+    for u in range(U):
+        lists[u, :counts[u]] = np.sort(rng.choice(NW, counts[u], replace=False))
+    bad = {(3, 0): NW + 3, (4096, 2): -1}
+    valid = lists.copy()
+    for (u, j), w in bad.items():
+        lists[u, j] = w
+    lst = torch.from_numpy(lists).cuda()
+    cnt = torch.from_numpy(counts.astype(np.int32)).cuda()
+    L = abi.lib()
+    log(f"case: quantise {int(counts.sum())} listed windows over {U} units ({dtype})")
+    abi.check(L.kvc_quantize_int2(C.byref(sess._cache), abi.ptr(lst), abi.ptr(cnt), NW, int(counts.sum()),
+                                  abi.stream_handle()), "quantize")
+    torch.cuda.synchronize()
+    assert sess.device_status() == abi.KVC_DEV_BOUND_EXCEEDED
+    sample = [0, 1, 3, 10, 4095, 4096, 4097, 4099]
+    sel = torch.tensor(sample, dtype=torch.int64, device="cuda")
+    g = lambda t: t.index_select(0, sel).cpu().numpy()  # noqa: E731
+    kc, vc = g(sess.k_codes), g(sess.v_codes).view(np.uint16)
+    km, vm, led = g(sess.k_meta).view(np.uint32), g(sess.v_meta).view(np.uint32), g(sess.ledgered)
+    expect = {}
+    for r, u in enumerate(sample):
+        b = int(umap[u])
+        listed = {int(w) for j, w in enumerate(valid[u, :counts[u]]) if (u, j) not in bad}
+        for w in range(NW):
+            if w not in listed:
+                assert led[r, w] == 0 and not kc[r, w].any() and not km[r, w].any(), f"unit {u} window {w}"
+                continue
+            kq, ks, kz = quantize(inp.k_win[b, w], dtype)
+            vq, vs, vz = quantize(inp.v_win[b, w], dtype)
+            expect[(u, w)] = (kq, ks, kz, vq, vs, vz)
+            assert led[r, w] == 1, f"ledger flag unit {u} window {w}"
+            assert kc[r, w].tobytes() == layout.k_codes_to_lib(kq).tobytes(), f"K codes unit {u} window {w}"
+            assert vc[r, w].tobytes() == layout.v_codes_to_lib(vq).tobytes(), f"V codes unit {u} window {w}"
+            assert km[r, w].tobytes() == layout.k_meta_to_lib(ks, kz).tobytes(), f"K meta unit {u} window {w}"
+            assert vm[r, w].tobytes() == layout.v_meta_to_lib(vs, vz).tobytes(), f"V meta unit {u} window {w}"
+    # promotion of the same lists over scribbled full-precision copies
+    sess.k_win.fill_(0x7E7E)
+    sess.v_win.fill_(0x7E7E)
+    log("case: promote the same lists")
+    abi.check(L.kvc_promote(C.byref(sess._cache), abi.ptr(lst), abi.ptr(cnt), NW, int(counts.sum()),
+                            abi.stream_handle()), "promote")
+    torch.cuda.synchronize()
+    assert sess.device_status() == abi.KVC_DEV_BOUND_EXCEEDED
+    kw, vw = g(sess.k_win).view(np.uint16), g(sess.v_win).view(np.uint16)
+    for r, u in enumerate(sample):
+        for w in range(NW):
+            if (u, w) not in expect:
+                assert np.all(kw[r, w] == 0x7E7E) and np.all(vw[r, w] == 0x7E7E), f"unit {u} window {w} written"
+                continue
+            kq, ks, kz, vq, vs, vz = expect[(u, w)]
+            assert kw[r, w].tobytes() == f32_to_storage_rne(dequantize(kq, ks, kz), dtype).tobytes(), (u, w)
+            assert (layout.v_win_from_lib(vw[r, w]).tobytes() ==
+                    f32_to_storage_rne(dequantize(vq, vs, vz), dtype).tobytes()), (u, w)
+    log(f"ledger lists over {U} units: {len(expect)} sampled windows match")
 
 
 def test_probabilities_sum_to_one_and_runs_are_bitwise_reproducible(gpu_lib):
