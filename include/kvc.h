@@ -290,6 +290,43 @@ typedef struct kvc_compact_args {
   int32_t kv_dtype;
 } kvc_compact_args;
 
+/* kvc_paged_decode_attn: decode attention over per-row variable-length page lists (DBTrimKV page, "Metodologia:
+ * Evicção Baseada em Retenção Global", section 4: after the global budget every (layer, KV head) row keeps a
+ * sequence of its own length in paged storage; kvc_compact_pages writes such pages). For row r, token i is row
+ * i % page of pool page page_list[r * page_stride + i / page]; the row's G query heads attend over its lengths[r]
+ * tokens with scaled dot-product attention: out[r][h] = sum_i softmax_i(q[r][h] . k_i / sqrt(128)) v_i (fp32).
+ * A row of length 0 gets zeros.
+ *   q              [n_rows][group][128] storage dtype, 16-byte aligned.
+ *   k_pool, v_pool [n_pool_pages][page][128] storage dtype (token-major pages), 16-byte aligned; rows of a
+ *                  listed page past the row's length are read but never weigh in.
+ *   page_list      [n_rows][page_stride] int32 pool page ids; entries past a row's page count are never read.
+ *   lengths        [n_rows] int32 tokens per row.
+ *   out            [n_rows][group][128] float32.
+ *   status         int32 device error bits: KVC_DEV_BOUND_EXCEEDED if a length exceeds max_pages * page (tokens
+ *                  past the bound are ignored) or a listed page id is outside [0, n_pool_pages) (its tokens are
+ *                  ignored).
+ *   group in {1, 2, 4, 8}; page a multiple of 16 in [16, 1024]; max_pages = HOST bound on every row's page count
+ *   (sizes the grid), 1 <= max_pages <= page_stride, max_pages * page <= 2^24; head_dim 128; n_pool_pages >= 1.
+ * Workspace: kvc_paged_decode_workspace(args) bytes, any contents, 256-byte aligned. */
+typedef struct kvc_paged_decode_args {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* page_list;
+  const int32_t* lengths;
+  float* out;
+  int32_t* status;
+  int64_t n_rows;
+  int64_t n_pool_pages;
+  int64_t page_stride;
+  int32_t group;
+  int32_t page;
+  int32_t max_pages;
+  int32_t head_dim;
+  int32_t kv_dtype;
+  int32_t reserved;
+} kvc_paged_decode_args;
+
 /* kvc_score(KVC_SCORE_WINDOWS): the scoring half of a decode step — the same kernels as kvc_decode_attn with
  * out = NULL: probabilities, window mass and the cumulative score update over the mixed cache. */
 typedef struct kvc_window_score_args {
@@ -336,6 +373,10 @@ int kvc_promote(const kvc_cache* cache, const int32_t* list, const int32_t* coun
 
 size_t kvc_compact_pages_workspace(const kvc_compact_args* args);
 int kvc_compact_pages(const kvc_compact_args* args, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+size_t kvc_paged_decode_workspace(const kvc_paged_decode_args* args);
+int kvc_paged_decode_attn(const kvc_paged_decode_args* args, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
 
 /* Reads *cache->status into *host_status (synchronises the stream) and, if clear != 0, zeroes it. */
 int kvc_read_device_status(const kvc_cache* cache, int32_t* host_status, int32_t clear, hipStream_t stream);

@@ -80,6 +80,13 @@ class KvcTwoStageArgs(C.Structure):
                 ("budget1", C.c_int32)]
 
 
+class KvcPagedDecodeArgs(C.Structure):
+    _fields_ = [("q", P), ("k_pool", P), ("v_pool", P), ("page_list", P), ("lengths", P), ("out", P), ("status", P),
+                ("n_rows", C.c_int64), ("n_pool_pages", C.c_int64), ("page_stride", C.c_int64),
+                ("group", C.c_int32), ("page", C.c_int32), ("max_pages", C.c_int32), ("head_dim", C.c_int32),
+                ("kv_dtype", C.c_int32), ("reserved", C.c_int32)]
+
+
 # name -> (restype, argtypes); every symbol include/kvc.h declares
 SIGNATURES = {
     "kvc_abi_version": (C.c_int, []),
@@ -95,6 +102,8 @@ SIGNATURES = {
     "kvc_read_device_status": (C.c_int, [C.POINTER(KvcCache), C.POINTER(C.c_int32), C.c_int32, P]),
     "kvc_compact_pages_workspace": (C.c_size_t, [C.POINTER(KvcCompactArgs)]),
     "kvc_compact_pages": (C.c_int, [C.POINTER(KvcCompactArgs), P, C.c_size_t, P]),
+    "kvc_paged_decode_workspace": (C.c_size_t, [C.POINTER(KvcPagedDecodeArgs)]),
+    "kvc_paged_decode_attn": (C.c_int, [C.POINTER(KvcPagedDecodeArgs), P, C.c_size_t, P]),
 }
 
 

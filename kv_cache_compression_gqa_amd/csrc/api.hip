@@ -66,6 +66,28 @@ int check_list(const kvc_cache* c, const int32_t* list, const int32_t* count, in
   return KVC_OK;
 }
 
+int check_paged(const kvc_paged_decode_args* a) {
+  if (a == nullptr || a->reserved != 0) return KVC_E_INVALID;
+  if (a->head_dim != kvc::kD) return KVC_E_UNSUPPORTED;
+  if (!(a->group == 1 || a->group == 2 || a->group == 4 || a->group == 8)) return KVC_E_UNSUPPORTED;
+  if (a->kv_dtype != KVC_F16 && a->kv_dtype != KVC_BF16) return KVC_E_UNSUPPORTED;
+  if (a->page < 16 || a->page > 1024 || a->page % 16 != 0) return KVC_E_INVALID;
+  if (a->max_pages < 1 || a->page_stride < a->max_pages || int64_t(a->max_pages) * a->page > (int64_t(1) << 24)) {
+    return KVC_E_INVALID;
+  }
+  if (a->n_rows < 0 || a->n_rows > (int64_t(1) << 20) || a->n_pool_pages < 1) return KVC_E_INVALID;
+  if (a->n_rows == 0) return KVC_OK;
+  const void* need16[] = {a->q, a->k_pool, a->v_pool};
+  for (const void* p : need16) {
+    if (p == nullptr || !aligned(p, 16)) return KVC_E_INVALID;
+  }
+  const void* need4[] = {a->page_list, a->lengths, a->out, a->status};
+  for (const void* p : need4) {
+    if (p == nullptr || !aligned(p, 4)) return KVC_E_INVALID;
+  }
+  return KVC_OK;
+}
+
 int check_retention(const kvc_retention_args* a) {
   if (a == nullptr || a->beta == nullptr || a->score == nullptr) return KVC_E_INVALID;
   if (!aligned(a->beta, 16) || !aligned(a->score, 16)) return KVC_E_INVALID;
@@ -270,6 +292,22 @@ int kvc_promote(const kvc_cache* cache, const int32_t* list, const int32_t* coun
   if (st != KVC_OK) return st;
   return kvc::launch_promote(*cache, list, count, list_stride, max_total, stream) == hipSuccess ? KVC_OK
                                                                                                 : KVC_E_HIP;
+}
+
+size_t kvc_paged_decode_workspace(const kvc_paged_decode_args* args) {
+  if (check_paged(args) != KVC_OK) return 0;
+  return kvc::paged_workspace_bytes(*args);
+}
+
+int kvc_paged_decode_attn(const kvc_paged_decode_args* args, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  const int st = check_paged(args);
+  if (st != KVC_OK) return st;
+  if (args->n_rows == 0) return KVC_OK;
+  if (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < kvc::paged_workspace_bytes(*args)) {
+    return KVC_E_WORKSPACE;
+  }
+  return kvc::launch_paged_decode(*args, workspace, stream) == hipSuccess ? KVC_OK : KVC_E_HIP;
 }
 
 int kvc_read_device_status(const kvc_cache* cache, int32_t* host_status, int32_t clear, hipStream_t stream) {

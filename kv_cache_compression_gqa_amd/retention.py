@@ -2,7 +2,8 @@
 
 DBTrimKV page ("Make Each Token Count: Towards Improving Long-Context Performance with KV Cache Eviction"),
 "Metodologia: Evicção Baseada em Retenção Global", sections 2-4. Thin wrappers over kvc_score(RETENTION),
-kvc_route(GLOBAL_TOPM) and kvc_compact_pages: torch tensors in, argument marshalling only.
+kvc_route(GLOBAL_TOPM), kvc_compact_pages and kvc_paged_decode_attn (decoding over the per-row page lists):
+torch tensors in, argument marshalling only.
 """
 from __future__ import annotations
 
@@ -97,3 +98,35 @@ def compact_pages(keep: torch.Tensor, page_table: torch.Tensor, k_pool: torch.Te
     abi.check(L.kvc_compact_pages(C.byref(a), ws.data_ptr(), need, _stream(stream)), "kvc_compact_pages")
     out.ws = ws
     return out
+
+
+class PagedDecoder:
+    """Decode attention over per-row page lists (kvc_paged_decode_attn): q [rows][G][128] against the rows' tokens
+    in (k_pool, v_pool) [n_pool][page][128]. The workspace is allocated once, for the given page bound."""
+
+    def __init__(self, n_rows: int, group: int, page: int, max_pages: int, kv_dtype: int, device="cuda"):
+        self.n_rows, self.group, self.page, self.max_pages, self.kv_dtype = n_rows, group, page, max_pages, kv_dtype
+        a = abi.KvcPagedDecodeArgs(q=1 << 12, k_pool=1 << 12, v_pool=1 << 12, page_list=1 << 12, lengths=1 << 12,
+                                   out=1 << 12, status=1 << 12, n_rows=n_rows, n_pool_pages=1,
+                                   page_stride=max_pages, group=group, page=page, max_pages=max_pages, head_dim=128,
+                                   kv_dtype=kv_dtype, reserved=0)
+        need = abi.lib().kvc_paged_decode_workspace(C.byref(a))
+        if need == 0:
+            raise abi.KvcError(abi.KVC_E_INVALID, "kvc_paged_decode_workspace")
+        self.ws = torch.empty(need, dtype=torch.uint8, device=device)
+        self.status = torch.zeros(1, dtype=torch.int32, device=device)
+
+    def __call__(self, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, page_list: torch.Tensor,
+                 lengths: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        n_pool, page, D = k_pool.shape
+        assert page == self.page and q.shape == (self.n_rows, self.group, D) and page_list.dim() == 2
+        assert page_list.shape[0] == self.n_rows and page_list.shape[1] >= self.max_pages
+        out = torch.empty((self.n_rows, self.group, D), dtype=torch.float32, device=q.device) if out is None else out
+        a = abi.KvcPagedDecodeArgs(q=q.data_ptr(), k_pool=k_pool.data_ptr(), v_pool=v_pool.data_ptr(),
+                                   page_list=page_list.data_ptr(), lengths=lengths.data_ptr(), out=out.data_ptr(),
+                                   status=self.status.data_ptr(), n_rows=self.n_rows, n_pool_pages=n_pool,
+                                   page_stride=page_list.stride(0), group=self.group, page=page,
+                                   max_pages=self.max_pages, head_dim=D, kv_dtype=self.kv_dtype, reserved=0)
+        abi.check(abi.lib().kvc_paged_decode_attn(C.byref(a), self.ws.data_ptr(), self.ws.numel(), _stream(stream)),
+                  "kvc_paged_decode_attn")
+        return out

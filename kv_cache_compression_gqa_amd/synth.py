@@ -232,3 +232,45 @@ def pool_table_bits(head_dim: int, seed: int, dtype: str = "bf16", pool_rows: in
         rng = unit_rng(seed, 1 << 22)
         _POOL_CACHE[key] = to_storage_bits(rng.standard_normal((pool_rows, head_dim)), dtype)
     return _POOL_CACHE[key]
+
+
+# ----------------------------------------------------------------------------------------------------------
+# Inputs of the decode over per-row page lists
+
+
+@dataclass
+class PagedInputs:
+    q: np.ndarray          # [rows][G][D] storage bits
+    k_pool: np.ndarray     # [n_pool][page][D] storage bits
+    v_pool: np.ndarray
+    page_list: np.ndarray  # [rows][max_pages] int32; entries past a row's page count are -7 (never read)
+    lengths: np.ndarray    # [rows] int32
+
+
+def make_paged(lengths, group: int, page: int, seed: int, dtype: str = "bf16", spare_pages: int = 3,
+               head_dim: int = 128, max_pages: int | None = None) -> PagedInputs:
+    """Rows of the given lengths, their pages at distinct random ids of a pool with ``spare_pages`` unlisted
+    pages. q ~ N(0, I); keys and values ~ N(0, 1), except that every row has four keys along its mean query
+    direction (logit about 6 for that mean), so the softmax has both flat and peaked parts."""
+    lengths = np.asarray(lengths, np.int64)
+    rows = lengths.size
+    n_pages = (lengths + page - 1) // page
+    mp = max(1, int(n_pages.max()) if rows else 1) if max_pages is None else max_pages
+    n_pool = int(n_pages.sum()) + spare_pages
+    rng = np.random.default_rng(seed)
+    ids = rng.permutation(n_pool).astype(np.int32)
+    page_list = np.full((rows, mp), -7, np.int32)
+    q = rng.standard_normal((rows, group, head_dim))
+    K = rng.standard_normal((n_pool, page, head_dim))
+    V = rng.standard_normal((n_pool, page, head_dim))
+    off = 0
+    for r in range(rows):
+        page_list[r, :n_pages[r]] = ids[off:off + n_pages[r]]
+        off += int(n_pages[r])
+        if lengths[r] > 0:
+            qm = q[r].mean(0)
+            key = 6.0 * np.sqrt(head_dim) * qm / (np.linalg.norm(qm) ** 2 + 1e-12)  # logit about 6 for the mean query
+            for i in rng.choice(int(lengths[r]), size=min(4, int(lengths[r])), replace=False):
+                K[page_list[r, i // page], i % page] = key
+    return PagedInputs(q=to_storage_bits(q, dtype), k_pool=to_storage_bits(K, dtype),
+                       v_pool=to_storage_bits(V, dtype), page_list=page_list, lengths=lengths.astype(np.int32))

