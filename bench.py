@@ -46,7 +46,8 @@ def parse():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB (counter calibration)")
     ap.add_argument("--workload", default="llama3_8b_layer_32k",
-                    choices=["llama3_8b_layer_32k", "batched_32l_b16", "criticalkv_64k", "dbtrim_128k"],
+                    choices=["llama3_8b_layer_32k", "batched_32l_b16", "criticalkv_64k", "dbtrim_128k",
+                             "dbtrim_paged_decode_128k"],
                     help="the decode step (default), the CriticalKV prefill selection or the DBTrimKV global budget")
     return ap.parse_args()
 
@@ -131,6 +132,8 @@ def main():
         return bench_dbtrim(args)
     if args.workload == "batched_32l_b16":
         return bench_batched(args)
+    if args.workload == "dbtrim_paged_decode_128k":
+        return bench_paged_decode(args)
     import torch
     sys.path.insert(0, ROOT)
     from kv_cache_compression_gqa_amd import configs, synth
@@ -425,6 +428,20 @@ def cpu_baseline_criticalkv(cfg, inp):
                       f"{cfg.d_model}): fp64 numpy oracle scores + two-stage selection; {el:.1f} s"}
 
 
+def _dbtrim_inputs(cfg):
+    """The DBTrimKV workload on the device: beta [rows][T] fp32, the source page table [rows][T/page] int32 and the
+    K/V pools [rows*T/page][page][128] bf16 (pool row r = seeded table row (r*40503+17) mod 65536)."""
+    import torch
+    from kv_cache_compression_gqa_amd import synth
+    L, H, T, page = cfg.layers, cfg.hkv, cfg.n_tokens, cfg.page
+    rows = L * H
+    beta = torch.from_numpy(synth.make_retention_beta(cfg).reshape(rows, T)).cuda()
+    pt = torch.from_numpy(synth.make_page_table(cfg).reshape(rows, T // page).astype(np.int32)).cuda()
+    n_src = rows * (T // page)
+    pools = [synth.device_pool(n_src, page, cfg.head_dim, sd, cfg.dtype) for sd in (cfg.seed * 7 + 1, cfg.seed * 7 + 2)]
+    return beta, pt, pools
+
+
 def bench_dbtrim(args):
     """DBTrimKV global budget: log-retention scores, global top-M and paged compaction over 32 layers x 8 KV heads
     x 131072 tokens (bf16 K/V pools of 2,097,152 16-token pages)."""
@@ -435,15 +452,7 @@ def bench_dbtrim(args):
     torch.cuda.set_device(0)
     L, H, T, page, D = cfg.layers, cfg.hkv, cfg.n_tokens, cfg.page, cfg.head_dim
     rows = L * H
-    beta = torch.from_numpy(synth.make_retention_beta(cfg).reshape(rows, T)).cuda()
-    pt = torch.from_numpy(synth.make_page_table(cfg).reshape(rows, T // page).astype(np.int32)).cuda()
-    n_src = rows * (T // page)
-    pools = []
-    for sd in (cfg.seed * 7 + 1, cfg.seed * 7 + 2):
-        tab = torch.from_numpy(synth.pool_table_bits(D, sd, cfg.dtype).view(np.int16)).cuda()
-        idx = (torch.arange(n_src * page, device="cuda", dtype=torch.int64) * 40503 + 17) % tab.shape[0]
-        pools.append(tab[idx].view(torch.bfloat16).view(n_src, page, D))
-        del idx
+    beta, pt, pools = _dbtrim_inputs(cfg)
     out_pages = cfg.keep // page + rows + 1
     print(f"inputs ready: {cfg.name}", file=sys.stderr, flush=True)
     st = {}
@@ -487,6 +496,91 @@ def bench_dbtrim(args):
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline_dbtrim(cfg)
     print(json.dumps(rec), flush=True)
+
+
+def bench_paged_decode(args):
+    """Decode attention over the per-row page lists that the DBTrimKV global budget leaves (32 layers x 8 KV heads,
+    10% of 131072 positions kept in all, 16-token pages): the budget is taken on the device (scores, top-M,
+    compaction), then one decode step (G = 4 query heads per row) attends over every row's kept tokens."""
+    import torch
+    sys.path.insert(0, ROOT)
+    from kv_cache_compression_gqa_amd import abi, configs, retention, synth
+    cfg = configs.DBTRIM_128K
+    torch.cuda.set_device(0)
+    L, H, T, page, D, G = cfg.layers, cfg.hkv, cfg.n_tokens, cfg.page, cfg.head_dim, 4
+    rows = L * H
+    beta, pt, pools = _dbtrim_inputs(cfg)
+    comp = retention.compact_pages(retention.global_topm(retention.retention_scores(beta, cfg.t), cfg.keep).keep, pt,
+                                   pools[0], pools[1], cfg.keep // page + rows + 1, abi.KVC_BF16)
+    torch.cuda.synchronize()
+    if int(comp.status.item()):
+        print("device status bits set by the compaction", file=sys.stderr)
+        sys.exit(1)
+    del beta, pools
+    torch.cuda.empty_cache()
+    lengths = comp.lengths
+    n_pages = comp.n_pages.to(torch.int64)
+    max_pages = int(n_pages.max().item())
+    col = torch.arange(max_pages, device="cuda", dtype=torch.int64)
+    # row r owns the fresh pages page_offset[r] .. page_offset[r] + n_pages[r] - 1, in order
+    pl = torch.where(col[None, :] < n_pages[:, None], comp.page_offset.to(torch.int64)[:, None] + col[None, :],
+                     torch.full_like(col[None, :], -7)).to(torch.int32).contiguous()
+    q = torch.from_numpy(synth.to_storage_bits(synth.unit_rng(cfg.seed, 1 << 25).standard_normal((rows, G, D)),
+                                               "bf16").view(np.int16)).cuda().view(torch.bfloat16)
+    kp = comp.k.view(-1, page, D)
+    vp = comp.v.view(-1, page, D)
+    dec = retention.PagedDecoder(rows, G, page, max_pages, abi.KVC_BF16)
+    out = torch.empty((rows, G, D), dtype=torch.float32, device="cuda")
+    print(f"inputs ready: {cfg.name} paged decode, {int(lengths.sum().item())} tokens", file=sys.stderr, flush=True)
+    K = max(1, args.steps)
+    wall, ms = _timed_calls(lambda: dec(q, kp, vp, pl, lengths, out=out), K, max(1, args.warmup))
+    torch.cuda.synchronize()
+    if int(dec.status.item()) or not bool(torch.isfinite(out).all()):
+        print("paged decode: device status bits set or non-finite output", file=sys.stderr)
+        sys.exit(1)
+    kept = int(lengths.sum().item())
+    launch_s = float(np.mean(ms)) * 1e-3
+    nbytes = kept * D * 2 * 2 + int(n_pages.sum().item()) * 4 + rows * 4 + rows * G * D * (2 + 4)
+    rec = {
+        "metric": "KV tokens attended/s (decode over the per-row page lists left by the DBTrimKV global budget)",
+        "value": kept * K / wall, "unit": "KV tokens/s", "n_gpus": 1, "steps": K, "warmup": max(1, args.warmup),
+        "ms_per_step": wall / K * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name + "_paged_decode", "rows": rows, "q_heads_per_row": G, "head_dim": D,
+                   "page": page, "kept_tokens": kept, "max_row_tokens": int(lengths.max().item())},
+        "roofline": {"bound": "hbm", "achieved": nbytes / launch_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": nbytes / launch_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "kvc_paged_decode_attn (paged_partial + paged_combine)",
+                     "avg_launch_us": launch_s * 1e6, "algorithmic_bytes_per_launch": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_paged(cfg, G)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline_paged(cfg, G, min_seconds=10.0):
+    """The oracle's paged decode on whole rows of the same length (the workload's mean kept count per row), row
+    after row, until at least ``min_seconds`` have passed."""
+    from kv_cache_compression_gqa_amd import synth
+    from oracle.fp import storage_to_f64
+    from oracle.paged import paged_gqa_decode
+    threads = _oracle_threads()
+    n = cfg.keep // (cfg.layers * cfg.hkv)
+    lists = synth.make_large_paged_lists([n] * 256, G, cfg.page, seed=91)
+    done, el = 0, 0.0
+    t0 = time.perf_counter()
+    while el < min_seconds:
+        r = done % 256
+        pos = np.arange(n)
+        ids = lists.page_list[r][pos // cfg.page].astype(np.int64) * cfg.page + pos % cfg.page
+        K = storage_to_f64(synth.pool_row_bits(ids, cfg.head_dim, lists.k_seed), "bf16").reshape(n, 1, -1)
+        V = storage_to_f64(synth.pool_row_bits(ids, cfg.head_dim, lists.v_seed), "bf16").reshape(n, 1, -1)
+        paged_gqa_decode(storage_to_f64(lists.q[r], "bf16"), K, V, pos, n, 1)
+        done += 1
+        el = time.perf_counter() - t0
+    return {"value": done * n / el, "unit": "KV tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} rows of {n} kept tokens (the mean row of the workload), G = {G}: fp64 numpy oracle "
+                      f"(page gather + decode attention); {el:.1f} s"}
 
 
 def cpu_baseline_dbtrim(cfg, layers=16):

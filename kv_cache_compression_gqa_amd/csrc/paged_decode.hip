@@ -15,7 +15,8 @@
 //     for all G heads; P reaches the lanes through a per-wave LDS tile. The four lanes that share a head_dim
 //     group are summed at the end of the slice.
 //   Every load of a chunk (K and V) is issued before its first use.
-// paged_combine: one workgroup per row merges the row's slices in a fixed order (bitwise reproducible).
+// paged_combine: one workgroup per row merges the row's slices in a fixed order (bitwise reproducible): the per-head
+// (max, sum) first, then the outputs with eight partial loads in flight per thread.
 #include <algorithm>
 
 #include "kvc_internal.h"
@@ -246,24 +247,74 @@ __global__ __launch_bounds__(kPWaves * kWave) void paged_partial(PagedParams p) 
   }
 }
 
-// One workgroup per row: thread i takes output elements i, i + 256, ... of the row's G*128; slices in order.
+// One workgroup per row. Wave w merges the (m, l) of heads w, w + 4 over the row's slices (lanes over slices in
+// a fixed order, then a wave reduction); thread t then owns float4 column c = t % C4 of the row's G*128 outputs
+// (C4 = 32 G) for slices pg, pg + PG, ... (PG = 256 / C4), eight loads in flight, and the PG sums are added in LDS
+// in order (bitwise reproducible).
 template <int G>
 __global__ __launch_bounds__(256) void paged_combine(PagedParams p) {
+  constexpr int C4 = G * kD / 4;
+  constexpr int PG = 256 / C4;
   const int row = blockIdx.x;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   const int len = min(max(p.lengths[row], 0), p.max_tokens);
   const int ns = min((len + kSliceTok - 1) / kSliceTok, p.slices);
-  for (int i = threadIdx.x; i < G * kD; i += 256) {
-    const int h = i / kD;
-    const float* ml = p.part_ml + size_t(row) * p.slices * G * 2;
-    float Mx = -INFINITY;
-    for (int s = 0; s < ns; ++s) Mx = fmaxf(Mx, ml[(s * G + h) * 2]);
-    float L = 0.0f, O = 0.0f;
-    for (int s = 0; s < ns; ++s) {
-      const float w = exp_diff(ml[(s * G + h) * 2], Mx);
-      L += w * ml[(s * G + h) * 2 + 1];
-      O += w * p.part_o[((size_t(row) * p.slices + s) * G + h) * kD + i % kD];
+  const float* ml = p.part_ml + size_t(row) * p.slices * G * 2;
+  const float4* po = reinterpret_cast<const float4*>(p.part_o + size_t(row) * p.slices * G * kD);
+  __shared__ float sM[G], sInvL[G];
+  __shared__ float4 red[256];
+  for (int h = wave; h < G; h += 4) {
+    float mr = -INFINITY, lr = 0.0f;
+    for (int s = lane; s < ns; s += kWave) {
+      const float2 v = *reinterpret_cast<const float2*>(ml + (s * G + h) * 2);
+      const float mn = fmaxf(mr, v.x);
+      lr = lr * exp_diff(mr, mn) + v.y * exp_diff(v.x, mn);
+      mr = mn;
     }
-    p.out[size_t(row) * G * kD + i] = L > 0.0f ? O / L : 0.0f;
+    const float mx = wave_max(mr);
+    const float sum = wave_sum(lr * exp_diff(mr, mx));
+    if (lane == 0) {
+      sM[h] = mx;
+      sInvL[h] = sum > 0.0f ? 1.0f / sum : 0.0f;
+    }
+  }
+  __syncthreads();
+  const int c = int(threadIdx.x) % C4, pg = int(threadIdx.x) / C4;
+  const int h = 4 * c / kD;
+  const float Mh = sM[h];
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int s0 = pg; s0 < ns; s0 += 8 * PG) {
+    float4 o8[8];
+    float m8[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int s = s0 + k * PG;
+      o8[k] = s < ns ? po[size_t(s) * C4 + c] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      m8[k] = s < ns ? ml[(s * G + h) * 2] : -INFINITY;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float w = exp_diff(m8[k], Mh);
+      acc.x += o8[k].x * w;
+      acc.y += o8[k].y * w;
+      acc.z += o8[k].z * w;
+      acc.w += o8[k].w * w;
+    }
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  if (int(threadIdx.x) < C4) {
+    float4 o = red[threadIdx.x];
+#pragma unroll
+    for (int g = 1; g < PG; ++g) {
+      const float4 v = red[g * C4 + threadIdx.x];
+      o.x += v.x;
+      o.y += v.y;
+      o.z += v.z;
+      o.w += v.w;
+    }
+    const float iL = sInvL[h];
+    reinterpret_cast<float4*>(p.out + size_t(row) * G * kD)[c] = make_float4(o.x * iL, o.y * iL, o.z * iL, o.w * iL);
   }
 }
 

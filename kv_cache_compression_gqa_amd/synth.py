@@ -274,3 +274,42 @@ def make_paged(lengths, group: int, page: int, seed: int, dtype: str = "bf16", s
                 K[page_list[r, i // page], i % page] = key
     return PagedInputs(q=to_storage_bits(q, dtype), k_pool=to_storage_bits(K, dtype),
                        v_pool=to_storage_bits(V, dtype), page_list=page_list, lengths=lengths.astype(np.int32))
+
+
+@dataclass
+class LargePagedLists:
+    q: np.ndarray          # [rows][G][D] storage bits, q ~ N(0, I)
+    page_list: np.ndarray  # [rows][max_pages] int32 (-7 past a row's page count)
+    lengths: np.ndarray    # [rows] int32
+    n_pool: int            # pool pages; pool row r = page * page_size + slot takes pool_row_bits([r], ...)
+    k_seed: int
+    v_seed: int
+
+
+def make_large_paged_lists(lengths, group: int, page: int, seed: int, dtype: str = "bf16", spare_pages: int = 5,
+                           head_dim: int = 128) -> LargePagedLists:
+    """Per-row page lists for a pool too large to draw on the host: the rows' pages are distinct ids of a seeded
+    permutation of the pool; the pool's K and V rows are defined by ``pool_row_bits`` (seeds ``k_seed`` and
+    ``v_seed``), so a device gather of ``pool_table_bits`` builds the pools and the host regenerates any row."""
+    lengths = np.asarray(lengths, np.int64)
+    n_pages = (lengths + page - 1) // page
+    n_pool = int(n_pages.sum()) + spare_pages
+    rng = unit_rng(seed, 1 << 24)
+    ids = rng.permutation(n_pool).astype(np.int32)
+    page_list = np.full((lengths.size, max(1, int(n_pages.max()))), -7, np.int32)
+    off = np.concatenate([[0], np.cumsum(n_pages)])
+    for r in range(lengths.size):
+        page_list[r, :n_pages[r]] = ids[off[r]:off[r + 1]]
+    q = to_storage_bits(rng.standard_normal((lengths.size, group, head_dim)), dtype)
+    return LargePagedLists(q=q, page_list=page_list, lengths=lengths.astype(np.int32), n_pool=n_pool,
+                           k_seed=seed * 7 + 3, v_seed=seed * 7 + 4)
+
+
+def device_pool(n_pages: int, page: int, head_dim: int, seed: int, dtype: str = "bf16", device="cuda"):
+    """The pool [n_pages][page][head_dim] (storage dtype) whose row r is pool_row_bits([r], ...): a device gather
+    of the seeded table (an index permutation only)."""
+    tab = torch.from_numpy(pool_table_bits(head_dim, seed, dtype).view(np.int16)).to(device)
+    idx = (torch.arange(n_pages * page, device=device, dtype=torch.int64) * 40503 + 17) % tab.shape[0]
+    out = tab[idx].view(torch.bfloat16 if dtype == "bf16" else torch.float16).view(n_pages, page, head_dim)
+    del idx
+    return out

@@ -92,3 +92,41 @@ def test_paged_decode_is_bitwise_reproducible(gpu_lib):
     a, _ = _run(inp, 8, 16, "bf16")
     b, _ = _run(inp, 8, 16, "bf16")
     assert np.array_equal(a, b)
+
+
+def test_paged_decode_full_retention_shape(gpu_lib):
+    """The DBTrimKV shape after its global budget: 32 layers x 8 KV heads = 256 rows, G = 4, 16-token pages, about
+    13107 kept tokens per row (a seeded length mix in [11000, 15000]) plus edge rows (empty, one token, one page,
+    one past a page, a row that keeps all 131072 positions); the pools (about 1.8 GB each) are built on the device
+    from the seeded table. Every row is checked for finiteness; sampled rows against the oracle."""
+    from kv_cache_compression_gqa_amd import configs
+    cfg = configs.DBTRIM_128K
+    rows, G, page = cfg.layers * cfg.hkv, 4, cfg.page
+    rng = np.random.default_rng(77)
+    lengths = rng.integers(11000, 15001, size=rows)
+    lengths[:5] = [0, 1, page, page + 1, cfg.n_tokens]
+    lists = synth.make_large_paged_lists(lengths, G, page, seed=78)
+    log(f"case: paged decode full shape, {rows} rows, {int(lengths.sum())} tokens, pool {lists.n_pool} pages")
+    kp = synth.device_pool(lists.n_pool, page, 128, lists.k_seed)
+    vp = synth.device_pool(lists.n_pool, page, 128, lists.v_seed)
+    dec = PagedDecoder(rows, G, page, lists.page_list.shape[1], abi.KVC_BF16)
+    out = dec(_dev(lists.q, "bf16"), kp, vp, torch.from_numpy(lists.page_list).cuda(),
+              torch.from_numpy(lists.lengths).cuda())
+    torch.cuda.synchronize()
+    assert int(dec.status.item()) == 0
+    out = out.cpu().numpy()
+    del kp, vp
+    torch.cuda.empty_cache()
+    assert np.isfinite(out).all() and not out[0].any()
+    for r in [1, 2, 3, 4, 5, 77, 200, rows - 1]:
+        n = int(lengths[r])
+        pos = np.arange(n)
+        ids = lists.page_list[r][pos // page].astype(np.int64) * page + pos % page
+        K = storage_to_f64(synth.pool_row_bits(ids, 128, lists.k_seed), "bf16")
+        V = storage_to_f64(synth.pool_row_bits(ids, 128, lists.v_seed), "bf16")
+        ref = paged_gqa_decode(storage_to_f64(lists.q[r], "bf16"), K.reshape(n, 1, 128), V.reshape(n, 1, 128),
+                               np.arange(n), n, 1)
+        for h in range(G):
+            err = np.abs(out[r, h] - ref[h]).max()
+            lim = RTOL * np.abs(ref[h]).max()
+            assert err <= lim, f"row {r} (length {n}) head {h}: max err {err} > {lim}"
