@@ -62,21 +62,22 @@ def step_bytes_and_tokens(sess, W=32, D=128):
     return U * per_unit, positions
 
 
-def kernel_source_sha():
+def kernel_source_sha(files=("decode_attn.hip", "kvc_internal.h")):
     h = hashlib.sha256()
-    for f in ("decode_attn.hip", "kvc_internal.h"):
+    for f in files:
         h.update(open(os.path.join(ROOT, "kv_cache_compression_gqa_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(launch_bytes):
-    """HBM traffic per launch from the committed rocprofv3 counter summary, if it was taken on this kernel."""
-    path = os.path.join(ROOT, "profiles", "decode_attn_llama3_8b_layer_32k_traffic.json")
+def traffic_from_profile(name="decode_attn_llama3_8b_layer_32k", files=("decode_attn.hip", "kvc_internal.h")):
+    """HBM bytes per launch from the committed rocprofv3 counter summary profiles/<name>_traffic.json, if it was
+    taken on the current kernel source (its hash is stored with it); None otherwise."""
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
     try:
         rec = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_sha") != kernel_source_sha():
+    if rec.get("kernel_sha") != kernel_source_sha(files):
         return None
     return rec.get("bytes_per_launch")
 
@@ -120,6 +121,17 @@ def cpu_baseline(cfg, min_seconds=10.0, max_steps=160):
                       f"of one 32K layer after an untimed full-cache phase; fp64 numpy oracle; {elapsed:.1f} s"}
 
 
+def _calibration_copy(mib):
+    """One plain device-to-device copy of ``mib`` MiB (the reference kernel for scaling the HBM counters)."""
+    import torch
+    if mib > 0:
+        src = torch.ones(mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -156,17 +168,31 @@ def main():
     torch.cuda.synchronize()
     print(f"replicas ready: {R} x {cfg.name}", file=sys.stderr, flush=True)
 
-    # warm-up: every replica through its full-cache phase and first routing event
-    for i in range(args.warmup):
+    # warm-up: every replica through its full-cache phase and first routing event. Those first route_every steps
+    # of every replica (full-cache attention, then the first routing event with its quantisation and promotions)
+    # are captured in one HIP graph and timed: the full-cache phase of the schedule
+    n_full = cfg.route_every * R
+    full_plan = [step_bytes_and_tokens(sessions[i % R]) for i in range(R)]
+    full_ms = None
+    if not args.eager:
+        fgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(fgraph):
+            for i in range(n_full):
+                sessions[i % R].step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        fgraph.replay()
+        torch.cuda.synchronize()
+        full_ms = (time.perf_counter() - t0) / n_full * 1e3
+        del fgraph
+    else:
+        for i in range(n_full):
+            sessions[i % R].step()
+    for i in range(n_full, args.warmup):
         sessions[i % R].step()
     torch.cuda.synchronize()
     print(f"warm-up done ({args.warmup} steps)", file=sys.stderr, flush=True)
-    if args.copy_mib > 0:
-        src = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    _calibration_copy(args.copy_mib)
 
     K = args.steps
     plan = []  # (bytes, positions) per timed step, from the host-side counts at the time the step is issued
@@ -238,7 +264,7 @@ def main():
     avg_kern_s = float(np.mean(kern_ms)) * 1e-3
     avg_bytes = sum(b for b, _ in kern_plan) / K
     achieved = avg_bytes / avg_kern_s / 1e9
-    traffic = traffic_from_profile(avg_bytes)
+    traffic = traffic_from_profile()
     rec = {
         "metric": "KV tokens scored+routed+attended/s per decode step; % of HBM roofline",
         "value": total_pos / wall,
@@ -248,7 +274,11 @@ def main():
         "config": {"workload": cfg.name, "batch": 1, "q_heads": cfg.hq, "kv_heads": cfg.hkv, "head_dim": 128,
                    "context": cfg.context, "window": cfg.window, "tiers": "20% full / 30% int2 / 50% evicted",
                    "route_every": cfg.route_every, "phase": "routed steady state", "replicas": R,
-                   "launch": "eager" if graph is None else "hip graph"},
+                   "launch": "eager" if graph is None else "hip graph",
+                   "full_cache_phase_ms_per_step": full_ms,
+                   "full_cache_phase_bytes_per_step": full_plan[0][0],
+                   "schedule_64_steps_ms_per_step": None if full_ms is None else
+                   (cfg.route_every * full_ms + (cfg.steps - cfg.route_every) * wall / K * 1e3) / cfg.steps},
         "hbm_roofline_frac_step": total_bytes / wall / (HBM_PEAK_GBS * 1e9),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
@@ -532,6 +562,7 @@ def bench_paged_decode(args):
     dec = retention.PagedDecoder(rows, G, page, max_pages, abi.KVC_BF16)
     out = torch.empty((rows, G, D), dtype=torch.float32, device="cuda")
     print(f"inputs ready: {cfg.name} paged decode, {int(lengths.sum().item())} tokens", file=sys.stderr, flush=True)
+    _calibration_copy(args.copy_mib)
     K = max(1, args.steps)
     wall, ms = _timed_calls(lambda: dec(q, kp, vp, pl, lengths, out=out), K, max(1, args.warmup))
     torch.cuda.synchronize()
@@ -549,7 +580,8 @@ def bench_paged_decode(args):
         "config": {"workload": cfg.name + "_paged_decode", "rows": rows, "q_heads_per_row": G, "head_dim": D,
                    "page": page, "kept_tokens": kept, "max_row_tokens": int(lengths.max().item())},
         "roofline": {"bound": "hbm", "achieved": nbytes / launch_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": nbytes / launch_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "frac": nbytes / launch_s / 1e9 / HBM_PEAK_GBS,
+                     "traffic": traffic_from_profile("dbtrim_paged_decode_128k", ("paged_decode.hip", "kvc_internal.h")),
                      "kernel": "kvc_paged_decode_attn (paged_partial + paged_combine)",
                      "avg_launch_us": launch_s * 1e6, "algorithmic_bytes_per_launch": nbytes},
     }
