@@ -15,6 +15,9 @@ Readings where the page is silent (each is listed with its reason in the design 
     probability in the window), starting at 0 at the first decode step;
   * order inside a step: append (k_t, v_t) -> attend over the current tiers -> accumulate -> route when
     t % R == 0 (the new tiers serve from step t+1);
+  * "materialises attention during routing events" (Implementação) is the alternative schedule: the window mass
+    is added to the cumulative score only at the steps that end with a routing event (step(accumulate=False) in
+    between); scoring every step is the default;
   * routing ranks the resident windows by (score desc, window asc): ranks [0, b_full) FULL, the next b_int2
     INT2, the rest EVICTED for good;
   * the partial last window and every decode-time token form an unrouted tail that is always attended;
@@ -98,7 +101,9 @@ class QEvictUnit:
         return np.concatenate(Ks), np.concatenate(Vs), np.concatenate(kw)
 
     # -- one decode step -------------------------------------------------------------------------------------
-    def step(self, q_bits: np.ndarray, k_new=None, v_new=None) -> StepResult:
+    def step(self, q_bits: np.ndarray, k_new=None, v_new=None, accumulate: bool = True) -> StepResult:
+        """One decode step. ``accumulate`` = False leaves the cumulative scores alone (the page's cheaper schedule
+        scores only at routing events and decodes plainly in between)."""
         if k_new is not None:
             self.tail_k.append(np.array(k_new, np.uint16))
             self.tail_v.append(np.array(v_new, np.uint16))
@@ -106,7 +111,8 @@ class QEvictUnit:
         q = storage_to_f64(q_bits, self.dtype)
         s, p, o = gqa_decode(q, K, V)
         mass = window_mass(p, kw, self.n_windows)
-        self.cum += mass
+        if accumulate:
+            self.cum += mass
         self.t += 1
         tail_mass = float(p[:, kw < 0].sum() / p.shape[0])
         return StepResult(logits=s, p=p, o=o, mass=mass, key_window=kw, tail_mass=tail_mass)
