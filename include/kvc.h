@@ -327,6 +327,41 @@ typedef struct kvc_paged_decode_args {
   int32_t reserved;
 } kvc_paged_decode_args;
 
+/* kvc_route_diagnostics: per-unit diagnostics of the routing dynamics and of the output error of the compressed
+ * cache. QEvict page, "Principais Contribuições", item 1: future missed mass (the share of later attention on
+ * states a policy has already dropped), global latent importance reactivation (windows that left the active set
+ * coming back) and selection churn (instability of the assignment between consecutive routing steps); CriticalKV
+ * page, "Framework Teórico": the perturbation L = ||o - o^||_1 between the outputs over the full cache and over
+ * the kept subset. The active set is the FULL tier. For unit u, over its windows w < n_windows[u]:
+ *   counts[u][0] = #{w : tier_prev[w] != tier[w]}                 (churn = counts[0] / n_windows)
+ *   counts[u][1] = #{w : tier[w] == FULL and tier_prev[w] != FULL} (re-entries into the active set)
+ *   counts[u][2] = #{w : tier[w] == FULL}
+ *   counts[u][3] = #{w : tier[w] != EVICTED}
+ *   values[u][0] = sum of mass_full[w] over w with tier[w] == EVICTED   (future missed mass; 0 if mass_full NULL)
+ *   values[u][1 + h] = sum_d |o_full[u][h][d] - o[u][h][d]|             (0 if o_full or o is NULL)
+ *   tier_prev  [U][n_windows_max] int8 tiers before a routing event, or NULL (taken equal to tier).
+ *   tier       [U][n_windows_max] int8 tiers after it (or the tiers serving a step).
+ *   n_windows  [U] int32 (clamped to [0, n_windows_max]).
+ *   mass_full  [U][n_windows_max] float: the window mass of the same step under attention over the full,
+ *              uncompressed cache (kvc_decode_attn on a cache whose windows are all FULL), or NULL.
+ *   o_full, o  [U][group][128] float: outputs of the step over the full and the compressed cache, or NULL.
+ *   counts     [U][4] int32 out; values [U][1 + group] float out (sums in a fixed order: reproducible).
+ *   group in {1, 2, 4, 8}; head_dim 128; 1 <= n_units <= 2^20; 1 <= n_windows_max <= 2^20. No workspace. */
+typedef struct kvc_diag_args {
+  const int8_t* tier_prev;
+  const int8_t* tier;
+  const int32_t* n_windows;
+  const float* mass_full;
+  const float* o_full;
+  const float* o;
+  int32_t* counts;
+  float* values;
+  int32_t n_units;
+  int32_t n_windows_max;
+  int32_t group;
+  int32_t head_dim;
+} kvc_diag_args;
+
 /* kvc_score(KVC_SCORE_WINDOWS): the scoring half of a decode step — the same kernels as kvc_decode_attn with
  * out = NULL: probabilities, window mass and the cumulative score update over the mixed cache. */
 typedef struct kvc_window_score_args {
@@ -377,6 +412,8 @@ int kvc_compact_pages(const kvc_compact_args* args, void* workspace, size_t work
 size_t kvc_paged_decode_workspace(const kvc_paged_decode_args* args);
 int kvc_paged_decode_attn(const kvc_paged_decode_args* args, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
+
+int kvc_route_diagnostics(const kvc_diag_args* args, hipStream_t stream);
 
 /* Reads *cache->status into *host_status (synchronises the stream) and, if clear != 0, zeroes it. */
 int kvc_read_device_status(const kvc_cache* cache, int32_t* host_status, int32_t clear, hipStream_t stream);

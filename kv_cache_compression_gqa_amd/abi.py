@@ -87,6 +87,12 @@ class KvcPagedDecodeArgs(C.Structure):
                 ("kv_dtype", C.c_int32), ("reserved", C.c_int32)]
 
 
+class KvcDiagArgs(C.Structure):
+    _fields_ = [("tier_prev", P), ("tier", P), ("n_windows", P), ("mass_full", P), ("o_full", P), ("o", P),
+                ("counts", P), ("values", P), ("n_units", C.c_int32), ("n_windows_max", C.c_int32),
+                ("group", C.c_int32), ("head_dim", C.c_int32)]
+
+
 # name -> (restype, argtypes); every symbol include/kvc.h declares
 SIGNATURES = {
     "kvc_abi_version": (C.c_int, []),
@@ -104,6 +110,7 @@ SIGNATURES = {
     "kvc_compact_pages": (C.c_int, [C.POINTER(KvcCompactArgs), P, C.c_size_t, P]),
     "kvc_paged_decode_workspace": (C.c_size_t, [C.POINTER(KvcPagedDecodeArgs)]),
     "kvc_paged_decode_attn": (C.c_int, [C.POINTER(KvcPagedDecodeArgs), P, C.c_size_t, P]),
+    "kvc_route_diagnostics": (C.c_int, [C.POINTER(KvcDiagArgs), P]),
 }
 
 

@@ -310,6 +310,22 @@ int kvc_paged_decode_attn(const kvc_paged_decode_args* args, void* workspace, si
   return kvc::launch_paged_decode(*args, workspace, stream) == hipSuccess ? KVC_OK : KVC_E_HIP;
 }
 
+int kvc_route_diagnostics(const kvc_diag_args* args, hipStream_t stream) {
+  if (args == nullptr) return KVC_E_INVALID;
+  const kvc_diag_args& a = *args;
+  if (a.head_dim != kvc::kD) return KVC_E_UNSUPPORTED;
+  if (!(a.group == 1 || a.group == 2 || a.group == 4 || a.group == 8)) return KVC_E_UNSUPPORTED;
+  if (a.n_units < 1 || a.n_units > (1 << 20) || a.n_windows_max < 1 || a.n_windows_max > (1 << 20)) {
+    return KVC_E_INVALID;
+  }
+  if (a.tier == nullptr || a.n_windows == nullptr || a.counts == nullptr || a.values == nullptr) return KVC_E_INVALID;
+  const void* need4[] = {a.n_windows, a.mass_full, a.o_full, a.o, a.counts, a.values};
+  for (const void* p : need4) {
+    if (p != nullptr && !aligned(p, 4)) return KVC_E_INVALID;
+  }
+  return kvc::launch_diagnostics(a, stream) == hipSuccess ? KVC_OK : KVC_E_HIP;
+}
+
 int kvc_read_device_status(const kvc_cache* cache, int32_t* host_status, int32_t clear, hipStream_t stream) {
   if (cache == nullptr || cache->status == nullptr || host_status == nullptr) return KVC_E_INVALID;
   if (hipMemcpyAsync(host_status, cache->status, sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess) {

@@ -36,7 +36,13 @@ class DecodeSession:
     draw while every unit keeps memory and state of its own."""
 
     def __init__(self, inp: DecodeInputs, device="cuda", tail_max: int | None = None, steps: int | None = None,
-                 budgets=None, unit_map=None):
+                 budgets=None, unit_map=None, score_schedule: str = "every"):
+        """``score_schedule``: "every" adds every step's window mass to the cumulative score; "event" adds it only
+        at the steps that end with a routing event (attention is then materialised for scoring only when the
+        routing needs it, and the steps in between are plain decode steps)."""
+        if score_schedule not in ("every", "event"):
+            raise ValueError(score_schedule)
+        self.score_schedule = score_schedule
         cfg = inp.cfg
         self.cfg = cfg
         self.inp = inp
@@ -167,7 +173,9 @@ class DecodeSession:
         """Decode step t+1 using the pre-generated inputs of that step; routes when due. ``events`` = (before,
         after) torch events recorded on the stream around the decode launch."""
         ti = self.t
-        args = self.decode_args(ti, probs=probs, mass=mass, append=append)
+        R = self.cfg.route_every
+        accumulate = self.score_schedule == "every" or (R > 0 and (ti + 1) % R == 0)
+        args = self.decode_args(ti, probs=probs, mass=mass, append=append, accumulate=accumulate)
         ws = self.workspace(args)
         L = abi.lib()
         if events is not None:
@@ -210,3 +218,18 @@ class DecodeSession:
         abi.check(abi.lib().kvc_read_device_status(C.byref(self._cache), C.byref(st), 1 if clear else 0,
                                                    abi.stream_handle(stream)), "kvc_read_device_status")
         return int(st.value)
+
+
+def route_diagnostics(tier: torch.Tensor, n_windows: torch.Tensor, group: int, tier_prev=None, mass_full=None,
+                      o_full=None, o=None, stream=None):
+    """kvc_route_diagnostics: per-unit (changed, entered FULL, FULL, resident) window counts and (future missed
+    mass, L1 output perturbation per query head). Returns (counts [U][4] int32, values [U][1 + G] float32) on the
+    device."""
+    U, NW = tier.shape
+    counts = torch.empty((U, 4), dtype=torch.int32, device=tier.device)
+    values = torch.empty((U, 1 + group), dtype=torch.float32, device=tier.device)
+    a = abi.KvcDiagArgs(tier_prev=abi.ptr(tier_prev), tier=abi.ptr(tier), n_windows=abi.ptr(n_windows),
+                        mass_full=abi.ptr(mass_full), o_full=abi.ptr(o_full), o=abi.ptr(o), counts=abi.ptr(counts),
+                        values=abi.ptr(values), n_units=U, n_windows_max=NW, group=group, head_dim=128)
+    abi.check(abi.lib().kvc_route_diagnostics(C.byref(a), abi.stream_handle(stream)), "kvc_route_diagnostics")
+    return counts, values

@@ -92,15 +92,16 @@ def compare_route(sess: DecodeSession, oracles, gpu_cum):
 
 
 def run_decode_parity(cfg, units=None, steps=None, check_units=None, check_steps=None, probs=True, log=print,
-                      inp=None, unit_map=None):
+                      inp=None, unit_map=None, score_schedule="every"):
     """Run ``steps`` decode steps (routing on the workload's cadence) on the GPU for every unit, and on the oracle
     for the units in ``check_units`` (default all; units are independent, so a sample of them is followed exactly).
+    ``score_schedule`` "event" adds the window mass to the cumulative score only at routing-event steps.
     Outputs are compared at every step in ``check_steps`` (default all); routing at every event. ``inp`` and
     ``unit_map`` (optional) give held inputs and the held unit each session unit starts from."""
     if inp is None:
         inp = synth.make_decode(cfg, units=units, steps=steps)
     S = inp.q.shape[0]
-    sess = DecodeSession(inp, unit_map=unit_map)
+    sess = DecodeSession(inp, unit_map=unit_map, score_schedule=score_schedule)
     U = sess.U
     umap = sess.unit_map
     oracles = make_oracles(inp, check_units, unit_map)
@@ -117,7 +118,8 @@ def run_decode_parity(cfg, units=None, steps=None, check_units=None, check_steps
         cum_h = sess.cum.cpu().numpy()
         for j, o in oracles.items():
             b = int(umap[j])
-            r = o.step(inp.q[t, b], inp.k_new[t, b], inp.v_new[t, b])
+            acc = score_schedule == "every" or (cfg.route_every > 0 and (t + 1) % cfg.route_every == 0)
+            r = o.step(inp.q[t, b], inp.k_new[t, b], inp.v_new[t, b], accumulate=acc)
             if t not in check_steps:
                 continue
             nw = oracles[j].n_windows

@@ -177,3 +177,24 @@ def test_criticalkv_and_two_stage_validation_rejects_before_launch():
     assert ts(budget1=11) == abi.KVC_E_BUDGET
     assert ts(n=70000, budget=10) == abi.KVC_E_UNSUPPORTED
     assert ts(budget=0, budget1=0) == abi.KVC_OK  # nothing to select: no launch
+
+
+def test_route_diagnostics_validation_rejects_before_launch():
+    L = abi.lib()
+    assert C.sizeof(abi.KvcDiagArgs) == 8 * 8 + 4 * 4
+
+    def args(**over):
+        kw = dict(tier_prev=FAKE, tier=FAKE, n_windows=FAKE, mass_full=FAKE, o_full=FAKE, o=FAKE, counts=FAKE,
+                  values=FAKE, n_units=4, n_windows_max=32, group=4, head_dim=128)
+        kw.update(over)
+        return abi.KvcDiagArgs(**kw)
+
+    assert L.kvc_route_diagnostics(None, None) == abi.KVC_E_INVALID
+    assert L.kvc_route_diagnostics(C.byref(args(head_dim=64)), None) == abi.KVC_E_UNSUPPORTED
+    assert L.kvc_route_diagnostics(C.byref(args(group=3)), None) == abi.KVC_E_UNSUPPORTED
+    assert L.kvc_route_diagnostics(C.byref(args(n_units=0)), None) == abi.KVC_E_INVALID
+    assert L.kvc_route_diagnostics(C.byref(args(n_windows_max=0)), None) == abi.KVC_E_INVALID
+    assert L.kvc_route_diagnostics(C.byref(args(tier=None)), None) == abi.KVC_E_INVALID
+    assert L.kvc_route_diagnostics(C.byref(args(counts=None)), None) == abi.KVC_E_INVALID
+    assert L.kvc_route_diagnostics(C.byref(args(values=None)), None) == abi.KVC_E_INVALID
+    assert L.kvc_route_diagnostics(C.byref(args(mass_full=FAKE + 2)), None) == abi.KVC_E_INVALID

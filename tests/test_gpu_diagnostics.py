@@ -1,0 +1,127 @@
+"""GPU parity of the routing diagnostics (kvc_route_diagnostics) and of the event-only scoring schedule against
+the oracle (needs an MI355X).
+
+Tolerances: window counts bit-exact (on the same tiers); future missed mass |g - r| <= 2e-3 |r| + 1e-9; the L1
+output perturbation per head within the bound that the output tolerance gives it: each of the 2 x 128 output
+elements it sums may be off by 2e-3 max|o| of its row, so |g - r| <= 2e-3 |r| + 2 * 128 * 2e-3 * max|o|.
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_compression_gqa_amd import configs, synth
+from kv_cache_compression_gqa_amd.session import DecodeSession, route_diagnostics
+from oracle import attention, diagnostics, qevict
+from oracle.select import EVICTED, FULL, INT2
+from tests.decode_parity import compare_route, make_oracles, run_decode_parity
+
+pytestmark = pytest.mark.gpu
+RTOL = 2e-3
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_event_only_schedule_matches_oracle(gpu_lib, dtype):
+    log(f"case: event-only scoring schedule, tiny workload, {dtype}")
+    cfg = dataclasses.replace(configs.TINY, dtype=dtype)
+    run_decode_parity(cfg, steps=12, score_schedule="event", log=log)
+
+
+def test_event_only_schedule_2k_context(gpu_lib):
+    log("case: event-only scoring schedule, 8 units at 2048 tokens, routing every 4 steps")
+    cfg = dataclasses.replace(configs.LLAMA3_8B_LAYER_32K, name="ctx2k", context=2048, steps=12, route_every=4)
+    run_decode_parity(cfg, score_schedule="event", probs=False, log=log)
+
+
+def test_diagnostics_kernel_on_synthetic_tiers(gpu_lib):
+    """Random tiers and masses over 5000 windows, G = 8, plus a unit with no windows and one whose count exceeds
+    the capacity (clamped), against the oracle's definitions; NULL inputs give zeros."""
+    log("case: diagnostics kernel, synthetic tiers, U=4 NW=5000 G=8")
+    rng = np.random.default_rng(31)
+    U, NW, G = 4, 5000, 8
+    prev = rng.integers(0, 3, size=(U, NW)).astype(np.int8)
+    now = prev.copy()
+    flip = rng.random((U, NW)) < 0.3
+    now[flip] = rng.integers(0, 3, size=int(flip.sum())).astype(np.int8)
+    nwin = np.array([NW, 0, 4097, NW + 100], np.int32)
+    mass = rng.random((U, NW)).astype(np.float32) / NW
+    of = rng.standard_normal((U, G, 128)).astype(np.float32)
+    oc = (of + 0.01 * rng.standard_normal((U, G, 128))).astype(np.float32)
+    d = lambda a: torch.from_numpy(a).cuda()  # noqa: E731
+    counts, values = route_diagnostics(d(now), d(nwin), G, tier_prev=d(prev), mass_full=d(mass), o_full=d(of),
+                                       o=d(oc))
+    torch.cuda.synchronize()
+    counts, values = counts.cpu().numpy(), values.cpu().numpy()
+    for u in range(U):
+        n = min(max(int(nwin[u]), 0), NW)
+        assert tuple(counts[u]) == diagnostics.route_counts(prev[u, :n], now[u, :n]), f"unit {u}"
+        ref = diagnostics.future_missed_mass(mass[u, :n].astype(np.float64), now[u, :n])
+        assert abs(values[u, 0] - ref) <= RTOL * abs(ref) + 1e-9
+        L = diagnostics.perturbation_l1(of[u], oc[u])
+        assert np.all(np.abs(values[u, 1:] - L) <= RTOL * np.abs(L) + 1e-6)
+    counts, values = route_diagnostics(d(now), d(nwin), G)
+    torch.cuda.synchronize()
+    counts, values = counts.cpu().numpy(), values.cpu().numpy()
+    assert np.all(counts[:, :2] == 0) and np.all(values == 0)
+    assert tuple(counts[0, 2:]) == diagnostics.route_counts(now[0], now[0])[2:]
+
+
+def test_route_diagnostics_match_oracle(gpu_lib):
+    """A compressed run next to a full-cache run of the same inputs (all windows FULL, never routed): per step the
+    future missed mass and the output perturbation, per routing event the window counts, against the oracle (its
+    router fed the GPU's scores, its full-cache attention over the original windows)."""
+    cfg = dataclasses.replace(configs.LLAMA3_8B_LAYER_32K, name="ctx2k", context=2048, steps=12, route_every=4)
+    log(f"case: route diagnostics, {cfg.name}, 8 units, 12 steps, routing every 4")
+    inp = synth.make_decode(cfg)
+    sess = DecodeSession(inp)
+    nw_all = inp.n_windows.astype(np.int32)
+    shadow = DecodeSession(inp, budgets=(nw_all, np.zeros_like(nw_all)))
+    oracles = make_oracles(inp)
+    U, NW, G = sess.U, sess.NW, sess.G
+    mf = torch.zeros((U, NW), dtype=torch.float32, device="cuda")
+    tier_prev = torch.empty_like(sess.tier)
+    tails = {j: ([], []) for j in oracles}
+    saw_eviction = False
+    for t in range(cfg.steps):
+        sess.step(route=False)
+        shadow.step(mass=mf, route=False)
+        counts, values = route_diagnostics(sess.tier, sess.n_windows, G, mass_full=mf, o_full=shadow.out, o=sess.out)
+        torch.cuda.synchronize()
+        counts, values = counts.cpu().numpy(), values.cpu().numpy()
+        for j, o in oracles.items():
+            r = o.step(inp.q[t, j], inp.k_new[t, j], inp.v_new[t, j])
+            tails[j][0].append(inp.k_new[t, j])
+            tails[j][1].append(inp.v_new[t, j])
+            nw, t0 = o.n_windows, int(inp.tail0[j])
+            _, p, o_full = qevict.full_cache_attention(
+                inp.k_win[j, :nw], inp.v_win[j, :nw], np.concatenate([inp.k_tail0[j, :t0], np.stack(tails[j][0])]),
+                np.concatenate([inp.v_tail0[j, :t0], np.stack(tails[j][1])]), inp.q[t, j], cfg.dtype)
+            kw = np.concatenate([np.repeat(np.arange(nw), o.W), np.full(p.shape[1] - nw * o.W, -1)])
+            fmm = diagnostics.future_missed_mass(attention.window_mass(p, kw, nw), o.tier)
+            saw_eviction |= bool(np.any(o.tier == EVICTED))
+            assert abs(values[j, 0] - fmm) <= RTOL * abs(fmm) + 1e-9, f"FMM step {t} unit {j}: {values[j, 0]} {fmm}"
+            L = diagnostics.perturbation_l1(o_full, r.o)
+            lim = RTOL * np.abs(L) + 2 * 128 * RTOL * np.maximum(np.abs(o_full).max(1), np.abs(r.o).max(1))
+            assert np.all(np.abs(values[j, 1:] - L) <= lim), f"L step {t} unit {j}: {values[j, 1:]} {L}"
+            assert tuple(counts[j]) == diagnostics.route_counts(o.tier, o.tier)
+        if (t + 1) % cfg.route_every == 0:
+            tier_prev.copy_(sess.tier)
+            before = {j: o.tier.copy() for j, o in oracles.items()}
+            gpu_cum = sess.cum.cpu().numpy().astype(np.float64)
+            sess.route()
+            counts, _ = route_diagnostics(sess.tier, sess.n_windows, G, tier_prev=tier_prev)
+            torch.cuda.synchronize()
+            compare_route(sess, oracles, gpu_cum)
+            counts = counts.cpu().numpy()
+            for j, o in oracles.items():
+                assert tuple(counts[j]) == diagnostics.route_counts(before[j], o.tier), f"counts event {t} unit {j}"
+            log(f"step {t + 1}: routed; counts match")
+    assert saw_eviction
+    assert sess.device_status() == 0 and shadow.device_status() == 0
