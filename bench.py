@@ -47,7 +47,7 @@ def parse():
                     help="also run one plain device-to-device copy of this many MiB (counter calibration)")
     ap.add_argument("--workload", default="llama3_8b_layer_32k",
                     choices=["llama3_8b_layer_32k", "batched_32l_b16", "criticalkv_64k", "dbtrim_128k",
-                             "dbtrim_paged_decode_128k"],
+                             "dbtrim_paged_decode_128k", "qevict_diagnostics_32k"],
                     help="the decode step (default), the CriticalKV prefill selection or the DBTrimKV global budget")
     return ap.parse_args()
 
@@ -146,6 +146,8 @@ def main():
         return bench_batched(args)
     if args.workload == "dbtrim_paged_decode_128k":
         return bench_paged_decode(args)
+    if args.workload == "qevict_diagnostics_32k":
+        return bench_diagnostics(args)
     import torch
     sys.path.insert(0, ROOT)
     from kv_cache_compression_gqa_amd import configs, synth
@@ -613,6 +615,117 @@ def cpu_baseline_paged(cfg, G, min_seconds=10.0):
     return {"value": done * n / el, "unit": "KV tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{done} rows of {n} kept tokens (the mean row of the workload), G = {G}: fp64 numpy oracle "
                       f"(page gather + decode attention); {el:.1f} s"}
+
+
+def bench_diagnostics(args):
+    """QEvict's dynamics diagnostics on a synthetic run of the 32K layer: the compressed run next to a full-cache
+    run of the same inputs (all windows FULL, never routed). Per step: the future missed mass (full-cache attention
+    on evicted windows) and the L1 output perturbation per head; per routing event: churn and re-entries into the
+    FULL tier. The kernel (kvc_route_diagnostics) is timed with HIP events on the per-step call."""
+    import torch
+    sys.path.insert(0, ROOT)
+    from kv_cache_compression_gqa_amd import configs, synth
+    from kv_cache_compression_gqa_amd.session import DecodeSession, route_diagnostics
+    cfg = configs.LLAMA3_8B_LAYER_32K
+    torch.cuda.set_device(0)
+    inp = synth.make_decode(cfg)
+    sess = DecodeSession(inp)
+    nw = inp.n_windows.astype(np.int32)
+    shadow = DecodeSession(inp, budgets=(nw, np.zeros_like(nw)))
+    U, NW, G = sess.U, sess.NW, sess.G
+    mf = torch.zeros((U, NW), dtype=torch.float32, device="cuda")
+    tier_prev = torch.empty_like(sess.tier)
+    per_step, per_event = [], []
+    for t in range(cfg.steps):
+        sess.step(route=False)
+        shadow.step(mass=mf, route=False)
+        per_step.append(route_diagnostics(sess.tier, sess.n_windows, G, mass_full=mf, o_full=shadow.out,
+                                          o=sess.out)[1])
+        if (t + 1) % cfg.route_every == 0:
+            tier_prev.copy_(sess.tier)
+            sess.route()
+            per_event.append(route_diagnostics(sess.tier, sess.n_windows, G, tier_prev=tier_prev)[0])
+    torch.cuda.synchronize()
+    if sess.device_status() or shadow.device_status():
+        print("device status bits set", file=sys.stderr)
+        sys.exit(1)
+    vals = torch.stack(per_step).cpu().numpy()      # [steps][U][1 + G]
+    cnts = torch.stack(per_event).cpu().numpy()     # [events][U][4]
+    out_norm = float(torch.abs(shadow.out).sum(dim=2).mean().item())
+    # the kernel: K calls (every input given) captured in one HIP graph, timed by one pair of HIP events on the
+    # stream they run on
+    K = max(1, args.steps)
+    counts = torch.empty((U, 4), dtype=torch.int32, device="cuda")
+    values = torch.empty((U, 1 + G), dtype=torch.float32, device="cuda")
+
+    def fn():
+        route_diagnostics(sess.tier, sess.n_windows, G, tier_prev=tier_prev, mass_full=mf, o_full=shadow.out,
+                          o=sess.out, counts=counts, values=values)
+
+    for _ in range(max(1, args.warmup)):
+        fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(K):
+            fn()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_s = ev0.elapsed_time(ev1) / K * 1e-3
+    nbytes = U * NW * (1 + 1 + 4) + 2 * U * G * 128 * 4 + U * 4 + U * (4 * 4 + (1 + G) * 4)
+    R = cfg.route_every
+    rec = {
+        "metric": "KV windows diagnosed/s (QEvict churn, re-entries, future missed mass; CriticalKV L1 perturbation)",
+        "value": U * NW * K / wall, "unit": "windows/s", "n_gpus": 1, "steps": K, "warmup": max(1, args.warmup),
+        "ms_per_step": wall / K * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": cfg.name + "_diagnostics", "units": U, "windows": NW, "steps": cfg.steps,
+                   "route_every": R},
+        "diagnostics": {
+            "future_missed_mass_mean_routed_steps": float(vals[R:, :, 0].mean()),
+            "future_missed_mass_last_step": float(vals[-1, :, 0].mean()),
+            "churn_per_event": [float(c) for c in (cnts[:, :, 0].sum(1) / (U * NW))],
+            "reentries_per_event": [int(c) for c in cnts[:, :, 1].sum(1)],
+            "global_lir": float(cnts[:, :, 1].sum() / max(1, cnts[:, :, 2].sum())),
+            "l1_perturbation_mean_routed_steps": float(vals[R:, :, 1:].mean()),
+            "full_cache_output_l1_mean": out_norm},
+        "roofline": {"bound": "hbm", "achieved": nbytes / call_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": nbytes / call_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "kvc_route_diagnostics (diag_kernel, graph-timed; latency-bound: 8 workgroups)",
+                     "avg_launch_us": call_s * 1e6, "algorithmic_bytes_per_launch": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_diagnostics(U, NW, G)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline_diagnostics(U, NW, G, min_seconds=10.0):
+    """The oracle's diagnostics (counts, future missed mass, L1 perturbation) per unit over seeded tiers, masses and
+    outputs of the same shape, repeated until ``min_seconds`` have passed."""
+    from oracle import diagnostics
+    rng = np.random.default_rng(7)
+    prev = rng.integers(0, 3, size=(U, NW)).astype(np.int8)
+    now = rng.integers(0, 3, size=(U, NW)).astype(np.int8)
+    mass = rng.random((U, NW)) / NW
+    of, oc = rng.standard_normal((2, U, G, 128))
+    calls, el = 0, 0.0
+    t0 = time.perf_counter()
+    while el < min_seconds:
+        for u in range(U):
+            diagnostics.route_counts(prev[u], now[u])
+            diagnostics.future_missed_mass(mass[u], now[u])
+            diagnostics.perturbation_l1(of[u], oc[u])
+        calls += 1
+        el = time.perf_counter() - t0
+    return {"value": calls * U * NW / el, "unit": "windows/s", "cores": _oracle_threads(), "kind": "oracle",
+            "sample": f"{calls} calls over {U} units x {NW} windows (seeded tiers, masses, outputs): fp64 numpy "
+                      f"oracle; {el:.1f} s"}
 
 
 def cpu_baseline_dbtrim(cfg, layers=16):

@@ -6,31 +6,18 @@
 // assignment changes between consecutive routing steps). CriticalKV page ("Framework Teórico") measures a kept
 // subset by the L1 distance between the attention output over the full cache and over the subset.
 //
-// diag_kernel: one 256-thread workgroup per unit. Thread t takes windows t, t + 256, ... (ascending) and counts
-// tier changes, entries into FULL, FULL and resident windows, and sums the full-cache mass of the EVICTED
-// windows; the counts are summed per wave and then over the four waves, the mass by a fixed-order tree in LDS
-// (bitwise reproducible). Then, per query head, thread d < 128 takes |o_full - o| at head_dim d, summed by the
-// same tree. Everything it reads is a few KB per unit, so the kernel is latency-bound.
+// diag_kernel: one 256-thread workgroup per unit. Thread d < 128 first loads |o_full - o| at head_dim d of every
+// query head; thread t then takes windows t, t + 256, ... (ascending) and counts tier changes, entries into FULL,
+// FULL and resident windows, and sums the full-cache mass of the EVICTED windows. Every sum is taken per wave
+// (DPP row sums, then the four rows in order) and then over the four waves in order, so the results are bitwise
+// reproducible. Everything it reads is a few KB per unit: the kernel is latency-bound.
 #include "kvc_internal.h"
 
 namespace kvc {
 namespace {
 
 constexpr int kDiagThreads = 256;
-
-__device__ __forceinline__ float block_sum_tree(float v, float* red) {
-  const int t = threadIdx.x;
-  red[t] = v;
-  __syncthreads();
-#pragma unroll
-  for (int s = kDiagThreads / 2; s > 0; s >>= 1) {
-    if (t < s) red[t] += red[t + s];
-    __syncthreads();
-  }
-  const float r = red[0];
-  __syncthreads();
-  return r;
-}
+constexpr int kDiagWaves = kDiagThreads / kWave;
 
 template <int G>
 __global__ __launch_bounds__(kDiagThreads) void diag_kernel(kvc_diag_args a) {
@@ -40,6 +27,16 @@ __global__ __launch_bounds__(kDiagThreads) void diag_kernel(kvc_diag_args a) {
   const int NW = a.n_windows_max;
   const int nw = min(max(a.n_windows[u], 0), NW);
   const size_t base = size_t(u) * NW;
+  float part[1 + G];
+  const bool have_o = a.o_full != nullptr && a.o != nullptr;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    part[1 + h] = 0.0f;
+    if (have_o && t < kD) {
+      const size_t i = (size_t(u) * G + h) * kD + t;
+      part[1 + h] = fabsf(a.o_full[i] - a.o[i]);
+    }
+  }
   int ch = 0, re = 0, nf = 0, nr = 0;
   float fmm = 0.0f;
   for (int w = t; w < nw; w += kDiagThreads) {
@@ -51,36 +48,35 @@ __global__ __launch_bounds__(kDiagThreads) void diag_kernel(kvc_diag_args a) {
     nr += now != KVC_TIER_EVICTED ? 1 : 0;
     if (a.mass_full != nullptr && now == KVC_TIER_EVICTED) fmm += a.mass_full[base + w];
   }
-  __shared__ int cnt[4][kDiagThreads / kWave];
-  __shared__ float red[kDiagThreads];
+  part[0] = fmm;
+  __shared__ int cnt[4][kDiagWaves];
+  __shared__ float vred[1 + G][kDiagWaves];
   ch = wave_sum_int(ch);
   re = wave_sum_int(re);
   nf = wave_sum_int(nf);
   nr = wave_sum_int(nr);
+#pragma unroll
+  for (int i = 0; i < 1 + G; ++i) part[i] = wave_sum(part[i]);
   if (lane == 0) {
     cnt[0][wave] = ch;
     cnt[1][wave] = re;
     cnt[2][wave] = nf;
     cnt[3][wave] = nr;
+#pragma unroll
+    for (int i = 0; i < 1 + G; ++i) vred[i][wave] = part[i];
   }
-  const float fmm_all = block_sum_tree(fmm, red);  // its barriers also publish cnt
+  __syncthreads();
   if (t < 4) {
     int s = 0;
 #pragma unroll
-    for (int i = 0; i < kDiagThreads / kWave; ++i) s += cnt[t][i];
+    for (int i = 0; i < kDiagWaves; ++i) s += cnt[t][i];
     a.counts[size_t(u) * 4 + t] = s;
-  }
-  if (t == 0) a.values[size_t(u) * (1 + G)] = fmm_all;
-  const bool have_o = a.o_full != nullptr && a.o != nullptr;
+  } else if (t >= kWave && t < kWave + 1 + G) {
+    const int i = t - kWave;
+    float s = 0.0f;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float v = 0.0f;
-    if (have_o && t < kD) {
-      const size_t i = (size_t(u) * G + h) * kD + t;
-      v = fabsf(a.o_full[i] - a.o[i]);
-    }
-    const float L = block_sum_tree(v, red);
-    if (t == 0) a.values[size_t(u) * (1 + G) + 1 + h] = L;
+    for (int k = 0; k < kDiagWaves; ++k) s += vred[i][k];
+    a.values[size_t(u) * (1 + G) + i] = s;
   }
 }
 

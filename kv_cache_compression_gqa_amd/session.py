@@ -221,13 +221,16 @@ class DecodeSession:
 
 
 def route_diagnostics(tier: torch.Tensor, n_windows: torch.Tensor, group: int, tier_prev=None, mass_full=None,
-                      o_full=None, o=None, stream=None):
+                      o_full=None, o=None, stream=None, counts=None, values=None):
     """kvc_route_diagnostics: per-unit (changed, entered FULL, FULL, resident) window counts and (future missed
     mass, L1 output perturbation per query head). Returns (counts [U][4] int32, values [U][1 + G] float32) on the
-    device."""
+    device (written into ``counts`` / ``values`` when given)."""
     U, NW = tier.shape
-    counts = torch.empty((U, 4), dtype=torch.int32, device=tier.device)
-    values = torch.empty((U, 1 + group), dtype=torch.float32, device=tier.device)
+    if counts is None:
+        counts = torch.empty((U, 4), dtype=torch.int32, device=tier.device)
+    if values is None:
+        values = torch.empty((U, 1 + group), dtype=torch.float32, device=tier.device)
+    assert counts.shape == (U, 4) and values.shape == (U, 1 + group)
     a = abi.KvcDiagArgs(tier_prev=abi.ptr(tier_prev), tier=abi.ptr(tier), n_windows=abi.ptr(n_windows),
                         mass_full=abi.ptr(mass_full), o_full=abi.ptr(o_full), o=abi.ptr(o), counts=abi.ptr(counts),
                         values=abi.ptr(values), n_units=U, n_windows_max=NW, group=group, head_dim=128)
