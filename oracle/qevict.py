@@ -30,7 +30,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from .attention import gqa_decode, window_mass
+from .attention import gqa_decode, weighted_window_mass, window_mass
 from .fp import f32_to_storage_rne, storage_to_f64
 from .int2 import dequantize, quantize
 from .select import EVICTED, FULL, INT2, three_tier
@@ -88,29 +88,38 @@ class QEvictUnit:
     def assemble(self):
         """Resident keys in attention order: FULL windows ascending, INT2 windows ascending, then the tail."""
         full, int2 = self.resident_windows()
-        Ks, Vs, kw = [], [], []
+        Ks, Vs, kw, kp = [], [], [], []
         for w in list(full) + list(int2):
             k, v = self.window_values(int(w))
             Ks.append(k)
             Vs.append(v)
             kw.append(np.full(self.W, w, np.int64))
+            kp.append(w * self.W + np.arange(self.W, dtype=np.int64))
         if self.tail_k:
             Ks.append(storage_to_f64(np.stack(self.tail_k), self.dtype))
             Vs.append(storage_to_f64(np.stack(self.tail_v), self.dtype))
             kw.append(np.full(len(self.tail_k), -1, np.int64))
+            kp.append(np.full(len(self.tail_k), -1, np.int64))
+        self.key_pos = np.concatenate(kp)
         return np.concatenate(Ks), np.concatenate(Vs), np.concatenate(kw)
 
     # -- one decode step -------------------------------------------------------------------------------------
-    def step(self, q_bits: np.ndarray, k_new=None, v_new=None, accumulate: bool = True) -> StepResult:
+    def step(self, q_bits: np.ndarray, k_new=None, v_new=None, accumulate: bool = True,
+             token_weight=None) -> StepResult:
         """One decode step. ``accumulate`` = False leaves the cumulative scores alone (the page's cheaper schedule
-        scores only at routing events and decodes plainly in between)."""
+        scores only at routing events and decodes plainly in between). ``token_weight`` [G][>= n_windows * W]
+        weights each window key's probability per query head (CriticalKV's |V W_O|_1 plugged into the window
+        score); None = the plain attention mass."""
         if k_new is not None:
             self.tail_k.append(np.array(k_new, np.uint16))
             self.tail_v.append(np.array(v_new, np.uint16))
         K, V, kw = self.assemble()
         q = storage_to_f64(q_bits, self.dtype)
         s, p, o = gqa_decode(q, K, V)
-        mass = window_mass(p, kw, self.n_windows)
+        if token_weight is None:
+            mass = window_mass(p, kw, self.n_windows)
+        else:
+            mass = weighted_window_mass(p, self.key_pos, np.asarray(token_weight, np.float64), self.n_windows, self.W)
         if accumulate:
             self.cum += mass
         self.t += 1

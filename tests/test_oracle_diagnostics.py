@@ -121,3 +121,32 @@ def test_event_only_schedule():
             event.route(CFG.budget_full, CFG.budget_int2)
     # the event schedule's score is the sum of the masses of the event steps only
     assert np.allclose(event.cum, masses[R - 1] + masses[2 * R - 1] + masses[3 * R - 1], rtol=0, atol=1e-15)
+
+
+def test_weighted_window_mass():
+    """The projected-value weighting of the window score: all-ones weights give the plain mass exactly; a weight
+    that picks one position gives that key's head-mean probability; constant weights scale the mass; a dense
+    random weighting equals the sum written as one matrix product per window."""
+    inp, unit = make_unit(steps=6)
+    nw, W = unit.n_windows, unit.W
+    G = inp.q.shape[2]
+    rng = np.random.default_rng(3)
+    for t in range(6):
+        r = unit.step(inp.q[t, 0], inp.k_new[t, 0], inp.v_new[t, 0])
+        kp = unit.key_pos
+        ones = np.ones((G, nw * W))
+        assert np.array_equal(attention.weighted_window_mass(r.p, kp, ones, nw, W), r.mass)
+        assert np.allclose(attention.weighted_window_mass(r.p, kp, 2.5 * ones, nw, W), 2.5 * r.mass, rtol=1e-15)
+        pick = np.zeros((G, nw * W))
+        j = int(np.flatnonzero(kp >= 0)[5])
+        pick[:, kp[j]] = 1.0
+        m = attention.weighted_window_mass(r.p, kp, pick, nw, W)
+        assert abs(m[kp[j] // W] - r.p[:, j].mean()) <= 1e-15 and np.count_nonzero(m) == 1
+        wt = rng.lognormal(size=(G, nw * W))
+        m = attention.weighted_window_mass(r.p, kp, wt, nw, W)
+        for w in range(nw):
+            cols = np.flatnonzero((kp >= 0) & (kp // W == w))
+            ref = sum((r.p[:, c] * wt[:, kp[c]]).sum() for c in cols) / G
+            assert abs(m[w] - ref) <= 1e-12 * max(1.0, abs(ref))
+        if (t + 1) % 3 == 0:
+            unit.route(CFG.budget_full, CFG.budget_int2)
