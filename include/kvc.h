@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 1
+#define KVC_ABI_VERSION 2
 
 typedef enum {
   KVC_OK = 0,
@@ -125,6 +125,13 @@ typedef struct kvc_cache {
  *            tail keys, new key). probs_stride >= max over units of W*(n_full+n_int2) + tail_len + (k_new?1:0).
  *   mass     [U][NW] float or NULL: this step's window mass (0 for windows that are not resident).
  *   accumulate_cum  0 or 1.
+ *   token_weight   [U][G][weight_stride] float, or NULL. When given, each window key's probability is weighted
+ *            per query head in the window score (CriticalKV page, "Algoritmo": the attention weight times the L1
+ *            norm of the value projected through W_O, used as a plug-in for an existing accumulation pipeline):
+ *            mass_w = (1/G) sum_h sum_{i in w} p_{h,i} token_weight[u][h][i], i the prefill position (w*W + j).
+ *            kvc_score(KVC_SCORE_CRITICALKV)'s norm output [hq][n_keys] is this layout for the units = the KV
+ *            heads of one layer (weight_stride = n_keys). The outputs o and probs are unchanged.
+ *   weight_stride  >= n_windows_max * W when token_weight is given.
  *   max_full, max_int2, max_tail   HOST upper bounds over units of n_full, n_int2 and tail_len (before the
  *            append). They size the grid; a unit whose device count exceeds them sets KVC_DEV_BOUND_EXCEEDED and
  *            its step is undefined.
@@ -142,6 +149,8 @@ typedef struct kvc_decode_args {
   int32_t max_int2;
   int32_t max_tail;
   int32_t reserved;
+  const float* token_weight; /* [U][G][weight_stride] float or NULL; see above */
+  int64_t weight_stride;
 } kvc_decode_args;
 
 /* Three-tier routing (QEvict page, "Metodologia: QEvict" and "Mecanismos Principais"). Per unit, the resident

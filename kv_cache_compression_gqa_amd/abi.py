@@ -41,7 +41,8 @@ class KvcCache(C.Structure):
 class KvcDecodeArgs(C.Structure):
     _fields_ = [("q", P), ("k_new", P), ("v_new", P), ("out", P), ("probs", P), ("mass", P),
                 ("probs_stride", C.c_int32), ("accumulate_cum", C.c_int32), ("max_full", C.c_int32),
-                ("max_int2", C.c_int32), ("max_tail", C.c_int32), ("reserved", C.c_int32)]
+                ("max_int2", C.c_int32), ("max_tail", C.c_int32), ("reserved", C.c_int32), ("token_weight", P),
+                ("weight_stride", C.c_int64)]
 
 
 class KvcTierRouteArgs(C.Structure):
@@ -130,7 +131,7 @@ def lib():
             fn = getattr(L, name)
             fn.restype = res
             fn.argtypes = args
-        if L.kvc_abi_version() != 1:
+        if L.kvc_abi_version() != 2:
             raise RuntimeError("kvc ABI version mismatch")
         _lib = L
     return _lib

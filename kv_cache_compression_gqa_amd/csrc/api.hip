@@ -37,6 +37,10 @@ int check_decode(const kvc_cache* c, const kvc_decode_args* a, bool need_out) {
   if (a->k_new != nullptr && (!aligned(a->k_new, 16) || !aligned(a->v_new, 16))) return KVC_E_INVALID;
   if (need_out && a->out == nullptr) return KVC_E_INVALID;
   if (a->accumulate_cum != 0 && a->accumulate_cum != 1) return KVC_E_INVALID;
+  if (a->token_weight != nullptr &&
+      (!aligned(a->token_weight, 4) || a->weight_stride < int64_t(c->n_windows_max) * kvc::kW)) {
+    return KVC_E_INVALID;
+  }
   const int has_new = a->k_new != nullptr ? 1 : 0;
   if (a->max_full < 0 || a->max_int2 < 0 || a->max_tail < 0) return KVC_E_BUDGET;
   if (int64_t(a->max_full) + a->max_int2 > c->n_windows_max) return KVC_E_BUDGET;

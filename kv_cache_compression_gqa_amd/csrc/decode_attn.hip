@@ -18,7 +18,9 @@
 //     tokens x 32 head_dim of K. INT2 keys enter B as 128+c (bf16) / 1024+c (fp16) bit patterns, one group of 32
 //     head_dim per MFMA; the group's scale/zero are applied to the fp32 product:  s*acc + (z - magic*s)*sum(q).
 //   * softmax over the task's keys (max, exp, sums by DPP reductions over 16-lane rows); each window's exp-sum and the
-//     reference max it is relative to are written for the score.
+//     reference max it is relative to are written for the score. With per-position weights (WEIGHTED: CriticalKV
+//     page, "Algoritmo", the projected-value norm plugged into the window score) the window's exp-sum weights each
+//     key per head; the weights are loaded with the task's other loads.
 //   * P.V on MFMA: A = 16 head_dim x 32 tokens of V (V is stored transposed per window), B = P^T split into a
 //     high and a low part (columns 0..G-1 and G..2G-1) so the product keeps ~16 bits of P. INT2 values enter A as
 //     exact fp16 codes and the per-token scale is folded into B (P*s); the zero term sum(P*z) is a VALU bias.
@@ -80,6 +82,8 @@ struct DecodeParams {
   float* wsum;     // [U][NW][G]
   float* wref;     // [U][NW][G]
   int32_t* unit_tl;  // [U] the tail length the step's partials were computed with (before the append)
+  const float* wnorm;  // [U][G][wstride] per-head weight of each window position in the score, or null
+  long wstride;
 };
 
 // The compiler fetches kernel arguments on first use, each fetch a round trip it then waits for; these pins make
@@ -89,7 +93,8 @@ __device__ __forceinline__ void fetch_args_partial(const DecodeParams& p) {
                "s"(p.v_meta), "s"(p.k_tail), "s"(p.v_tail), "s"(p.res_list), "s"(p.n_full), "s"(p.n_int2),
                "s"(p.tail_len));
   asm volatile("" ::"s"(p.q), "s"(p.k_new), "s"(p.max_full), "s"(p.max_int2), "s"(p.max_tail), "s"(p.n_tb),
-               "s"(p.n_qt), "s"(p.P), "s"(p.part_ml), "s"(p.part_o), "s"(p.wsum), "s"(p.wref), "s"(p.unit_tl));
+               "s"(p.n_qt), "s"(p.P), "s"(p.part_ml), "s"(p.part_o), "s"(p.wsum), "s"(p.wref), "s"(p.unit_tl),
+               "s"(p.wnorm), "s"(p.wstride));
 }
 __device__ __forceinline__ void fetch_args_combine(const DecodeParams& p) {
   asm volatile("" ::"s"(p.NW), "s"(p.TM), "s"(p.P), "s"(p.CB), "s"(p.out), "s"(p.part_ml), "s"(p.part_o), "s"(p.tier),
@@ -277,8 +282,25 @@ __device__ __forceinline__ void store_window_sums(const DecodeParams& p, const C
   }
 }
 
+// Per-head weights of one window's tokens for the weighted score: lane (col, q) takes tokens col and 16 + col of
+// head rows 4q + r (rows past G read head G-1; their sums are never stored).
+template <int G>
+__device__ __forceinline__ void load_weights(const DecodeParams& p, const Ctx& c, int id, float (&wn)[4][2]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float* wp = p.wnorm + (size_t(c.u) * G + min(4 * c.q + r, G - 1)) * p.wstride + size_t(id) * kW;
+    wn[r][0] = wp[c.col];
+    wn[r][1] = wp[16 + c.col];
+  }
+}
+// Weighted window exp-sums (S holds exp(s - m) of the window's two 16-token tiles).
+__device__ __forceinline__ void weighted_sums(const f32x4 (&S)[2], const float (&wn)[4][2], float (&ws)[4]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) ws[r] = row_sum16(S[0][r] * wn[r][0] + S[1][r] * wn[r][1]);
+}
+
 // One FULL window (TAIL = false, window id) or one 32-token tail block (TAIL = true, block index blk).
-template <int G, class T, bool PROBS, bool TAIL>
+template <int G, class T, bool PROBS, bool TAIL, bool WEIGHTED>
 __device__ __forceinline__ void dense_task(const DecodeParams& p, const Ctx& c, int id, int blk, int nvalid, int pos,
                                            const u32x4 (&aq)[4], float* plds, WaveOut& wo) {
   using M = typename MfmaOf<T>::M;
@@ -293,6 +315,8 @@ __device__ __forceinline__ void dense_task(const DecodeParams& p, const Ctx& c, 
   }
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) vr[dt] = ld16(vb + (16 * dt + c.col) * kW + 8 * c.q);
+  float wn[4][2];
+  if constexpr (WEIGHTED && !TAIL) load_weights<G>(p, c, id, wn);
   __builtin_amdgcn_sched_barrier(0);  // every load of the task is issued before the first use
   const int tnew = TAIL && c.has_new ? c.tl - 32 * blk : -1;  // the step's token: not in the tail yet
   if (TAIL && c.has_new) {
@@ -319,6 +343,7 @@ __device__ __forceinline__ void dense_task(const DecodeParams& p, const Ctx& c, 
   if (PROBS) store_logits<G>(p, c, S[0], pos, nvalid);
   float ws[1][4];
   task_softmax<1>(S, wo, ws);
+  if constexpr (WEIGHTED && !TAIL) weighted_sums(S[0], wn, ws[0]);
   if (!TAIL) store_window_sums<G>(p, c, id, ws[0], wo.m);
   float x[8];
   p_to_b<G>(c, S[0], plds, x);
@@ -378,7 +403,7 @@ __device__ __forceinline__ void q_group_sums(const Ctx& c, const u32x4 (&aq)[4],
 }
 
 // QW INT2 windows (ok[i]: window i exists; masked windows read window 0 and contribute nothing).
-template <int G, class T, bool PROBS, int QW>
+template <int G, class T, bool PROBS, int QW, bool WEIGHTED>
 __device__ __forceinline__ void int2_task(const DecodeParams& p, const Ctx& c, const int (&ids)[QW],
                                           const bool (&ok)[QW], int pos0, const u32x4 (&aq)[4], float* plds,
                                           uint32_t* ms, WaveOut& wo) {
@@ -397,6 +422,11 @@ __device__ __forceinline__ void int2_task(const DecodeParams& p, const Ctx& c, c
     vc[i] = ld16(p.v_codes + win * (kW * kD / 8) + (c.col * 4 + c.q) * 8);
     km[i] = ld8(p.k_meta + win * kMetaWords + 2 * c.lane);
     vm[i] = ld8(p.v_meta + win * kMetaWords + 2 * c.lane);
+  }
+  float wn[QW][4][2];
+  if constexpr (WEIGHTED) {
+#pragma unroll
+    for (int i = 0; i < QW; ++i) load_weights<G>(p, c, ids[i], wn[i]);
   }
   __builtin_amdgcn_sched_barrier(0);  // every load of the task is issued before the first use
 #pragma unroll
@@ -437,6 +467,7 @@ __device__ __forceinline__ void int2_task(const DecodeParams& p, const Ctx& c, c
   task_softmax<QW>(S, wo, ws);
 #pragma unroll
   for (int i = 0; i < QW; ++i) {
+    if constexpr (WEIGHTED) weighted_sums(S[i], wn[i], ws[i]);
     if (ok[i]) store_window_sums<G>(p, c, ids[i], ws[i], wo.m);
   }
   // P.V: A = exact fp16 codes of 16 head_dim x 32 tokens, B = (P * scale)^T hi/lo, bias = sum P * zero
@@ -475,7 +506,7 @@ __device__ __forceinline__ void int2_task(const DecodeParams& p, const Ctx& c, c
   }
 }
 
-template <int G, class T, bool PROBS, int QW, int WPB>
+template <int G, class T, bool PROBS, int QW, int WPB, bool WEIGHTED>
 __global__ __launch_bounds__(WPB * kWave) __attribute__((amdgpu_waves_per_eu(4))) void decode_partial(DecodeParams p) {
   fetch_args_partial(p);
   // one-round launches (WPB 8) go slice-major, so that every unit's slices are spread over the launch order; many
@@ -568,12 +599,12 @@ __global__ __launch_bounds__(WPB * kWave) __attribute__((amdgpu_waves_per_eu(4))
         ids[i] = ok[i] ? sid[i] : 0;
       }
       if (bad && lane == 0) atomicOr(p.status, KVC_DEV_BOUND_EXCEEDED);
-      int2_task<G, T, PROBS, QW>(p, c, ids, ok, (c.nf + q0) * kW, aq, plds, meta_all[wave], wo);
+      int2_task<G, T, PROBS, QW, WEIGHTED>(p, c, ids, ok, (c.nf + q0) * kW, aq, plds, meta_all[wave], wo);
     }
   } else if (task < t_full) {
     const int blk = task - t_tail;
     if (kW * blk < c.total_tail) {
-      dense_task<G, T, PROBS, true>(p, c, 0, blk, min(kW, c.total_tail - kW * blk), (c.nf + c.nq + blk) * kW, aq,
+      dense_task<G, T, PROBS, true, WEIGHTED>(p, c, 0, blk, min(kW, c.total_tail - kW * blk), (c.nf + c.nq + blk) * kW, aq,
                                     plds, wo);
     }
   } else if (task < t_end && f < c.nf) {
@@ -581,7 +612,7 @@ __global__ __launch_bounds__(WPB * kWave) __attribute__((amdgpu_waves_per_eu(4))
     if (unsigned(id) >= unsigned(p.NW)) {
       if (lane == 0) atomicOr(p.status, KVC_DEV_BOUND_EXCEEDED);
     } else {
-      dense_task<G, T, PROBS, false>(p, c, id, 0, kW, f * kW, aq, plds, wo);
+      dense_task<G, T, PROBS, false, WEIGHTED>(p, c, id, 0, kW, f * kW, aq, plds, wo);
     }
   }
 
@@ -832,12 +863,21 @@ struct Shape {
   int qw, wpb;
 };
 
+template <int G, class T, int QW, int WPB, bool WEIGHTED>
+void launch_partial_w(const DecodeParams& p, int U, hipStream_t s) {
+  if (p.probs != nullptr) {
+    hipLaunchKernelGGL((decode_partial<G, T, true, QW, WPB, WEIGHTED>), dim3(U * p.P), dim3(WPB * kWave), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((decode_partial<G, T, false, QW, WPB, WEIGHTED>), dim3(U * p.P), dim3(WPB * kWave), 0, s, p);
+  }
+}
+
 template <int G, class T, int QW, int WPB>
 void launch_partial(const DecodeParams& p, int U, hipStream_t s) {
-  if (p.probs != nullptr) {
-    hipLaunchKernelGGL((decode_partial<G, T, true, QW, WPB>), dim3(U * p.P), dim3(WPB * kWave), 0, s, p);
+  if (p.wnorm != nullptr) {
+    launch_partial_w<G, T, QW, WPB, true>(p, U, s);
   } else {
-    hipLaunchKernelGGL((decode_partial<G, T, false, QW, WPB>), dim3(U * p.P), dim3(WPB * kWave), 0, s, p);
+    launch_partial_w<G, T, QW, WPB, false>(p, U, s);
   }
 }
 
@@ -954,6 +994,8 @@ hipError_t launch_decode(const kvc_cache& c, const kvc_decode_args& a, void* ws,
   p.max_full = a.max_full;
   p.max_int2 = a.max_int2;
   p.max_tail = a.max_tail;
+  p.wnorm = a.token_weight;
+  p.wstride = long(a.weight_stride);
   const Shape sh = decode_shape(c, a);
   const TaskCounts tc = task_counts(a, sh.qw);
   p.n_tb = tc.n_tb;

@@ -136,7 +136,7 @@ class DecodeSession:
 
     # -- one decode step --------------------------------------------------------------------------------------
     def decode_args(self, t_index: int, out=None, probs=None, mass=None, append=True, accumulate=True,
-                    score_only=False):
+                    score_only=False, token_weight=None):
         mf, mq, mt = self.bounds()
         a = abi.KvcDecodeArgs(
             q=abi.ptr(self.q[t_index]),
@@ -145,7 +145,11 @@ class DecodeSession:
             out=None if score_only else abi.ptr(self.out if out is None else out),
             probs=abi.ptr(probs), mass=abi.ptr(mass),
             probs_stride=0 if probs is None else int(probs.shape[-1]),
-            accumulate_cum=1 if accumulate else 0, max_full=mf, max_int2=mq, max_tail=mt, reserved=0)
+            accumulate_cum=1 if accumulate else 0, max_full=mf, max_int2=mq, max_tail=mt, reserved=0,
+            token_weight=abi.ptr(token_weight), weight_stride=0 if token_weight is None else int(token_weight.stride(1)))
+        if token_weight is not None:
+            assert token_weight.dtype == torch.float32 and token_weight.stride(2) == 1
+            assert token_weight.shape[:2] == (self.U, self.G) and token_weight.stride(0) == self.G * token_weight.stride(1)
         return a
 
     def workspace(self, args: abi.KvcDecodeArgs):
@@ -169,13 +173,16 @@ class DecodeSession:
         finally:
             self.h_tail = saved
 
-    def step(self, probs=None, mass=None, append=True, route=True, stream=None, events=None):
+    def step(self, probs=None, mass=None, append=True, route=True, stream=None, events=None, token_weight=None):
         """Decode step t+1 using the pre-generated inputs of that step; routes when due. ``events`` = (before,
-        after) torch events recorded on the stream around the decode launch."""
+        after) torch events recorded on the stream around the decode launch. ``token_weight`` [U][G][>= NW*W]
+        float32 weights every window key's probability per query head in the window score (e.g. the projected-value
+        norms of kvc_score(CRITICALKV)); None scores by the plain attention mass."""
         ti = self.t
         R = self.cfg.route_every
         accumulate = self.score_schedule == "every" or (R > 0 and (ti + 1) % R == 0)
-        args = self.decode_args(ti, probs=probs, mass=mass, append=append, accumulate=accumulate)
+        args = self.decode_args(ti, probs=probs, mass=mass, append=append, accumulate=accumulate,
+                                token_weight=token_weight)
         ws = self.workspace(args)
         L = abi.lib()
         if events is not None:

@@ -92,10 +92,12 @@ def compare_route(sess: DecodeSession, oracles, gpu_cum):
 
 
 def run_decode_parity(cfg, units=None, steps=None, check_units=None, check_steps=None, probs=True, log=print,
-                      inp=None, unit_map=None, score_schedule="every"):
+                      inp=None, unit_map=None, score_schedule="every", token_weight=None, oracle_weight=None):
     """Run ``steps`` decode steps (routing on the workload's cadence) on the GPU for every unit, and on the oracle
     for the units in ``check_units`` (default all; units are independent, so a sample of them is followed exactly).
     ``score_schedule`` "event" adds the window mass to the cumulative score only at routing-event steps.
+    ``token_weight`` (device [U][G][S] float32) weights the window score on the GPU and ``oracle_weight`` (host
+    [U][G][S]) on the oracle side.
     Outputs are compared at every step in ``check_steps`` (default all); routing at every event. ``inp`` and
     ``unit_map`` (optional) give held inputs and the held unit each session unit starts from."""
     if inp is None:
@@ -110,7 +112,7 @@ def run_decode_parity(cfg, units=None, steps=None, check_units=None, check_steps
         stride = sess.probs_stride()
         pr = torch.zeros((U, sess.G, stride), dtype=torch.float32, device=sess.device) if probs else None
         mass = torch.zeros((U, sess.NW), dtype=torch.float32, device=sess.device)
-        sess.step(probs=pr, mass=mass, route=False)
+        sess.step(probs=pr, mass=mass, route=False, token_weight=token_weight)
         torch.cuda.synchronize()
         out = sess.out.cpu().numpy()
         pr_h = pr.cpu().numpy() if probs else None
@@ -119,7 +121,8 @@ def run_decode_parity(cfg, units=None, steps=None, check_units=None, check_steps
         for j, o in oracles.items():
             b = int(umap[j])
             acc = score_schedule == "every" or (cfg.route_every > 0 and (t + 1) % cfg.route_every == 0)
-            r = o.step(inp.q[t, b], inp.k_new[t, b], inp.v_new[t, b], accumulate=acc)
+            r = o.step(inp.q[t, b], inp.k_new[t, b], inp.v_new[t, b], accumulate=acc,
+                       token_weight=None if oracle_weight is None else oracle_weight[j])
             if t not in check_steps:
                 continue
             nw = oracles[j].n_windows

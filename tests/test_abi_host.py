@@ -24,13 +24,13 @@ def test_every_declared_symbol_is_exported_and_bound():
     for n in names:
         assert hasattr(L, n), n
         assert n in abi.SIGNATURES, n
-    assert L.kvc_abi_version() == 1
+    assert L.kvc_abi_version() == 2
 
 
 def test_struct_sizes_match_header_layout():
     # 8 int32 + 17 pointers
     assert C.sizeof(abi.KvcCache) == 8 * 4 + 17 * 8
-    assert C.sizeof(abi.KvcDecodeArgs) == 6 * 8 + 6 * 4
+    assert C.sizeof(abi.KvcDecodeArgs) == 6 * 8 + 6 * 4 + 2 * 8
     assert C.sizeof(abi.KvcTierRouteArgs) == 8 * 8
 
 
