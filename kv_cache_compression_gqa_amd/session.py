@@ -125,6 +125,7 @@ class DecodeSession:
             n_int2=abi.ptr(self.n_int2), status=abi.ptr(self.status))
         self._ws = None
         self._ws_bytes = 0
+        self.token_weight = None  # default per-position weights of the window score (step(token_weight=...))
 
     # -- bounds -----------------------------------------------------------------------------------------------
     def bounds(self):
@@ -182,7 +183,7 @@ class DecodeSession:
         R = self.cfg.route_every
         accumulate = self.score_schedule == "every" or (R > 0 and (ti + 1) % R == 0)
         args = self.decode_args(ti, probs=probs, mass=mass, append=append, accumulate=accumulate,
-                                token_weight=token_weight)
+                                token_weight=self.token_weight if token_weight is None else token_weight)
         ws = self.workspace(args)
         L = abi.lib()
         if events is not None:
