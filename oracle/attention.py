@@ -18,13 +18,16 @@ import math
 import numpy as np
 
 
-def gqa_decode(q: np.ndarray, K: np.ndarray, V: np.ndarray):
-    """q [G][D], K [n][D], V [n][D] (fp64) -> (logits [G][n], p [G][n], o [G][D])."""
+def gqa_decode(q: np.ndarray, K: np.ndarray, V: np.ndarray, bias=None):
+    """q [G][D], K [n][D], V [n][D] (fp64) -> (logits [G][n], p [G][n], o [G][D]). ``bias`` [n] (optional) is
+    added to every head's logits (the size correction of summary keys)."""
     q = np.asarray(q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
     D = q.shape[-1]
     s = (q @ K.T) / math.sqrt(D)
+    if bias is not None:
+        s = s + np.asarray(bias, dtype=np.float64)[None, :]
     m = s.max(axis=1, keepdims=True)
     e = np.exp(s - m)
     p = e / e.sum(axis=1, keepdims=True)

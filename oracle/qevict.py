@@ -22,7 +22,9 @@ Readings where the page is silent (each is listed with its reason in the design 
     INT2, the rest EVICTED for good;
   * the partial last window and every decode-time token form an unrouted tail that is always attended;
   * a promoted window's full-precision data is RNE_storage(x^) of its ledger copy; its ledger is kept;
-  * keys and values of INT2 windows are attended as x^ = fl32(c*s + z).
+  * keys and values of INT2 windows are attended as x^ = fl32(c*s + z);
+  * with summaries on (SEKV's mixed-resolution term), an evicted window is attended through one summary key and
+    value after the tail (oracle.summary).
 """
 from __future__ import annotations
 
@@ -34,6 +36,7 @@ from .attention import gqa_decode, weighted_window_mass, window_mass
 from .fp import f32_to_storage_rne, storage_to_f64
 from .int2 import dequantize, quantize
 from .select import EVICTED, FULL, INT2, three_tier
+from .summary import SIZE_CORRECTION, summarize
 
 
 @dataclass
@@ -58,8 +61,12 @@ class RoutePlan:
 
 class QEvictUnit:
     def __init__(self, k_win: np.ndarray, v_win: np.ndarray, k_tail: np.ndarray, v_tail: np.ndarray,
-                 dtype: str):
-        """k_win/v_win [n_w][W][D] storage patterns; k_tail/v_tail [t0][D] storage patterns."""
+                 dtype: str, summaries: bool = False):
+        """k_win/v_win [n_w][W][D] storage patterns; k_tail/v_tail [t0][D] storage patterns. ``summaries``: an
+        evicted window leaves a summary key and value that are attended with a size correction (SEKV's
+        mixed-resolution term; see oracle.summary)."""
+        self.summaries = summaries
+        self.sum_k, self.sum_v = [], []   # storage patterns [D], in eviction order
         self.dtype = dtype
         self.kw = np.array(k_win, dtype=np.uint16, copy=True)
         self.vw = np.array(v_win, dtype=np.uint16, copy=True)
@@ -100,7 +107,15 @@ class QEvictUnit:
             Vs.append(storage_to_f64(np.stack(self.tail_v), self.dtype))
             kw.append(np.full(len(self.tail_k), -1, np.int64))
             kp.append(np.full(len(self.tail_k), -1, np.int64))
+        if self.sum_k:
+            Ks.append(storage_to_f64(np.stack(self.sum_k), self.dtype))
+            Vs.append(storage_to_f64(np.stack(self.sum_v), self.dtype))
+            kw.append(np.full(len(self.sum_k), -1, np.int64))
+            kp.append(np.full(len(self.sum_k), -1, np.int64))
         self.key_pos = np.concatenate(kp)
+        n_sum = len(self.sum_k)
+        n = sum(len(a) for a in kw)
+        self.key_bias = np.concatenate([np.zeros(n - n_sum), np.full(n_sum, SIZE_CORRECTION)])
         return np.concatenate(Ks), np.concatenate(Vs), np.concatenate(kw)
 
     # -- one decode step -------------------------------------------------------------------------------------
@@ -115,7 +130,7 @@ class QEvictUnit:
             self.tail_v.append(np.array(v_new, np.uint16))
         K, V, kw = self.assemble()
         q = storage_to_f64(q_bits, self.dtype)
-        s, p, o = gqa_decode(q, K, V)
+        s, p, o = gqa_decode(q, K, V, bias=self.key_bias if self.sum_k else None)
         if token_weight is None:
             mass = window_mass(p, kw, self.n_windows)
         else:
@@ -149,6 +164,9 @@ class QEvictUnit:
             self.kw[w] = f32_to_storage_rne(dequantize(e["kc"], e["ks"], e["kz"]), self.dtype)
             self.vw[w] = f32_to_storage_rne(dequantize(e["vc"], e["vs"], e["vz"]), self.dtype)
         for w in evicted:
+            if self.summaries:   # from the full-precision slot as it stands (original, or a promoted copy)
+                self.sum_k.append(summarize(self.kw[w], self.dtype))
+                self.sum_v.append(summarize(self.vw[w], self.dtype))
             self.ledger.pop(int(w), None)
         self.tier = after
         return RoutePlan(tier_before=before, tier_after=after, quantized=quantized, promoted=promoted,

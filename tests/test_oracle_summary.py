@@ -1,0 +1,89 @@
+"""Pins for the oracle's span summaries (SEKV's mixed-resolution term; CPU only): the summary of a window against
+an exact rational mean, the size correction against the 32 tokens it stands for when they are identical, and
+the bookkeeping of a run (one summary per evicted window, in eviction order, never changed, mass conservation)."""
+from fractions import Fraction
+
+import numpy as np
+
+from kv_cache_compression_gqa_amd import configs, synth
+from oracle import attention, qevict, summary
+from oracle.fp import f32_to_storage_rne, storage_to_f64
+from oracle.select import EVICTED
+
+CFG = configs.TINY
+
+
+def test_summary_is_the_rounded_exact_mean():
+    rng = np.random.default_rng(9)
+    for dtype in ("bf16", "f16"):
+        bits = synth.to_storage_bits(rng.standard_normal((32, 128)) * 3.0, dtype)
+        got = summary.summarize(bits, dtype)
+        vals = storage_to_f64(bits, dtype)
+        for d in range(128):
+            exact = sum(Fraction(float(v)) for v in vals[:, d]) / 32      # exact rational mean
+            want = f32_to_storage_rne(np.array([np.float32(float(exact))]), dtype)[0]
+            assert got[d] == want, (dtype, d)
+
+
+def test_size_correction_matches_identical_tokens():
+    """A window of 32 identical keys and values, and its summary with the ln 32 correction, get the same attention
+    mass and give the same output."""
+    rng = np.random.default_rng(10)
+    dtype = "bf16"
+    k = synth.to_storage_bits(rng.standard_normal(128), dtype)
+    v = synth.to_storage_bits(rng.standard_normal(128), dtype)
+    others_k = storage_to_f64(synth.to_storage_bits(rng.standard_normal((40, 128)), dtype), dtype)
+    others_v = storage_to_f64(synth.to_storage_bits(rng.standard_normal((40, 128)), dtype), dtype)
+    win_k = np.tile(k, (32, 1))
+    win_v = np.tile(v, (32, 1))
+    sk, sv = summary.summarize(win_k, dtype), summary.summarize(win_v, dtype)
+    assert np.array_equal(sk, k) and np.array_equal(sv, v)
+    q = rng.standard_normal((4, 128))
+    K_full = np.concatenate([others_k, storage_to_f64(win_k, dtype)])
+    V_full = np.concatenate([others_v, storage_to_f64(win_v, dtype)])
+    _, p_full, o_full = attention.gqa_decode(q, K_full, V_full)
+    K_sum = np.concatenate([others_k, storage_to_f64(sk, dtype)[None]])
+    V_sum = np.concatenate([others_v, storage_to_f64(sv, dtype)[None]])
+    bias = np.concatenate([np.zeros(40), [summary.SIZE_CORRECTION]])
+    _, p_sum, o_sum = attention.gqa_decode(q, K_sum, V_sum, bias=bias)
+    assert np.allclose(p_full[:, 40:].sum(1), p_sum[:, 40], rtol=1e-12, atol=0)
+    assert np.allclose(o_full, o_sum, rtol=1e-12, atol=1e-14)
+    # without the correction the summary would carry 1/32 of the window's weight before renormalisation
+    _, p_raw, _ = attention.gqa_decode(q, K_sum, V_sum)
+    assert np.all(p_raw[:, 40] < p_sum[:, 40])
+
+
+def test_run_bookkeeping():
+    inp = synth.make_decode(CFG, units=[0], steps=12)
+    nw, t0 = int(inp.n_windows[0]), int(inp.tail0[0])
+    unit = qevict.QEvictUnit(inp.k_win[0, :nw], inp.v_win[0, :nw], inp.k_tail0[0, :t0], inp.v_tail0[0, :t0],
+                             CFG.dtype, summaries=True)
+    plain = qevict.QEvictUnit(inp.k_win[0, :nw], inp.v_win[0, :nw], inp.k_tail0[0, :t0], inp.v_tail0[0, :t0],
+                              CFG.dtype)
+    seen = []
+    for t in range(12):
+        r = unit.step(inp.q[t, 0], inp.k_new[t, 0], inp.v_new[t, 0])
+        rp = plain.step(inp.q[t, 0], inp.k_new[t, 0], inp.v_new[t, 0])
+        n_sum = len(unit.sum_k)
+        # mass conservation: windows + tail + summaries
+        total = r.mass.sum() + r.p[:, r.key_window < 0].sum() / r.p.shape[0]
+        assert abs(total - 1.0) <= 1e-12
+        if n_sum == 0:
+            assert np.array_equal(r.o, rp.o) and np.array_equal(r.mass, rp.mass)
+        assert r.p.shape[1] == rp.p.shape[1] + n_sum
+        if (t + 1) % 4 == 0:
+            before = unit.tier.copy()
+            kw_before = unit.kw.copy()
+            vw_before = unit.vw.copy()
+            plan = unit.route(CFG.budget_full, CFG.budget_int2, scores=plain.cum)
+            plain.route(CFG.budget_full, CFG.budget_int2)
+            new = list(plan.evicted)
+            assert len(unit.sum_k) == n_sum + len(new)
+            for i, w in enumerate(new):
+                assert before[w] != EVICTED
+                assert np.array_equal(unit.sum_k[n_sum + i], summary.summarize(kw_before[w], CFG.dtype))
+                assert np.array_equal(unit.sum_v[n_sum + i], summary.summarize(vw_before[w], CFG.dtype))
+            for i, (a, b) in enumerate(seen):   # earlier summaries never change
+                assert np.array_equal(unit.sum_k[i], a) and np.array_equal(unit.sum_v[i], b)
+            seen = list(zip(unit.sum_k, unit.sum_v))
+    assert len(unit.sum_k) == int(np.count_nonzero(unit.tier == EVICTED))
