@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 2
+#define KVC_ABI_VERSION 3
 
 typedef enum {
   KVC_OK = 0,
@@ -79,6 +79,14 @@ typedef enum { KVC_TIER_FULL = 0, KVC_TIER_INT2 = 1, KVC_TIER_EVICTED = 2 } kvc_
  *   n_full, n_int2 [U] int32       lengths of the two parts of res_list.
  *   status         [1] int32       device error bits (KVC_DEV_*).
  *
+ *   k_sum, v_sum, n_sum, sum_max   optional span summaries (SEKV page, "Metodologia" sections 2 and 3: spans that
+ *                                  are not expanded enter the attention as summary vectors with a size
+ *                                  correction). When a window is evicted, kvc_summarize_evicted appends the means
+ *                                  of its 32 keys and values (exact sum, divided by 32, rounded to fp32 and then to
+ *                                  the storage dtype) at position n_sum[u]; kvc_decode_attn attends them after the
+ *                                  tail with logit q.k/sqrt(D) + ln 32 when step.max_summary > 0. K is token-major,
+ *                                  V head_dim-major inside 32-summary blocks (the tail's layouts).
+ *
  * The layouts put, for every MFMA operand the decode kernel builds, one lane's data in one 16-byte load.
  * All K/V rows must be 16-byte aligned (every base pointer 256-byte aligned is sufficient). */
 typedef struct kvc_cache {
@@ -107,6 +115,11 @@ typedef struct kvc_cache {
   int32_t* n_full;
   int32_t* n_int2;
   int32_t* status;
+  void* k_sum;       /* span summaries (optional, see below): [U][sum_max][D] storage dtype, or NULL */
+  void* v_sum;       /* [U][sum_max/32][D][32] storage dtype */
+  int32_t* n_sum;    /* [U] summaries written so far */
+  int32_t sum_max;   /* capacity per unit, a multiple of 32 (0 with k_sum == NULL) */
+  int32_t reserved2; /* must be 0 */
 } kvc_cache;
 
 /* One decode step (QEvict page, "Mecanismos Principais": attention is materialised to update the cumulative
@@ -132,6 +145,9 @@ typedef struct kvc_cache {
  *            kvc_score(KVC_SCORE_CRITICALKV)'s norm output [hq][n_keys] is this layout for the units = the KV
  *            heads of one layer (weight_stride = n_keys). The outputs o and probs are unchanged.
  *   weight_stride  >= n_windows_max * W when token_weight is given.
+ *   max_summary    0, or a HOST bound (<= cache.sum_max) on every unit's n_sum: the unit's summaries are then
+ *            attended as keys after the tail (key k_sum[u][j], value v_sum of summary j, logit + ln 32); they
+ *            belong to no window (no mass, no cumulative score). Requires cache.k_sum and probs == NULL.
  *   max_full, max_int2, max_tail   HOST upper bounds over units of n_full, n_int2 and tail_len (before the
  *            append). They size the grid; a unit whose device count exceeds them sets KVC_DEV_BOUND_EXCEEDED and
  *            its step is undefined.
@@ -151,6 +167,8 @@ typedef struct kvc_decode_args {
   int32_t reserved;
   const float* token_weight; /* [U][G][weight_stride] float or NULL; see above */
   int64_t weight_stride;
+  int32_t max_summary;       /* HOST bound on n_sum over units; 0 = no summaries attended; see above */
+  int32_t reserved2;         /* must be 0 */
 } kvc_decode_args;
 
 /* Three-tier routing (QEvict page, "Metodologia: QEvict" and "Mecanismos Principais"). Per unit, the resident
@@ -423,6 +441,18 @@ int kvc_paged_decode_attn(const kvc_paged_decode_args* args, void* workspace, si
                           hipStream_t stream);
 
 int kvc_route_diagnostics(const kvc_diag_args* args, hipStream_t stream);
+
+/* kvc_summarize_evicted: after a routing event, append the summary of every window evicted by it (SEKV page,
+ * "Metodologia" sections 2 and 3; see k_sum above). For unit u the windows w < n_windows[u] with
+ * tier_prev[u][w] != EVICTED and cache.tier[u][w] == EVICTED, ascending, get summaries n_sum[u], n_sum[u] + 1, ...
+ * from their full-precision slot (k_win, v_win) as it stands; n_sum[u] advances by their count. A unit whose
+ * summaries would pass sum_max keeps the first ones and raises KVC_DEV_BOUND_EXCEEDED.
+ *   tier_prev  [U][NW] int8: the tiers before the event.
+ *   max_new    HOST bound on the windows any unit evicts in this event (sizes the grid; more are an error bit).
+ * Workspace: kvc_summarize_workspace(cache) bytes, any contents, 256-byte aligned. */
+size_t kvc_summarize_workspace(const kvc_cache* cache);
+int kvc_summarize_evicted(const kvc_cache* cache, const int8_t* tier_prev, int32_t max_new, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
 
 /* Reads *cache->status into *host_status (synchronises the stream) and, if clear != 0, zeroes it. */
 int kvc_read_device_status(const kvc_cache* cache, int32_t* host_status, int32_t clear, hipStream_t stream);

@@ -35,14 +35,15 @@ class KvcCache(C.Structure):
                 ("reserved", C.c_int32),
                 ("n_windows", P), ("k_win", P), ("v_win", P), ("k_codes", P), ("v_codes", P), ("k_meta", P),
                 ("v_meta", P), ("k_tail", P), ("v_tail", P), ("tail_len", P), ("tier", P), ("ledgered", P),
-                ("cum", P), ("res_list", P), ("n_full", P), ("n_int2", P), ("status", P)]
+                ("cum", P), ("res_list", P), ("n_full", P), ("n_int2", P), ("status", P), ("k_sum", P),
+                ("v_sum", P), ("n_sum", P), ("sum_max", C.c_int32), ("reserved2", C.c_int32)]
 
 
 class KvcDecodeArgs(C.Structure):
     _fields_ = [("q", P), ("k_new", P), ("v_new", P), ("out", P), ("probs", P), ("mass", P),
                 ("probs_stride", C.c_int32), ("accumulate_cum", C.c_int32), ("max_full", C.c_int32),
                 ("max_int2", C.c_int32), ("max_tail", C.c_int32), ("reserved", C.c_int32), ("token_weight", P),
-                ("weight_stride", C.c_int64)]
+                ("weight_stride", C.c_int64), ("max_summary", C.c_int32), ("reserved2", C.c_int32)]
 
 
 class KvcTierRouteArgs(C.Structure):
@@ -112,6 +113,8 @@ SIGNATURES = {
     "kvc_paged_decode_workspace": (C.c_size_t, [C.POINTER(KvcPagedDecodeArgs)]),
     "kvc_paged_decode_attn": (C.c_int, [C.POINTER(KvcPagedDecodeArgs), P, C.c_size_t, P]),
     "kvc_route_diagnostics": (C.c_int, [C.POINTER(KvcDiagArgs), P]),
+    "kvc_summarize_workspace": (C.c_size_t, [C.POINTER(KvcCache)]),
+    "kvc_summarize_evicted": (C.c_int, [C.POINTER(KvcCache), P, C.c_int32, P, C.c_size_t, P]),
 }
 
 
@@ -131,7 +134,7 @@ def lib():
             fn = getattr(L, name)
             fn.restype = res
             fn.argtypes = args
-        if L.kvc_abi_version() != 2:
+        if L.kvc_abi_version() != 3:
             raise RuntimeError("kvc ABI version mismatch")
         _lib = L
     return _lib

@@ -26,6 +26,15 @@ int check_cache(const kvc_cache* c) {
     if (p == nullptr || !aligned(p, 4)) return KVC_E_INVALID;
   }
   if (c->tier == nullptr || c->ledgered == nullptr) return KVC_E_INVALID;
+  if (c->reserved2 != 0) return KVC_E_INVALID;
+  if (c->k_sum != nullptr) {
+    if (c->v_sum == nullptr || c->n_sum == nullptr || !aligned(c->k_sum, 16) || !aligned(c->v_sum, 16) ||
+        !aligned(c->n_sum, 4) || c->sum_max < kvc::kW || c->sum_max % kvc::kW != 0) {
+      return KVC_E_INVALID;
+    }
+  } else if (c->sum_max != 0) {
+    return KVC_E_INVALID;
+  }
   return KVC_OK;
 }
 
@@ -37,6 +46,11 @@ int check_decode(const kvc_cache* c, const kvc_decode_args* a, bool need_out) {
   if (a->k_new != nullptr && (!aligned(a->k_new, 16) || !aligned(a->v_new, 16))) return KVC_E_INVALID;
   if (need_out && a->out == nullptr) return KVC_E_INVALID;
   if (a->accumulate_cum != 0 && a->accumulate_cum != 1) return KVC_E_INVALID;
+  if (a->reserved2 != 0 || a->max_summary < 0) return KVC_E_INVALID;
+  if (a->max_summary > 0) {
+    if (c->k_sum == nullptr || a->max_summary > c->sum_max) return KVC_E_BUDGET;
+    if (a->probs != nullptr) return KVC_E_UNSUPPORTED;
+  }
   if (a->token_weight != nullptr &&
       (!aligned(a->token_weight, 4) || a->weight_stride < int64_t(c->n_windows_max) * kvc::kW)) {
     return KVC_E_INVALID;
@@ -328,6 +342,23 @@ int kvc_route_diagnostics(const kvc_diag_args* args, hipStream_t stream) {
     if (p != nullptr && !aligned(p, 4)) return KVC_E_INVALID;
   }
   return kvc::launch_diagnostics(a, stream) == hipSuccess ? KVC_OK : KVC_E_HIP;
+}
+
+size_t kvc_summarize_workspace(const kvc_cache* cache) {
+  if (check_cache(cache) != KVC_OK) return 0;
+  return kvc::summarize_workspace_bytes(*cache);
+}
+
+int kvc_summarize_evicted(const kvc_cache* cache, const int8_t* tier_prev, int32_t max_new, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_cache(cache);
+  if (st != KVC_OK) return st;
+  if (cache->k_sum == nullptr || tier_prev == nullptr) return KVC_E_INVALID;
+  if (max_new < 0 || max_new > cache->n_windows_max) return KVC_E_INVALID;
+  if (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < kvc::summarize_workspace_bytes(*cache)) {
+    return KVC_E_WORKSPACE;
+  }
+  return kvc::launch_summarize(*cache, tier_prev, max_new, workspace, stream) == hipSuccess ? KVC_OK : KVC_E_HIP;
 }
 
 int kvc_read_device_status(const kvc_cache* cache, int32_t* host_status, int32_t clear, hipStream_t stream) {

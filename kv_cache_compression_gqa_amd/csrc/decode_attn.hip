@@ -45,6 +45,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kMaxParts = 16384;    // workgroups (partials) per unit
 constexpr int kMetaWords = kW * kGroups;  // scale/zero words per window and per K or V
 constexpr float kInvSqrtD = 0.088388347648318440550f;  // 1/sqrt(128)
+constexpr float kLn32 = 3.4657359027997265471f;          // size correction of a 32-token span summary
 
 struct DecodeParams {
   int NW, TM;
@@ -84,6 +85,11 @@ struct DecodeParams {
   int32_t* unit_tl;  // [U] the tail length the step's partials were computed with (before the append)
   const float* wnorm;  // [U][G][wstride] per-head weight of each window position in the score, or null
   long wstride;
+  const uint16_t* k_sum;  // [U][SM][D] span summaries (keys), token-major
+  const uint16_t* v_sum;  // [U][SM/32][D][32]
+  const int32_t* n_sum;   // [U]
+  int SM, max_sum;        // capacity; host bound on n_sum (0: no summaries attended)
+  int n_sb;               // summary-block tasks per unit (bound)
 };
 
 // The compiler fetches kernel arguments on first use, each fetch a round trip it then waits for; these pins make
@@ -300,13 +306,15 @@ __device__ __forceinline__ void weighted_sums(const f32x4 (&S)[2], const float (
 }
 
 // One FULL window (TAIL = false, window id) or one 32-token tail block (TAIL = true, block index blk).
-template <int G, class T, bool PROBS, bool TAIL, bool WEIGHTED>
+// SUMM (with TAIL): one 32-summary block of the unit's span summaries, in the tail's layouts, logits + ln 32.
+template <int G, class T, bool PROBS, bool TAIL, bool WEIGHTED, bool SUMM = false>
 __device__ __forceinline__ void dense_task(const DecodeParams& p, const Ctx& c, int id, int blk, int nvalid, int pos,
                                            const u32x4 (&aq)[4], float* plds, WaveOut& wo) {
   using M = typename MfmaOf<T>::M;
-  const size_t base = TAIL ? (size_t(c.u) * p.TM + 32 * blk) * kD : (c.unit_win + id) * size_t(kW * kD);
-  const uint16_t* kb = (TAIL ? p.k_tail : p.k_win) + base;
-  const uint16_t* vb = (TAIL ? p.v_tail : p.v_win) + base;
+  static_assert(!SUMM || (TAIL && !PROBS), "summary blocks use the tail path and no probabilities");
+  const size_t base = TAIL ? (size_t(c.u) * (SUMM ? p.SM : p.TM) + 32 * blk) * kD : (c.unit_win + id) * size_t(kW * kD);
+  const uint16_t* kb = (TAIL ? (SUMM ? p.k_sum : p.k_tail) : p.k_win) + base;
+  const uint16_t* vb = (TAIL ? (SUMM ? p.v_sum : p.v_tail) : p.v_win) + base;
   u32x4 kr[8], vr[8];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -318,8 +326,8 @@ __device__ __forceinline__ void dense_task(const DecodeParams& p, const Ctx& c, 
   float wn[4][2];
   if constexpr (WEIGHTED && !TAIL) load_weights<G>(p, c, id, wn);
   __builtin_amdgcn_sched_barrier(0);  // every load of the task is issued before the first use
-  const int tnew = TAIL && c.has_new ? c.tl - 32 * blk : -1;  // the step's token: not in the tail yet
-  if (TAIL && c.has_new) {
+  const int tnew = TAIL && !SUMM && c.has_new ? c.tl - 32 * blk : -1;  // the step's token: not in the tail yet
+  if (TAIL && !SUMM && c.has_new) {
     u32x4 kn[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) kn[k] = ld16(p.k_new + size_t(c.u) * kD + 32 * k + 8 * c.q);
@@ -338,7 +346,7 @@ __device__ __forceinline__ void dense_task(const DecodeParams& p, const Ctx& c, 
     for (int k = 0; k < 4; ++k) S[0][t] = M::mfma(aq[k], kr[t * 4 + k], S[0][t]);
     const bool ok = 16 * t + c.col < nvalid;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) S[0][t][r] = ok ? S[0][t][r] * kInvSqrtD : -INFINITY;
+    for (int r = 0; r < 4; ++r) S[0][t][r] = ok ? S[0][t][r] * kInvSqrtD + (SUMM ? kLn32 : 0.0f) : -INFINITY;
   }
   if (PROBS) store_logits<G>(p, c, S[0], pos, nvalid);
   float ws[1][4];
@@ -355,7 +363,7 @@ __device__ __forceinline__ void dense_task(const DecodeParams& p, const Ctx& c, 
     const int n_ok = min(max(nvalid - t0, 0), 8);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const uint32_t nv = c.has_new ? uint32_t(p.v_new[size_t(c.u) * kD + 16 * dt + c.col]) : 0u;
+      const uint32_t nv = !SUMM && c.has_new ? uint32_t(p.v_new[size_t(c.u) * kD + 16 * dt + c.col]) : 0u;
       uint32_t w[4] = {vr[dt].x, vr[dt].y, vr[dt].z, vr[dt].w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -506,7 +514,7 @@ __device__ __forceinline__ void int2_task(const DecodeParams& p, const Ctx& c, c
   }
 }
 
-template <int G, class T, bool PROBS, int QW, int WPB, bool WEIGHTED>
+template <int G, class T, bool PROBS, int QW, int WPB, bool WEIGHTED, bool SUMMARY>
 __global__ __launch_bounds__(WPB * kWave) __attribute__((amdgpu_waves_per_eu(4))) void decode_partial(DecodeParams p) {
   fetch_args_partial(p);
   // one-round launches (WPB 8) go slice-major, so that every unit's slices are spread over the launch order; many
@@ -532,7 +540,8 @@ __global__ __launch_bounds__(WPB * kWave) __attribute__((amdgpu_waves_per_eu(4))
   c.unit_win = size_t(u) * p.NW;
   const int32_t* res = p.res_list + c.unit_win;
   const int MF = p.max_full;
-  const int t_tail = p.n_qt, t_full = p.n_qt + p.n_tb, t_end = t_full + MF;
+  // task ranges: INT2 tasks, tail blocks, span-summary blocks (SUMMARY only), FULL windows
+  const int t_tail = p.n_qt, t_sum = p.n_qt + p.n_tb, t_full = t_sum + (SUMMARY ? p.n_sb : 0), t_end = t_full + MF;
   const int q0 = task * QW;    // INT2 task: first INT2 slot
   const int f = task - t_full;  // FULL task: slot in res_list
 
@@ -601,11 +610,19 @@ __global__ __launch_bounds__(WPB * kWave) __attribute__((amdgpu_waves_per_eu(4))
       if (bad && lane == 0) atomicOr(p.status, KVC_DEV_BOUND_EXCEEDED);
       int2_task<G, T, PROBS, QW, WEIGHTED>(p, c, ids, ok, (c.nf + q0) * kW, aq, plds, meta_all[wave], wo);
     }
-  } else if (task < t_full) {
+  } else if (task < t_sum) {
     const int blk = task - t_tail;
     if (kW * blk < c.total_tail) {
       dense_task<G, T, PROBS, true, WEIGHTED>(p, c, 0, blk, min(kW, c.total_tail - kW * blk), (c.nf + c.nq + blk) * kW, aq,
                                     plds, wo);
+    }
+  } else if (SUMMARY && task < t_full) {
+    if constexpr (SUMMARY) {
+      const int blk = task - t_sum;
+      const int ns_dev = p.n_sum[u];
+      const int ns = min(max(ns_dev, 0), p.max_sum);
+      if (blk == 0 && lane == 0 && ns != ns_dev) atomicOr(p.status, KVC_DEV_BOUND_EXCEEDED);
+      if (kW * blk < ns) dense_task<G, T, false, true, WEIGHTED, true>(p, c, 0, blk, min(kW, ns - kW * blk), 0, aq, plds, wo);
     }
   } else if (task < t_end && f < c.nf) {
     const int id = sid[0];
@@ -865,10 +882,15 @@ struct Shape {
 
 template <int G, class T, int QW, int WPB, bool WEIGHTED>
 void launch_partial_w(const DecodeParams& p, int U, hipStream_t s) {
-  if (p.probs != nullptr) {
-    hipLaunchKernelGGL((decode_partial<G, T, true, QW, WPB, WEIGHTED>), dim3(U * p.P), dim3(WPB * kWave), 0, s, p);
+  if (p.max_sum > 0) {  // summaries are attended only without probabilities (checked by the caller)
+    hipLaunchKernelGGL((decode_partial<G, T, false, QW, WPB, WEIGHTED, true>), dim3(U * p.P), dim3(WPB * kWave), 0, s,
+                       p);
+  } else if (p.probs != nullptr) {
+    hipLaunchKernelGGL((decode_partial<G, T, true, QW, WPB, WEIGHTED, false>), dim3(U * p.P), dim3(WPB * kWave), 0, s,
+                       p);
   } else {
-    hipLaunchKernelGGL((decode_partial<G, T, false, QW, WPB, WEIGHTED>), dim3(U * p.P), dim3(WPB * kWave), 0, s, p);
+    hipLaunchKernelGGL((decode_partial<G, T, false, QW, WPB, WEIGHTED, false>), dim3(U * p.P), dim3(WPB * kWave), 0,
+                       s, p);
   }
 }
 
@@ -895,7 +917,7 @@ hipError_t launch_g(const DecodeParams& p, int U, Shape sh, hipStream_t s) {
 }
 
 struct TaskCounts {
-  int n_tb, n_qt, tasks;
+  int n_tb, n_qt, n_sb, tasks;
 };
 
 TaskCounts task_counts(const kvc_decode_args& a, int qw) {
@@ -903,7 +925,8 @@ TaskCounts task_counts(const kvc_decode_args& a, int qw) {
   TaskCounts t;
   t.n_tb = (a.max_tail + has_new + kW - 1) / kW;
   t.n_qt = (a.max_int2 + qw - 1) / qw;
-  t.tasks = a.max_full + t.n_tb + t.n_qt;
+  t.n_sb = (a.max_summary + kW - 1) / kW;
+  t.tasks = a.max_full + t.n_tb + t.n_qt + t.n_sb;
   return t;
 }
 
@@ -1000,6 +1023,12 @@ hipError_t launch_decode(const kvc_cache& c, const kvc_decode_args& a, void* ws,
   const TaskCounts tc = task_counts(a, sh.qw);
   p.n_tb = tc.n_tb;
   p.n_qt = tc.n_qt;
+  p.n_sb = tc.n_sb;
+  p.k_sum = static_cast<const uint16_t*>(c.k_sum);
+  p.v_sum = static_cast<const uint16_t*>(c.v_sum);
+  p.n_sum = c.n_sum;
+  p.SM = c.sum_max;
+  p.max_sum = a.max_summary;
   p.P = decode_slices(c, a);
   p.CB = combine_blocks(c, p.P);
   if (p.P > kMaxParts) return hipErrorInvalidValue;

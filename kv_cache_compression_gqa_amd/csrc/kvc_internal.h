@@ -122,5 +122,7 @@ hipError_t launch_two_stage(const kvc_two_stage_args& a, hipStream_t s);
 size_t paged_workspace_bytes(const kvc_paged_decode_args& a);
 hipError_t launch_paged_decode(const kvc_paged_decode_args& a, void* ws, hipStream_t s);
 hipError_t launch_diagnostics(const kvc_diag_args& a, hipStream_t s);
+size_t summarize_workspace_bytes(const kvc_cache& c);
+hipError_t launch_summarize(const kvc_cache& c, const int8_t* tier_prev, int32_t max_new, void* ws, hipStream_t s);
 
 }  // namespace kvc

@@ -36,10 +36,11 @@ class DecodeSession:
     draw while every unit keeps memory and state of its own."""
 
     def __init__(self, inp: DecodeInputs, device="cuda", tail_max: int | None = None, steps: int | None = None,
-                 budgets=None, unit_map=None, score_schedule: str = "every"):
+                 budgets=None, unit_map=None, score_schedule: str = "every", summaries: bool = False):
         """``score_schedule``: "every" adds every step's window mass to the cumulative score; "event" adds it only
         at the steps that end with a routing event (attention is then materialised for scoring only when the
-        routing needs it, and the steps in between are plain decode steps)."""
+        routing needs it, and the steps in between are plain decode steps). ``summaries``: every evicted window
+        leaves a span summary (mean key and value) that later steps attend with a ln 32 size correction."""
         if score_schedule not in ("every", "event"):
             raise ValueError(score_schedule)
         self.score_schedule = score_schedule
@@ -91,6 +92,18 @@ class DecodeSession:
         self.n_full = _dev(n_windows_u.astype(np.int32), torch.int32, dev)
         self.n_int2 = torch.zeros(U, dtype=torch.int32, device=dev)
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+        # span summaries of evicted windows (every window is evicted at most once)
+        self.summaries = summaries
+        self.SM = ((NW + W - 1) // W) * W if summaries else 0
+        if summaries:
+            self.k_sum = torch.zeros((U, self.SM, D), dtype=torch.int16, device=dev)
+            self.v_sum = torch.zeros((U, self.SM // W, D, W), dtype=torch.int16, device=dev)
+            self.n_sum = torch.zeros(U, dtype=torch.int32, device=dev)
+            self.tier_prev = torch.empty((U, NW), dtype=torch.int8, device=dev)
+        else:
+            self.k_sum = self.v_sum = self.n_sum = self.tier_prev = None
+        self.h_sum = np.zeros(U, np.int64)
+        self._sum_ws = None
         # per-step inputs
         self.q = expand_steps(_bits(inp.q, dev))
         self.k_new = expand_steps(_bits(inp.k_new, dev))
@@ -122,7 +135,8 @@ class DecodeSession:
             v_meta=abi.ptr(self.v_meta), k_tail=abi.ptr(self.k_tail), v_tail=abi.ptr(self.v_tail),
             tail_len=abi.ptr(self.tail_len), tier=abi.ptr(self.tier), ledgered=abi.ptr(self.ledgered),
             cum=abi.ptr(self.cum), res_list=abi.ptr(self.res_list), n_full=abi.ptr(self.n_full),
-            n_int2=abi.ptr(self.n_int2), status=abi.ptr(self.status))
+            n_int2=abi.ptr(self.n_int2), status=abi.ptr(self.status), k_sum=abi.ptr(self.k_sum),
+            v_sum=abi.ptr(self.v_sum), n_sum=abi.ptr(self.n_sum), sum_max=self.SM, reserved2=0)
         self._ws = None
         self._ws_bytes = 0
         self.token_weight = None  # default per-position weights of the window score (step(token_weight=...))
@@ -147,7 +161,8 @@ class DecodeSession:
             probs=abi.ptr(probs), mass=abi.ptr(mass),
             probs_stride=0 if probs is None else int(probs.shape[-1]),
             accumulate_cum=1 if accumulate else 0, max_full=mf, max_int2=mq, max_tail=mt, reserved=0,
-            token_weight=abi.ptr(token_weight), weight_stride=0 if token_weight is None else int(token_weight.stride(1)))
+            token_weight=abi.ptr(token_weight), weight_stride=0 if token_weight is None else int(token_weight.stride(1)),
+            max_summary=int(self.h_sum.max()) if self.summaries else 0, reserved2=0)
         if token_weight is not None:
             assert token_weight.dtype == torch.float32 and token_weight.stride(2) == 1
             assert token_weight.shape[:2] == (self.U, self.G) and token_weight.stride(0) == self.G * token_weight.stride(1)
@@ -203,6 +218,8 @@ class DecodeSession:
     def route(self, scores=None, stream=None):
         L = abi.lib()
         sh = abi.stream_handle(stream)
+        if self.summaries:
+            self.tier_prev.copy_(self.tier)
         ra = abi.KvcTierRouteArgs(
             cache=C.pointer(self._cache), scores=abi.ptr(scores), budget_full=abi.ptr(self.budget_full),
             budget_int2=abi.ptr(self.budget_int2), quant_list=abi.ptr(self.quant_list), n_quant=abi.ptr(self.n_quant),
@@ -220,6 +237,17 @@ class DecodeSession:
         new_full = np.minimum(self.bf_host, n_res)
         new_int2 = np.minimum(self.bq_host, n_res - new_full)
         self.h_full, self.h_int2 = new_full.astype(np.int64), new_int2.astype(np.int64)
+        evicted = n_res - (new_full + new_int2)
+        if self.summaries and int(evicted.max()) > 0:
+            if self._sum_ws is None:
+                need = L.kvc_summarize_workspace(C.byref(self._cache))
+                if need == 0:
+                    raise abi.KvcError(abi.KVC_E_INVALID, "kvc_summarize_workspace")
+                self._sum_ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+            abi.check(L.kvc_summarize_evicted(C.byref(self._cache), abi.ptr(self.tier_prev), int(evicted.max()),
+                                              abi.ptr(self._sum_ws), self._sum_ws.numel(), sh),
+                      "kvc_summarize_evicted")
+            self.h_sum = self.h_sum + evicted
 
     def device_status(self, clear=True, stream=None) -> int:
         st = C.c_int32(0)

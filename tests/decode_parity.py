@@ -40,7 +40,7 @@ def row_check(name, g, r, rtol=RTOL):
         assert err <= lim, f"{name} head {h}: max err {err} > {lim}"
 
 
-def make_oracles(inp, units=None, unit_map=None):
+def make_oracles(inp, units=None, unit_map=None, summaries=False):
     """Oracle units keyed by session unit j (held unit unit_map[j] of ``inp``)."""
     umap = np.arange(len(inp.units)) if unit_map is None else np.asarray(unit_map)
     out = {}
@@ -49,7 +49,7 @@ def make_oracles(inp, units=None, unit_map=None):
         nw = int(inp.n_windows[b])
         t0 = int(inp.tail0[b])
         out[j] = QEvictUnit(inp.k_win[b, :nw], inp.v_win[b, :nw], inp.k_tail0[b, :t0], inp.v_tail0[b, :t0],
-                            inp.cfg.dtype)
+                            inp.cfg.dtype, summaries=summaries)
     return out
 
 
@@ -89,10 +89,21 @@ def compare_route(sess: DecodeSession, oracles, gpu_cum):
         for w in full:
             assert kw[r, w].tobytes() == o.kw[w].tobytes(), f"K full copy unit {j} window {w}"
             assert layout.v_win_from_lib(vw[r, w]).tobytes() == o.vw[w].tobytes(), f"V full copy unit {j} window {w}"
+    if sess.summaries:
+        ns, ks, vs = g(sess.n_sum), g(sess.k_sum).view(np.uint16), g(sess.v_sum).view(np.uint16)
+        for r, j in enumerate(keys):
+            o = oracles[j]
+            assert ns[r] == len(o.sum_k), f"summary count unit {j}: {ns[r]} vs {len(o.sum_k)}"
+            vrows = ks.shape[1]
+            vsum = vs[r].transpose(0, 2, 1).reshape(vrows, -1)   # [SM/32][D][32] -> [SM][D]
+            for i in range(len(o.sum_k)):
+                assert ks[r, i].tobytes() == o.sum_k[i].tobytes(), f"K summary {i} unit {j}"
+                assert vsum[i].tobytes() == o.sum_v[i].tobytes(), f"V summary {i} unit {j}"
 
 
 def run_decode_parity(cfg, units=None, steps=None, check_units=None, check_steps=None, probs=True, log=print,
-                      inp=None, unit_map=None, score_schedule="every", token_weight=None, oracle_weight=None):
+                      inp=None, unit_map=None, score_schedule="every", token_weight=None, oracle_weight=None,
+                      summaries=False):
     """Run ``steps`` decode steps (routing on the workload's cadence) on the GPU for every unit, and on the oracle
     for the units in ``check_units`` (default all; units are independent, so a sample of them is followed exactly).
     ``score_schedule`` "event" adds the window mass to the cumulative score only at routing-event steps.
@@ -103,10 +114,10 @@ def run_decode_parity(cfg, units=None, steps=None, check_units=None, check_steps
     if inp is None:
         inp = synth.make_decode(cfg, units=units, steps=steps)
     S = inp.q.shape[0]
-    sess = DecodeSession(inp, unit_map=unit_map, score_schedule=score_schedule)
+    sess = DecodeSession(inp, unit_map=unit_map, score_schedule=score_schedule, summaries=summaries)
     U = sess.U
     umap = sess.unit_map
-    oracles = make_oracles(inp, check_units, unit_map)
+    oracles = make_oracles(inp, check_units, unit_map, summaries=summaries)
     check_steps = set(range(S)) if check_steps is None else set(check_steps)
     for t in range(S):
         stride = sess.probs_stride()

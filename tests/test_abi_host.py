@@ -24,13 +24,13 @@ def test_every_declared_symbol_is_exported_and_bound():
     for n in names:
         assert hasattr(L, n), n
         assert n in abi.SIGNATURES, n
-    assert L.kvc_abi_version() == 2
+    assert L.kvc_abi_version() == 3
 
 
 def test_struct_sizes_match_header_layout():
-    # 8 int32 + 17 pointers
-    assert C.sizeof(abi.KvcCache) == 8 * 4 + 17 * 8
-    assert C.sizeof(abi.KvcDecodeArgs) == 6 * 8 + 6 * 4 + 2 * 8
+    # 8 int32 + 17 pointers, then 3 pointers + 2 int32 for the span summaries
+    assert C.sizeof(abi.KvcCache) == 8 * 4 + 17 * 8 + 3 * 8 + 2 * 4
+    assert C.sizeof(abi.KvcDecodeArgs) == 6 * 8 + 6 * 4 + 2 * 8 + 2 * 4
     assert C.sizeof(abi.KvcTierRouteArgs) == 8 * 8
 
 
@@ -48,6 +48,7 @@ def good_cache(**over):
               reserved=0)
     for f, _ in abi.KvcCache._fields_[8:]:
         kw[f] = FAKE
+    kw.update(k_sum=None, v_sum=None, n_sum=None, sum_max=0, reserved2=0)   # no span summaries
     kw.update(over)
     return abi.KvcCache(**kw)
 

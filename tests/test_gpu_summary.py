@@ -1,0 +1,72 @@
+"""GPU parity of the span-summary term (SEKV's mixed-resolution attention, untrained reading): every evicted window
+leaves the means of its keys and values, attended after the tail with a ln 32 size correction (needs an MI355X).
+
+Bars: summaries byte-exact (both sides round the exact mean to fp32 and then to the storage dtype); outputs, window
+masses and cumulative scores as for the plain decode (2e-3); tiers and lists bit-exact on the GPU's scores.
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_compression_gqa_amd import abi, configs, synth
+from kv_cache_compression_gqa_amd.session import DecodeSession
+from tests.decode_parity import run_decode_parity
+
+pytestmark = pytest.mark.gpu
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_summaries_tiny(gpu_lib, dtype):
+    log(f"case: span summaries, tiny workload, {dtype}, 12 steps")
+    cfg = dataclasses.replace(configs.TINY, dtype=dtype)
+    sess, oracles = run_decode_parity(cfg, steps=12, probs=False, summaries=True, log=log)
+    assert int(sess.n_sum.max().item()) == 16   # the first event evicts 16 windows per unit, later ones none
+
+
+def test_summaries_2k_context_g8_and_g1(gpu_lib):
+    for hq, hkv in ((64, 8), (8, 8)):
+        cfg = dataclasses.replace(configs.LLAMA3_8B_LAYER_32K, name=f"ctx2k_g{hq // hkv}", hq=hq, hkv=hkv,
+                                  context=2048 + 40, steps=12, route_every=4)
+        log(f"case: span summaries, {cfg.name}, {hkv} units")
+        run_decode_parity(cfg, probs=False, summaries=True, log=log)
+
+
+def test_summaries_many_units(gpu_lib):
+    """1280 units (the many-round launch shape: two INT2 windows per task, 4-wave workgroups)."""
+    cfg = dataclasses.replace(configs.TINY, name="many_sum", seed=14, hq=16, hkv=2, dtype="f16", layers=32,
+                              batch=20, context=640, n_salient=5, budget_full=4, budget_int2=7, steps=4,
+                              route_every=2)
+    inp, umap = synth.make_decode_shared_layers(cfg)
+    log(f"case: span summaries, {cfg.n_units} units")
+    run_decode_parity(cfg, inp=inp, unit_map=umap, check_units=[0, 333, 777, cfg.n_units - 1], probs=False,
+                      summaries=True, log=log)
+
+
+def test_summaries_reject_probabilities_and_over_capacity(gpu_lib):
+    cfg = configs.TINY
+    inp = synth.make_decode(cfg, steps=6)
+    sess = DecodeSession(inp, summaries=True)
+    for _ in range(4):
+        sess.step()
+    assert int(sess.h_sum.max()) > 0
+    import ctypes as C
+    pr = torch.zeros((sess.U, sess.G, sess.probs_stride()), dtype=torch.float32, device="cuda")
+    args = sess.decode_args(sess.t, probs=pr)
+    ws = sess.workspace(sess.decode_args(sess.t))
+    L = abi.lib()
+    st = L.kvc_decode_attn(C.byref(sess._cache), C.byref(args), abi.ptr(ws), ws.numel(), None)
+    assert st == abi.KVC_E_UNSUPPORTED            # summaries are attended without probabilities only
+    assert L.kvc_decode_attn_workspace(C.byref(sess._cache), C.byref(args)) == 0
+    args = sess.decode_args(sess.t)
+    args.max_summary = sess.SM + 32                # past the capacity
+    st = L.kvc_decode_attn(C.byref(sess._cache), C.byref(args), abi.ptr(ws), ws.numel(), None)
+    assert st == abi.KVC_E_BUDGET
+    assert sess.device_status() == 0
