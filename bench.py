@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch steps eagerly instead of one captured graph")
+    ap.add_argument("--summaries", action="store_true",
+                    help="32K layer: evicted windows leave span summaries attended with a ln 32 size correction")
     ap.add_argument("--weighted", action="store_true",
                     help="32K layer: weight the window score by CriticalKV's |V W_O|_1 (norms from kvc_score)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -62,6 +64,8 @@ def step_bytes_and_tokens(sess, W=32, D=128):
     per_unit = tok_full * 2 * D * 2 + tok_int2 * 2 * (D // 4 + (D // 32) * 4) + tok_tail * 2 * D * 2 + G * D * 2
     if sess.token_weight is not None:  # one fp32 weight per (window token, head)
         per_unit += (tok_full + tok_int2) * G * 4
+    if sess.summaries:  # one key and one value row per summary
+        per_unit += int(sess.h_sum.max()) * 2 * D * 2
     positions = tok_full + tok_int2 + tok_tail
     return U * per_unit, positions
 
@@ -196,7 +200,7 @@ def main():
         w_o, q_obs = _criticalkv_projection(cfg)
     for r in range(R):
         inp = synth.make_decode(dataclasses.replace(cfg, seed=cfg.seed * 1000 + r), steps=per_rep)
-        s = DecodeSession(inp, tail_max=per_rep + 1)
+        s = DecodeSession(inp, tail_max=per_rep + 1, summaries=args.summaries)
         s.reserve_workspace(per_rep)
         if args.weighted:
             s.token_weight = _projected_value_norms(s, inp, w_o, q_obs)
@@ -300,7 +304,8 @@ def main():
     avg_kern_s = float(np.mean(kern_ms)) * 1e-3
     avg_bytes = sum(b for b, _ in kern_plan) / K
     achieved = avg_bytes / avg_kern_s / 1e9
-    traffic = None if args.weighted else traffic_from_profile()  # the counters were taken unweighted
+    # the counters were taken on the plain step
+    traffic = None if (args.weighted or args.summaries) else traffic_from_profile()
     rec = {
         "metric": "KV tokens scored+routed+attended/s per decode step; % of HBM roofline",
         "value": total_pos / wall,
@@ -312,6 +317,7 @@ def main():
                    "route_every": cfg.route_every, "phase": "routed steady state", "replicas": R,
                    "window_score": "attention mass x |V W_O|_1 (CriticalKV norms)" if args.weighted else
                    "attention mass",
+                   "evicted_windows": "span summaries (mean key/value, logit + ln 32)" if args.summaries else "dropped",
                    "launch": "eager" if graph is None else "hip graph",
                    "full_cache_phase_ms_per_step": full_ms,
                    "full_cache_phase_bytes_per_step": full_plan[0][0],
@@ -324,7 +330,7 @@ def main():
                      "avg_launch_us": avg_kern_s * 1e6,
                      "algorithmic_bytes_per_launch": avg_bytes},
     }
-    if not args.no_cpu_baseline and not args.weighted:
+    if not args.no_cpu_baseline and not args.weighted and not args.summaries:
         print("timing the CPU oracle sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(rec), flush=True)

@@ -552,6 +552,9 @@ __global__ __launch_bounds__(WPB * kWave) __attribute__((amdgpu_waves_per_eu(4))
     const int ridx = min(max(task >= t_full ? f : MF + q0 + lane - 3, 0), p.NW - 1);
     const int32_t* cnt = lane == 0 ? p.n_full : (lane == 1 ? p.n_int2 : p.tail_len);
     const int32_t* gp = lane < 3 ? cnt + u : res + ridx;
+    if constexpr (SUMMARY) {  // a summary-block task takes the unit's summary count in lane 3
+      if (task >= t_sum && task < t_full && lane == 3) gp = p.n_sum + u;
+    }
     gv = *gp;
   }
   int sid[QW];
@@ -619,7 +622,7 @@ __global__ __launch_bounds__(WPB * kWave) __attribute__((amdgpu_waves_per_eu(4))
   } else if (SUMMARY && task < t_full) {
     if constexpr (SUMMARY) {
       const int blk = task - t_sum;
-      const int ns_dev = p.n_sum[u];
+      const int ns_dev = __builtin_amdgcn_readlane(gv, 3);
       const int ns = min(max(ns_dev, 0), p.max_sum);
       if (blk == 0 && lane == 0 && ns != ns_dev) atomicOr(p.status, KVC_DEV_BOUND_EXCEEDED);
       if (kW * blk < ns) dense_task<G, T, false, true, WEIGHTED, true>(p, c, 0, blk, min(kW, ns - kW * blk), 0, aq, plds, wo);
