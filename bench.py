@@ -169,8 +169,8 @@ def _projected_value_norms(sess, inp, w_o, q_obs):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
-              "(the per-unit work shards with no exchange; see the design notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (every (batch, layer, KV head) "
+              "unit is independent, so units would shard over GPUs with no exchange)", file=sys.stderr)
         sys.exit(2)
     if args.workload == "criticalkv_64k":
         return bench_criticalkv(args)
