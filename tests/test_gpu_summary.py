@@ -70,3 +70,16 @@ def test_summaries_reject_probabilities_and_over_capacity(gpu_lib):
     st = L.kvc_decode_attn(C.byref(sess._cache), C.byref(args), abi.ptr(ws), ws.numel(), None)
     assert st == abi.KVC_E_BUDGET
     assert sess.device_status() == 0
+
+
+def test_summaries_with_weighted_score_and_event_schedule(gpu_lib):
+    """Every option of the step at once: span summaries, the weighted window score and the event-only schedule
+    (the weighted + summary kernel instantiation), with a tail that grows past one 32-token block."""
+    cfg = dataclasses.replace(configs.TINY, name="tiny_all", steps=40, route_every=8, context=1024 + 20)
+    log("case: summaries + weighted score + event schedule, tiny workload, 40 steps")
+    inp = synth.make_decode(cfg)
+    U, NW = len(inp.units), inp.n_windows_max
+    G = cfg.hq // cfg.hkv
+    w = np.random.default_rng(21).lognormal(size=(U, G, NW * cfg.window)).astype(np.float32)
+    run_decode_parity(cfg, inp=inp, token_weight=torch.from_numpy(w).cuda(), oracle_weight=w.astype(np.float64),
+                      score_schedule="event", summaries=True, probs=False, log=log)
