@@ -954,9 +954,11 @@ Shape decode_shape(const kvc_cache& c, const kvc_decode_args& a) {
 }
 
 int combine_blocks(const kvc_cache& c, int P) {
-  // partial groups so that a thread holds at most kPre partials, output elements E = 256 / PG (at most G*D)
+  // partial groups so that a thread holds at most kPre partials, output elements E = 256 / PG (at most G*D); at
+  // most 16 groups, so that a workgroup reads at least 16 consecutive floats (64 bytes) of every partial row:
+  // with many partials (the full-cache phase), 4-element slices pulled whole 128-byte lines for 16 bytes
   int pg = 1;
-  while (pg < 256 && pg * kPre < P) pg *= 2;
+  while (pg < 16 && pg * kPre < P) pg *= 2;
   int E = min(256 / pg, c.group * kD);
   int cb = c.group * kD / E;
   // many units: fewer, fuller workgroups (about four per CU in all); a thread then takes more partials, the ones
