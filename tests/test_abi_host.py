@@ -199,3 +199,43 @@ def test_route_diagnostics_validation_rejects_before_launch():
     assert L.kvc_route_diagnostics(C.byref(args(counts=None)), None) == abi.KVC_E_INVALID
     assert L.kvc_route_diagnostics(C.byref(args(values=None)), None) == abi.KVC_E_INVALID
     assert L.kvc_route_diagnostics(C.byref(args(mass_full=FAKE + 2)), None) == abi.KVC_E_INVALID
+
+
+def test_summary_validation_rejects_before_launch():
+    L = abi.lib()
+    # the cache's summary fields: all or nothing, capacity a multiple of 32
+    assert L.kvc_decode_attn_workspace(C.byref(good_cache(k_sum=FAKE)), C.byref(good_step())) == 0
+    assert L.kvc_decode_attn_workspace(C.byref(good_cache(sum_max=32)), C.byref(good_step())) == 0
+    assert L.kvc_decode_attn_workspace(C.byref(good_cache(reserved2=1)), C.byref(good_step())) == 0
+    with_sum = dict(k_sum=FAKE, v_sum=FAKE, n_sum=FAKE, sum_max=64)
+    assert L.kvc_decode_attn_workspace(C.byref(good_cache(**with_sum, )), C.byref(good_step())) > 0
+    assert L.kvc_decode_attn_workspace(C.byref(good_cache(k_sum=FAKE, v_sum=FAKE, n_sum=FAKE, sum_max=48)),
+                                       C.byref(good_step())) == 0
+    # a step that attends summaries needs them in the cache, within the capacity, and no probabilities
+    c, s = good_cache(), good_step(max_summary=32)
+    assert L.kvc_decode_attn(C.byref(c), C.byref(s), FAKE, 1 << 30, None) == abi.KVC_E_BUDGET
+    c, s = good_cache(**with_sum), good_step(max_summary=96)
+    assert L.kvc_decode_attn(C.byref(c), C.byref(s), FAKE, 1 << 30, None) == abi.KVC_E_BUDGET
+    s = good_step(max_summary=32, probs=FAKE, probs_stride=1024)
+    assert L.kvc_decode_attn(C.byref(c), C.byref(s), FAKE, 1 << 30, None) == abi.KVC_E_UNSUPPORTED
+    s = good_step(max_summary=-1)
+    assert L.kvc_decode_attn(C.byref(c), C.byref(s), FAKE, 1 << 30, None) == abi.KVC_E_INVALID
+    # kvc_summarize_evicted
+    need = L.kvc_summarize_workspace(C.byref(c))
+    assert need > 0 and L.kvc_summarize_workspace(None) == 0
+    assert L.kvc_summarize_evicted(None, FAKE, 1, FAKE, need, None) == abi.KVC_E_INVALID
+    assert L.kvc_summarize_evicted(C.byref(good_cache()), FAKE, 1, FAKE, need, None) == abi.KVC_E_INVALID
+    assert L.kvc_summarize_evicted(C.byref(c), None, 1, FAKE, need, None) == abi.KVC_E_INVALID
+    assert L.kvc_summarize_evicted(C.byref(c), FAKE, 33, FAKE, need, None) == abi.KVC_E_INVALID   # > NW
+    assert L.kvc_summarize_evicted(C.byref(c), FAKE, -1, FAKE, need, None) == abi.KVC_E_INVALID
+    assert L.kvc_summarize_evicted(C.byref(c), FAKE, 1, FAKE, need - 1, None) == abi.KVC_E_WORKSPACE
+    assert L.kvc_summarize_evicted(C.byref(c), FAKE, 1, FAKE + 16, need, None) == abi.KVC_E_WORKSPACE
+
+
+def test_token_weight_validation_rejects_before_launch():
+    L = abi.lib()
+    c = good_cache()
+    s = good_step(token_weight=FAKE, weight_stride=32 * 32 - 1)   # below n_windows_max * W
+    assert L.kvc_decode_attn(C.byref(c), C.byref(s), FAKE, 1 << 30, None) == abi.KVC_E_INVALID
+    s = good_step(token_weight=FAKE + 2, weight_stride=32 * 32)
+    assert L.kvc_decode_attn(C.byref(c), C.byref(s), FAKE, 1 << 30, None) == abi.KVC_E_INVALID
