@@ -11,8 +11,8 @@
  *     launches nothing.
  *   - All pointers are DEVICE pointers unless a field says "host". The caller allocates and owns every buffer,
  *     workspaces included (sizes from the *_workspace queries). The library allocates no device memory, keeps
- *     no pointer after a call returns and has no global state; buffers must stay valid until the stream has
- *     executed the work.
+ *     no pointer after a call returns and has no global state beyond a per-device cache of the compute-unit
+ *     count; buffers must stay valid until the stream has executed the work.
  *   - Work is enqueued on the given stream (0 = the default stream); nothing synchronises and nothing is
  *     copied device->host, so sequences of calls can be captured in a HIP graph.
  *   - Results are bitwise reproducible run to run (no floating-point atomics; fixed combine order).

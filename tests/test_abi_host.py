@@ -239,3 +239,26 @@ def test_token_weight_validation_rejects_before_launch():
     assert L.kvc_decode_attn(C.byref(c), C.byref(s), FAKE, 1 << 30, None) == abi.KVC_E_INVALID
     s = good_step(token_weight=FAKE + 2, weight_stride=32 * 32)
     assert L.kvc_decode_attn(C.byref(c), C.byref(s), FAKE, 1 << 30, None) == abi.KVC_E_INVALID
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/kvc.h compiles as C99 with warnings as errors, and a C program links against the library and sees
+    the same ABI version the header states."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "kvc_check.c"
+    src.write_text('#include "kvc.h"\n'
+                   "int main(void) {\n"
+                   "  kvc_cache c; kvc_decode_args a; kvc_diag_args d; (void)c; (void)a; (void)d;\n"
+                   "  return kvc_abi_version() == KVC_ABI_VERSION ? 0 : 1;\n"
+                   "}\n")
+    lib_dir = os.path.dirname(abi.lib_path())
+    exe = tmp_path / "kvc_check"
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                        "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", str(src), "-L", lib_dir,
+                        "-lkvc", f"-Wl,-rpath,{lib_dir}", "-o", str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    assert subprocess.run([str(exe)]).returncode == 0
