@@ -332,7 +332,7 @@ def main():
     }
     if not args.no_cpu_baseline and not args.weighted and not args.summaries:
         print("timing the CPU oracle sample", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(cfg)
+        rec["cpu_baseline"] = _with_host(cpu_baseline(cfg))
     print(json.dumps(rec), flush=True)
 
 
@@ -415,7 +415,42 @@ def bench_batched(args):
                      "kernel": "kvc_decode_attn (decode_partial + decode_combine)", "avg_launch_us": avg_s * 1e6,
                      "algorithmic_bytes_per_launch": avg_bytes},
     }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = _with_host(cpu_baseline_batched(cfg))
     print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline_batched(cfg, min_seconds=10.0, n_units=32):
+    """The oracle on a sample of the batched workload's units (seeded draws at the workload's sequence lengths):
+    each unit's first decode step over its full cache and routing, then routed steps with routing every step,
+    one step of every sampled unit per round, until ``min_seconds`` have passed."""
+    sys.path.insert(0, ROOT)
+    from kv_cache_compression_gqa_amd import synth
+    from oracle.qevict import QEvictUnit
+    units = list(range(0, cfg.n_units, max(1, cfg.n_units // n_units)))[:n_units]
+    max_rounds = 256
+    inp = synth.make_decode(cfg, units=units, steps=1 + max_rounds)
+    ors = []
+    for j in range(len(units)):
+        nw, t0 = int(inp.n_windows[j]), int(inp.tail0[j])
+        o = QEvictUnit(inp.k_win[j, :nw], inp.v_win[j, :nw], inp.k_tail0[j, :t0], inp.v_tail0[j, :t0], cfg.dtype)
+        o.step(inp.q[0, j], inp.k_new[0, j], inp.v_new[0, j])
+        o.route(*cfg.budgets(nw))
+        ors.append(o)
+    tokens, rounds = 0.0, 0
+    t0 = time.perf_counter()
+    while rounds < max_rounds and time.perf_counter() - t0 < min_seconds:
+        t = 1 + rounds
+        for j, o in enumerate(ors):
+            r = o.step(inp.q[t, j], inp.k_new[t, j], inp.v_new[t, j])
+            tokens += r.p.shape[1] / cfg.hkv
+            o.route(*cfg.budgets(o.n_windows))
+        rounds += 1
+    el = time.perf_counter() - t0
+    return {"value": tokens / el, "unit": "KV tokens/s", "cores": _oracle_threads(), "kind": "oracle",
+            "sample": f"{len(units)} of {cfg.n_units} units (spread over layers, sequences and heads), {rounds} routed "
+                      f"steps each with routing every step after an untimed full-cache step; fp64 numpy oracle; "
+                      f"{el:.1f} s"}
 
 
 def _timed_calls(fn, K, W):
@@ -474,7 +509,7 @@ def bench_criticalkv(args):
                      "avg_launch_us": avg_s * 1e6, "algorithmic_flops_per_launch": flops_n + flops_a},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline_criticalkv(cfg, inp)
+        rec["cpu_baseline"] = _with_host(cpu_baseline_criticalkv(cfg, inp))
     print(json.dumps(rec), flush=True)
 
 
@@ -568,7 +603,7 @@ def bench_dbtrim(args):
                      "algorithmic_bytes_per_launch": comp_bytes},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline_dbtrim(cfg)
+        rec["cpu_baseline"] = _with_host(cpu_baseline_dbtrim(cfg))
     print(json.dumps(rec), flush=True)
 
 
@@ -630,7 +665,7 @@ def bench_paged_decode(args):
                      "avg_launch_us": launch_s * 1e6, "algorithmic_bytes_per_launch": nbytes},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline_paged(cfg, G)
+        rec["cpu_baseline"] = _with_host(cpu_baseline_paged(cfg, G))
     print(json.dumps(rec), flush=True)
 
 
@@ -743,7 +778,7 @@ def bench_diagnostics(args):
                      "avg_launch_us": call_s * 1e6, "algorithmic_bytes_per_launch": nbytes},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline_diagnostics(U, NW, G)
+        rec["cpu_baseline"] = _with_host(cpu_baseline_diagnostics(U, NW, G))
     print(json.dumps(rec), flush=True)
 
 
@@ -791,6 +826,20 @@ def cpu_baseline_dbtrim(cfg, layers=16):
     return {"value": beta.size / el, "unit": "KV entries/s", "cores": threads, "kind": "oracle",
             "sample": f"{layers} of {cfg.layers} layers ({beta.size} entries, M = 10%): fp64 numpy oracle scores, "
                       f"top-M, compaction plan and K/V row gather; {el:.1f} s"}
+
+
+def _with_host(rec):
+    """Adds the host CPU model (first "model name" of /proc/cpuinfo) to a CPU-baseline record."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    rec["cpu_model"] = model
+    return rec
 
 
 def _oracle_threads():
