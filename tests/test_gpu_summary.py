@@ -83,3 +83,13 @@ def test_summaries_with_weighted_score_and_event_schedule(gpu_lib):
     w = np.random.default_rng(21).lognormal(size=(U, G, NW * cfg.window)).astype(np.float32)
     run_decode_parity(cfg, inp=inp, token_weight=torch.from_numpy(w).cuda(), oracle_weight=w.astype(np.float64),
                       score_schedule="event", summaries=True, probs=False, log=log)
+
+
+def test_summaries_llama_layer_32k(gpu_lib):
+    """The 32K layer at full size (8 KV-head units, 1024 windows each) with span summaries, through its first
+    routing event (513 summaries per unit) and four summary-attending steps; the oracle follows units 0 and 5."""
+    cfg = dataclasses.replace(configs.LLAMA3_8B_LAYER_32K, steps=20)
+    log("case: span summaries, llama3_8b_layer_ctx32k_bf16, 20 steps, oracle on units 0 and 5")
+    sess, _ = run_decode_parity(cfg, check_units=[0, 5], check_steps=[0, 15, 16, 17, 19], probs=False,
+                                summaries=True, log=log)
+    assert int(sess.n_sum.min().item()) == 513

@@ -77,3 +77,16 @@ def test_criticalkv_norms_weight_the_window_score(gpu_lib):
     got = norm.cpu().numpy()
     assert np.all(np.abs(got - ref) <= 2e-3 * np.abs(ref) + 1e-12)
     run_decode_parity(cfg, inp=inp, token_weight=norm, oracle_weight=ref, log=log)
+
+
+def test_weighted_score_llama_layer_32k(gpu_lib):
+    """The 32K layer at full size with log-normal per-position weights in the window score, through the first
+    routing event; the oracle follows units 0 and 5."""
+    cfg = dataclasses.replace(configs.LLAMA3_8B_LAYER_32K, steps=20)
+    log("case: weighted window score, llama3_8b_layer_ctx32k_bf16, 20 steps, oracle on units 0 and 5")
+    inp = synth.make_decode(cfg)
+    U, NW = len(inp.units), inp.n_windows_max
+    G = cfg.hq // cfg.hkv
+    w = np.random.default_rng(23).lognormal(size=(U, G, NW * cfg.window)).astype(np.float32)
+    run_decode_parity(cfg, inp=inp, token_weight=torch.from_numpy(w).cuda(), oracle_weight=w.astype(np.float64),
+                      check_units=[0, 5], check_steps=[0, 15, 16, 19], probs=False, log=log)
