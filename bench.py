@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch steps eagerly instead of one captured graph")
+    ap.add_argument("--event-schedule", action="store_true",
+                    help="32K layer: add the window mass to the scores only at routing-event steps (plain decode "
+                         "steps in between)")
     ap.add_argument("--summaries", action="store_true",
                     help="32K layer: evicted windows leave span summaries attended with a ln 32 size correction")
     ap.add_argument("--weighted", action="store_true",
@@ -200,7 +203,8 @@ def main():
         w_o, q_obs = _criticalkv_projection(cfg)
     for r in range(R):
         inp = synth.make_decode(dataclasses.replace(cfg, seed=cfg.seed * 1000 + r), steps=per_rep)
-        s = DecodeSession(inp, tail_max=per_rep + 1, summaries=args.summaries)
+        s = DecodeSession(inp, tail_max=per_rep + 1, summaries=args.summaries,
+                          score_schedule="event" if args.event_schedule else "every")
         s.reserve_workspace(per_rep)
         if args.weighted:
             s.token_weight = _projected_value_norms(s, inp, w_o, q_obs)
@@ -305,7 +309,7 @@ def main():
     avg_bytes = sum(b for b, _ in kern_plan) / K
     achieved = avg_bytes / avg_kern_s / 1e9
     # the counters were taken on the plain step
-    traffic = None if (args.weighted or args.summaries) else traffic_from_profile()
+    traffic = None if (args.weighted or args.summaries or args.event_schedule) else traffic_from_profile()
     rec = {
         "metric": "KV tokens scored+routed+attended/s per decode step; % of HBM roofline",
         "value": total_pos / wall,
@@ -318,6 +322,7 @@ def main():
                    "window_score": "attention mass x |V W_O|_1 (CriticalKV norms)" if args.weighted else
                    "attention mass",
                    "evicted_windows": "span summaries (mean key/value, logit + ln 32)" if args.summaries else "dropped",
+                   "score_schedule": "routing events only" if args.event_schedule else "every step",
                    "launch": "eager" if graph is None else "hip graph",
                    "full_cache_phase_ms_per_step": full_ms,
                    "full_cache_phase_bytes_per_step": full_plan[0][0],
@@ -330,7 +335,7 @@ def main():
                      "avg_launch_us": avg_kern_s * 1e6,
                      "algorithmic_bytes_per_launch": avg_bytes},
     }
-    if not args.no_cpu_baseline and not args.weighted and not args.summaries:
+    if not args.no_cpu_baseline and not (args.weighted or args.summaries or args.event_schedule):
         print("timing the CPU oracle sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = _with_host(cpu_baseline(cfg))
     print(json.dumps(rec), flush=True)

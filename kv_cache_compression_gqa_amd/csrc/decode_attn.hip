@@ -89,6 +89,7 @@ struct DecodeParams {
   const uint16_t* v_sum;  // [U][SM/32][D][32]
   const int32_t* n_sum;   // [U]
   int SM, max_sum;        // capacity; host bound on n_sum (0: no summaries attended)
+  int score;              // 0: neither the cumulative score nor the window mass is asked for (a plain decode step)
   int n_sb;               // summary-block tasks per unit (bound)
 };
 
@@ -277,7 +278,7 @@ __device__ __forceinline__ void p_to_b(const Ctx& c, const f32x4 (&Pw)[2], float
 template <int G>
 __device__ __forceinline__ void store_window_sums(const DecodeParams& p, const Ctx& c, int id, const float (&ws)[4],
                                                   const float (&m)[4]) {
-  if (c.col != 0 || 4 * c.q >= G) return;
+  if (p.score == 0 || c.col != 0 || 4 * c.q >= G) return;  // a plain decode step keeps no window sums
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int h = 4 * c.q + r;
@@ -768,7 +769,7 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeParams p) {
   load_heads<G>(p.wref + (unit_win + w0c) * G, wr0);
   const float cum0 = p.cum[unit_win + w0c];
   const int nw = min(max(p.n_windows[u], 0), p.NW);
-  const int we = min(nw, wb + wpb);
+  const int we = p.score ? min(nw, wb + wpb) : wb;  // a plain decode step (no score, no mass) has no window pass
   // the append's loads (tail length, the new K row and V column), issued with the others
   const int has_new = p.k_new != nullptr ? 1 : 0;
   const int tl = p.unit_tl[u];
@@ -1022,6 +1023,7 @@ hipError_t launch_decode(const kvc_cache& c, const kvc_decode_args& a, void* ws,
   p.max_full = a.max_full;
   p.max_int2 = a.max_int2;
   p.max_tail = a.max_tail;
+  p.score = (a.accumulate_cum != 0 || a.mass != nullptr) ? 1 : 0;
   p.wnorm = a.token_weight;
   p.wstride = long(a.weight_stride);
   const Shape sh = decode_shape(c, a);

@@ -125,3 +125,34 @@ def test_route_diagnostics_match_oracle(gpu_lib):
             log(f"step {t + 1}: routed; counts match")
     assert saw_eviction
     assert sess.device_status() == 0 and shadow.device_status() == 0
+
+
+def test_event_schedule_plain_steps_skip_the_window_pass(gpu_lib):
+    """Event-only schedule with no mass asked for between events: those steps run as plain decode steps (no window
+    sums kept, no window pass in the combine); outputs still match the oracle at every step, and the cumulative
+    scores after each event step do too."""
+    from tests.decode_parity import make_oracles, row_check, rel_check
+    cfg = dataclasses.replace(configs.LLAMA3_8B_LAYER_32K, name="ctx2k", context=2048 + 9, steps=12, route_every=4)
+    log("case: event-only schedule with plain steps, 8 units at 2K")
+    inp = synth.make_decode(cfg)
+    sess = DecodeSession(inp, score_schedule="event")
+    oracles = make_oracles(inp)
+    for t in range(cfg.steps):
+        event = (t + 1) % cfg.route_every == 0
+        mass = torch.zeros((sess.U, sess.NW), dtype=torch.float32, device="cuda") if event else None
+        sess.step(mass=mass, route=False)
+        torch.cuda.synchronize()
+        out = sess.out.cpu().numpy()
+        cum = sess.cum.cpu().numpy()
+        for j, o in oracles.items():
+            r = o.step(inp.q[t, j], inp.k_new[t, j], inp.v_new[t, j], accumulate=event)
+            row_check(f"out step {t} unit {j}", out[j], r.o)
+            rel_check(f"cum step {t} unit {j}", cum[j, :o.n_windows], o.cum)
+            if event:
+                rel_check(f"mass step {t} unit {j}", mass.cpu().numpy()[j, :o.n_windows], r.mass)
+        if event:
+            gpu_cum = sess.cum.cpu().numpy().astype(np.float64)
+            sess.route()
+            torch.cuda.synchronize()
+            compare_route(sess, oracles, gpu_cum)
+    assert sess.device_status() == 0
