@@ -299,3 +299,15 @@ def test_batched_32_layers_batch_16_full_size(gpu_lib):
     print(f"batched: {cfg.n_units} units, lengths {sorted(set(inp.lengths.tolist()))[:3]}..", flush=True)
     check = [0, 9, 130, 1234, 2048 + 77, cfg.n_units - 1]
     run_decode_parity(cfg, inp=inp, unit_map=umap, check_units=check, probs=True)
+
+
+def test_one_round_launch_a_few_tasks_over(gpu_lib):
+    """64 units whose step has 4 tasks more than one round of 8-wave workgroups holds (8 per unit on a 256-CU
+    GPU): the launch spills a few workgroups into a second round. Without and with probabilities, against the
+    oracle."""
+    cfg = dataclasses.replace(configs.LLAMA3_8B_LAYER_32K, name="extra_tasks", layers=8, context=134 * 32 + 40,
+                              steps=8, route_every=4)
+    inp = synth.make_decode(cfg)
+    log(f"case: {cfg.name}, {cfg.n_units} units, probabilities off then on")
+    run_decode_parity(cfg, inp=inp, check_units=[0, 21, 63], probs=False, log=log)
+    run_decode_parity(cfg, inp=inp, check_units=[0, 63], probs=True, log=log)
