@@ -132,6 +132,26 @@ def cpu_baseline(cfg, min_seconds=10.0, max_steps=160):
                       f"of one 32K layer after an untimed full-cache phase; fp64 numpy oracle; {elapsed:.1f} s"}
 
 
+def _copy_probe_gbs(gib=2, reps=5):
+    """Context for the roofline: the HBM traffic (bytes read + written) of a plain device-to-device copy of a 2 GiB
+    buffer (far above the Infinity Cache) on this GPU, GB/s."""
+    import torch
+    x = torch.ones(gib << 30, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        y.copy_(x)
+    b.record()
+    torch.cuda.synchronize()
+    gbs = 2 * x.numel() * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del x, y
+    torch.cuda.empty_cache()
+    return gbs
+
+
 def _calibration_copy(mib):
     """One plain device-to-device copy of ``mib`` MiB (the reference kernel for scaling the HBM counters)."""
     import torch
@@ -335,6 +355,7 @@ def main():
                      "avg_launch_us": avg_kern_s * 1e6,
                      "algorithmic_bytes_per_launch": avg_bytes},
     }
+    rec["hbm_copy_probe_gbs"] = _copy_probe_gbs()
     if not args.no_cpu_baseline and not (args.weighted or args.summaries or args.event_schedule):
         print("timing the CPU oracle sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = _with_host(cpu_baseline(cfg))
