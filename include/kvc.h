@@ -454,6 +454,18 @@ size_t kvc_summarize_workspace(const kvc_cache* cache);
 int kvc_summarize_evicted(const kvc_cache* cache, const int8_t* tier_prev, int32_t max_new, void* workspace,
                           size_t workspace_bytes, hipStream_t stream);
 
+/* kvc_topk: the budgeted selection itself. Every selection on the pages keeps the highest-scoring entries under a
+ * fixed budget: QEvict's tiers ("Metodologia: QEvict"), DBTrimKV's global top-M ("Metodologia", section 3),
+ * CriticalKV's stages ("Algoritmo: Seleção Constrainda por Perturbação"). Here: the first k entries of scores in
+ * the order (score desc, index asc) — a unique set — written as their indices in ascending index order.
+ *   scores   [n] float, finite (a NaN makes the result undefined), 16-byte aligned.
+ *   idx_out  [k] int32 out, ascending.
+ *   0 <= k <= n < 2^31 - 16.
+ * Workspace: kvc_topk_workspace(n, k) bytes, any contents, 256-byte aligned. */
+size_t kvc_topk_workspace(int64_t n, int64_t k);
+int kvc_topk(const float* scores, int64_t n, int64_t k, int32_t* idx_out, void* workspace, size_t workspace_bytes,
+             hipStream_t stream);
+
 /* Reads *cache->status into *host_status (synchronises the stream) and, if clear != 0, zeroes it. */
 int kvc_read_device_status(const kvc_cache* cache, int32_t* host_status, int32_t clear, hipStream_t stream);
 

@@ -114,6 +114,8 @@ SIGNATURES = {
     "kvc_paged_decode_attn": (C.c_int, [C.POINTER(KvcPagedDecodeArgs), P, C.c_size_t, P]),
     "kvc_route_diagnostics": (C.c_int, [C.POINTER(KvcDiagArgs), P]),
     "kvc_summarize_workspace": (C.c_size_t, [C.POINTER(KvcCache)]),
+    "kvc_topk_workspace": (C.c_size_t, [C.c_int64, C.c_int64]),
+    "kvc_topk": (C.c_int, [P, C.c_int64, C.c_int64, P, P, C.c_size_t, P]),
     "kvc_summarize_evicted": (C.c_int, [C.POINTER(KvcCache), P, C.c_int32, P, C.c_size_t, P]),
 }
 

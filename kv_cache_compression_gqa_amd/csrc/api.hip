@@ -361,6 +361,24 @@ int kvc_summarize_evicted(const kvc_cache* cache, const int8_t* tier_prev, int32
   return kvc::launch_summarize(*cache, tier_prev, max_new, workspace, stream) == hipSuccess ? KVC_OK : KVC_E_HIP;
 }
 
+size_t kvc_topk_workspace(int64_t n, int64_t k) {
+  if (n < 0 || n >= (int64_t(1) << 31) - 16 || k < 0 || k > n) return 0;
+  return kvc::topk_workspace_bytes(n);
+}
+
+int kvc_topk(const float* scores, int64_t n, int64_t k, int32_t* idx_out, void* workspace, size_t workspace_bytes,
+             hipStream_t stream) {
+  if (n < 0 || k < 0) return KVC_E_INVALID;
+  if (n >= (int64_t(1) << 31) - 16) return KVC_E_UNSUPPORTED;
+  if (k > n) return KVC_E_BUDGET;
+  if (k == 0) return KVC_OK;
+  if (scores == nullptr || !aligned(scores, 16) || idx_out == nullptr || !aligned(idx_out, 4)) return KVC_E_INVALID;
+  if (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < kvc::topk_workspace_bytes(n)) {
+    return KVC_E_WORKSPACE;
+  }
+  return kvc::launch_topk(scores, n, k, idx_out, workspace, stream) == hipSuccess ? KVC_OK : KVC_E_HIP;
+}
+
 int kvc_read_device_status(const kvc_cache* cache, int32_t* host_status, int32_t clear, hipStream_t stream) {
   if (cache == nullptr || cache->status == nullptr || host_status == nullptr) return KVC_E_INVALID;
   if (hipMemcpyAsync(host_status, cache->status, sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess) {

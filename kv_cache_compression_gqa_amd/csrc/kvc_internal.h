@@ -123,6 +123,8 @@ size_t paged_workspace_bytes(const kvc_paged_decode_args& a);
 hipError_t launch_paged_decode(const kvc_paged_decode_args& a, void* ws, hipStream_t s);
 hipError_t launch_diagnostics(const kvc_diag_args& a, hipStream_t s);
 size_t summarize_workspace_bytes(const kvc_cache& c);
+size_t topk_workspace_bytes(int64_t n);
+hipError_t launch_topk(const float* scores, int64_t n, int64_t k, int32_t* idx, void* ws, hipStream_t s);
 hipError_t launch_summarize(const kvc_cache& c, const int8_t* tier_prev, int32_t max_new, void* ws, hipStream_t s);
 
 }  // namespace kvc

@@ -262,3 +262,20 @@ def test_header_is_plain_c_and_links(tmp_path):
                         "-lkvc", f"-Wl,-rpath,{lib_dir}", "-o", str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
     assert subprocess.run([str(exe)]).returncode == 0
+
+
+def test_topk_validation_rejects_before_launch():
+    L = abi.lib()
+    assert L.kvc_topk_workspace(-1, 0) == 0 and L.kvc_topk_workspace(10, 11) == 0
+    assert L.kvc_topk_workspace(10, -1) == 0 and L.kvc_topk_workspace(1 << 31, 1) == 0
+    need = L.kvc_topk_workspace(1000, 10)
+    assert need > 0
+    assert L.kvc_topk(FAKE, 1000, 0, None, None, 0, None) == abi.KVC_OK          # nothing to select
+    assert L.kvc_topk(FAKE, 1000, 1001, FAKE, FAKE, need, None) == abi.KVC_E_BUDGET
+    assert L.kvc_topk(FAKE, -1, 1, FAKE, FAKE, need, None) == abi.KVC_E_INVALID
+    assert L.kvc_topk(FAKE, 1 << 31, 1, FAKE, FAKE, need, None) == abi.KVC_E_UNSUPPORTED
+    assert L.kvc_topk(None, 1000, 10, FAKE, FAKE, need, None) == abi.KVC_E_INVALID
+    assert L.kvc_topk(FAKE + 4, 1000, 10, FAKE, FAKE, need, None) == abi.KVC_E_INVALID
+    assert L.kvc_topk(FAKE, 1000, 10, None, FAKE, need, None) == abi.KVC_E_INVALID
+    assert L.kvc_topk(FAKE, 1000, 10, FAKE, FAKE, need - 1, None) == abi.KVC_E_WORKSPACE
+    assert L.kvc_topk(FAKE, 1000, 10, FAKE, FAKE + 16, need, None) == abi.KVC_E_WORKSPACE
