@@ -54,7 +54,7 @@ def parse():
                     help="also run one plain device-to-device copy of this many MiB (counter calibration)")
     ap.add_argument("--workload", default="llama3_8b_layer_32k",
                     choices=["llama3_8b_layer_32k", "batched_32l_b16", "criticalkv_64k", "dbtrim_128k",
-                             "dbtrim_paged_decode_128k", "qevict_diagnostics_32k"],
+                             "dbtrim_paged_decode_128k", "qevict_diagnostics_32k", "topk_33m"],
                     help="the decode step (default), the CriticalKV prefill selection or the DBTrimKV global budget")
     return ap.parse_args()
 
@@ -205,6 +205,8 @@ def main():
         return bench_paged_decode(args)
     if args.workload == "qevict_diagnostics_32k":
         return bench_diagnostics(args)
+    if args.workload == "topk_33m":
+        return bench_topk(args)
     import torch
     sys.path.insert(0, ROOT)
     from kv_cache_compression_gqa_amd import configs, synth
@@ -852,6 +854,70 @@ def cpu_baseline_dbtrim(cfg, layers=16):
     return {"value": beta.size / el, "unit": "KV entries/s", "cores": threads, "kind": "oracle",
             "sample": f"{layers} of {cfg.layers} layers ({beta.size} entries, M = 10%): fp64 numpy oracle scores, "
                       f"top-M, compaction plan and K/V row gather; {el:.1f} s"}
+
+
+def bench_topk(args):
+    """Generic budgeted top-k (kvc_topk) over the DBTrimKV log-retention scores of 32 layers x 8 KV heads x 131072
+    tokens (n = 33,554,432 fp32 scores, k = 10% of them), indices written ascending."""
+    import ctypes as C
+
+    import torch
+    sys.path.insert(0, ROOT)
+    from kv_cache_compression_gqa_amd import abi, configs, retention, synth
+    cfg = configs.DBTRIM_128K
+    torch.cuda.set_device(0)
+    rows, T = cfg.layers * cfg.hkv, cfg.n_tokens
+    beta = torch.from_numpy(synth.make_retention_beta(cfg).reshape(rows, T)).cuda()
+    scores = retention.retention_scores(beta, cfg.t).reshape(-1)
+    del beta
+    n, k = scores.numel(), cfg.keep
+    L = abi.lib()
+    need = L.kvc_topk_workspace(n, k)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    idx = torch.empty(k, dtype=torch.int32, device="cuda")
+    stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    print(f"inputs ready: topk n={n} k={k}", file=sys.stderr, flush=True)
+
+    def call():
+        abi.check(L.kvc_topk(scores.data_ptr(), n, k, idx.data_ptr(), ws.data_ptr(), need, stream), "kvc_topk")
+
+    K = max(1, min(args.steps, 20))
+    wall, ms = _timed_calls(call, K, 2)
+    got = idx.cpu().numpy()
+    if got.size != k or not (np.diff(got) > 0).all():
+        print("top-k indices not strictly ascending", file=sys.stderr)
+        sys.exit(1)
+    call_s = float(np.mean(ms)) * 1e-3
+    alg = n * 4 + k * 4  # every score read once, every index written once
+    rec = {
+        "metric": "scores selected/s (generic budgeted top-k)", "value": n * K / wall, "unit": "scores/s",
+        "n_gpus": 1, "steps": K, "warmup": 2, "ms_per_step": wall / K * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "topk_33m", "n": n, "k": k, "scores": "DBTrimKV log-retention, 32 x 8 x 131072"},
+        "roofline": {"bound": "hbm", "achieved": alg / call_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": alg / call_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "kvc_topk (topm passes + count / offsets / write)", "avg_launch_us": call_s * 1e6,
+                     "algorithmic_bytes_per_launch": alg},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = _with_host(cpu_baseline_topk(cfg))
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline_topk(cfg, layers=32):
+    """The oracle's top-k (a full (score desc, index asc) sort) over the retention scores of the first ``layers``
+    layers, k = 10%."""
+    from kv_cache_compression_gqa_amd import synth
+    from oracle import dbtrim, select
+    threads = _oracle_threads()
+    s = dbtrim.log_retention(synth.make_retention_beta(cfg, layers=layers), cfg.t).reshape(-1)
+    k = int(np.floor(cfg.keep_frac * s.size))
+    t0 = time.perf_counter()
+    sel = np.sort(select.topk(s, k))
+    el = time.perf_counter() - t0
+    assert sel.size == k
+    return {"value": s.size / el, "unit": "scores/s", "cores": threads, "kind": "oracle",
+            "sample": f"{layers} of {cfg.layers} layers ({s.size} scores, k = 10%): fp64 numpy lexsort; {el:.1f} s"}
 
 
 def _with_host(rec):

@@ -98,17 +98,23 @@ __global__ __launch_bounds__(kKThreads) void topk_write(const uint8_t* __restric
     if (lane >= d) inc += o;
   }
   __shared__ int wsum[kKThreads / kWave];
+  __shared__ int32_t stage[kKChunk];  // the chunk's kept indices in order, written out as one contiguous run
   if (lane == kWave - 1) wsum[wave] = inc;
   __syncthreads();
-  int base = offsets[blockIdx.x];
-  for (int w = 0; w < wave; ++w) base += wsum[w];
-  int pos = base + inc - c;
+  int lpos = inc - c, total = 0;
+#pragma unroll
+  for (int w = 0; w < kKThreads / kWave; ++w) {
+    if (w < wave) lpos += wsum[w];
+    total += wsum[w];
+  }
 #pragma unroll
   for (int j = 0; j < kKPer; ++j) {
-    if (b[j]) {
-      if (pos < k) idx[pos] = int32_t(beg + j);
-      ++pos;
-    }
+    if (b[j]) stage[lpos++] = int32_t(beg + j);
+  }
+  __syncthreads();
+  const int64_t base = offsets[blockIdx.x];
+  for (int i = threadIdx.x; i < total; i += kKThreads) {
+    if (base + i < k) idx[base + i] = stage[i];
   }
 }
 
