@@ -382,8 +382,8 @@ def bench_batched(args):
     K = max(1, min(args.steps, cfg.steps))
     warm = 2
     torch.cuda.set_device(0)
-    inp, umap = synth.make_decode_shared_layers(cfg, steps=warm + 2 * K)
-    sess = DecodeSession(inp, unit_map=umap, tail_max=int(inp.tail0.max()) + warm + 2 * K + 1)
+    inp, layers = synth.make_decode_shared_layers(cfg, steps=warm + 2 * K)
+    sess = DecodeSession(inp, plan=layers, tail_max=int(inp.tail0.max()) + warm + 2 * K + 1)
     sess.reserve_workspace(warm + 2 * K)
     torch.cuda.synchronize()
     print(f"session ready: {cfg.name}, {sess.U} units", file=sys.stderr, flush=True)
@@ -567,7 +567,7 @@ def cpu_baseline_criticalkv(cfg, inp):
 
 def _dbtrim_inputs(cfg):
     """The DBTrimKV workload on the device: beta [rows][T] fp32, the source page table [rows][T/page] int32 and the
-    K/V pools [rows*T/page][page][128] bf16 (pool row r = seeded table row (r*40503+17) mod 65536)."""
+    K/V pools [rows*T/page][page][128] bf16 (pool row r = seeded table row synth.pool_row_index(r))."""
     import torch
     from kv_cache_compression_gqa_amd import synth
     L, H, T, page = cfg.layers, cfg.hkv, cfg.n_tokens, cfg.page

@@ -31,14 +31,16 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 3
+#define KVC_ABI_VERSION 4
 
 typedef enum {
   KVC_OK = 0,
   KVC_E_INVALID = -1,      /* null pointer, bad size, misaligned buffer, inconsistent arguments */
   KVC_E_UNSUPPORTED = -2,  /* head_dim != 128, window != 32, group not in {1,2,4,8}, unknown dtype or mode */
   KVC_E_WORKSPACE = -3,    /* workspace missing or smaller than the *_workspace query says */
-  KVC_E_LEDGER = -4,       /* write-once ledger violation (reported on the host path) */
+  KVC_E_LEDGER = -4,       /* reserved: no call returns it. Whether a window already has its ledger copy is device
+                              state, so a write-once violation is not seen on the host: kvc_quantize_int2 skips
+                              such a window and sets KVC_DEV_LEDGER_REWRITE (read with kvc_read_device_status) */
   KVC_E_BUDGET = -5,       /* a budget or bound is negative or larger than the capacity */
   KVC_E_HIP = -6           /* a HIP launch failed */
 } kvc_status;
@@ -235,12 +237,13 @@ typedef struct kvc_criticalkv_args {
 } kvc_criticalkv_args;
 
 /* kvc_route(KVC_ROUTE_TWO_STAGE): CriticalKV's two-stage budgeted selection (CriticalKV page, "Algoritmo:
- * Seleção Constrainda por Perturbação"), per row (KV head): the first budget1 entries in (a desc, index asc)
- * order, then the first budget - budget1 of the remaining entries in (s2 desc, index asc) order; the union is
- * written ascending.
- *   a, s2  [rows][n] float (finite);  idx [rows][budget] int32 out.  0 <= budget1 <= budget <= n <= 65536.
- *   budget1 = floor(alpha * budget) is the caller's (an integer, so no float rounding is left to the library).
- * No workspace. */
+ * Seleção Constrainda por Perturbação": a share alpha of the budget goes to the attention weights alone, the rest
+ * to the perturbation-aware score), per row (KV head): with budget1 = floor(alpha * budget) (computed by the
+ * library in double precision), the first budget1 entries in (a desc, index asc) order, then the first
+ * budget - budget1 of the remaining entries in (s2 desc, index asc) order; the union is written ascending.
+ *   a, s2  [rows][n] float (finite; a NaN makes the result undefined);  idx [rows][budget] int32 out.
+ *   0 <= budget <= n <= 65536;  0 <= alpha <= 1.
+ * Workspace: kvc_route_workspace(KVC_ROUTE_TWO_STAGE, args) bytes, any contents, 256-byte aligned. */
 typedef struct kvc_two_stage_args {
   const float* a;
   const float* s2;
@@ -248,7 +251,8 @@ typedef struct kvc_two_stage_args {
   int32_t rows;
   int32_t n;
   int32_t budget;
-  int32_t budget1;
+  int32_t reserved; /* must be 0 */
+  double alpha;     /* stage-1 share of the budget */
 } kvc_two_stage_args;
 
 /* kvc_score(KVC_SCORE_RETENTION): DBTrimKV retention score (DBTrimKV page, "Metodologia: Evicção Baseada em
@@ -269,7 +273,7 @@ typedef struct kvc_retention_args {
  * every layer and head is ranked on one scale and the top M are kept). The kept set is the first m entries in
  * the order (score desc, flat index asc), so it is unique.
  *   scores     [n] float, finite, 16-byte aligned; rows of row_len entries (row_len % 16 == 0, n % row_len == 0,
- *              n < 2^31); 0 <= m <= n.
+ *              n <= 2^31 - 8208, larger n: KVC_E_UNSUPPORTED); 0 <= m <= n.
  *   keep       [n] uint8 out, 1 = kept (16-byte aligned);  row_counts [n / row_len] int32 out: kept per row.
  *   status     int32 device error bits (KVC_DEV_NAN_SCORE: a NaN score was seen; the result is then undefined).
  * Workspace: kvc_route_workspace(KVC_ROUTE_GLOBAL_TOPM, args) bytes, any contents. */
@@ -460,7 +464,7 @@ int kvc_summarize_evicted(const kvc_cache* cache, const int8_t* tier_prev, int32
  * the order (score desc, index asc) — a unique set — written as their indices in ascending index order.
  *   scores   [n] float, finite (a NaN makes the result undefined), 16-byte aligned.
  *   idx_out  [k] int32 out, ascending.
- *   0 <= k <= n < 2^31 - 16.
+ *   0 <= k <= n <= 2^31 - 8208 (larger n: KVC_E_UNSUPPORTED).
  * Workspace: kvc_topk_workspace(n, k) bytes, any contents, 256-byte aligned. */
 size_t kvc_topk_workspace(int64_t n, int64_t k);
 int kvc_topk(const float* scores, int64_t n, int64_t k, int32_t* idx_out, void* workspace, size_t workspace_bytes,

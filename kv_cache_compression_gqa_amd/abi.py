@@ -11,6 +11,7 @@ import os
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libkvc.so")
 _lib = None
 
+ABI_VERSION = 4  # KVC_ABI_VERSION of include/kvc.h
 KVC_OK, KVC_E_INVALID, KVC_E_UNSUPPORTED, KVC_E_WORKSPACE, KVC_E_LEDGER, KVC_E_BUDGET, KVC_E_HIP = \
     0, -1, -2, -3, -4, -5, -6
 KVC_DEV_LEDGER_REWRITE, KVC_DEV_BOUND_EXCEEDED, KVC_DEV_NAN_SCORE = 0x1, 0x2, 0x4
@@ -79,7 +80,7 @@ class KvcCriticalKVArgs(C.Structure):
 
 class KvcTwoStageArgs(C.Structure):
     _fields_ = [("a", P), ("s2", P), ("idx", P), ("rows", C.c_int32), ("n", C.c_int32), ("budget", C.c_int32),
-                ("budget1", C.c_int32)]
+                ("reserved", C.c_int32), ("alpha", C.c_double)]
 
 
 class KvcPagedDecodeArgs(C.Structure):
@@ -136,7 +137,7 @@ def lib():
             fn = getattr(L, name)
             fn.restype = res
             fn.argtypes = args
-        if L.kvc_abi_version() != 3:
+        if L.kvc_abi_version() != ABI_VERSION:
             raise RuntimeError("kvc ABI version mismatch")
         _lib = L
     return _lib

@@ -7,7 +7,6 @@ marshalling only.
 from __future__ import annotations
 
 import ctypes as C
-import math
 
 import torch
 
@@ -43,13 +42,20 @@ def scores(q_obs: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w_o: torch.Ten
     return out
 
 
-def two_stage(a: torch.Tensor, s2: torch.Tensor, budget: int, alpha: float, stream=None) -> torch.Tensor:
+def two_stage(a: torch.Tensor, s2: torch.Tensor, budget: int, alpha: float, stream=None, workspace=None):
     """a, s2 [rows][n] float32 (cuda) -> [rows][budget] int32 ascending: first floor(alpha*budget) by a, the rest
-    by s2 among the entries not yet taken; ties to the lower index."""
+    by s2 among the entries not yet taken; ties to the lower index (the library takes the floor)."""
     rows, n = a.shape
     idx = torch.empty((rows, budget), dtype=torch.int32, device=a.device)
     args = abi.KvcTwoStageArgs(a=a.data_ptr(), s2=s2.data_ptr(), idx=idx.data_ptr(), rows=rows, n=n, budget=budget,
-                               budget1=int(math.floor(alpha * budget)))
-    abi.check(abi.lib().kvc_route(abi.KVC_ROUTE_TWO_STAGE, C.cast(C.byref(args), C.c_void_p), None, 0,
-                                  _stream(stream)), "kvc_route(TWO_STAGE)")
+                               reserved=0, alpha=float(alpha))
+    L = abi.lib()
+    pa = C.cast(C.byref(args), C.c_void_p)
+    need = L.kvc_route_workspace(abi.KVC_ROUTE_TWO_STAGE, pa)
+    if need == 0 and rows > 0 and budget > 0:
+        raise abi.KvcError(abi.KVC_E_INVALID, "kvc_route_workspace(TWO_STAGE)")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=a.device)
+    abi.check(L.kvc_route(abi.KVC_ROUTE_TWO_STAGE, pa, workspace.data_ptr(), workspace.numel(), _stream(stream)),
+              "kvc_route(TWO_STAGE)")
     return idx

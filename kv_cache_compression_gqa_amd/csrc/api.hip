@@ -2,6 +2,8 @@
 // no state is kept between calls.
 #include <stdint.h>
 
+#include <cmath>
+
 #include "kvc_internal.h"
 
 namespace {
@@ -123,7 +125,8 @@ int check_topm(const kvc_topm_args* a) {
     return KVC_E_INVALID;
   }
   if (a->row_len <= 0 || a->row_len % 16 != 0 || a->n < 0 || a->n % a->row_len != 0) return KVC_E_INVALID;
-  if (a->n >= (int64_t(1) << 31)) return KVC_E_UNSUPPORTED;
+  // the kernels count blocks per row in int32: (row_len + block - 1) stays below 2^31
+  if (a->n > kvc::kTopmMaxN) return KVC_E_UNSUPPORTED;
   if (a->m < 0 || a->m > a->n) return KVC_E_BUDGET;
   return KVC_OK;
 }
@@ -162,8 +165,10 @@ int check_two_stage(const kvc_two_stage_args* a) {
   if (a == nullptr || a->a == nullptr || a->s2 == nullptr || a->idx == nullptr) return KVC_E_INVALID;
   if (!aligned(a->a, 4) || !aligned(a->s2, 4) || !aligned(a->idx, 4)) return KVC_E_INVALID;
   if (a->rows < 0 || a->n < 0) return KVC_E_INVALID;
+  if (a->reserved != 0) return KVC_E_INVALID;
   if (a->n > 65536) return KVC_E_UNSUPPORTED;
-  if (a->budget < 0 || a->budget1 < 0 || a->budget1 > a->budget || a->budget > a->n) return KVC_E_BUDGET;
+  if (!(a->alpha >= 0.0 && a->alpha <= 1.0)) return KVC_E_BUDGET;  // NaN fails too
+  if (a->budget < 0 || a->budget > a->n) return KVC_E_BUDGET;
   return KVC_OK;
 }
 
@@ -246,6 +251,11 @@ size_t kvc_route_workspace(int32_t mode, const void* args) {
     if (check_topm(a) != KVC_OK) return 0;
     return kvc::topm_workspace_bytes(*a);
   }
+  if (mode == KVC_ROUTE_TWO_STAGE) {
+    const kvc_two_stage_args* a = static_cast<const kvc_two_stage_args*>(args);
+    if (check_two_stage(a) != KVC_OK) return 0;
+    return kvc::two_stage_workspace_bytes(*a);
+  }
   return 0;
 }
 
@@ -276,7 +286,12 @@ int kvc_route(int32_t mode, const void* args, void* workspace, size_t workspace_
     const int st = check_two_stage(a);
     if (st != KVC_OK) return st;
     if (a->rows == 0 || a->budget == 0) return KVC_OK;
-    return kvc::launch_two_stage(*a, stream) == hipSuccess ? KVC_OK : KVC_E_HIP;
+    if (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < kvc::two_stage_workspace_bytes(*a)) {
+      return KVC_E_WORKSPACE;
+    }
+    // the stage split is CriticalKV's b' = floor(alpha * b), taken here in double precision
+    const int32_t budget1 = int32_t(std::floor(a->alpha * double(a->budget)));
+    return kvc::launch_two_stage(*a, budget1, workspace, stream) == hipSuccess ? KVC_OK : KVC_E_HIP;
   }
   return KVC_E_UNSUPPORTED;
 }
@@ -362,14 +377,14 @@ int kvc_summarize_evicted(const kvc_cache* cache, const int8_t* tier_prev, int32
 }
 
 size_t kvc_topk_workspace(int64_t n, int64_t k) {
-  if (n < 0 || n >= (int64_t(1) << 31) - 16 || k < 0 || k > n) return 0;
+  if (n < 0 || n > kvc::kTopmMaxN || k < 0 || k > n) return 0;
   return kvc::topk_workspace_bytes(n);
 }
 
 int kvc_topk(const float* scores, int64_t n, int64_t k, int32_t* idx_out, void* workspace, size_t workspace_bytes,
              hipStream_t stream) {
   if (n < 0 || k < 0) return KVC_E_INVALID;
-  if (n >= (int64_t(1) << 31) - 16) return KVC_E_UNSUPPORTED;
+  if (n > kvc::kTopmMaxN) return KVC_E_UNSUPPORTED;
   if (k > n) return KVC_E_BUDGET;
   if (k == 0) return KVC_OK;
   if (scores == nullptr || !aligned(scores, 16) || idx_out == nullptr || !aligned(idx_out, 4)) return KVC_E_INVALID;

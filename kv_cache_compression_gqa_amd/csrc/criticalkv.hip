@@ -654,8 +654,10 @@ hipError_t launch_criticalkv(const kvc_criticalkv_args& a, void* ws, hipStream_t
   return a.kv_dtype == KVC_BF16 ? launch_ckv<BF16>(a, ws, s) : launch_ckv<F16>(a, ws, s);
 }
 
-hipError_t launch_two_stage(const kvc_two_stage_args& a, hipStream_t s) {
-  hipLaunchKernelGGL(two_stage, dim3(a.rows), dim3(kSelThreads), 0, s, a.a, a.s2, a.n, a.budget, a.budget1, a.idx);
+size_t two_stage_workspace_bytes(const kvc_two_stage_args&) { return 256; }
+
+hipError_t launch_two_stage(const kvc_two_stage_args& a, int32_t budget1, void*, hipStream_t s) {
+  hipLaunchKernelGGL(two_stage, dim3(a.rows), dim3(kSelThreads), 0, s, a.a, a.s2, a.n, a.budget, budget1, a.idx);
   return hipGetLastError();
 }
 

@@ -99,6 +99,10 @@ __device__ __forceinline__ float exp_diff(float a, float b) { return a == -INFIN
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Largest entry count of the global top-M and the generic top-k: block counts per row are computed in int32 as
+// (row_len + 8191) / 8192, so n (and every row) stays at least one block below 2^31.
+constexpr int64_t kTopmMaxN = (int64_t(1) << 31) - 8192 - 16;
+
 // ---- launchers (host) -------------------------------------------------------------------------------------
 int decode_slices(const kvc_cache& c, const kvc_decode_args& a);
 bool decode_supported(const kvc_cache& c, const kvc_decode_args& a);
@@ -118,7 +122,8 @@ hipError_t launch_compact(const kvc_compact_args& a, void* ws, hipStream_t s);
 size_t criticalkv_workspace_bytes(const kvc_criticalkv_args& a);
 bool criticalkv_supported(const kvc_criticalkv_args& a);
 hipError_t launch_criticalkv(const kvc_criticalkv_args& a, void* ws, hipStream_t s);
-hipError_t launch_two_stage(const kvc_two_stage_args& a, hipStream_t s);
+size_t two_stage_workspace_bytes(const kvc_two_stage_args& a);
+hipError_t launch_two_stage(const kvc_two_stage_args& a, int32_t budget1, void* ws, hipStream_t s);
 size_t paged_workspace_bytes(const kvc_paged_decode_args& a);
 hipError_t launch_paged_decode(const kvc_paged_decode_args& a, void* ws, hipStream_t s);
 hipError_t launch_diagnostics(const kvc_diag_args& a, hipStream_t s);

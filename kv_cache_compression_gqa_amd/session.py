@@ -19,7 +19,7 @@ import numpy as np
 import torch
 
 from . import abi, layout
-from .synth import DecodeInputs
+from .synth import DecodeInputs, SharedLayers
 
 
 def _dev(a: np.ndarray, dtype, device):
@@ -33,10 +33,12 @@ def _bits(a: np.ndarray, device):
 class DecodeSession:
     """``unit_map`` (optional, [U] ints): unit u of the session starts from held unit ``unit_map[u]`` of ``inp``
     (its cache, tail and per-step inputs are copied on the device), so that many units can share one seeded
-    draw while every unit keeps memory and state of its own."""
+    draw while every unit keeps memory and state of its own. ``plan`` (a ``synth.SharedLayers``, instead of
+    ``unit_map``): the same, with every unit's windows rotated as the plan says and per-step inputs of its own."""
 
     def __init__(self, inp: DecodeInputs, device="cuda", tail_max: int | None = None, steps: int | None = None,
-                 budgets=None, unit_map=None, score_schedule: str = "every", summaries: bool = False):
+                 budgets=None, unit_map=None, score_schedule: str = "every", summaries: bool = False,
+                 plan: SharedLayers | None = None):
         """``score_schedule``: "every" adds every step's window mass to the cumulative score; "event" adds it only
         at the steps that end with a routing event (attention is then materialised for scoring only when the
         routing needs it, and the steps in between are plain decode steps). ``summaries``: every evicted window
@@ -49,6 +51,11 @@ class DecodeSession:
         self.inp = inp
         self.device = torch.device(device)
         dev = self.device
+        if plan is not None:
+            if unit_map is not None:
+                raise ValueError("give unit_map or plan, not both")
+            unit_map = plan.unit_map
+        self.plan = plan
         umap = np.arange(len(inp.units)) if unit_map is None else np.asarray(unit_map, np.int64)
         self.unit_map = umap
         idx = torch.from_numpy(umap).to(dev)
@@ -59,6 +66,17 @@ class DecodeSession:
         def expand_steps(t):
             return t if unit_map is None else t.index_select(1, idx).contiguous()
 
+        def expand_windows(t):  # [U'][NW]... -> [U][NW]...: held unit, windows in the plan's order
+            if plan is None:
+                return expand(t)
+            NWh = t.shape[1]
+            nw = torch.from_numpy(inp.n_windows[umap]).to(dev)
+            rot = torch.from_numpy(np.asarray(plan.rot, np.int64)).to(dev)
+            w = torch.arange(NWh, device=dev, dtype=torch.int64)[None, :]
+            src = torch.where(w < nw[:, None], (w + rot[:, None]) % nw.clamp(min=1)[:, None], w)
+            flat = (idx[:, None] * NWh + src).reshape(-1)
+            return t.reshape(t.shape[0] * NWh, *t.shape[2:]).index_select(0, flat).reshape(len(umap), *t.shape[1:])
+
         n_windows_u = inp.n_windows[umap]
         tail0_u = inp.tail0[umap]
         U = len(umap)
@@ -68,8 +86,8 @@ class DecodeSession:
         self.U, self.NW, self.G, self.D, self.W = U, NW, G, D, W
         tm = tail_max if tail_max is not None else int(inp.tail0.max()) + S + 1
         self.TM = max(32, (tm + 31) // 32 * 32)
-        self.k_win = expand(_bits(inp.k_win, dev))
-        self.v_win = expand(_bits(layout.v_win_to_lib(inp.v_win), dev))   # [U][NW][D][W]
+        self.k_win = expand_windows(_bits(inp.k_win, dev))
+        self.v_win = expand_windows(_bits(layout.v_win_to_lib(inp.v_win), dev))   # [U][NW][D][W]
         self.k_codes = torch.zeros((U, NW, W, D // 4), dtype=torch.uint8, device=dev)
         self.v_codes = torch.zeros((U, NW, 16, 4, 8), dtype=torch.int16, device=dev)
         self.k_meta = torch.zeros((U, NW, W, D // 32), dtype=torch.int32, device=dev)
@@ -105,9 +123,14 @@ class DecodeSession:
         self.h_sum = np.zeros(U, np.int64)
         self._sum_ws = None
         # per-step inputs
-        self.q = expand_steps(_bits(inp.q, dev))
-        self.k_new = expand_steps(_bits(inp.k_new, dev))
-        self.v_new = expand_steps(_bits(inp.v_new, dev))
+        if plan is not None:
+            self.q = _bits(plan.q, dev)
+            self.k_new = _bits(plan.k_new, dev)
+            self.v_new = _bits(plan.v_new, dev)
+        else:
+            self.q = expand_steps(_bits(inp.q, dev))
+            self.k_new = expand_steps(_bits(inp.k_new, dev))
+            self.v_new = expand_steps(_bits(inp.v_new, dev))
         self.out = torch.zeros((U, G, D), dtype=torch.float32, device=dev)
         # budgets
         if budgets is None:

@@ -75,6 +75,7 @@ class DecodeInputs:
     k_new: np.ndarray          # [S][U'][D] uint16
     v_new: np.ndarray
     salient: list             # per held unit: sorted salient positions
+    qbar: np.ndarray | None = None  # [U'][D] float64 query direction of each held unit
 
 
 def _unit_decode_draws(cfg: DecodeWorkload, unit: int, length: int, steps: int):
@@ -92,7 +93,7 @@ def _unit_decode_draws(cfg: DecodeWorkload, unit: int, length: int, steps: int):
     q = qbar[None, None, :] + eps
     k_new = rng.standard_normal((steps, D))
     v_new = rng.standard_normal((steps, D))
-    return K, V, q, k_new, v_new, sal
+    return K, V, q, k_new, v_new, sal, qbar
 
 
 def make_decode(cfg: DecodeWorkload, units=None, steps: int | None = None) -> DecodeInputs:
@@ -113,9 +114,10 @@ def make_decode(cfg: DecodeWorkload, units=None, steps: int | None = None) -> De
     kn = np.zeros((steps, Up, D), np.uint16)
     vn = np.zeros((steps, Up, D), np.uint16)
     sal_list = []
+    qbars = np.zeros((Up, D))
     for j, u in enumerate(all_units):
         L = int(lens[j])
-        K, V, qq, k_new, v_new, sal = _unit_decode_draws(cfg, int(u), L, steps)
+        K, V, qq, k_new, v_new, sal, qbars[j] = _unit_decode_draws(cfg, int(u), L, steps)
         n = int(nw[j]) * W
         kb = to_storage_bits(K, cfg.dtype)
         vb = to_storage_bits(V, cfg.dtype)
@@ -129,19 +131,65 @@ def make_decode(cfg: DecodeWorkload, units=None, steps: int | None = None) -> De
         sal_list.append(sal)
     return DecodeInputs(cfg=cfg, units=all_units, lengths=lens, n_windows=nw.astype(np.int64),
                         tail0=(lens - nw * W).astype(np.int64), n_windows_max=NW, k_win=k_win, v_win=v_win,
-                        k_tail0=k_t, v_tail0=v_t, q=q, k_new=kn, v_new=vn, salient=sal_list)
+                        k_tail0=k_t, v_tail0=v_t, q=q, k_new=kn, v_new=vn, salient=sal_list, qbar=qbars)
+
+
+@dataclass
+class SharedLayers:
+    """How the units of a many-layer workload start from the held draws of layer 0.
+
+    Unit u = (layer l, sequence b, KV head g) starts from held unit j = unit_map[u] = (0, b, g), with:
+      * its prefill windows rotated by rot[u] = (37 * l) mod n_windows: window w of unit u holds held window
+        (w + rot[u]) mod n_windows (an index permutation: the layers of one (b, g) hold the same key and value rows
+        at different window positions, so a read of another layer's unit returns other data);
+      * the held prefill tail as it is;
+      * per-step inputs of its own: q_h = qbar_j + eps with eps ~ N(0, I_D), and a new key and value ~ N(0, 1) per
+        step, drawn from unit u's own stream (layer 0 keeps the held draws).
+    """
+
+    unit_map: np.ndarray  # [U] held unit of each unit
+    rot: np.ndarray       # [U] window rotation
+    q: np.ndarray         # [S][U][G][D] storage bits
+    k_new: np.ndarray     # [S][U][D] storage bits
+    v_new: np.ndarray
+
+    def window_order(self, inp: DecodeInputs, u: int) -> np.ndarray:
+        """Held window ids of unit u's windows 0 .. n_windows - 1."""
+        nw = int(inp.n_windows[int(self.unit_map[u])])
+        return (np.arange(nw) + int(self.rot[u])) % max(nw, 1)
 
 
 def make_decode_shared_layers(cfg: DecodeWorkload, steps: int | None = None):
     """Held inputs for the units of layer 0 (one seeded draw per (sequence, KV head), each at its sequence's
-    length) and the map that starts every unit (layer l, b, g) from held unit (0, b, g). The layers then share
-    their initial contents while each keeps memory and state of its own; generating every layer's draw on the
-    host would take minutes at 32 layers x batch 16."""
+    length) and the ``SharedLayers`` plan that starts every unit (layer l, b, g) from held unit (0, b, g) with its
+    windows rotated per layer and per-step inputs of its own. Every unit then holds its own memory, state and
+    data order; drawing every layer's whole prefill on the host would take minutes at 32 layers x batch 16."""
+    steps = cfg.steps if steps is None else steps
     base = np.array([cfg.unit_index(0, b, g) for b in range(cfg.batch) for g in range(cfg.hkv)], dtype=np.int64)
     inp = make_decode(cfg, units=base, steps=steps)
-    umap = np.array([cfg.unit_coords(u)[1] * cfg.hkv + cfg.unit_coords(u)[2] for u in range(cfg.n_units)],
-                    dtype=np.int64)
-    return inp, umap
+    U, G, D = cfg.n_units, cfg.group, cfg.head_dim
+    coords = [cfg.unit_coords(u) for u in range(U)]
+    umap = np.array([b * cfg.hkv + g for (_, b, g) in coords], dtype=np.int64)
+    layer = np.array([l for (l, _, _) in coords], dtype=np.int64)
+    nw = inp.n_windows[umap]
+    rot = np.where(nw > 0, (37 * layer) % np.maximum(nw, 1), 0).astype(np.int64)
+    q = np.zeros((steps, U, G, D))
+    kn = np.zeros((steps, U, D))
+    vn = np.zeros((steps, U, D))
+    held = layer == 0
+    for u in np.nonzero(~held)[0]:
+        rng = unit_rng(cfg.seed, int(u))
+        q[:, u] = inp.qbar[umap[u]][None, None, :] + rng.standard_normal((steps, G, D))
+        kn[:, u] = rng.standard_normal((steps, D))
+        vn[:, u] = rng.standard_normal((steps, D))
+    qb = to_storage_bits(q, cfg.dtype)
+    kb = to_storage_bits(kn, cfg.dtype)
+    vb = to_storage_bits(vn, cfg.dtype)
+    h = np.nonzero(held)[0]
+    qb[:, h] = inp.q[:, umap[h]]
+    kb[:, h] = inp.k_new[:, umap[h]]
+    vb[:, h] = inp.v_new[:, umap[h]]
+    return inp, SharedLayers(unit_map=umap, rot=rot, q=qb, k_new=kb, v_new=vb)
 
 
 # ----------------------------------------------------------------------------------------------------------
@@ -214,13 +262,18 @@ def make_page_table(cfg: RetentionWorkload, layers: int | None = None, n_tokens:
     return rng.permutation(n_pages).astype(np.int32).reshape(L, cfg.hkv, T // cfg.page)
 
 
+def pool_row_index(row_ids, pool_rows: int = 1 << 16):
+    """Table row of pool row r: (r * 40503 + 17 + (r >> 16) * 7919) mod pool_rows (numpy or torch int64). The
+    second term shifts every block of 65536 rows by a different odd offset, so rows repeat only every 2^32."""
+    return (row_ids * 40503 + 17 + (row_ids >> 16) * 7919) % pool_rows
+
+
 def pool_row_bits(row_ids: np.ndarray, head_dim: int, seed: int, dtype: str = "bf16",
                   pool_rows: int = 1 << 16) -> np.ndarray:
-    """K/V pool rows for the paged cache: row r (global row id = page*page_size + slot) takes row
-    (r * 40503 + 17) mod pool_rows of a seeded N(0,1) table, so huge pools need only a small table."""
+    """K/V pool rows for the paged cache: row r (global row id = page*page_size + slot) takes table row
+    ``pool_row_index(r)`` of a seeded N(0,1) table, so huge pools need only a small table."""
     table = pool_table_bits(head_dim, seed, dtype, pool_rows)
-    idx = (row_ids.astype(np.int64) * 40503 + 17) % pool_rows
-    return table[idx]
+    return table[pool_row_index(np.asarray(row_ids).astype(np.int64), pool_rows)]
 
 
 _POOL_CACHE: dict = {}
@@ -309,7 +362,7 @@ def device_pool(n_pages: int, page: int, head_dim: int, seed: int, dtype: str = 
     """The pool [n_pages][page][head_dim] (storage dtype) whose row r is pool_row_bits([r], ...): a device gather
     of the seeded table (an index permutation only)."""
     tab = torch.from_numpy(pool_table_bits(head_dim, seed, dtype).view(np.int16)).to(device)
-    idx = (torch.arange(n_pages * page, device=device, dtype=torch.int64) * 40503 + 17) % tab.shape[0]
+    idx = pool_row_index(torch.arange(n_pages * page, device=device, dtype=torch.int64), tab.shape[0])
     out = tab[idx].view(torch.bfloat16 if dtype == "bf16" else torch.float16).view(n_pages, page, head_dim)
     del idx
     return out

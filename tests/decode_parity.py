@@ -40,17 +40,29 @@ def row_check(name, g, r, rtol=RTOL):
         assert err <= lim, f"{name} head {h}: max err {err} > {lim}"
 
 
-def make_oracles(inp, units=None, unit_map=None, summaries=False):
-    """Oracle units keyed by session unit j (held unit unit_map[j] of ``inp``)."""
+def make_oracles(inp, units=None, unit_map=None, summaries=False, plan=None):
+    """Oracle units keyed by session unit j (held unit unit_map[j] of ``inp``; with a ``synth.SharedLayers``
+    plan, held unit plan.unit_map[j] with its windows in the plan's order)."""
+    if plan is not None:
+        unit_map = plan.unit_map
     umap = np.arange(len(inp.units)) if unit_map is None else np.asarray(unit_map)
     out = {}
     for j in (range(len(umap)) if units is None else units):
         b = int(umap[j])
         nw = int(inp.n_windows[b])
         t0 = int(inp.tail0[b])
-        out[j] = QEvictUnit(inp.k_win[b, :nw], inp.v_win[b, :nw], inp.k_tail0[b, :t0], inp.v_tail0[b, :t0],
+        order = np.arange(nw) if plan is None else plan.window_order(inp, j)
+        out[j] = QEvictUnit(inp.k_win[b, order], inp.v_win[b, order], inp.k_tail0[b, :t0], inp.v_tail0[b, :t0],
                             inp.cfg.dtype, summaries=summaries)
     return out
+
+
+def step_inputs(inp, t, j, unit_map=None, plan=None):
+    """(q, k_new, v_new) of session unit j at step t."""
+    if plan is not None:
+        return plan.q[t, j], plan.k_new[t, j], plan.v_new[t, j]
+    b = j if unit_map is None else int(unit_map[j])
+    return inp.q[t, b], inp.k_new[t, b], inp.v_new[t, b]
 
 
 def compare_route(sess: DecodeSession, oracles, gpu_cum):
@@ -103,21 +115,23 @@ def compare_route(sess: DecodeSession, oracles, gpu_cum):
 
 def run_decode_parity(cfg, units=None, steps=None, check_units=None, check_steps=None, probs=True, log=print,
                       inp=None, unit_map=None, score_schedule="every", token_weight=None, oracle_weight=None,
-                      summaries=False):
+                      summaries=False, plan=None):
     """Run ``steps`` decode steps (routing on the workload's cadence) on the GPU for every unit, and on the oracle
     for the units in ``check_units`` (default all; units are independent, so a sample of them is followed exactly).
     ``score_schedule`` "event" adds the window mass to the cumulative score only at routing-event steps.
     ``token_weight`` (device [U][G][S] float32) weights the window score on the GPU and ``oracle_weight`` (host
     [U][G][S]) on the oracle side.
     Outputs are compared at every step in ``check_steps`` (default all); routing at every event. ``inp`` and
-    ``unit_map`` (optional) give held inputs and the held unit each session unit starts from."""
+    ``unit_map`` (optional) give held inputs and the held unit each session unit starts from; ``plan`` (a
+    ``synth.SharedLayers``) gives it with per-unit window order and per-step inputs. Returns (session, oracles,
+    last GPU output [U][G][D])."""
     if inp is None:
         inp = synth.make_decode(cfg, units=units, steps=steps)
     S = inp.q.shape[0]
-    sess = DecodeSession(inp, unit_map=unit_map, score_schedule=score_schedule, summaries=summaries)
+    sess = DecodeSession(inp, unit_map=unit_map, score_schedule=score_schedule, summaries=summaries, plan=plan)
     U = sess.U
     umap = sess.unit_map
-    oracles = make_oracles(inp, check_units, unit_map, summaries=summaries)
+    oracles = make_oracles(inp, check_units, unit_map, summaries=summaries, plan=plan)
     check_steps = set(range(S)) if check_steps is None else set(check_steps)
     for t in range(S):
         stride = sess.probs_stride()
@@ -130,9 +144,8 @@ def run_decode_parity(cfg, units=None, steps=None, check_units=None, check_steps
         mass_h = mass.cpu().numpy()
         cum_h = sess.cum.cpu().numpy()
         for j, o in oracles.items():
-            b = int(umap[j])
             acc = score_schedule == "every" or (cfg.route_every > 0 and (t + 1) % cfg.route_every == 0)
-            r = o.step(inp.q[t, b], inp.k_new[t, b], inp.v_new[t, b], accumulate=acc,
+            r = o.step(*step_inputs(inp, t, j, umap, plan), accumulate=acc,
                        token_weight=None if oracle_weight is None else oracle_weight[j])
             if t not in check_steps:
                 continue
@@ -150,4 +163,4 @@ def run_decode_parity(cfg, units=None, steps=None, check_units=None, check_steps
             log(f"step {t + 1}: routed; tiers, lists, ledger and promoted copies match")
     st = sess.device_status()
     assert st == 0, f"device status bits {st:#x}"
-    return sess, oracles
+    return sess, oracles, out

@@ -24,7 +24,7 @@ def test_every_declared_symbol_is_exported_and_bound():
     for n in names:
         assert hasattr(L, n), n
         assert n in abi.SIGNATURES, n
-    assert L.kvc_abi_version() == 3
+    assert L.kvc_abi_version() == abi.ABI_VERSION == 4
 
 
 def test_struct_sizes_match_header_layout():
@@ -133,6 +133,10 @@ def test_retention_topm_compact_validation_rejects_before_launch():
     assert topm(m=-1)[0] == abi.KVC_E_BUDGET
     assert topm(row_len=24, n=48)[0] == abi.KVC_E_INVALID
     assert topm(n=50)[0] == abi.KVC_E_INVALID
+    # sizes whose per-row block count would overflow int32 arithmetic are refused
+    big = (1 << 31) - 8192   # one past the largest supported n (2^31 - 8208, a multiple of 16)
+    assert topm(n=big, row_len=big, m=1)[0] == abi.KVC_E_UNSUPPORTED
+    assert topm(n=big - 16, row_len=big - 16, m=1)[0] != abi.KVC_E_UNSUPPORTED
     assert topm()[0] == abi.KVC_E_WORKSPACE
     st, t = topm()
     assert L.kvc_route_workspace(abi.KVC_ROUTE_GLOBAL_TOPM, C.cast(C.byref(t), C.c_void_p)) > 0
@@ -170,14 +174,25 @@ def test_criticalkv_and_two_stage_validation_rejects_before_launch():
     assert st == abi.KVC_E_WORKSPACE and ws >= 8 * 256 * 128 * 2
 
     def ts(**over):
-        kw = dict(a=FAKE, s2=FAKE, idx=FAKE, rows=2, n=100, budget=10, budget1=5)
+        kw = dict(a=FAKE, s2=FAKE, idx=FAKE, rows=2, n=100, budget=10, reserved=0, alpha=0.5)
         kw.update(over)
         t = abi.KvcTwoStageArgs(**kw)
-        return L.kvc_route(abi.KVC_ROUTE_TWO_STAGE, C.cast(C.byref(t), C.c_void_p), None, 0, None)
+        pa = C.cast(C.byref(t), C.c_void_p)
+        return L.kvc_route(abi.KVC_ROUTE_TWO_STAGE, pa, FAKE, L.kvc_route_workspace(abi.KVC_ROUTE_TWO_STAGE, pa),
+                           None)
     assert ts(budget=101) == abi.KVC_E_BUDGET
-    assert ts(budget1=11) == abi.KVC_E_BUDGET
+    assert ts(alpha=1.5) == abi.KVC_E_BUDGET
+    assert ts(alpha=-0.1) == abi.KVC_E_BUDGET
+    assert ts(alpha=float("nan")) == abi.KVC_E_BUDGET
+    assert ts(reserved=1) == abi.KVC_E_INVALID
     assert ts(n=70000, budget=10) == abi.KVC_E_UNSUPPORTED
-    assert ts(budget=0, budget1=0) == abi.KVC_OK  # nothing to select: no launch
+    assert ts(budget=0) == abi.KVC_OK  # nothing to select: no launch
+    t = abi.KvcTwoStageArgs(a=FAKE, s2=FAKE, idx=FAKE, rows=2, n=100, budget=10, reserved=0, alpha=0.5)
+    pa = C.cast(C.byref(t), C.c_void_p)
+    need = L.kvc_route_workspace(abi.KVC_ROUTE_TWO_STAGE, pa)
+    assert need > 0
+    assert L.kvc_route(abi.KVC_ROUTE_TWO_STAGE, pa, None, need, None) == abi.KVC_E_WORKSPACE
+    assert L.kvc_route(abi.KVC_ROUTE_TWO_STAGE, pa, FAKE, need - 1, None) == abi.KVC_E_WORKSPACE
 
 
 def test_route_diagnostics_validation_rejects_before_launch():
@@ -274,6 +289,9 @@ def test_topk_validation_rejects_before_launch():
     assert L.kvc_topk(FAKE, 1000, 1001, FAKE, FAKE, need, None) == abi.KVC_E_BUDGET
     assert L.kvc_topk(FAKE, -1, 1, FAKE, FAKE, need, None) == abi.KVC_E_INVALID
     assert L.kvc_topk(FAKE, 1 << 31, 1, FAKE, FAKE, need, None) == abi.KVC_E_UNSUPPORTED
+    limit = (1 << 31) - 8208
+    assert L.kvc_topk_workspace(limit + 1, 1) == 0 and L.kvc_topk_workspace(limit, 1) > 0
+    assert L.kvc_topk(FAKE, limit + 1, 1, FAKE, FAKE, need, None) == abi.KVC_E_UNSUPPORTED
     assert L.kvc_topk(None, 1000, 10, FAKE, FAKE, need, None) == abi.KVC_E_INVALID
     assert L.kvc_topk(FAKE + 4, 1000, 10, FAKE, FAKE, need, None) == abi.KVC_E_INVALID
     assert L.kvc_topk(FAKE, 1000, 10, None, FAKE, need, None) == abi.KVC_E_INVALID

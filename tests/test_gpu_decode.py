@@ -74,14 +74,18 @@ def test_degenerate_budgets_and_contexts(gpu_lib, case):
 def test_many_units_two_int2_windows_per_task(gpu_lib):
     """1280 units: a step takes many rounds of workgroups, so the launch switches to two INT2 windows per wave
     task and 4-wave workgroups. G = 8 (f16), 1 (bf16) and 2 (f16), probabilities on; the oracle follows units
-    spread over layers, sequences and heads."""
+    spread over layers, sequences and heads, two of them layers 0 and 9 of one (sequence, KV head), whose
+    outputs must differ (every layer holds its windows in an order of its own and has its own step inputs)."""
     for hq, hkv, batch, dtype in ((16, 2, 20, "f16"), (4, 4, 10, "bf16"), (8, 4, 10, "f16")):
         cfg = dataclasses.replace(configs.TINY, name=f"many_g{hq // hkv}", seed=14, hq=hq, hkv=hkv, dtype=dtype,
                                   layers=32, batch=batch, context=640, n_salient=5, budget_full=4, budget_int2=7,
                                   steps=4, route_every=2)
-        inp, umap = synth.make_decode_shared_layers(cfg)
+        inp, plan = synth.make_decode_shared_layers(cfg)
+        pair = [cfg.unit_index(0, 3, 1), cfg.unit_index(9, 3, 1)]
         log(f"case: {cfg.name}, {cfg.n_units} units, {dtype}")
-        run_decode_parity(cfg, inp=inp, unit_map=umap, check_units=[0, 333, 777, cfg.n_units - 1], log=log)
+        _, _, out = run_decode_parity(cfg, inp=inp, plan=plan,
+                                      check_units=sorted(set([0, 333, 777, cfg.n_units - 1] + pair)), log=log)
+        assert not np.allclose(out[pair[0]], out[pair[1]], rtol=1e-2, atol=0.0)
 
 
 def test_llama_layer_32k_run_matches_oracle(gpu_lib):
@@ -293,12 +297,18 @@ def test_batched_32_layers_batch_16_full_size(gpu_lib):
     """4096 units (32 layers x batch 16 x 8 KV heads), lengths uniform in [4096, 8192] per sequence, 25% FULL +
     25% INT2 per unit, routing after every step: every unit runs on the GPU; sampled units across layers,
     sequences and heads follow the oracle exactly (outputs, probabilities, mass and cum every step; tiers,
-    lists, ledger and promoted copies at every routing event)."""
+    lists, ledger and promoted copies at every routing event). Every layer of a (sequence, KV head) holds its
+    windows in an order of its own and takes per-unit step inputs, so four layers of one (sequence, KV head)
+    are followed and their outputs must differ: a read or write of another layer's unit cannot pass."""
     cfg = configs.BATCHED_32L_B16
-    inp, umap = synth.make_decode_shared_layers(cfg)
+    inp, plan = synth.make_decode_shared_layers(cfg)
     print(f"batched: {cfg.n_units} units, lengths {sorted(set(inp.lengths.tolist()))[:3]}..", flush=True)
-    check = [0, 9, 130, 1234, 2048 + 77, cfg.n_units - 1]
-    run_decode_parity(cfg, inp=inp, unit_map=umap, check_units=check, probs=True)
+    same_bg = [cfg.unit_index(l, 5, 3) for l in (0, 1, 17, 31)]
+    check = sorted(set([0, 9, 130, 1234, 2048 + 77, cfg.n_units - 1] + same_bg))
+    _, _, out = run_decode_parity(cfg, inp=inp, plan=plan, check_units=check, probs=True)
+    for i, a in enumerate(same_bg):
+        for b in same_bg[i + 1:]:
+            assert not np.allclose(out[a], out[b], rtol=1e-2, atol=0.0), f"units {a} and {b} give the same output"
 
 
 def test_one_round_launch_a_few_tasks_over(gpu_lib):

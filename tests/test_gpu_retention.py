@@ -40,12 +40,12 @@ def _check_topm(sc_gpu, tm, m):
 
 
 def _pools(n_src_pages, page, D, seed_k, seed_v, dtype):
-    """K/V pools on the GPU: row r is row (r * 40503 + 17) mod 65536 of a seeded table (the generator's rule)."""
+    """K/V pools on the GPU: row r is table row synth.pool_row_index(r) of a seeded table (the generator's rule)."""
     import torch
     tk = torch.from_numpy(synth.pool_table_bits(D, seed_k, dtype).view(np.int16)).cuda()
     tv = torch.from_numpy(synth.pool_table_bits(D, seed_v, dtype).view(np.int16)).cuda()
     rows = torch.arange(n_src_pages * page, device="cuda", dtype=torch.int64)
-    idx = (rows * 40503 + 17) % tk.shape[0]
+    idx = synth.pool_row_index(rows, tk.shape[0])
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
     k = tk[idx].view(tdt).view(n_src_pages, page, D)
     v = tv[idx].view(tdt).view(n_src_pages, page, D)

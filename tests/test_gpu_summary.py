@@ -27,7 +27,7 @@ def log(msg):
 def test_summaries_tiny(gpu_lib, dtype):
     log(f"case: span summaries, tiny workload, {dtype}, 12 steps")
     cfg = dataclasses.replace(configs.TINY, dtype=dtype)
-    sess, oracles = run_decode_parity(cfg, steps=12, probs=False, summaries=True, log=log)
+    sess, oracles, _ = run_decode_parity(cfg, steps=12, probs=False, summaries=True, log=log)
     assert int(sess.n_sum.max().item()) == 16   # the first event evicts 16 windows per unit, later ones none
 
 
@@ -44,9 +44,9 @@ def test_summaries_many_units(gpu_lib):
     cfg = dataclasses.replace(configs.TINY, name="many_sum", seed=14, hq=16, hkv=2, dtype="f16", layers=32,
                               batch=20, context=640, n_salient=5, budget_full=4, budget_int2=7, steps=4,
                               route_every=2)
-    inp, umap = synth.make_decode_shared_layers(cfg)
+    inp, plan = synth.make_decode_shared_layers(cfg)
     log(f"case: span summaries, {cfg.n_units} units")
-    run_decode_parity(cfg, inp=inp, unit_map=umap, check_units=[0, 333, 777, cfg.n_units - 1], probs=False,
+    run_decode_parity(cfg, inp=inp, plan=plan, check_units=[0, 333, 777, cfg.n_units - 1], probs=False,
                       summaries=True, log=log)
 
 
@@ -90,6 +90,6 @@ def test_summaries_llama_layer_32k(gpu_lib):
     routing event (513 summaries per unit) and four summary-attending steps; the oracle follows units 0 and 5."""
     cfg = dataclasses.replace(configs.LLAMA3_8B_LAYER_32K, steps=20)
     log("case: span summaries, llama3_8b_layer_ctx32k_bf16, 20 steps, oracle on units 0 and 5")
-    sess, _ = run_decode_parity(cfg, check_units=[0, 5], check_steps=[0, 15, 16, 17, 19], probs=False,
+    sess, _, _ = run_decode_parity(cfg, check_units=[0, 5], check_steps=[0, 15, 16, 17, 19], probs=False,
                                 summaries=True, log=log)
     assert int(sess.n_sum.min().item()) == 513
