@@ -23,8 +23,14 @@ Readings where the page is silent (each is listed with its reason in the design 
   * the partial last window and every decode-time token form an unrouted tail that is always attended;
   * a promoted window's full-precision data is RNE_storage(x^) of its ledger copy; its ledger is kept;
   * keys and values of INT2 windows are attended as x^ = fl32(c*s + z);
+  * memory follows the tiers ("Metodologia: QEvict": the routing runs under a fixed memory budget): a window holds
+    a full-precision copy only while it is FULL (demotion and eviction release it) and a ledger copy from its
+    first demotion until its eviction, so after an event at most b_full full-precision copies and at most
+    b_full + b_int2 ledger copies exist;
   * with summaries on (SEKV's mixed-resolution term), an evicted window is attended through one summary key and
-    value after the tail (oracle.summary).
+    value after the tail (oracle.summary), taken from the copy the cache holds for it when it is evicted: its
+    full-precision copy if it was FULL, its ledger copy brought back to the storage dtype (RNE_storage(x^), what a
+    promotion would store) if it was INT2.
 """
 from __future__ import annotations
 
@@ -68,9 +74,12 @@ class QEvictUnit:
         self.summaries = summaries
         self.sum_k, self.sum_v = [], []   # storage patterns [D], in eviction order
         self.dtype = dtype
-        self.kw = np.array(k_win, dtype=np.uint16, copy=True)
-        self.vw = np.array(v_win, dtype=np.uint16, copy=True)
-        self.n_windows, self.W, self.D = self.kw.shape
+        k_win = np.asarray(k_win, dtype=np.uint16)
+        v_win = np.asarray(v_win, dtype=np.uint16)
+        self.n_windows, self.W, self.D = k_win.shape
+        # full-precision copies, window -> [W][D] storage patterns: only the windows that are FULL hold one
+        self.kw = {w: k_win[w].copy() for w in range(self.n_windows)}
+        self.vw = {w: v_win[w].copy() for w in range(self.n_windows)}
         self.tail_k = [np.array(r, np.uint16) for r in k_tail]
         self.tail_v = [np.array(r, np.uint16) for r in v_tail]
         self.tier = np.full(self.n_windows, FULL, np.int8)
@@ -81,6 +90,16 @@ class QEvictUnit:
     # -- state views ------------------------------------------------------------------------------------------
     def resident_windows(self):
         return np.flatnonzero(self.tier == FULL), np.flatnonzero(self.tier == INT2)
+
+    def copies(self):
+        """(full-precision copies, ledger copies) the unit holds."""
+        return len(self.kw), len(self.ledger)
+
+    def _ledger_as_storage(self, w: int):
+        """Window w's ledger copy brought back to the storage dtype, RNE_storage(x^) (what a promotion stores)."""
+        e = self.ledger[w]
+        return (f32_to_storage_rne(dequantize(e["kc"], e["ks"], e["kz"]), self.dtype),
+                f32_to_storage_rne(dequantize(e["vc"], e["vs"], e["vz"]), self.dtype))
 
     def window_values(self, w: int):
         """Attended (K, V) of window w in fp64 under its current tier."""
@@ -157,17 +176,23 @@ class QEvictUnit:
         promoted = np.flatnonzero((before == INT2) & (after == FULL))
         evicted = np.flatnonzero((before != EVICTED) & (after == EVICTED))
         quantized = np.array([w for w in demoted if int(w) not in self.ledger], dtype=np.int64)
-        for w in quantized:
+        for w in quantized:   # first demotion: quantised from the full-precision copy it still holds
             self._quantize_window(int(w))
-        for w in promoted:
-            e = self.ledger[int(w)]
-            self.kw[w] = f32_to_storage_rne(dequantize(e["kc"], e["ks"], e["kz"]), self.dtype)
-            self.vw[w] = f32_to_storage_rne(dequantize(e["vc"], e["vs"], e["vz"]), self.dtype)
         for w in evicted:
-            if self.summaries:   # from the full-precision slot as it stands (original, or a promoted copy)
-                self.sum_k.append(summarize(self.kw[w], self.dtype))
-                self.sum_v.append(summarize(self.vw[w], self.dtype))
-            self.ledger.pop(int(w), None)
+            w = int(w)
+            if self.summaries:   # from the copy the cache holds for the window now
+                if before[w] == FULL:
+                    ks, vs = self.kw[w], self.vw[w]
+                else:
+                    ks, vs = self._ledger_as_storage(w)
+                self.sum_k.append(summarize(ks, self.dtype))
+                self.sum_v.append(summarize(vs, self.dtype))
+            self.ledger.pop(w, None)
+        for w in list(demoted) + list(evicted):   # their full-precision copies are released
+            self.kw.pop(int(w), None)
+            self.vw.pop(int(w), None)
+        for w in promoted:   # rebuilt from the ledger by dequantisation
+            self.kw[int(w)], self.vw[int(w)] = self._ledger_as_storage(int(w))
         self.tier = after
         return RoutePlan(tier_before=before, tier_after=after, quantized=quantized, promoted=promoted,
                          demoted=demoted, evicted=evicted)

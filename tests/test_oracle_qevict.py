@@ -1,6 +1,6 @@
 """Pins for the oracle's QEvict decode run (CPU only): full budget = plain attention, mass conservation,
 eviction permanence, write-once ledger under repeated promote/demote, attention over INT2 = attention over
-explicitly dequantised values."""
+explicitly dequantised values, copies held bounded by the budgets."""
 import numpy as np
 
 from kv_cache_compression_gqa_amd import configs, synth
@@ -119,3 +119,26 @@ def test_attention_over_int2_is_attention_over_dequantised_values():
     _, p, o = attention.gqa_decode(storage_to_f64(inp.q[4, 0], CFG.dtype), np.concatenate(Ks), np.concatenate(Vs))
     assert np.array_equal(p, r.p) and np.array_equal(o, r.o)
     assert r.p.shape[1] == 16 * 32 + len(unit.tail_k)
+
+
+def test_copies_held_follow_the_tiers_and_stay_within_the_budgets():
+    """The memory budget: after every routing event a unit holds exactly one full-precision copy per FULL window
+    and one ledger copy per resident window that has been INT2 at least once, so at most b_full and
+    b_full + b_int2 of them; before the first event every window holds its full-precision copy and none a ledger."""
+    inp, unit = make_unit(steps=16)
+    assert unit.copies() == (unit.n_windows, 0)
+    ever_int2 = set()
+    for t in range(16):
+        unit.step(inp.q[t, 0], inp.k_new[t, 0], inp.v_new[t, 0])
+        if (t + 1) % 2 == 0:
+            rng = np.random.default_rng(t)
+            scores = rng.standard_normal(unit.n_windows)     # churn: windows move between the tiers
+            unit.route(CFG.budget_full, CFG.budget_int2, scores=scores)
+            full, q2 = unit.resident_windows()
+            ever_int2 |= set(q2.tolist())
+            ever_int2 &= set(full.tolist()) | set(q2.tolist())
+            n_full, n_led = unit.copies()
+            assert n_full == full.size <= CFG.budget_full
+            assert sorted(unit.kw) == full.tolist() and sorted(unit.vw) == full.tolist()
+            assert sorted(unit.ledger) == sorted(ever_int2)
+            assert n_led <= CFG.budget_full + CFG.budget_int2

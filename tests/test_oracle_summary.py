@@ -1,14 +1,15 @@
 """Pins for the oracle's span summaries (SEKV's mixed-resolution term; CPU only): the summary of a window against
 an exact rational mean, the size correction against the 32 tokens it stands for when they are identical, and
-the bookkeeping of a run (one summary per evicted window, in eviction order, never changed, mass conservation)."""
+the bookkeeping of a run (one summary per evicted window, in eviction order, never changed, mass conservation),
+and the source of the summary of a window evicted from the INT2 tier (its ledger copy)."""
 from fractions import Fraction
 
 import numpy as np
 
 from kv_cache_compression_gqa_amd import configs, synth
-from oracle import attention, qevict, summary
+from oracle import attention, int2, qevict, summary
 from oracle.fp import f32_to_storage_rne, storage_to_f64
-from oracle.select import EVICTED
+from oracle.select import EVICTED, FULL
 
 CFG = configs.TINY
 
@@ -54,6 +55,9 @@ def test_size_correction_matches_identical_tokens():
 
 
 def test_run_bookkeeping():
+    """One summary per evicted window, in eviction order, never changed; mass conservation with summaries. The
+    budgets shrink at the third event, so windows are evicted from both tiers: a window evicted from FULL is
+    summarised from its full-precision copy, one evicted from INT2 from its ledger copy in the storage dtype."""
     inp = synth.make_decode(CFG, units=[0], steps=12)
     nw, t0 = int(inp.n_windows[0]), int(inp.tail0[0])
     unit = qevict.QEvictUnit(inp.k_win[0, :nw], inp.v_win[0, :nw], inp.k_tail0[0, :t0], inp.v_tail0[0, :t0],
@@ -61,6 +65,7 @@ def test_run_bookkeeping():
     plain = qevict.QEvictUnit(inp.k_win[0, :nw], inp.v_win[0, :nw], inp.k_tail0[0, :t0], inp.v_tail0[0, :t0],
                               CFG.dtype)
     seen = []
+    from_int2 = 0
     for t in range(12):
         r = unit.step(inp.q[t, 0], inp.k_new[t, 0], inp.v_new[t, 0])
         rp = plain.step(inp.q[t, 0], inp.k_new[t, 0], inp.v_new[t, 0])
@@ -72,18 +77,61 @@ def test_run_bookkeeping():
             assert np.array_equal(r.o, rp.o) and np.array_equal(r.mass, rp.mass)
         assert r.p.shape[1] == rp.p.shape[1] + n_sum
         if (t + 1) % 4 == 0:
+            bf, bq = (CFG.budget_full, CFG.budget_int2) if t < 11 else (6, 3)
             before = unit.tier.copy()
-            kw_before = unit.kw.copy()
-            vw_before = unit.vw.copy()
-            plan = unit.route(CFG.budget_full, CFG.budget_int2, scores=plain.cum)
-            plain.route(CFG.budget_full, CFG.budget_int2)
+            kw_before = dict(unit.kw)
+            vw_before = dict(unit.vw)
+            led_before = {w: dict(e) for w, e in unit.ledger.items()}
+            plan = unit.route(bf, bq, scores=plain.cum)
+            plain.route(bf, bq)
             new = list(plan.evicted)
             assert len(unit.sum_k) == n_sum + len(new)
             for i, w in enumerate(new):
                 assert before[w] != EVICTED
-                assert np.array_equal(unit.sum_k[n_sum + i], summary.summarize(kw_before[w], CFG.dtype))
-                assert np.array_equal(unit.sum_v[n_sum + i], summary.summarize(vw_before[w], CFG.dtype))
+                if before[w] == FULL:
+                    ks, vs = kw_before[w], vw_before[w]
+                else:
+                    e = led_before[w]
+                    ks = f32_to_storage_rne(int2.dequantize(e["kc"], e["ks"], e["kz"]), CFG.dtype)
+                    vs = f32_to_storage_rne(int2.dequantize(e["vc"], e["vs"], e["vz"]), CFG.dtype)
+                    from_int2 += 1
+                assert np.array_equal(unit.sum_k[n_sum + i], summary.summarize(ks, CFG.dtype))
+                assert np.array_equal(unit.sum_v[n_sum + i], summary.summarize(vs, CFG.dtype))
             for i, (a, b) in enumerate(seen):   # earlier summaries never change
                 assert np.array_equal(unit.sum_k[i], a) and np.array_equal(unit.sum_v[i], b)
             seen = list(zip(unit.sum_k, unit.sum_v))
+    assert from_int2 > 0
     assert len(unit.sum_k) == int(np.count_nonzero(unit.tier == EVICTED))
+
+
+def _grid_window(rng, dtype):
+    """[32][128] storage patterns whose every (token, 32-element group) is on the grid z + k s, k = 0..3, with
+    both ends present and z, s, every value exact in fp16 and bf16: the INT2 quantiser recovers it exactly."""
+    out = np.empty((32, 128))
+    for t in range(32):
+        for g in range(4):
+            z = -2.0 + 0.25 * rng.integers(0, 8)
+            s = 0.125 * rng.integers(1, 5)
+            k = rng.integers(0, 4, 32)
+            k[rng.choice(32, 2, replace=False)] = (0, 3)
+            out[t, 32 * g:32 * g + 32] = z + k * s
+    return synth.to_storage_bits(out, dtype)
+
+
+def test_summary_of_a_window_evicted_from_int2_is_taken_from_its_ledger():
+    """Windows on an exact INT2 grid: quantisation loses nothing, so the summary a window gets when it is evicted
+    from the INT2 tier (made from its ledger copy) equals the summary of its original data, window by window; a
+    window off the grid gets the summary of its dequantised copy, which differs from that of its original data."""
+    rng = np.random.default_rng(21)
+    for dtype in ("bf16", "f16"):
+        k_win = np.stack([_grid_window(rng, dtype) for _ in range(6)])
+        v_win = np.stack([_grid_window(rng, dtype) for _ in range(6)])
+        k_win[5] = synth.to_storage_bits(rng.standard_normal((32, 128)), dtype)   # off the grid
+        unit = qevict.QEvictUnit(k_win, v_win, k_win[0, :0], v_win[0, :0], dtype, summaries=True)
+        unit.route(1, 5, scores=np.arange(6, 0, -1.0))       # window 0 FULL, 1..5 INT2 (quantised)
+        plan = unit.route(1, 0, scores=np.arange(6, 0, -1.0))  # 1..5 evicted from INT2
+        assert list(plan.evicted) == [1, 2, 3, 4, 5]
+        for i, w in enumerate(range(1, 5)):
+            assert np.array_equal(unit.sum_k[i], summary.summarize(k_win[w], dtype)), (dtype, w)
+            assert np.array_equal(unit.sum_v[i], summary.summarize(v_win[w], dtype)), (dtype, w)
+        assert not np.array_equal(unit.sum_k[4], summary.summarize(k_win[5], dtype))
