@@ -6,16 +6,21 @@ A step is one decode step of that schedule in its routed steady state: append th
 FULL + INT2 + tail keys with the window mass and cumulative score fused in, and — every 16th step — re-route the
 windows (radix select), quantise first demotions into the write-once ledger and promote by dequantisation.
 
-Cold caches: R independent replicas (distinct seeds; >= 1 GB of cache in total, far above the 256 MB Infinity
-Cache) are stepped round-robin. Warm-up takes every replica through its first 16 full-cache steps and first
-routing event; the K timed steps are captured in one HIP graph and replayed once between barriers.
+Cold caches: R = 16 independent replicas (distinct seeds) are stepped round-robin; a routed step touches 34.4 MB
+per replica, so 15 other replicas' 516 MB pass between two visits to one, twice the 256 MB Infinity Cache.
+Warm-up takes every replica through its first 16 full-cache steps and first routing event, then replica r takes
+floor(16 r / R) more steps, so the replicas' routing events are spread evenly over the round-robin and a timed
+window of K steps holds about K / 16 of them (reported as routing_events_timed). The K timed steps are captured
+in one HIP graph and replayed once between barriers.
 
 value  = KV tokens scored + routed + attended per second = sum over timed steps of the resident positions of the
          sequence (FULL and INT2 window tokens + tail + new token) / wall time.
 roofline = the decode kernels' algorithmic bytes per launch (resident K/V bytes: 512 B per full-precision token,
          96 B per INT2 token incl. its scale/zero words, 512 B per tail token, plus q) / their average duration,
          measured with HIP events recorded around every decode launch inside the timed graph.
-cpu_baseline = the CPU oracle (fp64 numpy) on a bounded sample of the same routed steps.
+cpu_baseline = the CPU oracle (fp64 numpy, one thread) on a bounded sample of the same routed steps.
+hbm_read_probe_gbs = a read-only streaming kernel over 2 GiB (the read ceiling of this GPU); read_floor_one_launch_us
+         = one launch that only loads the routed launch's bytes in the decode kernel's per-wave pattern.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--replicas R] [--no-cpu-baseline]
 """
@@ -40,7 +45,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=128)
-    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--replicas", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch steps eagerly instead of one captured graph")
     ap.add_argument("--event-schedule", action="store_true",
@@ -96,15 +101,12 @@ def traffic_from_profile(name="decode_attn_llama3_8b_layer_32k", files=("decode_
 def cpu_baseline(cfg, min_seconds=10.0, max_steps=160):
     """Time the oracle on routed steps of the same workload: every KV-head unit of one layer is taken through its
     full-cache phase and first routing event (untimed), then routed steps (with a routing event every 16) are
-    timed, one step of every unit per round, until ``min_seconds`` of CPU work or ``max_steps`` rounds."""
+    timed, one step of every unit per round, until ``min_seconds`` of CPU work or ``max_steps`` rounds. The oracle
+    steps the units one after another in one Python thread; its numpy BLAS pool is held to one thread while it is
+    timed, so that ``cores`` is the parallelism it really uses."""
     sys.path.insert(0, ROOT)
     from kv_cache_compression_gqa_amd import synth
     from oracle.qevict import QEvictUnit
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # noqa: BLE001
-        threads = len(os.sched_getaffinity(0))
     units = cfg.n_units
     inp = synth.make_decode(cfg, steps=cfg.route_every + max_steps)
     ors = []
@@ -117,19 +119,38 @@ def cpu_baseline(cfg, min_seconds=10.0, max_steps=160):
         ors.append(o)
     tokens = 0.0
     rounds = 0
-    t0 = time.perf_counter()
-    while rounds < max_steps and (time.perf_counter() - t0) < min_seconds:
-        t = cfg.route_every + rounds
-        for j, o in enumerate(ors):
-            r = o.step(inp.q[t, j], inp.k_new[t, j], inp.v_new[t, j])
-            tokens += r.p.shape[1] / cfg.hkv    # one unit carries one KV head of the sequence's tokens
-            if (t + 1) % cfg.route_every == 0:
-                o.route(*cfg.budgets(o.n_windows))
-        rounds += 1
-    elapsed = time.perf_counter() - t0
-    return {"value": tokens / elapsed, "unit": "KV tokens/s", "cores": int(threads), "kind": "oracle",
+    with _one_thread():
+        t0 = time.perf_counter()
+        while rounds < max_steps and (time.perf_counter() - t0) < min_seconds:
+            t = cfg.route_every + rounds
+            for j, o in enumerate(ors):
+                r = o.step(inp.q[t, j], inp.k_new[t, j], inp.v_new[t, j])
+                tokens += r.p.shape[1] / cfg.hkv    # one unit carries one KV head of the sequence's tokens
+                if (t + 1) % cfg.route_every == 0:
+                    o.route(*cfg.budgets(o.n_windows))
+            rounds += 1
+        elapsed = time.perf_counter() - t0
+    return {"value": tokens / elapsed, "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{rounds} routed decode steps (routing every {cfg.route_every}) of all {units} KV-head units "
-                      f"of one 32K layer after an untimed full-cache phase; fp64 numpy oracle; {elapsed:.1f} s"}
+                      f"of one 32K layer after an untimed full-cache phase; fp64 numpy oracle, units one after "
+                      f"another in one thread (BLAS pool held to 1); {elapsed:.1f} s"}
+
+
+class _one_thread:
+    """Holds numpy's BLAS/OpenMP pools to one thread inside the block (threadpoolctl)."""
+
+    def __enter__(self):
+        try:
+            from threadpoolctl import threadpool_limits
+            self._lim = threadpool_limits(limits=1)
+        except Exception:  # noqa: BLE001
+            self._lim = None
+        return self
+
+    def __exit__(self, *exc):
+        if self._lim is not None:
+            self._lim.unregister()
+        return False
 
 
 def _copy_probe_gbs(gib=2, reps=5):
@@ -150,6 +171,52 @@ def _copy_probe_gbs(gib=2, reps=5):
     del x, y
     torch.cuda.empty_cache()
     return gbs
+
+
+def _read_probes(step_bytes, launches=64, gib=2, reps=5):
+    """The library's HBM read probes (kvc_probe.h) on a 2 GiB buffer:
+    - ``stream_gbs``: a grid-stride streaming read of the whole buffer, GB/s (the read ceiling of this GPU);
+    - ``wave_us``: one launch that only loads ``step_bytes`` (rounded to 16 KiB tasks) in the decode kernel's
+      per-wave pattern, every launch from a different slice of the buffer, ``launches`` launches captured in one
+      HIP graph and timed with one event pair on their stream: the floor of one launch that moves those bytes."""
+    import torch
+    from kv_cache_compression_gqa_amd import abi
+    L = abi.lib()
+    buf = torch.ones(gib << 30, dtype=torch.uint8, device="cuda")
+    wgs = L.kvc_probe_stream_workgroups(0)
+    sink = torch.empty(max(wgs, 1 << 16), dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+    sh = abi.stream_handle(st)
+    abi.check(L.kvc_probe_stream_read(abi.ptr(buf), buf.numel(), 0, abi.ptr(sink), sh), "kvc_probe_stream_read")
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(st)
+    for _ in range(reps):
+        abi.check(L.kvc_probe_stream_read(abi.ptr(buf), buf.numel(), 0, abi.ptr(sink), sh), "kvc_probe_stream_read")
+    b.record(st)
+    torch.cuda.synchronize()
+    stream_gbs = buf.numel() * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    task = 16384
+    nb = max(task, (int(step_bytes) + task - 1) // task * task)
+    slices = buf.numel() // nb
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gs = torch.cuda.current_stream()
+        for i in range(launches):
+            off = (i * 7 % slices) * nb
+            abi.check(L.kvc_probe_wave_read(buf.data_ptr() + off, nb, abi.ptr(sink), abi.stream_handle(gs)),
+                      "kvc_probe_wave_read")
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    a.record(st)
+    g.replay()
+    b.record(st)
+    torch.cuda.synchronize()
+    wave_us = a.elapsed_time(b) * 1e3 / launches
+    del g, buf, sink
+    torch.cuda.empty_cache()
+    return {"stream_gbs": stream_gbs, "wave_us": wave_us, "wave_bytes": nb}
 
 
 def _calibration_copy(mib):
@@ -214,11 +281,14 @@ def main():
 
     cfg = configs.LLAMA3_8B_LAYER_32K
     R = args.replicas
-    if args.warmup < cfg.route_every * R:
-        print(f"warmup raised to {cfg.route_every * R} so every replica is past its first routing event",
-              file=sys.stderr)
-        args.warmup = cfg.route_every * R
-    per_rep = (args.warmup + 2 * args.steps + R - 1) // R + 1
+    E = cfg.route_every
+    # routing phases staggered: after the full-cache phase replica r takes floor(r * E / R) more steps, so the
+    # replicas' routing events are spread evenly over the round-robin and any window of >= E steps times its share
+    offsets = [(r * E) // R for r in range(R)]
+    n_full = E * R
+    extra_rounds = max(0, -(-(args.warmup - n_full - sum(offsets)) // R))
+    warm_total = n_full + sum(offsets) + extra_rounds * R
+    per_rep = E + max(offsets) + extra_rounds + 2 * args.steps // R + 4
     torch.cuda.set_device(0)
     sessions = []
     if args.weighted:
@@ -237,7 +307,6 @@ def main():
     # warm-up: every replica through its full-cache phase and first routing event. Those first route_every steps
     # of every replica (full-cache attention, then the first routing event with its quantisation and promotions)
     # are captured in one HIP graph and timed: the full-cache phase of the schedule
-    n_full = cfg.route_every * R
     full_plan = [step_bytes_and_tokens(sessions[i % R]) for i in range(R)]
     full_ms = None
     if not args.eager:
@@ -254,18 +323,22 @@ def main():
     else:
         for i in range(n_full):
             sessions[i % R].step()
-    for i in range(n_full, args.warmup):
-        sessions[i % R].step()
+    for r in range(R):
+        for _ in range(offsets[r] + extra_rounds):
+            sessions[r].step()
     torch.cuda.synchronize()
-    print(f"warm-up done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    print(f"warm-up done ({warm_total} steps; replica offsets {offsets})", file=sys.stderr, flush=True)
     _calibration_copy(args.copy_mib)
 
     K = args.steps
     plan = []  # (bytes, positions) per timed step, from the host-side counts at the time the step is issued
+    events_timed = [0]
 
     def issue(i, events=None):
         s = sessions[i % R]
         plan.append(step_bytes_and_tokens(s))
+        if E > 0 and (s.t + 1) % E == 0:
+            events_timed[0] += 1
         s.step(events=events)
 
     # timed region: K steps, captured in one HIP graph and replayed once (or launched eagerly with --eager)
@@ -274,7 +347,7 @@ def main():
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             for i in range(K):
-                issue(args.warmup + i)
+                issue(i)
         torch.cuda.synchronize()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -282,7 +355,7 @@ def main():
         graph.replay()
     else:
         for i in range(K):
-            issue(args.warmup + i)
+            issue(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     timed_plan = list(plan)
@@ -304,7 +377,7 @@ def main():
         kgraph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(kgraph):
             for i in range(K):
-                issue_decode(args.warmup + K + i)
+                issue_decode(K + i)
         torch.cuda.synchronize()
         ev0.record()
         kgraph.replay()
@@ -315,7 +388,7 @@ def main():
             busy.fill_(1.0)
         ev0.record()
         for i in range(K):
-            issue_decode(args.warmup + K + i)
+            issue_decode(K + i)
         ev1.record()
         del busy
     torch.cuda.synchronize()
@@ -336,11 +409,12 @@ def main():
         "metric": "KV tokens scored+routed+attended/s per decode step; % of HBM roofline",
         "value": total_pos / wall,
         "unit": "KV tokens/s",
-        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": wall / K * 1e3,
+        "n_gpus": 1, "steps": K, "warmup": warm_total, "ms_per_step": wall / K * 1e3,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg.name, "batch": 1, "q_heads": cfg.hq, "kv_heads": cfg.hkv, "head_dim": 128,
                    "context": cfg.context, "window": cfg.window, "tiers": "20% full / 30% int2 / 50% evicted",
                    "route_every": cfg.route_every, "phase": "routed steady state", "replicas": R,
+                   "routing_events_timed": events_timed[0], "replica_step_offsets": offsets,
                    "window_score": "attention mass x |V W_O|_1 (CriticalKV norms)" if args.weighted else
                    "attention mass",
                    "evicted_windows": "span summaries (mean key/value, logit + ln 32)" if args.summaries else "dropped",
@@ -358,6 +432,11 @@ def main():
                      "algorithmic_bytes_per_launch": avg_bytes},
     }
     rec["hbm_copy_probe_gbs"] = _copy_probe_gbs()
+    probe = _read_probes(avg_bytes)
+    rec["hbm_read_probe_gbs"] = probe["stream_gbs"]
+    rec["roofline"]["frac_of_read_probe"] = achieved / probe["stream_gbs"]
+    rec["read_floor_one_launch_us"] = probe["wave_us"]
+    rec["read_floor_bytes"] = probe["wave_bytes"]
     if not args.no_cpu_baseline and not (args.weighted or args.summaries or args.event_schedule):
         print("timing the CPU oracle sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = _with_host(cpu_baseline(cfg))

@@ -96,8 +96,11 @@ class KvcDiagArgs(C.Structure):
                 ("group", C.c_int32), ("head_dim", C.c_int32)]
 
 
-# name -> (restype, argtypes); every symbol include/kvc.h declares
+# name -> (restype, argtypes); every symbol include/kvc.h and include/kvc_probe.h declare
 SIGNATURES = {
+    "kvc_probe_stream_workgroups": (C.c_int, [C.c_int32]),
+    "kvc_probe_stream_read": (C.c_int, [P, C.c_size_t, C.c_int32, P, P]),
+    "kvc_probe_wave_read": (C.c_int, [P, C.c_size_t, P, P]),
     "kvc_abi_version": (C.c_int, []),
     "kvc_status_str": (C.c_char_p, [C.c_int]),
     "kvc_decode_attn_workspace": (C.c_size_t, [C.POINTER(KvcCache), C.POINTER(KvcDecodeArgs)]),

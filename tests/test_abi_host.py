@@ -12,9 +12,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def declared_functions():
-    src = open(os.path.join(ROOT, "include", "kvc.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(kvc_[a-z0-9_]+)\s*\(", src)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", h)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(kvc_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_every_declared_symbol_is_exported_and_bound():
@@ -257,7 +261,7 @@ def test_token_weight_validation_rejects_before_launch():
 
 
 def test_header_is_plain_c_and_links(tmp_path):
-    """include/kvc.h compiles as C99 with warnings as errors, and a C program links against the library and sees
+    """include/kvc.h and include/kvc_probe.h compile as C99 with warnings as errors, and a C program links against the library and sees
     the same ABI version the header states."""
     import shutil
     import subprocess
@@ -266,8 +270,10 @@ def test_header_is_plain_c_and_links(tmp_path):
         pytest.skip("gcc not available")
     src = tmp_path / "kvc_check.c"
     src.write_text('#include "kvc.h"\n'
+                   '#include "kvc_probe.h"\n'
                    "int main(void) {\n"
                    "  kvc_cache c; kvc_decode_args a; kvc_diag_args d; (void)c; (void)a; (void)d;\n"
+                   "  if (kvc_probe_stream_workgroups(3) != 3) return 2;\n"
                    "  return kvc_abi_version() == KVC_ABI_VERSION ? 0 : 1;\n"
                    "}\n")
     lib_dir = os.path.dirname(abi.lib_path())
@@ -277,6 +283,18 @@ def test_header_is_plain_c_and_links(tmp_path):
                         "-lkvc", f"-Wl,-rpath,{lib_dir}", "-o", str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
     assert subprocess.run([str(exe)]).returncode == 0
+
+
+def test_probe_validation_rejects_before_launch():
+    L = abi.lib()
+    assert L.kvc_probe_stream_workgroups(-1) == 0 and L.kvc_probe_stream_workgroups(12) == 12
+    assert L.kvc_probe_stream_read(None, 1024, 0, FAKE, None) == abi.KVC_E_INVALID
+    assert L.kvc_probe_stream_read(FAKE + 4, 1024, 0, FAKE, None) == abi.KVC_E_INVALID
+    assert L.kvc_probe_stream_read(FAKE, 1000, 0, FAKE, None) == abi.KVC_E_INVALID
+    assert L.kvc_probe_stream_read(FAKE, 1 << 41, 0, FAKE, None) == abi.KVC_E_UNSUPPORTED
+    assert L.kvc_probe_wave_read(FAKE, 1000, FAKE, None) == abi.KVC_E_INVALID
+    assert L.kvc_probe_wave_read(FAKE, 16384, None, None) == abi.KVC_E_INVALID
+    assert L.kvc_probe_wave_read(FAKE, 0, FAKE, None) == abi.KVC_OK
 
 
 def test_topk_validation_rejects_before_launch():
