@@ -409,6 +409,17 @@ size_t kvc_decode_attn_workspace(const kvc_cache* cache, const kvc_decode_args* 
 int kvc_decode_attn(const kvc_cache* cache, const kvc_decode_args* step, void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
 
+/* kvc_decode_attn_static: kvc_decode_attn for callers that cannot allocate device memory (code being captured
+ * into a HIP graph, serving loops that must not call hipMalloc, harnesses that forbid allocation). Same arguments,
+ * kernels and results as kvc_decode_attn, but no workspace argument: the step's scratch (split-K partials, window
+ * exp-sums) lives in a static device array of the library, kvc_decode_attn_static_max_bytes() = 16 MiB, one copy
+ * per GPU held until the process ends. A step whose kvc_decode_attn_workspace() exceeds that returns
+ * KVC_E_WORKSPACE before any GPU work. It allocates nothing; the first call on a device looks the array up on that
+ * device. Every call on one GPU uses the same array: calls that can overlap on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller. */
+int kvc_decode_attn_static(const kvc_cache* cache, const kvc_decode_args* step, hipStream_t stream);
+size_t kvc_decode_attn_static_max_bytes(void);
+
 /* Workspace for kvc_score in the given mode (KVC_SCORE_WINDOWS: same as kvc_decode_attn). */
 size_t kvc_score_workspace(int32_t mode, const void* args);
 int kvc_score(int32_t mode, const void* args, void* workspace, size_t workspace_bytes, hipStream_t stream);

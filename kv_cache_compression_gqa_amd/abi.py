@@ -105,6 +105,8 @@ SIGNATURES = {
     "kvc_status_str": (C.c_char_p, [C.c_int]),
     "kvc_decode_attn_workspace": (C.c_size_t, [C.POINTER(KvcCache), C.POINTER(KvcDecodeArgs)]),
     "kvc_decode_attn": (C.c_int, [C.POINTER(KvcCache), C.POINTER(KvcDecodeArgs), P, C.c_size_t, P]),
+    "kvc_decode_attn_static": (C.c_int, [C.POINTER(KvcCache), C.POINTER(KvcDecodeArgs), P]),
+    "kvc_decode_attn_static_max_bytes": (C.c_size_t, []),
     "kvc_score_workspace": (C.c_size_t, [C.c_int32, P]),
     "kvc_score": (C.c_int, [C.c_int32, P, P, C.c_size_t, P]),
     "kvc_route_workspace": (C.c_size_t, [C.c_int32, P]),

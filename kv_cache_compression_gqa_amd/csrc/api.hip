@@ -203,6 +203,14 @@ int kvc_decode_attn(const kvc_cache* cache, const kvc_decode_args* step, void* w
   return run_decode(cache, step, workspace, workspace_bytes, stream);
 }
 
+int kvc_decode_attn_static(const kvc_cache* cache, const kvc_decode_args* step, hipStream_t stream) {
+  const int st = check_decode(cache, step, true);
+  if (st != KVC_OK) return st;
+  return kvc::decode_static(*cache, *step, stream);
+}
+
+size_t kvc_decode_attn_static_max_bytes(void) { return kvc::kStaticScratchBytes; }
+
 size_t kvc_score_workspace(int32_t mode, const void* args) {
   if (args == nullptr) return 0;
   if (mode == KVC_SCORE_WINDOWS) {

@@ -108,6 +108,9 @@ int decode_slices(const kvc_cache& c, const kvc_decode_args& a);
 bool decode_supported(const kvc_cache& c, const kvc_decode_args& a);
 size_t decode_workspace_bytes(const kvc_cache& c, const kvc_decode_args& a);
 hipError_t launch_decode(const kvc_cache& c, const kvc_decode_args& a, void* ws, hipStream_t s);
+// kvc_decode_attn_static: the decode scratch in a static device array of this size (16 MiB per device)
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+int decode_static(const kvc_cache& c, const kvc_decode_args& a, hipStream_t s);
 hipError_t launch_route_tiers(const kvc_tier_route_args& a, hipStream_t s);
 hipError_t launch_quantize(const kvc_cache& c, const int32_t* list, const int32_t* count, int32_t stride,
                            int64_t max_total, hipStream_t s);

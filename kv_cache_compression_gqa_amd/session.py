@@ -212,22 +212,30 @@ class DecodeSession:
         finally:
             self.h_tail = saved
 
-    def step(self, probs=None, mass=None, append=True, route=True, stream=None, events=None, token_weight=None):
+    def step(self, probs=None, mass=None, append=True, route=True, stream=None, events=None, token_weight=None,
+             static_scratch=False):
         """Decode step t+1 using the pre-generated inputs of that step; routes when due. ``events`` = (before,
         after) torch events recorded on the stream around the decode launch. ``token_weight`` [U][G][>= NW*W]
         float32 weights every window key's probability per query head in the window score (e.g. the projected-value
-        norms of kvc_score(CRITICALKV)); None scores by the plain attention mass."""
+        norms of kvc_score(CRITICALKV)); None scores by the plain attention mass. ``static_scratch``: run the step
+        through kvc_decode_attn_static (the library's static scratch array; no workspace is allocated)."""
         ti = self.t
         R = self.cfg.route_every
         accumulate = self.score_schedule == "every" or (R > 0 and (ti + 1) % R == 0)
         args = self.decode_args(ti, probs=probs, mass=mass, append=append, accumulate=accumulate,
                                 token_weight=self.token_weight if token_weight is None else token_weight)
-        ws = self.workspace(args)
         L = abi.lib()
-        if events is not None:
-            events[0].record()
-        abi.check(L.kvc_decode_attn(C.byref(self._cache), C.byref(args), abi.ptr(ws), self._ws_bytes,
-                                    abi.stream_handle(stream)), "kvc_decode_attn")
+        if static_scratch:
+            if events is not None:
+                events[0].record()
+            abi.check(L.kvc_decode_attn_static(C.byref(self._cache), C.byref(args), abi.stream_handle(stream)),
+                      "kvc_decode_attn_static")
+        else:
+            ws = self.workspace(args)
+            if events is not None:
+                events[0].record()
+            abi.check(L.kvc_decode_attn(C.byref(self._cache), C.byref(args), abi.ptr(ws), self._ws_bytes,
+                                        abi.stream_handle(stream)), "kvc_decode_attn")
         if events is not None:
             events[1].record()
         if append:

@@ -87,6 +87,20 @@ def test_decode_attn_validation(cache_over, step_over, status):
     assert L.kvc_decode_attn(C.byref(c), C.byref(s), FAKE, 1 << 30, None) == status
 
 
+def test_decode_attn_static_validation_rejects_before_launch():
+    """kvc_decode_attn_static validates like kvc_decode_attn and refuses a step whose scratch exceeds its static
+    array (16 MiB) before touching the GPU."""
+    L = abi.lib()
+    assert L.kvc_decode_attn_static_max_bytes() == 16 << 20
+    c, s = good_cache(head_dim=64), good_step()
+    assert L.kvc_decode_attn_static(C.byref(c), C.byref(s), None) == abi.KVC_E_UNSUPPORTED
+    assert L.kvc_decode_attn_static(C.byref(good_cache()), C.byref(good_step(q=None)), None) == abi.KVC_E_INVALID
+    big = good_cache(n_units=4096, n_windows_max=256)
+    sb = good_step(max_full=64, max_int2=64, max_tail=10)
+    assert L.kvc_decode_attn_workspace(C.byref(big), C.byref(sb)) > 16 << 20
+    assert L.kvc_decode_attn_static(C.byref(big), C.byref(sb), None) == abi.KVC_E_WORKSPACE
+
+
 def test_decode_attn_workspace_checks():
     L = abi.lib()
     c, s = good_cache(), good_step()
