@@ -249,7 +249,7 @@ def _projected_value_norms(sess, inp, w_o, q_obs):
     from kv_cache_compression_gqa_amd import abi, criticalkv
     U, NW, W, D, G = sess.U, sess.NW, sess.W, sess.D, sess.G
     n = NW * W
-    k = sess.k_win.view(torch.bfloat16).view(U, n, D)
+    k = sess.k_full.view(torch.bfloat16).view(U, n, D)   # before the first event: slot = window
     v = torch.from_numpy(np.ascontiguousarray(inp.v_win).reshape(U, n, D).view(np.int16)).cuda().view(torch.bfloat16)
     out = criticalkv.scores(q_obs, k, v, w_o, abi.KVC_BF16)
     torch.cuda.synchronize()
@@ -320,6 +320,10 @@ def main():
         torch.cuda.synchronize()
         full_ms = (time.perf_counter() - t0) / n_full * 1e3
         del fgraph
+        for s in sessions:   # the first event moved the FULL windows into the b_full pool (inside the graph)
+            s.release_prefill_pool()
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
     else:
         for i in range(n_full):
             sessions[i % R].step()
@@ -420,6 +424,8 @@ def main():
                    "evicted_windows": "span summaries (mean key/value, logit + ln 32)" if args.summaries else "dropped",
                    "score_schedule": "routing events only" if args.event_schedule else "every step",
                    "launch": "eager" if graph is None else "hip graph",
+                   "window_bytes_per_replica": sessions[0].window_bytes(),
+                   "uncompressed_window_bytes_per_replica": sessions[0].U * sessions[0].NW * 2 * 32 * 128 * 2,
                    "full_cache_phase_ms_per_step": full_ms,
                    "full_cache_phase_bytes_per_step": full_plan[0][0],
                    "schedule_64_steps_ms_per_step": None if full_ms is None else

@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 4
+#define KVC_ABI_VERSION 5
 
 typedef enum {
   KVC_OK = 0,
@@ -55,29 +55,37 @@ typedef enum { KVC_TIER_FULL = 0, KVC_TIER_INT2 = 1, KVC_TIER_EVICTED = 2 } kvc_
 
 /* The compressed cache of U independent units. A unit is one (batch, layer, KV head); its G query heads share
  * it (grouped-query attention, QEvict page, "Mecanismos Principais"). Window w of a unit holds prefill
- * positions [w*W, (w+1)*W) (QEvict page, "Metodologia": contiguous windows). Storage is indexed by window
- * position, so promotion and demotion never move another window's data:
+ * positions [w*W, (w+1)*W) (QEvict page, "Metodologia": contiguous windows). Window data live in two slot pools
+ * whose sizes bound the cache's memory (QEvict page, "Metodologia: QEvict": routing under a fixed memory budget):
+ * a window holds a full-precision slot only while it is FULL and a ledger slot from its first demotion to its
+ * eviction; tables map windows to slots, so promotion and demotion move no other window's data.
  *
- *   k_win          [U][NW][W][D]   K storage dtype, token-major. The full-precision copy of window w, valid while
- *                                  w is FULL; rewritten with the dequantised ledger copy when w is promoted.
- *   v_win          [U][NW][D][W]   V storage dtype, head_dim-major inside each window (V^T), same lifetime.
- *   k_codes        [U][NW][W][32]  INT2 ledger, K: 32 bytes per token; byte 8*s + 2*g + h holds the codes of
+ *   k_full         [U][FS][W][D]   K storage dtype, token-major: full-precision slot s of a unit.
+ *   v_full         [U][FS][D][W]   V storage dtype, head_dim-major inside each slot (V^T).
+ *   k_codes        [U][LS][W][32]  INT2 ledger slot, K: 32 bytes per token; byte 8*s + 2*g + h holds the codes of
  *                                  head_dim 32g + 8s + 4h + e (e = 0..3) at bits 2e.
- *   k_meta         [U][NW][W][4]   one 32-bit word per (token, 32-element group g): fp16 scale in bits 0..15,
+ *   k_meta         [U][LS][W][4]   one 32-bit word per (token, 32-element group g): fp16 scale in bits 0..15,
  *                                  fp16 zero in bits 16..31. Dequantised value x = fmaf(code, scale, zero).
- *   v_codes        [U][NW][16][4][8] 16-bit words: word (r, q, dt) holds the codes of tokens 8q + e
+ *   v_codes        [U][LS][16][4][8] 16-bit words: word (r, q, dt) holds the codes of tokens 8q + e
  *                                  (e = 0..7) of head_dim 16dt + r at bits 2e.
- *   v_meta         [U][NW][4][4][8] words: word (q, g, e) = scale/zero of token 8q + e, group g.
+ *   v_meta         [U][LS][4][4][8] words: word (q, g, e) = scale/zero of token 8q + e, group g.
  *   k_tail         [U][TM][D]      unrouted tail: the partial last prefill window plus every decode-time token,
  *                                  always attended, outside the budgets.
  *   v_tail         [U][TM/32][D][32]  the same tail tokens, head_dim-major inside each 32-token block.
  *   tail_len       [U] int32       valid tail rows (advanced by kvc_decode_attn when it appends a token).
  *   n_windows      [U] int32       routable windows of the unit (<= NW).
  *   tier           [U][NW] int8    kvc_tier of every window (entries >= n_windows unused).
- *   ledgered       [U][NW] uint8   1 once the window's INT2 copy exists (write-once); cleared at eviction.
+ *   full_slot      [U][NW] int32   the full-precision slot of window w while w is FULL. When an event demotes or
+ *                                  evicts w the entry keeps the slot w held until then (the slot is free from then
+ *                                  on: see the order of calls below).
+ *   ledger_slot    [U][NW] int32   the ledger slot of window w once kvc_route has given it one (at its first
+ *                                  demotion); when an event evicts w the entry keeps the slot it held.
+ *   ledgered       [U][NW] uint8   1 once the window's INT2 copy has been written (write-once); 0 again at eviction.
  *   cum            [U][NW] float   cumulative window score (sum over steps of the window's attention mass).
  *   res_list       [U][NW] int32   resident windows: the n_full FULL ids ascending, then the n_int2 INT2 ids
  *                                  ascending.
+ *   res_slot       [U][NW] int32   the slot of each res_list entry: full-precision slot for the FULL part, ledger
+ *                                  slot for the INT2 part (written by kvc_route and kvc_repack_full).
  *   n_full, n_int2 [U] int32       lengths of the two parts of res_list.
  *   status         [1] int32       device error bits (KVC_DEV_*).
  *
@@ -89,6 +97,20 @@ typedef enum { KVC_TIER_FULL = 0, KVC_TIER_INT2 = 1, KVC_TIER_EVICTED = 2 } kvc_
  *                                  tail with logit q.k/sqrt(D) + ln 32 when step.max_summary > 0. K is token-major,
  *                                  V head_dim-major inside 32-summary blocks (the tail's layouts).
  *
+ * Slot pools. A fresh cache has every window FULL: FS >= n_windows with full_slot[w] = w (any distinct slots
+ * < FS will do), res_list = res_slot = 0, 1, ..., ledger_slot = -1, ledgered = 0. LS >= b_full + b_int2 holds
+ * every ledger copy a unit can have (one per resident window that has been INT2). After the first routing event
+ * at most b_full windows are FULL, and kvc_repack_full moves their full-precision copies into a pool of
+ * FS' >= b_full slots, so the prefill-sized pool can be released: from then on the cache holds at most
+ * (FS' * 16 KiB + LS * 3 KiB) of window data per unit.
+ *
+ * Order of the calls of one routing event. kvc_route frees the slots of the windows it demotes or evicts and
+ * gives the freed slots to the windows it promotes (full-precision slots) or demotes for the first time (ledger
+ * slots), lowest free slot first in ascending window order. The calls that read what the event freed must run
+ * before the calls that overwrite it: kvc_route, then kvc_summarize_evicted (if summaries are kept; it reads the
+ * evicted windows' freed slots), then kvc_quantize_int2 (it reads the freed full-precision slots of the windows
+ * demoted for the first time), then kvc_promote (it writes the promoted windows' new full-precision slots).
+ *
  * The layouts put, for every MFMA operand the decode kernel builds, one lane's data in one 16-byte load.
  * All K/V rows must be 16-byte aligned (every base pointer 256-byte aligned is sufficient). */
 typedef struct kvc_cache {
@@ -99,10 +121,12 @@ typedef struct kvc_cache {
   int32_t n_windows_max; /* NW >= 1 */
   int32_t tail_max;      /* TM >= 32, a multiple of 32 */
   int32_t kv_dtype;      /* kvc_dtype */
+  int32_t full_slots;    /* FS >= 1: full-precision slots per unit */
+  int32_t ledger_slots;  /* LS >= 1: ledger slots per unit */
   int32_t reserved;      /* must be 0 */
   const int32_t* n_windows;
-  void* k_win;
-  void* v_win;
+  void* k_full;
+  void* v_full;
   uint8_t* k_codes;
   uint8_t* v_codes;
   uint32_t* k_meta;
@@ -112,8 +136,11 @@ typedef struct kvc_cache {
   int32_t* tail_len;
   int8_t* tier;
   uint8_t* ledgered;
+  int32_t* full_slot;
+  int32_t* ledger_slot;
   float* cum;
   int32_t* res_list;
+  int32_t* res_slot;
   int32_t* n_full;
   int32_t* n_int2;
   int32_t* status;
@@ -177,7 +204,13 @@ typedef struct kvc_decode_args {
  * windows (tier != EVICTED) are ranked by (score desc, window index asc); ranks [0, budget_full) become FULL,
  * the next budget_int2 become INT2, the rest EVICTED — permanently (evicted windows are never ranked again).
  * Outputs, per unit:
- *   tier, res_list, n_full, n_int2 of the cache are rewritten; ledgered is cleared for evicted windows;
+ *   tier, res_list, res_slot, n_full, n_int2 of the cache are rewritten; ledgered is cleared for evicted windows;
+ *   slots: a window leaving FULL frees its full-precision slot, an evicted window frees its ledger slot; a window
+ *                                 promoted to FULL takes the lowest free full-precision slot and a window demoted
+ *                                 for the first time the lowest free ledger slot, in ascending window order
+ *                                 (full_slot / ledger_slot updated). A unit whose pools run out (FS < budget_full,
+ *                                 or LS below its ledgered windows) sets KVC_DEV_BOUND_EXCEEDED and those windows
+ *                                 get slot -1 (never read);
  *   quant_list[u][0..n_quant[u])  windows going FULL -> INT2 with no ledger copy yet (ascending): pass to
  *                                 kvc_quantize_int2 (their first demotion, the only time they are quantised);
  *   promo_list[u][0..n_promo[u])  windows going INT2 -> FULL (ascending): pass to kvc_promote.
@@ -185,6 +218,7 @@ typedef struct kvc_decode_args {
  *   scores         [U][NW] float, or NULL to rank by cache.cum. Must be finite (NaN: KVC_DEV_NAN_SCORE, the
  *                  unit keeps its tiers).
  *   budget_full, budget_int2   [U] int32 device arrays (>= 0).
+ *   n_windows_max <= 4096 (KVC_E_UNSUPPORTED above: a unit's routing state sits in one workgroup's LDS).
  *   quant_list, promo_list     [U][NW] int32;  n_quant, n_promo  [U] int32. */
 typedef struct kvc_tier_route_args {
   const kvc_cache* cache;
@@ -429,9 +463,10 @@ size_t kvc_route_workspace(int32_t mode, const void* args);
 int kvc_route(int32_t mode, const void* args, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Write-once INT2 quantisation (QEvict page, "Mecanismos Principais", write-once quantization ledger): for
- * every listed window, K and V are quantised from their current full-precision copy into the ledger and the
+ * every listed window w, K and V are quantised from its full-precision copy (slot full_slot[w], the slot it held
+ * until the routing event that demoted it: run this before kvc_promote) into ledger slot ledger_slot[w], and the
  * window is marked ledgered. A listed window that is already ledgered is skipped and KVC_DEV_LEDGER_REWRITE is
- * set: the ledger is never rewritten.
+ * set: the ledger is never rewritten. A slot outside its pool sets KVC_DEV_BOUND_EXCEEDED (window skipped).
  *   list [U][list_stride] int32 window ids; count [U] int32 entries per unit; max_total = HOST bound of
  *   sum(count) (sizes the launch; 0 launches nothing).
  * Quantiser, per token and per 32-element group (INT2 is the width the page names; the rest is this library's
@@ -442,9 +477,9 @@ int kvc_quantize_int2(const kvc_cache* cache, const int32_t* list, const int32_t
                       int64_t max_total, hipStream_t stream);
 
 /* Promotion (QEvict page, "Mecanismos Principais": a quantized window whose cumulative score rises is
- * dequantised and promoted back to full precision): for every listed window, k_win/v_win are rewritten with
- * round-to-nearest-even(fmaf(code, scale, zero)) in the storage dtype. The ledger copy is kept. Same list
- * conventions as kvc_quantize_int2. */
+ * dequantised and promoted back to full precision): for every listed window w, full-precision slot full_slot[w]
+ * is written with round-to-nearest-even(fmaf(code, scale, zero)) in the storage dtype from ledger slot
+ * ledger_slot[w]. The ledger copy is kept. Same list conventions as kvc_quantize_int2. */
 int kvc_promote(const kvc_cache* cache, const int32_t* list, const int32_t* count, int32_t list_stride,
                 int64_t max_total, hipStream_t stream);
 
@@ -460,8 +495,11 @@ int kvc_route_diagnostics(const kvc_diag_args* args, hipStream_t stream);
 /* kvc_summarize_evicted: after a routing event, append the summary of every window evicted by it (SEKV page,
  * "Metodologia" sections 2 and 3; see k_sum above). For unit u the windows w < n_windows[u] with
  * tier_prev[u][w] != EVICTED and cache.tier[u][w] == EVICTED, ascending, get summaries n_sum[u], n_sum[u] + 1, ...
- * from their full-precision slot (k_win, v_win) as it stands; n_sum[u] advances by their count. A unit whose
- * summaries would pass sum_max keeps the first ones and raises KVC_DEV_BOUND_EXCEEDED.
+ * from the copy the cache held for them: a window evicted from FULL from its full-precision slot full_slot[w], one
+ * evicted from INT2 from its ledger slot ledger_slot[w] brought back to the storage dtype (round-to-nearest-even of
+ * fmaf(code, scale, zero), what a promotion stores). Both slots were freed by the event: call this right after
+ * kvc_route, before kvc_quantize_int2 and kvc_promote. n_sum[u] advances by the count. A unit whose summaries
+ * would pass sum_max keeps the first ones and raises KVC_DEV_BOUND_EXCEEDED.
  *   tier_prev  [U][NW] int8: the tiers before the event.
  *   max_new    HOST bound on the windows any unit evicts in this event (sizes the grid; more are an error bit).
  * Workspace: kvc_summarize_workspace(cache) bytes, any contents, 256-byte aligned. */
@@ -480,6 +518,16 @@ int kvc_summarize_evicted(const kvc_cache* cache, const int8_t* tier_prev, int32
 size_t kvc_topk_workspace(int64_t n, int64_t k);
 int kvc_topk(const float* scores, int64_t n, int64_t k, int32_t* idx_out, void* workspace, size_t workspace_bytes,
              hipStream_t stream);
+
+/* kvc_repack_full: move the full-precision copies of every unit's FULL windows into a new pool, so that the
+ * prefill-sized pool can be released once routing has cut the FULL tier to its budget (QEvict page, "Metodologia:
+ * QEvict": the cache stays within a fixed memory budget). For unit u, FULL window res_list[u][i] (i < n_full[u])
+ * is copied from slot res_slot[u][i] of cache.k_full / v_full to slot i of k_dst / v_dst ([U][dst_slots][W][D] and
+ * [U][dst_slots][D][W], storage dtype, 16-byte aligned, not overlapping the cache's pools), and full_slot and
+ * res_slot are rewritten to i. The caller then points cache.k_full / v_full at the new pool and sets
+ * cache.full_slots = dst_slots. Requires n_full[u] <= dst_slots: a unit above it sets KVC_DEV_BOUND_EXCEEDED, and
+ * its windows past dst_slots get slot -1. No workspace. */
+int kvc_repack_full(const kvc_cache* cache, void* k_dst, void* v_dst, int32_t dst_slots, hipStream_t stream);
 
 /* Reads *cache->status into *host_status (synchronises the stream) and, if clear != 0, zeroes it. */
 int kvc_read_device_status(const kvc_cache* cache, int32_t* host_status, int32_t clear, hipStream_t stream);

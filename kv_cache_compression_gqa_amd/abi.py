@@ -11,7 +11,7 @@ import os
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libkvc.so")
 _lib = None
 
-ABI_VERSION = 4  # KVC_ABI_VERSION of include/kvc.h
+ABI_VERSION = 5  # KVC_ABI_VERSION of include/kvc.h
 KVC_OK, KVC_E_INVALID, KVC_E_UNSUPPORTED, KVC_E_WORKSPACE, KVC_E_LEDGER, KVC_E_BUDGET, KVC_E_HIP = \
     0, -1, -2, -3, -4, -5, -6
 KVC_DEV_LEDGER_REWRITE, KVC_DEV_BOUND_EXCEEDED, KVC_DEV_NAN_SCORE = 0x1, 0x2, 0x4
@@ -33,11 +33,12 @@ class KvcError(RuntimeError):
 class KvcCache(C.Structure):
     _fields_ = [("n_units", C.c_int32), ("group", C.c_int32), ("head_dim", C.c_int32), ("window", C.c_int32),
                 ("n_windows_max", C.c_int32), ("tail_max", C.c_int32), ("kv_dtype", C.c_int32),
-                ("reserved", C.c_int32),
-                ("n_windows", P), ("k_win", P), ("v_win", P), ("k_codes", P), ("v_codes", P), ("k_meta", P),
+                ("full_slots", C.c_int32), ("ledger_slots", C.c_int32), ("reserved", C.c_int32),
+                ("n_windows", P), ("k_full", P), ("v_full", P), ("k_codes", P), ("v_codes", P), ("k_meta", P),
                 ("v_meta", P), ("k_tail", P), ("v_tail", P), ("tail_len", P), ("tier", P), ("ledgered", P),
-                ("cum", P), ("res_list", P), ("n_full", P), ("n_int2", P), ("status", P), ("k_sum", P),
-                ("v_sum", P), ("n_sum", P), ("sum_max", C.c_int32), ("reserved2", C.c_int32)]
+                ("full_slot", P), ("ledger_slot", P), ("cum", P), ("res_list", P), ("res_slot", P), ("n_full", P),
+                ("n_int2", P), ("status", P), ("k_sum", P), ("v_sum", P), ("n_sum", P), ("sum_max", C.c_int32),
+                ("reserved2", C.c_int32)]
 
 
 class KvcDecodeArgs(C.Structure):
@@ -123,6 +124,7 @@ SIGNATURES = {
     "kvc_topk_workspace": (C.c_size_t, [C.c_int64, C.c_int64]),
     "kvc_topk": (C.c_int, [P, C.c_int64, C.c_int64, P, P, C.c_size_t, P]),
     "kvc_summarize_evicted": (C.c_int, [C.POINTER(KvcCache), P, C.c_int32, P, C.c_size_t, P]),
+    "kvc_repack_full": (C.c_int, [C.POINTER(KvcCache), P, P, C.c_int32, P]),
 }
 
 

@@ -19,11 +19,16 @@ int check_cache(const kvc_cache* c) {
       c->tail_max < 32 || c->tail_max % 32 != 0 || c->reserved != 0) {
     return KVC_E_INVALID;
   }
-  const void* need16[] = {c->k_win, c->v_win, c->k_tail, c->v_tail, c->k_codes, c->v_codes, c->k_meta, c->v_meta};
+  if (c->full_slots < 1 || c->ledger_slots < 1 || c->full_slots > c->n_windows_max ||
+      c->ledger_slots > c->n_windows_max) {
+    return KVC_E_INVALID;
+  }
+  const void* need16[] = {c->k_full, c->v_full, c->k_tail, c->v_tail, c->k_codes, c->v_codes, c->k_meta, c->v_meta};
   for (const void* p : need16) {
     if (p == nullptr || !aligned(p, 16)) return KVC_E_INVALID;
   }
-  const void* need4[] = {c->n_windows, c->tail_len, c->cum, c->res_list, c->n_full, c->n_int2, c->status};
+  const void* need4[] = {c->n_windows, c->tail_len, c->cum, c->res_list, c->res_slot, c->full_slot, c->ledger_slot,
+                         c->n_full, c->n_int2, c->status};
   for (const void* p : need4) {
     if (p == nullptr || !aligned(p, 4)) return KVC_E_INVALID;
   }
@@ -273,6 +278,8 @@ int kvc_route(int32_t mode, const void* args, void* workspace, size_t workspace_
     const kvc_tier_route_args* a = static_cast<const kvc_tier_route_args*>(args);
     const int st = check_cache(a->cache);
     if (st != KVC_OK) return st;
+    // one workgroup per unit holds the unit's keys, flags and slot lists in LDS (about 9 bytes per window)
+    if (a->cache->n_windows_max > kvc::kRouteMaxWindows) return KVC_E_UNSUPPORTED;
     const void* ptrs[] = {a->budget_full, a->budget_int2, a->quant_list, a->n_quant, a->promo_list, a->n_promo};
     for (const void* p : ptrs) {
       if (p == nullptr || !aligned(p, 4)) return KVC_E_INVALID;
@@ -400,6 +407,14 @@ int kvc_topk(const float* scores, int64_t n, int64_t k, int32_t* idx_out, void* 
     return KVC_E_WORKSPACE;
   }
   return kvc::launch_topk(scores, n, k, idx_out, workspace, stream) == hipSuccess ? KVC_OK : KVC_E_HIP;
+}
+
+int kvc_repack_full(const kvc_cache* cache, void* k_dst, void* v_dst, int32_t dst_slots, hipStream_t stream) {
+  const int st = check_cache(cache);
+  if (st != KVC_OK) return st;
+  if (k_dst == nullptr || v_dst == nullptr || !aligned(k_dst, 16) || !aligned(v_dst, 16)) return KVC_E_INVALID;
+  if (dst_slots < 1 || dst_slots > cache->n_windows_max) return KVC_E_INVALID;
+  return kvc::launch_repack(*cache, k_dst, v_dst, dst_slots, stream) == hipSuccess ? KVC_OK : KVC_E_HIP;
 }
 
 int kvc_read_device_status(const kvc_cache* cache, int32_t* host_status, int32_t clear, hipStream_t stream) {

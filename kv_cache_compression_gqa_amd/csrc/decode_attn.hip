@@ -7,9 +7,10 @@
 // decode_partial: one workgroup of WPB waves per (unit, slice); every wave owns ONE task and issues all of its
 // loads at once, so a CU keeps its whole share of a step in flight (a decode step moves ~130 KB per CU at the
 // 32K-context shape, less than the CU's register file):
-//   * dense task: one FULL window or one 32-token tail block: K (8 KiB) and V^T (8 KiB) straight into the MFMA
-//     operand registers (16 bytes per lane per instruction);
-//   * INT2 task: QW INT2 windows: codes into registers, the per-token scale/zero words through LDS.
+//   * dense task: one FULL window (read from its full-precision slot res_slot[f]) or one 32-token tail block: K
+//     (8 KiB) and V^T (8 KiB) straight into the MFMA operand registers (16 bytes per lane per instruction);
+//   * INT2 task: QW INT2 windows (read from their ledger slots): codes into registers, the per-token scale/zero
+//     words through LDS.
 //   Tasks of a unit, in launch order: the INT2 windows in groups of QW (their loads are the most scattered and
 //   their arithmetic the longest, so they go first), the tail blocks, then FULL window res_list[f] per task.
 //   Tasks past the device counts are empty. The INT2 window ids are read at the offset the device count usually
@@ -49,8 +50,9 @@ constexpr float kLn32 = 3.4657359027997265471f;          // size correction of a
 
 struct DecodeParams {
   int NW, TM;
-  const uint16_t* k_win;
-  const uint16_t* v_win;
+  int FS, LS;              // full-precision and ledger slots per unit
+  const uint16_t* k_full;  // [U][FS][W][D]
+  const uint16_t* v_full;  // [U][FS][D][W]
   const uint8_t* k_codes;
   const uint16_t* v_codes;
   const uint32_t* k_meta;
@@ -59,6 +61,7 @@ struct DecodeParams {
   uint16_t* v_tail;
   int32_t* tail_len;
   const int32_t* res_list;
+  const int32_t* res_slot;
   const int32_t* n_full;
   const int32_t* n_int2;
   const int32_t* n_windows;
@@ -96,9 +99,9 @@ struct DecodeParams {
 // The compiler fetches kernel arguments on first use, each fetch a round trip it then waits for; these pins make
 // it fetch a kernel's arguments together at entry.
 __device__ __forceinline__ void fetch_args_partial(const DecodeParams& p) {
-  asm volatile("" ::"s"(p.NW), "s"(p.TM), "s"(p.k_win), "s"(p.v_win), "s"(p.k_codes), "s"(p.v_codes), "s"(p.k_meta),
+  asm volatile("" ::"s"(p.NW), "s"(p.TM), "s"(p.k_full), "s"(p.v_full), "s"(p.k_codes), "s"(p.v_codes), "s"(p.k_meta),
                "s"(p.v_meta), "s"(p.k_tail), "s"(p.v_tail), "s"(p.res_list), "s"(p.n_full), "s"(p.n_int2),
-               "s"(p.tail_len));
+               "s"(p.tail_len), "s"(p.res_slot), "s"(p.FS), "s"(p.LS));
   asm volatile("" ::"s"(p.q), "s"(p.k_new), "s"(p.max_full), "s"(p.max_int2), "s"(p.max_tail), "s"(p.n_tb),
                "s"(p.n_qt), "s"(p.P), "s"(p.part_ml), "s"(p.part_o), "s"(p.wsum), "s"(p.wref), "s"(p.unit_tl),
                "s"(p.wnorm), "s"(p.wstride));
@@ -306,16 +309,18 @@ __device__ __forceinline__ void weighted_sums(const f32x4 (&S)[2], const float (
   for (int r = 0; r < 4; ++r) ws[r] = row_sum16(S[0][r] * wn[r][0] + S[1][r] * wn[r][1]);
 }
 
-// One FULL window (TAIL = false, window id) or one 32-token tail block (TAIL = true, block index blk).
-// SUMM (with TAIL): one 32-summary block of the unit's span summaries, in the tail's layouts, logits + ln 32.
+// One FULL window (TAIL = false, window id, full-precision slot) or one 32-token tail block (TAIL = true, block
+// index blk). SUMM (with TAIL): one 32-summary block of the unit's span summaries, in the tail's layouts, logits +
+// ln 32.
 template <int G, class T, bool PROBS, bool TAIL, bool WEIGHTED, bool SUMM = false>
-__device__ __forceinline__ void dense_task(const DecodeParams& p, const Ctx& c, int id, int blk, int nvalid, int pos,
-                                           const u32x4 (&aq)[4], float* plds, WaveOut& wo) {
+__device__ __forceinline__ void dense_task(const DecodeParams& p, const Ctx& c, int id, int slot, int blk, int nvalid,
+                                           int pos, const u32x4 (&aq)[4], float* plds, WaveOut& wo) {
   using M = typename MfmaOf<T>::M;
   static_assert(!SUMM || (TAIL && !PROBS), "summary blocks use the tail path and no probabilities");
-  const size_t base = TAIL ? (size_t(c.u) * (SUMM ? p.SM : p.TM) + 32 * blk) * kD : (c.unit_win + id) * size_t(kW * kD);
-  const uint16_t* kb = (TAIL ? (SUMM ? p.k_sum : p.k_tail) : p.k_win) + base;
-  const uint16_t* vb = (TAIL ? (SUMM ? p.v_sum : p.v_tail) : p.v_win) + base;
+  const size_t base = TAIL ? (size_t(c.u) * (SUMM ? p.SM : p.TM) + 32 * blk) * kD
+                           : (size_t(c.u) * p.FS + slot) * size_t(kW * kD);
+  const uint16_t* kb = (TAIL ? (SUMM ? p.k_sum : p.k_tail) : p.k_full) + base;
+  const uint16_t* vb = (TAIL ? (SUMM ? p.v_sum : p.v_tail) : p.v_full) + base;
   u32x4 kr[8], vr[8];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -411,11 +416,12 @@ __device__ __forceinline__ void q_group_sums(const Ctx& c, const u32x4 (&aq)[4],
   }
 }
 
-// QW INT2 windows (ok[i]: window i exists; masked windows read window 0 and contribute nothing).
+// QW INT2 windows: window ids and their ledger slots (ok[i]: window i exists; masked windows read slot 0 and
+// contribute nothing).
 template <int G, class T, bool PROBS, int QW, bool WEIGHTED>
 __device__ __forceinline__ void int2_task(const DecodeParams& p, const Ctx& c, const int (&ids)[QW],
-                                          const bool (&ok)[QW], int pos0, const u32x4 (&aq)[4], float* plds,
-                                          uint32_t* ms, WaveOut& wo) {
+                                          const int (&slots)[QW], const bool (&ok)[QW], int pos0,
+                                          const u32x4 (&aq)[4], float* plds, uint32_t* ms, WaveOut& wo) {
   using M = typename MfmaOf<T>::M;
   // all loads first: K codes (tokens col and 16 + col, bytes 8q .. 8q+7), V codes (16 bytes of this lane's
   // operand rows), and 8 bytes of each of the K and V scale/zero tables (lane l: words 2l, 2l+1)
@@ -423,7 +429,7 @@ __device__ __forceinline__ void int2_task(const DecodeParams& p, const Ctx& c, c
   uint2 km[QW], vm[QW];
 #pragma unroll
   for (int i = 0; i < QW; ++i) {
-    const size_t win = c.unit_win + ids[i];
+    const size_t win = size_t(c.u) * p.LS + slots[i];
     const uint8_t* kcb = p.k_codes + win * (kW * kCodeBytes);
     const uint2 a = ld8(kcb + c.col * kCodeBytes + 8 * c.q);
     const uint2 b = ld8(kcb + (16 + c.col) * kCodeBytes + 8 * c.q);
@@ -540,27 +546,35 @@ __global__ __launch_bounds__(WPB * kWave) __attribute__((amdgpu_waves_per_eu(4))
   c.col = lane & 15;
   c.unit_win = size_t(u) * p.NW;
   const int32_t* res = p.res_list + c.unit_win;
+  const int32_t* rslot = p.res_slot + c.unit_win;
   const int MF = p.max_full;
   // task ranges: INT2 tasks, tail blocks, span-summary blocks (SUMMARY only), FULL windows
   const int t_tail = p.n_qt, t_sum = p.n_qt + p.n_tb, t_full = t_sum + (SUMMARY ? p.n_sb : 0), t_end = t_full + MF;
   const int q0 = task * QW;    // INT2 task: first INT2 slot
   const int f = task - t_full;  // FULL task: slot in res_list
 
-  // one vector load gathers the unit's device counts (lanes 0..2) and this wave's window ids (lanes 3..): the
-  // FULL window res_list[f], or the INT2 windows at the usual offset n_full == max_full (re-read otherwise)
+  // one vector load gathers the unit's device counts (lanes 0..2), this wave's window ids (lanes 3 .. 3+QW-1)
+  // and their slots (lanes 3+QW ..): the FULL window res_list[f] and res_slot[f], or the INT2 windows at the usual
+  // offset n_full == max_full (re-read otherwise)
   int gv;
   {
-    const int ridx = min(max(task >= t_full ? f : MF + q0 + lane - 3, 0), p.NW - 1);
+    const int k = lane - 3;
+    const bool want_slot = k >= QW;
+    const int kk = want_slot ? k - QW : k;
+    const int ridx = min(max(task >= t_full ? f : MF + q0 + kk, 0), p.NW - 1);
     const int32_t* cnt = lane == 0 ? p.n_full : (lane == 1 ? p.n_int2 : p.tail_len);
-    const int32_t* gp = lane < 3 ? cnt + u : res + ridx;
+    const int32_t* gp = lane < 3 ? cnt + u : (want_slot ? rslot : res) + ridx;
     if constexpr (SUMMARY) {  // a summary-block task takes the unit's summary count in lane 3
       if (task >= t_sum && task < t_full && lane == 3) gp = p.n_sum + u;
     }
     gv = *gp;
   }
-  int sid[QW];
+  int sid[QW], sslot[QW];
 #pragma unroll
-  for (int i = 0; i < QW; ++i) sid[i] = __builtin_amdgcn_readlane(gv, 3 + i);
+  for (int i = 0; i < QW; ++i) {
+    sid[i] = __builtin_amdgcn_readlane(gv, 3 + i);
+    sslot[i] = __builtin_amdgcn_readlane(gv, 3 + QW + i);
+  }
   // device counts are clamped to the host bounds the grid was sized for, so every index stays in range
   const int nf_dev = __builtin_amdgcn_readlane(gv, 0);
   const int nq_dev = __builtin_amdgcn_readlane(gv, 1);
@@ -599,26 +613,30 @@ __global__ __launch_bounds__(WPB * kWave) __attribute__((amdgpu_waves_per_eu(4))
     if (q0 < c.nq) {
       if (c.nf != MF) {
 #pragma unroll
-        for (int i = 0; i < QW; ++i) sid[i] = res[min(c.nf + q0 + i, p.NW - 1)];
+        for (int i = 0; i < QW; ++i) {
+          sid[i] = res[min(c.nf + q0 + i, p.NW - 1)];
+          sslot[i] = rslot[min(c.nf + q0 + i, p.NW - 1)];
+        }
       }
-      int ids[QW];
+      int ids[QW], slots[QW];
       bool ok[QW];
       bool bad = false;
 #pragma unroll
       for (int i = 0; i < QW; ++i) {
-        const bool in_range = unsigned(sid[i]) < unsigned(p.NW);
+        const bool in_range = unsigned(sid[i]) < unsigned(p.NW) && unsigned(sslot[i]) < unsigned(p.LS);
         ok[i] = q0 + i < c.nq && in_range;
         bad |= q0 + i < c.nq && !in_range;
         ids[i] = ok[i] ? sid[i] : 0;
+        slots[i] = ok[i] ? sslot[i] : 0;
       }
       if (bad && lane == 0) atomicOr(p.status, KVC_DEV_BOUND_EXCEEDED);
-      int2_task<G, T, PROBS, QW, WEIGHTED>(p, c, ids, ok, (c.nf + q0) * kW, aq, plds, meta_all[wave], wo);
+      int2_task<G, T, PROBS, QW, WEIGHTED>(p, c, ids, slots, ok, (c.nf + q0) * kW, aq, plds, meta_all[wave], wo);
     }
   } else if (task < t_sum) {
     const int blk = task - t_tail;
     if (kW * blk < c.total_tail) {
-      dense_task<G, T, PROBS, true, WEIGHTED>(p, c, 0, blk, min(kW, c.total_tail - kW * blk), (c.nf + c.nq + blk) * kW, aq,
-                                    plds, wo);
+      dense_task<G, T, PROBS, true, WEIGHTED>(p, c, 0, 0, blk, min(kW, c.total_tail - kW * blk),
+                                              (c.nf + c.nq + blk) * kW, aq, plds, wo);
     }
   } else if (SUMMARY && task < t_full) {
     if constexpr (SUMMARY) {
@@ -626,14 +644,16 @@ __global__ __launch_bounds__(WPB * kWave) __attribute__((amdgpu_waves_per_eu(4))
       const int ns_dev = __builtin_amdgcn_readlane(gv, 3);
       const int ns = min(max(ns_dev, 0), p.max_sum);
       if (blk == 0 && lane == 0 && ns != ns_dev) atomicOr(p.status, KVC_DEV_BOUND_EXCEEDED);
-      if (kW * blk < ns) dense_task<G, T, false, true, WEIGHTED, true>(p, c, 0, blk, min(kW, ns - kW * blk), 0, aq, plds, wo);
+      if (kW * blk < ns) {
+        dense_task<G, T, false, true, WEIGHTED, true>(p, c, 0, 0, blk, min(kW, ns - kW * blk), 0, aq, plds, wo);
+      }
     }
   } else if (task < t_end && f < c.nf) {
-    const int id = sid[0];
-    if (unsigned(id) >= unsigned(p.NW)) {
+    const int id = sid[0], slot = sslot[0];
+    if (unsigned(id) >= unsigned(p.NW) || unsigned(slot) >= unsigned(p.FS)) {
       if (lane == 0) atomicOr(p.status, KVC_DEV_BOUND_EXCEEDED);
     } else {
-      dense_task<G, T, PROBS, false, WEIGHTED>(p, c, id, 0, kW, f * kW, aq, plds, wo);
+      dense_task<G, T, PROBS, false, WEIGHTED>(p, c, id, slot, 0, kW, f * kW, aq, plds, wo);
     }
   }
 
@@ -996,8 +1016,10 @@ hipError_t launch_decode(const kvc_cache& c, const kvc_decode_args& a, void* ws,
   DecodeParams p{};
   p.NW = c.n_windows_max;
   p.TM = c.tail_max;
-  p.k_win = static_cast<const uint16_t*>(c.k_win);
-  p.v_win = static_cast<const uint16_t*>(c.v_win);
+  p.FS = c.full_slots;
+  p.LS = c.ledger_slots;
+  p.k_full = static_cast<const uint16_t*>(c.k_full);
+  p.v_full = static_cast<const uint16_t*>(c.v_full);
   p.k_codes = c.k_codes;
   p.v_codes = reinterpret_cast<const uint16_t*>(c.v_codes);
   p.k_meta = c.k_meta;
@@ -1006,6 +1028,7 @@ hipError_t launch_decode(const kvc_cache& c, const kvc_decode_args& a, void* ws,
   p.v_tail = static_cast<uint16_t*>(c.v_tail);
   p.tail_len = c.tail_len;
   p.res_list = c.res_list;
+  p.res_slot = c.res_slot;
   p.n_full = c.n_full;
   p.n_int2 = c.n_int2;
   p.n_windows = c.n_windows;

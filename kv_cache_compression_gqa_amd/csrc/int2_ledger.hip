@@ -163,12 +163,13 @@ struct QuantIn {
   uint4 v0, v1, k0, k1, k2, k3;
 };
 
+// win: the window's full-precision slot, flat over units (u * FS + slot)
 __device__ __forceinline__ QuantIn quant_load(const kvc_cache& c, size_t win, int tok, int grp) {
   QuantIn in;
-  const uint4* vsrc = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(c.v_win) + win * kW * kD);
+  const uint4* vsrc = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(c.v_full) + win * kW * kD);
   in.v0 = vsrc[2 * threadIdx.x];
   in.v1 = vsrc[2 * threadIdx.x + 1];
-  const uint4* ksrc = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(c.k_win) + (win * kW + tok) * kD +
+  const uint4* ksrc = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(c.k_full) + (win * kW + tok) * kD +
                                                      grp * kGroupElems);
   in.k0 = ksrc[0];
   in.k1 = ksrc[1];
@@ -187,12 +188,13 @@ struct QuantLds {
   uint32_t meta[2 * kW * kGroups];      // K meta words, then V meta words, as stored
 };
 
-// Quantise one window from its loaded data (the whole workgroup; LDS-only barriers). Thread t < 128 quantises K
-// group (t/4, t%4), thread t >= 128 V group (token (t-128)/4, t%4); the results are staged in LDS and every thread
-// then writes one dword each of the K codes, the V code words and the meta words (1 KiB apiece, contiguous).
+// Quantise one window from its loaded data (the whole workgroup; LDS-only barriers) into ledger slot win (flat over
+// units, u * LS + slot) and mark window flag (u * NW + w) ledgered. Thread t < 128 quantises K group (t/4, t%4),
+// thread t >= 128 V group (token (t-128)/4, t%4); the results are staged in LDS and every thread then writes one
+// dword each of the K codes, the V code words and the meta words (1 KiB apiece, contiguous).
 template <class T>
-__device__ __forceinline__ void quant_window(const QuantIn& in, const kvc_cache& c, size_t win, QuantLds& L,
-                                             int half, int tok, int grp) {
+__device__ __forceinline__ void quant_window(const QuantIn& in, const kvc_cache& c, size_t win, size_t flag,
+                                             QuantLds& L, int half, int tok, int grp) {
   {
     uint4* dst = reinterpret_cast<uint4*>(L.vt);
     dst[2 * threadIdx.x] = in.v0;
@@ -246,7 +248,7 @@ __device__ __forceinline__ void quant_window(const QuantIn& in, const kvc_cache&
   reinterpret_cast<uint32_t*>(c.v_codes)[win * kBlock + threadIdx.x] = vpair;
   uint32_t* mdst = half == 0 ? c.k_meta + win * (kW * kGroups) : c.v_meta + win * (kW * kGroups) - kW * kGroups;
   mdst[threadIdx.x] = L.meta[threadIdx.x];  // thread t < 128: K word t; t >= 128: V word t - 128
-  c.ledgered[win] = 1;  // every thread, the same byte
+  c.ledgered[flag] = 1;  // every thread, the same byte
   lds_barrier();  // the LDS buffers are rewritten by the next window
 }
 
@@ -256,51 +258,61 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(kvc_cache c, const int
                                                           int stride, int u0, int nu) {
   __shared__ int pre[kPreWords];
   __shared__ int wsum[kBlock / kWave];
-  __shared__ int item_u[kWave], item_w[kWave], n_items;
+  __shared__ int item_src[kWave], item_dst[kWave], item_flag[kWave], n_items;
   __shared__ QuantLds L;
   const int total = unit_prefix(count, u0, nu, stride, pre, wsum);
   const int NW = c.n_windows_max;
+  const int FS = c.full_slots, LS = c.ledger_slots;
   const int NG = gridDim.x;
   const int half = threadIdx.x >> 7;         // 0 = K, 1 = V (uniform per wave)
   const int tok = (threadIdx.x & 127) >> 2;
   const int grp = threadIdx.x & 3;
-  // items f0 + i * NG (i < 64) of this workgroup, resolved by its first wave at once; ids out of range and
-  // windows already ledgered (write-once) are reported and dropped here, so every window of the loop is written
+  // items f0 + i * NG (i < 64) of this workgroup, resolved by its first wave at once with their two slots (the
+  // full-precision slot the window held until its demotion, the ledger slot routing gave it); ids or slots out of
+  // range and windows already ledgered (write-once) are reported and dropped here, so every window of the loop is
+  // written
   for (int f0 = blockIdx.x; f0 < total; f0 += kWave * NG) {
     if (threadIdx.x < kWave) {
       const int f = f0 + int(threadIdx.x) * NG;
       int u, w;
       resolve_item(list, stride, pre, u0, nu, total, f, u, w);
-      const bool ok = f < total && unsigned(w) < unsigned(NW);
-      const bool led = ok && c.ledgered[size_t(u) * NW + w] != 0;
-      const uint64_t bad = __ballot(f < total && !ok), rew = __ballot(led), keep = __ballot(ok && !led);
+      const bool in_range = f < total && unsigned(w) < unsigned(NW);
+      const size_t wi = size_t(u) * NW + (in_range ? w : 0);
+      const int fsl = in_range ? c.full_slot[wi] : 0;
+      const int lsl = in_range ? c.ledger_slot[wi] : 0;
+      const bool led = in_range && c.ledgered[wi] != 0;  // write-once: checked before the slots
+      const bool ok = in_range && !led && unsigned(fsl) < unsigned(FS) && unsigned(lsl) < unsigned(LS);
+      const uint64_t bad = __ballot(f < total && !led && !ok), rew = __ballot(led), keep = __ballot(ok);
       if (threadIdx.x == 0 && (bad | rew) != 0) {
         atomicOr(c.status, (bad != 0 ? KVC_DEV_BOUND_EXCEEDED : 0) | (rew != 0 ? KVC_DEV_LEDGER_REWRITE : 0));
       }
-      if (ok && !led) {
+      if (ok) {
         const int pos = __popcll(keep & ((uint64_t(1) << threadIdx.x) - 1));
-        item_u[pos] = u;
-        item_w[pos] = w;
+        item_src[pos] = u * FS + fsl;
+        item_dst[pos] = u * LS + lsl;
+        item_flag[pos] = int(wi);
       }
       if (threadIdx.x == 0) n_items = __popcll(keep);
     }
     lds_barrier();
     const int n = n_items;
-    auto win_of = [&](int i) { return size_t(item_u[i]) * NW + item_w[i]; };
+    auto src_of = [&](int i) { return size_t(item_src[i]); };
+    auto dst_of = [&](int i) { return size_t(item_dst[i]); };
+    auto flag_of = [&](int i) { return size_t(item_flag[i]); };
     // two buffers, as in the promotion (the load after the last window re-reads it)
     if (n > 0) {
-      QuantIn A = quant_load(c, win_of(0), tok, grp);
-      QuantIn B = quant_load(c, win_of(min(1, n - 1)), tok, grp);
-      quant_window<T>(A, c, win_of(0), L, half, tok, grp);
+      QuantIn A = quant_load(c, src_of(0), tok, grp);
+      QuantIn B = quant_load(c, src_of(min(1, n - 1)), tok, grp);
+      quant_window<T>(A, c, dst_of(0), flag_of(0), L, half, tok, grp);
       for (int i = 1; i < n; i += 2) {
-        A = quant_load(c, win_of(min(i + 1, n - 1)), tok, grp);
-        quant_window<T>(B, c, win_of(i), L, half, tok, grp);
+        A = quant_load(c, src_of(min(i + 1, n - 1)), tok, grp);
+        quant_window<T>(B, c, dst_of(i), flag_of(i), L, half, tok, grp);
         if (i + 1 >= n) break;
-        B = quant_load(c, win_of(min(i + 2, n - 1)), tok, grp);
-        quant_window<T>(A, c, win_of(i + 1), L, half, tok, grp);
+        B = quant_load(c, src_of(min(i + 2, n - 1)), tok, grp);
+        quant_window<T>(A, c, dst_of(i + 1), flag_of(i + 1), L, half, tok, grp);
       }
     }
-    lds_barrier();  // item_u / item_w are rewritten by the next batch
+    lds_barrier();  // the item lists are rewritten by the next batch
   }
 }
 
@@ -327,6 +339,7 @@ struct PromoteIn {
   uint4 vm[8];
 };
 
+// win: the ledger slot, flat over units
 __device__ __forceinline__ void promote_load(PromoteIn& in, const kvc_cache& c, size_t win, int lane) {
   const int t = lane >> 1, h = lane & 1, q = lane & 3;
   in.kc = *reinterpret_cast<const uint4*>(c.k_codes + (win * kW + t) * kCodeBytes + 16 * h);
@@ -338,12 +351,13 @@ __device__ __forceinline__ void promote_load(PromoteIn& in, const kvc_cache& c, 
   for (int k = 0; k < 8; ++k) in.vm[k] = vmp[k];
 }
 
-// One 16-byte store per K word and per V word (for a fixed dt the wave writes 1 KiB contiguously).
+// One 16-byte store per K word and per V word (for a fixed dt the wave writes 1 KiB contiguously). win: the
+// full-precision slot, flat over units.
 template <class T>
 __device__ __forceinline__ void promote_store(const PromoteIn& in, const kvc_cache& c, size_t win, int lane) {
   const int t = lane >> 1, h = lane & 1;
   const int r = lane >> 2, q = lane & 3;
-  uint16_t* krow = static_cast<uint16_t*>(c.k_win) + (win * kW + t) * kD;
+  uint16_t* krow = static_cast<uint16_t*>(c.k_full) + (win * kW + t) * kD;
   const uint32_t kcw[4] = {in.kc.x, in.kc.y, in.kc.z, in.kc.w};
   const uint32_t kmw[4] = {in.km.x, in.km.y, in.km.z, in.km.w};
 #pragma unroll
@@ -356,7 +370,7 @@ __device__ __forceinline__ void promote_store(const PromoteIn& in, const kvc_cac
     const float za[8] = {zc, zc, zc, zc, zc, zc, zc, zc};
     *reinterpret_cast<uint4*>(krow + 32 * g + 8 * s) = dequant8<T>(c16, sa, za);
   }
-  uint16_t* vbase = static_cast<uint16_t*>(c.v_win) + win * (kD * kW) + 8 * q;
+  uint16_t* vbase = static_cast<uint16_t*>(c.v_full) + win * (kD * kW) + 8 * q;
   const uint32_t vcw[4] = {in.vc.x, in.vc.y, in.vc.z, in.vc.w};
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -385,22 +399,28 @@ __global__ __launch_bounds__(kBlock) void promote_kernel(kvc_cache c, const int3
   __shared__ int wsum[kBlock / kWave];
   const int total = unit_prefix(count, u0, nu, stride, pre, wsum);
   const int NW = c.n_windows_max;
+  const int FS = c.full_slots, LS = c.ledger_slots;
   const int lane = threadIdx.x & (kWave - 1);
   const int nwaves = int(gridDim.x) * (kBlock / kWave);
   const int gw = int(blockIdx.x) * (kBlock / kWave) + int(threadIdx.x >> 6);
-  // items f0 + i * nwaves (i < 64) of this wave, one per lane, resolved at once; ids out of range are reported
-  // and dropped, so every window of the loop is written
+  // items f0 + i * nwaves (i < 64) of this wave, one per lane, resolved at once with their ledger slot (source) and
+  // full-precision slot (destination); ids or slots out of range are reported and dropped, so every window of the
+  // loop is written
   for (int f0 = gw; f0 < total; f0 += kWave * nwaves) {
     const int f = f0 + lane * nwaves;
     int u, w;
     resolve_item(list, stride, pre, u0, nu, total, f, u, w);
-    const bool ok = f < total && unsigned(w) < unsigned(NW);
+    const bool in_range = f < total && unsigned(w) < unsigned(NW);
+    const size_t wi = size_t(u) * NW + (in_range ? w : 0);
+    const int lsl = in_range ? c.ledger_slot[wi] : 0;
+    const int fsl = in_range ? c.full_slot[wi] : 0;
+    const bool ok = in_range && unsigned(fsl) < unsigned(FS) && unsigned(lsl) < unsigned(LS);
     if (lane == 0 && __ballot(f < total && !ok) != 0) atomicOr(c.status, KVC_DEV_BOUND_EXCEEDED);
     uint64_t rest = __ballot(ok);
     if (rest == 0) continue;
-    auto win_of = [&](int i) {
-      return size_t(__builtin_amdgcn_readlane(u, i)) * NW + __builtin_amdgcn_readlane(w, i);
-    };
+    const int src = u * LS + lsl, dst = u * FS + fsl;
+    auto led_of = [&](int i) { return size_t(__builtin_amdgcn_readlane(src, i)); };
+    auto win_of = [&](int i) { return size_t(__builtin_amdgcn_readlane(dst, i)); };
     auto take = [&](int cur) {  // next kept lane, or cur again when none is left
       if (rest == 0) return cur;
       const int i = __builtin_ctzll(rest);
@@ -413,17 +433,17 @@ __global__ __launch_bounds__(kBlock) void promote_kernel(kvc_cache c, const int3
     PromoteIn A, B;
     const int i0 = take(-1);
     int ib = take(i0);
-    promote_load(A, c, win_of(i0), lane);
-    promote_load(B, c, win_of(ib), lane);
+    promote_load(A, c, led_of(i0), lane);
+    promote_load(B, c, led_of(ib), lane);
     promote_store<T>(A, c, win_of(i0), lane);
     if (ib == i0) continue;
     while (true) {
       const int ia = take(ib);
-      promote_load(A, c, win_of(ia), lane);
+      promote_load(A, c, led_of(ia), lane);
       promote_store<T>(B, c, win_of(ib), lane);
       if (ia == ib) break;
       ib = take(ia);
-      promote_load(B, c, win_of(ib), lane);
+      promote_load(B, c, led_of(ib), lane);
       promote_store<T>(A, c, win_of(ia), lane);
       if (ib == ia) break;
     }

@@ -111,7 +111,9 @@ hipError_t launch_decode(const kvc_cache& c, const kvc_decode_args& a, void* ws,
 // kvc_decode_attn_static: the decode scratch in a static device array of this size (16 MiB per device)
 constexpr size_t kStaticScratchBytes = size_t(16) << 20;
 int decode_static(const kvc_cache& c, const kvc_decode_args& a, hipStream_t s);
+constexpr int kRouteMaxWindows = 4096;  // windows per unit that kvc_route(KVC_ROUTE_TIERS) takes
 hipError_t launch_route_tiers(const kvc_tier_route_args& a, hipStream_t s);
+hipError_t launch_repack(const kvc_cache& c, void* k_dst, void* v_dst, int32_t dst_slots, hipStream_t s);
 hipError_t launch_quantize(const kvc_cache& c, const int32_t* list, const int32_t* count, int32_t stride,
                            int64_t max_total, hipStream_t s);
 hipError_t launch_promote(const kvc_cache& c, const int32_t* list, const int32_t* count, int32_t stride,

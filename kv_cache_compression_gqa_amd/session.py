@@ -86,12 +86,30 @@ class DecodeSession:
         self.U, self.NW, self.G, self.D, self.W = U, NW, G, D, W
         tm = tail_max if tail_max is not None else int(inp.tail0.max()) + S + 1
         self.TM = max(32, (tm + 31) // 32 * 32)
-        self.k_win = expand_windows(_bits(inp.k_win, dev))
-        self.v_win = expand_windows(_bits(layout.v_win_to_lib(inp.v_win), dev))   # [U][NW][D][W]
-        self.k_codes = torch.zeros((U, NW, W, D // 4), dtype=torch.uint8, device=dev)
-        self.v_codes = torch.zeros((U, NW, 16, 4, 8), dtype=torch.int16, device=dev)
-        self.k_meta = torch.zeros((U, NW, W, D // 32), dtype=torch.int32, device=dev)
-        self.v_meta = torch.zeros((U, NW, 4, 4, 8), dtype=torch.int32, device=dev)
+        # budgets
+        if budgets is None:
+            bf = np.array([cfg.budgets(int(n))[0] for n in n_windows_u], np.int32)
+            bq = np.array([cfg.budgets(int(n))[1] for n in n_windows_u], np.int32)
+        else:
+            bf, bq = (np.asarray(b, np.int32) for b in budgets)
+        self.bf_host, self.bq_host = bf, bq
+        # slot pools: the prefill pool holds every window (slot = window); the ledger pool one slot per resident
+        # window (b_full + b_int2); after the first routing event the FULL windows move into a pool of b_full slots
+        # (allocated now, so that no allocation happens inside a routing event) and the prefill pool is released
+        self.FS = NW
+        self.LS = int(min(NW, max(1, int((bf.astype(np.int64) + bq).max()))))
+        self.FS_small = int(min(NW, max(1, int(bf.max()))))
+        self.k_full = expand_windows(_bits(inp.k_win, dev))                               # [U][FS][W][D]
+        self.v_full = expand_windows(_bits(layout.v_win_to_lib(inp.v_win), dev))          # [U][FS][D][W]
+        self._small = (torch.empty((U, self.FS_small, W, D), dtype=torch.int16, device=dev),
+                       torch.empty((U, self.FS_small, D, W), dtype=torch.int16, device=dev))
+        self._prefill_pool = None   # the prefill pool between the first event and its release
+        self.repacked = False
+        LS = self.LS
+        self.k_codes = torch.zeros((U, LS, W, D // 4), dtype=torch.uint8, device=dev)
+        self.v_codes = torch.zeros((U, LS, 16, 4, 8), dtype=torch.int16, device=dev)
+        self.k_meta = torch.zeros((U, LS, W, D // 32), dtype=torch.int32, device=dev)
+        self.v_meta = torch.zeros((U, LS, 4, 4, 8), dtype=torch.int32, device=dev)
         self.k_tail = torch.zeros((U, self.TM, D), dtype=torch.int16, device=dev)
         self.v_tail = torch.zeros((U, self.TM // W, D, W), dtype=torch.int16, device=dev)
         t0 = int(inp.tail0.max())
@@ -107,6 +125,9 @@ class DecodeSession:
         self.cum = torch.zeros((U, NW), dtype=torch.float32, device=dev)
         res = np.tile(np.arange(NW, dtype=np.int32), (U, 1))
         self.res_list = _dev(res, torch.int32, dev)
+        self.res_slot = self.res_list.clone()
+        self.full_slot = self.res_list.clone()
+        self.ledger_slot = torch.full((U, NW), -1, dtype=torch.int32, device=dev)
         self.n_full = _dev(n_windows_u.astype(np.int32), torch.int32, dev)
         self.n_int2 = torch.zeros(U, dtype=torch.int32, device=dev)
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -132,13 +153,6 @@ class DecodeSession:
             self.k_new = expand_steps(_bits(inp.k_new, dev))
             self.v_new = expand_steps(_bits(inp.v_new, dev))
         self.out = torch.zeros((U, G, D), dtype=torch.float32, device=dev)
-        # budgets
-        if budgets is None:
-            bf = np.array([cfg.budgets(int(n))[0] for n in n_windows_u], np.int32)
-            bq = np.array([cfg.budgets(int(n))[1] for n in n_windows_u], np.int32)
-        else:
-            bf, bq = (np.asarray(b, np.int32) for b in budgets)
-        self.bf_host, self.bq_host = bf, bq
         self.budget_full = _dev(bf, torch.int32, dev)
         self.budget_int2 = _dev(bq, torch.int32, dev)
         self.quant_list = torch.zeros((U, NW), dtype=torch.int32, device=dev)
@@ -152,12 +166,13 @@ class DecodeSession:
         self.t = 0
         self._cache = abi.KvcCache(
             n_units=U, group=G, head_dim=D, window=W, n_windows_max=NW, tail_max=self.TM,
-            kv_dtype=abi.KVC_BF16 if cfg.dtype == "bf16" else abi.KVC_F16, reserved=0,
-            n_windows=abi.ptr(self.n_windows), k_win=abi.ptr(self.k_win), v_win=abi.ptr(self.v_win),
+            kv_dtype=abi.KVC_BF16 if cfg.dtype == "bf16" else abi.KVC_F16, full_slots=self.FS, ledger_slots=self.LS,
+            reserved=0, n_windows=abi.ptr(self.n_windows), k_full=abi.ptr(self.k_full), v_full=abi.ptr(self.v_full),
             k_codes=abi.ptr(self.k_codes), v_codes=abi.ptr(self.v_codes), k_meta=abi.ptr(self.k_meta),
             v_meta=abi.ptr(self.v_meta), k_tail=abi.ptr(self.k_tail), v_tail=abi.ptr(self.v_tail),
             tail_len=abi.ptr(self.tail_len), tier=abi.ptr(self.tier), ledgered=abi.ptr(self.ledgered),
-            cum=abi.ptr(self.cum), res_list=abi.ptr(self.res_list), n_full=abi.ptr(self.n_full),
+            full_slot=abi.ptr(self.full_slot), ledger_slot=abi.ptr(self.ledger_slot), cum=abi.ptr(self.cum),
+            res_list=abi.ptr(self.res_list), res_slot=abi.ptr(self.res_slot), n_full=abi.ptr(self.n_full),
             n_int2=abi.ptr(self.n_int2), status=abi.ptr(self.status), k_sum=abi.ptr(self.k_sum),
             v_sum=abi.ptr(self.v_sum), n_sum=abi.ptr(self.n_sum), sum_max=self.SM, reserved2=0)
         self._ws = None
@@ -247,6 +262,10 @@ class DecodeSession:
 
     # -- routing event ----------------------------------------------------------------------------------------
     def route(self, scores=None, stream=None):
+        """One routing event: kvc_route, then (the order the freed slots require) kvc_summarize_evicted,
+        kvc_quantize_int2 and kvc_promote; after the first event the FULL windows move into the b_full-slot pool
+        (kvc_repack_full), and the prefill pool is released unless a graph is being captured
+        (release_prefill_pool() then)."""
         L = abi.lib()
         sh = abi.stream_handle(stream)
         if self.summaries:
@@ -256,20 +275,11 @@ class DecodeSession:
             budget_int2=abi.ptr(self.budget_int2), quant_list=abi.ptr(self.quant_list), n_quant=abi.ptr(self.n_quant),
             promo_list=abi.ptr(self.promo_list), n_promo=abi.ptr(self.n_promo))
         abi.check(L.kvc_route(abi.KVC_ROUTE_TIERS, C.byref(ra), None, 0, sh), "kvc_route")
-        # bounds of this event's lists: first demotions <= min(b_int2, FULL before); promotions <= min(b_full,
-        # INT2 before)
-        q_bound = int(np.minimum(self.bq_host, self.h_full).sum())
-        p_bound = int(np.minimum(self.bf_host, self.h_int2).sum())
-        abi.check(L.kvc_quantize_int2(C.byref(self._cache), abi.ptr(self.quant_list), abi.ptr(self.n_quant),
-                                      self.NW, q_bound, sh), "kvc_quantize_int2")
-        abi.check(L.kvc_promote(C.byref(self._cache), abi.ptr(self.promo_list), abi.ptr(self.n_promo), self.NW,
-                                p_bound, sh), "kvc_promote")
         n_res = self.h_full + self.h_int2
         new_full = np.minimum(self.bf_host, n_res)
         new_int2 = np.minimum(self.bq_host, n_res - new_full)
-        self.h_full, self.h_int2 = new_full.astype(np.int64), new_int2.astype(np.int64)
         evicted = n_res - (new_full + new_int2)
-        if self.summaries and int(evicted.max()) > 0:
+        if self.summaries and int(evicted.max()) > 0:   # reads the slots the event freed: before any rewrite
             if self._sum_ws is None:
                 need = L.kvc_summarize_workspace(C.byref(self._cache))
                 if need == 0:
@@ -279,6 +289,45 @@ class DecodeSession:
                                               abi.ptr(self._sum_ws), self._sum_ws.numel(), sh),
                       "kvc_summarize_evicted")
             self.h_sum = self.h_sum + evicted
+        # bounds of this event's lists: first demotions <= min(b_int2, FULL before); promotions <= min(b_full,
+        # INT2 before)
+        q_bound = int(np.minimum(self.bq_host, self.h_full).sum())
+        p_bound = int(np.minimum(self.bf_host, self.h_int2).sum())
+        abi.check(L.kvc_quantize_int2(C.byref(self._cache), abi.ptr(self.quant_list), abi.ptr(self.n_quant),
+                                      self.NW, q_bound, sh), "kvc_quantize_int2")
+        abi.check(L.kvc_promote(C.byref(self._cache), abi.ptr(self.promo_list), abi.ptr(self.n_promo), self.NW,
+                                p_bound, sh), "kvc_promote")
+        self.h_full, self.h_int2 = new_full.astype(np.int64), new_int2.astype(np.int64)
+        if not self.repacked and self.FS_small < self.FS:
+            k_small, v_small = self._small
+            abi.check(L.kvc_repack_full(C.byref(self._cache), abi.ptr(k_small), abi.ptr(v_small), self.FS_small, sh),
+                      "kvc_repack_full")
+            self._prefill_pool = (self.k_full, self.v_full)
+            self.k_full, self.v_full = k_small, v_small
+            self._cache.k_full, self._cache.v_full = abi.ptr(k_small), abi.ptr(v_small)
+            self._cache.full_slots = self.FS = self.FS_small
+            self.repacked = True
+            if stream is not None:   # the repack reads the prefill pool on that stream
+                for t in self._prefill_pool:
+                    t.record_stream(stream)
+            if not torch.cuda.is_current_stream_capturing():
+                self.release_prefill_pool()
+
+    def release_prefill_pool(self):
+        """Drop the prefill-sized full-precision pool once the repack that emptied it has been issued (the caching
+        allocator reuses the memory only after the stream has passed the repack)."""
+        self._prefill_pool = None
+        self._small = None
+
+    def window_bytes(self) -> int:
+        """Device bytes of window data the session holds: full-precision and ledger pools (prefill pool included
+        while it is held)."""
+        t = [self.k_full, self.v_full, self.k_codes, self.v_codes, self.k_meta, self.v_meta]
+        if self._prefill_pool is not None:
+            t += list(self._prefill_pool)
+        if self._small is not None and not self.repacked:
+            t += list(self._small)
+        return int(sum(x.numel() * x.element_size() for x in t))
 
     def device_status(self, clear=True, stream=None) -> int:
         st = C.c_int32(0)

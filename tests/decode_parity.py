@@ -5,7 +5,9 @@ Tolerances (fp32 accumulation on the GPU against the fp64 oracle):
   * per-key probabilities, window mass, cumulative score:  |g - r| <= 2e-3 * |r| + 1e-12
   * tiers, resident lists, quantise / promote lists: bit-exact when the oracle's router is fed the GPU's fp32
     cumulative scores (teacher forcing: the oracle then continues on those tiers)
-  * ledger codes + metadata and promoted full-precision windows: byte-exact.
+  * ledger codes + metadata and promoted full-precision windows: byte-exact;
+  * slots (storage is an implementation choice, so the oracle has none): checked against the library's own
+    allocation rule, every slot distinct and inside its pool; the bytes above are read through them.
 """
 from __future__ import annotations
 
@@ -15,7 +17,7 @@ import torch
 from kv_cache_compression_gqa_amd import layout, synth
 from kv_cache_compression_gqa_amd.session import DecodeSession
 from oracle.qevict import QEvictUnit
-from oracle.select import FULL, INT2
+from oracle.select import EVICTED, FULL, INT2
 
 RTOL = 2e-3
 
@@ -65,21 +67,54 @@ def step_inputs(inp, t, j, unit_map=None, plan=None):
     return inp.q[t, b], inp.k_new[t, b], inp.v_new[t, b]
 
 
-def compare_route(sess: DecodeSession, oracles, gpu_cum):
+def slot_snapshot(sess: DecodeSession):
+    """Host copy of the tables the slot check needs, taken just before a routing event."""
+    return dict(tier=sess.tier.cpu().numpy(), full_slot=sess.full_slot.cpu().numpy(),
+                ledger_slot=sess.ledger_slot.cpu().numpy(), ledgered=sess.ledgered.cpu().numpy(), FS=sess.FS,
+                LS=sess.LS, repacked=sess.repacked)
+
+
+def expected_slots(before, j, tier_after, repack_to=None):
+    """The library's slot rule for unit j (include/kvc.h, kvc_route): windows that stay FULL keep their
+    full-precision slot, resident windows that have a ledger copy keep their ledger slot; the free slots of each
+    pool, ascending, go to the promoted windows (full-precision) and to the windows demoted for the first time
+    (ledger) in ascending window order. ``repack_to``: kvc_repack_full ran after the event, so the FULL windows,
+    ascending, hold slots 0, 1, ... Returns ({window: full slot}, {window: ledger slot})."""
+    tb, fs, ls, led = (before[k][j] for k in ("tier", "full_slot", "ledger_slot", "ledgered"))
+    nw = len(tier_after)
+    kept = [w for w in range(nw) if tb[w] == FULL and tier_after[w] == FULL]
+    free = sorted(set(range(before["FS"])) - {int(fs[w]) for w in kept})
+    exp_full = {w: int(fs[w]) for w in kept}
+    for k, w in enumerate(w for w in range(nw) if tb[w] == INT2 and tier_after[w] == FULL):
+        exp_full[w] = free[k]
+    if repack_to is not None:
+        exp_full = {w: i for i, w in enumerate(sorted(exp_full))}
+    kept_l = [w for w in range(nw) if led[w] and tier_after[w] != EVICTED]
+    free_l = sorted(set(range(before["LS"])) - {int(ls[w]) for w in kept_l})
+    exp_led = {w: int(ls[w]) for w in kept_l}
+    for k, w in enumerate(w for w in range(nw) if tb[w] == FULL and tier_after[w] == INT2 and not led[w]):
+        exp_led[w] = free_l[k]
+    return exp_full, exp_led
+
+
+def compare_route(sess: DecodeSession, oracles, gpu_cum, before):
     """Routing of the oracle units (fed the GPU's cumulative scores) against the session: tiers, resident lists,
-    plan lists, ledger flags and bytes, full-precision copies of resident FULL windows. Only the checked units'
-    rows are copied to the host."""
+    plan lists, ledger flags and bytes, full-precision copies of resident FULL windows, and the slots every window
+    holds (the library's allocation rule; the copies are read through them). ``before``: slot_snapshot() taken
+    just before the event. Only the checked units' rows are copied to the host."""
     keys = sorted(oracles)
     sel = torch.tensor(keys, dtype=torch.int64, device=sess.device)
     g = lambda t: t.index_select(0, sel).cpu().numpy()  # noqa: E731
     tier, res, nf, nq = g(sess.tier), g(sess.res_list), g(sess.n_full), g(sess.n_int2)
+    rslot, fslot, lslot = g(sess.res_slot), g(sess.full_slot), g(sess.ledger_slot)
     qn, ql, pn, pl, led = g(sess.n_quant), g(sess.quant_list), g(sess.n_promo), g(sess.promo_list), g(sess.ledgered)
     kc = g(sess.k_codes)
     vc = g(sess.v_codes).view(np.uint16)
     km = g(sess.k_meta).view(np.uint32)
     vm = g(sess.v_meta).view(np.uint32)
-    kw = g(sess.k_win).view(np.uint16)
-    vw = g(sess.v_win).view(np.uint16)
+    kw = g(sess.k_full).view(np.uint16)
+    vw = g(sess.v_full).view(np.uint16)
+    repacked_now = sess.repacked and not before["repacked"]
     for r, j in enumerate(keys):
         o = oracles[j]
         nw = o.n_windows
@@ -93,14 +128,26 @@ def compare_route(sess: DecodeSession, oracles, gpu_cum):
         np.testing.assert_array_equal(pl[r, :pn[r]], plan.promoted)
         for w in range(nw):
             assert bool(led[r, w]) == (w in o.ledger), f"ledger flag unit {j} window {w}"
+        exp_full, exp_led = expected_slots(before, j, o.tier, sess.FS if repacked_now else None)
+        assert sorted(exp_full) == full.tolist() and sorted(exp_led) == sorted(o.ledger)
+        for w, sl in exp_full.items():
+            assert fslot[r, w] == sl, f"full slot unit {j} window {w}: {fslot[r, w]} != {sl}"
+        for w, sl in exp_led.items():
+            assert lslot[r, w] == sl, f"ledger slot unit {j} window {w}: {lslot[r, w]} != {sl}"
+        np.testing.assert_array_equal(rslot[r, :nf[r]], [exp_full[w] for w in full], err_msg=f"res_slot {j}")
+        np.testing.assert_array_equal(rslot[r, nf[r]:nf[r] + nq[r]], [exp_led[w] for w in q2], err_msg=f"res_slot {j}")
+        assert all(0 <= sl < sess.FS for sl in exp_full.values()) and len(set(exp_full.values())) == len(exp_full)
+        assert all(0 <= sl < sess.LS for sl in exp_led.values()) and len(set(exp_led.values())) == len(exp_led)
         for w, e in o.ledger.items():
-            assert kc[r, w].tobytes() == layout.k_codes_to_lib(e["kc"]).tobytes(), f"K codes unit {j} window {w}"
-            assert vc[r, w].tobytes() == layout.v_codes_to_lib(e["vc"]).tobytes(), f"V codes unit {j} window {w}"
-            assert km[r, w].tobytes() == layout.k_meta_to_lib(e["ks"], e["kz"]).tobytes(), f"K meta {j} {w}"
-            assert vm[r, w].tobytes() == layout.v_meta_to_lib(e["vs"], e["vz"]).tobytes(), f"V meta {j} {w}"
+            sl = exp_led[w]
+            assert kc[r, sl].tobytes() == layout.k_codes_to_lib(e["kc"]).tobytes(), f"K codes unit {j} window {w}"
+            assert vc[r, sl].tobytes() == layout.v_codes_to_lib(e["vc"]).tobytes(), f"V codes unit {j} window {w}"
+            assert km[r, sl].tobytes() == layout.k_meta_to_lib(e["ks"], e["kz"]).tobytes(), f"K meta {j} {w}"
+            assert vm[r, sl].tobytes() == layout.v_meta_to_lib(e["vs"], e["vz"]).tobytes(), f"V meta {j} {w}"
         for w in full:
-            assert kw[r, w].tobytes() == o.kw[w].tobytes(), f"K full copy unit {j} window {w}"
-            assert layout.v_win_from_lib(vw[r, w]).tobytes() == o.vw[w].tobytes(), f"V full copy unit {j} window {w}"
+            sl = exp_full[int(w)]
+            assert kw[r, sl].tobytes() == o.kw[w].tobytes(), f"K full copy unit {j} window {w}"
+            assert layout.v_win_from_lib(vw[r, sl]).tobytes() == o.vw[w].tobytes(), f"V full copy unit {j} window {w}"
     if sess.summaries:
         ns, ks, vs = g(sess.n_sum), g(sess.k_sum).view(np.uint16), g(sess.v_sum).view(np.uint16)
         for r, j in enumerate(keys):
@@ -157,9 +204,10 @@ def run_decode_parity(cfg, units=None, steps=None, check_units=None, check_steps
             rel_check(f"cum step {t} unit {j}", cum_h[j, :nw], oracles[j].cum)
         if cfg.route_every > 0 and (t + 1) % cfg.route_every == 0:
             gpu_cum = sess.cum.cpu().numpy().astype(np.float64)
+            before = slot_snapshot(sess)
             sess.route()
             torch.cuda.synchronize()
-            compare_route(sess, oracles, gpu_cum)
+            compare_route(sess, oracles, gpu_cum, before)
             log(f"step {t + 1}: routed; tiers, lists, ledger and promoted copies match")
     st = sess.device_status()
     assert st == 0, f"device status bits {st:#x}"

@@ -28,12 +28,12 @@ def test_every_declared_symbol_is_exported_and_bound():
     for n in names:
         assert hasattr(L, n), n
         assert n in abi.SIGNATURES, n
-    assert L.kvc_abi_version() == abi.ABI_VERSION == 4
+    assert L.kvc_abi_version() == abi.ABI_VERSION == 5
 
 
 def test_struct_sizes_match_header_layout():
-    # 8 int32 + 17 pointers, then 3 pointers + 2 int32 for the span summaries
-    assert C.sizeof(abi.KvcCache) == 8 * 4 + 17 * 8 + 3 * 8 + 2 * 4
+    # 10 int32 + 20 pointers, then 3 pointers + 2 int32 for the span summaries
+    assert C.sizeof(abi.KvcCache) == 10 * 4 + 20 * 8 + 3 * 8 + 2 * 4
     assert C.sizeof(abi.KvcDecodeArgs) == 6 * 8 + 6 * 4 + 2 * 8 + 2 * 4
     assert C.sizeof(abi.KvcTierRouteArgs) == 8 * 8
 
@@ -49,8 +49,8 @@ FAKE = 0x10000  # 64 KiB-aligned fake device address; validation fails before an
 
 def good_cache(**over):
     kw = dict(n_units=2, group=4, head_dim=128, window=32, n_windows_max=32, tail_max=64, kv_dtype=abi.KVC_BF16,
-              reserved=0)
-    for f, _ in abi.KvcCache._fields_[8:]:
+              full_slots=32, ledger_slots=16, reserved=0)
+    for f, _ in abi.KvcCache._fields_[10:]:
         kw[f] = FAKE
     kw.update(k_sum=None, v_sum=None, n_sum=None, sum_max=0, reserved2=0)   # no span summaries
     kw.update(over)
@@ -70,7 +70,11 @@ def good_step(**over):
     (dict(group=3), {}, abi.KVC_E_UNSUPPORTED),
     (dict(kv_dtype=7), {}, abi.KVC_E_UNSUPPORTED),
     (dict(n_units=0), {}, abi.KVC_E_INVALID),
-    (dict(k_win=None), {}, abi.KVC_E_INVALID),
+    (dict(k_full=None), {}, abi.KVC_E_INVALID),
+    (dict(full_slot=None), {}, abi.KVC_E_INVALID),
+    (dict(res_slot=FAKE + 2), {}, abi.KVC_E_INVALID),
+    (dict(full_slots=0), {}, abi.KVC_E_INVALID),
+    (dict(ledger_slots=-1), {}, abi.KVC_E_INVALID),
     (dict(k_tail=FAKE + 2), {}, abi.KVC_E_INVALID),
     ({}, dict(q=None), abi.KVC_E_INVALID),
     ({}, dict(v_new=None), abi.KVC_E_INVALID),

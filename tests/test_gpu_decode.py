@@ -15,7 +15,7 @@ import torch
 from kv_cache_compression_gqa_amd import configs, synth
 from kv_cache_compression_gqa_amd.session import DecodeSession
 from oracle import select as osel
-from tests.decode_parity import compare_route, make_oracles, run_decode_parity
+from tests.decode_parity import compare_route, make_oracles, run_decode_parity, slot_snapshot
 
 pytestmark = pytest.mark.gpu
 
@@ -125,16 +125,18 @@ def test_quantise_and_promote_adversarial_groups(gpu_lib, dtype):
     sc = np.zeros((len(inp.units), nw), np.float32)
     sc[:, :16] = np.arange(16, 0, -1)
     scores = torch.from_numpy(sc).cuda()
+    snap = slot_snapshot(sess)
     sess.route(scores=scores)
     torch.cuda.synchronize()
-    compare_route(sess, oracles, sc.astype(np.float64))
+    compare_route(sess, oracles, sc.astype(np.float64), snap)
     # promote 8..15 back to FULL, demote 0..7 to INT2 (their first demotion)
     sc2 = np.zeros_like(sc)
     sc2[:, 8:16] = 10.0
     sc2[:, 0:8] = 5.0
+    snap = slot_snapshot(sess)
     sess.route(scores=torch.from_numpy(sc2).cuda())
     torch.cuda.synchronize()
-    compare_route(sess, oracles, sc2.astype(np.float64))
+    compare_route(sess, oracles, sc2.astype(np.float64), snap)
     assert sess.device_status() == 0
 
 
@@ -150,13 +152,16 @@ def test_route_adversarial_scores(gpu_lib):
             sess = DecodeSession(inp, budgets=(np.full(2, bf), np.full(2, bq)))
             oracles = make_oracles(inp)
             sc = np.stack([case, case[::-1]]).astype(np.float32)
+            snap = slot_snapshot(sess)
             sess.route(scores=torch.from_numpy(sc).cuda())
             torch.cuda.synchronize()
-            compare_route(sess, oracles, sc.astype(np.float64))
+            compare_route(sess, oracles, sc.astype(np.float64), snap)
     log("route: 49 adversarial cases match")
 
 
 def test_write_once_violation_is_refused(gpu_lib):
+    """A second quantisation of a window that already has its ledger copy is skipped and reported, even after
+    every full-precision slot has been scribbled over: the ledger pool keeps its bytes."""
     inp = synth.make_decode(configs.TINY, steps=1)
     sess = DecodeSession(inp)
     sc = np.zeros((2, 32), np.float32)
@@ -164,28 +169,29 @@ def test_write_once_violation_is_refused(gpu_lib):
     sess.route(scores=torch.from_numpy(sc).cuda())
     torch.cuda.synchronize()
     assert sess.device_status() == 0
-    before = (sess.k_codes.clone(), sess.k_meta.clone(), sess.v_codes.clone())
-    # ask for window 10 (already ledgered) again, after scribbling over its full-precision copy
-    sess.k_win[0, 10].fill_(123)
+    before = (sess.k_codes.clone(), sess.k_meta.clone(), sess.v_codes.clone(), sess.v_meta.clone())
+    sess.k_full.fill_(123)
+    sess.v_full.fill_(123)
     lst = torch.zeros((2, 32), dtype=torch.int32, device="cuda")
-    lst[0, 0] = 10
+    lst[0, 0] = 10   # an INT2 window since the event
     cnt = torch.tensor([1, 0], dtype=torch.int32, device="cuda")
     import ctypes as C
     from kv_cache_compression_gqa_amd import abi
     abi.check(abi.lib().kvc_quantize_int2(C.byref(sess._cache), abi.ptr(lst), abi.ptr(cnt), 32, 1,
                                           abi.stream_handle()), "quantize")
     torch.cuda.synchronize()
-    assert sess.device_status() & abi.KVC_DEV_LEDGER_REWRITE
-    assert torch.equal(before[0], sess.k_codes) and torch.equal(before[1], sess.k_meta)
-    assert torch.equal(before[2], sess.v_codes)
+    assert sess.device_status() == abi.KVC_DEV_LEDGER_REWRITE
+    for a, b in zip(before, (sess.k_codes, sess.k_meta, sess.v_codes, sess.v_meta)):
+        assert torch.equal(a, b)
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_ledger_lists_over_more_units_than_one_launch_span(gpu_lib, dtype):
     """kvc_quantize_int2, then kvc_promote, on per-unit lists over 4100 units (the library serves at most 4096
     units per launch), with ragged counts (0 to 8 windows, one unit listing every window, one empty list) and
-    out-of-range ids: codes, scale/zero words, ledger flags and promoted copies are byte-exact against the oracle
-    quantiser on sampled units on both sides of the span boundary, and the bad ids set the bound status bit."""
+    out-of-range ids, every unit's windows at shuffled full-precision and ledger slots: codes, scale/zero words,
+    ledger flags and promoted copies are byte-exact against the oracle quantiser at the windows' slots on sampled
+    units on both sides of the span boundary, unlisted slots stay untouched, and the bad ids set the bound bit."""
     import ctypes as C
     from kv_cache_compression_gqa_amd import abi, layout
     from oracle.fp import f32_to_storage_rne
@@ -194,9 +200,20 @@ def test_ledger_lists_over_more_units_than_one_launch_span(gpu_lib, dtype):
     inp = synth.make_decode(cfg, steps=1)
     U = 4100
     umap = np.arange(U) % len(inp.units)
-    sess = DecodeSession(inp, unit_map=umap)
+    sess = DecodeSession(inp, unit_map=umap, budgets=(np.full(U, 16), np.full(U, 16)))
     NW = sess.NW
+    assert sess.FS == NW and sess.LS == NW
     rng = np.random.default_rng(25)
+    # shuffled slots: window w of unit u sits in full-precision slot fperm[u, w] and gets ledger slot lperm[u, w]
+    fperm = np.stack([rng.permutation(NW) for _ in range(U)]).astype(np.int64)
+    lperm = np.stack([rng.permutation(NW) for _ in range(U)]).astype(np.int64)
+    uidx = torch.arange(U, device="cuda")[:, None]
+    ft = torch.from_numpy(fperm).cuda()
+    for pool in (sess.k_full, sess.v_full):
+        orig = pool.clone()
+        pool[uidx, ft] = orig
+    sess.full_slot.copy_(ft.to(torch.int32))
+    sess.ledger_slot.copy_(torch.from_numpy(lperm).cuda().to(torch.int32))
     counts = rng.integers(0, 9, U)
     counts[[3, 4097]] = NW
     counts[[10, 4096]] = (0, 5)
@@ -225,34 +242,36 @@ def test_ledger_lists_over_more_units_than_one_launch_span(gpu_lib, dtype):
         b = int(umap[u])
         listed = {int(w) for j, w in enumerate(valid[u, :counts[u]]) if (u, j) not in bad}
         for w in range(NW):
+            sl = int(lperm[u, w])
             if w not in listed:
-                assert led[r, w] == 0 and not kc[r, w].any() and not km[r, w].any(), f"unit {u} window {w}"
+                assert led[r, w] == 0 and not kc[r, sl].any() and not km[r, sl].any(), f"unit {u} window {w}"
                 continue
             kq, ks, kz = quantize(inp.k_win[b, w], dtype)
             vq, vs, vz = quantize(inp.v_win[b, w], dtype)
             expect[(u, w)] = (kq, ks, kz, vq, vs, vz)
             assert led[r, w] == 1, f"ledger flag unit {u} window {w}"
-            assert kc[r, w].tobytes() == layout.k_codes_to_lib(kq).tobytes(), f"K codes unit {u} window {w}"
-            assert vc[r, w].tobytes() == layout.v_codes_to_lib(vq).tobytes(), f"V codes unit {u} window {w}"
-            assert km[r, w].tobytes() == layout.k_meta_to_lib(ks, kz).tobytes(), f"K meta unit {u} window {w}"
-            assert vm[r, w].tobytes() == layout.v_meta_to_lib(vs, vz).tobytes(), f"V meta unit {u} window {w}"
-    # promotion of the same lists over scribbled full-precision copies
-    sess.k_win.fill_(0x7E7E)
-    sess.v_win.fill_(0x7E7E)
+            assert kc[r, sl].tobytes() == layout.k_codes_to_lib(kq).tobytes(), f"K codes unit {u} window {w}"
+            assert vc[r, sl].tobytes() == layout.v_codes_to_lib(vq).tobytes(), f"V codes unit {u} window {w}"
+            assert km[r, sl].tobytes() == layout.k_meta_to_lib(ks, kz).tobytes(), f"K meta unit {u} window {w}"
+            assert vm[r, sl].tobytes() == layout.v_meta_to_lib(vs, vz).tobytes(), f"V meta unit {u} window {w}"
+    # promotion of the same lists over scribbled full-precision slots
+    sess.k_full.fill_(0x7E7E)
+    sess.v_full.fill_(0x7E7E)
     log("case: promote the same lists")
     abi.check(L.kvc_promote(C.byref(sess._cache), abi.ptr(lst), abi.ptr(cnt), NW, int(counts.sum()),
                             abi.stream_handle()), "promote")
     torch.cuda.synchronize()
     assert sess.device_status() == abi.KVC_DEV_BOUND_EXCEEDED
-    kw, vw = g(sess.k_win).view(np.uint16), g(sess.v_win).view(np.uint16)
+    kw, vw = g(sess.k_full).view(np.uint16), g(sess.v_full).view(np.uint16)
     for r, u in enumerate(sample):
         for w in range(NW):
+            sl = int(fperm[u, w])
             if (u, w) not in expect:
-                assert np.all(kw[r, w] == 0x7E7E) and np.all(vw[r, w] == 0x7E7E), f"unit {u} window {w} written"
+                assert np.all(kw[r, sl] == 0x7E7E) and np.all(vw[r, sl] == 0x7E7E), f"unit {u} window {w} written"
                 continue
             kq, ks, kz, vq, vs, vz = expect[(u, w)]
-            assert kw[r, w].tobytes() == f32_to_storage_rne(dequantize(kq, ks, kz), dtype).tobytes(), (u, w)
-            assert (layout.v_win_from_lib(vw[r, w]).tobytes() ==
+            assert kw[r, sl].tobytes() == f32_to_storage_rne(dequantize(kq, ks, kz), dtype).tobytes(), (u, w)
+            assert (layout.v_win_from_lib(vw[r, sl]).tobytes() ==
                     f32_to_storage_rne(dequantize(vq, vs, vz), dtype).tobytes()), (u, w)
     log(f"ledger lists over {U} units: {len(expect)} sampled windows match")
 

@@ -16,7 +16,7 @@ from kv_cache_compression_gqa_amd import configs, synth
 from kv_cache_compression_gqa_amd.session import DecodeSession, route_diagnostics
 from oracle import attention, diagnostics, qevict
 from oracle.select import EVICTED, FULL, INT2
-from tests.decode_parity import compare_route, make_oracles, run_decode_parity
+from tests.decode_parity import compare_route, make_oracles, run_decode_parity, slot_snapshot
 
 pytestmark = pytest.mark.gpu
 RTOL = 2e-3
@@ -115,10 +115,11 @@ def test_route_diagnostics_match_oracle(gpu_lib):
             tier_prev.copy_(sess.tier)
             before = {j: o.tier.copy() for j, o in oracles.items()}
             gpu_cum = sess.cum.cpu().numpy().astype(np.float64)
+            snap = slot_snapshot(sess)
             sess.route()
             counts, _ = route_diagnostics(sess.tier, sess.n_windows, G, tier_prev=tier_prev)
             torch.cuda.synchronize()
-            compare_route(sess, oracles, gpu_cum)
+            compare_route(sess, oracles, gpu_cum, snap)
             counts = counts.cpu().numpy()
             for j, o in oracles.items():
                 assert tuple(counts[j]) == diagnostics.route_counts(before[j], o.tier), f"counts event {t} unit {j}"
@@ -152,7 +153,8 @@ def test_event_schedule_plain_steps_skip_the_window_pass(gpu_lib):
                 rel_check(f"mass step {t} unit {j}", mass.cpu().numpy()[j, :o.n_windows], r.mass)
         if event:
             gpu_cum = sess.cum.cpu().numpy().astype(np.float64)
+            snap = slot_snapshot(sess)
             sess.route()
             torch.cuda.synchronize()
-            compare_route(sess, oracles, gpu_cum)
+            compare_route(sess, oracles, gpu_cum, snap)
     assert sess.device_status() == 0

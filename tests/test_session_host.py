@@ -12,7 +12,13 @@ def test_session_state_and_bounds_on_cpu():
     for cfg in (configs.TINY, dataclasses.replace(configs.TINY, context=1000, name="r")):
         inp = synth.make_decode(cfg)
         s = DecodeSession(inp, device="cpu")
-        assert s.k_win.shape == (2, inp.n_windows_max, 32, 128)
+        NW = inp.n_windows_max
+        assert s.k_full.shape == (2, NW, 32, 128) and s.FS == NW   # prefill pool: one slot per window
+        bf, bq = cfg.budgets(int(inp.n_windows.max()))
+        assert s.LS == min(NW, bf + bq) and s.k_codes.shape == (2, s.LS, 32, 32)
+        assert s.FS_small == min(NW, max(1, bf)) and not s.repacked
+        assert torch.equal(s.full_slot, s.res_list) and torch.equal(s.res_slot, s.res_list)
+        assert torch.all(s.ledger_slot == -1)
         assert s.TM >= int(inp.tail0.max()) + cfg.steps + 1
         np.testing.assert_array_equal(s.k_tail[:, :int(inp.tail0.max())].numpy().view(np.uint16),
                                       inp.k_tail0[:, :int(inp.tail0.max())])
@@ -32,3 +38,7 @@ def test_session_budget_bounds_follow_routing():
     nf = np.minimum(s.bf_host, n_res)
     nq = np.minimum(s.bq_host, n_res - nf)
     assert list(nf) == [204, 204] and list(nq) == [307, 307]
+    # window memory: the prefill pool plus the pre-allocated b_full pool, then after the first event only the
+    # b_full pool and the ledger pool (204 x 16 KiB + 511 x 3 KiB per unit)
+    assert s.LS == 511 and s.FS_small == 204
+    assert s.window_bytes() == 2 * (1024 + 204) * 16384 + 2 * 511 * 3072
