@@ -1,4 +1,4 @@
-// CriticalKV scores and two-stage selection for one layer at prefill.
+// CriticalKV scores for one layer at prefill (the two-stage selection that uses them is in two_stage.hip).
 //
 // What it computes follows the CriticalKV page ("Resumo Técnico: CriticalKV"):
 //   * "Framework Teórico": the output perturbation of dropping an entry is bounded through its attention weight A
@@ -21,9 +21,7 @@
 //   obs_combine: merges the chunks' (max, sum) per row;
 //   obs_attn<2>: recomputes the logits, p = exp(s - m) / l, and sums each head's T rows with DPP row reductions
 //     into A_{h,i};
-//   group_scores: A_g and S2_g;
-//   two_stage: one workgroup per KV head: two radix selects (8-bit digits) in (score desc, index asc) order, the
-//     second over the entries the first did not take; output ascending.
+//   group_scores: A_g and S2_g.
 #include <algorithm>
 #include <type_traits>
 
@@ -400,211 +398,6 @@ __global__ __launch_bounds__(256) void group_scores(const float* __restrict__ a_
   s2_group[i] = s2 / group;
 }
 
-// ---- two-stage selection ----------------------------------------------------------------------------------------
-// One workgroup of 1024 threads per row; thread t owns entries [64t, 64t + 64) (index order = thread order). The
-// row's scores (256 KB at most) are re-read for every pass (they stay in L2); only the per-thread taken bits are
-// kept in registers.
-constexpr int kSelThreads = 1024;
-constexpr int kSelPer = 64;
-constexpr int kSelMaxN = kSelThreads * kSelPer;
-constexpr int kSelWaves = kSelThreads / kWave;
-constexpr int kSelBatch = 16;  // float4 loads in flight per thread (all of them)
-
-__device__ __forceinline__ uint32_t sel_key(float s) {
-  const uint32_t u = __float_as_uint(s == 0.0f ? 0.0f : s);
-  return ~((u & 0x80000000u) ? ~u : (u | 0x80000000u));  // smaller key = larger score
-}
-
-struct SelShared {
-  uint32_t hist[kSelWaves][256];
-  uint32_t bins[256];
-  uint32_t wsum[kSelWaves];
-  uint32_t prefix;
-  int32_t need;
-};
-
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const uint32_t o = __shfl_up(v, d, kWave);
-    if (lane >= d) v += o;
-  }
-  return v;
-}
-
-// exclusive prefix of v over the block in thread order
-__device__ uint32_t block_excl_scan(uint32_t v, SelShared& sh) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
-  const uint32_t inc = wave_incl_scan(v);
-  if (lane == kWave - 1) sh.wsum[wave] = inc;
-  __syncthreads();
-  uint32_t base = 0;
-  for (int w = 0; w < wave; ++w) base += sh.wsum[w];
-  __syncthreads();
-  return base + inc - v;
-}
-
-// f(e, key) for each of the thread's entries e (index i0 + e < n), in ascending e, kSelBatch float4 loads at a time
-template <class F>
-__device__ __forceinline__ void for_keys(const float* __restrict__ sc, int n, int i0, F&& f) {
-#pragma unroll
-  for (int c0 = 0; c0 < kSelPer / 4; c0 += kSelBatch) {
-    float4 v[kSelBatch];
-#pragma unroll
-    for (int k = 0; k < kSelBatch; ++k) {
-      const int i = i0 + 4 * (c0 + k);
-      if (i + 3 < n) {
-        v[k] = *reinterpret_cast<const float4*>(sc + i);
-      } else {
-        v[k].x = i < n ? sc[i] : 0.0f;
-        v[k].y = i + 1 < n ? sc[i + 1] : 0.0f;
-        v[k].z = i + 2 < n ? sc[i + 2] : 0.0f;
-        v[k].w = 0.0f;
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kSelBatch; ++k) {
-      const float x[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = 4 * (c0 + k) + j;
-        if (i0 + e < n) f(e, sel_key(x[j]));
-      }
-    }
-  }
-}
-
-// Takes (sets in `taken`) the first b entries not yet taken in (key asc, index asc). Each pass: 8-bit digit
-// histograms in per-wave LDS copies, summed per bin by 256 threads, then one wave finds the bin holding the
-// need-th key. For the top digit, a per-thread four-entry count cache takes the place of most atomics; grouping
-// a wave's lanes by bin before each atomic, tried before, cost as much as the contention it saved on
-// attention-like scores and three times more on widely spread ones.
-__device__ __forceinline__ void select_stage(const float* __restrict__ sc, int n, int i0, uint64_t& taken, int b,
-                                             SelShared& sh) {
-  if (b <= 0) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
-  const uint64_t done = taken;
-  if (threadIdx.x == 0) {
-    sh.prefix = 0u;
-    sh.need = b;
-  }
-  for (int pass = 0; pass < 4; ++pass) {
-    for (int i = threadIdx.x; i < kSelWaves * 256; i += kSelThreads) (&sh.hist[0][0])[i] = 0u;
-    __syncthreads();
-    const uint32_t prefix = sh.prefix;
-    const int shift = 24 - 8 * pass;
-    if (pass == 0) {
-      // the top digit (sign and exponent bits) takes few distinct values per thread: counts gather in a four-entry
-      // per-thread cache and reach LDS when evicted or at the end
-      uint32_t cb[4] = {256u, 256u, 256u, 256u}, cc[4] = {0u, 0u, 0u, 0u};
-      for_keys(sc, n, i0, [&](int e, uint32_t key) {
-        if ((done >> e) & 1u) return;
-        const uint32_t b = key >> 24;
-        if (b == cb[0]) {
-          ++cc[0];
-        } else if (b == cb[1]) {
-          ++cc[1];
-        } else if (b == cb[2]) {
-          ++cc[2];
-        } else if (b == cb[3]) {
-          ++cc[3];
-        } else {
-          if (cc[3] != 0u) atomicAdd(&sh.hist[wave][cb[3]], cc[3]);
-          cb[3] = cb[2];
-          cc[3] = cc[2];
-          cb[2] = cb[1];
-          cc[2] = cc[1];
-          cb[1] = cb[0];
-          cc[1] = cc[0];
-          cb[0] = b;
-          cc[0] = 1u;
-        }
-      });
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (cc[j] != 0u) atomicAdd(&sh.hist[wave][cb[j]], cc[j]);
-      }
-    } else {
-      for_keys(sc, n, i0, [&](int e, uint32_t key) {
-        if (!((done >> e) & 1u) && (key >> (shift + 8)) == prefix) atomicAdd(&sh.hist[wave][(key >> shift) & 255u], 1u);
-      });
-    }
-    __syncthreads();
-    if (threadIdx.x < 256) {  // the per-wave copies summed per bin, by 256 threads at once
-      uint32_t x = 0;
-#pragma unroll
-      for (int w = 0; w < kSelWaves; ++w) x += sh.hist[w][threadIdx.x];
-      sh.bins[threadIdx.x] = x;
-    }
-    __syncthreads();
-    if (wave == 0) {
-      // lane l holds bins 4l .. 4l+3; first bin whose running count reaches need
-      uint32_t c[4], tot = 0;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        c[k] = sh.bins[4 * lane + k];
-        tot += c[k];
-      }
-      const uint32_t inc = wave_incl_scan(tot);
-      const int need = sh.need;
-      const uint64_t hit = __ballot(int(inc) >= need);
-      const int l0 = hit ? __builtin_ctzll(hit) : kWave - 1;
-      if (lane == l0) {
-        int rem = need - int(inc - tot);
-        int bin = 4 * lane;
-        for (int k = 0; k < 3 && int(c[k]) < rem; ++k) {
-          rem -= int(c[k]);
-          ++bin;
-        }
-        sh.prefix = (prefix << 8) | uint32_t(bin);
-        sh.need = rem;
-      }
-    }
-    __syncthreads();
-  }
-  const uint32_t thr = sh.prefix;
-  const int need = sh.need;
-  uint32_t ties = 0;
-  uint64_t below = 0, tie = 0;
-  for_keys(sc, n, i0, [&](int e, uint32_t key) {
-    if ((done >> e) & 1u) return;
-    below |= uint64_t(key < thr ? 1 : 0) << e;
-    tie |= uint64_t(key == thr ? 1 : 0) << e;
-  });
-  ties = uint32_t(__popcll(tie));
-  uint32_t rank = block_excl_scan(ties, sh);
-  // the first `need` threshold ties in index order are taken with every key below the threshold
-  uint64_t t = below;
-  while (tie) {
-    const int e = __builtin_ctzll(tie);
-    if (int(rank) < need) t |= uint64_t(1) << e;
-    ++rank;
-    tie &= tie - 1;
-  }
-  taken |= t;
-  __syncthreads();
-}
-
-__global__ __launch_bounds__(kSelThreads) void two_stage(const float* __restrict__ a, const float* __restrict__ s2,
-                                                         int n, int budget, int budget1, int32_t* __restrict__ idx) {
-  __shared__ SelShared sh;
-  const int row = blockIdx.x;
-  const int i0 = threadIdx.x * kSelPer;
-  uint64_t taken = 0;
-  select_stage(a + size_t(row) * n, n, i0, taken, budget1, sh);
-  select_stage(s2 + size_t(row) * n, n, i0, taken, budget - budget1, sh);
-  // ascending output: exclusive scan of per-thread counts
-  uint32_t o = block_excl_scan(uint32_t(__popcll(taken)), sh);
-  uint64_t t = taken;
-  while (t) {
-    const int e = __builtin_ctzll(t);
-    if (int(o) < budget) idx[size_t(row) * budget + o] = i0 + e;
-    ++o;
-    t &= t - 1;
-  }
-}
-
 size_t al(size_t x) { return align_up(x, 256); }
 
 int obs_chunks(const kvc_criticalkv_args& a) { return (a.n_keys + kObsChunk - 1) / kObsChunk; }
@@ -652,13 +445,6 @@ hipError_t launch_ckv(const kvc_criticalkv_args& a, void* ws, hipStream_t s) {
 
 hipError_t launch_criticalkv(const kvc_criticalkv_args& a, void* ws, hipStream_t s) {
   return a.kv_dtype == KVC_BF16 ? launch_ckv<BF16>(a, ws, s) : launch_ckv<F16>(a, ws, s);
-}
-
-size_t two_stage_workspace_bytes(const kvc_two_stage_args&) { return 256; }
-
-hipError_t launch_two_stage(const kvc_two_stage_args& a, int32_t budget1, void*, hipStream_t s) {
-  hipLaunchKernelGGL(two_stage, dim3(a.rows), dim3(kSelThreads), 0, s, a.a, a.s2, a.n, a.budget, budget1, a.idx);
-  return hipGetLastError();
 }
 
 }  // namespace kvc

@@ -91,6 +91,25 @@ def test_two_stage_ties_and_edges(gpu_lib, budget, alpha):
     _check_selection(a, s2, budget, alpha)
 
 
+def test_two_stage_constant_rows_and_degenerate_budgets(gpu_lib):
+    """Rows whose every entry is equal (all 65536 in one histogram bin: more candidates than the LDS path holds, so
+    they are ranked from global memory; the order is then the index order), a row of one entry, stage budgets of
+    0 and of everything, odd lengths."""
+    rng = np.random.default_rng(41)
+    a = np.full((2, 65536), 0.25, np.float32)
+    s2 = np.full((2, 65536), -1.5, np.float32)
+    s2[1, ::7] = 3.0
+    for budget, alpha in ((2048, 0.5), (65536, 0.5), (5000, 0.0), (5000, 1.0), (1, 1.0)):
+        _check_selection(a, s2, budget, alpha)
+    one = np.array([[0.5]], np.float32)
+    _check_selection(one, one, 1, 0.5)
+    _check_selection(one, one, 1, 0.0)
+    a = rng.standard_normal((3, 4097)).astype(np.float32)
+    s2 = rng.standard_normal((3, 4097)).astype(np.float32)
+    for budget, alpha in ((4097, 0.3), (4096, 0.0), (100, 1.0), (2049, 0.5)):
+        _check_selection(a, s2, budget, alpha)
+
+
 def test_two_stage_small_rows(gpu_lib):
     rng = np.random.default_rng(5)
     a = rng.standard_normal((5, 300)).astype(np.float32)
