@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 5
+#define KVC_ABI_VERSION 6
 
 typedef enum {
   KVC_OK = 0,
@@ -308,9 +308,14 @@ typedef struct kvc_retention_args {
  * the order (score desc, flat index asc), so it is unique.
  *   scores     [n] float, finite, 16-byte aligned; rows of row_len entries (row_len % 16 == 0, n % row_len == 0,
  *              n <= 2^31 - 8208, larger n: KVC_E_UNSUPPORTED); 0 <= m <= n.
+ *   beta, t    instead of scores (scores == NULL): the scores are DBTrimKV's log-retention computed in place,
+ *              score[r][i] = float(t - i) * logf(beta[r][i]) with i the position inside row r (the same bits as
+ *              kvc_score(KVC_SCORE_RETENTION) writes), so the score array is never written or read. beta in (0, 1),
+ *              16-byte aligned, [n] float. Exactly one of scores and beta is given.
  *   keep       [n] uint8 out, 1 = kept (16-byte aligned);  row_counts [n / row_len] int32 out: kept per row.
  *   status     int32 device error bits (KVC_DEV_NAN_SCORE: a NaN score was seen; the result is then undefined).
- * Workspace: kvc_route_workspace(KVC_ROUTE_GLOBAL_TOPM, args) bytes, any contents. */
+ * Workspace: kvc_route_workspace(KVC_ROUTE_GLOBAL_TOPM, args) bytes (about 8 n: the entries of the threshold's
+ * histogram bin are compacted into it), any contents, 256-byte aligned. */
 typedef struct kvc_topm_args {
   const float* scores;
   int64_t n;
@@ -320,6 +325,9 @@ typedef struct kvc_topm_args {
   uint8_t* keep;
   int32_t* row_counts;
   int32_t* status;
+  const float* beta; /* fused log-retention input (with scores == NULL), see above */
+  int32_t t;
+  int32_t reserved2; /* must be 0 */
 } kvc_topm_args;
 
 /* kvc_compact_pages: per-row variable-length paged lists (DBTrimKV page, "Metodologia", section 4: paged
@@ -511,10 +519,11 @@ int kvc_summarize_evicted(const kvc_cache* cache, const int8_t* tier_prev, int32
  * fixed budget: QEvict's tiers ("Metodologia: QEvict"), DBTrimKV's global top-M ("Metodologia", section 3),
  * CriticalKV's stages ("Algoritmo: Seleção Constrainda por Perturbação"). Here: the first k entries of scores in
  * the order (score desc, index asc) — a unique set — written as their indices in ascending index order.
- *   scores   [n] float, finite (a NaN makes the result undefined), 16-byte aligned.
+ *   scores   [n] float, finite (a NaN makes the order undefined; the output is still k distinct indices in
+ *            [0, n)), 16-byte aligned.
  *   idx_out  [k] int32 out, ascending.
  *   0 <= k <= n <= 2^31 - 8208 (larger n: KVC_E_UNSUPPORTED).
- * Workspace: kvc_topk_workspace(n, k) bytes, any contents, 256-byte aligned. */
+ * Workspace: kvc_topk_workspace(n, k) bytes (about 9 n), any contents, 256-byte aligned. */
 size_t kvc_topk_workspace(int64_t n, int64_t k);
 int kvc_topk(const float* scores, int64_t n, int64_t k, int32_t* idx_out, void* workspace, size_t workspace_bytes,
              hipStream_t stream);

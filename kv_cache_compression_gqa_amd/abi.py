@@ -11,7 +11,7 @@ import os
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libkvc.so")
 _lib = None
 
-ABI_VERSION = 5  # KVC_ABI_VERSION of include/kvc.h
+ABI_VERSION = 6  # KVC_ABI_VERSION of include/kvc.h
 KVC_OK, KVC_E_INVALID, KVC_E_UNSUPPORTED, KVC_E_WORKSPACE, KVC_E_LEDGER, KVC_E_BUDGET, KVC_E_HIP = \
     0, -1, -2, -3, -4, -5, -6
 KVC_DEV_LEDGER_REWRITE, KVC_DEV_BOUND_EXCEEDED, KVC_DEV_NAN_SCORE = 0x1, 0x2, 0x4
@@ -63,7 +63,7 @@ class KvcRetentionArgs(C.Structure):
 
 class KvcTopmArgs(C.Structure):
     _fields_ = [("scores", P), ("n", C.c_int64), ("m", C.c_int64), ("row_len", C.c_int32), ("reserved", C.c_int32),
-                ("keep", P), ("row_counts", P), ("status", P)]
+                ("keep", P), ("row_counts", P), ("status", P), ("beta", P), ("t", C.c_int32), ("reserved2", C.c_int32)]
 
 
 class KvcCompactArgs(C.Structure):

@@ -122,11 +122,13 @@ int check_retention(const kvc_retention_args* a) {
 }
 
 int check_topm(const kvc_topm_args* a) {
-  if (a == nullptr || a->scores == nullptr || a->keep == nullptr || a->row_counts == nullptr ||
-      a->status == nullptr || a->reserved != 0) {
+  if (a == nullptr || a->keep == nullptr || a->row_counts == nullptr || a->status == nullptr || a->reserved != 0 ||
+      a->reserved2 != 0) {
     return KVC_E_INVALID;
   }
-  if (!aligned(a->scores, 16) || !aligned(a->keep, 16) || !aligned(a->row_counts, 4) || !aligned(a->status, 4)) {
+  const float* src = a->scores != nullptr ? a->scores : a->beta;
+  if ((a->scores == nullptr) == (a->beta == nullptr)) return KVC_E_INVALID;  // exactly one input
+  if (!aligned(src, 16) || !aligned(a->keep, 16) || !aligned(a->row_counts, 4) || !aligned(a->status, 4)) {
     return KVC_E_INVALID;
   }
   if (a->row_len <= 0 || a->row_len % 16 != 0 || a->n < 0 || a->n % a->row_len != 0) return KVC_E_INVALID;

@@ -120,6 +120,23 @@ hipError_t launch_promote(const kvc_cache& c, const int32_t* list, const int32_t
                           int64_t max_total, hipStream_t s);
 
 hipError_t launch_retention_score(const kvc_retention_args& a, hipStream_t s);
+
+// Global top-M engine (topm.hip): scores from memory, or DBTrimKV's log-retention (t - i) * logf(beta) with i the
+// position inside a row, computed where it is used (beta rows need row_len % 16 == 0).
+constexpr int kTopmChunk = 8192;
+struct TopmInput {
+  const float* scores;  // [n], or nullptr with beta
+  const float* beta;    // [n] when scores is nullptr
+  int32_t t;
+  int32_t row_len;      // entries per row; n % row_len == 0
+  int64_t n;
+};
+int64_t topm_chunks(int64_t n, int32_t row_len);
+size_t topm_engine_workspace(int64_t n, int32_t row_len);
+// keep [n] out (0/1); row_counts [n / row_len] out or nullptr; status: KVC_DEV_NAN_SCORE; *chunk_kept (if given)
+// points into the workspace at the kept count of every chunk (valid once the launches have run)
+hipError_t launch_topm_engine(const TopmInput& in, int64_t m, uint8_t* keep, int32_t* row_counts, int32_t* status,
+                              void* ws, int32_t** chunk_kept, hipStream_t s);
 size_t topm_workspace_bytes(const kvc_topm_args& a);
 hipError_t launch_topm(const kvc_topm_args& a, void* ws, hipStream_t s);
 size_t compact_workspace_bytes(const kvc_compact_args& a);

@@ -12,12 +12,7 @@
 //
 // Kernels (all HBM-bound streaming passes, 256 threads, 16-byte vector accesses):
 //   retention_score: score = float(t - i) * logf(beta).
-//   top-M: a three-pass radix select on the order-preserving 32-bit image of the score (11 + 11 + 10 bits).
-//   Each pass streams the scores and builds a 2048-bin histogram of the next digit of the keys that match the
-//   prefix chosen so far, in four per-wave LDS copies, merged into global bins with one atomic per non-empty
-//   bin. A single workgroup then picks the bin holding the M-th key. The mark pass keeps every key below the
-//   threshold and counts the threshold ties per block. A scan of those counts gives each block its share of
-//   the ties, which a fix-up pass takes in index order (only blocks with ties do work).
+//   top-M: the engine of topm.hip (two passes over the scores, or over beta with the score computed in place).
 //   compaction: per (row, chunk) counts, one workgroup that scans rows and chunks (lengths, page offsets), an
 //   index pass that writes the source pool row of every output row (-1 for the unused rows of a row's last
 //   page), and a gather in output order (16 lanes x 16 bytes per 128-element row, eight rows per lane group in
@@ -53,27 +48,7 @@ __global__ __launch_bounds__(kTB) void retention_score_kernel(const float* __res
   }
 }
 
-// ---- global top-M --------------------------------------------------------------------------------------------
-struct TopmState {
-  uint32_t prefix;  // key bits chosen so far
-  uint32_t pad;
-  int64_t need;     // entries still to take among the keys that match the prefix
-};
-
-struct TopmWs {
-  TopmState* state;
-  uint32_t* hist;      // [3][kBins]
-  uint32_t* tie_cnt;   // [blocks]
-  uint32_t* tie_take;  // [blocks]
-};
-
-// order-preserving image of a finite score, inverted so that a smaller key is a larger score (+0 == -0)
-__device__ __forceinline__ uint32_t desc_key(float s) {
-  const uint32_t u = __float_as_uint(s == 0.0f ? 0.0f : s);
-  const uint32_t asc = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ~asc;
-}
-
+// ---- shared helpers ------------------------------------------------------------------------------------------
 struct BlockRange {
   int64_t beg, end;
   int64_t row;
@@ -110,217 +85,6 @@ __device__ V block_excl_scan(V v, V* wsum, V* total) {
   __syncthreads();
   *total = tot;
   return base + inc - v;
-}
-
-__global__ __launch_bounds__(kTB) void topm_clear(TopmWs ws, int32_t* row_counts, int64_t n_rows) {
-  const int64_t i = int64_t(blockIdx.x) * kTB + threadIdx.x;
-  if (i < 3 * kBins) ws.hist[i] = 0u;
-  if (i < n_rows) row_counts[i] = 0;
-}
-
-// digit of a key in pass P, and whether the key matches the prefix chosen by the earlier passes
-template <int P>
-__device__ __forceinline__ bool digit_of(uint32_t key, uint32_t prefix, uint32_t& bin) {
-  if (P == 0) {
-    bin = key >> 21;
-    return true;
-  } else if (P == 1) {
-    bin = (key >> 10) & 0x7FFu;
-    return (key >> 21) == prefix;
-  } else {
-    bin = key & 0x3FFu;
-    return (key >> 10) == prefix;
-  }
-}
-
-// A histogram workgroup of pass P takes hist_group(P) consecutive chunks of one row: one LDS clear and one flush
-// of the 2048 bins to the global histogram serve all of them (the flush's global atomics land on the same few
-// hot bins from every workgroup). Passes 0 and 1 gain; pass 2, with few matching keys, runs one chunk each. The
-// next chunk's loads are issued before the current chunk's atomics.
-constexpr int hist_group(int P) { return P == 2 ? 1 : 4; }
-
-template <int P>
-__global__ __launch_bounds__(kTB) void topm_hist(const float* __restrict__ scores, TopmWs ws, int32_t row_len) {
-  __shared__ uint32_t h[4][kBins];
-  const int wave = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < 4 * kBins; i += kTB) (&h[0][0])[i] = 0u;
-  __syncthreads();
-  const uint32_t prefix = P == 0 ? 0u : ws.state->prefix;
-  const int per_row = (row_len + kChunk - 1) / kChunk;
-  constexpr int kG = hist_group(P);
-  const int groups = (per_row + kG - 1) / kG;
-  const int64_t row = blockIdx.x / groups;
-  const int c0 = int(blockIdx.x - row * groups) * kG;
-  const int nc = min(kG, per_row - c0);
-  // every load of a chunk in flight at once (clamped into the chunk's range)
-  auto load = [&](int c, float4 (&v)[kVecPerThread]) {
-    const BlockRange r = block_range(row * per_row + c, row_len, kChunk);
-#pragma unroll
-    for (int u = 0; u < kVecPerThread; ++u) {
-      const int64_t e = min(r.beg + 4 * (threadIdx.x + kTB * u), r.end - 4);
-      v[u] = *reinterpret_cast<const float4*>(scores + e);
-    }
-  };
-  float4 v[kVecPerThread], vn[kVecPerThread];
-  load(c0, v);
-  for (int k = 0; k < nc; ++k) {
-    if (k + 1 < nc) load(c0 + k + 1, vn);
-    const BlockRange r = block_range(row * per_row + c0 + k, row_len, kChunk);
-#pragma unroll
-    for (int u = 0; u < kVecPerThread; ++u) {
-      if (r.beg + 4 * (threadIdx.x + kTB * u) >= r.end) break;
-      const float vs[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        uint32_t bin;
-        if (digit_of<P>(desc_key(vs[c]), prefix, bin)) atomicAdd(&h[wave][bin], 1u);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kVecPerThread; ++u) v[u] = vn[u];
-  }
-  __syncthreads();
-  for (int bin = threadIdx.x; bin < kBins; bin += kTB) {
-    const uint32_t s = h[0][bin] + h[1][bin] + h[2][bin] + h[3][bin];
-    if (s != 0u) atomicAdd(&ws.hist[P * kBins + bin], s);
-  }
-}
-
-// one workgroup: the bin of pass P that holds the need-th key (1-based) of the current prefix
-template <int P>
-__global__ __launch_bounds__(kTB) void topm_pick(TopmWs ws, int64_t m) {
-  constexpr int nb = P == 2 ? 1024 : kBins;
-  constexpr int per = nb / kTB;
-  constexpr int bits = P == 2 ? 10 : 11;
-  __shared__ long long wsum[kTB / kWave];
-  const long long need = P == 0 ? m : ws.state->need;
-  const uint32_t prev = P == 0 ? 0u : ws.state->prefix;
-  const uint32_t* hp = ws.hist + P * kBins + threadIdx.x * per;
-  uint32_t c[per];
-  long long mine = 0;
-#pragma unroll
-  for (int k = 0; k < per; ++k) {
-    c[k] = hp[k];
-    mine += c[k];
-  }
-  long long total;
-  const long long excl = block_excl_scan<long long>(mine, wsum, &total);
-  // the thread whose bins hold the need-th key (need <= 0: nothing to take, bin 0; need > total cannot happen)
-  const bool mine_bin = need <= 0 ? threadIdx.x == 0 : (excl < need && excl + mine >= need);
-  if (mine_bin) {
-    long long rem = need - excl;
-    int b = 0;
-    while (b < per - 1 && rem > c[b]) rem -= c[b++];
-    ws.state->prefix = (prev << bits) | uint32_t(threadIdx.x * per + b);
-    ws.state->need = need <= 0 ? 0 : rem;
-  }
-}
-
-// keep every key below the threshold; count the threshold ties of the block
-__global__ __launch_bounds__(kTB) void topm_mark(const float* __restrict__ scores, uint8_t* __restrict__ keep,
-                                                 int32_t* row_counts, TopmWs ws, int32_t row_len, int32_t* status) {
-  __shared__ uint32_t red[2][kTB / kWave];
-  const uint32_t thr = ws.state->prefix;
-  const BlockRange r = block_range(blockIdx.x, row_len, kChunk);
-  uint32_t kept = 0, ties = 0;
-  bool nan = false;
-  float4 vv[kVecPerThread];
-#pragma unroll
-  for (int u = 0; u < kVecPerThread; ++u) {
-    const int64_t e = min(r.beg + 4 * (threadIdx.x + kTB * u), r.end - 4);
-    vv[u] = *reinterpret_cast<const float4*>(scores + e);
-  }
-#pragma unroll
-  for (int u = 0; u < kVecPerThread; ++u) {
-    const int64_t e = r.beg + 4 * (threadIdx.x + kTB * u);
-    if (e >= r.end) break;
-    const float4 v = vv[u];
-    const float vs[4] = {v.x, v.y, v.z, v.w};
-    uint32_t out = 0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t key = desc_key(vs[c]);
-      nan |= vs[c] != vs[c];
-      const uint32_t k1 = key < thr ? 1u : 0u;
-      kept += k1;
-      ties += key == thr ? 1u : 0u;
-      out |= k1 << (8 * c);
-    }
-    *reinterpret_cast<uint32_t*>(keep + e) = out;
-  }
-  if (nan) atomicOr(status, KVC_DEV_NAN_SCORE);
-  kept = uint32_t(wave_sum_int(int(kept)));
-  ties = uint32_t(wave_sum_int(int(ties)));
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
-    red[0][wave] = kept;
-    red[1][wave] = ties;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t k = 0, t = 0;
-    for (int w = 0; w < kTB / kWave; ++w) {
-      k += red[0][w];
-      t += red[1][w];
-    }
-    if (k != 0u) atomicAdd(&row_counts[r.row], int(k));
-    ws.tie_cnt[blockIdx.x] = t;
-  }
-}
-
-// one workgroup: exclusive scan of the blocks' tie counts -> how many ties each block takes
-__global__ __launch_bounds__(kTB) void topm_tie_scan(TopmWs ws, int64_t n_blocks) {
-  __shared__ long long wsum[kTB / kWave];
-  const int64_t per = (n_blocks + kTB - 1) / kTB;
-  const int64_t b0 = threadIdx.x * per, b1 = min(n_blocks, b0 + per);
-  long long mine = 0;
-  for (int64_t b = b0; b < b1; ++b) mine += ws.tie_cnt[b];
-  long long total;
-  long long off = block_excl_scan<long long>(mine, wsum, &total);
-  const long long need = ws.state->need;
-  for (int64_t b = b0; b < b1; ++b) {
-    const long long c = ws.tie_cnt[b];
-    ws.tie_take[b] = uint32_t(max(0LL, min(c, need - off)));
-    off += c;
-  }
-}
-
-// blocks holding kept ties: take the first tie_take of them in index order
-__global__ __launch_bounds__(kTB) void topm_fix(const float* __restrict__ scores, uint8_t* __restrict__ keep,
-                                                int32_t* row_counts, TopmWs ws, int32_t row_len) {
-  const uint32_t take = ws.tie_take[blockIdx.x];
-  if (take == 0u) return;
-  __shared__ uint32_t wsum[kTB / kWave];
-  const uint32_t thr = ws.state->prefix;
-  const BlockRange r = block_range(blockIdx.x, row_len, kChunk);
-  uint32_t done = 0;  // ties already seen before this iteration, in index order
-  for (int64_t base = r.beg; base < r.end; base += 4 * kTB) {
-    const int64_t e = base + 4 * threadIdx.x;
-    uint32_t flags = 0, cnt = 0;
-    if (e < r.end) {
-      const float4 v = *reinterpret_cast<const float4*>(scores + e);
-      const float vs[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if (desc_key(vs[c]) == thr) {
-          flags |= 1u << c;
-          ++cnt;
-        }
-      }
-    }
-    uint32_t tot;
-    uint32_t rank = done + block_excl_scan<uint32_t>(cnt, wsum, &tot);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      if ((flags >> c) & 1u) {
-        if (rank < take) keep[e + c] = 1;
-        ++rank;
-      }
-    }
-    done += tot;
-    if (done >= take) break;
-  }
-  if (threadIdx.x == 0) atomicAdd(&row_counts[r.row], int(take));
 }
 
 // ---- compaction ----------------------------------------------------------------------------------------------
@@ -479,47 +243,16 @@ hipError_t launch_retention_score(const kvc_retention_args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-int64_t topm_blocks(const kvc_topm_args& a) {
-  const int64_t per_row = (a.row_len + kChunk - 1) / kChunk;
-  return (a.n / a.row_len) * per_row;
-}
+size_t topm_workspace_bytes(const kvc_topm_args& a) { return topm_engine_workspace(a.n, a.row_len); }
 
-size_t topm_workspace_bytes(const kvc_topm_args& a) {
-  const int64_t nb = topm_blocks(a);
-  return al(sizeof(TopmState)) + al(3 * kBins * sizeof(uint32_t)) + 2 * al(size_t(nb) * sizeof(uint32_t));
-}
-
-hipError_t launch_topm(const kvc_topm_args& a, void* ws_ptr, hipStream_t s) {
-  char* w = static_cast<char*>(ws_ptr);
-  TopmWs ws;
-  ws.state = reinterpret_cast<TopmState*>(w);
-  w += al(sizeof(TopmState));
-  ws.hist = reinterpret_cast<uint32_t*>(w);
-  w += al(3 * kBins * sizeof(uint32_t));
-  const int64_t nb = topm_blocks(a);
-  ws.tie_cnt = reinterpret_cast<uint32_t*>(w);
-  w += al(size_t(nb) * sizeof(uint32_t));
-  ws.tie_take = reinterpret_cast<uint32_t*>(w);
-  const int64_t n_rows = a.n / a.row_len;
-  const int64_t clear_n = std::max<int64_t>(3 * kBins, n_rows);
-  hipLaunchKernelGGL(topm_clear, dim3(unsigned((clear_n + kTB - 1) / kTB)), dim3(kTB), 0, s, ws, a.row_counts, n_rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.n == 0) return e;
-  // m == 0 and m == n need no special case: the picks then select the first key's bin with nothing to take, or
-  // the last key's bin with every key taken
-  const dim3 grid{unsigned(nb), 1, 1};
-  const int64_t per_row = (a.row_len + kChunk - 1) / kChunk;
-  auto hgrid = [&](int g) { return dim3{unsigned(n_rows * ((per_row + g - 1) / g)), 1, 1}; };
-  hipLaunchKernelGGL(topm_hist<0>, hgrid(hist_group(0)), dim3(kTB), 0, s, a.scores, ws, a.row_len);
-  hipLaunchKernelGGL(topm_pick<0>, dim3(1), dim3(kTB), 0, s, ws, a.m);
-  hipLaunchKernelGGL(topm_hist<1>, hgrid(hist_group(1)), dim3(kTB), 0, s, a.scores, ws, a.row_len);
-  hipLaunchKernelGGL(topm_pick<1>, dim3(1), dim3(kTB), 0, s, ws, a.m);
-  hipLaunchKernelGGL(topm_hist<2>, hgrid(hist_group(2)), dim3(kTB), 0, s, a.scores, ws, a.row_len);
-  hipLaunchKernelGGL(topm_pick<2>, dim3(1), dim3(kTB), 0, s, ws, a.m);
-  hipLaunchKernelGGL(topm_mark, grid, dim3(kTB), 0, s, a.scores, a.keep, a.row_counts, ws, a.row_len, a.status);
-  hipLaunchKernelGGL(topm_tie_scan, dim3(1), dim3(kTB), 0, s, ws, nb);
-  hipLaunchKernelGGL(topm_fix, grid, dim3(kTB), 0, s, a.scores, a.keep, a.row_counts, ws, a.row_len);
-  return hipGetLastError();
+hipError_t launch_topm(const kvc_topm_args& a, void* ws, hipStream_t s) {
+  TopmInput in;
+  in.scores = a.scores;
+  in.beta = a.scores == nullptr ? a.beta : nullptr;
+  in.t = a.t;
+  in.row_len = a.row_len;
+  in.n = a.n;
+  return launch_topm_engine(in, a.m, a.keep, a.row_counts, a.status, ws, nullptr, s);
 }
 
 int64_t compact_blocks(const kvc_compact_args& a) {

@@ -38,24 +38,31 @@ class TopM:
     status: torch.Tensor      # [1] int32
 
 
-def global_topm(scores: torch.Tensor, m: int, stream=None) -> TopM:
-    """scores [rows][row_len] float32 (cuda) -> keep mask of the first m entries in (score desc, flat asc) order."""
-    assert scores.is_cuda and scores.dtype == torch.float32 and scores.is_contiguous() and scores.dim() == 2
-    rows, row_len = scores.shape
-    dev = scores.device
+def global_topm(scores: torch.Tensor | None, m: int, stream=None, beta: torch.Tensor | None = None,
+                t: int | None = None, workspace: torch.Tensor | None = None) -> TopM:
+    """scores [rows][row_len] float32 (cuda) -> keep mask of the first m entries in (score desc, flat asc) order.
+    With ``scores`` None, ``beta`` [rows][row_len] and ``t``: the scores are the log-retention (t - i) ln(beta),
+    computed by the kernels where they are used (never written). ``workspace``: a uint8 tensor to reuse if large
+    enough."""
+    src = scores if scores is not None else beta
+    assert src is not None and (scores is None) != (beta is None)
+    assert src.is_cuda and src.dtype == torch.float32 and src.is_contiguous() and src.dim() == 2
+    rows, row_len = src.shape
+    dev = src.device
     res = TopM(keep=torch.empty((rows, row_len), dtype=torch.uint8, device=dev),
                row_counts=torch.empty(rows, dtype=torch.int32, device=dev),
                status=torch.zeros(1, dtype=torch.int32, device=dev))
-    a = abi.KvcTopmArgs(scores=scores.data_ptr(), n=rows * row_len, m=int(m), row_len=row_len, reserved=0,
+    a = abi.KvcTopmArgs(scores=abi.ptr(scores), n=rows * row_len, m=int(m), row_len=row_len, reserved=0,
                         keep=res.keep.data_ptr(), row_counts=res.row_counts.data_ptr(),
-                        status=res.status.data_ptr())
+                        status=res.status.data_ptr(), beta=abi.ptr(beta), t=int(t or 0), reserved2=0)
     L = abi.lib()
     pa = C.cast(C.byref(a), C.c_void_p)
     need = L.kvc_route_workspace(abi.KVC_ROUTE_GLOBAL_TOPM, pa)
     if need == 0:
         raise abi.KvcError(abi.KVC_E_INVALID, "kvc_route_workspace(GLOBAL_TOPM)")
-    ws = torch.empty(need, dtype=torch.uint8, device=dev)
-    abi.check(L.kvc_route(abi.KVC_ROUTE_GLOBAL_TOPM, pa, ws.data_ptr(), need, _stream(stream)),
+    ws = workspace if workspace is not None and workspace.numel() >= need else \
+        torch.empty(need, dtype=torch.uint8, device=dev)
+    abi.check(L.kvc_route(abi.KVC_ROUTE_GLOBAL_TOPM, pa, ws.data_ptr(), ws.numel(), _stream(stream)),
               "kvc_route(GLOBAL_TOPM)")
     res.ws = ws  # keep alive until the stream reaches the work
     return res

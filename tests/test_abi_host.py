@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported_and_bound():
     for n in names:
         assert hasattr(L, n), n
         assert n in abi.SIGNATURES, n
-    assert L.kvc_abi_version() == abi.ABI_VERSION == 5
+    assert L.kvc_abi_version() == abi.ABI_VERSION == 6
 
 
 def test_struct_sizes_match_header_layout():
@@ -147,7 +147,8 @@ def test_retention_topm_compact_validation_rejects_before_launch():
     assert L.kvc_score(abi.KVC_SCORE_RETENTION, C.cast(C.byref(a), C.c_void_p), None, 0, None) == abi.KVC_E_INVALID
     # top-M: m outside [0, n], row length not a multiple of 16, missing workspace
     def topm(**over):
-        kw = dict(scores=FAKE, n=64, m=8, row_len=32, reserved=0, keep=FAKE, row_counts=FAKE, status=FAKE)
+        kw = dict(scores=FAKE, n=64, m=8, row_len=32, reserved=0, keep=FAKE, row_counts=FAKE, status=FAKE, beta=None,
+                  t=64, reserved2=0)
         kw.update(over)
         t = abi.KvcTopmArgs(**kw)
         return L.kvc_route(abi.KVC_ROUTE_GLOBAL_TOPM, C.cast(C.byref(t), C.c_void_p), None, 0, None), t
@@ -155,6 +156,11 @@ def test_retention_topm_compact_validation_rejects_before_launch():
     assert topm(m=-1)[0] == abi.KVC_E_BUDGET
     assert topm(row_len=24, n=48)[0] == abi.KVC_E_INVALID
     assert topm(n=50)[0] == abi.KVC_E_INVALID
+    assert topm(beta=FAKE)[0] == abi.KVC_E_INVALID                 # scores and beta both given
+    assert topm(scores=None)[0] == abi.KVC_E_INVALID               # neither
+    assert topm(scores=None, beta=FAKE + 4)[0] == abi.KVC_E_INVALID
+    assert topm(scores=None, beta=FAKE)[0] == abi.KVC_E_WORKSPACE  # fused input accepted (no workspace given)
+    assert topm(reserved2=1)[0] == abi.KVC_E_INVALID
     # sizes whose per-row block count would overflow int32 arithmetic are refused
     big = (1 << 31) - 8192   # one past the largest supported n (2^31 - 8208, a multiple of 16)
     assert topm(n=big, row_len=big, m=1)[0] == abi.KVC_E_UNSUPPORTED

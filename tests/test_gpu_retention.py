@@ -116,6 +116,22 @@ def test_topm_edge_cases_and_ties(gpu_lib, m_kind):
     _check_topm(torch.from_numpy(s), tm, m)
 
 
+@pytest.mark.parametrize("layers,T,frac", [(2, 2048, 0.1), (1, 4112, 0.37), (3, 8192, 0.0), (1, 2064, 1.0)])
+def test_topm_fused_retention_equals_score_then_select(gpu_lib, layers, T, frac):
+    """The top-M taken on beta with the log-retention computed in place keeps exactly what the top-M of the scores
+    written by kvc_score(RETENTION) keeps: same mask, same row counts (the same bits are ranked)."""
+    import torch
+    from kv_cache_compression_gqa_amd import retention
+    cfg = configs.DBTRIM_128K
+    beta = torch.from_numpy(synth.make_retention_beta(cfg, layers=layers, n_tokens=T).reshape(layers * cfg.hkv, T)).cuda()
+    m = int(np.floor(frac * beta.numel()))
+    a = retention.global_topm(retention.retention_scores(beta, T), m)
+    b = retention.global_topm(None, m, beta=beta, t=T)
+    torch.cuda.synchronize()
+    assert torch.equal(a.keep, b.keep) and torch.equal(a.row_counts, b.row_counts)
+    assert int(b.status.item()) == 0 and int(b.row_counts.sum().item()) == m
+
+
 def test_compaction_edge_rows(gpu_lib):
     """Rows with nothing kept, everything kept, exactly one page, one row past a page, only the last position, and
     a random tenth, over two 4096-position chunks per row; then a rejected source page id, whose rows must come
@@ -165,6 +181,11 @@ def test_retention_full_size(gpu_lib):
     assert np.all(np.abs(g - ref) <= RTOL * np.abs(ref) + 1e-12)
     keep = _check_topm(sc, tm, cfg.keep)
     assert int(keep.sum()) == cfg.keep
+    from kv_cache_compression_gqa_amd import retention
+    fused = retention.global_topm(None, cfg.keep, beta=torch.from_numpy(beta).cuda(), t=cfg.t)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.keep, tm.keep) and torch.equal(fused.row_counts, tm.row_counts)
+    del fused
     pt = synth.make_page_table(cfg)
     _check_compaction(keep, pt, cfg, L, T)
     torch.cuda.empty_cache()

@@ -51,3 +51,22 @@ def test_topk_large(gpu_lib):
     got = selection.topk(torch.from_numpy(s32).cuda(), k).cpu().numpy()
     want = np.sort(osel.topk(s32.astype(np.float64), k))
     assert np.array_equal(got, want)
+
+
+def test_topk_nan_and_infinite_scores_give_indices_in_range(gpu_lib):
+    """A NaN leaves the order undefined, but the output is still k distinct ascending indices in [0, n), whatever
+    the length (no padded entry can be chosen); -inf and -FLT_MAX rank last among finite scores."""
+    rng = np.random.default_rng(7)
+    for n in (17, 1000, 8195):
+        s32 = rng.standard_normal(n).astype(np.float32)
+        s32[:3] = [np.float32(-np.inf), np.float32(-3.4028235e38), np.float32(-np.inf)]
+        for k in (n - 1, n):
+            got = selection.topk(torch.from_numpy(s32).cuda(), k).cpu().numpy()
+            want = np.sort(osel.topk(s32.astype(np.float64), k))
+            assert np.array_equal(got, want), (n, k)
+        bad = s32.copy()
+        bad[5] = np.float32("nan")
+        bad[6] = -np.float32("nan")
+        for k in (1, n // 2, n - 1, n):
+            got = selection.topk(torch.from_numpy(bad).cuda(), k).cpu().numpy()
+            assert got.size == k and np.all(np.diff(got) > 0) and got.min() >= 0 and got.max() < n, (n, k)
