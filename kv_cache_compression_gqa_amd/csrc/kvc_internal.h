@@ -123,7 +123,7 @@ hipError_t launch_retention_score(const kvc_retention_args& a, hipStream_t s);
 
 // Global top-M engine (topm.hip): scores from memory, or DBTrimKV's log-retention (t - i) * logf(beta) with i the
 // position inside a row, computed where it is used (beta rows need row_len % 16 == 0).
-constexpr int kTopmChunk = 8192;
+constexpr int kTopmChunk = 2048;  // entries per chunk: one wave's unit of work
 struct TopmInput {
   const float* scores;  // [n], or nullptr with beta
   const float* beta;    // [n] when scores is nullptr
@@ -133,10 +133,25 @@ struct TopmInput {
 };
 int64_t topm_chunks(int64_t n, int32_t row_len);
 size_t topm_engine_workspace(int64_t n, int32_t row_len);
-// keep [n] out (0/1); row_counts [n / row_len] out or nullptr; status: KVC_DEV_NAN_SCORE; *chunk_kept (if given)
-// points into the workspace at the kept count of every chunk (valid once the launches have run)
-hipError_t launch_topm_engine(const TopmInput& in, int64_t m, uint8_t* keep, int32_t* row_counts, int32_t* status,
-                              void* ws, int32_t** chunk_kept, hipStream_t s);
+// What the engine writes. keep: one byte (0/1) per entry; or keep_bits, one bit per entry (only for a single row,
+// row_len == n: word w holds entries 32 w .. 32 w + 31; topm_chunks * 64 words). row_counts: [n / row_len] or
+// nullptr. status: KVC_DEV_NAN_SCORE is ORed in (zeroed first when clear_status).
+struct TopmOutput {
+  uint8_t* keep = nullptr;
+  uint32_t* keep_bits = nullptr;
+  int32_t* row_counts = nullptr;
+  int32_t* status = nullptr;
+  bool clear_status = false;
+};
+// Kept counts in the workspace once the launches have run: per chunk, and per group of kTopmGroup consecutive
+// chunks.
+constexpr int kTopmGroup = 64;
+struct TopmCounts {
+  const int32_t* chunk_kept;
+  const int32_t* group_kept;
+};
+hipError_t launch_topm_engine(const TopmInput& in, int64_t m, const TopmOutput& out, void* ws, hipStream_t s,
+                              TopmCounts* counts = nullptr);
 size_t topm_workspace_bytes(const kvc_topm_args& a);
 hipError_t launch_topm(const kvc_topm_args& a, void* ws, hipStream_t s);
 size_t compact_workspace_bytes(const kvc_compact_args& a);

@@ -252,7 +252,11 @@ hipError_t launch_topm(const kvc_topm_args& a, void* ws, hipStream_t s) {
   in.t = a.t;
   in.row_len = a.row_len;
   in.n = a.n;
-  return launch_topm_engine(in, a.m, a.keep, a.row_counts, a.status, ws, nullptr, s);
+  TopmOutput out;
+  out.keep = a.keep;
+  out.row_counts = a.row_counts;
+  out.status = a.status;
+  return launch_topm_engine(in, a.m, out, ws, s);
 }
 
 int64_t compact_blocks(const kvc_compact_args& a) {

@@ -3,114 +3,110 @@
 // two stages, DBTrimKV's global top-M; this entry point exposes the selection itself.
 //
 // The kept set is found by the global top-M engine (topm.hip) over one row of n entries (any n: the last chunk is
-// ragged, nothing is padded); it leaves a byte mask and the kept count of every 8192-entry chunk. topk_offsets
-// turns the counts into exclusive offsets (one workgroup), and topk_write writes each chunk's kept indices at its
-// offset in ascending order (a block scan of per-thread counts, the indices staged in LDS and stored as one run).
+// ragged, nothing is padded). It leaves a bit mask (one bit per entry) and the kept counts of its chunks and of their
+// groups. topk_write handles 8192 entries per workgroup: their place in the output is the sum of the counts before
+// them; each thread expands its mask word into LDS at its prefix position (16-bit offsets), and the workgroup then
+// stores the run contiguously.
+#include <algorithm>
+
 #include "kvc_internal.h"
 
 namespace kvc {
 namespace {
 
 constexpr int kKThreads = 256;
-constexpr int kKChunk = kTopmChunk;           // 8192 entries: the engine's chunks
-constexpr int kKPer = kKChunk / kKThreads;    // 32 mask bytes per thread
+constexpr int kBlock = 8192;                         // entries per workgroup
+constexpr int kWords = kBlock / 32;                  // mask words per workgroup: one per thread
+constexpr int kChunksPerBlock = kBlock / kTopmChunk;  // engine chunks per workgroup
+static_assert(kWords == kKThreads, "one mask word per thread");
+static_assert(kTopmGroup % kChunksPerBlock == 0, "a workgroup's chunks lie in one group");
 
-// exclusive offsets of nb chunk counts, one 1024-thread workgroup: thread t sums a contiguous run of chunks, a
-// wave-shuffle scan plus one LDS step places the runs
-__global__ __launch_bounds__(1024) void topk_offsets(const int32_t* __restrict__ counts, int64_t nb,
-                                                     int32_t* __restrict__ offsets) {
-  const int t = threadIdx.x;
-  const int lane = t & (kWave - 1), wave = t >> 6;
-  const int64_t per = (nb + 1023) / 1024;
-  const int64_t lo = min(nb, t * per), hi = min(nb, lo + per);
-  int s = 0;
-  for (int64_t i = lo; i < hi; ++i) s += counts[i];
-  int inc = s;
+// exclusive prefix over the workgroup (thread order) and the total; two barriers
+__device__ int block_scan_int(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  int inc = v;
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) {
     const int o = __shfl_up(inc, d, kWave);
     if (lane >= d) inc += o;
   }
-  __shared__ int wsum[1024 / kWave];
   if (lane == kWave - 1) wsum[wave] = inc;
   __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += wsum[w];
-  int run = base + inc - s;
-  for (int64_t i = lo; i < hi; ++i) {
-    offsets[i] = run;
-    run += counts[i];
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int q = 0; q < kKThreads / kWave; ++q) {
+    base += q < wave ? wsum[q] : 0;
+    tot += wsum[q];
   }
+  __syncthreads();
+  *total = tot;
+  return base + inc - v;
 }
 
-__global__ __launch_bounds__(kKThreads) void topk_write(const uint8_t* __restrict__ keep, int64_t n,
-                                                        const int32_t* __restrict__ offsets, int64_t k,
-                                                        int32_t* __restrict__ idx) {
-  const int64_t beg = int64_t(blockIdx.x) * kKChunk + int64_t(threadIdx.x) * kKPer;
-  uint32_t bits = 0u;  // bit j: entry beg + j kept
-  if (beg + kKPer <= n) {
-    const uint4 v0 = *reinterpret_cast<const uint4*>(keep + beg);
-    const uint4 v1 = *reinterpret_cast<const uint4*>(keep + beg + 16);
-    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-    for (int j = 0; j < kKPer; ++j) bits |= ((w[j >> 2] >> (8 * (j & 3))) & 1u) << j;
-  } else {
-    for (int j = 0; j < kKPer; ++j) bits |= (beg + j < n ? uint32_t(keep[beg + j] & 1) : 0u) << j;
-  }
-  const int c = __popc(bits);
-  // exclusive prefix of the per-thread counts over the workgroup (thread order = index order)
+__device__ long long block_sum_ll(long long v, long long* wsum) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  int inc = c;
 #pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int o = __shfl_up(inc, d, kWave);
-    if (lane >= d) inc += o;
-  }
+  for (int d = 1; d < kWave; d <<= 1) v += __shfl_xor(v, d, kWave);
+  if (lane == 0) wsum[wave] = v;
+  __syncthreads();
+  long long tot = 0;
+#pragma unroll
+  for (int q = 0; q < kKThreads / kWave; ++q) tot += wsum[q];
+  __syncthreads();
+  return tot;
+}
+
+__global__ __launch_bounds__(kKThreads) void topk_write(const uint32_t* __restrict__ bits,
+                                                        const int32_t* __restrict__ chunk_kept,
+                                                        const int32_t* __restrict__ group_kept, int64_t n,
+                                                        int64_t k, int32_t* __restrict__ idx) {
+  __shared__ uint16_t stage[kBlock];  // offsets (entry - first) of the kept entries, in order
   __shared__ int wsum[kKThreads / kWave];
-  __shared__ int32_t stage[kKChunk];  // the chunk's kept indices in order, written out as one contiguous run
-  if (lane == kWave - 1) wsum[wave] = inc;
-  __syncthreads();
-  int lpos = inc - c, total = 0;
-#pragma unroll
-  for (int w = 0; w < kKThreads / kWave; ++w) {
-    if (w < wave) lpos += wsum[w];
-    total += wsum[w];
+  __shared__ long long bsum[kKThreads / kWave];
+  const int64_t word = int64_t(blockIdx.x) * kWords + threadIdx.x;
+  // only entries below n count: the engine clears the bits past n in its last chunk, and the words past that chunk
+  // (in this workgroup's range) are never written
+  const int64_t lo = word * 32;
+  uint32_t w = lo >= n ? 0u : (lo + 32 <= n ? bits[word] : bits[word] & ((1u << (n - lo)) - 1u));
+  // kept entries before this workgroup's first chunk: whole groups, then the group's chunks before it
+  const int64_t c0 = int64_t(blockIdx.x) * kChunksPerBlock;
+  const int64_t grp = c0 / kTopmGroup, gfirst = grp * kTopmGroup;
+  long long before = 0;
+  for (int64_t q = threadIdx.x; q < grp; q += kKThreads) before += group_kept[q];
+  if (int64_t(threadIdx.x) < c0 - gfirst) before += chunk_kept[gfirst + threadIdx.x];
+  int total;
+  int p = block_scan_int(__popc(w), wsum, &total);
+  const long long base = block_sum_ll(before, bsum);
+  while (w) {
+    const int j = __builtin_ctz(w);
+    w &= w - 1;
+    stage[p++] = uint16_t(32 * threadIdx.x + j);
   }
-  while (bits) {
-    const int j = __builtin_ctz(bits);
-    bits &= bits - 1;
-    stage[lpos++] = int32_t(beg + j);
-  }
   __syncthreads();
-  const int64_t base = offsets[blockIdx.x];
+  const int32_t first = int32_t(int64_t(blockIdx.x) * kBlock);
   for (int i = threadIdx.x; i < total; i += kKThreads) {
-    if (base + i < k) idx[base + i] = stage[i];
+    if (base + i < k) idx[base + i] = first + int32_t(stage[i]);
   }
 }
 
 struct TopkLayout {
   int64_t nb;
-  size_t keep_off, offsets_off, misc_off, engine_off, total;
+  size_t bits_off, misc_off, engine_off, total;
 };
 
 TopkLayout topk_layout(int64_t n) {
   TopkLayout L;
-  L.nb = topm_chunks(n, int32_t(n));
+  L.nb = (n + kBlock - 1) / kBlock;  // workgroups of topk_write
+  const size_t nb = size_t(std::max<int64_t>(L.nb, 1));
   size_t o = 0;
-  L.keep_off = o;
-  o += align_up(size_t(std::max<int64_t>(n, 1)) + 32, 256);
-  L.offsets_off = o;
-  o += align_up(size_t(std::max<int64_t>(L.nb, 1)) * sizeof(int32_t), 256);
-  L.misc_off = o;  // row count + status of the engine
+  L.bits_off = o;
+  o += align_up(nb * kWords * sizeof(uint32_t), 256);
+  L.misc_off = o;  // the engine's status word
   o += 256;
   L.engine_off = o;
   o += topm_engine_workspace(n, int32_t(n));
   L.total = o;
   return L;
-}
-
-__global__ void topk_zero(int32_t* __restrict__ w) {
-  if (threadIdx.x == 0) w[0] = 0;
 }
 
 }  // namespace
@@ -120,23 +116,21 @@ size_t topk_workspace_bytes(int64_t n) { return topk_layout(n).total; }
 hipError_t launch_topk(const float* scores, int64_t n, int64_t k, int32_t* idx, void* ws, hipStream_t s) {
   const TopkLayout L = topk_layout(n);
   char* w = static_cast<char*>(ws);
-  uint8_t* keep = reinterpret_cast<uint8_t*>(w + L.keep_off);
-  int32_t* offsets = reinterpret_cast<int32_t*>(w + L.offsets_off);
-  int32_t* misc = reinterpret_cast<int32_t*>(w + L.misc_off);
-  hipLaunchKernelGGL(topk_zero, dim3(1), dim3(kWave), 0, s, misc + 1);  // the engine's status word (a kernel: graphs)
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   TopmInput in;
   in.scores = scores;
   in.beta = nullptr;
   in.t = 0;
   in.row_len = int32_t(n);
   in.n = n;
-  int32_t* chunk_kept = nullptr;
-  e = launch_topm_engine(in, k, keep, nullptr, misc + 1, w + L.engine_off, &chunk_kept, s);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_offsets, dim3(1), dim3(1024), 0, s, chunk_kept, L.nb, offsets);
-  hipLaunchKernelGGL(topk_write, dim3(unsigned(L.nb)), dim3(kKThreads), 0, s, keep, n, offsets, k, idx);
+  TopmOutput out;
+  out.keep_bits = reinterpret_cast<uint32_t*>(w + L.bits_off);
+  out.status = reinterpret_cast<int32_t*>(w + L.misc_off);
+  out.clear_status = true;
+  TopmCounts counts;
+  hipError_t e = launch_topm_engine(in, k, out, w + L.engine_off, s, &counts);
+  if (e != hipSuccess || L.nb == 0) return e;
+  hipLaunchKernelGGL(topk_write, dim3(unsigned(L.nb)), dim3(kKThreads), 0, s, out.keep_bits, counts.chunk_kept,
+                     counts.group_kept, n, k, idx);
   return hipGetLastError();
 }
 

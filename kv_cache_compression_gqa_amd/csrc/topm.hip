@@ -6,17 +6,20 @@
 // scores are read from memory or computed on the fly as DBTrimKV's log-retention (t - i) * logf(beta) (the
 // retention score of section 2; computing it where it is used saves writing and re-reading it). Passes over the
 // whole input: two; everything after them touches only the entries of one histogram bin.
-//   hist1     (chunks of 8192 entries, four per workgroup): 2048-bin histogram of the top 11 key bits (LDS per
-//             wave, one global atomic per non-empty bin).
-//   classify  (one workgroup per chunk): picks the bin b1 holding the m-th key from the histogram (every workgroup
-//             takes the same decision from the same counts), writes the keep mask (1 below b1), and compacts the
-//             entries of b1 into the chunk's candidate segment in index order, with a histogram of their next 11
-//             bits. Kept entries are counted per chunk and per row.
-//   cand_hist3 (per chunk, candidates only): picks b2, histogram of the last 10 bits of the candidates in b2.
-//   cand_mark (per chunk, candidates only): picks b3 (threshold key T), keeps every candidate below T and counts the
-//             ties (key == T) per chunk.
-//   tie_scan  (one workgroup): how many ties each chunk takes, in chunk order, so that ties are taken lowest index
-//             first; tie_fix then takes them.
+// The unit of work is a chunk of 2048 entries inside one row: one wave reads it with eight 16-byte loads per lane.
+//   hist1      (64 chunks per 1024-thread workgroup, one chunk per wave at a time): 2048-bin histogram of the top 11
+//              key bits, one LDS copy per wave, one global atomic per non-empty bin.
+//   classify   (16 chunks per 256-thread workgroup, one per wave at a time, no barrier): picks the bin b1 holding the m-th key
+//              (every workgroup takes the same decision from the same counts), writes the keep mask (1 below b1)
+//              and moves the entries of b1 to their chunk's candidate segment, in index order; kept entries are
+//              counted per chunk and row.
+//   cand_hist2 (256 chunks' candidates per workgroup): histogram of the candidates' next 11 key bits.
+//   cand_hist3 (groups of 64 chunks): picks b2; histogram of the last 10 bits of the candidates in b2.
+//   cand_mark  (same groups): picks b3, i.e. the threshold key T; keeps every candidate below T and counts the ties
+//              (key == T) of its group.
+//   tie_fix    (same groups): the ties still needed go to the groups in index order: a group's share follows from
+//              the tie counts of the groups before it; it takes them lowest index first.
+// Workgroup 0 of a kernel records its pick for the kernels after it; no workgroup waits for another inside a kernel.
 #include <algorithm>
 
 #include "kvc_internal.h"
@@ -24,27 +27,31 @@
 namespace kvc {
 namespace {
 
-constexpr int kTB = 256;
-constexpr int kChunk = kTopmChunk;             // entries per chunk (inside one row)
-constexpr int kU = kChunk / (4 * kTB);         // float4 loads per thread and chunk
+constexpr int kChunk = kTopmChunk;        // entries per chunk (inside one row): one wave's unit
+constexpr int kU = kChunk / (4 * kWave);  // float4 loads per lane and chunk
 constexpr int kBins = 2048;
-constexpr int kHistGroup = 4;                  // chunks per histogram workgroup
+constexpr int kHistTB = 1024, kHistPer = 4;  // hist1: threads, chunks per wave
+constexpr int kClsTB = 256, kClsPer = 4;     // classify
+constexpr int kH2TB = 1024, kH2G = 256;      // cand_hist2: threads, chunks per workgroup
+constexpr int kCandTB = 256, kCandG = kTopmGroup;  // cand_hist3 / cand_mark / tie_fix
+static_assert(kU == 8, "two u64 of four 16-bit fields hold a lane's per-slice candidate counts");
+static_assert(kCandG <= kWave, "a group's chunk prefix is one wave scan");
+static_assert(kH2G <= kH2TB, "one chunk count per thread");
 
 struct State {
-  int32_t b1, b2, b3, pad;
-  uint32_t thr;
-  uint32_t pad2;
+  int32_t b1, b2, b3, any;  // any: the threshold key is defined (m > 0)
+  uint32_t thr, pad;
   int64_t need1, need2, need3;
 };
 
 struct Ws {
   State* st;
-  uint32_t* hist;      // [3][kBins]
-  uint2* cand;         // [nb][kChunk] (key, entry index) per chunk segment, index order
-  int32_t* ccnt;       // [nb] candidates per chunk
-  int32_t* kept;       // [nb] entries kept per chunk
-  uint32_t* tie_cnt;   // [nb]
-  uint32_t* tie_take;  // [nb]
+  uint32_t* hist;       // [3][kBins]
+  uint2* cand;          // [nb][kChunk] (key, entry index) per chunk segment, index order
+  int32_t* ccnt;        // [nb] candidates per chunk
+  int32_t* kept;        // [nb] entries kept per chunk
+  uint32_t* tie_cnt;    // [groups of kCandG chunks]
+  int32_t* group_kept;  // [groups]
 };
 
 __device__ __forceinline__ uint32_t desc_key(float s) {
@@ -67,18 +74,19 @@ __device__ __forceinline__ Chunk chunk_of(int64_t b, int32_t row_len) {
   return r;
 }
 
-// A chunk's scores: thread t, slice u holds entries r.beg + 4 (t + 256 u) .. + 3. Every float4 load is issued
-// unconditionally at an address clamped into the chunk's last whole float4 (the rows of a chunk are 16-byte
-// aligned); only a chunk whose end is not a multiple of 4 (the last one of a ragged kvc_topk input) re-reads its
-// last entries one by one. Entries at or past the end are never counted. With beta as input, the log-retention is
-// computed in place.
-__device__ __forceinline__ void load_chunk(const TopmInput& in, const Chunk& r, float4 (&v)[kU]) {
-  const float* src = in.scores != nullptr ? in.scores : in.beta;
+// A chunk's scores, read by one wave: lane l, slice u holds entries r.beg + 4 (l + 64 u) .. + 3. Every float4 load
+// is issued unconditionally at an address clamped into the chunk's last whole float4 (the rows of a chunk are
+// 16-byte aligned); only a chunk whose end is not a multiple of 4 (the last one of a ragged kvc_topk input) re-reads
+// its last entries one by one. Entries at or past the end are never counted. With beta as input, the log-retention
+// is computed in place.
+template <bool kBeta>
+__device__ __forceinline__ void load_chunk(const TopmInput& in, const Chunk& r, int lane, float4 (&v)[kU]) {
+  const float* src = kBeta ? in.beta : in.scores;
   const int64_t last4 = (r.end & ~int64_t(3)) - 4;  // start of the chunk's last whole float4
   if (last4 >= r.beg) {  // uniform: a chunk of fewer than 4 entries is read one by one below
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int64_t e = r.beg + 4 * (threadIdx.x + kTB * u);
+      const int64_t e = r.beg + 4 * (lane + kWave * u);
       v[u] = *reinterpret_cast<const float4*>(src + min(e, last4));
     }
   } else {
@@ -88,7 +96,7 @@ __device__ __forceinline__ void load_chunk(const TopmInput& in, const Chunk& r, 
   if ((r.end & 3) != 0) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int64_t e = r.beg + 4 * (threadIdx.x + kTB * u);
+      const int64_t e = r.beg + 4 * (lane + kWave * u);
       if (e < r.end && e + 4 > r.end) {
         v[u].x = src[e];
         v[u].y = e + 1 < r.end ? src[e + 1] : 0.0f;
@@ -97,10 +105,10 @@ __device__ __forceinline__ void load_chunk(const TopmInput& in, const Chunk& r, 
       }
     }
   }
-  if (in.scores == nullptr) {  // DBTrimKV log-retention, as kvc_score(KVC_SCORE_RETENTION) computes it
+  if (kBeta) {  // DBTrimKV log-retention, as kvc_score(KVC_SCORE_RETENTION) computes it
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int i = int(r.beg - r.row * in.row_len) + 4 * (threadIdx.x + kTB * u);
+      const int i = int(r.beg - r.row * in.row_len) + 4 * (lane + kWave * u);
       v[u].x = float(in.t - i) * logf(v[u].x);
       v[u].y = float(in.t - i - 1) * logf(v[u].y);
       v[u].z = float(in.t - i - 2) * logf(v[u].z);
@@ -109,7 +117,7 @@ __device__ __forceinline__ void load_chunk(const TopmInput& in, const Chunk& r, 
   }
 }
 
-template <class V>
+template <class V, int TB>
 __device__ V block_excl_scan(V v, V* wsum, V* total) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   V inc = v;
@@ -122,7 +130,7 @@ __device__ V block_excl_scan(V v, V* wsum, V* total) {
   __syncthreads();
   V base = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kTB / kWave; ++w) {
+  for (int w = 0; w < TB / kWave; ++w) {
     base += w < wave ? wsum[w] : V(0);
     tot += wsum[w];
   }
@@ -131,9 +139,17 @@ __device__ V block_excl_scan(V v, V* wsum, V* total) {
   return base + inc - v;
 }
 
-// The bin of histogram h (nbins = 1024 or 2048) holding the need-th key, and how many keys of that bin are needed:
-// pk = {bin, need} ({-1, 0} when need <= 0). Wave 0 alone: lane l owns bins [l * nbins / 64, (l + 1) * nbins / 64);
-// the caller publishes pk with a barrier.
+// block sum (every thread gets it); two barriers
+template <class V, int TB>
+__device__ V block_sum(V v, V* wsum) {
+  V tot;
+  (void)block_excl_scan<V, TB>(v, wsum, &tot);
+  return tot;
+}
+
+// The bin of global histogram h (nbins = 1024 or 2048) holding the need-th key, and how many keys of that bin are
+// needed: pk = {bin, need} ({-1, 0} when need <= 0). Wave 0 alone: lane l owns bins [l * nbins / 64,
+// (l + 1) * nbins / 64); the caller publishes pk with a barrier.
 __device__ void wave_pick(const uint32_t* h, int nbins, int64_t need, long long* pk) {
   if (threadIdx.x >= kWave) return;
   const int lane = threadIdx.x;
@@ -171,51 +187,97 @@ __device__ void wave_pick(const uint32_t* h, int nbins, int64_t need, long long*
   }
 }
 
-// Exclusive scan (thread order) of four 16-bit fields packed in a u64 (every field's block total < 65536), and the
-// block totals. Contains one barrier; sm must hold kTB / kWave entries and is not reused by the caller.
-__device__ __forceinline__ unsigned long long scan_fields(unsigned long long v, unsigned long long* sm,
-                                                          unsigned long long& total) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  unsigned long long inc = v;
+// Candidates of the chunks b0 .. b0 + g - 1 as one index-ordered sequence: pref[k] = candidates of the group's chunks
+// before chunk k (pref[g] = all). Wave 0 alone; the caller publishes pref with a barrier.
+__device__ void group_prefix(const Ws& ws, int64_t b0, int g, int* pref) {
+  if (threadIdx.x >= kWave) return;
+  const int lane = threadIdx.x;
+  const int c = lane < g ? ws.ccnt[b0 + lane] : 0;
+  int inc = c;
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) {
-    const unsigned long long o = __shfl_up(inc, d, kWave);
+    const int o = __shfl_up(inc, d, kWave);
     if (lane >= d) inc += o;
   }
-  if (lane == kWave - 1) sm[wave] = inc;
+  if (lane == 0) pref[0] = 0;
+  if (lane < g) pref[lane + 1] = inc;
+}
+
+// The same for up to TB chunks with the whole workgroup (contains barriers; every thread calls it).
+template <int TB>
+__device__ void group_prefix_block(const Ws& ws, int64_t b0, int g, int* pref, int* wsum) {
+  const int c = int(threadIdx.x) < g ? ws.ccnt[b0 + threadIdx.x] : 0;
+  int total;
+  const int ex = block_excl_scan<int, TB>(c, wsum, &total);
+  if (int(threadIdx.x) < g) pref[threadIdx.x] = ex;
+  if (threadIdx.x == 0) pref[g] = total;
   __syncthreads();
-  unsigned long long base = 0, tot = 0;
+}
+
+// chunk k of the group holding the j-th candidate of the sequence: the last k with pref[k] <= j (G = 16 or 64)
+template <int G>
+__device__ __forceinline__ int chunk_in_group(const int* pref, int g, int j) {
+  int lo = 0;
 #pragma unroll
-  for (int w = 0; w < kTB / kWave; ++w) {
-    base += w < wave ? sm[w] : 0ull;
-    tot += sm[w];
+  for (int step = G / 2; step >= 1; step >>= 1) {
+    if (lo + step < g && pref[lo + step] <= j) lo += step;
   }
-  total = tot;
-  return base + inc - v;
+  return lo;
 }
 
-__global__ __launch_bounds__(kTB) void eng_clear(Ws ws, int32_t* row_counts, int64_t n_rows) {
-  const int64_t i = int64_t(blockIdx.x) * kTB + threadIdx.x;
-  if (i < 3 * kBins) ws.hist[i] = 0u;
-  if (row_counts != nullptr && i < n_rows) row_counts[i] = 0;
+__device__ __forceinline__ const uint2* seg_of(const Ws& ws, int64_t b) { return ws.cand + size_t(b) * kChunk; }
+
+// set bits of the wave ballot m in the lanes below this one
+__device__ __forceinline__ int lanes_below(unsigned long long m) {
+  return int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
 }
 
-__global__ __launch_bounds__(kTB) void eng_hist1(TopmInput in, Ws ws, int64_t nb) {
-  __shared__ uint32_t h[kTB / kWave][kBins];
-  const int wave = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < (kTB / kWave) * kBins; i += kTB) (&h[0][0])[i] = 0u;
+// bit i of x (x < 256) moved to bit 4 i
+__device__ __forceinline__ uint32_t spread4(uint32_t x) {
+  x = (x | (x << 12)) & 0x000F000Fu;
+  x = (x | (x << 6)) & 0x03030303u;
+  x = (x | (x << 3)) & 0x11111111u;
+  return x;
+}
+
+// Adds the kept counts of the chunks b0 .. b0 + g - 1 (thread t < g holds chunk b0 + t's, g <= G) to their rows:
+// one global atomic per distinct row, summed in LDS first (slot = row - row of b0; g chunks span at most g rows).
+// Every thread calls it (two barriers); rc holds G ints.
+template <int G>
+__device__ void add_row_counts(int32_t* row_counts, int64_t b0, int g, int cnt, int32_t row_len, int* rc) {
+  if (threadIdx.x < G) rc[threadIdx.x] = 0;
   __syncthreads();
-  const int64_t b0 = int64_t(blockIdx.x) * kHistGroup;
-  const int nc = int(min(int64_t(kHistGroup), nb - b0));
-  auto load = [&](int k, float4 (&v)[kU]) { load_chunk(in, chunk_of(b0 + k, in.row_len), v); };
+  const int64_t per_row = (int64_t(row_len) + kChunk - 1) / kChunk;
+  const int64_t row0 = b0 / per_row;
+  if (int(threadIdx.x) < g && cnt > 0) atomicAdd(&rc[int((b0 + threadIdx.x) / per_row - row0)], cnt);
+  __syncthreads();
+  if (threadIdx.x < G && rc[threadIdx.x] > 0) atomicAdd(&row_counts[row0 + threadIdx.x], rc[threadIdx.x]);
+}
+
+__global__ __launch_bounds__(256) void eng_clear(Ws ws, int32_t* row_counts, int64_t n_rows, int32_t* status) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i < 3 * kBins) ws.hist[i] = 0u;
+  if (i < int64_t(sizeof(State) / sizeof(uint32_t))) reinterpret_cast<uint32_t*>(ws.st)[i] = 0u;
+  if (row_counts != nullptr && i < n_rows) row_counts[i] = 0;
+  if (status != nullptr && i == 0) *status = 0;
+}
+
+template <bool kBeta>
+__global__ __launch_bounds__(kHistTB) void eng_hist1(TopmInput in, Ws ws, int64_t nb) {
+  constexpr int W = kHistTB / kWave;
+  __shared__ uint32_t h[W][kBins];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
+  int64_t b = int64_t(blockIdx.x) * (W * kHistPer) + wave;  // wave's chunks: b, b + W, ...
   float4 v[kU], vn[kU];
-  load(0, v);
-  for (int k = 0; k < nc; ++k) {
-    if (k + 1 < nc) load(k + 1, vn);
-    const Chunk r = chunk_of(b0 + k, in.row_len);
+  if (b < nb) load_chunk<kBeta>(in, chunk_of(b, in.row_len), lane, v);
+  for (int i = threadIdx.x; i < W * kBins; i += kHistTB) (&h[0][0])[i] = 0u;
+  __syncthreads();
+  for (int i = 0; i < kHistPer && b < nb; ++i, b += W) {  // wave-uniform
+    if (i + 1 < kHistPer && b + W < nb) load_chunk<kBeta>(in, chunk_of(b + W, in.row_len), lane, vn);
+    const Chunk r = chunk_of(b, in.row_len);
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int64_t e = r.beg + 4 * (threadIdx.x + kTB * u);
+      const int64_t e = r.beg + 4 * (lane + kWave * u);
       const float vs[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -226,21 +288,28 @@ __global__ __launch_bounds__(kTB) void eng_hist1(TopmInput in, Ws ws, int64_t nb
     for (int u = 0; u < kU; ++u) v[u] = vn[u];
   }
   __syncthreads();
-  for (int bin = threadIdx.x; bin < kBins; bin += kTB) {
-    const uint32_t s = h[0][bin] + h[1][bin] + h[2][bin] + h[3][bin];
+  for (int bin = threadIdx.x; bin < kBins; bin += kHistTB) {
+    uint32_t s = 0u;
+#pragma unroll
+    for (int w = 0; w < W; ++w) s += h[w][bin];
     if (s != 0u) atomicAdd(&ws.hist[bin], s);
   }
 }
 
-__global__ __launch_bounds__(kTB) void eng_classify(TopmInput in, Ws ws, int64_t m, uint8_t* __restrict__ keep,
-                                                    int32_t* row_counts, int32_t* status) {
+// kBits: the keep mask as bits (one row: chunk starts are multiples of 2048), else as bytes; kBeta: scores computed
+// from beta
+template <bool kBits, bool kBeta>
+__global__ __launch_bounds__(kClsTB) void eng_classify(TopmInput in, Ws ws, int64_t nb, int64_t m,
+                                                       uint8_t* __restrict__ keep, uint32_t* __restrict__ keep_bits,
+                                                       int32_t* row_counts, int32_t* status) {
+  constexpr int W = kClsTB / kWave, kSpan = W * kClsPer;
   __shared__ long long pk[2];
-  __shared__ unsigned long long sm[3][kTB / kWave];
-  __shared__ uint32_t h2[kBins];
-  const Chunk r = chunk_of(blockIdx.x, in.row_len);
-  float4 v[kU];
-  load_chunk(in, r, v);  // the chunk's loads first
-  for (int i = threadIdx.x; i < kBins; i += kTB) h2[i] = 0u;
+  __shared__ int kc[kSpan], rc[kSpan];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
+  const int64_t b0 = int64_t(blockIdx.x) * kSpan;
+  int64_t b = b0 + wave;
+  float4 v[kU], vn[kU];
+  if (b < nb) load_chunk<kBeta>(in, chunk_of(b, in.row_len), lane, v);  // the first chunk's loads before the pick
   wave_pick(ws.hist, kBins, m, pk);
   __syncthreads();
   const int b1 = int(pk[0]);
@@ -248,216 +317,259 @@ __global__ __launch_bounds__(kTB) void eng_classify(TopmInput in, Ws ws, int64_t
     ws.st->b1 = b1;
     ws.st->need1 = pk[1];
   }
-  uint32_t cand_bits = 0u;
-  unsigned long long f0 = 0ull, f1 = 0ull, f2 = 0ull;  // candidates per slice (16-bit fields), kept (f2)
   bool nan = false;
+  for (int i = 0; i < kClsPer && b < nb; ++i, b += W) {  // wave-uniform; no barrier below
+    if (i + 1 < kClsPer && b + W < nb) load_chunk<kBeta>(in, chunk_of(b + W, in.row_len), lane, vn);
+    const Chunk r = chunk_of(b, in.row_len);
+    uint2* seg = ws.cand + size_t(b) * kChunk;
+    int base = 0, kept = 0;  // wave-uniform: candidates written so far, entries kept
 #pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    const int64_t e = r.beg + 4 * (threadIdx.x + kTB * u);
-    const float vs[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-    uint32_t out = 0u;
-    unsigned long long cu = 0ull;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const bool valid = e + c < r.end;
-      const uint32_t key = desc_key(vs[c]);
-      nan |= valid && vs[c] != vs[c];
-      const int d = int(key >> 21);
-      const bool k1 = valid && d < b1;
-      const bool cd = valid && d == b1;
-      f2 += k1 ? 1ull : 0ull;
-      out |= (k1 ? 1u : 0u) << (8 * c);
-      cand_bits |= (cd ? 1u : 0u) << (4 * u + c);
-      cu += cd ? 1ull : 0ull;
-      if (cd) atomicAdd(&h2[(key >> 10) & 0x7FFu], 1u);
-    }
-    if (u < 4) f0 += cu << (16 * u);
-    else f1 += cu << (16 * (u - 4));
-    if (e + 4 <= r.end) {
-      *reinterpret_cast<uint32_t*>(keep + e) = out;
-    } else {
+    for (int u = 0; u < kU; ++u) {
+      const int64_t e = r.beg + 4 * (lane + kWave * u);
+      const float vs[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      bool k1[4], cd[4];
+      unsigned long long K[4], C[4];  // ballots: entry c of every lane kept / a candidate
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        if (e + c < r.end) keep[e + c] = uint8_t((out >> (8 * c)) & 1u);
+        const bool valid = e + c < r.end;
+        nan |= valid && vs[c] != vs[c];
+        const int d = int(desc_key(vs[c]) >> 21);
+        k1[c] = valid && d < b1;
+        cd[c] = valid && d == b1;
+        K[c] = __ballot(k1[c]);
+        C[c] = __ballot(cd[c]);
+      }
+      kept += __popcll(K[0]) + __popcll(K[1]) + __popcll(K[2]) + __popcll(K[3]);
+      if (kBits) {  // lane 8q writes the word of lanes 8q .. 8q + 7: bit 4 i + c = entry c of lane 8q + i
+        if ((lane & 7) == 0) {
+          const int sh = lane;  // 8 q
+          const uint32_t x = spread4(uint32_t(K[0] >> sh) & 0xFFu) | (spread4(uint32_t(K[1] >> sh) & 0xFFu) << 1) |
+                             (spread4(uint32_t(K[2] >> sh) & 0xFFu) << 2) | (spread4(uint32_t(K[3] >> sh) & 0xFFu) << 3);
+          keep_bits[e >> 5] = x;
+        }
+      } else {
+        const uint32_t out = (k1[0] ? 1u : 0u) | (k1[1] ? 0x100u : 0u) | (k1[2] ? 0x10000u : 0u) |
+                             (k1[3] ? 0x1000000u : 0u);
+        if (e + 4 <= r.end) {
+          *reinterpret_cast<uint32_t*>(keep + e) = out;
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            if (e + c < r.end) keep[e + c] = uint8_t((out >> (8 * c)) & 1u);
+          }
+        }
+      }
+      // this slice's candidates in index order (lanes in order, then c), after those of the slices before it
+      if ((C[0] | C[1] | C[2] | C[3]) != 0ull) {  // wave-uniform
+        int p = base + lanes_below(C[0]) + lanes_below(C[1]) + lanes_below(C[2]) + lanes_below(C[3]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (cd[c]) seg[p++] = make_uint2(desc_key(vs[c]), uint32_t(e + c));
+        }
+        base += __popcll(C[0]) + __popcll(C[1]) + __popcll(C[2]) + __popcll(C[3]);
       }
     }
+    if (lane == 0) {
+      ws.ccnt[b] = base;
+      ws.kept[b] = kept;
+      kc[b - b0] = kept;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) v[u] = vn[u];
   }
   if (nan) atomicOr(status, KVC_DEV_NAN_SCORE);
-  // candidates in index order: slice u before slice u + 1, threads in order inside a slice (one scan of packed
-  // per-slice counts)
-  unsigned long long t0, t1, t2;
-  const unsigned long long e0 = scan_fields(f0, sm[0], t0);
-  const unsigned long long e1 = scan_fields(f1, sm[1], t1);
-  (void)scan_fields(f2, sm[2], t2);
-  int base = 0;
-  uint2* seg = ws.cand + size_t(blockIdx.x) * kChunk;
-#pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    const unsigned long long ex = u < 4 ? e0 : e1;
-    const unsigned long long tt = u < 4 ? t0 : t1;
-    const int sh = 16 * (u & 3);
-    int p = base + int((ex >> sh) & 0xFFFFull);
-    const int64_t e = r.beg + 4 * (threadIdx.x + kTB * u);
-    const float vs[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      if ((cand_bits >> (4 * u + c)) & 1u) seg[p++] = make_uint2(desc_key(vs[c]), uint32_t(e + c));
-    }
-    base += int((tt >> sh) & 0xFFFFull);
-  }
-  const int ktot = int(t2);
-  if (threadIdx.x == 0) {
-    ws.ccnt[blockIdx.x] = base;
-    ws.kept[blockIdx.x] = ktot;
-    if (row_counts != nullptr && ktot > 0) atomicAdd(&row_counts[r.row], ktot);
-  }
-  if (base > 0) {  // h2 complete: the scans' barriers follow every atomic
-    for (int bin = threadIdx.x; bin < kBins; bin += kTB) {
-      if (h2[bin] != 0u) atomicAdd(&ws.hist[kBins + bin], h2[bin]);
-    }
+  if (row_counts != nullptr) {
+    __syncthreads();
+    const int g = int(min(int64_t(kSpan), nb - b0));
+    add_row_counts<kSpan>(row_counts, b0, g, int(threadIdx.x) < g ? kc[threadIdx.x] : 0, in.row_len, rc);
   }
 }
 
-// candidates of bin b2 (picked from the second histogram): histogram of their last 10 bits
-__global__ __launch_bounds__(kTB) void eng_cand_hist3(Ws ws) {
-  __shared__ long long pk[2];
+// histogram of the candidates' key bits 20..10 (every candidate is in bin b1)
+__global__ __launch_bounds__(kH2TB) void eng_cand_hist2(Ws ws, int64_t nb) {
+  __shared__ uint32_t h[kBins];
+  __shared__ int pref[kH2G + 1];
+  __shared__ int wsum[kH2TB / kWave];
+  for (int i = threadIdx.x; i < kBins; i += kH2TB) h[i] = 0u;
+  const int64_t b0 = int64_t(blockIdx.x) * kH2G;
+  const int g = int(min(int64_t(kH2G), nb - b0));
+  group_prefix_block<kH2TB>(ws, b0, g, pref, wsum);
+  const int total = pref[g];
+  constexpr int kUn = 4;
+  for (int j0 = threadIdx.x; j0 < total; j0 += kH2TB * kUn) {
+    uint32_t key[kUn];
+#pragma unroll
+    for (int q = 0; q < kUn; ++q) {
+      const int j = j0 + q * kH2TB;
+      key[q] = 0u;
+      if (j < total) {
+        const int k = chunk_in_group<kH2G>(pref, g, j);
+        key[q] = seg_of(ws, b0 + k)[j - pref[k]].x;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kUn; ++q) {
+      if (j0 + q * kH2TB < total) atomicAdd(&h[(key[q] >> 10) & 0x7FFu], 1u);
+    }
+  }
+  __syncthreads();
+  for (int bin = threadIdx.x; bin < kBins; bin += kH2TB) {
+    if (h[bin] != 0u) atomicAdd(&ws.hist[kBins + bin], h[bin]);
+  }
+}
+
+// picks b2; histogram of the last 10 key bits of the candidates in b2
+__global__ __launch_bounds__(kCandTB) void eng_cand_hist3(Ws ws, int64_t nb) {
   __shared__ uint32_t h3[1024];
-  const int nc = ws.ccnt[blockIdx.x];
-  if (nc == 0 && blockIdx.x != 0) return;  // workgroup 0 always records the pick
-  const int64_t need1 = ws.st->need1;
-  wave_pick(ws.hist + kBins, kBins, need1, pk);
+  __shared__ int pref[kCandG + 1];
+  __shared__ long long pk[2];
+  for (int i = threadIdx.x; i < 1024; i += kCandTB) h3[i] = 0u;
+  const int64_t b0 = int64_t(blockIdx.x) * kCandG;
+  const int g = int(min(int64_t(kCandG), nb - b0));
+  group_prefix(ws, b0, g, pref);
+  wave_pick(ws.hist + kBins, kBins, ws.st->need1, pk);
   __syncthreads();
   const int b2 = int(pk[0]);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     ws.st->b2 = b2;
     ws.st->need2 = pk[1];
   }
-  if (nc == 0) return;
-  for (int i = threadIdx.x; i < 1024; i += kTB) h3[i] = 0u;
-  __syncthreads();
-  const uint2* seg = ws.cand + size_t(blockIdx.x) * kChunk;
-  for (int i = threadIdx.x; i < nc; i += kTB) {
-    const uint32_t key = seg[i].x;
+  const int total = pref[g];
+  for (int j = threadIdx.x; j < total; j += kCandTB) {
+    const int k = chunk_in_group<kCandG>(pref, g, j);
+    const uint32_t key = seg_of(ws, b0 + k)[j - pref[k]].x;
     if (int((key >> 10) & 0x7FFu) == b2) atomicAdd(&h3[key & 0x3FFu], 1u);
   }
   __syncthreads();
-  for (int bin = threadIdx.x; bin < 1024; bin += kTB) {
+  for (int bin = threadIdx.x; bin < 1024; bin += kCandTB) {
     if (h3[bin] != 0u) atomicAdd(&ws.hist[2 * kBins + bin], h3[bin]);
   }
 }
 
-// threshold key T from the third histogram; candidates below T kept, ties counted
-__global__ __launch_bounds__(kTB) void eng_cand_mark(Ws ws, uint8_t* __restrict__ keep, int32_t* row_counts,
-                                                     int32_t row_len) {
-  __shared__ long long pk[2];
-  __shared__ int red[2][kTB / kWave];
-  const int nc = ws.ccnt[blockIdx.x];
-  if (nc == 0 && blockIdx.x != 0) {
-    if (threadIdx.x == 0) ws.tie_cnt[blockIdx.x] = 0u;
-    return;
+template <bool kBits>
+__device__ __forceinline__ void mark_kept(uint8_t* keep, uint32_t* keep_bits, uint32_t i) {
+  if (kBits) {
+    atomicOr(&keep_bits[i >> 5], 1u << (i & 31u));
+  } else {
+    keep[i] = 1;
   }
+}
+
+// picks b3, i.e. the threshold key T; candidates below T are kept, ties (key == T) counted per group
+template <bool kBits>
+__global__ __launch_bounds__(kCandTB) void eng_cand_mark(Ws ws, int64_t nb, uint8_t* __restrict__ keep,
+                                                         uint32_t* __restrict__ keep_bits, int32_t* row_counts,
+                                                         int32_t row_len) {
+  __shared__ int pref[kCandG + 1];
+  __shared__ int kc[kCandG], rc[kCandG];
+  __shared__ long long pk[2];
+  __shared__ int wsum[kCandTB / kWave];
+  if (threadIdx.x < kCandG) kc[threadIdx.x] = 0;
+  const int64_t b0 = int64_t(blockIdx.x) * kCandG;
+  const int g = int(min(int64_t(kCandG), nb - b0));
+  group_prefix(ws, b0, g, pref);
   const int b1 = ws.st->b1, b2 = ws.st->b2;
-  const int64_t need2 = ws.st->need2;
-  wave_pick(ws.hist + 2 * kBins, 1024, need2, pk);
+  wave_pick(ws.hist + 2 * kBins, 1024, ws.st->need2, pk);
   __syncthreads();
   const int b3 = int(pk[0]);
-  const uint32_t thr = (uint32_t(b1) << 21) | (uint32_t(b2) << 10) | uint32_t(b3 < 0 ? 0 : b3);
+  const bool any = b1 >= 0 && b2 >= 0 && b3 >= 0;  // otherwise nothing is taken among the candidates
+  const uint32_t thr = (uint32_t(max(b1, 0)) << 21) | (uint32_t(max(b2, 0)) << 10) | uint32_t(max(b3, 0));
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     ws.st->b3 = b3;
+    ws.st->any = any ? 1 : 0;
     ws.st->thr = thr;
     ws.st->need3 = pk[1];
   }
-  const bool any = b1 >= 0 && b2 >= 0 && b3 >= 0;  // otherwise nothing is taken among the candidates
-  const uint2* seg = ws.cand + size_t(blockIdx.x) * kChunk;
-  int kept = 0, ties = 0;
-  for (int i = threadIdx.x; i < nc; i += kTB) {
-    const uint2 cdt = seg[i];
-    if (any && cdt.x < thr) {
-      keep[cdt.y] = 1;
-      ++kept;
+  const int total = any ? pref[g] : 0;
+  int ties = 0;
+  for (int j = threadIdx.x; j < total; j += kCandTB) {
+    const int k = chunk_in_group<kCandG>(pref, g, j);
+    const uint2 cdt = seg_of(ws, b0 + k)[j - pref[k]];
+    if (cdt.x < thr) {
+      mark_kept<kBits>(keep, keep_bits, cdt.y);
+      atomicAdd(&kc[k], 1);
     }
-    ties += (any && cdt.x == thr) ? 1 : 0;
+    ties += cdt.x == thr ? 1 : 0;
   }
-  kept = wave_sum_int(kept);
-  ties = wave_sum_int(ties);
-  if ((threadIdx.x & (kWave - 1)) == 0) {
-    red[0][threadIdx.x >> 6] = kept;
-    red[1][threadIdx.x >> 6] = ties;
+  ties = block_sum<int, kCandTB>(ties, wsum);  // its barriers also complete kc
+  const int mine = int(threadIdx.x) < g ? kc[threadIdx.x] : 0;
+  if (mine > 0) ws.kept[b0 + threadIdx.x] += mine;
+  if (threadIdx.x == 0) ws.tie_cnt[blockIdx.x] = uint32_t(ties);
+  if (row_counts != nullptr) add_row_counts<kCandG>(row_counts, b0, g, mine, row_len, rc);
+}
+
+// The ties still needed (need3) go to the groups in order: a group takes min(its ties, need3 - ties of the groups
+// before it), lowest index first. Also writes the group's final kept count.
+template <bool kBits>
+__global__ __launch_bounds__(kCandTB) void eng_tie_fix(Ws ws, int64_t nb, uint8_t* __restrict__ keep,
+                                                       uint32_t* __restrict__ keep_bits, int32_t* row_counts,
+                                                       int32_t row_len) {
+  __shared__ int pref[kCandG + 1];
+  __shared__ int kc[kCandG], rc[kCandG];
+  __shared__ long long lsum[kCandTB / kWave];
+  __shared__ uint32_t usum[kCandTB / kWave];
+  __shared__ int isum[kCandTB / kWave];
+  if (threadIdx.x < kCandG) kc[threadIdx.x] = 0;
+  const int64_t b0 = int64_t(blockIdx.x) * kCandG;
+  const int g = int(min(int64_t(kCandG), nb - b0));
+  group_prefix(ws, b0, g, pref);
+  long long before = 0;
+  for (int64_t q = threadIdx.x; q < int64_t(blockIdx.x); q += kCandTB) before += ws.tie_cnt[q];
+  before = block_sum<long long, kCandTB>(before, lsum);
+  const long long mine = ws.tie_cnt[blockIdx.x];
+  const uint32_t take = uint32_t(max(0LL, min(mine, ws.st->need3 - before)));
+  if (take != 0u) {
+    const uint32_t thr = ws.st->thr;
+    const int total = pref[g];
+    uint32_t done = 0;
+    for (int base = 0; base < total && done < take; base += kCandTB) {
+      const int j = base + int(threadIdx.x);
+      int k = 0;
+      uint2 cdt = make_uint2(0xFFFFFFFFu, 0u);
+      if (j < total) {
+        k = chunk_in_group<kCandG>(pref, g, j);
+        cdt = seg_of(ws, b0 + k)[j - pref[k]];
+      }
+      const uint32_t t = (j < total && cdt.x == thr) ? 1u : 0u;
+      uint32_t tot;
+      const uint32_t rank = done + block_excl_scan<uint32_t, kCandTB>(t, usum, &tot);
+      if (t && rank < take) {
+        mark_kept<kBits>(keep, keep_bits, cdt.y);
+        atomicAdd(&kc[k], 1);
+      }
+      done = min(take, done + tot);
+    }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int k = 0, t = 0;
-    for (int w = 0; w < kTB / kWave; ++w) {
-      k += red[0][w];
-      t += red[1][w];
-    }
-    ws.tie_cnt[blockIdx.x] = uint32_t(t);
-    if (k > 0) {
-      ws.kept[blockIdx.x] += k;
-      if (row_counts != nullptr) atomicAdd(&row_counts[chunk_of(blockIdx.x, row_len).row], k);
-    }
+  int kept_k = 0;
+  const int taken = int(threadIdx.x) < g ? kc[threadIdx.x] : 0;
+  if (int(threadIdx.x) < g) {
+    const int64_t b = b0 + threadIdx.x;
+    kept_k = ws.kept[b] + taken;
+    if (taken > 0) ws.kept[b] = kept_k;
   }
-}
-
-// one workgroup: exclusive scan of the chunks' tie counts -> how many ties each chunk takes
-__global__ __launch_bounds__(kTB) void eng_tie_scan(Ws ws, int64_t nb) {
-  __shared__ long long wsum[kTB / kWave];
-  const int64_t per = (nb + kTB - 1) / kTB;
-  const int64_t b0 = min(nb, int64_t(threadIdx.x) * per), b1 = min(nb, b0 + per);
-  long long mine = 0;
-  for (int64_t b = b0; b < b1; ++b) mine += ws.tie_cnt[b];
-  long long total;
-  long long off = block_excl_scan<long long>(mine, wsum, &total);
-  const long long need = ws.st->need3;
-  for (int64_t b = b0; b < b1; ++b) {
-    const long long c = ws.tie_cnt[b];
-    ws.tie_take[b] = uint32_t(max(0LL, min(c, need - off)));
-    off += c;
-  }
-}
-
-// chunks holding kept ties: take the first tie_take of their ties, in index order (= candidate order)
-__global__ __launch_bounds__(kTB) void eng_tie_fix(Ws ws, uint8_t* __restrict__ keep, int32_t* row_counts,
-                                                   int32_t row_len) {
-  const uint32_t take = ws.tie_take[blockIdx.x];
-  if (take == 0u) return;
-  __shared__ uint32_t wsum[kTB / kWave];
-  const uint32_t thr = ws.st->thr;
-  const int nc = ws.ccnt[blockIdx.x];
-  const uint2* seg = ws.cand + size_t(blockIdx.x) * kChunk;
-  uint32_t done = 0;
-  for (int base = 0; base < nc; base += kTB) {
-    const int i = base + int(threadIdx.x);
-    const uint2 cdt = i < nc ? seg[i] : make_uint2(0xFFFFFFFFu, 0u);
-    const uint32_t t = (i < nc && cdt.x == thr) ? 1u : 0u;
-    uint32_t tot;
-    const uint32_t rank = done + block_excl_scan<uint32_t>(t, wsum, &tot);
-    if (t && rank < take) keep[cdt.y] = 1;
-    done += tot;
-    if (done >= take) break;
-  }
-  if (threadIdx.x == 0) {
-    ws.kept[blockIdx.x] += int(take);
-    if (row_counts != nullptr) atomicAdd(&row_counts[chunk_of(blockIdx.x, row_len).row], int(take));
-  }
+  kept_k = block_sum<int, kCandTB>(kept_k, isum);
+  if (threadIdx.x == 0) ws.group_kept[blockIdx.x] = kept_k;
+  if (row_counts != nullptr && take != 0u) add_row_counts<kCandG>(row_counts, b0, g, taken, row_len, rc);
 }
 
 size_t al(size_t x) { return align_up(x, 256); }
 
 struct Layout {
-  int64_t nb;
-  size_t st, hist, cand, ccnt, kept, tie_cnt, tie_take, total;
+  int64_t nb, groups;
+  size_t st, hist, cand, ccnt, kept, tie_cnt, group_kept, total;
 };
 
 Layout layout(int64_t n, int32_t row_len) {
   Layout L;
   L.nb = topm_chunks(n, row_len);
-  const size_t nb = size_t(std::max<int64_t>(L.nb, 1));
+  L.groups = (L.nb + kCandG - 1) / kCandG;
+  const size_t nb = size_t(std::max<int64_t>(L.nb, 1)), ng = size_t(std::max<int64_t>(L.groups, 1));
   size_t o = 0;
   L.st = o;
   o += al(sizeof(State));
   L.hist = o;
-  o += al(3 * kBins * 4);
+  o += al(size_t(3) * kBins * 4);
   L.cand = o;
   o += al(nb * kChunk * sizeof(uint2));
   L.ccnt = o;
@@ -465,11 +577,28 @@ Layout layout(int64_t n, int32_t row_len) {
   L.kept = o;
   o += al(nb * 4);
   L.tie_cnt = o;
-  o += al(nb * 4);
-  L.tie_take = o;
-  o += al(nb * 4);
+  o += al(ng * 4);
+  L.group_kept = o;
+  o += al(ng * 4);
   L.total = o;
   return L;
+}
+
+template <bool kBits, bool kBeta>
+void launch_passes(const TopmInput& in, int64_t m, const TopmOutput& out, const Ws& ws, const Layout& L,
+                   hipStream_t s) {
+  const int64_t nb = L.nb;
+  constexpr int64_t hist_span = int64_t(kHistTB / kWave) * kHistPer, cls_span = int64_t(kClsTB / kWave) * kClsPer;
+  hipLaunchKernelGGL(eng_hist1<kBeta>, dim3(unsigned((nb + hist_span - 1) / hist_span)), dim3(kHistTB), 0, s, in, ws, nb);
+  hipLaunchKernelGGL((eng_classify<kBits, kBeta>), dim3(unsigned((nb + cls_span - 1) / cls_span)), dim3(kClsTB), 0, s, in, ws, nb, m,
+                     out.keep, out.keep_bits, out.row_counts, out.status);
+  hipLaunchKernelGGL(eng_cand_hist2, dim3(unsigned((nb + kH2G - 1) / kH2G)), dim3(kH2TB), 0, s, ws, nb);
+  const unsigned ng = unsigned(L.groups);
+  hipLaunchKernelGGL(eng_cand_hist3, dim3(ng), dim3(kCandTB), 0, s, ws, nb);
+  hipLaunchKernelGGL(eng_cand_mark<kBits>, dim3(ng), dim3(kCandTB), 0, s, ws, nb, out.keep, out.keep_bits,
+                     out.row_counts, in.row_len);
+  hipLaunchKernelGGL(eng_tie_fix<kBits>, dim3(ng), dim3(kCandTB), 0, s, ws, nb, out.keep, out.keep_bits,
+                     out.row_counts, in.row_len);
 }
 
 }  // namespace
@@ -481,8 +610,10 @@ int64_t topm_chunks(int64_t n, int32_t row_len) {
 
 size_t topm_engine_workspace(int64_t n, int32_t row_len) { return layout(n, row_len).total; }
 
-hipError_t launch_topm_engine(const TopmInput& in, int64_t m, uint8_t* keep, int32_t* row_counts, int32_t* status,
-                              void* ws_ptr, int32_t** chunk_kept, hipStream_t s) {
+hipError_t launch_topm_engine(const TopmInput& in, int64_t m, const TopmOutput& out, void* ws_ptr, hipStream_t s,
+                              TopmCounts* counts) {
+  if ((out.keep == nullptr) == (out.keep_bits == nullptr)) return hipErrorInvalidValue;
+  if (out.keep_bits != nullptr && int64_t(in.row_len) != in.n) return hipErrorInvalidValue;  // bits: one row only
   const Layout L = layout(in.n, in.row_len);
   char* w = static_cast<char*>(ws_ptr);
   Ws ws;
@@ -492,20 +623,28 @@ hipError_t launch_topm_engine(const TopmInput& in, int64_t m, uint8_t* keep, int
   ws.ccnt = reinterpret_cast<int32_t*>(w + L.ccnt);
   ws.kept = reinterpret_cast<int32_t*>(w + L.kept);
   ws.tie_cnt = reinterpret_cast<uint32_t*>(w + L.tie_cnt);
-  ws.tie_take = reinterpret_cast<uint32_t*>(w + L.tie_take);
-  if (chunk_kept != nullptr) *chunk_kept = ws.kept;
+  ws.group_kept = reinterpret_cast<int32_t*>(w + L.group_kept);
+  if (counts != nullptr) {
+    counts->chunk_kept = ws.kept;
+    counts->group_kept = ws.group_kept;
+  }
   const int64_t n_rows = in.row_len > 0 ? in.n / in.row_len : 0;
-  const int64_t clear_n = std::max<int64_t>(3 * kBins, row_counts != nullptr ? n_rows : 0);
-  hipLaunchKernelGGL(eng_clear, dim3(unsigned((clear_n + kTB - 1) / kTB)), dim3(kTB), 0, s, ws, row_counts, n_rows);
+  const int64_t clear_n = std::max<int64_t>(3 * kBins, out.row_counts != nullptr ? n_rows : 0);
+  hipLaunchKernelGGL(eng_clear, dim3(unsigned((clear_n + 255) / 256)), dim3(256), 0, s, ws, out.row_counts, n_rows,
+                     out.clear_status ? out.status : nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || L.nb == 0) return e;
-  const unsigned nb = unsigned(L.nb);
-  hipLaunchKernelGGL(eng_hist1, dim3(unsigned((L.nb + kHistGroup - 1) / kHistGroup)), dim3(kTB), 0, s, in, ws, L.nb);
-  hipLaunchKernelGGL(eng_classify, dim3(nb), dim3(kTB), 0, s, in, ws, m, keep, row_counts, status);
-  hipLaunchKernelGGL(eng_cand_hist3, dim3(nb), dim3(kTB), 0, s, ws);
-  hipLaunchKernelGGL(eng_cand_mark, dim3(nb), dim3(kTB), 0, s, ws, keep, row_counts, in.row_len);
-  hipLaunchKernelGGL(eng_tie_scan, dim3(1), dim3(kTB), 0, s, ws, L.nb);
-  hipLaunchKernelGGL(eng_tie_fix, dim3(nb), dim3(kTB), 0, s, ws, keep, row_counts, in.row_len);
+  if (out.keep_bits != nullptr) {
+    if (in.scores != nullptr) {
+      launch_passes<true, false>(in, m, out, ws, L, s);
+    } else {
+      return hipErrorInvalidValue;  // the bit mask serves kvc_topk, which reads scores
+    }
+  } else if (in.scores != nullptr) {
+    launch_passes<false, false>(in, m, out, ws, L, s);
+  } else {
+    launch_passes<false, true>(in, m, out, ws, L, s);
+  }
   return hipGetLastError();
 }
 

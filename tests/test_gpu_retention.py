@@ -116,6 +116,21 @@ def test_topm_edge_cases_and_ties(gpu_lib, m_kind):
     _check_topm(torch.from_numpy(s), tm, m)
 
 
+@pytest.mark.parametrize("rows,row_len", [(300, 48), (70, 2064)])
+def test_topm_many_short_rows(gpu_lib, rows, row_len):
+    """Rows shorter than a chunk (one chunk per row, so a group of chunks spans dozens of rows) and rows one float4
+    past a chunk: the per-row counts and the tie cut stay exact."""
+    import torch
+    from kv_cache_compression_gqa_amd import retention
+    rng = np.random.default_rng(rows)
+    s = (np.round(rng.standard_normal((rows, row_len)) * 2.0) / 2.0).astype(np.float32)
+    n = s.size
+    for m in (1, n // 3, n - 7):
+        tm = retention.global_topm(torch.from_numpy(s).cuda(), m)
+        torch.cuda.synchronize()
+        _check_topm(torch.from_numpy(s), tm, m)
+
+
 @pytest.mark.parametrize("layers,T,frac", [(2, 2048, 0.1), (1, 4112, 0.37), (3, 8192, 0.0), (1, 2064, 1.0)])
 def test_topm_fused_retention_equals_score_then_select(gpu_lib, layers, T, frac):
     """The top-M taken on beta with the log-retention computed in place keeps exactly what the top-M of the scores
