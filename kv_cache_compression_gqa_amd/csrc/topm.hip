@@ -4,23 +4,31 @@
 //
 // Keys are the inverted order-preserving images of the scores (a smaller key is a larger score; +0 == -0). The
 // scores are read from memory or computed on the fly as DBTrimKV's log-retention (t - i) * logf(beta) (the
-// retention score of section 2; computing it where it is used saves writing and re-reading it). Passes over the
-// whole input: two; everything after them touches only the entries of one histogram bin.
+// retention score of section 2; computing it where it is used saves writing and re-reading it). The input is read
+// once in full; everything after that touches only the candidates, the entries of a few histogram bins.
 // The unit of work is a chunk of 2048 entries inside one row: one wave reads it with eight 16-byte loads per lane.
-//   hist1      (64 chunks per 1024-thread workgroup, one chunk per wave at a time): 2048-bin histogram of the top 11
-//              key bits, one LDS copy per wave, one global atomic per non-empty bin.
-//   classify   (16 chunks per 256-thread workgroup, one per wave at a time, no barrier): picks the bin b1 holding the m-th key
-//              (every workgroup takes the same decision from the same counts), writes the keep mask (1 below b1)
-//              and moves the entries of b1 to their chunk's candidate segment, in index order; kept entries are
-//              counted per chunk and row.
-//   cand_hist2 (256 chunks' candidates per workgroup): histogram of the candidates' next 11 key bits.
-//   cand_hist3 (groups of 64 chunks): picks b2; histogram of the last 10 bits of the candidates in b2.
+//   sample     histogram (top 11 key bits) of S = min(65536, n / 4) float4s, one per stratum of n / S entries at a
+//              pseudo-random offset inside it (a fixed hash of the stratum number), so that no row structure aliases
+//              with the sampling.
+//   classify   (16 chunks per 256-thread workgroup, one per wave at a time, no barrier inside the loop): locates in
+//              the sample the window [lo, hi] of bins that holds the m-th key with a wide margin (six standard
+//              deviations of the sampled count, on the host); entries below lo are kept, entries of lo .. hi go
+//              to their chunk's candidate segment in index order, and the exact histogram is built on the way.
+//   fallback   each workgroup picks the exact bin b1 from that histogram; if the window held it (the usual case) it
+//              returns at once, otherwise it classifies its chunks again against b1 alone.
+//   cand_hist2 (256 chunks' candidates per workgroup): picks b1; histogram of the next 11 key bits of the candidates
+//              in b1.
+//   cand_hist3 (groups of 64 chunks): picks b2; histogram of the last 10 key bits of the candidates in (b1, b2).
 //   cand_mark  (same groups): picks b3, i.e. the threshold key T; keeps every candidate below T and counts the ties
 //              (key == T) of its group.
 //   tie_fix    (same groups): the ties still needed go to the groups in index order: a group's share follows from
-//              the tie counts of the groups before it; it takes them lowest index first.
+//              the tie counts of the groups before it; it takes them lowest index first. It also adds the groups'
+//              final kept counts to their rows.
 // Workgroup 0 of a kernel records its pick for the kernels after it; no workgroup waits for another inside a kernel.
 #include <algorithm>
+#include <cmath>
+#include <limits>
+#include <type_traits>
 
 #include "kvc_internal.h"
 
@@ -30,23 +38,25 @@ namespace {
 constexpr int kChunk = kTopmChunk;        // entries per chunk (inside one row): one wave's unit
 constexpr int kU = kChunk / (4 * kWave);  // float4 loads per lane and chunk
 constexpr int kBins = 2048;
-constexpr int kHistTB = 1024, kHistPer = 4;  // hist1: threads, chunks per wave
-constexpr int kClsTB = 256, kClsPer = 4;     // classify
-constexpr int kH2TB = 1024, kH2G = 256;      // cand_hist2: threads, chunks per workgroup
+constexpr int64_t kSampleMax = 65536;      // sampled float4s
+constexpr int kSampleTB = 256, kSamplePer = 4;  // sample: threads, float4s per thread
+constexpr int kClsTB = 256, kClsPer = 4;   // classify: threads, chunks per wave
+constexpr int kFallbackPer = 16;           // the fallback classification: chunks per wave
+constexpr int kH2TB = 1024, kH2G = 256;    // cand_hist2: threads, chunks per workgroup
 constexpr int kCandTB = 256, kCandG = kTopmGroup;  // cand_hist3 / cand_mark / tie_fix
-static_assert(kU == 8, "two u64 of four 16-bit fields hold a lane's per-slice candidate counts");
 static_assert(kCandG <= kWave, "a group's chunk prefix is one wave scan");
 static_assert(kH2G <= kH2TB, "one chunk count per thread");
 
 struct State {
   int32_t b1, b2, b3, any;  // any: the threshold key is defined (m > 0)
-  uint32_t thr, pad;
+  uint32_t thr;
+  int32_t lo, hi, pad;      // the sampled window of bins
   int64_t need1, need2, need3;
 };
 
 struct Ws {
   State* st;
-  uint32_t* hist;       // [3][kBins]
+  uint32_t* hist;       // [4][kBins]: exact top bits, candidates' middle bits, last bits, sample
   uint2* cand;          // [nb][kChunk] (key, entry index) per chunk segment, index order
   int32_t* ccnt;        // [nb] candidates per chunk
   int32_t* kept;        // [nb] entries kept per chunk
@@ -54,12 +64,12 @@ struct Ws {
   int32_t* group_kept;  // [groups]
 };
 
+// A larger score has a smaller key. Adding +0 turns -0 into +0 (round to nearest), so the two zeros tie; then a
+// negative score keeps its bits and a positive one has its 31 low bits flipped.
 __device__ __forceinline__ uint32_t desc_key(float s) {
-  const uint32_t u = __float_as_uint(s == 0.0f ? 0.0f : s);
-  const uint32_t asc = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ~asc;
+  const uint32_t u = __float_as_uint(s + 0.0f);
+  return u ^ (~uint32_t(int32_t(u) >> 31) & 0x7FFFFFFFu);
 }
-
 struct Chunk {
   int64_t beg, end, row;
 };
@@ -187,6 +197,48 @@ __device__ void wave_pick(const uint32_t* h, int nbins, int64_t need, long long*
   }
 }
 
+// Bins of global histogram h holding its lo_pos-th and hi_pos-th keys (1-based): pk[0] = 0 when lo_pos < 1, pk[1] =
+// kBins - 1 when hi_pos exceeds the histogram's total. Wave 0 alone; the caller publishes pk with a barrier.
+__device__ void wave_locate(const uint32_t* h, int64_t lo_pos, int64_t hi_pos, long long* pk) {
+  if (threadIdx.x >= kWave) return;
+  const int lane = threadIdx.x;
+  constexpr int per = kBins / kWave;
+  uint32_t c[per];
+  const uint4* hp = reinterpret_cast<const uint4*>(h + lane * per);
+#pragma unroll
+  for (int q = 0; q < per / 4; ++q) {
+    const uint4 x = hp[q];
+    c[4 * q] = x.x;
+    c[4 * q + 1] = x.y;
+    c[4 * q + 2] = x.z;
+    c[4 * q + 3] = x.w;
+  }
+  long long own = 0;
+#pragma unroll
+  for (int k = 0; k < per; ++k) own += c[k];
+  long long inc = own;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const long long o = __shfl_up(inc, d, kWave);
+    if (lane >= d) inc += o;
+  }
+  const long long excl = inc - own;
+  if (lane == 0) {
+    pk[0] = 0;
+    pk[1] = kBins - 1;
+  }
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const int64_t pos = which == 0 ? lo_pos : hi_pos;
+    if (pos >= 1 && excl < pos && pos <= inc) {
+      long long rem = pos - excl;
+      int b = 0;
+      while (b < per - 1 && rem > (long long)c[b]) rem -= c[b++];
+      pk[which] = lane * per + b;
+    }
+  }
+}
+
 // Candidates of the chunks b0 .. b0 + g - 1 as one index-ordered sequence: pref[k] = candidates of the group's chunks
 // before chunk k (pref[g] = all). Wave 0 alone; the caller publishes pref with a barrier.
 __device__ void group_prefix(const Ws& ws, int64_t b0, int g, int* pref) {
@@ -256,86 +308,110 @@ __device__ void add_row_counts(int32_t* row_counts, int64_t b0, int g, int cnt, 
 
 __global__ __launch_bounds__(256) void eng_clear(Ws ws, int32_t* row_counts, int64_t n_rows, int32_t* status) {
   const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (i < 3 * kBins) ws.hist[i] = 0u;
+  if (i < 4 * kBins) ws.hist[i] = 0u;
   if (i < int64_t(sizeof(State) / sizeof(uint32_t))) reinterpret_cast<uint32_t*>(ws.st)[i] = 0u;
   if (row_counts != nullptr && i < n_rows) row_counts[i] = 0;
   if (status != nullptr && i == 0) *status = 0;
 }
 
+// One float4 per stratum: stratum j of S covers float4s [j n4 / S, (j + 1) n4 / S); the float4 taken is at the
+// fraction (hash(j) mod 2^16) / 2^16 of it (hash(j) = 40503 j + 17).
 template <bool kBeta>
-__global__ __launch_bounds__(kHistTB) void eng_hist1(TopmInput in, Ws ws, int64_t nb) {
-  constexpr int W = kHistTB / kWave;
-  __shared__ uint32_t h[W][kBins];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
-  int64_t b = int64_t(blockIdx.x) * (W * kHistPer) + wave;  // wave's chunks: b, b + W, ...
-  float4 v[kU], vn[kU];
-  if (b < nb) load_chunk<kBeta>(in, chunk_of(b, in.row_len), lane, v);
-  for (int i = threadIdx.x; i < W * kBins; i += kHistTB) (&h[0][0])[i] = 0u;
-  __syncthreads();
-  for (int i = 0; i < kHistPer && b < nb; ++i, b += W) {  // wave-uniform
-    if (i + 1 < kHistPer && b + W < nb) load_chunk<kBeta>(in, chunk_of(b + W, in.row_len), lane, vn);
-    const Chunk r = chunk_of(b, in.row_len);
+__global__ __launch_bounds__(kSampleTB) void eng_sample(TopmInput in, Ws ws, int64_t S) {
+  __shared__ uint32_t h[kBins];
+  for (int i = threadIdx.x; i < kBins; i += kSampleTB) h[i] = 0u;
+  const int64_t n4 = in.n / 4;
+  const float* src = kBeta ? in.beta : in.scores;
+  float4 x[kSamplePer];
+  int64_t e[kSamplePer];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int64_t e = r.beg + 4 * (lane + kWave * u);
-      const float vs[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if (e + c < r.end) atomicAdd(&h[wave][desc_key(vs[c]) >> 21], 1u);
-      }
+  for (int q = 0; q < kSamplePer; ++q) {  // every load first
+    const int64_t j = (int64_t(blockIdx.x) * kSamplePer + q) * kSampleTB + threadIdx.x;
+    e[q] = -1;
+    if (j < S) {
+      const int64_t jit = (j * 40503 + 17) & 0xFFFF;
+      e[q] = 4 * (((j * 65536 + jit) * n4) / (S * 65536));  // e + 3 < n
+      x[q] = *reinterpret_cast<const float4*>(src + e[q]);
     }
-#pragma unroll
-    for (int u = 0; u < kU; ++u) v[u] = vn[u];
   }
   __syncthreads();
-  for (int bin = threadIdx.x; bin < kBins; bin += kHistTB) {
-    uint32_t s = 0u;
 #pragma unroll
-    for (int w = 0; w < W; ++w) s += h[w][bin];
-    if (s != 0u) atomicAdd(&ws.hist[bin], s);
+  for (int q = 0; q < kSamplePer; ++q) {
+    if (e[q] < 0) continue;
+    float4 y = x[q];
+    if (kBeta) {
+      const int i = int(e[q] % in.row_len);  // the 4 entries lie in one row (row_len % 16 == 0)
+      y.x = float(in.t - i) * logf(y.x);
+      y.y = float(in.t - i - 1) * logf(y.y);
+      y.z = float(in.t - i - 2) * logf(y.z);
+      y.w = float(in.t - i - 3) * logf(y.w);
+    }
+    atomicAdd(&h[desc_key(y.x) >> 21], 1u);
+    atomicAdd(&h[desc_key(y.y) >> 21], 1u);
+    atomicAdd(&h[desc_key(y.z) >> 21], 1u);
+    atomicAdd(&h[desc_key(y.w) >> 21], 1u);
+  }
+  __syncthreads();
+  for (int bin = threadIdx.x; bin < kBins; bin += kSampleTB) {
+    if (h[bin] != 0u) atomicAdd(&ws.hist[3 * kBins + bin], h[bin]);
   }
 }
 
 // kBits: the keep mask as bits (one row: chunk starts are multiples of 2048), else as bytes; kBeta: scores computed
-// from beta
-template <bool kBits, bool kBeta>
-__global__ __launch_bounds__(kClsTB) void eng_classify(TopmInput in, Ws ws, int64_t nb, int64_t m,
-                                                       uint8_t* __restrict__ keep, uint32_t* __restrict__ keep_bits,
-                                                       int32_t* row_counts, int32_t* status) {
-  constexpr int W = kClsTB / kWave, kSpan = W * kClsPer;
+// from beta. kSpec: the first classification, against the window [lo, hi] located in the sample, building the exact
+// histogram on the way. Otherwise the fallback: every workgroup picks the exact bin b1 and returns at once when the
+// window held it, else classifies its chunks again against [b1, b1] (rewriting their mask, candidates and counts).
+template <bool kBits, bool kBeta, bool kSpec, int kPer>
+__global__ __launch_bounds__(kClsTB) void eng_classify(TopmInput in, Ws ws, int64_t nb, int64_t m, int64_t lo_pos,
+                                                       int64_t hi_pos, uint8_t* __restrict__ keep,
+                                                       uint32_t* __restrict__ keep_bits, int32_t* status) {
+  constexpr int W = kClsTB / kWave, kSpan = W * kPer;
   __shared__ long long pk[2];
-  __shared__ int kc[kSpan], rc[kSpan];
+  __shared__ uint32_t h[kSpec ? kBins : 1];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
-  const int64_t b0 = int64_t(blockIdx.x) * kSpan;
-  int64_t b = b0 + wave;
+  int64_t b = int64_t(blockIdx.x) * kSpan + wave;
   float4 v[kU], vn[kU];
-  if (b < nb) load_chunk<kBeta>(in, chunk_of(b, in.row_len), lane, v);  // the first chunk's loads before the pick
-  wave_pick(ws.hist, kBins, m, pk);
-  __syncthreads();
-  const int b1 = int(pk[0]);
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    ws.st->b1 = b1;
-    ws.st->need1 = pk[1];
+  int lo, hi;
+  if (kSpec) {
+    if (b < nb) load_chunk<kBeta>(in, chunk_of(b, in.row_len), lane, v);  // the first chunk's loads first
+    for (int i = threadIdx.x; i < kBins; i += kClsTB) h[i] = 0u;
+    wave_locate(ws.hist + 3 * kBins, lo_pos, hi_pos, pk);
+    __syncthreads();
+    lo = int(pk[0]);
+    hi = int(pk[1]);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      ws.st->lo = lo;
+      ws.st->hi = hi;
+    }
+  } else {
+    wave_pick(ws.hist, kBins, m, pk);
+    __syncthreads();
+    const int b1 = int(pk[0]), slo = ws.st->lo, shi = ws.st->hi;
+    if ((b1 < 0 && slo == 0) || (slo <= b1 && b1 <= shi)) return;  // uniform: the window held b1
+    lo = hi = b1;
+    if (b < nb) load_chunk<kBeta>(in, chunk_of(b, in.row_len), lane, v);
   }
   bool nan = false;
-  for (int i = 0; i < kClsPer && b < nb; ++i, b += W) {  // wave-uniform; no barrier below
-    if (i + 1 < kClsPer && b + W < nb) load_chunk<kBeta>(in, chunk_of(b + W, in.row_len), lane, vn);
+  for (int i = 0; i < kPer && b < nb; ++i, b += W) {  // wave-uniform; no barrier below
+    if (i + 1 < kPer && b + W < nb) load_chunk<kBeta>(in, chunk_of(b + W, in.row_len), lane, vn);
     const Chunk r = chunk_of(b, in.row_len);
     uint2* seg = ws.cand + size_t(b) * kChunk;
     int base = 0, kept = 0;  // wave-uniform: candidates written so far, entries kept
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
+    // one slice of 256 entries; kFull: the chunk has all 2048 (no entry past its end)
+    auto slice = [&](auto full, int u) {
+      constexpr bool kFull = decltype(full)::value;
       const int64_t e = r.beg + 4 * (lane + kWave * u);
       const float vs[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      nan |= __builtin_isunordered(vs[0], vs[1]) || __builtin_isunordered(vs[2], vs[3]);
       bool k1[4], cd[4];
       unsigned long long K[4], C[4];  // ballots: entry c of every lane kept / a candidate
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const bool valid = e + c < r.end;
-        nan |= valid && vs[c] != vs[c];
+        const bool valid = kFull || e + c < r.end;
         const int d = int(desc_key(vs[c]) >> 21);
-        k1[c] = valid && d < b1;
-        cd[c] = valid && d == b1;
+        if (kSpec && valid) atomicAdd(&h[d], 1u);
+        k1[c] = valid && d < lo;
+        cd[c] = valid && uint32_t(d - lo) <= uint32_t(hi - lo);
         K[c] = __ballot(k1[c]);
         C[c] = __ballot(cd[c]);
       }
@@ -350,7 +426,7 @@ __global__ __launch_bounds__(kClsTB) void eng_classify(TopmInput in, Ws ws, int6
       } else {
         const uint32_t out = (k1[0] ? 1u : 0u) | (k1[1] ? 0x100u : 0u) | (k1[2] ? 0x10000u : 0u) |
                              (k1[3] ? 0x1000000u : 0u);
-        if (e + 4 <= r.end) {
+        if (kFull || e + 4 <= r.end) {
           *reinterpret_cast<uint32_t*>(keep + e) = out;
         } else {
 #pragma unroll
@@ -368,32 +444,46 @@ __global__ __launch_bounds__(kClsTB) void eng_classify(TopmInput in, Ws ws, int6
         }
         base += __popcll(C[0]) + __popcll(C[1]) + __popcll(C[2]) + __popcll(C[3]);
       }
+    };
+    if (r.end - r.beg == kChunk) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) slice(std::true_type(), u);
+    } else {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) slice(std::false_type(), u);
     }
     if (lane == 0) {
       ws.ccnt[b] = base;
       ws.kept[b] = kept;
-      kc[b - b0] = kept;
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) v[u] = vn[u];
   }
-  if (nan) atomicOr(status, KVC_DEV_NAN_SCORE);
-  if (row_counts != nullptr) {
+  if (kSpec) {
+    if (nan) atomicOr(status, KVC_DEV_NAN_SCORE);
     __syncthreads();
-    const int g = int(min(int64_t(kSpan), nb - b0));
-    add_row_counts<kSpan>(row_counts, b0, g, int(threadIdx.x) < g ? kc[threadIdx.x] : 0, in.row_len, rc);
+    for (int bin = threadIdx.x; bin < kBins; bin += kClsTB) {
+      if (h[bin] != 0u) atomicAdd(&ws.hist[bin], h[bin]);
+    }
   }
 }
 
-// histogram of the candidates' key bits 20..10 (every candidate is in bin b1)
-__global__ __launch_bounds__(kH2TB) void eng_cand_hist2(Ws ws, int64_t nb) {
+// picks b1; histogram of key bits 20..10 of the candidates in b1
+__global__ __launch_bounds__(kH2TB) void eng_cand_hist2(Ws ws, int64_t nb, int64_t m) {
   __shared__ uint32_t h[kBins];
   __shared__ int pref[kH2G + 1];
   __shared__ int wsum[kH2TB / kWave];
+  __shared__ long long pk[2];
   for (int i = threadIdx.x; i < kBins; i += kH2TB) h[i] = 0u;
   const int64_t b0 = int64_t(blockIdx.x) * kH2G;
   const int g = int(min(int64_t(kH2G), nb - b0));
+  wave_pick(ws.hist, kBins, m, pk);  // the exact b1 (wave 0, published by the barriers below)
   group_prefix_block<kH2TB>(ws, b0, g, pref, wsum);
+  const int b1 = int(pk[0]);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    ws.st->b1 = b1;
+    ws.st->need1 = pk[1];
+  }
   const int total = pref[g];
   constexpr int kUn = 4;
   for (int j0 = threadIdx.x; j0 < total; j0 += kH2TB * kUn) {
@@ -409,7 +499,7 @@ __global__ __launch_bounds__(kH2TB) void eng_cand_hist2(Ws ws, int64_t nb) {
     }
 #pragma unroll
     for (int q = 0; q < kUn; ++q) {
-      if (j0 + q * kH2TB < total) atomicAdd(&h[(key[q] >> 10) & 0x7FFu], 1u);
+      if (j0 + q * kH2TB < total && int(key[q] >> 21) == b1) atomicAdd(&h[(key[q] >> 10) & 0x7FFu], 1u);
     }
   }
   __syncthreads();
@@ -418,7 +508,7 @@ __global__ __launch_bounds__(kH2TB) void eng_cand_hist2(Ws ws, int64_t nb) {
   }
 }
 
-// picks b2; histogram of the last 10 key bits of the candidates in b2
+// picks b2; histogram of the last 10 key bits of the candidates in (b1, b2)
 __global__ __launch_bounds__(kCandTB) void eng_cand_hist3(Ws ws, int64_t nb) {
   __shared__ uint32_t h3[1024];
   __shared__ int pref[kCandG + 1];
@@ -434,11 +524,25 @@ __global__ __launch_bounds__(kCandTB) void eng_cand_hist3(Ws ws, int64_t nb) {
     ws.st->b2 = b2;
     ws.st->need2 = pk[1];
   }
-  const int total = pref[g];
-  for (int j = threadIdx.x; j < total; j += kCandTB) {
-    const int k = chunk_in_group<kCandG>(pref, g, j);
-    const uint32_t key = seg_of(ws, b0 + k)[j - pref[k]].x;
-    if (int((key >> 10) & 0x7FFu) == b2) atomicAdd(&h3[key & 0x3FFu], 1u);
+  const int b1 = ws.st->b1;
+  const int total = (b1 >= 0 && b2 >= 0) ? pref[g] : 0;
+  const uint32_t top = (uint32_t(b1) << 11) | uint32_t(b2);  // key bits 31..10 of the candidates counted
+  constexpr int kUn = 4;  // loads in flight per thread
+  for (int j0 = threadIdx.x; j0 < total; j0 += kCandTB * kUn) {
+    uint32_t key[kUn];
+#pragma unroll
+    for (int q = 0; q < kUn; ++q) {
+      const int j = j0 + q * kCandTB;
+      key[q] = 0xFFFFFFFFu;
+      if (j < total) {
+        const int k = chunk_in_group<kCandG>(pref, g, j);
+        key[q] = seg_of(ws, b0 + k)[j - pref[k]].x;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kUn; ++q) {
+      if (j0 + q * kCandTB < total && (key[q] >> 10) == top) atomicAdd(&h3[key[q] & 0x3FFu], 1u);
+    }
   }
   __syncthreads();
   for (int bin = threadIdx.x; bin < 1024; bin += kCandTB) {
@@ -458,10 +562,9 @@ __device__ __forceinline__ void mark_kept(uint8_t* keep, uint32_t* keep_bits, ui
 // picks b3, i.e. the threshold key T; candidates below T are kept, ties (key == T) counted per group
 template <bool kBits>
 __global__ __launch_bounds__(kCandTB) void eng_cand_mark(Ws ws, int64_t nb, uint8_t* __restrict__ keep,
-                                                         uint32_t* __restrict__ keep_bits, int32_t* row_counts,
-                                                         int32_t row_len) {
+                                                         uint32_t* __restrict__ keep_bits) {
   __shared__ int pref[kCandG + 1];
-  __shared__ int kc[kCandG], rc[kCandG];
+  __shared__ int kc[kCandG];
   __shared__ long long pk[2];
   __shared__ int wsum[kCandTB / kWave];
   if (threadIdx.x < kCandG) kc[threadIdx.x] = 0;
@@ -482,20 +585,33 @@ __global__ __launch_bounds__(kCandTB) void eng_cand_mark(Ws ws, int64_t nb, uint
   }
   const int total = any ? pref[g] : 0;
   int ties = 0;
-  for (int j = threadIdx.x; j < total; j += kCandTB) {
-    const int k = chunk_in_group<kCandG>(pref, g, j);
-    const uint2 cdt = seg_of(ws, b0 + k)[j - pref[k]];
-    if (cdt.x < thr) {
-      mark_kept<kBits>(keep, keep_bits, cdt.y);
-      atomicAdd(&kc[k], 1);
+  constexpr int kUn = 4;  // loads in flight per thread
+  for (int j0 = threadIdx.x; j0 < total; j0 += kCandTB * kUn) {
+    uint2 cdt[kUn];
+    int kk[kUn];
+#pragma unroll
+    for (int q = 0; q < kUn; ++q) {
+      const int j = j0 + q * kCandTB;
+      cdt[q] = make_uint2(0xFFFFFFFFu, 0u);
+      kk[q] = 0;
+      if (j < total) {
+        kk[q] = chunk_in_group<kCandG>(pref, g, j);
+        cdt[q] = seg_of(ws, b0 + kk[q])[j - pref[kk[q]]];
+      }
     }
-    ties += cdt.x == thr ? 1 : 0;
+#pragma unroll
+    for (int q = 0; q < kUn; ++q) {
+      if (j0 + q * kCandTB >= total) continue;
+      if (cdt[q].x < thr) {
+        mark_kept<kBits>(keep, keep_bits, cdt[q].y);
+        atomicAdd(&kc[kk[q]], 1);
+      }
+      ties += cdt[q].x == thr ? 1 : 0;
+    }
   }
   ties = block_sum<int, kCandTB>(ties, wsum);  // its barriers also complete kc
-  const int mine = int(threadIdx.x) < g ? kc[threadIdx.x] : 0;
-  if (mine > 0) ws.kept[b0 + threadIdx.x] += mine;
+  if (int(threadIdx.x) < g && kc[threadIdx.x] > 0) ws.kept[b0 + threadIdx.x] += kc[threadIdx.x];
   if (threadIdx.x == 0) ws.tie_cnt[blockIdx.x] = uint32_t(ties);
-  if (row_counts != nullptr) add_row_counts<kCandG>(row_counts, b0, g, mine, row_len, rc);
 }
 
 // The ties still needed (need3) go to the groups in order: a group takes min(its ties, need3 - ties of the groups
@@ -541,16 +657,16 @@ __global__ __launch_bounds__(kCandTB) void eng_tie_fix(Ws ws, int64_t nb, uint8_
     }
   }
   __syncthreads();
-  int kept_k = 0;
-  const int taken = int(threadIdx.x) < g ? kc[threadIdx.x] : 0;
+  int kept_k = 0;  // chunk b0 + t's final kept count (t < g)
   if (int(threadIdx.x) < g) {
     const int64_t b = b0 + threadIdx.x;
+    const int taken = kc[threadIdx.x];
     kept_k = ws.kept[b] + taken;
     if (taken > 0) ws.kept[b] = kept_k;
   }
-  kept_k = block_sum<int, kCandTB>(kept_k, isum);
-  if (threadIdx.x == 0) ws.group_kept[blockIdx.x] = kept_k;
-  if (row_counts != nullptr && take != 0u) add_row_counts<kCandG>(row_counts, b0, g, taken, row_len, rc);
+  const int group_total = block_sum<int, kCandTB>(kept_k, isum);
+  if (threadIdx.x == 0) ws.group_kept[blockIdx.x] = group_total;
+  if (row_counts != nullptr) add_row_counts<kCandG>(row_counts, b0, g, kept_k, row_len, rc);
 }
 
 size_t al(size_t x) { return align_up(x, 256); }
@@ -569,7 +685,7 @@ Layout layout(int64_t n, int32_t row_len) {
   L.st = o;
   o += al(sizeof(State));
   L.hist = o;
-  o += al(size_t(3) * kBins * 4);
+  o += al(size_t(4) * kBins * 4);
   L.cand = o;
   o += al(nb * kChunk * sizeof(uint2));
   L.ccnt = o;
@@ -588,15 +704,27 @@ template <bool kBits, bool kBeta>
 void launch_passes(const TopmInput& in, int64_t m, const TopmOutput& out, const Ws& ws, const Layout& L,
                    hipStream_t s) {
   const int64_t nb = L.nb;
-  constexpr int64_t hist_span = int64_t(kHistTB / kWave) * kHistPer, cls_span = int64_t(kClsTB / kWave) * kClsPer;
-  hipLaunchKernelGGL(eng_hist1<kBeta>, dim3(unsigned((nb + hist_span - 1) / hist_span)), dim3(kHistTB), 0, s, in, ws, nb);
-  hipLaunchKernelGGL((eng_classify<kBits, kBeta>), dim3(unsigned((nb + cls_span - 1) / cls_span)), dim3(kClsTB), 0, s, in, ws, nb, m,
-                     out.keep, out.keep_bits, out.row_counts, out.status);
-  hipLaunchKernelGGL(eng_cand_hist2, dim3(unsigned((nb + kH2G - 1) / kH2G)), dim3(kH2TB), 0, s, ws, nb);
+  // the sample and the window around the m-th key's expected place in it: six standard deviations of a binomial
+  // count plus four, so that a miss (handled by the fallback pass) is rare
+  const int64_t S = std::min<int64_t>(kSampleMax, in.n / 4);
+  int64_t lo_pos = 0, hi_pos = std::numeric_limits<int64_t>::max();
+  if (S > 0) {
+    const double st = 4.0 * double(S), q = double(m) / double(in.n);
+    const double c = q * st, d = 6.0 * std::sqrt(st * q * (1.0 - q)) + 4.0;
+    lo_pos = int64_t(std::floor(c - d));
+    hi_pos = int64_t(std::ceil(c + d));
+    constexpr int64_t per_wg = int64_t(kSampleTB) * kSamplePer;
+    hipLaunchKernelGGL(eng_sample<kBeta>, dim3(unsigned((S + per_wg - 1) / per_wg)), dim3(kSampleTB), 0, s, in, ws, S);
+  }
+  constexpr int64_t spec_span = int64_t(kClsTB / kWave) * kClsPer, fb_span = int64_t(kClsTB / kWave) * kFallbackPer;
+  hipLaunchKernelGGL((eng_classify<kBits, kBeta, true, kClsPer>), dim3(unsigned((nb + spec_span - 1) / spec_span)),
+                     dim3(kClsTB), 0, s, in, ws, nb, m, lo_pos, hi_pos, out.keep, out.keep_bits, out.status);
+  hipLaunchKernelGGL((eng_classify<kBits, kBeta, false, kFallbackPer>), dim3(unsigned((nb + fb_span - 1) / fb_span)),
+                     dim3(kClsTB), 0, s, in, ws, nb, m, lo_pos, hi_pos, out.keep, out.keep_bits, out.status);
+  hipLaunchKernelGGL(eng_cand_hist2, dim3(unsigned((nb + kH2G - 1) / kH2G)), dim3(kH2TB), 0, s, ws, nb, m);
   const unsigned ng = unsigned(L.groups);
   hipLaunchKernelGGL(eng_cand_hist3, dim3(ng), dim3(kCandTB), 0, s, ws, nb);
-  hipLaunchKernelGGL(eng_cand_mark<kBits>, dim3(ng), dim3(kCandTB), 0, s, ws, nb, out.keep, out.keep_bits,
-                     out.row_counts, in.row_len);
+  hipLaunchKernelGGL(eng_cand_mark<kBits>, dim3(ng), dim3(kCandTB), 0, s, ws, nb, out.keep, out.keep_bits);
   hipLaunchKernelGGL(eng_tie_fix<kBits>, dim3(ng), dim3(kCandTB), 0, s, ws, nb, out.keep, out.keep_bits,
                      out.row_counts, in.row_len);
 }
@@ -629,7 +757,7 @@ hipError_t launch_topm_engine(const TopmInput& in, int64_t m, const TopmOutput& 
     counts->group_kept = ws.group_kept;
   }
   const int64_t n_rows = in.row_len > 0 ? in.n / in.row_len : 0;
-  const int64_t clear_n = std::max<int64_t>(3 * kBins, out.row_counts != nullptr ? n_rows : 0);
+  const int64_t clear_n = std::max<int64_t>(4 * kBins, out.row_counts != nullptr ? n_rows : 0);
   hipLaunchKernelGGL(eng_clear, dim3(unsigned((clear_n + 255) / 256)), dim3(256), 0, s, ws, out.row_counts, n_rows,
                      out.clear_status ? out.status : nullptr);
   hipError_t e = hipGetLastError();

@@ -12,6 +12,7 @@ import pytest
 from kv_cache_compression_gqa_amd import abi, configs, synth
 from oracle import dbtrim, select
 from tests.decode_parity import rel_check
+from tests.engine_sampling import sampled_entries
 
 pytestmark = pytest.mark.gpu
 
@@ -114,6 +115,29 @@ def test_topm_edge_cases_and_ties(gpu_lib, m_kind):
     tm = retention.global_topm(torch.from_numpy(s).cuda(), m)
     torch.cuda.synchronize()
     _check_topm(torch.from_numpy(s), tm, m)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_topm_misleading_sample_takes_the_fallback(gpu_lib, fused):
+    """Every sampled entry is made the lowest score, so the sampled window misses the m-th key by far and the second
+    classification has to redo the mask: the result is still the exact top-M (scores), and the fused beta path still
+    equals score-then-select."""
+    import torch
+    from kv_cache_compression_gqa_amd import retention
+    rows, T = 16, 16384
+    cfg = configs.DBTRIM_128K
+    beta = synth.make_retention_beta(cfg, layers=2, n_tokens=T).reshape(rows, T).copy()
+    beta.reshape(-1)[sampled_entries(beta.size)] = np.float32(2.0 ** -24)  # log-retention far below every other
+    bt = torch.from_numpy(beta).cuda()
+    sc = retention.retention_scores(bt, T)
+    m = int(0.1 * beta.size)
+    a = retention.global_topm(sc, m)
+    torch.cuda.synchronize()
+    _check_topm(sc, a, m)
+    if fused:
+        b = retention.global_topm(None, m, beta=bt, t=T)
+        torch.cuda.synchronize()
+        assert torch.equal(a.keep, b.keep) and torch.equal(a.row_counts, b.row_counts)
 
 
 @pytest.mark.parametrize("rows,row_len", [(300, 48), (70, 2064)])

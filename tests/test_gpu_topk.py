@@ -70,3 +70,31 @@ def test_topk_nan_and_infinite_scores_give_indices_in_range(gpu_lib):
         for k in (1, n // 2, n - 1, n):
             got = selection.topk(torch.from_numpy(bad).cuda(), k).cpu().numpy()
             assert got.size == k and np.all(np.diff(got) > 0) and got.min() >= 0 and got.max() < n, (n, k)
+
+
+def test_topk_misleading_sample_takes_the_fallback(gpu_lib):
+    """The entries the engine samples (its documented rule, see test_gpu_retention.sampled_entries) hold the highest
+    scores, so the sampled window lies far above the k-th key; the fallback classification still gives the exact
+    top-k, here with a ragged length."""
+    from tests.test_gpu_retention import sampled_entries
+    rng = np.random.default_rng(5)
+    n = (1 << 20) + 3
+    s32 = rng.standard_normal(n).astype(np.float32)
+    s32[sampled_entries(n)] = np.float32(1e6)
+    for k in (n // 10, n // 2):
+        got = selection.topk(torch.from_numpy(s32).cuda(), k).cpu().numpy()
+        want = np.sort(osel.topk(s32.astype(np.float64), k))
+        assert np.array_equal(got, want), k
+
+
+def test_topk_zeros_and_denormals_rank_by_value(gpu_lib):
+    """+0 and -0 tie (ranked by index); the smallest positive and negative subnormals rank on either side of them."""
+    tiny = np.float32(1.4e-45)
+    base = np.array([0.0, -0.0, tiny, -tiny, 2 * tiny, -2 * tiny, 1e-38, -1e-38, 1.0, -1.0], np.float32)
+    s32 = np.tile(base, 3000)
+    np.random.default_rng(3).shuffle(s32)
+    n = s32.size
+    for k in (1, 3000, 6000, 9000, 12000, 15000, n - 1):
+        got = selection.topk(torch.from_numpy(s32).cuda(), k).cpu().numpy()
+        want = np.sort(osel.topk(s32.astype(np.float64), k))
+        assert np.array_equal(got, want), k
