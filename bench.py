@@ -445,7 +445,7 @@ def main():
     rec["read_floor_bytes"] = probe["wave_bytes"]
     if not args.no_cpu_baseline and not (args.weighted or args.summaries or args.event_schedule):
         print("timing the CPU oracle sample", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = _with_host(cpu_baseline(cfg))
+        rec["cpu_baseline"] = _one_thread_baseline(cpu_baseline, cfg)
     print(json.dumps(rec), flush=True)
 
 
@@ -475,6 +475,7 @@ def bench_batched(args):
     for _ in range(warm):
         sess.step()
     torch.cuda.synchronize()
+    _calibration_copy(args.copy_mib)
     plan = []
 
     def issue(events=None):
@@ -524,12 +525,13 @@ def bench_batched(args):
                    "units": sess.U, "launch": "eager" if graph is None else "hip graph"},
         "hbm_roofline_frac_step": sum(b for b, _ in timed) / wall / (HBM_PEAK_GBS * 1e9),
         "roofline": {"bound": "hbm", "achieved": avg_bytes / avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": avg_bytes / avg_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "frac": avg_bytes / avg_s / 1e9 / HBM_PEAK_GBS,
+                     "traffic": traffic_from_profile("decode_batched_32l_b16"),
                      "kernel": "kvc_decode_attn (decode_partial + decode_combine)", "avg_launch_us": avg_s * 1e6,
                      "algorithmic_bytes_per_launch": avg_bytes},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = _with_host(cpu_baseline_batched(cfg))
+        rec["cpu_baseline"] = _one_thread_baseline(cpu_baseline_batched, cfg)
     print(json.dumps(rec), flush=True)
 
 
@@ -560,7 +562,7 @@ def cpu_baseline_batched(cfg, min_seconds=10.0, n_units=32):
             o.route(*cfg.budgets(o.n_windows))
         rounds += 1
     el = time.perf_counter() - t0
-    return {"value": tokens / el, "unit": "KV tokens/s", "cores": _oracle_threads(), "kind": "oracle",
+    return {"value": tokens / el, "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{len(units)} of {cfg.n_units} units (spread over layers, sequences and heads), {rounds} routed "
                       f"steps each with routing every step after an untimed full-cache step; fp64 numpy oracle; "
                       f"{el:.1f} s"}
@@ -622,7 +624,7 @@ def bench_criticalkv(args):
                      "avg_launch_us": avg_s * 1e6, "algorithmic_flops_per_launch": flops_n + flops_a},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = _with_host(cpu_baseline_criticalkv(cfg, inp))
+        rec["cpu_baseline"] = _one_thread_baseline(cpu_baseline_criticalkv, cfg, inp)
     print(json.dumps(rec), flush=True)
 
 
@@ -631,7 +633,6 @@ def cpu_baseline_criticalkv(cfg, inp):
     the two-stage selection), one head at a time until at least 10 s of CPU work or all heads."""
     from oracle import criticalkv as ock
     from oracle import fp as ofp
-    threads = _oracle_threads()
     G, D = cfg.group, cfg.head_dim
     heads, el = 0, 0.0
     while heads < cfg.hkv and el < 10.0:
@@ -645,7 +646,7 @@ def cpu_baseline_criticalkv(cfg, inp):
         ock.select(A_g, S2_g, cfg.budget, cfg.alpha)
         el += time.perf_counter() - t0
         heads += 1
-    return {"value": heads * cfg.n_keys / el, "unit": "KV entries/s", "cores": threads, "kind": "oracle",
+    return {"value": heads * cfg.n_keys / el, "unit": "KV entries/s", "cores": 1, "kind": "oracle",
             "sample": f"{heads} of {cfg.hkv} KV heads ({G} query heads each, all {cfg.n_keys} keys, d_model "
                       f"{cfg.d_model}): fp64 numpy oracle scores + two-stage selection; {el:.1f} s"}
 
@@ -698,6 +699,7 @@ def bench_dbtrim(args):
     score()
     topm()
     select()
+    _calibration_copy(args.copy_mib)
     res = {}
     for name, fn in (("score", score), ("topm", topm), ("select", select), ("compact", compact)):
         res[name] = _timed_calls(fn, K, 1)
@@ -723,12 +725,13 @@ def bench_dbtrim(args):
                    "ms_score": float(np.mean(res["score"][1])), "ms_topm_from_scores": float(np.mean(res["topm"][1])),
                    "ms_compact": comp_s * 1e3},
         "roofline": {"bound": "hbm", "achieved": comp_bytes / comp_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": comp_bytes / comp_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "frac": comp_bytes / comp_s / 1e9 / HBM_PEAK_GBS,
+                     "traffic": traffic_from_profile("dbtrim_global_128k", ("retention.hip", "kvc_internal.h")),
                      "kernel": "kvc_compact_pages (compact_gather dominates)", "avg_launch_us": comp_s * 1e6,
                      "algorithmic_bytes_per_launch": comp_bytes},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = _with_host(cpu_baseline_dbtrim(cfg))
+        rec["cpu_baseline"] = _one_thread_baseline(cpu_baseline_dbtrim, cfg)
     print(json.dumps(rec), flush=True)
 
 
@@ -790,7 +793,7 @@ def bench_paged_decode(args):
                      "avg_launch_us": launch_s * 1e6, "algorithmic_bytes_per_launch": nbytes},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = _with_host(cpu_baseline_paged(cfg, G))
+        rec["cpu_baseline"] = _one_thread_baseline(cpu_baseline_paged, cfg, G)
     print(json.dumps(rec), flush=True)
 
 
@@ -800,7 +803,6 @@ def cpu_baseline_paged(cfg, G, min_seconds=10.0):
     from kv_cache_compression_gqa_amd import synth
     from oracle.fp import storage_to_f64
     from oracle.paged import paged_gqa_decode
-    threads = _oracle_threads()
     n = cfg.keep // (cfg.layers * cfg.hkv)
     lists = synth.make_large_paged_lists([n] * 256, G, cfg.page, seed=91)
     done, el = 0, 0.0
@@ -814,7 +816,7 @@ def cpu_baseline_paged(cfg, G, min_seconds=10.0):
         paged_gqa_decode(storage_to_f64(lists.q[r], "bf16"), K, V, pos, n, 1)
         done += 1
         el = time.perf_counter() - t0
-    return {"value": done * n / el, "unit": "KV tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": done * n / el, "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{done} rows of {n} kept tokens (the mean row of the workload), G = {G}: fp64 numpy oracle "
                       f"(page gather + decode attention); {el:.1f} s"}
 
@@ -903,7 +905,7 @@ def bench_diagnostics(args):
                      "avg_launch_us": call_s * 1e6, "algorithmic_bytes_per_launch": nbytes},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = _with_host(cpu_baseline_diagnostics(U, NW, G))
+        rec["cpu_baseline"] = _one_thread_baseline(cpu_baseline_diagnostics, U, NW, G)
     print(json.dumps(rec), flush=True)
 
 
@@ -925,7 +927,7 @@ def cpu_baseline_diagnostics(U, NW, G, min_seconds=10.0):
             diagnostics.perturbation_l1(of[u], oc[u])
         calls += 1
         el = time.perf_counter() - t0
-    return {"value": calls * U * NW / el, "unit": "windows/s", "cores": _oracle_threads(), "kind": "oracle",
+    return {"value": calls * U * NW / el, "unit": "windows/s", "cores": 1, "kind": "oracle",
             "sample": f"{calls} calls over {U} units x {NW} windows (seeded tiers, masses, outputs): fp64 numpy "
                       f"oracle; {el:.1f} s"}
 
@@ -935,7 +937,6 @@ def cpu_baseline_dbtrim(cfg, layers=16):
     and the row gather of the kept K/V rows."""
     from kv_cache_compression_gqa_amd import synth
     from oracle import dbtrim
-    threads = _oracle_threads()
     beta = synth.make_retention_beta(cfg, layers=layers)
     pt = synth.make_page_table(cfg, layers=layers)
     m = int(np.floor(cfg.keep_frac * beta.size))
@@ -948,7 +949,7 @@ def cpu_baseline_dbtrim(cfg, layers=16):
     rows_v = synth.pool_row_bits(live, cfg.head_dim, cfg.seed * 7 + 2, cfg.dtype)
     el = time.perf_counter() - t0
     assert rows_k.shape[0] == rows_v.shape[0] == m
-    return {"value": beta.size / el, "unit": "KV entries/s", "cores": threads, "kind": "oracle",
+    return {"value": beta.size / el, "unit": "KV entries/s", "cores": 1, "kind": "oracle",
             "sample": f"{layers} of {cfg.layers} layers ({beta.size} entries, M = 10%): fp64 numpy oracle scores, "
                       f"top-M, compaction plan and K/V row gather; {el:.1f} s"}
 
@@ -997,7 +998,7 @@ def bench_topk(args):
                      "algorithmic_bytes_per_launch": alg},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = _with_host(cpu_baseline_topk(cfg))
+        rec["cpu_baseline"] = _one_thread_baseline(cpu_baseline_topk, cfg)
     print(json.dumps(rec), flush=True)
 
 
@@ -1006,15 +1007,23 @@ def cpu_baseline_topk(cfg, layers=32):
     layers, k = 10%."""
     from kv_cache_compression_gqa_amd import synth
     from oracle import dbtrim, select
-    threads = _oracle_threads()
     s = dbtrim.log_retention(synth.make_retention_beta(cfg, layers=layers), cfg.t).reshape(-1)
     k = int(np.floor(cfg.keep_frac * s.size))
     t0 = time.perf_counter()
     sel = np.sort(select.topk(s, k))
     el = time.perf_counter() - t0
     assert sel.size == k
-    return {"value": s.size / el, "unit": "scores/s", "cores": threads, "kind": "oracle",
+    return {"value": s.size / el, "unit": "scores/s", "cores": 1, "kind": "oracle",
             "sample": f"{layers} of {cfg.layers} layers ({s.size} scores, k = 10%): fp64 numpy lexsort; {el:.1f} s"}
+
+
+def _one_thread_baseline(fn, *args):
+    """Runs a CPU baseline with numpy's BLAS/OpenMP pools held to one thread (the oracle's loops are sequential
+    Python; its library calls then use one core too), so that its ``cores`` = 1 is the parallelism really used."""
+    with _one_thread():
+        rec = fn(*args)
+    rec["cores"] = 1
+    return _with_host(rec)
 
 
 def _with_host(rec):
@@ -1029,14 +1038,6 @@ def _with_host(rec):
         pass
     rec["cpu_model"] = model
     return rec
-
-
-def _oracle_threads():
-    try:
-        from threadpoolctl import threadpool_info
-        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # noqa: BLE001
-        return len(os.sched_getaffinity(0))
 
 
 if __name__ == "__main__":
