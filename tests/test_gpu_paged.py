@@ -4,7 +4,9 @@ Tolerance (fp32 accumulation on the GPU against the fp64 oracle), per (row, head
 Covers ragged lengths (0, 1, one short of a page, exact pages, one past, several slices), page sizes 16 and 32,
 G = 1, 2, 4, 8, fp16 and bf16, page ids scattered over a pool with unlisted pages, list entries past a row's page
 count that must never be read, bad page ids and lengths over the host bound (status bit; the other rows stay
-exact), determinism, and the full DBTrimKV shape on the GPU's own compaction output (sampled rows).
+exact), determinism, the full DBTrimKV shape on synthetic page lists with edge rows (sampled rows), and the full
+shape on the GPU's own compaction output: score, global top-M and kvc_compact_pages on the device, then the
+decode over the fresh pages they leave (sampled rows against the oracle over the kept source rows).
 """
 import sys
 
@@ -130,3 +132,55 @@ def test_paged_decode_full_retention_shape(gpu_lib):
             err = np.abs(out[r, h] - ref[h]).max()
             lim = RTOL * np.abs(ref[h]).max()
             assert err <= lim, f"row {r} (length {n}) head {h}: max err {err} > {lim}"
+
+
+def test_paged_decode_on_compaction_output(gpu_lib):
+    """The whole DBTrimKV path at full size on the device (32 x 8 rows of 131072 positions, M = 10%): log-retention
+    scores, the global top-M, kvc_compact_pages into fresh 16-token pages, then the paged decode over those pages.
+    Sampled rows are checked against the oracle attending over the row's kept positions, ascending, with K and V
+    taken from the source pool rows the page table maps them to."""
+    from kv_cache_compression_gqa_amd import configs, retention
+    cfg = configs.DBTRIM_128K
+    L, H, T, page, D, G = cfg.layers, cfg.hkv, cfg.n_tokens, cfg.page, cfg.head_dim, 4
+    rows = L * H
+    log(f"case: paged decode on the compaction output, {rows} rows x {T}, M={cfg.keep}")
+    beta = torch.from_numpy(synth.make_retention_beta(cfg).reshape(rows, T)).cuda()
+    pt_np = synth.make_page_table(cfg).reshape(rows, T // page).astype(np.int32)
+    pt = torch.from_numpy(pt_np).cuda()
+    seeds = (cfg.seed * 7 + 1, cfg.seed * 7 + 2)
+    n_src = rows * (T // page)
+    kp_src, vp_src = (synth.device_pool(n_src, page, D, sd, cfg.dtype) for sd in seeds)
+    tm = retention.global_topm(retention.retention_scores(beta, cfg.t), cfg.keep)
+    comp = retention.compact_pages(tm.keep, pt, kp_src, vp_src, cfg.keep // page + rows + 1, abi.KVC_BF16)
+    torch.cuda.synchronize()
+    assert int(tm.status.item()) == 0 and int(comp.status.item()) == 0
+    keep = tm.keep.cpu().numpy().astype(bool)
+    del beta, kp_src, vp_src, tm
+    torch.cuda.empty_cache()
+    lengths = comp.lengths
+    n_pages = comp.n_pages.to(torch.int64)
+    max_pages = int(n_pages.max().item())
+    col = torch.arange(max_pages, device="cuda", dtype=torch.int64)
+    pl = torch.where(col[None, :] < n_pages[:, None], comp.page_offset.to(torch.int64)[:, None] + col[None, :],
+                     torch.full_like(col[None, :], -7)).to(torch.int32).contiguous()
+    q_bits = synth.to_storage_bits(synth.unit_rng(cfg.seed, 1 << 25).standard_normal((rows, G, D)), "bf16")
+    dec = PagedDecoder(rows, G, page, max_pages, abi.KVC_BF16)
+    out = dec(_dev(q_bits, "bf16"), comp.k.view(-1, page, D), comp.v.view(-1, page, D), pl, lengths)
+    torch.cuda.synchronize()
+    assert int(dec.status.item()) == 0
+    out = out.cpu().numpy()
+    np.testing.assert_array_equal(lengths.cpu().numpy(), keep.sum(axis=1))
+    assert np.isfinite(out).all()
+    for r in [0, 1, 37, 128, 200, rows - 1]:
+        pos = np.nonzero(keep[r])[0]
+        n = pos.size
+        src = pt_np[r][pos // page].astype(np.int64) * page + pos % page
+        K = storage_to_f64(synth.pool_row_bits(src, D, seeds[0], cfg.dtype), "bf16")
+        V = storage_to_f64(synth.pool_row_bits(src, D, seeds[1], cfg.dtype), "bf16")
+        ref = paged_gqa_decode(storage_to_f64(q_bits[r], "bf16"), K.reshape(n, 1, D), V.reshape(n, 1, D),
+                               np.arange(n), n, 1)
+        for h in range(G):
+            err = np.abs(out[r, h] - ref[h]).max()
+            lim = RTOL * np.abs(ref[h]).max()
+            assert err <= lim, f"row {r} (length {n}) head {h}: max err {err} > {lim}"
+    log("paged decode on the compaction output: sampled rows match")
