@@ -55,6 +55,8 @@ def parse():
                     help="32K layer: evicted windows leave span summaries attended with a ln 32 size correction")
     ap.add_argument("--weighted", action="store_true",
                     help="32K layer: weight the window score by CriticalKV's |V W_O|_1 (norms from kvc_score)")
+    ap.add_argument("--serial-routing", action="store_true",
+                    help="32K layer: run every routing event on the decode stream (no overlap with other replicas)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB (counter calibration)")
     ap.add_argument("--workload", default="llama3_8b_layer_32k",
@@ -338,12 +340,20 @@ def main():
     plan = []  # (bytes, positions) per timed step, from the host-side counts at the time the step is issued
     events_timed = [0]
 
+    # a replica's routing event runs on a second stream (default priority), after its decode and before its next
+    # step, so that the other replicas' decode steps overlap it (independent units, as the layers of a model are)
+    route_stream = None if args.serial_routing else torch.cuda.Stream()
+
     def issue(i, events=None):
         s = sessions[i % R]
         plan.append(step_bytes_and_tokens(s))
         if E > 0 and (s.t + 1) % E == 0:
             events_timed[0] += 1
-        s.step(events=events)
+        s.step(events=events, route_stream=route_stream)
+
+    def join_routes():
+        for s in sessions:
+            s.wait_route()
 
     # timed region: K steps, captured in one HIP graph and replayed once (or launched eagerly with --eager)
     graph = None
@@ -352,6 +362,7 @@ def main():
         with torch.cuda.graph(graph):
             for i in range(K):
                 issue(i)
+            join_routes()
         torch.cuda.synchronize()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -360,6 +371,7 @@ def main():
     else:
         for i in range(K):
             issue(i)
+        join_routes()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     timed_plan = list(plan)
@@ -418,6 +430,7 @@ def main():
         "config": {"workload": cfg.name, "batch": 1, "q_heads": cfg.hq, "kv_heads": cfg.hkv, "head_dim": 128,
                    "context": cfg.context, "window": cfg.window, "tiers": "20% full / 30% int2 / 50% evicted",
                    "route_every": cfg.route_every, "phase": "routed steady state", "replicas": R,
+                   "routing_stream": "serial" if args.serial_routing else "second stream, overlapping other replicas",
                    "routing_events_timed": events_timed[0], "replica_step_offsets": offsets,
                    "window_score": "attention mass x |V W_O|_1 (CriticalKV norms)" if args.weighted else
                    "attention mass",

@@ -105,6 +105,7 @@ class DecodeSession:
                        torch.empty((U, self.FS_small, D, W), dtype=torch.int16, device=dev))
         self._prefill_pool = None   # the prefill pool between the first event and its release
         self.repacked = False
+        self._route_done = None     # event of a routing event issued on another stream, not yet waited for
         LS = self.LS
         self.k_codes = torch.zeros((U, LS, W, D // 4), dtype=torch.uint8, device=dev)
         self.v_codes = torch.zeros((U, LS, 16, 4, 8), dtype=torch.int16, device=dev)
@@ -228,12 +229,15 @@ class DecodeSession:
             self.h_tail = saved
 
     def step(self, probs=None, mass=None, append=True, route=True, stream=None, events=None, token_weight=None,
-             static_scratch=False):
+             static_scratch=False, route_stream=None):
         """Decode step t+1 using the pre-generated inputs of that step; routes when due. ``events`` = (before,
         after) torch events recorded on the stream around the decode launch. ``token_weight`` [U][G][>= NW*W]
         float32 weights every window key's probability per query head in the window score (e.g. the projected-value
         norms of kvc_score(CRITICALKV)); None scores by the plain attention mass. ``static_scratch``: run the step
-        through kvc_decode_attn_static (the library's static scratch array; no workspace is allocated)."""
+        through kvc_decode_attn_static (the library's static scratch array; no workspace is allocated).
+        ``route_stream``: a due routing event runs there, after this step's decode (event wait), so that other work
+        on the step's stream can overlap it; this session's next step waits for it (or call wait_route())."""
+        self.wait_route(stream)
         ti = self.t
         R = self.cfg.route_every
         accumulate = self.score_schedule == "every" or (R > 0 and (ti + 1) % R == 0)
@@ -257,8 +261,22 @@ class DecodeSession:
             self.h_tail += 1
         self.t += 1
         if route and self.cfg.route_every > 0 and self.t % self.cfg.route_every == 0:
-            self.route(stream=stream)
+            if route_stream is None:
+                self.route(stream=stream)
+            else:
+                decoded = torch.cuda.Event()
+                decoded.record(stream)
+                route_stream.wait_event(decoded)
+                self.route(stream=route_stream)
+                self._route_done = torch.cuda.Event()
+                self._route_done.record(route_stream)
         return self.out
+
+    def wait_route(self, stream=None):
+        """Makes ``stream`` (default: the current stream) wait for a routing event issued on another stream."""
+        if self._route_done is not None:
+            (stream if stream is not None else torch.cuda.current_stream()).wait_event(self._route_done)
+            self._route_done = None
 
     # -- routing event ----------------------------------------------------------------------------------------
     def route(self, scores=None, stream=None):

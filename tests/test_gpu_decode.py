@@ -340,3 +340,54 @@ def test_one_round_launch_a_few_tasks_over(gpu_lib):
     log(f"case: {cfg.name}, {cfg.n_units} units, probabilities off then on")
     run_decode_parity(cfg, inp=inp, check_units=[0, 21, 63], probs=False, log=log)
     run_decode_parity(cfg, inp=inp, check_units=[0, 63], probs=True, log=log)
+
+
+def test_routing_on_a_second_stream_matches_serial(gpu_lib):
+    """Routing events issued on a second stream (after the step's decode, waited for by the session's next step),
+    with other sessions' steps in between, give bit-identical outputs, scores, tiers, lists and slots to the serial
+    order: eagerly, and captured in one HIP graph with the stream fork and join (replayed once)."""
+    cfg = configs.TINY
+    n_sess, steps = 3, cfg.steps
+
+    def state(s):
+        return [s.out.clone(), s.cum.clone(), s.tier.clone(), s.res_list.clone(), s.full_slot.clone(),
+                s.ledger_slot.clone(), s.k_full.clone(), s.k_codes.clone()]
+
+    def run(mode):
+        sessions = [DecodeSession(synth.make_decode(cfg)) for _ in range(n_sess)]
+        for s in sessions:
+            s.reserve_workspace(steps)
+        rs = None if mode == "serial" else torch.cuda.Stream()
+        outs = []
+
+        def issue():
+            for t in range(steps):
+                for s in sessions:
+                    s.step(route_stream=rs)
+                    if mode != "graph":
+                        outs.append(s.out.clone())
+            for s in sessions:
+                s.wait_route()
+
+        torch.cuda.synchronize()
+        if mode == "graph":
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                issue()
+            torch.cuda.synchronize()
+            g.replay()
+        else:
+            issue()
+        torch.cuda.synchronize()
+        return outs, [state(s) for s in sessions]
+
+    serial_outs, serial_state = run("serial")
+    eager_outs, eager_state = run("eager")
+    assert len(serial_outs) == len(eager_outs) == n_sess * steps
+    for a, b in zip(serial_outs, eager_outs):
+        assert torch.equal(a, b)
+    for mode_state in (eager_state, run("graph")[1]):
+        for sa, sb in zip(serial_state, mode_state):
+            for x, y in zip(sa, sb):
+                assert torch.equal(x, y)
+    log("routing on a second stream: eager and captured runs equal the serial run")
