@@ -73,10 +73,10 @@ def test_topk_nan_and_infinite_scores_give_indices_in_range(gpu_lib):
 
 
 def test_topk_misleading_sample_takes_the_fallback(gpu_lib):
-    """The entries the engine samples (its documented rule, see test_gpu_retention.sampled_entries) hold the highest
+    """The entries the engine samples (its documented rule, tests.engine_sampling.sampled_entries) hold the highest
     scores, so the sampled window lies far above the k-th key; the fallback classification still gives the exact
     top-k, here with a ragged length."""
-    from tests.test_gpu_retention import sampled_entries
+    from tests.engine_sampling import sampled_entries
     rng = np.random.default_rng(5)
     n = (1 << 20) + 3
     s32 = rng.standard_normal(n).astype(np.float32)
