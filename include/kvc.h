@@ -218,7 +218,7 @@ typedef struct kvc_decode_args {
  *   scores         [U][NW] float, or NULL to rank by cache.cum. Must be finite (NaN: KVC_DEV_NAN_SCORE, the
  *                  unit keeps its tiers).
  *   budget_full, budget_int2   [U] int32 device arrays (>= 0).
- *   n_windows_max <= 4096 (KVC_E_UNSUPPORTED above: a unit's routing state sits in one workgroup's LDS).
+ *   n_windows_max <= 4096 (KVC_E_UNSUPPORTED above: one workgroup routes a unit, at most 4 windows per thread).
  *   quant_list, promo_list     [U][NW] int32;  n_quant, n_promo  [U] int32. */
 typedef struct kvc_tier_route_args {
   const kvc_cache* cache;

@@ -280,7 +280,7 @@ int kvc_route(int32_t mode, const void* args, void* workspace, size_t workspace_
     const kvc_tier_route_args* a = static_cast<const kvc_tier_route_args*>(args);
     const int st = check_cache(a->cache);
     if (st != KVC_OK) return st;
-    // one workgroup per unit holds the unit's keys, flags and slot lists in LDS (about 9 bytes per window)
+    // one workgroup per unit, at most 1024 threads holding at most 4 windows each in registers
     if (a->cache->n_windows_max > kvc::kRouteMaxWindows) return KVC_E_UNSUPPORTED;
     const void* ptrs[] = {a->budget_full, a->budget_int2, a->quant_list, a->n_quant, a->promo_list, a->n_promo};
     for (const void* p : ptrs) {
