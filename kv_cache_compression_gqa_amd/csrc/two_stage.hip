@@ -4,17 +4,20 @@
 //
 // A row is split into 4096-entry chunks handled by separate workgroups (rows x chunks in flight), so the work is
 // spread over the GPU instead of one compute unit per row. Keys are the order-preserving 32-bit images of the
-// scores, inverted (a smaller key is a larger score; +0 == -0). Per stage:
-//   * a histogram of the top 11 key bits (2048 bins), per chunk (stage 1) or per row (stage 2);
-//   * classify (rows x chunks): every workgroup picks, from the row's histogram, the bin b holding the budget's
-//     last entry and how many entries of b it needs; entries in bins below b are selected, entries of bin b become
-//     candidates (appended to the row's candidate list with their index);
-//   * resolve (one workgroup per row): the candidates are ranked by (key, index), which is unique, by a radix
-//     select on the 21 low key bits and the 16 index bits; the first `need` are selected. No tie scan is needed.
-// Stage 1's classify also builds stage 2's histogram over the entries it does not select outright (its
-// candidates included); stage 1's resolve takes the candidates it selects back out of it. The last kernel resolves
-// stage 2; the classify and resolve kernels count every chunk's selections, so the last kernel, (rows x chunks)
-// workgroups again, writes every row's selected indices in ascending order.
+// scores, inverted (a smaller key is a larger score; +0 == -0). Four launches:
+//   * ts_hist1: a histogram of the top 11 bits of stage 1's keys (2048 bins) per chunk;
+//   * ts_classify1: every workgroup sums its row's chunk histograms and picks the bin b holding the budget1-th
+//     key and how many entries of b it needs; entries below b are selected, entries of b become candidates
+//     (appended to the row's list with their index and their stage-2 bin); stage 2's row histogram is gathered
+//     over every entry not selected outright;
+//   * ts_stage2: every (row, chunk) workgroup resolves the row's stage-1 candidates itself (the same result in
+//     each: the candidates are ranked by (key, index), which is unique, by a radix select on the 21 low key bits
+//     and the 16 index bits), takes the selected ones out of stage 2's histogram, picks stage 2's bin, and
+//     classifies its chunk for stage 2 as above; it stores its chunk's count of entries selected so far;
+//   * ts_finish: every (row, chunk) workgroup resolves the row's stage-2 candidates itself, counts the selected
+//     ones per chunk, and writes its chunk's selected indices at the row's running offset, ascending.
+// Resolving in every workgroup of a row replaces a one-workgroup-per-row launch and the per-chunk atomics its
+// results needed; the workgroups of a row run side by side.
 #include <algorithm>
 
 #include "kvc_internal.h"
@@ -31,15 +34,16 @@ constexpr int kMaxN = 65536;
 constexpr int kMaxChunks = kMaxN / kC;  // 16
 
 struct TsWs {
-  uint32_t* hist1;     // [rows][chunks][kBins] stage-1 histogram per chunk
-  uint32_t* hist2;     // [rows][kBins] stage-2 histogram per row
-  int32_t* ncand;      // [2][rows] candidates appended per stage
-  int32_t* pick;       // [2][rows][2] bin (-1: none), entries of the bin still to take
-  uint32_t* cand_key;  // [rows][n] candidate keys (the stage's)
-  int32_t* cand_idx;   // [rows][n] candidate indices
-  uint8_t* cstate;     // [rows][n] resolve state of the candidates kept in global memory
-  uint8_t* sel;        // [rows][n16] 1 = selected (either stage)
-  int32_t* ccnt;       // [rows][chunks] entries of each chunk selected so far
+  uint32_t* hist1;      // [rows][chunks][kBins] stage-1 histogram per chunk
+  uint32_t* hist2;      // [rows][kBins] stage-2 histogram over the entries stage 1 does not select outright
+  int32_t* ncand;       // [2][rows] candidates appended per stage
+  int32_t* pick;        // [2][rows][2] bin (-1: none), entries of the bin still to take
+  uint32_t* cand_key;   // [2][rows][n] candidate keys, per stage
+  int32_t* cand_idx;    // [2][rows][n] candidate indices, per stage
+  uint16_t* cand_bin2;  // [rows][n] stage-2 bin of each stage-1 candidate
+  uint8_t* cstate;      // [rows * chunks][n] resolve state of candidates beyond LDS, per workgroup
+  uint8_t* sel;         // [rows][n16] 1 = selected (either stage)
+  int32_t* ccnt;        // [rows][chunks] entries of each chunk selected by stage 1 or outright by stage 2
 };
 
 // inverted order-preserving key: smaller key = larger score; -0 folded onto +0 (NaN: undefined order)
@@ -106,7 +110,6 @@ __global__ __launch_bounds__(kT) void ts_hist1(const float* __restrict__ a, int 
   // this row's stage-2 histogram and candidate counters start at zero (they are filled by later kernels)
   for (int i = c * kT + threadIdx.x; i < kBins; i += chunks * kT) ws.hist2[size_t(row) * kBins + i] = 0u;
   if (c == 0 && threadIdx.x < 2) ws.ncand[threadIdx.x * int(gridDim.x / chunks) + row] = 0;
-  if (threadIdx.x == 0) ws.ccnt[blockIdx.x] = 0;
   const float* ar = a + size_t(row) * n;
   float x[kPer];
 #pragma unroll
@@ -125,47 +128,43 @@ __global__ __launch_bounds__(kT) void ts_hist1(const float* __restrict__ a, int 
   for (int b = threadIdx.x; b < kBins; b += kT) out[b] = h[0][b] + h[1][b] + h[2][b] + h[3][b];
 }
 
-// ---- classify: pick the row's bin, select the entries below it, collect the bin's entries as candidates --------
-// STAGE 1: keys from a, stage-1 histograms summed over the row's chunks; stage 2's histogram gathered over every
-// entry not selected outright. STAGE 2: keys from s2 among the entries stage 1 left, histogram from hist2.
-template <int STAGE>
-__global__ __launch_bounds__(kT) void ts_classify(const float* __restrict__ a, const float* __restrict__ s2, int n,
-                                                  int n16, int chunks, int budget_stage, TsWs ws) {
-  __shared__ uint32_t h2[STAGE == 1 ? kT / kWave : 1][kBins];
+// This chunk's candidates (bit k of is_cand: entry k*kT + t of thread t) appended to the row's list of a stage:
+// one slot range per workgroup from the row's counter, then in thread order. Contains barriers.
+__device__ __forceinline__ int append_candidates(uint32_t is_cand, int* ncand_row, int* wsum, int* cbase) {
+  int total;
+  const int pos = block_excl_scan<int>(__popc(is_cand), wsum, &total);
+  if (threadIdx.x == 0) *cbase = total > 0 ? atomicAdd(ncand_row, total) : 0;
+  __syncthreads();
+  return pos + *cbase;
+}
+
+// ---- stage 1: pick the row's bin, select the entries below it, collect the bin's entries as candidates ---------
+// Stage 2's histogram is gathered over every entry not selected outright (the candidates included).
+__global__ __launch_bounds__(kT) void ts_classify1(const float* __restrict__ a, const float* __restrict__ s2, int n,
+                                                   int n16, int chunks, int budget1, TsWs ws) {
+  __shared__ uint32_t h2[kT / kWave][kBins];
   __shared__ int wsum[kT / kWave];
   __shared__ int pk[2];
   __shared__ int cbase;
   const int row = blockIdx.x / chunks, c = blockIdx.x - row * chunks;
-  const int rows = int(gridDim.x) / chunks;
   const int wave = threadIdx.x >> 6;
-  const float* src = (STAGE == 1 ? a : s2) + size_t(row) * n;
   uint8_t* sel = ws.sel + size_t(row) * n16;
-  // loads first: this chunk's keys (and stage 2's second scores, or the stage-1 selection)
+  // loads first: this chunk's keys and second scores, and every chunk histogram of the row
   float x[kPer], y[kPer];
-  uint8_t was[kPer];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     const int e = min(c * kC + k * kT + int(threadIdx.x), n - 1);
-    x[k] = src[e];
-    if (STAGE == 1) y[k] = s2[size_t(row) * n + e];
-    else was[k] = sel[e];
+    x[k] = a[size_t(row) * n + e];
+    y[k] = s2[size_t(row) * n + e];
   }
   // the row's histogram: thread t sums bins 8t .. 8t+7
   uint32_t cnt[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-  if (STAGE == 1) {
-    for (int i = threadIdx.x; i < (kT / kWave) * kBins; i += kT) (&h2[0][0])[i] = 0u;
-  }
-  if (STAGE == 2) {
-    const uint4* hp = reinterpret_cast<const uint4*>(ws.hist2 + size_t(row) * kBins + 8 * threadIdx.x);
-    const uint4 p0 = hp[0], p1 = hp[1];
-    cnt[0] = p0.x; cnt[1] = p0.y; cnt[2] = p0.z; cnt[3] = p0.w;
-    cnt[4] = p1.x; cnt[5] = p1.y; cnt[6] = p1.z; cnt[7] = p1.w;
-  } else {
-    uint32_t* hsrc = ws.hist1;
+  for (int i = threadIdx.x; i < (kT / kWave) * kBins; i += kT) (&h2[0][0])[i] = 0u;
+  {
     uint4 p[kMaxChunks][2];  // every chunk's bins issued at once (clamped to the last chunk, masked below)
 #pragma unroll
     for (int ch = 0; ch < kMaxChunks; ++ch) {
-      const uint4* hp = reinterpret_cast<const uint4*>(hsrc + (size_t(row) * chunks + min(ch, chunks - 1)) * kBins +
+      const uint4* hp = reinterpret_cast<const uint4*>(ws.hist1 + (size_t(row) * chunks + min(ch, chunks - 1)) * kBins +
                                                        8 * threadIdx.x);
       p[ch][0] = hp[0];
       p[ch][1] = hp[1];
@@ -178,57 +177,43 @@ __global__ __launch_bounds__(kT) void ts_classify(const float* __restrict__ a, c
       }
     }
   }
-  pick_bin(cnt, budget_stage, pk, wsum);
+  pick_bin(cnt, budget1, pk, wsum);
   const int b = pk[0];
   if (c == 0 && threadIdx.x == 0) {
-    ws.pick[((STAGE - 1) * rows + row) * 2 + 0] = pk[0];
-    ws.pick[((STAGE - 1) * rows + row) * 2 + 1] = pk[1];
+    ws.pick[row * 2 + 0] = pk[0];
+    ws.pick[row * 2 + 1] = pk[1];
   }
-  // classify
   uint32_t key[kPer];
+  uint16_t bin2[kPer];
   uint32_t is_cand = 0u;
-  int nc = 0, nt = 0;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     const int e = c * kC + k * kT + int(threadIdx.x);
     key[k] = dkey(x[k]);
-    const bool elig = e < n && (STAGE == 1 || was[k] == 0);
+    bin2[k] = uint16_t(dkey(y[k]) >> 21);
     const int d = int(key[k] >> 21);
-    const bool take = elig && d < b;
-    const bool cand = elig && d == b;
-    if (e < n && (STAGE == 1 || take)) sel[e] = (STAGE == 1 ? 0 : was[k]) | (take ? 1 : 0);
+    const bool take = e < n && d < b;
+    const bool cand = e < n && d == b;
+    if (e < n) sel[e] = take ? 1 : 0;
     is_cand |= (cand ? 1u : 0u) << k;
-    nc += cand ? 1 : 0;
-    nt += take ? 1 : 0;
-    if (STAGE == 1 && elig && !take) atomicAdd(&h2[wave][dkey(y[k]) >> 21], 1u);
+    if (e < n && !take) atomicAdd(&h2[wave][bin2[k]], 1u);
   }
-  // this chunk's outright selections; candidates: one slot range per workgroup from the row's counter, then in
-  // thread order
-  int taken;
-  (void)block_excl_scan<int>(nt, wsum, &taken);
-  int total;
-  int pos = block_excl_scan<int>(nc, wsum, &total);
-  if (threadIdx.x == 0) {
-    cbase = total > 0 ? atomicAdd(&ws.ncand[(STAGE - 1) * rows + row], total) : 0;
-    if (taken > 0) atomicAdd(&ws.ccnt[blockIdx.x], taken);
-  }
-  __syncthreads();
-  pos += cbase;
+  int pos = append_candidates(is_cand, &ws.ncand[row], wsum, &cbase);
   uint32_t* ck = ws.cand_key + size_t(row) * n;
   int32_t* ci = ws.cand_idx + size_t(row) * n;
+  uint16_t* cb = ws.cand_bin2 + size_t(row) * n;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     if ((is_cand >> k) & 1u) {
       ck[pos] = key[k];
       ci[pos] = c * kC + k * kT + int(threadIdx.x);
+      cb[pos] = bin2[k];
       ++pos;
     }
   }
-  if (STAGE == 1) {
-    for (int bin = threadIdx.x; bin < kBins; bin += kT) {
-      const uint32_t s = h2[0][bin] + h2[1][bin] + h2[2][bin] + h2[3][bin];
-      if (s != 0u) atomicAdd(&ws.hist2[size_t(row) * kBins + bin], s);
-    }
+  for (int bin = threadIdx.x; bin < kBins; bin += kT) {
+    const uint32_t s = h2[0][bin] + h2[1][bin] + h2[2][bin] + h2[3][bin];
+    if (s != 0u) atomicAdd(&ws.hist2[size_t(row) * kBins + bin], s);
   }
 }
 
@@ -236,7 +221,8 @@ __global__ __launch_bounds__(kT) void ts_classify(const float* __restrict__ a, c
 // Candidate state: 2 = still in play, 1 = selected, 0 = out. Radix passes, most significant first, over the 21 low
 // key bits (11 + 10) and the 16 index bits (8 + 8); each pass selects the in-play candidates whose digit is below
 // the digit holding the need-th one. Stops as soon as nothing is left to decide. Works on LDS copies (ck, ci, cs
-// pointing to LDS) or on global memory (generic pointers). Contains barriers.
+// pointing to LDS) or on global memory (generic pointers). Contains barriers and ends with one, so the state is
+// complete for every thread and the histogram is free on return.
 struct ResolveLds {
   uint32_t hist[kBins];
   int wsum[kT / kWave];
@@ -281,85 +267,171 @@ __device__ void resolve(const uint32_t* ck, const IdxT* ci, uint8_t* cs, int tot
   // (key, index) is unique: the index passes leave one candidate in play with need == 1, which returned above
 }
 
-// Resolve the row's candidates of a stage: mark the selected ones in sel; stage 1 also takes them out of stage 2's
-// histogram. STAGE 2 then writes the row's selected indices ascending.
-template <int STAGE, class IdxT>
-__device__ void resolve_mark(const uint32_t* ck, const IdxT* ci, uint8_t* cs, int total, int need, ResolveLds& L,
-                             const float* __restrict__ s2, int n, int row, uint8_t* sel, TsWs& ws) {
-  resolve(ck, ci, cs, total, need, L);
-  // the selected candidates: marked in sel; per-chunk counts and (stage 1) stage-2 histogram decrements gathered in
-  // LDS first, so that global memory sees one atomic per chunk and per bin, not one per candidate
-  const int chunks = (n + kC - 1) / kC;
-  __shared__ int chunk_add[kMaxChunks];
-  for (int i = threadIdx.x; i < kBins; i += kT) L.hist[i] = 0u;
-  if (threadIdx.x < kMaxChunks) chunk_add[threadIdx.x] = 0;
-  __syncthreads();
-  for (int i = threadIdx.x; i < total; i += kT) {
-    if (cs[i] == 1) {
-      const int e = int(ci[i]);
-      sel[e] = 1;
-      atomicAdd(&chunk_add[e / kC], 1);
-      if (STAGE == 1) atomicAdd(&L.hist[dkey(s2[size_t(row) * n + e]) >> 21], 1u);
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x < chunks && chunk_add[threadIdx.x] != 0) {
-    atomicAdd(&ws.ccnt[row * chunks + threadIdx.x], chunk_add[threadIdx.x]);
-  }
-  if (STAGE == 1) {
-    for (int b = threadIdx.x; b < kBins; b += kT) {
-      if (L.hist[b] != 0u) atomicSub(&ws.hist2[size_t(row) * kBins + b], L.hist[b]);
-    }
-  }
-}
+// The row's candidates of one stage, resolved in this workgroup: copied to LDS when they fit, else resolved in
+// place with this workgroup's own state array in global memory.
+struct CandLds {
+  uint32_t k[kCandLds];
+  uint16_t i[kCandLds];  // indices < 65536
+  uint8_t s[kCandLds];
+};
 
-template <int STAGE>
-__global__ __launch_bounds__(kT) void ts_resolve(const float* __restrict__ s2, int n, TsWs ws) {
-  __shared__ uint32_t lk[kCandLds];
-  __shared__ uint16_t li[kCandLds];  // indices < 65536
-  __shared__ uint8_t ls[kCandLds];
-  __shared__ ResolveLds L;
-  const int row = blockIdx.x;
-  const int rows = int(gridDim.x);
-  const int total = min(ws.ncand[(STAGE - 1) * rows + row], n);
-  const int need = ws.pick[((STAGE - 1) * rows + row) * 2 + 1];
-  const uint32_t* gk = ws.cand_key + size_t(row) * n;
-  const int32_t* gi = ws.cand_idx + size_t(row) * n;
-  const int n16 = (n + 15) / 16 * 16;
-  uint8_t* sel = ws.sel + size_t(row) * n16;
-  if (total <= kCandLds) {
-    for (int i = threadIdx.x; i < total; i += kT) {
-      lk[i] = gk[i];
-      li[i] = uint16_t(gi[i]);
+struct RowCands {
+  const uint32_t* gk;  // the stage's list of the row
+  const int32_t* gi;
+  uint8_t* gs;         // this workgroup's state array (used when the list does not fit in LDS)
+  int total;
+  bool in_lds;
+  __device__ bool taken(const CandLds& C, int i) const { return (in_lds ? C.s[i] : gs[i]) == 1; }
+  __device__ int index(const CandLds& C, int i) const { return in_lds ? int(C.i[i]) : gi[i]; }
+};
+
+__device__ RowCands resolve_row(const TsWs& ws, int stage, int row, int rows, int n, int need, CandLds& C,
+                                ResolveLds& L) {
+  RowCands r;
+  const size_t off = (size_t(stage) * rows + row) * n;
+  r.gk = ws.cand_key + off;
+  r.gi = ws.cand_idx + off;
+  r.gs = ws.cstate + size_t(blockIdx.x) * n;
+  r.total = min(ws.ncand[stage * rows + row], n);
+  r.in_lds = r.total <= kCandLds;
+  if (r.in_lds) {
+    for (int i = threadIdx.x; i < r.total; i += kT) {
+      C.k[i] = r.gk[i];
+      C.i[i] = uint16_t(r.gi[i]);
     }
     __syncthreads();
-    resolve_mark<STAGE>(lk, li, ls, total, need, L, s2, n, row, sel, ws);
+    resolve(C.k, C.i, C.s, r.total, need, L);
   } else {
-    resolve_mark<STAGE>(gk, gi, ws.cstate + size_t(row) * n, total, need, L, s2, n, row, sel, ws);
+    resolve(r.gk, r.gi, r.gs, r.total, need, L);
+  }
+  return r;
+}
+
+// ---- stage 2: stage 1's resolution, stage 2's pick, stage-2 classification of this chunk -----------------------
+__global__ __launch_bounds__(kT) void ts_stage2(const float* __restrict__ s2, int n, int n16, int chunks, int budget2,
+                                                TsWs ws) {
+  __shared__ CandLds C;
+  __shared__ ResolveLds L;
+  __shared__ uint32_t mine[kC / 32];  // entries of this chunk that stage 1's resolution selects
+  __shared__ int wsum[kT / kWave];
+  __shared__ int cbase;
+  const int row = blockIdx.x / chunks, c = blockIdx.x - row * chunks;
+  const int rows = int(gridDim.x) / chunks;
+  uint8_t* sel = ws.sel + size_t(row) * n16;
+  // loads first: this chunk's second scores and stage-1 outright selections, the row's stage-2 histogram
+  float x[kPer];
+  uint8_t was[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int e = min(c * kC + k * kT + int(threadIdx.x), n - 1);
+    x[k] = s2[size_t(row) * n + e];
+    was[k] = sel[e];
+  }
+  uint32_t cnt[8];
+  {
+    const uint4* hp = reinterpret_cast<const uint4*>(ws.hist2 + size_t(row) * kBins + 8 * threadIdx.x);
+    const uint4 p0 = hp[0], p1 = hp[1];
+    cnt[0] = p0.x; cnt[1] = p0.y; cnt[2] = p0.z; cnt[3] = p0.w;
+    cnt[4] = p1.x; cnt[5] = p1.y; cnt[6] = p1.z; cnt[7] = p1.w;
+  }
+  if (threadIdx.x < kC / 32) mine[threadIdx.x] = 0u;
+  const RowCands r = resolve_row(ws, 0, row, rows, n, ws.pick[row * 2 + 1], C, L);
+  // the selected stage-1 candidates leave stage 2's histogram; the ones in this chunk are marked
+#pragma unroll
+  for (int k = 0; k < 8; ++k) L.hist[8 * threadIdx.x + k] = cnt[k];
+  __syncthreads();
+  const uint16_t* cb = ws.cand_bin2 + size_t(row) * n;
+  for (int i = threadIdx.x; i < r.total; i += kT) {
+    if (r.taken(C, i)) {
+      const int e = r.index(C, i);
+      atomicSub(&L.hist[cb[i]], 1u);
+      if (e / kC == c) atomicOr(&mine[(e - c * kC) >> 5], 1u << (e & 31));
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 8; ++k) cnt[k] = L.hist[8 * threadIdx.x + k];
+  pick_bin(cnt, budget2, L.pk, wsum);
+  const int b = L.pk[0];
+  if (c == 0 && threadIdx.x == 0) {
+    ws.pick[(rows + row) * 2 + 0] = L.pk[0];
+    ws.pick[(rows + row) * 2 + 1] = L.pk[1];
+  }
+  uint32_t key[kPer];
+  uint32_t is_cand = 0u;
+  int nsel = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int le = k * kT + int(threadIdx.x);
+    const int e = c * kC + le;
+    const bool m1 = (mine[le >> 5] >> (le & 31)) & 1u;
+    const bool prev = was[k] != 0 || m1;
+    key[k] = dkey(x[k]);
+    const int d = int(key[k] >> 21);
+    const bool take = e < n && !prev && d < b;
+    const bool cand = e < n && !prev && d == b;
+    if (e < n && (m1 || take)) sel[e] = 1;
+    nsel += e < n && (prev || take) ? 1 : 0;
+    is_cand |= (cand ? 1u : 0u) << k;
+  }
+  int chunk_sel;
+  (void)block_excl_scan<int>(nsel, wsum, &chunk_sel);
+  if (threadIdx.x == 0) ws.ccnt[blockIdx.x] = chunk_sel;
+  int pos = append_candidates(is_cand, &ws.ncand[rows + row], wsum, &cbase);
+  uint32_t* ck = ws.cand_key + (size_t(rows) + row) * n;
+  int32_t* ci = ws.cand_idx + (size_t(rows) + row) * n;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    if ((is_cand >> k) & 1u) {
+      ck[pos] = key[k];
+      ci[pos] = c * kC + k * kT + int(threadIdx.x);
+      ++pos;
+    }
   }
 }
 
-// The selected indices of every row, ascending: workgroup (row, chunk) starts at the selections of the row's
-// earlier chunks and writes its chunk's (thread t: entries 16t .. 16t+15 of the chunk, in order).
-__global__ __launch_bounds__(kT) void ts_output(int n, int n16, int chunks, int budget, TsWs ws,
+// ---- finish: stage 2's resolution, then this chunk's selected indices at the row's running offset --------------
+// Thread t writes entries 16t .. 16t+15 of the chunk, in order.
+__global__ __launch_bounds__(kT) void ts_finish(int n, int n16, int chunks, int budget, TsWs ws,
                                                 int32_t* __restrict__ idx_out) {
+  __shared__ CandLds C;
+  __shared__ ResolveLds L;
+  __shared__ uint32_t mine[kC / 32];  // entries of this chunk that stage 2's resolution selects
+  __shared__ int chunk_add[kMaxChunks];
   __shared__ int wsum[kT / kWave];
   const int row = blockIdx.x / chunks, c = blockIdx.x - row * chunks;
-  int prev[kMaxChunks];  // the earlier chunks' counts, loaded at once
+  const int rows = int(gridDim.x) / chunks;
+  // loads first: the earlier chunks' counts and this thread's 16 selection bytes
+  int prev[kMaxChunks];
 #pragma unroll
   for (int ch = 0; ch < kMaxChunks; ++ch) prev[ch] = ch < c ? ws.ccnt[row * chunks + ch] : 0;
-  int base = 0;
-#pragma unroll
-  for (int ch = 0; ch < kMaxChunks; ++ch) base += prev[ch];
   const int e0 = c * kC + 16 * int(threadIdx.x);
   uint32_t wv[4] = {0u, 0u, 0u, 0u};
   if (e0 < n16) {
     const uint4 v = *reinterpret_cast<const uint4*>(ws.sel + size_t(row) * n16 + e0);
     wv[0] = v.x; wv[1] = v.y; wv[2] = v.z; wv[3] = v.w;
   }
+  if (threadIdx.x < kC / 32) mine[threadIdx.x] = 0u;
+  if (threadIdx.x < kMaxChunks) chunk_add[threadIdx.x] = 0;
+  const RowCands r = resolve_row(ws, 1, row, rows, n, ws.pick[(rows + row) * 2 + 1], C, L);
+  for (int i = threadIdx.x; i < r.total; i += kT) {
+    if (r.taken(C, i)) {
+      const int e = r.index(C, i);
+      atomicAdd(&chunk_add[e / kC], 1);
+      if (e / kC == c) atomicOr(&mine[(e - c * kC) >> 5], 1u << (e & 31));
+    }
+  }
+  __syncthreads();
+  int base = 0;
+#pragma unroll
+  for (int ch = 0; ch < kMaxChunks; ++ch) base += ch < c ? prev[ch] + chunk_add[ch] : 0;
+  const uint32_t m16 = (mine[(16 * threadIdx.x) >> 5] >> ((16 * threadIdx.x) & 31)) & 0xFFFFu;
   uint32_t bits = 0u;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) bits |= ((e0 + j < n && ((wv[j >> 2] >> (8 * (j & 3))) & 0xFFu) != 0u) ? 1u : 0u) << j;
+  for (int j = 0; j < 16; ++j) {
+    const bool s = ((wv[j >> 2] >> (8 * (j & 3))) & 0xFFu) != 0u || ((m16 >> j) & 1u);
+    bits |= (e0 + j < n && s ? 1u : 0u) << j;
+  }
   int tot;
   int pos = base + block_excl_scan<int>(__popc(bits), wsum, &tot);
   int32_t* out = idx_out + size_t(row) * budget;
@@ -375,7 +447,7 @@ size_t al(size_t x) { return align_up(x, 256); }
 
 struct TsLayout {
   int chunks, n16;
-  size_t hist1, hist2, ncand, pick, cand_key, cand_idx, cstate, sel, ccnt, total;
+  size_t hist1, hist2, ncand, pick, cand_key, cand_idx, cand_bin2, cstate, sel, ccnt, total;
 };
 
 TsLayout ts_layout(const kvc_two_stage_args& a) {
@@ -393,11 +465,13 @@ TsLayout ts_layout(const kvc_two_stage_args& a) {
   L.pick = o;
   o += al(2 * rows * 2 * 4);
   L.cand_key = o;
-  o += al(rows * n * 4);
+  o += al(2 * rows * n * 4);
   L.cand_idx = o;
-  o += al(rows * n * 4);
+  o += al(2 * rows * n * 4);
+  L.cand_bin2 = o;
+  o += al(rows * n * 2);
   L.cstate = o;
-  o += al(rows * n);
+  o += al(rows * L.chunks * n);
   L.sel = o;
   o += al(rows * size_t(L.n16));
   L.ccnt = o;
@@ -421,17 +495,16 @@ hipError_t launch_two_stage(const kvc_two_stage_args& a, int32_t budget1, void* 
   ws.pick = reinterpret_cast<int32_t*>(w + Lo.pick);
   ws.cand_key = reinterpret_cast<uint32_t*>(w + Lo.cand_key);
   ws.cand_idx = reinterpret_cast<int32_t*>(w + Lo.cand_idx);
+  ws.cand_bin2 = reinterpret_cast<uint16_t*>(w + Lo.cand_bin2);
   ws.cstate = reinterpret_cast<uint8_t*>(w + Lo.cstate);
   ws.sel = reinterpret_cast<uint8_t*>(w + Lo.sel);
   ws.ccnt = reinterpret_cast<int32_t*>(w + Lo.ccnt);
   const unsigned grid = unsigned(a.rows) * unsigned(Lo.chunks);
   const int budget2 = a.budget - budget1;
   hipLaunchKernelGGL(ts_hist1, dim3(grid), dim3(kT), 0, s, a.a, a.n, Lo.chunks, ws);
-  hipLaunchKernelGGL(ts_classify<1>, dim3(grid), dim3(kT), 0, s, a.a, a.s2, a.n, Lo.n16, Lo.chunks, budget1, ws);
-  hipLaunchKernelGGL(ts_resolve<1>, dim3(unsigned(a.rows)), dim3(kT), 0, s, a.s2, a.n, ws);
-  hipLaunchKernelGGL(ts_classify<2>, dim3(grid), dim3(kT), 0, s, a.a, a.s2, a.n, Lo.n16, Lo.chunks, budget2, ws);
-  hipLaunchKernelGGL(ts_resolve<2>, dim3(unsigned(a.rows)), dim3(kT), 0, s, a.s2, a.n, ws);
-  hipLaunchKernelGGL(ts_output, dim3(grid), dim3(kT), 0, s, a.n, Lo.n16, Lo.chunks, a.budget, ws, a.idx);
+  hipLaunchKernelGGL(ts_classify1, dim3(grid), dim3(kT), 0, s, a.a, a.s2, a.n, Lo.n16, Lo.chunks, budget1, ws);
+  hipLaunchKernelGGL(ts_stage2, dim3(grid), dim3(kT), 0, s, a.s2, a.n, Lo.n16, Lo.chunks, budget2, ws);
+  hipLaunchKernelGGL(ts_finish, dim3(grid), dim3(kT), 0, s, a.n, Lo.n16, Lo.chunks, a.budget, ws, a.idx);
   return hipGetLastError();
 }
 

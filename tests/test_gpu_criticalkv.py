@@ -93,14 +93,18 @@ def test_two_stage_ties_and_edges(gpu_lib, budget, alpha):
 
 def test_two_stage_constant_rows_and_degenerate_budgets(gpu_lib):
     """Rows whose every entry is equal (all 65536 in one histogram bin: more candidates than the LDS path holds, so
-    they are ranked from global memory; the order is then the index order), a row of one entry, stage budgets of
-    0 and of everything, odd lengths."""
+    they are ranked from global memory; the order is then the index order), stage 1 from LDS with stage 2 from
+    global memory, a row of one entry, stage budgets of 0 and of everything, odd lengths."""
     rng = np.random.default_rng(41)
     a = np.full((2, 65536), 0.25, np.float32)
     s2 = np.full((2, 65536), -1.5, np.float32)
     s2[1, ::7] = 3.0
     for budget, alpha in ((2048, 0.5), (65536, 0.5), (5000, 0.0), (5000, 1.0), (1, 1.0)):
         _check_selection(a, s2, budget, alpha)
+    # stage 1 resolved from LDS, stage 2 (every second score equal) from global memory
+    a = rng.standard_normal((2, 65536)).astype(np.float32)
+    s2 = np.full((2, 65536), -1.5, np.float32)
+    _check_selection(a, s2, 2048, 0.5)
     one = np.array([[0.5]], np.float32)
     _check_selection(one, one, 1, 0.5)
     _check_selection(one, one, 1, 0.0)
