@@ -712,7 +712,7 @@ __global__ __launch_bounds__(WPB * kWave) __attribute__((amdgpu_waves_per_eu(4))
 // maxima of this thread, its windows' exp-sums, tiers and scores — is issued first; then each workgroup merges
 // the partials' (m, l) per head (one pass, fixed order), weights and sums its outputs in a fixed order (bitwise
 // reproducible), and turns its windows' exp-sums into probability mass.
-constexpr int kPre = 8;
+constexpr int kPre = 9;  // partials preloaded per thread: 8 groups cover up to 72 (a one-round launch a task over)
 constexpr int kMlPre = 4;
 
 // the G per-head values of one window (16-byte aligned rows for G = 4, 8; the workspace is 256-byte aligned)
