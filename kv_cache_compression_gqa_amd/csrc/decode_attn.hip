@@ -22,9 +22,10 @@
 //     reference max it is relative to are written for the score. With per-position weights (WEIGHTED: CriticalKV
 //     page, "Algoritmo", the projected-value norm plugged into the window score) the window's exp-sum weights each
 //     key per head; the weights are loaded with the task's other loads.
-//   * P.V on MFMA: A = 16 head_dim x 32 tokens of V (V is stored transposed per window), B = P^T split into a
-//     high and a low part (columns 0..G-1 and G..2G-1) so the product keeps ~16 bits of P. INT2 values enter A as
-//     exact fp16 codes and the per-token scale is folded into B (P*s); the zero term sum(P*z) is a VALU bias.
+//   * P.V on MFMA: A = 16 head_dim x 32 tokens of V (V is stored transposed per window), B = P^T (columns
+//     0..G-1) split into a high and a low part that two MFMAs accumulate into the same columns, so the product
+//     keeps ~16 bits of P with no merge afterwards. INT2 values enter A as exact fp16 codes and the per-token
+//     scale is folded into B (P*s); the zero term sum(P*z) is a VALU bias.
 //   The workgroup's waves merge their (m, l, o) in LDS into one partial per workgroup.
 // decode_combine: merges the partials of a unit in a fixed order (bitwise reproducible), writes o, converts the
 // window exp-sums into probability mass, adds it to the cumulative score, finalises the optional probabilities
@@ -192,7 +193,7 @@ struct Ctx {
 };
 
 // Per-lane result of a wave: heads 4*(lane/16) + r for m, l (the 16 lanes of a group agree); O^T tiles acc[dt]
-// (column lane%16 = head (hi) or head + G (lo), head_dim 16dt + 4*(lane/16) + r); bias[g] = sum P*z of the
+// (column lane%16 = head, for lanes with lane%16 < G; head_dim 16dt + 4*(lane/16) + r); bias[g] = sum P*z of the
 // INT2 values of head_dim group g (column lane%16 < G, partial over this lane's tokens).
 struct WaveOut {
   float m[4], l[4];
@@ -264,7 +265,7 @@ __device__ __forceinline__ void p_to_b(const Ctx& c, const f32x4 (&Pw)[2], float
       }
     }
   }
-  const int hcol = c.col < 2 * G ? (c.col % G) : 0;
+  const int hcol = c.col < G ? c.col : 0;
   const float4 a0 = *reinterpret_cast<const float4*>(plds + hcol * 32 + 8 * c.q);
   const float4 a1 = *reinterpret_cast<const float4*>(plds + hcol * 32 + 8 * c.q + 4);
   x[0] = a0.x;
@@ -361,8 +362,12 @@ __device__ __forceinline__ void dense_task(const DecodeParams& p, const Ctx& c, 
   if (!TAIL) store_window_sums<G>(p, c, id, ws[0], wo.m);
   float x[8];
   p_to_b<G>(c, S[0], plds, x);
-  u32x4 B = split8<M>(x, c.col >= G);
-  if (c.col >= 2 * G) B = zero4u();
+  // P^T as a high and a low part, accumulated into the same columns by two MFMAs (~16 bits of P)
+  u32x4 Bh = split8<M>(x, false), Bl = split8<M>(x, true);
+  if (c.col >= G) {
+    Bh = zero4u();
+    Bl = zero4u();
+  }
   if (TAIL) {  // the new token's values from v_new; values past the valid length zeroed (no inf * 0)
     const int t0 = 8 * c.q;
     const int e_new = tnew - t0;
@@ -383,7 +388,7 @@ __device__ __forceinline__ void dense_task(const DecodeParams& p, const Ctx& c, 
     }
   }
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) wo.acc[dt] = M::mfma(vr[dt], B, zero4());
+  for (int dt = 0; dt < 8; ++dt) wo.acc[dt] = M::mfma(vr[dt], Bl, M::mfma(vr[dt], Bh, zero4()));
 }
 
 // qsum[k][r] = sum over head_dim group k of q[head 4*(lane/16) + r] in fp32 (rows beyond G: 0)
@@ -486,8 +491,7 @@ __device__ __forceinline__ void int2_task(const DecodeParams& p, const Ctx& c, c
     if (ok[i]) store_window_sums<G>(p, c, ids[i], ws[i], wo.m);
   }
   // P.V: A = exact fp16 codes of 16 head_dim x 32 tokens, B = (P * scale)^T hi/lo, bias = sum P * zero
-  const bool live = c.col < 2 * G;
-  const bool low = c.col >= G;
+  const bool live = c.col < G;
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) wo.acc[dt] = zero4();
 #pragma unroll
@@ -508,14 +512,18 @@ __device__ __forceinline__ void int2_task(const DecodeParams& p, const Ctx& c, c
         zsum = fmaf(x[e], half_bits_to_float(mws[e] >> 16), zsum);
       }
       wo.bias[g] += zsum;
-      u32x4 B = split8<MF16>(y, low);
-      if (!live) B = zero4u();
+      u32x4 Bh = split8<MF16>(y, false), Bl = split8<MF16>(y, true);
+      if (!live) {
+        Bh = zero4u();
+        Bl = zero4u();
+      }
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const int dt = 2 * g + h2;
         const uint32_t wv = dt < 2 ? vc[i].x : (dt < 4 ? vc[i].y : (dt < 6 ? vc[i].z : vc[i].w));
         const uint32_t c16 = (wv >> (16 * (dt & 1))) & 0xFFFFu;
-        wo.acc[dt] = MF16::mfma(codes_to_f16(c16), B, wo.acc[dt]);
+        const u32x4 a = codes_to_f16(c16);
+        wo.acc[dt] = MF16::mfma(a, Bl, MF16::mfma(a, Bh, wo.acc[dt]));
       }
     }
   }
@@ -657,7 +665,7 @@ __global__ __launch_bounds__(WPB * kWave) __attribute__((amdgpu_waves_per_eu(4))
     }
   }
 
-  // ---- wave result: O[h][d] = acc(col h) + acc(col h + G) + bias(group of d); merged over the workgroup's waves ----
+  // ---- wave result: O[h][d] = acc(col h) + bias(group of d); merged over the workgroup's waves ---------------------
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     wo.bias[g] = xor_sum(wo.bias[g], 16);
@@ -667,8 +675,7 @@ __global__ __launch_bounds__(WPB * kWave) __attribute__((amdgpu_waves_per_eu(4))
   for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float lo = dpp_f<0x100 + G>(wo.acc[dt][r]);  // column col + G of the same row
-      if (c.col < G) sm_o[wave][c.col][16 * dt + 4 * c.q + r] = wo.acc[dt][r] + lo + wo.bias[dt >> 1];
+      if (c.col < G) sm_o[wave][c.col][16 * dt + 4 * c.q + r] = wo.acc[dt][r] + wo.bias[dt >> 1];
     }
   }
   if (c.col == 0 && 4 * c.q < G) {
