@@ -689,27 +689,31 @@ __global__ __launch_bounds__(WPB * kWave) __attribute__((amdgpu_waves_per_eu(4))
     }
   }
   __syncthreads();
+  // each wave's rescale factor per head, exp(m_w - max_w m_w), computed once
+  __shared__ float sm_sc[WPB][G];
+  if (threadIdx.x < WPB * G) {
+    const int w = threadIdx.x / G, h = threadIdx.x - w * G;
+    float Mx = sm_m[0][h];
+#pragma unroll
+    for (int w2 = 1; w2 < WPB; ++w2) Mx = fmaxf(Mx, sm_m[w2][h]);
+    sm_sc[w][h] = exp_diff(sm_m[w][h], Mx);
+    if (w == 0) {
+      float L = 0.0f;
+#pragma unroll
+      for (int w2 = 0; w2 < WPB; ++w2) L += sm_l[w2][h] * exp_diff(sm_m[w2][h], Mx);
+      const size_t part = size_t(u) * p.P + sl;
+      p.part_ml[(part * G + h) * 2 + 0] = Mx;
+      p.part_ml[(part * G + h) * 2 + 1] = L;
+    }
+  }
+  __syncthreads();
   const size_t part = size_t(u) * p.P + sl;
   for (int i = threadIdx.x; i < G * kD; i += (WPB * kWave)) {
     const int h = i / kD;
-    float Mx = sm_m[0][h];
-#pragma unroll
-    for (int w = 1; w < WPB; ++w) Mx = fmaxf(Mx, sm_m[w][h]);
     float O = 0.0f;
 #pragma unroll
-    for (int w = 0; w < WPB; ++w) O += sm_o[w][h][i % kD] * exp_diff(sm_m[w][h], Mx);
+    for (int w = 0; w < WPB; ++w) O += sm_o[w][h][i % kD] * sm_sc[w][h];
     p.part_o[part * G * kD + i] = O;
-  }
-  if (threadIdx.x < G) {
-    const int h = threadIdx.x;
-    float Mx = sm_m[0][h];
-#pragma unroll
-    for (int w = 1; w < WPB; ++w) Mx = fmaxf(Mx, sm_m[w][h]);
-    float L = 0.0f;
-#pragma unroll
-    for (int w = 0; w < WPB; ++w) L += sm_l[w][h] * exp_diff(sm_m[w][h], Mx);
-    p.part_ml[(part * G + h) * 2 + 0] = Mx;
-    p.part_ml[(part * G + h) * 2 + 1] = L;
   }
 }
 
