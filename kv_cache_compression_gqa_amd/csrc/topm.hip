@@ -361,8 +361,9 @@ __global__ __launch_bounds__(kSampleTB) void eng_sample(TopmInput in, Ws ws, int
 // from beta. kSpec: the first classification, against the window [lo, hi] located in the sample, building the exact
 // histogram on the way. Otherwise the fallback: every workgroup picks the exact bin b1 and returns at once when the
 // window held it, else classifies its chunks again against [b1, b1] (rewriting their mask, candidates and counts).
+// Four waves per SIMD (at most 128 VGPRs), so that the speculative pass's grid is resident in one round.
 template <bool kBits, bool kBeta, bool kSpec, int kPer>
-__global__ __launch_bounds__(kClsTB) void eng_classify(TopmInput in, Ws ws, int64_t nb, int64_t m, int64_t lo_pos,
+__global__ __launch_bounds__(kClsTB) __attribute__((amdgpu_waves_per_eu(4))) void eng_classify(TopmInput in, Ws ws, int64_t nb, int64_t m, int64_t lo_pos,
                                                        int64_t hi_pos, uint8_t* __restrict__ keep,
                                                        uint32_t* __restrict__ keep_bits, int32_t* status) {
   constexpr int W = kClsTB / kWave, kSpan = W * kPer;
