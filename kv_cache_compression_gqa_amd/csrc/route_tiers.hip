@@ -186,7 +186,7 @@ __global__ __launch_bounds__(TB) void route_tiers_kernel(kvc_tier_route_args a, 
     // resident count (the histogram's total), the two ranks, and both thresholds' first digits
     const uint4 c4 = *reinterpret_cast<const uint4*>(&sh.hist[0][0][4 * lane]);
     const int n_res = __builtin_amdgcn_readlane(wave_incl_scan(int(c4.x + c4.y + c4.z + c4.w)), kWave - 1);
-    const int k1 = min(bf, n_res), k2 = min(bf + bq, n_res);
+    const int k1 = min(bf, n_res), k2 = int(min(int64_t(bf) + bq, int64_t(n_res)));  // budgets up to INT_MAX each
     if (lane == 0) {
       sh.k[0] = k1;
       sh.k[1] = k2;

@@ -213,3 +213,25 @@ def test_route_nan_score_on_a_resident_window_is_refused(gpu_lib):
     for u in (1, 2):
         ta = three_tier(scores[u].astype(np.float64), tier[u], 4, 2)
         np.testing.assert_array_equal(got["tier"][u], ta)
+
+
+@pytest.mark.parametrize("NW", [64, 700, 4096], ids=["one-wave", "256-threads", "1024-threads"])
+def test_route_budgets_up_to_int_max(gpu_lib, NW):
+    """Budgets are any int32 >= 0: budget_full + budget_int2 past 2^31 - 1 still ranks every resident window into
+    FULL then INT2 (a wrapped sum would drop the INT2 tier)."""
+    big = 2**31 - 1
+    U = 1100 if NW == 64 else (300 if NW == 700 else 2)
+    rng = np.random.default_rng(NW + 5)
+    n, tier, led, fsl, lsl = random_state(rng, U, NW, NW, NW)
+    tb = Tables(U, NW, NW, NW, n, tier, led, fsl, lsl)
+    bf = rng.integers(0, NW + 1, U)
+    bf[0] = big
+    bq = np.full(U, big)
+    bq[1] = rng.integers(0, NW + 1)
+    scores = random_scores(rng, U, NW, "ties")
+    before = tb.host()
+    log(f"route int-max budgets NW={NW}")
+    tb.route(scores, bf, bq)
+    got = tb.host()
+    exp, lists = expected(before, n, scores, bf, bq, NW, NW)
+    check_event(got, exp, lists, n, f"int-max budgets NW={NW}")
