@@ -251,10 +251,10 @@ __device__ __forceinline__ void store_logits(const DecodeParams& p, const Ctx& c
   }
 }
 
-// P of one window (S layout: lane (token col, head row 4q + r)) -> this lane's B-operand row of P^T:
-// head col % G, tokens 8q .. 8q+7, through a per-wave LDS tile [8 heads][32 tokens].
+// P of one window (S layout: lane (token col, head row 4q + r)) -> this lane's B-operand row of P^T: head hcol
+// (< G), tokens 8q .. 8q+7, through a per-wave LDS tile [8 heads][32 tokens].
 template <int G>
-__device__ __forceinline__ void p_to_b(const Ctx& c, const f32x4 (&Pw)[2], float* plds, float (&x)[8]) {
+__device__ __forceinline__ void p_to_b(const Ctx& c, const f32x4 (&Pw)[2], float* plds, int hcol, float (&x)[8]) {
   if (4 * c.q < G) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -265,7 +265,6 @@ __device__ __forceinline__ void p_to_b(const Ctx& c, const f32x4 (&Pw)[2], float
       }
     }
   }
-  const int hcol = c.col < G ? c.col : 0;
   const float4 a0 = *reinterpret_cast<const float4*>(plds + hcol * 32 + 8 * c.q);
   const float4 a1 = *reinterpret_cast<const float4*>(plds + hcol * 32 + 8 * c.q + 4);
   x[0] = a0.x;
@@ -361,13 +360,10 @@ __device__ __forceinline__ void dense_task(const DecodeParams& p, const Ctx& c, 
   if constexpr (WEIGHTED && !TAIL) weighted_sums(S[0], wn, ws[0]);
   if (!TAIL) store_window_sums<G>(p, c, id, ws[0], wo.m);
   float x[8];
-  p_to_b<G>(c, S[0], plds, x);
-  // P^T as a high and a low part, accumulated into the same columns by two MFMAs (~16 bits of P)
-  u32x4 Bh = split8<M>(x, false), Bl = split8<M>(x, true);
-  if (c.col >= G) {
-    Bh = zero4u();
-    Bl = zero4u();
-  }
+  p_to_b<G>(c, S[0], plds, c.col < G ? c.col : 0, x);
+  // P^T as a high and a low part, accumulated into the same columns by two MFMAs (~16 bits of P); columns G..15
+  // repeat head 0 and their results are never read
+  const u32x4 Bh = split8<M>(x, false), Bl = split8<M>(x, true);
   if (TAIL) {  // the new token's values from v_new; values past the valid length zeroed (no inf * 0)
     const int t0 = 8 * c.q;
     const int e_new = tnew - t0;
@@ -490,17 +486,19 @@ __device__ __forceinline__ void int2_task(const DecodeParams& p, const Ctx& c, c
     if constexpr (WEIGHTED) weighted_sums(S[i], wn[i], ws[i]);
     if (ok[i]) store_window_sums<G>(p, c, ids[i], ws[i], wo.m);
   }
-  // P.V: A = exact fp16 codes of 16 head_dim x 32 tokens, B = (P * scale)^T hi/lo, bias = sum P * zero
-  const bool live = c.col < G;
+  // P.V: A = exact fp16 codes of 16 head_dim x 32 tokens, B = (P * scale)^T hi/lo, bias = sum P * zero.
+  // G <= 4: B column 4g + h carries head h scaled by head_dim group g's value scales, so one B pair serves all
+  // eight head_dim tiles and every lane's scaling is used; tile dt's result lies in the columns of its group dt/2,
+  // and bias[0] holds the lane's own group. G = 8: one B pair per group, columns = heads, bias[g] per group.
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) wo.acc[dt] = zero4();
 #pragma unroll
   for (int i = 0; i < QW; ++i) {
-    float x[8];
-    p_to_b<G>(c, S[i], plds, x);
     const uint32_t* vmw = ms + (2 * i + 1) * kMetaWords + c.q * 32;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    if constexpr (G <= 4) {
+      float x[8];
+      p_to_b<G>(c, S[i], plds, (c.col & 3) < G ? (c.col & 3) : 0, x);
+      const int g = c.col >> 2;
       const u32x4 m0 = ld16(vmw + 8 * g);
       const u32x4 m1 = ld16(vmw + 8 * g + 4);
       const uint32_t mws[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
@@ -511,19 +509,38 @@ __device__ __forceinline__ void int2_task(const DecodeParams& p, const Ctx& c, c
         y[e] = x[e] * half_bits_to_float(mws[e] & 0xFFFFu);
         zsum = fmaf(x[e], half_bits_to_float(mws[e] >> 16), zsum);
       }
-      wo.bias[g] += zsum;
-      u32x4 Bh = split8<MF16>(y, false), Bl = split8<MF16>(y, true);
-      if (!live) {
-        Bh = zero4u();
-        Bl = zero4u();
-      }
+      wo.bias[0] += zsum;
+      const u32x4 Bh = split8<MF16>(y, false), Bl = split8<MF16>(y, true);
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int dt = 2 * g + h2;
+      for (int dt = 0; dt < 8; ++dt) {
         const uint32_t wv = dt < 2 ? vc[i].x : (dt < 4 ? vc[i].y : (dt < 6 ? vc[i].z : vc[i].w));
-        const uint32_t c16 = (wv >> (16 * (dt & 1))) & 0xFFFFu;
-        const u32x4 a = codes_to_f16(c16);
+        const u32x4 a = codes_to_f16((wv >> (16 * (dt & 1))) & 0xFFFFu);
         wo.acc[dt] = MF16::mfma(a, Bl, MF16::mfma(a, Bh, wo.acc[dt]));
+      }
+    } else {
+      float x[8];
+      p_to_b<G>(c, S[i], plds, c.col < G ? c.col : 0, x);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x4 m0 = ld16(vmw + 8 * g);
+        const u32x4 m1 = ld16(vmw + 8 * g + 4);
+        const uint32_t mws[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+        float y[8];
+        float zsum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          y[e] = x[e] * half_bits_to_float(mws[e] & 0xFFFFu);
+          zsum = fmaf(x[e], half_bits_to_float(mws[e] >> 16), zsum);
+        }
+        wo.bias[g] += zsum;
+        const u32x4 Bh = split8<MF16>(y, false), Bl = split8<MF16>(y, true);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int dt = 2 * g + h2;
+          const uint32_t wv = dt < 2 ? vc[i].x : (dt < 4 ? vc[i].y : (dt < 6 ? vc[i].z : vc[i].w));
+          const u32x4 a = codes_to_f16((wv >> (16 * (dt & 1))) & 0xFFFFu);
+          wo.acc[dt] = MF16::mfma(a, Bl, MF16::mfma(a, Bh, wo.acc[dt]));
+        }
       }
     }
   }
@@ -616,9 +633,11 @@ __global__ __launch_bounds__(WPB * kWave) __attribute__((amdgpu_waves_per_eu(4))
 #pragma unroll
   for (int g = 0; g < 4; ++g) wo.bias[g] = 0.0f;
   float* plds = plds_all[wave];
+  bool grouped = false;  // the wave ran an INT2 task whose P.V leaves tile dt in the columns of group dt/2
 
   if (task < t_tail) {
     if (q0 < c.nq) {
+      grouped = G <= 4;
       if (c.nf != MF) {
 #pragma unroll
         for (int i = 0; i < QW; ++i) {
@@ -665,17 +684,23 @@ __global__ __launch_bounds__(WPB * kWave) __attribute__((amdgpu_waves_per_eu(4))
     }
   }
 
-  // ---- wave result: O[h][d] = acc(col h) + bias(group of d); merged over the workgroup's waves ---------------------
+  // ---- wave result: O[h][d] = acc + bias of d's head_dim group; merged over the workgroup's waves ----------------
+  // (grouped: head h of tile dt in column 4 (dt/2) + h, the lane's group bias in bias[0]; else head h in column h)
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    wo.bias[g] = xor_sum(wo.bias[g], 16);
-    wo.bias[g] = xor_sum(wo.bias[g], 32);
+    if (g == 0 || !grouped) {
+      wo.bias[g] = xor_sum(wo.bias[g], 16);
+      wo.bias[g] = xor_sum(wo.bias[g], 32);
+    }
   }
+  const int hl = grouped ? (c.col & 3) : c.col;
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
+    const bool st = hl < G && (!grouped || (c.col >> 2) == (dt >> 1));
+    const float b = grouped ? wo.bias[0] : wo.bias[dt >> 1];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      if (c.col < G) sm_o[wave][c.col][16 * dt + 4 * c.q + r] = wo.acc[dt][r] + wo.bias[dt >> 1];
+      if (st) sm_o[wave][hl][16 * dt + 4 * c.q + r] = wo.acc[dt][r] + b;
     }
   }
   if (c.col == 0 && 4 * c.q < G) {
