@@ -118,6 +118,7 @@ __device__ __forceinline__ void fetch_args_combine(const DecodeParams& p) {
 struct MBF16 {
   static constexpr uint32_t kMagic = 0x43004300u;  // two bf16 128.0
   static constexpr float kMagicVal = 128.0f;
+  static constexpr uint32_t kOnes = 0x3F803F80u;   // two bf16 1.0
   static __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                    0, 0, 0);
@@ -128,6 +129,7 @@ struct MBF16 {
 struct MF16 {
   static constexpr uint32_t kMagic = 0x64006400u;  // two fp16 1024.0
   static constexpr float kMagicVal = 1024.0f;
+  static constexpr uint32_t kOnes = 0x3C003C00u;   // two fp16 1.0
   static __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
                                                   0, 0);
@@ -141,6 +143,14 @@ template <> struct MfmaOf<F16> { using M = MF16; };
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.0f, 0.0f, 0.0f, 0.0f}; }
 __device__ __forceinline__ u32x4 zero4u() { return u32x4{0u, 0u, 0u, 0u}; }
+
+// The magic pattern in a VGPR the compiler cannot see through, so that every (x & mask) | magic below is one
+// v_and_or_b32 (a literal would need a separate v_or: one instruction takes at most one constant)
+__device__ __forceinline__ uint32_t magic_in_vgpr(uint32_t magic) {
+  uint32_t v;
+  asm("v_mov_b32 %0, %1" : "=v"(v) : "s"(magic));
+  return v;
+}
 
 // 8 two-bit codes (bits 2e, e = 0..7) -> 8 16-bit values  magic | code,  k-slot e = code e
 __device__ __forceinline__ u32x4 expand_codes(uint32_t c16, uint32_t magic) {
@@ -156,13 +166,9 @@ __device__ __forceinline__ uint32_t f16x2_minus_1024(uint32_t w) {
   v = v + m;
   return __builtin_bit_cast(uint32_t, v);
 }
-__device__ __forceinline__ u32x4 codes_to_f16(uint32_t c16) {
-  const uint32_t z = c16 | (c16 << 14);
-  const uint32_t w0 = (z & 0x00030003u) | MF16::kMagic;
-  const uint32_t w1 = ((z >> 4) & 0x00030003u) | MF16::kMagic;
-  const uint32_t w2 = ((z >> 8) & 0x00030003u) | MF16::kMagic;
-  const uint32_t w3 = ((z >> 12) & 0x00030003u) | MF16::kMagic;
-  return u32x4{f16x2_minus_1024(w0), f16x2_minus_1024(w1), f16x2_minus_1024(w2), f16x2_minus_1024(w3)};
+__device__ __forceinline__ u32x4 codes_to_f16(uint32_t c16, uint32_t magic) {
+  const u32x4 w = expand_codes(c16, magic);
+  return u32x4{f16x2_minus_1024(w.x), f16x2_minus_1024(w.y), f16x2_minus_1024(w.z), f16x2_minus_1024(w.w)};
 }
 
 // high or low part of 8 floats in a 16-bit MFMA type (x = hi + lo to ~16 significant bits)
@@ -185,6 +191,15 @@ __device__ __forceinline__ u32x4 split8(const float (&x)[8], bool low) {
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ uint2 ld8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
+
+// Sum over the four 16-lane rows (lanes l, l^16, l^32, l^48) by cross-row swaps; every lane gets the same bits
+// (each step adds the same two values in the same order in both rows of a pair).
+__device__ __forceinline__ float sum_rows4(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 struct Ctx {
   int u, lane, q, col;
@@ -451,10 +466,44 @@ __device__ __forceinline__ void int2_task(const DecodeParams& p, const Ctx& c, c
     *reinterpret_cast<uint2*>(ms + (2 * i) * kMetaWords + 2 * c.lane) = ok[i] ? km[i] : z2;
     *reinterpret_cast<uint2*>(ms + (2 * i + 1) * kMetaWords + 2 * c.lane) = ok[i] ? vm[i] : z2;
   }
-  float qsum[4][4];
-  q_group_sums<G, T>(c, aq, qsum);
   // logits: one MFMA per (16 tokens, group), the group's scale and zero applied to the fp32 product
   f32x4 S[QW][2];
+  if constexpr (G <= 4) {
+    // aq[k] holds group k's q in rows 4k .. 4k+3 (head = row % 4) and zeros elsewhere, so the four groups' MFMAs
+    // accumulate into one tile: lane (row block q, token col) holds group q's product for heads r = 0..3. Each
+    // lane applies its own group's scale and zero, and the four row blocks are summed. The same A against a B of
+    // ones gives every lane its group's q sums.
+    const u32x4 ones = {M::kOnes, M::kOnes, M::kOnes, M::kOnes};
+    const uint32_t mg = magic_in_vgpr(M::kMagic);
+    f32x4 qs = zero4();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) qs = M::mfma(aq[k], ones, qs);
+#pragma unroll
+    for (int i = 0; i < QW; ++i) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const uint32_t cw0 = t == 0 ? kc[i].x : kc[i].z;
+        const uint32_t cw1 = t == 0 ? kc[i].y : kc[i].w;
+        f32x4 o = zero4();
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t cw = k < 2 ? cw0 : cw1;
+          o = M::mfma(aq[k], expand_codes((cw >> (16 * (k & 1))) & 0xFFFFu, mg), o);
+        }
+        const uint32_t mw = ms[(2 * i) * kMetaWords + (16 * t + c.col) * kGroups + c.q];
+        const float s = half_bits_to_float(mw & 0xFFFFu);
+        const float zz = half_bits_to_float(mw >> 16) - M::kMagicVal * s;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = sum_rows4(fmaf(s, o[r], zz * qs[r]));
+          S[i][t][r] = ok[i] ? v * kInvSqrtD : -INFINITY;
+        }
+      }
+      if (PROBS && ok[i]) store_logits<G>(p, c, S[i], pos0 + kW * i, kW);
+    }
+  } else {
+  float qsum[4][4];
+  q_group_sums<G, T>(c, aq, qsum);
 #pragma unroll
   for (int i = 0; i < QW; ++i) {
 #pragma unroll
@@ -479,6 +528,7 @@ __device__ __forceinline__ void int2_task(const DecodeParams& p, const Ctx& c, c
     }
     if (PROBS && ok[i]) store_logits<G>(p, c, S[i], pos0 + kW * i, kW);
   }
+  }
   float ws[QW][4];
   task_softmax<QW>(S, wo, ws);
 #pragma unroll
@@ -492,6 +542,7 @@ __device__ __forceinline__ void int2_task(const DecodeParams& p, const Ctx& c, c
   // and bias[0] holds the lane's own group. G = 8: one B pair per group, columns = heads, bias[g] per group.
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) wo.acc[dt] = zero4();
+  const uint32_t mg16 = magic_in_vgpr(MF16::kMagic);
 #pragma unroll
   for (int i = 0; i < QW; ++i) {
     const uint32_t* vmw = ms + (2 * i + 1) * kMetaWords + c.q * 32;
@@ -514,7 +565,7 @@ __device__ __forceinline__ void int2_task(const DecodeParams& p, const Ctx& c, c
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const uint32_t wv = dt < 2 ? vc[i].x : (dt < 4 ? vc[i].y : (dt < 6 ? vc[i].z : vc[i].w));
-        const u32x4 a = codes_to_f16((wv >> (16 * (dt & 1))) & 0xFFFFu);
+        const u32x4 a = codes_to_f16((wv >> (16 * (dt & 1))) & 0xFFFFu, mg16);
         wo.acc[dt] = MF16::mfma(a, Bl, MF16::mfma(a, Bh, wo.acc[dt]));
       }
     } else {
@@ -538,7 +589,7 @@ __device__ __forceinline__ void int2_task(const DecodeParams& p, const Ctx& c, c
         for (int h2 = 0; h2 < 2; ++h2) {
           const int dt = 2 * g + h2;
           const uint32_t wv = dt < 2 ? vc[i].x : (dt < 4 ? vc[i].y : (dt < 6 ? vc[i].z : vc[i].w));
-          const u32x4 a = codes_to_f16((wv >> (16 * (dt & 1))) & 0xFFFFu);
+          const u32x4 a = codes_to_f16((wv >> (16 * (dt & 1))) & 0xFFFFu, mg16);
           wo.acc[dt] = MF16::mfma(a, Bl, MF16::mfma(a, Bh, wo.acc[dt]));
         }
       }
@@ -619,8 +670,17 @@ __global__ __launch_bounds__(WPB * kWave) __attribute__((amdgpu_waves_per_eu(4))
   // A operand: the G query heads (rows; rows beyond G repeat head G-1 and their results are never used);
   // k-block k = head_dim 32k + 8*(lane/16) .. +7
   u32x4 aq[4];
+  if (G <= 4 && task < t_tail) {
+    // INT2 task: the A of head_dim group k holds head h's q in row 4k + h (rows past G repeat head G-1), zero in
+    // the other rows, so the groups' products land in different rows of one tile
+    const int gk = c.col >> 2;
+    const u32x4 v = ld16(p.q + (size_t(u) * G + min(c.col & 3, G - 1)) * kD + 32 * gk + 8 * c.q);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) aq[k] = ld16(p.q + (size_t(u) * G + min(c.col, G - 1)) * kD + 32 * k + 8 * c.q);
+    for (int k = 0; k < 4; ++k) aq[k] = gk == k ? v : zero4u();
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) aq[k] = ld16(p.q + (size_t(u) * G + min(c.col, G - 1)) * kD + 32 * k + 8 * c.q);
+  }
 
   WaveOut wo;
 #pragma unroll
