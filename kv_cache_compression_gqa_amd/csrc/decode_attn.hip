@@ -18,6 +18,8 @@
 //   * q.K^T on MFMA (v_mfma_f32_16x16x32 bf16/f16): A = the G query heads (rows, zero-padded to 16), B = 16
 //     tokens x 32 head_dim of K. INT2 keys enter B as 128+c (bf16) / 1024+c (fp16) bit patterns, one group of 32
 //     head_dim per MFMA; the group's scale/zero are applied to the fp32 product:  s*acc + (z - magic*s)*sum(q).
+//     With G <= 4 an INT2 task puts group k's heads in rows 4k..4k+3 of group k's A, so the four group products
+//     share one tile (row block k = group k); each lane scales its own group and cross-row swaps add the groups.
 //   * softmax over the task's keys (max, exp, sums by DPP reductions over 16-lane rows); each window's exp-sum and the
 //     reference max it is relative to are written for the score. With per-position weights (WEIGHTED: CriticalKV
 //     page, "Algoritmo", the projected-value norm plugged into the window score) the window's exp-sum weights each
@@ -25,7 +27,8 @@
 //   * P.V on MFMA: A = 16 head_dim x 32 tokens of V (V is stored transposed per window), B = P^T (columns
 //     0..G-1) split into a high and a low part that two MFMAs accumulate into the same columns, so the product
 //     keeps ~16 bits of P with no merge afterwards. INT2 values enter A as exact fp16 codes and the per-token
-//     scale is folded into B (P*s); the zero term sum(P*z) is a VALU bias.
+//     scale is folded into B (P*s); the zero term sum(P*z) is a VALU bias. With G <= 4, B column 4g + h carries
+//     head h scaled by head_dim group g, so one B pair serves every head_dim tile of the window.
 //   The workgroup's waves merge their (m, l, o) in LDS into one partial per workgroup.
 // decode_combine: merges the partials of a unit in a fixed order (bitwise reproducible), writes o, converts the
 // window exp-sums into probability mass, adds it to the cumulative score, finalises the optional probabilities
