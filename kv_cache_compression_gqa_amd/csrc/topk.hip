@@ -4,8 +4,9 @@
 //
 // The kept set is found by the global top-M engine (topm.hip) over one row of n entries (any n: the last chunk is
 // ragged, nothing is padded). It leaves a bit mask (one bit per entry) and the kept counts of its chunks and of their
-// groups. topk_write handles 8192 entries per workgroup: their place in the output is the sum of the counts before
-// them; each thread expands its mask word into LDS at its prefix position (16-bit offsets), and the workgroup then
+// groups. topk_write handles four blocks of 8192 entries per workgroup (their mask words loaded up front): the
+// first block's place in the output is the sum of the counts before it, each next one follows the previous; per
+// block, each thread expands its mask word into LDS at its prefix position (16-bit offsets), and the workgroup then
 // stores the run contiguously.
 #include <algorithm>
 
@@ -15,11 +16,12 @@ namespace kvc {
 namespace {
 
 constexpr int kKThreads = 256;
-constexpr int kBlock = 8192;                         // entries per workgroup
-constexpr int kWords = kBlock / 32;                  // mask words per workgroup: one per thread
-constexpr int kChunksPerBlock = kBlock / kTopmChunk;  // engine chunks per workgroup
-static_assert(kWords == kKThreads, "one mask word per thread");
-static_assert(kTopmGroup % kChunksPerBlock == 0, "a workgroup's chunks lie in one group");
+constexpr int kBlock = 8192;                         // entries per block
+constexpr int kWords = kBlock / 32;                  // mask words per block: one per thread
+constexpr int kSub = 4;                              // blocks per workgroup
+constexpr int kChunksPerBlock = kBlock / kTopmChunk;  // engine chunks per block
+static_assert(kWords == kKThreads, "one mask word per thread and block");
+static_assert(kTopmGroup % (kSub * kChunksPerBlock) == 0, "a workgroup's chunks lie in one group");
 
 // exclusive prefix over the workgroup (thread order) and the total; two barriers
 __device__ int block_scan_int(int v, int* wsum, int* total) {
@@ -60,32 +62,42 @@ __global__ __launch_bounds__(kKThreads) void topk_write(const uint32_t* __restri
                                                         const int32_t* __restrict__ chunk_kept,
                                                         const int32_t* __restrict__ group_kept, int64_t n,
                                                         int64_t k, int32_t* __restrict__ idx) {
-  __shared__ uint16_t stage[kBlock];  // offsets (entry - first) of the kept entries, in order
+  __shared__ uint16_t stage[kBlock];  // offsets (entry - block start) of the block's kept entries, in order
   __shared__ int wsum[kKThreads / kWave];
   __shared__ long long bsum[kKThreads / kWave];
-  const int64_t word = int64_t(blockIdx.x) * kWords + threadIdx.x;
+  const int64_t blk0 = int64_t(blockIdx.x) * kSub;
   // only entries below n count: the engine clears the bits past n in its last chunk, and the words past that chunk
-  // (in this workgroup's range) are never written
-  const int64_t lo = word * 32;
-  uint32_t w = lo >= n ? 0u : (lo + 32 <= n ? bits[word] : bits[word] & ((1u << (n - lo)) - 1u));
+  // are never written
+  uint32_t w[kSub];
+#pragma unroll
+  for (int b = 0; b < kSub; ++b) {
+    const int64_t word = (blk0 + b) * kWords + threadIdx.x;
+    const int64_t lo = word * 32;
+    w[b] = lo >= n ? 0u : (lo + 32 <= n ? bits[word] : bits[word] & ((1u << (n - lo)) - 1u));
+  }
   // kept entries before this workgroup's first chunk: whole groups, then the group's chunks before it
-  const int64_t c0 = int64_t(blockIdx.x) * kChunksPerBlock;
+  const int64_t c0 = blk0 * kChunksPerBlock;
   const int64_t grp = c0 / kTopmGroup, gfirst = grp * kTopmGroup;
   long long before = 0;
   for (int64_t q = threadIdx.x; q < grp; q += kKThreads) before += group_kept[q];
   if (int64_t(threadIdx.x) < c0 - gfirst) before += chunk_kept[gfirst + threadIdx.x];
-  int total;
-  int p = block_scan_int(__popc(w), wsum, &total);
-  const long long base = block_sum_ll(before, bsum);
-  while (w) {
-    const int j = __builtin_ctz(w);
-    w &= w - 1;
-    stage[p++] = uint16_t(32 * threadIdx.x + j);
-  }
-  __syncthreads();
-  const int32_t first = int32_t(int64_t(blockIdx.x) * kBlock);
-  for (int i = threadIdx.x; i < total; i += kKThreads) {
-    if (base + i < k) idx[base + i] = first + int32_t(stage[i]);
+  long long base = block_sum_ll(before, bsum);
+#pragma unroll
+  for (int b = 0; b < kSub; ++b) {
+    int total;
+    int p = block_scan_int(__popc(w[b]), wsum, &total);  // its barriers also order the previous block's stage reads
+    uint32_t x = w[b];
+    while (x) {
+      const int j = __builtin_ctz(x);
+      x &= x - 1;
+      stage[p++] = uint16_t(32 * threadIdx.x + j);
+    }
+    __syncthreads();
+    const int32_t first = int32_t((blk0 + b) * kBlock);
+    for (int i = threadIdx.x; i < total; i += kKThreads) {
+      if (base + i < k) idx[base + i] = first + int32_t(stage[i]);
+    }
+    base += total;
   }
 }
 
@@ -96,8 +108,8 @@ struct TopkLayout {
 
 TopkLayout topk_layout(int64_t n) {
   TopkLayout L;
-  L.nb = (n + kBlock - 1) / kBlock;  // workgroups of topk_write
-  const size_t nb = size_t(std::max<int64_t>(L.nb, 1));
+  L.nb = (n + int64_t(kSub) * kBlock - 1) / (int64_t(kSub) * kBlock);  // workgroups of topk_write
+  const size_t nb = size_t(std::max<int64_t>(L.nb, 1)) * kSub;
   size_t o = 0;
   L.bits_off = o;
   o += align_up(nb * kWords * sizeof(uint32_t), 256);
