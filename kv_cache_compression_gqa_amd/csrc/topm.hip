@@ -14,10 +14,9 @@
 //              the sample the window [lo, hi] of bins that holds the m-th key with a wide margin (six standard
 //              deviations of the sampled count, on the host); entries below lo are kept, entries of lo .. hi go
 //              to their chunk's candidate segment in index order, and the exact histogram is built on the way.
-//   fallback   each workgroup picks the exact bin b1 from that histogram; if the window held it (the usual case) it
-//              returns at once, otherwise it classifies its chunks again against b1 alone.
-//   cand_hist2 (256 chunks' candidates per workgroup): picks b1; histogram of the next 11 key bits of the candidates
-//              in b1.
+//   cand_hist2 (256 chunks' candidates per workgroup): picks the exact bin b1 from that histogram; if the window did
+//              not hold it (rare), first classifies its own chunks again against b1 alone; then the histogram of the
+//              next 11 key bits of the candidates in b1.
 //   cand_hist3 (groups of 64 chunks): picks b2; histogram of the last 10 key bits of the candidates in (b1, b2).
 //   cand_mark  (same groups): picks b3, i.e. the threshold key T; keeps every candidate below T and counts the ties
 //              (key == T) of its group.
@@ -41,7 +40,6 @@ constexpr int kBins = 2048;
 constexpr int64_t kSampleMax = 65536;      // sampled float4s
 constexpr int kSampleTB = 256, kSamplePer = 4;  // sample: threads, float4s per thread
 constexpr int kClsTB = 256, kClsPer = 4;   // classify: threads, chunks per wave
-constexpr int kFallbackPer = 16;           // the fallback classification: chunks per wave
 constexpr int kH2TB = 1024, kH2G = 256;    // cand_hist2: threads, chunks per workgroup
 constexpr int kCandTB = 256, kCandG = kTopmGroup;  // cand_hist3 / cand_mark / tie_fix
 static_assert(kCandG <= kWave, "a group's chunk prefix is one wave scan");
@@ -357,44 +355,22 @@ __global__ __launch_bounds__(kSampleTB) void eng_sample(TopmInput in, Ws ws, int
   }
 }
 
-// kBits: the keep mask as bits (one row: chunk starts are multiples of 2048), else as bytes; kBeta: scores computed
-// from beta. kSpec: the first classification, against the window [lo, hi] located in the sample, building the exact
-// histogram on the way. Otherwise the fallback: every workgroup picks the exact bin b1 and returns at once when the
-// window held it, else classifies its chunks again against [b1, b1] (rewriting their mask, candidates and counts).
-// Four waves per SIMD (at most 128 VGPRs), so that the speculative pass's grid is resident in one round.
-template <bool kBits, bool kBeta, bool kSpec, int kPer>
-__global__ __launch_bounds__(kClsTB) __attribute__((amdgpu_waves_per_eu(4))) void eng_classify(TopmInput in, Ws ws, int64_t nb, int64_t m, int64_t lo_pos,
-                                                       int64_t hi_pos, uint8_t* __restrict__ keep,
-                                                       uint32_t* __restrict__ keep_bits, int32_t* status) {
-  constexpr int W = kClsTB / kWave, kSpan = W * kPer;
-  __shared__ long long pk[2];
-  __shared__ uint32_t h[kSpec ? kBins : 1];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
-  int64_t b = int64_t(blockIdx.x) * kSpan + wave;
-  float4 v[kU], vn[kU];
-  int lo, hi;
-  if (kSpec) {
-    if (b < nb) load_chunk<kBeta>(in, chunk_of(b, in.row_len), lane, v);  // the first chunk's loads first
-    for (int i = threadIdx.x; i < kBins; i += kClsTB) h[i] = 0u;
-    wave_locate(ws.hist + 3 * kBins, lo_pos, hi_pos, pk);
-    __syncthreads();
-    lo = int(pk[0]);
-    hi = int(pk[1]);
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-      ws.st->lo = lo;
-      ws.st->hi = hi;
-    }
-  } else {
-    wave_pick(ws.hist, kBins, m, pk);
-    __syncthreads();
-    const int b1 = int(pk[0]), slo = ws.st->lo, shi = ws.st->hi;
-    if ((b1 < 0 && slo == 0) || (slo <= b1 && b1 <= shi)) return;  // uniform: the window held b1
-    lo = hi = b1;
-    if (b < nb) load_chunk<kBeta>(in, chunk_of(b, in.row_len), lane, v);
-  }
+// One wave classifies chunks b, b + stride, ... (at most kPer of them, below nb) against the bins [lo, hi]: entries
+// below lo are kept, entries of lo .. hi go to their chunk's candidate segment in index order, and with kHist the
+// exact histogram of the top 11 key bits is built in h (LDS) on the way. kBits: the keep mask as bits (one row:
+// chunk starts are multiples of 2048), else as bytes; kBeta: scores computed from beta. v holds chunk b's scores,
+// loaded by the caller (so that they are in flight during its setup); kPrefetch: the next chunk's loads are issued
+// before the current one is classified (32 more VGPRs). Returns whether a NaN score was seen.
+template <bool kBits, bool kBeta, bool kHist, bool kPrefetch, int kPer>
+__device__ bool classify_chunks(const TopmInput& in, const Ws& ws, int64_t nb, int64_t b, int stride, int lo, int hi,
+                                uint8_t* __restrict__ keep, uint32_t* __restrict__ keep_bits, uint32_t* h,
+                                float4 (&v)[kU]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float4 vn[kU];
   bool nan = false;
-  for (int i = 0; i < kPer && b < nb; ++i, b += W) {  // wave-uniform; no barrier below
-    if (i + 1 < kPer && b + W < nb) load_chunk<kBeta>(in, chunk_of(b + W, in.row_len), lane, vn);
+  for (int i = 0; i < kPer && b < nb; ++i, b += stride) {  // wave-uniform; no barrier below
+    if (kPrefetch && i + 1 < kPer && b + stride < nb) load_chunk<kBeta>(in, chunk_of(b + stride, in.row_len), lane, vn);
+    if (!kPrefetch && i > 0) load_chunk<kBeta>(in, chunk_of(b, in.row_len), lane, v);
     const Chunk r = chunk_of(b, in.row_len);
     uint2* seg = ws.cand + size_t(b) * kChunk;
     int base = 0, kept = 0;  // wave-uniform: candidates written so far, entries kept
@@ -410,7 +386,7 @@ __global__ __launch_bounds__(kClsTB) __attribute__((amdgpu_waves_per_eu(4))) voi
       for (int c = 0; c < 4; ++c) {
         const bool valid = kFull || e + c < r.end;
         const int d = int(desc_key(vs[c]) >> 21);
-        if (kSpec && valid) atomicAdd(&h[d], 1u);
+        if (kHist && valid) atomicAdd(&h[d], 1u);
         k1[c] = valid && d < lo;
         cd[c] = valid && uint32_t(d - lo) <= uint32_t(hi - lo);
         K[c] = __ballot(k1[c]);
@@ -457,20 +433,49 @@ __global__ __launch_bounds__(kClsTB) __attribute__((amdgpu_waves_per_eu(4))) voi
       ws.ccnt[b] = base;
       ws.kept[b] = kept;
     }
+    if (kPrefetch) {
 #pragma unroll
-    for (int u = 0; u < kU; ++u) v[u] = vn[u];
-  }
-  if (kSpec) {
-    if (nan) atomicOr(status, KVC_DEV_NAN_SCORE);
-    __syncthreads();
-    for (int bin = threadIdx.x; bin < kBins; bin += kClsTB) {
-      if (h[bin] != 0u) atomicAdd(&ws.hist[bin], h[bin]);
+      for (int u = 0; u < kU; ++u) v[u] = vn[u];
     }
+  }
+  return nan;
+}
+
+// The first classification, against the window [lo, hi] of bins that the sample locates around the m-th key,
+// building the exact histogram on the way. Four waves per SIMD (at most 128 VGPRs), so that the grid is resident
+// in one round.
+template <bool kBits, bool kBeta>
+__global__ __launch_bounds__(kClsTB) __attribute__((amdgpu_waves_per_eu(4))) void eng_classify(
+    TopmInput in, Ws ws, int64_t nb, int64_t lo_pos, int64_t hi_pos, uint8_t* __restrict__ keep,
+    uint32_t* __restrict__ keep_bits, int32_t* status) {
+  constexpr int W = kClsTB / kWave, kSpan = W * kClsPer;
+  __shared__ long long pk[2];
+  __shared__ uint32_t h[kBins];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
+  const int64_t b = int64_t(blockIdx.x) * kSpan + wave;
+  float4 v[kU];
+  if (b < nb) load_chunk<kBeta>(in, chunk_of(b, in.row_len), lane, v);  // the first chunk's loads first
+  for (int i = threadIdx.x; i < kBins; i += kClsTB) h[i] = 0u;
+  wave_locate(ws.hist + 3 * kBins, lo_pos, hi_pos, pk);
+  __syncthreads();
+  const int lo = int(pk[0]), hi = int(pk[1]);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    ws.st->lo = lo;
+    ws.st->hi = hi;
+  }
+  const bool nan = classify_chunks<kBits, kBeta, true, true, kClsPer>(in, ws, nb, b, W, lo, hi, keep, keep_bits, h, v);
+  if (nan) atomicOr(status, KVC_DEV_NAN_SCORE);
+  __syncthreads();
+  for (int bin = threadIdx.x; bin < kBins; bin += kClsTB) {
+    if (h[bin] != 0u) atomicAdd(&ws.hist[bin], h[bin]);
   }
 }
 
-// picks b1; histogram of key bits 20..10 of the candidates in b1
-__global__ __launch_bounds__(kH2TB) void eng_cand_hist2(Ws ws, int64_t nb, int64_t m) {
+// picks b1; if the sampled window missed it (rare), classifies this workgroup's chunks again against [b1, b1]
+// (rewriting their mask, candidates and counts); then the histogram of key bits 20..10 of the candidates in b1
+template <bool kBits, bool kBeta>
+__global__ __launch_bounds__(kH2TB) void eng_cand_hist2(TopmInput in, Ws ws, int64_t nb, int64_t m,
+                                                        uint8_t* __restrict__ keep, uint32_t* __restrict__ keep_bits) {
   __shared__ uint32_t h[kBins];
   __shared__ int pref[kH2G + 1];
   __shared__ int wsum[kH2TB / kWave];
@@ -481,6 +486,18 @@ __global__ __launch_bounds__(kH2TB) void eng_cand_hist2(Ws ws, int64_t nb, int64
   wave_pick(ws.hist, kBins, m, pk);  // the exact b1 (wave 0, published by the barriers below)
   group_prefix_block<kH2TB>(ws, b0, g, pref, wsum);
   const int b1 = int(pk[0]);
+  const int slo = ws.st->lo, shi = ws.st->hi;
+  if (!((b1 < 0 && slo == 0) || (slo <= b1 && b1 <= shi))) {  // uniform: the window did not hold b1
+    constexpr int W = kH2TB / kWave;  // 16 waves of kH2G / W chunks each
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t b = b0 + (threadIdx.x >> 6);
+    float4 v[kU];
+    if (b < nb) load_chunk<kBeta>(in, chunk_of(b, in.row_len), lane, v);
+    (void)classify_chunks<kBits, kBeta, false, false, kH2G / W>(in, ws, nb, b, W, b1, b1, keep, keep_bits, nullptr, v);
+    __threadfence_block();  // the rewritten counts and candidates, read below by the workgroup's other waves
+    __syncthreads();
+    group_prefix_block<kH2TB>(ws, b0, g, pref, wsum);
+  }
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     ws.st->b1 = b1;
     ws.st->need1 = pk[1];
@@ -717,12 +734,11 @@ void launch_passes(const TopmInput& in, int64_t m, const TopmOutput& out, const 
     constexpr int64_t per_wg = int64_t(kSampleTB) * kSamplePer;
     hipLaunchKernelGGL(eng_sample<kBeta>, dim3(unsigned((S + per_wg - 1) / per_wg)), dim3(kSampleTB), 0, s, in, ws, S);
   }
-  constexpr int64_t spec_span = int64_t(kClsTB / kWave) * kClsPer, fb_span = int64_t(kClsTB / kWave) * kFallbackPer;
-  hipLaunchKernelGGL((eng_classify<kBits, kBeta, true, kClsPer>), dim3(unsigned((nb + spec_span - 1) / spec_span)),
-                     dim3(kClsTB), 0, s, in, ws, nb, m, lo_pos, hi_pos, out.keep, out.keep_bits, out.status);
-  hipLaunchKernelGGL((eng_classify<kBits, kBeta, false, kFallbackPer>), dim3(unsigned((nb + fb_span - 1) / fb_span)),
-                     dim3(kClsTB), 0, s, in, ws, nb, m, lo_pos, hi_pos, out.keep, out.keep_bits, out.status);
-  hipLaunchKernelGGL(eng_cand_hist2, dim3(unsigned((nb + kH2G - 1) / kH2G)), dim3(kH2TB), 0, s, ws, nb, m);
+  constexpr int64_t spec_span = int64_t(kClsTB / kWave) * kClsPer;
+  hipLaunchKernelGGL((eng_classify<kBits, kBeta>), dim3(unsigned((nb + spec_span - 1) / spec_span)), dim3(kClsTB), 0,
+                     s, in, ws, nb, lo_pos, hi_pos, out.keep, out.keep_bits, out.status);
+  hipLaunchKernelGGL((eng_cand_hist2<kBits, kBeta>), dim3(unsigned((nb + kH2G - 1) / kH2G)), dim3(kH2TB), 0, s, in,
+                     ws, nb, m, out.keep, out.keep_bits);
   const unsigned ng = unsigned(L.groups);
   hipLaunchKernelGGL(eng_cand_hist3, dim3(ng), dim3(kCandTB), 0, s, ws, nb);
   hipLaunchKernelGGL(eng_cand_mark<kBits>, dim3(ng), dim3(kCandTB), 0, s, ws, nb, out.keep, out.keep_bits);
