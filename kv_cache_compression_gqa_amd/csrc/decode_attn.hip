@@ -505,32 +505,32 @@ __device__ __forceinline__ void int2_task(const DecodeParams& p, const Ctx& c, c
       if (PROBS && ok[i]) store_logits<G>(p, c, S[i], pos0 + kW * i, kW);
     }
   } else {
-  float qsum[4][4];
-  q_group_sums<G, T>(c, aq, qsum);
+    float qsum[4][4];
+    q_group_sums<G, T>(c, aq, qsum);
 #pragma unroll
-  for (int i = 0; i < QW; ++i) {
+    for (int i = 0; i < QW; ++i) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      S[i][t] = zero4();
-      const u32x4 meta = ld16(ms + (2 * i) * kMetaWords + (16 * t + c.col) * kGroups);
-      const uint32_t cw0 = t == 0 ? kc[i].x : kc[i].z;
-      const uint32_t cw1 = t == 0 ? kc[i].y : kc[i].w;
+      for (int t = 0; t < 2; ++t) {
+        S[i][t] = zero4();
+        const u32x4 meta = ld16(ms + (2 * i) * kMetaWords + (16 * t + c.col) * kGroups);
+        const uint32_t cw0 = t == 0 ? kc[i].x : kc[i].z;
+        const uint32_t cw1 = t == 0 ? kc[i].y : kc[i].w;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t cw = k < 2 ? cw0 : cw1;
-        const uint32_t c16 = (cw >> (16 * (k & 1))) & 0xFFFFu;
-        const f32x4 o = M::mfma(aq[k], expand_codes(c16, M::kMagic), zero4());
-        const uint32_t mw = k == 0 ? meta.x : (k == 1 ? meta.y : (k == 2 ? meta.z : meta.w));
-        const float s = half_bits_to_float(mw & 0xFFFFu);
-        const float zz = half_bits_to_float(mw >> 16) - M::kMagicVal * s;
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t cw = k < 2 ? cw0 : cw1;
+          const uint32_t c16 = (cw >> (16 * (k & 1))) & 0xFFFFu;
+          const f32x4 o = M::mfma(aq[k], expand_codes(c16, M::kMagic), zero4());
+          const uint32_t mw = k == 0 ? meta.x : (k == 1 ? meta.y : (k == 2 ? meta.z : meta.w));
+          const float s = half_bits_to_float(mw & 0xFFFFu);
+          const float zz = half_bits_to_float(mw >> 16) - M::kMagicVal * s;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) S[i][t][r] += s * o[r] + zz * qsum[k][r];
+          for (int r = 0; r < 4; ++r) S[i][t][r] += s * o[r] + zz * qsum[k][r];
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[i][t][r] = ok[i] ? S[i][t][r] * kInvSqrtD : -INFINITY;
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) S[i][t][r] = ok[i] ? S[i][t][r] * kInvSqrtD : -INFINITY;
+      if (PROBS && ok[i]) store_logits<G>(p, c, S[i], pos0 + kW * i, kW);
     }
-    if (PROBS && ok[i]) store_logits<G>(p, c, S[i], pos0 + kW * i, kW);
-  }
   }
   float ws[QW][4];
   task_softmax<QW>(S, wo, ws);
