@@ -227,7 +227,9 @@ __global__ __launch_bounds__(TB) void route_tiers_kernel(kvc_tier_route_args a, 
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      if (!done[s] && wave == (W > 1 ? s : 0)) pick_digit(sh.hist[buf][s], need[s], &sh.digit[s], &sh.krem[s], &sh.eqc[s]);
+      if (!done[s] && wave == (W > 1 ? s : 0)) {
+        pick_digit(sh.hist[buf][s], need[s], &sh.digit[s], &sh.krem[s], &sh.eqc[s]);
+      }
     }
     __syncthreads();
 #pragma unroll

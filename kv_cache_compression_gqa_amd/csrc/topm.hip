@@ -396,8 +396,10 @@ __device__ bool classify_chunks(const TopmInput& in, const Ws& ws, int64_t nb, i
       if (kBits) {  // lane 8q writes the word of lanes 8q .. 8q + 7: bit 4 i + c = entry c of lane 8q + i
         if ((lane & 7) == 0) {
           const int sh = lane;  // 8 q
-          const uint32_t x = spread4(uint32_t(K[0] >> sh) & 0xFFu) | (spread4(uint32_t(K[1] >> sh) & 0xFFu) << 1) |
-                             (spread4(uint32_t(K[2] >> sh) & 0xFFu) << 2) | (spread4(uint32_t(K[3] >> sh) & 0xFFu) << 3);
+          const uint32_t x = spread4(uint32_t(K[0] >> sh) & 0xFFu) |
+                             (spread4(uint32_t(K[1] >> sh) & 0xFFu) << 1) |
+                             (spread4(uint32_t(K[2] >> sh) & 0xFFu) << 2) |
+                             (spread4(uint32_t(K[3] >> sh) & 0xFFu) << 3);
           keep_bits[e >> 5] = x;
         }
       } else {
