@@ -7,12 +7,15 @@ import math
 import numpy as np
 import pytest
 
-from oracle import attention, criticalkv, dbtrim, int2, qevict, select
+from oracle import attention, criticalkv, dbtrim, diagnostics, fp, int2, paged, qevict, select, summary
 from oracle.fp import f16_round_down, f16_round_up, storage_to_f32
 from tests import test_oracle_attention_select as pins_as
 from tests import test_oracle_criticalkv_dbtrim as pins_cd
+from tests import test_oracle_diagnostics as pins_dg
 from tests import test_oracle_fp_int2 as pins_int2
+from tests import test_oracle_paged as pins_pg
 from tests import test_oracle_qevict as pins_qe
+from tests import test_oracle_summary as pins_sm
 
 try:
     from exceptiongroup import BaseExceptionGroup  # hypothesis reports several distinct failures as a group
@@ -170,7 +173,42 @@ def promoted_copy_truncated(self, w):  # the promoted copy rounded toward zero i
     return out[0], out[1]
 
 
-ORIG = {"three_tier": select.three_tier, "compact_plan": dbtrim.compact_plan, "scores": criticalkv.scores}
+def gather_row_shifted(pool, page_list, length, page):  # row (i + 1) % page of the page: one row late
+    rows = [pool[int(page_list[i // page]), (i + 1) % page] for i in range(length)]
+    return np.array(rows, dtype=pool.dtype).reshape(length, pool.shape[-1])
+
+
+def summarize_over_31(rows_bits, dtype):  # the sum divided by one less than the window's length
+    x = fp.storage_to_f64(rows_bits, dtype)
+    return fp.f32_to_storage_rne((x.sum(axis=0) / (x.shape[0] - 1)).astype(np.float32), dtype)
+
+
+def missed_mass_counts_int2(mass_full, tier):  # the INT2 windows' mass counted as missed too
+    return float(np.asarray(mass_full, np.float64)[np.asarray(tier) != select.FULL].sum())
+
+
+def perturbation_l2(o_full, o):  # an L2 distance in place of L1
+    return np.sqrt(((np.asarray(o_full, np.float64) - np.asarray(o, np.float64)) ** 2).sum(axis=1))
+
+
+def weighted_mass_head0_weight(p, key_pos, weight, n_windows, window):  # head 0's weights for every head
+    return ORIG["weighted_window_mass"](p, key_pos, np.broadcast_to(weight[:1], weight.shape), n_windows, window)
+
+
+def pack_codes_reversed(codes):  # element 4b + j in bits 6 - 2j .. 7 - 2j
+    c = codes.reshape(codes.shape[:-1] + (codes.shape[-1] // 4, 4)).astype(np.uint8)
+    out = np.zeros(c.shape[:-1], np.uint8)
+    for j in range(4):
+        out |= (c[..., j] & 3) << (6 - 2 * j)
+    return out
+
+
+def f16_round_down_by_nearest(x):  # round to nearest in place of toward -inf
+    return np.asarray(x, np.float32).astype(np.float16)
+
+
+ORIG = {"three_tier": select.three_tier, "compact_plan": dbtrim.compact_plan, "scores": criticalkv.scores,
+        "weighted_window_mass": attention.weighted_window_mass}
 
 # (case, [(module, attribute, replacement)], [(pin, args)])
 CASES = [
@@ -207,6 +245,22 @@ CASES = [
      [(pins_cd.test_criticalkv_scores_group_means, ())]),
     ("QEvict: promoted copy truncated", [(qevict.QEvictUnit, "_ledger_as_storage", promoted_copy_truncated)],
      [(pins_qe.test_ledger_is_write_once_across_promote_demote_cycles, ())]),
+    ("paged: row of the page one late", [(paged, "gather_row", gather_row_shifted)],
+     [(pins_pg.test_paged_equals_attention_over_the_contiguous_sequence, ())]),
+    ("summary: mean over 31", [(summary, "summarize", summarize_over_31)],
+     [(pins_sm.test_summary_is_the_rounded_exact_mean, ())]),
+    ("summary: ln 16 size correction", [(summary, "SIZE_CORRECTION", math.log(16.0))],
+     [(pins_sm.test_size_correction_matches_identical_tokens, ())]),
+    ("diagnostics: INT2 mass counted as missed", [(diagnostics, "future_missed_mass", missed_mass_counts_int2)],
+     [(pins_dg.test_future_missed_mass_brute_force_and_conservation, ())]),
+    ("diagnostics: L2 perturbation", [(diagnostics, "perturbation_l1", perturbation_l2)],
+     [(pins_dg.test_perturbation_closed_form_and_full_budget_zero, ())]),
+    ("weighted mass: head 0's weights", [(attention, "weighted_window_mass", weighted_mass_head0_weight)],
+     [(pins_dg.test_weighted_window_mass, ())]),
+    ("INT2: codes packed high bits first", [(int2, "pack_codes", pack_codes_reversed)],
+     [(pins_int2.test_pack_bit_positions_hand_worked, ())]),
+    ("fp16: round-down by nearest", [(fp, "f16_round_down", f16_round_down_by_nearest)],
+     [(pins_int2.test_f16_directed_rounding_against_exhaustive_table, ())]),
 ]
 
 
