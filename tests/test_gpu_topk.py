@@ -87,6 +87,21 @@ def test_topk_misleading_sample_takes_the_fallback(gpu_lib):
         assert np.array_equal(got, want), k
 
 
+def test_topk_fallback_over_many_workgroups(gpu_lib):
+    """The fallback classification at 2^24 + 5 entries: with a misleading sample, every one of the 33 candidate
+    workgroups reclassifies its own 256 chunks (the last one ragged) before the candidate passes."""
+    from tests.engine_sampling import sampled_entries
+    rng = np.random.default_rng(21)
+    n = (1 << 24) + 5
+    s32 = np.round(rng.standard_normal(n), 3).astype(np.float32)
+    s32[sampled_entries(n)] = np.float32(1e6)
+    k = n // 10
+    log(f"topk fallback n={n} k={k}")
+    got = selection.topk(torch.from_numpy(s32).cuda(), k).cpu().numpy()
+    want = np.sort(osel.topk(s32.astype(np.float64), k))
+    assert np.array_equal(got, want)
+
+
 def test_topk_zeros_and_denormals_rank_by_value(gpu_lib):
     """+0 and -0 tie (ranked by index); the smallest positive and negative subnormals rank on either side of them."""
     tiny = np.float32(1.4e-45)
