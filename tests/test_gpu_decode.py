@@ -73,10 +73,10 @@ def test_degenerate_budgets_and_contexts(gpu_lib, case):
 
 def test_many_units_two_int2_windows_per_task(gpu_lib):
     """1280 units: a step takes many rounds of workgroups, so the launch switches to two INT2 windows per wave
-    task and 4-wave workgroups. G = 8 (f16), 1 (bf16) and 2 (f16), probabilities on; the oracle follows units
+    task and 4-wave workgroups. G = 8 (f16), 1 (bf16), 2 (f16) and 4 (f16), probabilities on; the oracle follows units
     spread over layers, sequences and heads, two of them layers 0 and 9 of one (sequence, KV head), whose
     outputs must differ (every layer holds its windows in an order of its own and has its own step inputs)."""
-    for hq, hkv, batch, dtype in ((16, 2, 20, "f16"), (4, 4, 10, "bf16"), (8, 4, 10, "f16")):
+    for hq, hkv, batch, dtype in ((16, 2, 20, "f16"), (4, 4, 10, "bf16"), (8, 4, 10, "f16"), (16, 4, 10, "f16")):
         cfg = dataclasses.replace(configs.TINY, name=f"many_g{hq // hkv}", seed=14, hq=hq, hkv=hkv, dtype=dtype,
                                   layers=32, batch=batch, context=640, n_salient=5, budget_full=4, budget_int2=7,
                                   steps=4, route_every=2)
