@@ -39,13 +39,14 @@ def test_summaries_2k_context_g8_and_g1(gpu_lib):
         run_decode_parity(cfg, probs=False, summaries=True, log=log)
 
 
-def test_summaries_many_units(gpu_lib):
-    """1280 units (the many-round launch shape: two INT2 windows per task, 4-wave workgroups)."""
-    cfg = dataclasses.replace(configs.TINY, name="many_sum", seed=14, hq=16, hkv=2, dtype="f16", layers=32,
-                              batch=20, context=640, n_salient=5, budget_full=4, budget_int2=7, steps=4,
+@pytest.mark.parametrize("hkv, batch, dtype", [(2, 20, "f16"), (4, 10, "bf16")], ids=["g8_f16", "g4_bf16"])
+def test_summaries_many_units(gpu_lib, hkv, batch, dtype):
+    """1280 units (the many-round launch shape: two INT2 windows per task, 4-wave workgroups), G = 8 and 4."""
+    cfg = dataclasses.replace(configs.TINY, name="many_sum", seed=14, hq=16, hkv=hkv, dtype=dtype, layers=32,
+                              batch=batch, context=640, n_salient=5, budget_full=4, budget_int2=7, steps=4,
                               route_every=2)
     inp, plan = synth.make_decode_shared_layers(cfg)
-    log(f"case: span summaries, {cfg.n_units} units")
+    log(f"case: span summaries, {cfg.n_units} units, G = {16 // hkv}, {dtype}")
     run_decode_parity(cfg, inp=inp, plan=plan, check_units=[0, 333, 777, cfg.n_units - 1], probs=False,
                       summaries=True, log=log)
 

@@ -47,6 +47,19 @@ def test_weighted_score_2k_context_g8(gpu_lib):
                       probs=False, log=log)
 
 
+def test_weighted_score_many_units(gpu_lib):
+    """1280 units at G = 4 (bf16): the many-round launch shape, whose INT2 tasks take two windows each, with the
+    weights loaded beside each task's other loads; units spread over layers, sequences and heads."""
+    cfg = dataclasses.replace(configs.TINY, name="many_weighted", seed=15, hq=16, hkv=4, dtype="bf16", layers=32,
+                              batch=10, context=640, n_salient=5, budget_full=4, budget_int2=7, steps=4, route_every=2)
+    inp, plan = synth.make_decode_shared_layers(cfg)
+    U, NW = cfg.n_units, inp.n_windows_max
+    w = np.random.default_rng(13).lognormal(size=(U, 4, NW * cfg.window)).astype(np.float32)
+    log(f"case: weighted window score, {U} units, G = 4")
+    run_decode_parity(cfg, inp=inp, plan=plan, check_units=[0, 333, 777, U - 1],
+                      token_weight=torch.from_numpy(w).cuda(), oracle_weight=w.astype(np.float64), log=log)
+
+
 def test_criticalkv_norms_weight_the_window_score(gpu_lib):
     """End to end: the GPU's |V W_O,h|_1 (kvc_score(CRITICALKV) over the tiny cache's prefill keys and values, a
     seeded W_O) weights the decode's window score; the oracle computes its own norms from the same inputs."""
