@@ -27,10 +27,7 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTB = 256;
-constexpr int kChunk = 8192;     // entries per top-M block (inside one row)
 constexpr int kCChunk = 4096;    // positions per compaction block (inside one row)
-constexpr int kBins = 2048;
-constexpr int kVecPerThread = kChunk / (4 * kTB);  // float4 loads per thread and top-M block
 
 // ---- retention score ----------------------------------------------------------------------------------------
 __global__ __launch_bounds__(kTB) void retention_score_kernel(const float* __restrict__ beta, float* __restrict__ score,
