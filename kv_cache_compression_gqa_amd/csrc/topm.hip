@@ -125,6 +125,12 @@ __device__ __forceinline__ void load_chunk(const TopmInput& in, const Chunk& r, 
   }
 }
 
+// x OR-ed with the x of the lane that DPP control kCtrl names (all source lanes lie inside the wave here)
+template <int kCtrl>
+__device__ __forceinline__ uint32_t or_dpp(uint32_t x) {
+  return x | uint32_t(__builtin_amdgcn_update_dpp(0, int(x), kCtrl, 0xF, 0xF, false));
+}
+
 template <class V, int TB>
 __device__ V block_excl_scan(V v, V* wsum, V* total) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
@@ -282,14 +288,6 @@ __device__ __forceinline__ int lanes_below(unsigned long long m) {
   return int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
 }
 
-// bit i of x (x < 256) moved to bit 4 i
-__device__ __forceinline__ uint32_t spread4(uint32_t x) {
-  x = (x | (x << 12)) & 0x000F000Fu;
-  x = (x | (x << 6)) & 0x03030303u;
-  x = (x | (x << 3)) & 0x11111111u;
-  return x;
-}
-
 // Adds the kept counts of the chunks b0 .. b0 + g - 1 (thread t < g holds chunk b0 + t's, g <= G) to their rows:
 // one global atomic per distinct row, summed in LDS first (slot = row - row of b0; g chunks span at most g rows).
 // Every thread calls it (two barriers); rc holds G ints.
@@ -393,15 +391,15 @@ __device__ bool classify_chunks(const TopmInput& in, const Ws& ws, int64_t nb, i
         C[c] = __ballot(cd[c]);
       }
       kept += __popcll(K[0]) + __popcll(K[1]) + __popcll(K[2]) + __popcll(K[3]);
-      if (kBits) {  // lane 8q writes the word of lanes 8q .. 8q + 7: bit 4 i + c = entry c of lane 8q + i
-        if ((lane & 7) == 0) {
-          const int sh = lane;  // 8 q
-          const uint32_t x = spread4(uint32_t(K[0] >> sh) & 0xFFu) |
-                             (spread4(uint32_t(K[1] >> sh) & 0xFFu) << 1) |
-                             (spread4(uint32_t(K[2] >> sh) & 0xFFu) << 2) |
-                             (spread4(uint32_t(K[3] >> sh) & 0xFFu) << 3);
-          keep_bits[e >> 5] = x;
-        }
+      if (kBits) {
+        // bit 4 i + c of the word of lanes 8 q .. 8 q + 7 is entry c of lane 8 q + i: each lane puts its four bits in
+        // place and the eight lanes' values are OR-ed (neighbours, then pairs, then the mirrored half of 8 lanes)
+        const uint32_t nib = (k1[0] ? 1u : 0u) | (k1[1] ? 2u : 0u) | (k1[2] ? 4u : 0u) | (k1[3] ? 8u : 0u);
+        uint32_t x = nib << (4 * (lane & 7));
+        x = or_dpp<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+        x = or_dpp<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+        x = or_dpp<0x141>(x);  // row_half_mirror
+        if ((lane & 7) == 0) keep_bits[e >> 5] = x;
       } else {
         const uint32_t out = (k1[0] ? 1u : 0u) | (k1[1] ? 0x100u : 0u) | (k1[2] ? 0x10000u : 0u) |
                              (k1[3] ? 0x1000000u : 0u);
@@ -453,7 +451,9 @@ __global__ __launch_bounds__(kClsTB) __attribute__((amdgpu_waves_per_eu(4))) voi
   constexpr int W = kClsTB / kWave, kSpan = W * kClsPer;
   __shared__ long long pk[2];
   __shared__ uint32_t h[kBins];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
+  // the chunk index as a scalar (not for the byte-mask, score-input case, which then spills and measured slower)
+  const int wave = (kBits || kBeta) ? __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6)) : int(threadIdx.x >> 6);
+  const int lane = threadIdx.x & (kWave - 1);
   const int64_t b = int64_t(blockIdx.x) * kSpan + wave;
   float4 v[kU];
   if (b < nb) load_chunk<kBeta>(in, chunk_of(b, in.row_len), lane, v);  // the first chunk's loads first
@@ -492,7 +492,8 @@ __global__ __launch_bounds__(kH2TB) void eng_cand_hist2(TopmInput in, Ws ws, int
   if (!((b1 < 0 && slo == 0) || (slo <= b1 && b1 <= shi))) {  // uniform: the window did not hold b1
     constexpr int W = kH2TB / kWave;  // 16 waves of kH2G / W chunks each
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t b = b0 + (threadIdx.x >> 6);
+    const int w = (kBits || kBeta) ? __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6)) : int(threadIdx.x >> 6);
+    const int64_t b = b0 + w;  // as in eng_classify
     float4 v[kU];
     if (b < nb) load_chunk<kBeta>(in, chunk_of(b, in.row_len), lane, v);
     (void)classify_chunks<kBits, kBeta, false, false, kH2G / W>(in, ws, nb, b, W, b1, b1, keep, keep_bits, nullptr, v);
